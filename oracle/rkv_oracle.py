@@ -1,0 +1,299 @@
+"""Plain fp64 CPU oracle of the ResidualKV cache-write path.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only ``tests/``,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import or call this module.  It shares no code with the GPU library
+(``reference_residual_encoding_amd``) and neither imports the other; inputs
+come from ``synth`` (random draws only).
+
+Source: the ResidualKV reading notes, "ResidualKV：基于参考向量与残差的
+KV Cache 压缩" (notes on arXiv 2602.08005v2), cited below as [RKV] with the
+notes' own section numbers.  Every step follows the order of [RKV] §2.1-§2.4:
+
+  1. reference schedule: a reference every ``s`` tokens          ([RKV] §2.6)
+  2. candidate pool of token i: earlier references; k_i = min(k, |pool|)
+                                                                 ([RKV] §2.1)
+  3. the k_i references nearest in squared L2 over the joint vector
+                                                  ([RKV] §2.2, retrieval eq.)
+  4. their arithmetic mean in KV space           ([RKV] §2.2, mean eq.)
+  5. z = f_c(kv_i) - f_c(mean), f_c the SwiGLU compressor
+                                          ([RKV] §2.3, f_c and boxed z eq.)
+  6. per-token group min-max quantiser            ([RKV] §2.4, three eqs.)
+  7. dequantisation of selected tokens           ([RKV] §2.4 third eq.,
+                                                   §2.7 decode step 3)
+
+Readings taken where the notes are silent (each is listed with its reason in
+the design notes of the repository):
+  * references sit at positions t with t % s == 0 of each sequence; the pool
+    of token t holds the references at positions j < t of the same sequence;
+  * distances are unweighted over all 2*d_k coordinates; ties in distance are
+    broken by the smaller position;
+  * Swish has beta = 1 (SiLU); f_c has no biases;
+  * reference tokens are stored as they are: their record is all zero and
+    their ref_idx row is all -1;
+  * quantiser groups are consecutive coordinates [j*g, (j+1)*g) of one token
+    (the last group may be shorter); each group stores two fp16 numbers, the
+    step Delta_h = fp16(Delta) and the minimum m_h = fp16(z_min); codes are
+    computed against the stored (Delta_h, m_h) so the decoder reproduces the
+    encoder's grid, rounded half-to-even and clamped to [0, 2^b - 1]; a group
+    whose Delta_h is 0 (constant group) stores q = 0 and decodes to m_h with
+    no division;
+  * the quantiser decides integers in float32, the precision of the GPU
+    kernel: z is rounded to float32 first and (max - min), the division by
+    2^b - 1 and (z - m_h) / Delta_h are float32 operations;
+  * codes are packed little-endian inside a byte: coordinate r of a byte
+    holds bits [r*b, (r+1)*b);
+  * dequantised values are q * Delta_h + m_h, exact in float64, then rounded
+    once to float32.
+
+Parity status: the selection, mean, compressor and quantiser are pinned by
+the tests in ``tests/test_oracle_pins.py`` (brute force, closed-form
+identities, special cases and hand-derived golden values).  The actual
+numbers of z and of the codes at the synthetic workloads have no printed
+counterpart in the pages: beyond those pins they are "parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Iterable, Optional, Sequence
+
+import numpy as np
+
+F64 = np.float64
+F32 = np.float32
+
+
+# ---------------------------------------------------------------- schedule
+def reference_positions(T: int, s: int) -> np.ndarray:
+    """Fixed-stride reference schedule, one reference every s tokens ([RKV] §2.6)."""
+    return np.arange(0, T, s, dtype=np.int64)
+
+
+def is_reference(t: int, s: int) -> bool:
+    return t % s == 0
+
+
+def candidate_pool(t: int, s: int) -> np.ndarray:
+    """T_ref,t: the references already in the cache when token t is written
+    ([RKV] §2.1 symbol table; §2.2 'existing reference pool')."""
+    return np.arange(0, t, s, dtype=np.int64)
+
+
+def k_effective(k: int, pool_size: int) -> int:
+    """Warm-up neighbour count k_i = min(k, |T_ref,i|) ([RKV] §2.1)."""
+    return min(k, pool_size)
+
+
+# ---------------------------------------------------------------- retrieval
+def squared_l2(x: np.ndarray, Y: np.ndarray) -> np.ndarray:
+    """||x - y_j||_2^2 for every row y_j of Y, by direct differences."""
+    diff = np.asarray(Y, F64) - np.asarray(x, F64)[None, :]
+    return np.einsum("jc,jc->j", diff, diff)
+
+
+def retrieve(kv_seq: np.ndarray, t: int, s: int, k: int):
+    """Top-k_t nearest references of token t ([RKV] §2.2 retrieval equation).
+
+    Returns (R, d_sorted): R are the chosen reference positions ordered by
+    (distance, position); d_sorted are all pool distances in the same order.
+    """
+    pool = candidate_pool(t, s)
+    d = squared_l2(kv_seq[t], kv_seq[pool])
+    order = np.lexsort((pool, d))            # primary key d, then position
+    k_t = k_effective(k, len(pool))
+    return pool[order[:k_t]], d[order]
+
+
+def reference_mean(kv_seq: np.ndarray, R: Sequence[int]) -> np.ndarray:
+    """Arithmetic mean of the retrieved references in KV space ([RKV] §2.2)."""
+    return np.asarray(kv_seq[np.asarray(R)], F64).sum(axis=0) / F64(len(R))
+
+
+# ---------------------------------------------------------------- compressor
+def swish(u: np.ndarray) -> np.ndarray:
+    """Swish with beta = 1: u * sigmoid(u)."""
+    return u / (1.0 + np.exp(-u))
+
+
+def f_c(x: np.ndarray, W1: np.ndarray, W2: np.ndarray, W3: np.ndarray) -> np.ndarray:
+    """SwiGLU compressor (Swish(x W_c1) * x W_c2) W_c3 ([RKV] §2.3), row-wise."""
+    x = np.asarray(x, F64)
+    return (swish(x @ W1) * (x @ W2)) @ W3
+
+
+def residual_latent(kv_t, mean, W1, W2, W3) -> np.ndarray:
+    """z = f_c(kv_i) - f_c(mean_ref,i) ([RKV] §2.3, boxed equation)."""
+    return f_c(kv_t, W1, W2, W3) - f_c(mean, W1, W2, W3)
+
+
+# ---------------------------------------------------------------- quantiser
+def group_bounds(d_c: int, g: int):
+    """Consecutive groups of at most g coordinates inside one token ([RKV] §2.4)."""
+    return [(a, min(a + g, d_c)) for a in range(0, d_c, g)]
+
+
+def quantize(z: np.ndarray, g: int, b: int):
+    """Per-token group min-max quantiser ([RKV] §2.4).
+
+    z: [n, d_c] latents.  Returns q [n, d_c] (int64 codes), Delta_h and m_h
+    [n, n_groups] as float16.  Integer decisions are taken in float32 (see
+    the module docstring).
+    """
+    z32 = np.asarray(z, F64).astype(F32)
+    n, d_c = z32.shape
+    levels = F32(2 ** b - 1)
+    bounds = group_bounds(d_c, g)
+    q = np.zeros((n, d_c), dtype=np.int64)
+    dh = np.zeros((n, len(bounds)), dtype=np.float16)
+    mh = np.zeros((n, len(bounds)), dtype=np.float16)
+    for gi, (a, e) in enumerate(bounds):
+        zg = z32[:, a:e]
+        zmin = zg.min(axis=1)
+        zmax = zg.max(axis=1)
+        delta = (zmax - zmin) / levels                 # float32 ops
+        dh[:, gi] = delta.astype(np.float16)
+        mh[:, gi] = zmin.astype(np.float16)
+        dhf = dh[:, gi].astype(F32)[:, None]
+        mhf = mh[:, gi].astype(F32)[:, None]
+        const = dhf == 0                               # constant group: no division
+        safe = np.where(const, F32(1), dhf)
+        t = (zg - mhf) / safe
+        qq = np.clip(np.rint(t), 0, int(levels)).astype(np.int64)
+        q[:, a:e] = np.where(const, 0, qq)
+    return q, dh, mh
+
+
+def dequantize(q: np.ndarray, dh: np.ndarray, mh: np.ndarray, g: int) -> np.ndarray:
+    """z~ = q * Delta + z_min per group ([RKV] §2.4 third equation).
+
+    Exact in float64 for fp16 (Delta_h, m_h) and b <= 8, then one rounding to
+    float32.  Returns float32 [n, d_c].
+    """
+    n, d_c = q.shape
+    out = np.empty((n, d_c), dtype=F64)
+    for gi, (a, e) in enumerate(group_bounds(d_c, g)):
+        out[:, a:e] = (q[:, a:e].astype(F64) * dh[:, gi:gi + 1].astype(F64)
+                       + mh[:, gi:gi + 1].astype(F64))
+    return out.astype(F32)
+
+
+def pack_codes(q: np.ndarray, b: int) -> np.ndarray:
+    """Little-endian packing: coordinate per*j + r -> bits [r*b, (r+1)*b) of byte j."""
+    n, d_c = q.shape
+    per = 8 // b
+    assert d_c % per == 0
+    qq = q.astype(np.uint32).reshape(n, d_c // per, per)
+    out = np.zeros((n, d_c // per), dtype=np.uint32)
+    for r in range(per):
+        out |= qq[:, :, r] << np.uint32(b * r)
+    return out.astype(np.uint8)
+
+
+def unpack_codes(codes: np.ndarray, b: int, d_c: int) -> np.ndarray:
+    n = codes.shape[0]
+    per = 8 // b
+    mask = (1 << b) - 1
+    c = codes.astype(np.int64)
+    out = np.empty((n, d_c // per, per), dtype=np.int64)
+    for r in range(per):
+        out[:, :, r] = (c >> (b * r)) & mask
+    return out.reshape(n, d_c)
+
+
+def record_bytes_per_token(d_c: int, g: int, b: int) -> int:
+    """b-bit payload plus two fp16 numbers per group ([RKV] §2.4, §3.3)."""
+    n_groups = -(-d_c // g)
+    return d_c * b // 8 + 4 * n_groups
+
+
+def q_b(b: int, g: int = 32) -> float:
+    """Relative group storage vs fp16: b/16 bits-ratio plus two fp16 per g ([RKV] §3.3)."""
+    return b / 16.0 + 2.0 / g
+
+
+def storage_ratio_vs_fp16(C: int, d_c: int, g: int, b: int) -> float:
+    """Bytes of one non-reference record over its fp16 joint vector (2*C bytes)."""
+    return record_bytes_per_token(d_c, g, b) / (2.0 * C)
+
+
+def keep_ratio(beta: float, rho_ref: float, qb: float, dc_over_2dk: float,
+               q_full: float = None) -> float:
+    """KR accounting of [RKV] §3.3: full-attention layers at 4-bit, sparse
+    layers holding fp8 references (half of fp16, at density rho_ref) plus the
+    short codes."""
+    if q_full is None:
+        q_full = q_b(4)
+    return beta * q_full + (1.0 - beta) * (0.5 * rho_ref + qb * dc_over_2dk)
+
+
+# ---------------------------------------------------------------- encode
+def encode_tokens(kv_seq: np.ndarray, W1, W2, W3, positions: Iterable[int], *,
+                  k: int, g: int, b: int, s: int, n_diag: Optional[int] = None) -> Dict:
+    """Encode the given positions of one sequence, each on its own.
+
+    kv_seq: [T, C] joint vectors [K heads | V heads], pre-RoPE ([RKV] §2.1).
+    Returns per position: ref_idx (sorted positions, -1 pad), z, q, Delta_h,
+    m_h, codes, and the first ``n_diag`` pool distances in (d, position)
+    order (for the tie rule of the parity tests).
+    """
+    kv_seq = np.asarray(kv_seq, F64)
+    W1 = np.asarray(W1, F64); W2 = np.asarray(W2, F64); W3 = np.asarray(W3, F64)
+    positions = np.asarray(list(positions), dtype=np.int64)
+    n = len(positions)
+    d_c = W3.shape[1]
+    if n_diag is None:
+        n_diag = k + 1
+    ref_idx = np.full((n, k), -1, dtype=np.int32)
+    d_diag = np.full((n, n_diag), np.inf)
+    z = np.zeros((n, d_c), dtype=F64)
+    enc_rows, enc_kv, enc_mean = [], [], []
+    for i, t in enumerate(positions):
+        if is_reference(int(t), s):
+            continue                       # references are stored as they are
+        R, d_sorted = retrieve(kv_seq, int(t), s, k)
+        ref_idx[i, :len(R)] = np.sort(R)
+        m = min(n_diag, len(d_sorted))
+        d_diag[i, :m] = d_sorted[:m]
+        enc_rows.append(i)
+        enc_kv.append(kv_seq[t])
+        enc_mean.append(reference_mean(kv_seq, R))
+    if enc_rows:
+        rows = np.asarray(enc_rows)
+        z[rows] = residual_latent(np.stack(enc_kv), np.stack(enc_mean), W1, W2, W3)
+    q, dh, mh = quantize(z, g, b)
+    ref_rows = np.array([is_reference(int(t), s) for t in positions], dtype=bool)
+    q[ref_rows] = 0                        # stored directly: all-zero record
+    dh[ref_rows] = 0
+    mh[ref_rows] = 0
+    return dict(positions=positions, ref_idx=ref_idx, z=z, q=q, scale=dh, zmin=mh,
+                codes=pack_codes(q, b), d_diag=d_diag, is_ref=ref_rows)
+
+
+def encode(kv: np.ndarray, W1, W2, W3, *, k: int, g: int, b: int, s: int) -> Dict:
+    """Encode every position of every sequence; kv is [B, T, C]."""
+    B, T, _ = kv.shape
+    parts = [encode_tokens(kv[bi], W1, W2, W3, range(T), k=k, g=g, b=b, s=s)
+             for bi in range(B)]
+    out = {}
+    for key in ("ref_idx", "z", "q", "scale", "zmin", "codes", "d_diag", "is_ref"):
+        out[key] = np.stack([p[key] for p in parts])
+    return out
+
+
+def gather(codes: np.ndarray, scale: np.ndarray, zmin: np.ndarray, idx: np.ndarray,
+           *, g: int, b: int, d_c: int) -> np.ndarray:
+    """Dequantise only the selected tokens, each from its own record
+    ([RKV] §2.4 last paragraph; §2.7 decode step 3).
+
+    codes/scale/zmin are flattened over [B*T]; idx are flat b*T+t indices.
+    An index outside [0, B*T) yields a NaN row.
+    """
+    idx = np.asarray(idx, dtype=np.int64)
+    total = codes.shape[0]
+    out = np.full((len(idx), d_c), np.nan, dtype=F32)
+    ok = (idx >= 0) & (idx < total)
+    if ok.any():
+        sel = idx[ok]
+        q = unpack_codes(codes[sel], b, d_c)
+        out[ok] = dequantize(q, scale[sel], zmin[sel], g)
+    return out

@@ -1,0 +1,365 @@
+"""Pins of the fp64 CPU oracle against what the ResidualKV notes and plain
+mathematics fix ([RKV] = the ResidualKV reading notes, arXiv 2602.08005v2,
+with the notes' own section numbers).
+
+Each test checks the oracle against something other than itself: brute force
+by another route, a closed-form identity, a special case with a known answer,
+a library routine, or a number the notes print.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import rkv_oracle as O
+from synth import CONFIGS, generate
+from synth.configs import LLAMA8K, MM_INT2, QWEN_LIKE, TINY
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    w = generate(TINY)
+    kv = w.kv_f32()[0].astype(np.float64)
+    W1, W2, W3 = (a.astype(np.float64) for a in w.weights_f32())
+    return w, kv, W1, W2, W3
+
+
+def _brute_topk(kv, t, s, k):
+    """Pure-Python brute force: every earlier reference, sorted on (d, j) tuples."""
+    x = [float(v) for v in kv[t]]
+    cands = []
+    for j in range(0, t, s):
+        y = kv[j]
+        d = 0.0
+        for a, bb in zip(x, y):
+            d += (a - float(bb)) ** 2
+        cands.append((d, j))
+    cands.sort()
+    return [j for _, j in cands[:min(k, len(cands))]]
+
+
+# ------------------------------------------------------------ selection
+def test_selection_matches_pure_python_brute_force(tiny):
+    w, kv, *_ = tiny
+    s, k = TINY.stride, TINY.k
+    for t in range(TINY.T):
+        if t % s == 0:
+            continue
+        R, _ = O.retrieve(kv, t, s, k)
+        assert sorted(R.tolist()) == sorted(_brute_topk(kv, t, s, k)), t
+
+
+@pytest.mark.parametrize("cfg", [LLAMA8K, QWEN_LIKE, MM_INT2], ids=lambda c: c.name)
+def test_selection_matches_sorted_brute_force_on_slices(cfg):
+    """Wide shapes: full distance list by broadcasting, Python sort on tuples."""
+    w = generate(cfg.with_(T=512, B=1, mm_blocks=1, mm_block_len=200))
+    kv = w.kv_f32()[0].astype(np.float64)
+    s, k = cfg.stride, cfg.k
+    rng = np.random.default_rng(1)
+    ts = [t for t in rng.choice(cfg.T if cfg.T <= 512 else 512, 60, replace=False) if t % s]
+    for t in ts:
+        refs = np.arange(0, t, s)
+        d = ((kv[refs] - kv[t]) ** 2).sum(axis=1)
+        want = [j for _, j in sorted(zip(d.tolist(), refs.tolist()))[:min(k, len(refs))]]
+        R, _ = O.retrieve(kv, int(t), s, k)
+        assert sorted(R.tolist()) == sorted(want)
+
+
+def test_topk_minimises_retrieval_radius(tiny):
+    """[RKV] §2.8: for a fixed pool and subset size, the k_i nearest
+    references minimise rho_i^2.  Checked by enumerating every subset."""
+    _, kv, *_ = tiny
+    s, k = TINY.stride, TINY.k
+    for t in [41, 77, 99, 130, 161, 189, 203, 222, 237, 255]:
+        pool = np.arange(0, t, s)
+        d = np.array([((kv[t] - kv[j]) ** 2).sum() for j in pool])
+        best = min(d[list(c)].mean() for c in itertools.combinations(range(len(pool)), k))
+        R, _ = O.retrieve(kv, t, s, k)
+        rho2 = np.mean([((kv[t] - kv[j]) ** 2).sum() for j in R])
+        assert rho2 == pytest.approx(best, rel=1e-12, abs=0)
+
+
+def test_warmup_neighbour_count():
+    """k_i = min(k, |T_ref,i|) ([RKV] §2.1); |T_ref,t| = ceil(t/s) with refs at t % s == 0."""
+    rng = np.random.default_rng(3)
+    for T, s, k in [(40, 8, 4), (37, 5, 3), (20, 3, 8), (9, 16, 4)]:
+        kv = rng.standard_normal((T, 12))
+        W1 = rng.standard_normal((12, 8)); W2 = rng.standard_normal((12, 8))
+        W3 = rng.standard_normal((8, 8))
+        out = O.encode_tokens(kv, W1, W2, W3, range(T), k=k, g=8, b=4, s=s)
+        for t in range(T):
+            n = int((out["ref_idx"][t] >= 0).sum())
+            want = 0 if t % s == 0 else min(k, math.ceil(t / s))
+            assert n == want, (T, s, k, t)
+            got = out["ref_idx"][t][:n]
+            assert np.all(got % s == 0) and np.all(got < t) and np.all(np.diff(got) > 0)
+
+
+# ------------------------------------------------------------ mean (Theorem IV.1)
+def test_theorem_iv1_decomposition(tiny):
+    """rho_i^2 = ||Delta_i||^2 + V_i exactly ([RKV] §2.8, Theorem IV.1).
+    A wrong mean (wrong divisor, wrong rows) breaks the identity."""
+    _, kv, *_ = tiny
+    s, k = TINY.stride, TINY.k
+    for t in range(1, TINY.T):
+        if t % s == 0:
+            continue
+        R, _ = O.retrieve(kv, t, s, k)
+        m = O.reference_mean(kv, R)
+        rho2 = np.mean([((kv[t] - kv[j]) ** 2).sum() for j in R])
+        delta2 = ((kv[t] - m) ** 2).sum()
+        V = np.mean([((kv[j] - m) ** 2).sum() for j in R])
+        assert rho2 == pytest.approx(delta2 + V, rel=1e-12)
+
+
+# ------------------------------------------------------------ compressor
+def test_fc_matches_torch_fp64(tiny):
+    _, kv, W1, W2, W3 = tiny
+    x = kv[:50]
+    want = (torch.nn.functional.silu(torch.from_numpy(x) @ torch.from_numpy(W1))
+            * (torch.from_numpy(x) @ torch.from_numpy(W2))) @ torch.from_numpy(W3)
+    np.testing.assert_allclose(O.f_c(x, W1, W2, W3), want.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_z_is_zero_when_token_equals_its_references():
+    rng = np.random.default_rng(5)
+    T, s, C = 64, 8, 16
+    kv = rng.standard_normal((T, C))
+    v = rng.standard_normal(C)
+    for j in (8, 16, 24, 32):
+        kv[j] = v
+    kv[45] = v
+    W1 = rng.standard_normal((C, 24)); W2 = rng.standard_normal((C, 24))
+    W3 = rng.standard_normal((24, 16))
+    out = O.encode_tokens(kv, W1, W2, W3, [45], k=4, g=8, b=4, s=s)
+    assert out["ref_idx"][0].tolist() == [8, 16, 24, 32]
+    assert np.all(out["z"][0] == 0.0)
+    assert np.all(out["codes"] == 0) and np.all(out["scale"] == 0) and np.all(out["zmin"] == 0)
+
+
+def test_subtraction_after_encoding_is_not_encoding_the_difference(tiny):
+    """[RKV] §2.3: f_c(kv) - f_c(mean) differs from f_c(kv - mean) (f_c is non-linear)."""
+    _, kv, W1, W2, W3 = tiny
+    s, k = TINY.stride, TINY.k
+    for t in [50, 100, 150, 200, 250]:
+        R, _ = O.retrieve(kv, t, s, k)
+        m = O.reference_mean(kv, R)
+        z = O.residual_latent(kv[t], m, W1, W2, W3)
+        wrong = O.f_c(kv[t] - m, W1, W2, W3)
+        assert np.linalg.norm(z - wrong) / np.linalg.norm(z) > 1e-2
+
+
+def test_zero_gate_weights_give_zero_latent(tiny):
+    _, kv, W1, W2, W3 = tiny
+    out = O.encode_tokens(kv, W1, np.zeros_like(W2), W3, range(30, 60), k=4, g=32, b=4, s=8)
+    assert np.all(out["z"] == 0.0)
+
+
+def test_encode_all_equals_per_token(tiny):
+    w, kv, W1, W2, W3 = tiny
+    full = O.encode(kv[None], W1, W2, W3, k=4, g=32, b=4, s=8)
+    some = O.encode_tokens(kv, W1, W2, W3, [3, 8, 9, 100, 255], k=4, g=32, b=4, s=8)
+    for i, t in enumerate([3, 8, 9, 100, 255]):
+        assert np.array_equal(full["ref_idx"][0, t], some["ref_idx"][i])
+        assert np.array_equal(full["codes"][0, t], some["codes"][i])
+        np.testing.assert_allclose(full["z"][0, t], some["z"][i], rtol=1e-12, atol=1e-14)
+
+
+# ------------------------------------------------------------ quantiser
+def _read_kv(path):
+    out = {}
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        key, *vals = line.split()
+        out[key] = vals
+    return out
+
+
+def test_quantiser_ramp_golden():
+    gd = _read_kv(os.path.join(GOLD, "quant_ramp_b4.txt"))
+    z = np.arange(32, dtype=np.float64)[None, :]
+    q, dh, mh = O.quantize(z, 32, 4)
+    assert float(dh[0, 0]) == float(gd["delta_h"][0])
+    assert float(mh[0, 0]) == float(gd["zmin_h"][0])
+    assert q[0].tolist() == [int(v) for v in gd["codes"]]
+    assert O.pack_codes(q, 4)[0].tolist() == [int(h, 16) for h in gd["packed_hex"]]
+    deq = O.dequantize(q, dh, mh, 32)[0]
+    assert deq.tolist() == [(i // 2) * 529 / 256 for i in range(32)]
+
+
+def test_packing_golden():
+    gd = _read_kv(os.path.join(GOLD, "packing.txt"))
+    for b in (4, 2):
+        q = np.array([[int(v) for v in gd[f"b{b}_codes"]]])
+        packed = O.pack_codes(q, b)[0].tolist()
+        assert packed == [int(h, 16) for h in gd[f"b{b}_hex"]]
+        assert O.unpack_codes(O.pack_codes(q, b), b, q.shape[1]).tolist() == q.tolist()
+
+
+@pytest.mark.parametrize("b", [2, 4])
+def test_quantiser_on_grid_values_are_exact(b):
+    """Values already on a grid m + q*Delta (Delta, m exact in fp16, both ends
+    present) must come back with those very codes and decode exactly."""
+    rng = np.random.default_rng(7)
+    L = 2 ** b - 1
+    for m, delta in [(-1.5, 0.25), (0.0, 1.0), (3.0, 0.0625), (-100.0, 8.0)]:
+        q = rng.integers(0, L + 1, size=(20, 32))
+        q[:, 0] = 0
+        q[:, 1] = L
+        z = m + q * delta
+        qq, dh, mh = O.quantize(z, 32, b)
+        assert np.array_equal(qq, q)
+        assert np.all(dh.astype(np.float64) == delta) and np.all(mh.astype(np.float64) == m)
+        assert np.array_equal(O.dequantize(qq, dh, mh, 32).astype(np.float64), z)
+
+
+def test_quantiser_rounds_half_to_even():
+    # group: 0 and 15 fix min = 0 and Delta = 1; midpoints k + 0.5 round to even
+    z = np.array([[0.0, 15.0, 0.5, 1.5, 2.5, 3.5, 12.5, 13.5]])
+    q, dh, mh = O.quantize(z, 8, 4)
+    assert q[0].tolist() == [0, 15, 0, 2, 2, 4, 12, 14]
+
+
+def test_constant_group_keeps_value_without_division():
+    """[RKV] §2.4: a constant group is kept as its value (no divide by zero)."""
+    z = np.zeros((3, 64))
+    z[0, :32] = 0.375          # exact in fp16
+    z[1, 32:] = -7.25          # exact in fp16
+    z[2, :32] = 0.1            # not exact in fp16: kept as fp16(0.1)
+    q, dh, mh = O.quantize(z, 32, 4)
+    assert np.all(q == 0) and np.all(dh == 0)
+    deq = O.dequantize(q, dh, mh, 32)
+    assert np.all(deq[0, :32] == 0.375) and np.all(deq[0, 32:] == 0.0)
+    assert np.all(deq[1, 32:] == -7.25)
+    assert np.all(deq[2, :32] == np.float32(np.float16(0.1)))
+    zero = O.encode_tokens(np.zeros((20, 8)), np.ones((8, 8)), np.ones((8, 8)),
+                           np.ones((8, 32)), range(20), k=4, g=32, b=4, s=4)
+    assert np.all(zero["codes"] == 0) and np.all(zero["scale"] == 0) and np.all(zero["zmin"] == 0)
+
+
+@pytest.mark.parametrize("b", [2, 4])
+def test_quantiser_error_bounds(b):
+    """Per coordinate |z~ - z| <= Delta_h/2 plus the slack of storing Delta and
+    z_min in fp16; and the norm bound of [RKV] §2.8 (Theorem IV.1, quantisation
+    part): ||e_q|| <= sqrt(sum |G| range^2) / (2(2^b-1)) <= sqrt(g/2)/(2^b-1) ||z||,
+    with the same fp16 slack added."""
+    rng = np.random.default_rng(11)
+    g, L = 32, 2 ** b - 1
+    z = np.concatenate([rng.standard_normal((200, 128)),
+                        0.01 * rng.standard_t(3, size=(200, 128)),
+                        rng.uniform(-50, 50, size=(200, 128))])
+    q, dh, mh = O.quantize(z, g, b)
+    assert q.min() >= 0 and q.max() <= L
+    deq = O.dequantize(q, dh, mh, g).astype(np.float64)
+    zf = z.astype(np.float32).astype(np.float64)
+    err_norm2 = np.zeros(len(z))
+    bound2 = np.zeros(len(z))
+    for gi, (a, e) in enumerate(O.group_bounds(128, g)):
+        zg = zf[:, a:e]
+        lo, hi = zg.min(1), zg.max(1)
+        delta = (hi - lo) / L
+        d16 = dh[:, gi].astype(np.float64)
+        m16 = mh[:, gi].astype(np.float64)
+        slack = np.abs(m16 - lo) + L * np.abs(d16 - delta) + 1e-6 * (np.abs(hi) + np.abs(lo))
+        per = d16 / 2 + slack
+        err = np.abs(deq[:, a:e] - zg)
+        assert np.all(err <= per[:, None]), gi
+        err_norm2 += (err ** 2).sum(1)
+        bound2 += (e - a) * ((hi - lo) / (2 * L) + slack) ** 2
+    assert np.all(np.sqrt(err_norm2) <= np.sqrt(bound2))
+    # second inequality (range^2 <= 2||z_G||^2), data side only
+    exact2 = sum((e - a) * (zf[:, a:e].max(1) - zf[:, a:e].min(1)) ** 2
+                 for a, e in O.group_bounds(128, g))
+    assert np.all(np.sqrt(exact2) / (2 * L) <= math.sqrt(g / 2) / L * np.linalg.norm(zf, axis=1) + 1e-12)
+
+
+def test_short_last_group():
+    z = np.arange(40, dtype=np.float64)[None, :]   # groups [0,32) and [32,40)
+    q, dh, mh = O.quantize(z, 32, 4)
+    assert dh.shape == (1, 2)
+    assert float(mh[0, 1]) == 32.0 and float(dh[0, 1]) == float(np.float16(np.float32(7) / np.float32(15)))
+
+
+# ------------------------------------------------------------ gather
+def test_gather_is_dequantise_of_selected_rows_and_nan_out_of_range():
+    rng = np.random.default_rng(13)
+    z = rng.standard_normal((10, 64))
+    q, dh, mh = O.quantize(z, 32, 4)
+    codes = O.pack_codes(q, 4)
+    idx = np.array([3, 0, 9, 3, -1, 10])
+    out = O.gather(codes, dh, mh, idx, g=32, b=4, d_c=64)
+    deq = O.dequantize(q, dh, mh, 32)
+    assert np.array_equal(out[0], deq[3]) and np.array_equal(out[1], deq[0])
+    assert np.array_equal(out[2], deq[9]) and np.array_equal(out[3], deq[3])
+    assert np.all(np.isnan(out[4])) and np.all(np.isnan(out[5]))
+    assert O.gather(codes, dh, mh, np.array([], dtype=np.int64), g=32, b=4, d_c=64).shape == (0, 64)
+
+
+# ------------------------------------------------------------ storage accounting
+def test_storage_accounting_matches_printed_numbers():
+    gd = json.load(open(os.path.join(GOLD, "storage_accounting.json")))
+    assert O.q_b(4) == gd["q4"] and O.q_b(2) == gd["q2"]
+    for key in ("kr_example", "kr_example_4_full_layers"):
+        e = gd[key]
+        kr = O.keep_ratio(e["beta"], e["rho_ref"], e["q_b"], e["dc_over_2dk"])
+        assert round(100 * kr, e["printed_decimals"]) == e["printed_percent"]
+    # one record per non-reference token: b-bit codes + two fp16 per group
+    for C, d_c, b in [(2048, 512, 4), (2048, 512, 2), (1024, 256, 4), (64, 32, 4)]:
+        assert O.storage_ratio_vs_fp16(C, d_c, 32, b) == pytest.approx(O.q_b(b) * d_c / C, rel=1e-15)
+
+
+# ------------------------------------------------------------ generators
+def test_generators_are_deterministic_and_shaped():
+    a = generate(TINY)
+    b = generate(TINY)
+    assert np.array_equal(a.kv, b.kv) and np.array_equal(a.w3, b.w3)
+    assert a.kv.shape == (1, 256, 64) and a.kv.dtype == np.float32
+    c = generate(LLAMA8K.with_(T=64))
+    assert c.kv.dtype == np.uint16 and c.kv.shape == (1, 64, 2048)
+    m = generate(MM_INT2.with_(B=2, T=4096))
+    for segs in m.segments:
+        assert segs[0][1] == 0 and segs[-1][2] == 4096
+        assert all(x[2] == y[1] for x, y in zip(segs, segs[1:]))
+    full = [s for s in generate(MM_INT2.with_(B=1)).segments[0] if s[0] == "image"]
+    assert len(full) == 24 and all(e - a_ == 576 for _, a_, e in full)
+
+
+def test_equal_distances_prefer_the_earlier_reference():
+    """Ties in distance are broken by the smaller position (a reading: the notes
+    leave ties open); copies of one vector at two reference slots must pick the
+    earlier slot first."""
+    rng = np.random.default_rng(17)
+    T, s, C = 80, 8, 16
+    kv = rng.standard_normal((T, C)) * 5
+    v = rng.standard_normal(C)
+    kv[40] = v
+    kv[16] = v
+    kv[64] = v
+    kv[71] = v + 1e-3
+    for k, want in [(1, [16]), (2, [16, 40]), (3, [16, 40, 64])]:
+        R, _ = O.retrieve(kv, 71, s, k)
+        assert R.tolist() == want
+
+
+def test_zero_references_reduce_z_to_library_compressor():
+    """With every reference equal to the zero vector the mean is 0 and
+    f_c(0) = 0 (no biases), so z must equal f_c(kv_t) computed by torch."""
+    rng = np.random.default_rng(19)
+    T, s, C = 48, 6, 16
+    kv = rng.standard_normal((T, C))
+    kv[::s] = 0.0
+    W1 = rng.standard_normal((C, 24)); W2 = rng.standard_normal((C, 24))
+    W3 = rng.standard_normal((24, 32))
+    ts = [t for t in range(T) if t % s]
+    out = O.encode_tokens(kv, W1, W2, W3, ts, k=4, g=32, b=4, s=s)
+    x = torch.from_numpy(kv[ts])
+    want = (torch.nn.functional.silu(x @ torch.from_numpy(W1)) * (x @ torch.from_numpy(W2))) @ torch.from_numpy(W3)
+    np.testing.assert_allclose(out["z"], want.numpy(), rtol=1e-12, atol=1e-13)
