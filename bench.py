@@ -1,0 +1,200 @@
+#!/usr/bin/env python3
+"""Benchmark of the ResidualKV cache-write path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+rkv_encode over B*T tokens (reference retrieval, reference mean, SwiGLU
+compressor residual, group quantiser) followed by rkv_dequant_gather of the
+workload's selected token subset.  Inputs are resident in HBM before the
+timed region starts.  Prints one JSON line.
+
+Workload (default): Llama-3.1-8B single-layer shape, B=1, T=32768, N=8, D=128
+(C = 2048), d_ff=1024, d_c=512, k=4, reference stride 16, INT4, g=32; gather
+of 30 % of the positions.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 matrix peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def stage_work(cfg, n_gather: int):
+    """Algorithmic work of one launch of each stage: (kind, amount).
+
+    MFMA stages count 2 flops per multiply-add of the contraction the method
+    needs (the bf16 hi/lo split of the W3 input is not counted); HBM-bound
+    stages count the bytes they must move."""
+    B, T, C, s = cfg.B, cfg.T, cfg.C, cfg.stride
+    nref = -(-T // s)
+    nr = T - nref
+    pairs = sum(-(-t // s) for t in range(T) if t % s) * B        # causal (token, reference) pairs
+    esz = 2 if cfg.dtype == "bf16" else 4
+    rec = cfg.d_c * cfg.b // 8 + 4 * (cfg.d_c // cfg.g)
+    return {
+        "pack": ("bytes", 2 * (2 * C * cfg.d_ff + cfg.d_ff * cfg.d_c) * esz),
+        "norms": ("bytes", B * nref * C * esz),
+        "dist": ("flops", 2.0 * C * pairs),
+        "merge": ("bytes", B * T * cfg.k * 4),
+        "proj": ("flops", 2.0 * C * 2 * cfg.d_ff * B * nref),
+        "swiglu": ("flops", 2.0 * C * 2 * cfg.d_ff * B * nr),
+        "w3": ("flops", 2.0 * cfg.d_ff * cfg.d_c * B * nr),
+        "quant": ("bytes", B * nr * cfg.d_c * 4 + B * T * rec),
+        "gather": ("bytes", n_gather * (rec + cfg.d_c * 2)),
+    }
+
+
+def cpu_baseline(w, n_tokens: int, seed: int = 0):
+    """The CPU oracle, as it stands, on a bounded sample of the workload."""
+    import numpy as np
+    from oracle import rkv_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    cfg = w.cfg
+    rng = np.random.default_rng(seed)
+    kv = w.kv_f32()[0].astype(np.float64)
+    W1, W2, W3 = (x.astype(np.float64) for x in w.weights_f32())
+    nonref = np.array([t for t in range(cfg.T) if t % cfg.stride], dtype=np.int64)
+    pos = np.sort(rng.choice(nonref, size=n_tokens, replace=False))
+    t0 = time.perf_counter()
+    O.encode_tokens(kv, W1, W2, W3, pos, k=cfg.k, g=cfg.g, b=cfg.b, s=cfg.stride)
+    dt = time.perf_counter() - t0
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_tokens} random non-reference tokens of sequence 0 of {cfg.name}, "
+                      f"each encoded on its own (retrieval over its causal pool, mean, two f_c, "
+                      f"quantiser), numpy fp64; {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama8b_T32k")
+    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the encode shards by sequence / token range, see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import reference_residual_encoding_amd as R
+    from reference_residual_encoding_amd import buffers as RB
+    from synth import config_by_name, generate
+
+    cfg = config_by_name(args.workload)
+    print(f"[bench] generating {cfg.name}", file=sys.stderr, flush=True)
+    w = generate(cfg)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(a):
+        if cfg.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    p = R.params(B=cfg.B, T=cfg.T, N=cfg.N, D=cfg.D, d_ff=cfg.d_ff, d_c=cfg.d_c, k=cfg.k,
+                 g=cfg.g, b=cfg.b, ref_stride=cfg.stride, dtype=cfg.dtype)
+    kv, w1, w2, w3 = (to_dev(x) for x in (w.kv, w.w1, w.w2, w.w3))
+    out = RB.alloc_encode(p, dev, with_z=False)
+    idx = torch.from_numpy(w.gather_idx.astype(np.int32)).to(dev)
+    gdst = torch.empty((idx.numel(), cfg.d_c), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        RB.encode(p, kv, w1, w2, w3, out, stream)
+        RB.dequant_gather(p, out, idx, "bf16", stream, dst=gdst)
+
+    # warm-up, with every stage bracketed by events to find the dominant one
+    R.rkv_profile_begin((1 << len(R.STAGES)) - 1)
+    for _ in range(max(args.warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+    stages_ms = {}
+    for i, name in enumerate(R.STAGES):
+        tot, n = R.rkv_profile_read(i)
+        if n:
+            stages_ms[name] = tot / n
+    dominant = max(stages_ms, key=stages_ms.get)
+    dom_i = R.STAGES.index(dominant)
+    print(f"[bench] warm-up stage ms: { {k: round(v, 4) for k, v in stages_ms.items()} }",
+          file=sys.stderr, flush=True)
+
+    # timed region: only the dominant stage keeps its event pair
+    R.rkv_profile_begin(1 << dom_i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    dom_total, dom_n = R.rkv_profile_read(dom_i)
+    R.rkv_profile_begin(0)
+    dom_ms = dom_total / dom_n
+
+    work = stage_work(cfg, idx.numel())
+    kind, amount = work[dominant]
+    if kind == "flops":
+        peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+        achieved = amount / (dom_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None, "kernel": dominant,
+                "kernel_ms": round(dom_ms, 4), "work_per_launch": amount}
+    else:
+        achieved = amount / (dom_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                "kernel": dominant, "kernel_ms": round(dom_ms, 4), "work_per_launch": amount}
+
+    mfma_flops = sum(work[s][1] for s in ("dist", "proj", "swiglu", "w3"))
+    encode_ms = sum(v for k, v in stages_ms.items() if k != "gather")
+    tokens = cfg.B * cfg.T
+    line = {
+        "metric": "KV tokens encoded/sec (Llama-3.1-8B layer shape, T=32k); % bf16 MFMA peak",
+        "value": round(tokens / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "N": cfg.N, "D": cfg.D,
+                   "C": cfg.C, "d_ff": cfg.d_ff, "d_c": cfg.d_c, "k": cfg.k, "g": cfg.g,
+                   "b": cfg.b, "ref_stride": cfg.stride, "gather_rows": int(idx.numel())},
+        "pct_bf16_mfma_peak": round(100.0 * mfma_flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "encode_mfma_tflops_algorithmic": round(mfma_flops / 1e12, 4),
+        "stages_ms_warmup": {k: round(v, 4) for k, v in stages_ms.items()},
+        "encode_ms_warmup": round(encode_ms, 4),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        print(f"[bench] cpu baseline on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,166 @@
+/*
+ * rkv.h - C ABI of librkv, the ResidualKV cache-write path for AMD MI355X
+ * (gfx950).
+ *
+ * Source of the method: the ResidualKV reading notes, "ResidualKV：基于参考向量
+ * 与残差的 KV Cache 压缩" (notes on arXiv 2602.08005v2), cited as [RKV] with the
+ * notes' own section numbers.  Argument names follow the notes' symbol table
+ * ([RKV] §2.1): B sequences of T tokens, N KV heads of dimension D, joint
+ * vector width C = 2*d_k = 2*N*D, compressor width d_ff, latent width d_c,
+ * k neighbours, quantiser group g and bit width b ([RKV] §2.4), reference
+ * stride s ([RKV] §2.6).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer argument is a DEVICE pointer owned by the caller (HBM of
+ *    the device that is current on the calling thread), 16-byte aligned.
+ *    The library never allocates, frees or synchronises; all work is
+ *    enqueued on `stream` and the call returns before it finishes.  Results
+ *    are valid once the stream is synchronised.  Two calls may run
+ *    concurrently on different streams if each has its own workspace.
+ *  - Every argument check runs on the host before anything is enqueued.  On
+ *    failure nothing is enqueued, the status is returned and
+ *    rkv_last_error() describes it (thread-local text).  A launch failure
+ *    reported by the HIP runtime returns RKV_ERR_DEVICE; a fault inside a
+ *    kernel surfaces at the caller's next synchronisation.
+ *  - Results are bitwise deterministic: no atomics decide any value.
+ *  - Token layout: kv[b][t][c] with c in [0, C): the N key heads (pre-RoPE)
+ *    then the N value heads, D coordinates each ([RKV] §2.1: K and V of all
+ *    heads flattened into one joint vector).
+ *  - Reference schedule: position t of a sequence is a reference iff
+ *    t % s == 0 ([RKV] §2.6, fixed stride).  The candidate pool of a
+ *    non-reference token t holds the references at positions j < t of the
+ *    same sequence; k_t = min(k, ceil(t / s)) ([RKV] §2.1).
+ */
+#ifndef RKV_H
+#define RKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RKV_ABI_VERSION 1
+
+typedef enum {
+  RKV_OK = 0,
+  RKV_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size or field     */
+  RKV_ERR_UNSUPPORTED = 2, /* valid for the method, not for this GPU path     */
+  RKV_ERR_WORKSPACE = 3,   /* workspace smaller than *_workspace_bytes()      */
+  RKV_ERR_DEVICE = 4       /* the HIP runtime reported an error               */
+} rkv_status;
+
+typedef enum { RKV_F32 = 0, RKV_BF16 = 1 } rkv_dtype;
+
+typedef struct {
+  int32_t B, T;       /* sequences; tokens per sequence                        */
+  int32_t N, D;       /* KV heads; head dimension.  C = 2*N*D                  */
+  int32_t d_ff, d_c;  /* compressor width; latent width                        */
+  int32_t k;          /* neighbours per token, 1..8 ([RKV] §2.2 uses 4)        */
+  int32_t g, b;       /* quantiser group size (8,16,32,64); bits (2 or 4)      */
+  int32_t ref_stride; /* s >= 1                                                */
+  rkv_dtype dtype;    /* element type of kv, w1, w2, w3                        */
+} rkv_params;
+
+/* GPU-path limits (RKV_ERR_UNSUPPORTED otherwise): C % 64 == 0,
+ * d_ff % 32 == 0, d_c % 32 == 0, d_c % g == 0, B*T < 2^31. */
+
+/* Bytes of device workspace rkv_encode / rkv_select need for *p (0 if *p is
+ * invalid).  The workspace holds repacked weights, reference projections,
+ * partial neighbour lists, the SwiGLU difference and the latent; its
+ * contents are private and need not be initialised. */
+size_t rkv_encode_workspace_bytes(const rkv_params* p);
+
+/* Encode a whole prefix of B sequences into the ResidualKV cache format.
+ *
+ * For every non-reference token t ([RKV] §2.2-§2.4):
+ *   R_t   = the k_t references nearest to kv_t in squared L2 over all C
+ *           coordinates (ties: smaller position first)   [RKV] §2.2 eq. 1
+ *   m_t   = mean of kv_j over j in R_t                   [RKV] §2.2 eq. 2
+ *   f_c(x)= (Swish(x W1) * (x W2)) W3, Swish = SiLU      [RKV] §2.3
+ *   z_t   = f_c(kv_t) - f_c(m_t)                         [RKV] §2.3 boxed eq.
+ *   per group of g consecutive latent coordinates: Delta = (max-min)/(2^b-1),
+ *   Delta_h = fp16(Delta), m_h = fp16(min),
+ *   q = clamp(rint((z - m_h)/Delta_h), 0, 2^b-1), q = 0 when Delta_h == 0
+ *                                                        [RKV] §2.4
+ * Reference tokens are stored as they are by the caller ([RKV] §2.4): their
+ * ref_idx row is all -1 and their record (codes, scale, zmin, z) is zero.
+ *
+ * Inputs:  kv [B][T][C]; w1, w2 [C][d_ff]; w3 [d_ff][d_c]; row-major, the
+ *          element type p->dtype; used as x*W (row vector times matrix).
+ * Outputs: ref_idx [B][T][k] int32: chosen reference positions within the
+ *                  sequence, ascending; -1 pads when k_t < k.
+ *          codes   [B][T][d_c*b/8]: packed little-endian inside a byte
+ *                  (coordinate (8/b)*j + r in bits [r*b, (r+1)*b) of byte j).
+ *          scale   [B][T][d_c/g]: fp16 bits of Delta_h.
+ *          zmin    [B][T][d_c/g]: fp16 bits of m_h.
+ *          z       optional [B][T][d_c] float latent (NULL: not written).
+ * workspace: at least rkv_encode_workspace_bytes(p) bytes of device memory.
+ * Arithmetic: bf16 inputs are multiplied exactly and accumulated in fp32 on
+ * the matrix cores; the quantiser works in fp32. */
+rkv_status rkv_encode(const rkv_params* p, const void* kv, const void* w1,
+                      const void* w2, const void* w3, int32_t* ref_idx,
+                      uint8_t* codes, uint16_t* scale, uint16_t* zmin,
+                      float* z, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/* Selective dequantisation: out[i][:] = q * Delta_h + m_h (one fp32 FMA per
+ * coordinate) for the record of flat token idx[i] = b*T + t
+ * ([RKV] §2.4 third eq.; §2.7 decode step 3: only selected tokens are
+ * decompressed, each from its own record).  Indices may repeat and come in
+ * any order; an index outside [0, B*T) yields a row of NaN.  Reference
+ * tokens decode to zeros.
+ * out: [n_idx][d_c], float (RKV_F32) or bf16 rounded to nearest even
+ * (RKV_BF16).  n_idx == 0 is a no-op.  Only p->B, T, d_c, g, b are read. */
+rkv_status rkv_dequant_gather(const rkv_params* p, const uint8_t* codes,
+                              const uint16_t* scale, const uint16_t* zmin,
+                              const int32_t* idx, int32_t n_idx, void* out,
+                              rkv_dtype out_dtype, hipStream_t stream);
+
+/* Stepwise export of the quantiser ([RKV] §2.4) alone: quantise `rows`
+ * latent rows z [rows][d_c] (float) into codes/scale/zmin laid out as in
+ * rkv_encode.  Only p->d_c, g, b are read. */
+rkv_status rkv_quantize(const rkv_params* p, const float* z, int64_t rows,
+                        uint8_t* codes, uint16_t* scale, uint16_t* zmin,
+                        hipStream_t stream);
+
+/* Stepwise export of retrieval ([RKV] §2.2 eq. 1) alone: writes ref_idx as
+ * rkv_encode does.  Needs the same workspace size as rkv_encode. */
+rkv_status rkv_select(const rkv_params* p, const void* kv, int32_t* ref_idx,
+                      void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/* Observability.  Stages of the encode path, in launch order, plus the
+ * gather.  rkv_profile_begin(mask) makes later rkv_encode /
+ * rkv_dequant_gather calls on this process record a HIP event pair around
+ * every stage whose bit (1u << stage) is set in mask, and clears previous
+ * records; mask 0 turns recording off (the default).  rkv_profile_read()
+ * waits for the recorded events of one stage and returns the summed
+ * duration in milliseconds and the number of launches.  Meant for
+ * single-threaded measurement; events are created on first use and kept. */
+typedef enum {
+  RKV_STAGE_PACK = 0,    /* weight repacking                               */
+  RKV_STAGE_NORMS = 1,   /* reference squared norms                        */
+  RKV_STAGE_DIST = 2,    /* distance contraction + per-chunk top-k          */
+  RKV_STAGE_MERGE = 3,   /* top-k merge, ref_idx                            */
+  RKV_STAGE_PROJ = 4,    /* reference projection R [W1|W2]                  */
+  RKV_STAGE_SWIGLU = 5,  /* token projection + SwiGLU difference            */
+  RKV_STAGE_W3 = 6,      /* latent z = delta_h W3                           */
+  RKV_STAGE_QUANT = 7,   /* group quantiser                                 */
+  RKV_STAGE_GATHER = 8,  /* gather-dequantise                               */
+  RKV_STAGE_COUNT = 9
+} rkv_stage;
+rkv_status rkv_profile_begin(uint32_t stage_mask);
+rkv_status rkv_profile_read(int32_t stage, double* total_ms, int64_t* launches);
+
+const char* rkv_status_str(rkv_status s);
+const char* rkv_last_error(void); /* detail of this thread's last failure */
+int rkv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RKV_H */

@@ -1,0 +1,188 @@
+"""Python binding of librkv, the ResidualKV cache-write path for MI355X.
+
+Argument marshalling only: every function forwards to the C entry point of
+the same name in ``librkv.so`` (declared in ``include/rkv.h``).  Tensors are
+passed as device pointers (``tensor.data_ptr()``) and streams as raw HIP
+stream handles; PyTorch is used by callers for device memory and streams.
+
+There is no fallback: if the compiled library is missing, every call raises.
+Build it with ``python -m reference_residual_encoding_amd._build`` or
+``__graft_entry__.build()``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librkv.so")
+
+RKV_OK = 0
+RKV_ERR_INVALID_ARG = 1
+RKV_ERR_UNSUPPORTED = 2
+RKV_ERR_WORKSPACE = 3
+RKV_ERR_DEVICE = 4
+
+RKV_F32 = 0
+RKV_BF16 = 1
+
+# Exported symbols of librkv.so (must match include/rkv.h).
+EXPORTS = (
+    "rkv_encode_workspace_bytes",
+    "rkv_encode",
+    "rkv_dequant_gather",
+    "rkv_quantize",
+    "rkv_select",
+    "rkv_status_str",
+    "rkv_last_error",
+    "rkv_abi_version",
+    "rkv_profile_begin",
+    "rkv_profile_read",
+)
+
+STAGES = ("pack", "norms", "dist", "merge", "proj", "swiglu", "w3", "quant", "gather")
+
+
+class rkv_params(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("B", "T", "N", "D", "d_ff", "d_c", "k", "g", "b", "ref_stride")] + \
+               [("dtype", ctypes.c_int32)]
+
+
+class RkvError(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str):
+        super().__init__(f"{fn}: {status_name(status)}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load librkv.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"librkv.so not built at {LIB_PATH}; run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(rkv_params)
+        vp, sz, i32, i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
+        L.rkv_encode_workspace_bytes.argtypes = [P]
+        L.rkv_encode_workspace_bytes.restype = sz
+        L.rkv_encode.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.rkv_encode.restype = ctypes.c_int
+        L.rkv_dequant_gather.argtypes = [P, vp, vp, vp, vp, i32, vp, ctypes.c_int, vp]
+        L.rkv_dequant_gather.restype = ctypes.c_int
+        L.rkv_quantize.argtypes = [P, vp, i64, vp, vp, vp, vp]
+        L.rkv_quantize.restype = ctypes.c_int
+        L.rkv_select.argtypes = [P, vp, vp, vp, sz, vp]
+        L.rkv_select.restype = ctypes.c_int
+        L.rkv_status_str.argtypes = [ctypes.c_int]
+        L.rkv_status_str.restype = ctypes.c_char_p
+        L.rkv_last_error.argtypes = []
+        L.rkv_last_error.restype = ctypes.c_char_p
+        L.rkv_abi_version.argtypes = []
+        L.rkv_abi_version.restype = ctypes.c_int
+        L.rkv_profile_begin.argtypes = [ctypes.c_uint32]
+        L.rkv_profile_begin.restype = ctypes.c_int
+        L.rkv_profile_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double),
+                                       ctypes.POINTER(ctypes.c_int64)]
+        L.rkv_profile_read.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_name(status: int) -> str:
+    return lib().rkv_status_str(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> int:
+    if status != RKV_OK:
+        raise RkvError(fn, status, lib().rkv_last_error().decode())
+    return status
+
+
+def params(*, B, T, N, D, d_ff, d_c, k, g, b, ref_stride, dtype) -> rkv_params:
+    """Build an rkv_params; dtype is RKV_F32/RKV_BF16 or "f32"/"bf16"."""
+    if isinstance(dtype, str):
+        dtype = {"f32": RKV_F32, "bf16": RKV_BF16}[dtype]
+    return rkv_params(B, T, N, D, d_ff, d_c, k, g, b, ref_stride, dtype)
+
+
+def _p(x) -> Optional[int]:
+    """Device pointer of a tensor (or an int / None)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _s(stream) -> Optional[int]:
+    if stream is None:
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# -- entry points, same names as the C ABI ---------------------------------
+def rkv_abi_version() -> int:
+    return lib().rkv_abi_version()
+
+
+def rkv_last_error() -> str:
+    return lib().rkv_last_error().decode()
+
+
+def rkv_status_str(status: int) -> str:
+    return status_name(status)
+
+
+def rkv_encode_workspace_bytes(p: rkv_params) -> int:
+    return int(lib().rkv_encode_workspace_bytes(ctypes.byref(p)))
+
+
+def rkv_encode(p: rkv_params, kv, w1, w2, w3, ref_idx, codes, scale, zmin, z, workspace,
+               workspace_bytes: int, stream=None, *, check: bool = True) -> int:
+    st = lib().rkv_encode(ctypes.byref(p), _p(kv), _p(w1), _p(w2), _p(w3), _p(ref_idx),
+                          _p(codes), _p(scale), _p(zmin), _p(z), _p(workspace),
+                          int(workspace_bytes), _s(stream))
+    return _check("rkv_encode", st) if check else st
+
+
+def rkv_dequant_gather(p: rkv_params, codes, scale, zmin, idx, n_idx: int, out, out_dtype,
+                       stream=None, *, check: bool = True) -> int:
+    if isinstance(out_dtype, str):
+        out_dtype = {"f32": RKV_F32, "bf16": RKV_BF16}[out_dtype]
+    st = lib().rkv_dequant_gather(ctypes.byref(p), _p(codes), _p(scale), _p(zmin), _p(idx),
+                                  int(n_idx), _p(out), int(out_dtype), _s(stream))
+    return _check("rkv_dequant_gather", st) if check else st
+
+
+def rkv_quantize(p: rkv_params, z, rows: int, codes, scale, zmin, stream=None, *,
+                 check: bool = True) -> int:
+    st = lib().rkv_quantize(ctypes.byref(p), _p(z), int(rows), _p(codes), _p(scale), _p(zmin),
+                            _s(stream))
+    return _check("rkv_quantize", st) if check else st
+
+
+def rkv_select(p: rkv_params, kv, ref_idx, workspace, workspace_bytes: int, stream=None, *,
+               check: bool = True) -> int:
+    st = lib().rkv_select(ctypes.byref(p), _p(kv), _p(ref_idx), _p(workspace),
+                          int(workspace_bytes), _s(stream))
+    return _check("rkv_select", st) if check else st
+
+
+def rkv_profile_begin(stage_mask: int) -> int:
+    return _check("rkv_profile_begin", lib().rkv_profile_begin(int(stage_mask)))
+
+
+def rkv_profile_read(stage: int):
+    """Returns (total_ms, launches) of one stage since rkv_profile_begin."""
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    _check("rkv_profile_read", lib().rkv_profile_read(int(stage), ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value

@@ -1,0 +1,268 @@
+// librkv C ABI: argument validation, workspace planning, kernel dispatch.
+// The operations themselves are documented in include/rkv.h.
+#include "rkv.h"
+
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "rkv_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+rkv_status fail(rkv_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+rkv_status ok() {
+  g_last_error.clear();
+  return RKV_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define RKV_NEED_PTR(ptr)                                                              \
+  do {                                                                                 \
+    if ((ptr) == nullptr) return fail(RKV_ERR_INVALID_ARG, "%s is NULL", #ptr);        \
+    if (!aligned16(ptr)) return fail(RKV_ERR_INVALID_ARG, "%s is not 16-byte aligned", #ptr); \
+  } while (0)
+
+// Fields read by the quantiser and the gather.
+rkv_status check_record(const rkv_params* p) {
+  if (p->d_c <= 0) return fail(RKV_ERR_INVALID_ARG, "d_c must be positive (got %d)", p->d_c);
+  if (p->b != 2 && p->b != 4) return fail(RKV_ERR_INVALID_ARG, "b must be 2 or 4 (got %d)", p->b);
+  if (p->g <= 0) return fail(RKV_ERR_INVALID_ARG, "g must be positive (got %d)", p->g);
+  if (p->g != 8 && p->g != 16 && p->g != 32 && p->g != 64)
+    return fail(RKV_ERR_UNSUPPORTED, "g must be 8, 16, 32 or 64 on the GPU path (got %d)", p->g);
+  if (p->d_c % 32 != 0)
+    return fail(RKV_ERR_UNSUPPORTED, "d_c must be a multiple of 32 (got %d)", p->d_c);
+  if (p->d_c % p->g != 0)
+    return fail(RKV_ERR_UNSUPPORTED, "g must divide d_c (g=%d, d_c=%d)", p->g, p->d_c);
+  return RKV_OK;
+}
+
+rkv_status check_params(const rkv_params* p) {
+  if (p == nullptr) return fail(RKV_ERR_INVALID_ARG, "params is NULL");
+  if (p->B <= 0 || p->T <= 0) return fail(RKV_ERR_INVALID_ARG, "B and T must be positive (B=%d, T=%d)", p->B, p->T);
+  if (p->N <= 0 || p->D <= 0) return fail(RKV_ERR_INVALID_ARG, "N and D must be positive (N=%d, D=%d)", p->N, p->D);
+  if (p->d_ff <= 0) return fail(RKV_ERR_INVALID_ARG, "d_ff must be positive (got %d)", p->d_ff);
+  if (p->k <= 0) return fail(RKV_ERR_INVALID_ARG, "k must be positive (got %d)", p->k);
+  if (p->ref_stride <= 0) return fail(RKV_ERR_INVALID_ARG, "ref_stride must be positive (got %d)", p->ref_stride);
+  if (p->dtype != RKV_F32 && p->dtype != RKV_BF16) return fail(RKV_ERR_INVALID_ARG, "unknown dtype %d", int(p->dtype));
+  rkv_status st = check_record(p);
+  if (st != RKV_OK) return st;
+  if (p->k > 8) return fail(RKV_ERR_UNSUPPORTED, "k must be at most 8 on the GPU path (got %d)", p->k);
+  const long long C = 2LL * p->N * p->D;
+  if (C > (1LL << 20)) return fail(RKV_ERR_UNSUPPORTED, "C = 2*N*D too large (%lld)", C);
+  if (C % 64 != 0) return fail(RKV_ERR_UNSUPPORTED, "C = 2*N*D must be a multiple of 64 (got %lld)", C);
+  if (p->d_ff % 32 != 0) return fail(RKV_ERR_UNSUPPORTED, "d_ff must be a multiple of 32 (got %d)", p->d_ff);
+  if ((long long)p->B * p->T >= (1LL << 31)) return fail(RKV_ERR_UNSUPPORTED, "B*T must be below 2^31");
+  if ((long long)p->B * p->T * C >= (1LL << 40)) return fail(RKV_ERR_UNSUPPORTED, "B*T*C too large");
+  return RKV_OK;
+}
+
+rkv::Shape shape_of(const rkv_params* p) {
+  return rkv::make_shape(p->B, p->T, p->N, p->D, p->d_ff, p->d_c, p->k, p->g, p->b, p->ref_stride,
+                         p->dtype == RKV_BF16);
+}
+
+rkv_status device_status(hipError_t e, const char* where) {
+  if (e != hipSuccess) return fail(RKV_ERR_DEVICE, "%s: %s", where, hipGetErrorString(e));
+  return ok();
+}
+
+// Stage profiling: HIP event pairs recorded around selected stages.
+struct Profiler {
+  std::mutex mu;
+  uint32_t mask = 0;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[RKV_STAGE_COUNT];
+  size_t used[RKV_STAGE_COUNT] = {};
+};
+Profiler g_prof;
+
+struct StageScope {
+  hipEvent_t end = nullptr;
+  hipStream_t st;
+  StageScope(int stage, hipStream_t s) : st(s) {
+    if (!(g_prof.mask & (1u << stage))) return;
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    auto& v = g_prof.ev[stage];
+    size_t& n = g_prof.used[stage];
+    if (n == v.size()) {
+      hipEvent_t a, b;
+      if (hipEventCreate(&a) != hipSuccess) return;
+      if (hipEventCreate(&b) != hipSuccess) { (void)hipEventDestroy(a); return; }
+      v.emplace_back(a, b);
+    }
+    if (hipEventRecord(v[n].first, st) != hipSuccess) return;
+    end = v[n].second;
+    ++n;
+  }
+  ~StageScope() {
+    if (end) (void)hipEventRecord(end, st);
+  }
+};
+
+}  // namespace
+
+extern "C" {
+
+rkv_status rkv_profile_begin(uint32_t stage_mask) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  g_prof.mask = stage_mask & ((1u << RKV_STAGE_COUNT) - 1);
+  for (auto& u : g_prof.used) u = 0;
+  return ok();
+}
+
+rkv_status rkv_profile_read(int32_t stage, double* total_ms, int64_t* launches) {
+  if (stage < 0 || stage >= RKV_STAGE_COUNT) return fail(RKV_ERR_INVALID_ARG, "bad stage %d", stage);
+  if (!total_ms || !launches) return fail(RKV_ERR_INVALID_ARG, "output pointer is NULL");
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  double sum = 0.0;
+  for (size_t i = 0; i < g_prof.used[stage]; ++i) {
+    auto& pr = g_prof.ev[stage][i];
+    hipError_t e = hipEventSynchronize(pr.second);
+    if (e != hipSuccess) return device_status(e, "profile");
+    float ms = 0.0f;
+    e = hipEventElapsedTime(&ms, pr.first, pr.second);
+    if (e != hipSuccess) return device_status(e, "profile");
+    sum += ms;
+  }
+  *total_ms = sum;
+  *launches = int64_t(g_prof.used[stage]);
+  return ok();
+}
+
+int rkv_abi_version(void) { return RKV_ABI_VERSION; }
+
+const char* rkv_status_str(rkv_status s) {
+  switch (s) {
+    case RKV_OK: return "RKV_OK";
+    case RKV_ERR_INVALID_ARG: return "RKV_ERR_INVALID_ARG";
+    case RKV_ERR_UNSUPPORTED: return "RKV_ERR_UNSUPPORTED";
+    case RKV_ERR_WORKSPACE: return "RKV_ERR_WORKSPACE";
+    case RKV_ERR_DEVICE: return "RKV_ERR_DEVICE";
+  }
+  return "RKV_ERR_UNKNOWN";
+}
+
+const char* rkv_last_error(void) { return g_last_error.c_str(); }
+
+size_t rkv_encode_workspace_bytes(const rkv_params* p) {
+  if (check_params(p) != RKV_OK) return 0;
+  return rkv::plan_workspace(shape_of(p)).total;
+}
+
+rkv_status rkv_encode(const rkv_params* p, const void* kv, const void* w1, const void* w2,
+                      const void* w3, int32_t* ref_idx, uint8_t* codes, uint16_t* scale,
+                      uint16_t* zmin, float* z, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  rkv_status st = check_params(p);
+  if (st != RKV_OK) return st;
+  RKV_NEED_PTR(kv);
+  RKV_NEED_PTR(w1);
+  RKV_NEED_PTR(w2);
+  RKV_NEED_PTR(w3);
+  RKV_NEED_PTR(ref_idx);
+  RKV_NEED_PTR(codes);
+  RKV_NEED_PTR(scale);
+  RKV_NEED_PTR(zmin);
+  RKV_NEED_PTR(workspace);
+  if (z != nullptr && !aligned16(z)) return fail(RKV_ERR_INVALID_ARG, "z is not 16-byte aligned");
+  const rkv::Shape sh = shape_of(p);
+  const rkv::Workspace L = rkv::plan_workspace(sh);
+  if (workspace_bytes < L.total)
+    return fail(RKV_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
+  char* ws = static_cast<char*>(workspace);
+  hipError_t e;
+#define RKV_STAGE(stage, call, name)                          \
+  do {                                                        \
+    StageScope scope_(stage, stream);                         \
+    if ((e = (call)) != hipSuccess) return device_status(e, name); \
+  } while (0)
+  RKV_STAGE(RKV_STAGE_PACK, rkv::launch_pack_weights(sh, w1, w2, w3, ws, L, stream), "pack");
+  RKV_STAGE(RKV_STAGE_NORMS, rkv::launch_ref_norms(sh, kv, ws, L, stream), "norms");
+  RKV_STAGE(RKV_STAGE_DIST, rkv::launch_dist(sh, kv, ws, L, stream), "dist");
+  RKV_STAGE(RKV_STAGE_MERGE, rkv::launch_merge(sh, ref_idx, ws, L, stream), "merge");
+  if (sh.nr > 0) {
+    RKV_STAGE(RKV_STAGE_PROJ, rkv::launch_ref_proj(sh, kv, ws, L, stream), "proj");
+    RKV_STAGE(RKV_STAGE_SWIGLU, rkv::launch_swiglu(sh, kv, ref_idx, ws, L, stream), "swiglu");
+    RKV_STAGE(RKV_STAGE_W3, rkv::launch_w3(sh, ws, L, stream), "w3");
+  }
+  RKV_STAGE(RKV_STAGE_QUANT,
+            rkv::launch_quantize(reinterpret_cast<const float*>(ws + L.zc), int64_t(sh.B) * sh.T,
+                                 sh.T, sh.s, sh.d_c, sh.g, sh.b, codes, scale, zmin, z, stream),
+            "quantize");
+  return ok();
+}
+
+rkv_status rkv_select(const rkv_params* p, const void* kv, int32_t* ref_idx, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  rkv_status st = check_params(p);
+  if (st != RKV_OK) return st;
+  RKV_NEED_PTR(kv);
+  RKV_NEED_PTR(ref_idx);
+  RKV_NEED_PTR(workspace);
+  const rkv::Shape sh = shape_of(p);
+  const rkv::Workspace L = rkv::plan_workspace(sh);
+  if (workspace_bytes < L.total)
+    return fail(RKV_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
+  char* ws = static_cast<char*>(workspace);
+  hipError_t e;
+  RKV_STAGE(RKV_STAGE_NORMS, rkv::launch_ref_norms(sh, kv, ws, L, stream), "norms");
+  RKV_STAGE(RKV_STAGE_DIST, rkv::launch_dist(sh, kv, ws, L, stream), "dist");
+  RKV_STAGE(RKV_STAGE_MERGE, rkv::launch_merge(sh, ref_idx, ws, L, stream), "merge");
+  return ok();
+}
+
+rkv_status rkv_quantize(const rkv_params* p, const float* z, int64_t rows, uint8_t* codes,
+                        uint16_t* scale, uint16_t* zmin, hipStream_t stream) {
+  if (p == nullptr) return fail(RKV_ERR_INVALID_ARG, "params is NULL");
+  rkv_status st = check_record(p);
+  if (st != RKV_OK) return st;
+  if (rows < 0) return fail(RKV_ERR_INVALID_ARG, "rows must be non-negative (got %lld)", (long long)rows);
+  if (rows * (long long)p->d_c >= (1LL << 40)) return fail(RKV_ERR_UNSUPPORTED, "rows*d_c too large");
+  if (rows == 0) return ok();
+  RKV_NEED_PTR(z);
+  RKV_NEED_PTR(codes);
+  RKV_NEED_PTR(scale);
+  RKV_NEED_PTR(zmin);
+  hipError_t e = rkv::launch_quantize(z, rows, 0, 0, p->d_c, p->g, p->b, codes, scale, zmin,
+                                      nullptr, stream);
+  return device_status(e, "quantize");
+}
+
+rkv_status rkv_dequant_gather(const rkv_params* p, const uint8_t* codes, const uint16_t* scale,
+                              const uint16_t* zmin, const int32_t* idx, int32_t n_idx, void* out,
+                              rkv_dtype out_dtype, hipStream_t stream) {
+  if (p == nullptr) return fail(RKV_ERR_INVALID_ARG, "params is NULL");
+  rkv_status st = check_record(p);
+  if (st != RKV_OK) return st;
+  if (p->B <= 0 || p->T <= 0) return fail(RKV_ERR_INVALID_ARG, "B and T must be positive (B=%d, T=%d)", p->B, p->T);
+  if (n_idx < 0) return fail(RKV_ERR_INVALID_ARG, "n_idx must be non-negative (got %d)", n_idx);
+  if (out_dtype != RKV_F32 && out_dtype != RKV_BF16) return fail(RKV_ERR_INVALID_ARG, "unknown out_dtype %d", int(out_dtype));
+  if (n_idx == 0) return ok();
+  RKV_NEED_PTR(codes);
+  RKV_NEED_PTR(scale);
+  RKV_NEED_PTR(zmin);
+  RKV_NEED_PTR(idx);
+  RKV_NEED_PTR(out);
+  hipError_t e;
+  RKV_STAGE(RKV_STAGE_GATHER,
+            rkv::launch_gather(codes, scale, zmin, idx, n_idx, int64_t(p->B) * p->T, p->d_c, p->g,
+                               p->b, out, out_dtype == RKV_BF16, stream),
+            "gather");
+  return ok();
+}
+
+}  // extern "C"

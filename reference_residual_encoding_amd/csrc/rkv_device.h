@@ -1,0 +1,63 @@
+// Device-side helpers shared by the librkv kernels (gfx950 / CDNA4).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rkv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native, splits into VGPRs
+
+// bfloat16 <-> float.  Inputs are finite; NaN keeps a NaN payload.
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(uint32_t(h) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  return uint16_t((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// IEEE half (round to nearest even) <-> float.
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
+// Row of element r (0..15) of a 32x32 fp32 MFMA accumulator held by `lane`;
+// its column is lane % 32.
+__device__ __forceinline__ int mfma32_row(int r, int lane) {
+  return (r & 3) + 8 * (r >> 2) + 4 * (lane >> 5);
+}
+
+// Position of the q-th non-reference token of a sequence whose references
+// sit at multiples of s (s >= 2): s-1 non-references follow each reference.
+__device__ __forceinline__ int nonref_pos(int q, int s) {
+  const int sm1 = s - 1;
+  return (q / sm1) * s + (q % sm1) + 1;
+}
+
+__device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
+
+// Keep the KL smallest (d, j) pairs in ascending (d, j) order.
+template <int KL>
+__device__ __forceinline__ void topk_insert(float (&bd)[KL], int (&bi)[KL], float d, int j) {
+  if (d < bd[KL - 1] || (d == bd[KL - 1] && j < bi[KL - 1])) {
+    bd[KL - 1] = d;
+    bi[KL - 1] = j;
+#pragma unroll
+    for (int i = KL - 1; i > 0; --i) {
+      const bool sw = bd[i] < bd[i - 1] || (bd[i] == bd[i - 1] && bi[i] < bi[i - 1]);
+      const float td = sw ? bd[i - 1] : bd[i];
+      const int ti = sw ? bi[i - 1] : bi[i];
+      bd[i - 1] = sw ? bd[i] : bd[i - 1];
+      bi[i - 1] = sw ? bi[i] : bi[i - 1];
+      bd[i] = td;
+      bi[i] = ti;
+    }
+  }
+}
+
+}  // namespace rkv

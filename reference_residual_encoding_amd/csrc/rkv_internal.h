@@ -1,0 +1,55 @@
+// Host-side interface between the ABI layer (rkv_api.cpp) and the kernel
+// launchers (rkv_kernels.hip).  Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rkv {
+
+// Derived sizes of one encode problem.
+struct Shape {
+  int B, T, C, d_ff, d_c, k, g, b, s;
+  bool bf16;
+  int esize;     // bytes per kv / weight element
+  int nref;      // references per sequence, ceil(T/s)
+  int nr;        // non-references per sequence, T - nref
+  int kl;        // neighbour-list length kept per chunk (4 or 8, >= k)
+  int n_chunks;  // reference chunks per sequence in the distance kernel
+  int k3;        // contraction length of the W3 product (2*d_ff bf16 hi/lo, d_ff fp32)
+};
+
+// Byte offsets of the workspace regions (each 256-byte aligned).
+struct Workspace {
+  size_t wp, w3p, ysq, proj, part, dh, zc, total;
+};
+
+Shape make_shape(int B, int T, int N, int D, int d_ff, int d_c, int k, int g, int b, int s,
+                 bool bf16);
+Workspace plan_workspace(const Shape& sh);
+
+// Each launcher enqueues on `st` and returns hipGetLastError().
+hipError_t launch_pack_weights(const Shape& sh, const void* w1, const void* w2, const void* w3,
+                               char* ws, const Workspace& L, hipStream_t st);
+hipError_t launch_ref_norms(const Shape& sh, const void* kv, char* ws, const Workspace& L,
+                            hipStream_t st);
+hipError_t launch_dist(const Shape& sh, const void* kv, char* ws, const Workspace& L,
+                       hipStream_t st);
+hipError_t launch_merge(const Shape& sh, int32_t* ref_idx, char* ws, const Workspace& L,
+                        hipStream_t st);
+hipError_t launch_ref_proj(const Shape& sh, const void* kv, char* ws, const Workspace& L,
+                           hipStream_t st);
+hipError_t launch_swiglu(const Shape& sh, const void* kv, const int32_t* ref_idx, char* ws,
+                         const Workspace& L, hipStream_t st);
+hipError_t launch_w3(const Shape& sh, char* ws, const Workspace& L, hipStream_t st);
+// Quantise rows of z.  With s >= 1 rows are the B*T tokens of an encode and
+// z is the compact non-reference latent (reference rows write zeros); with
+// s == 0 rows map one to one onto z.  zout (optional) receives the latent.
+hipError_t launch_quantize(const float* z, int64_t rows, int T, int s, int d_c, int g, int b,
+                           uint8_t* codes, uint16_t* scale, uint16_t* zmin, float* zout,
+                           hipStream_t st);
+hipError_t launch_gather(const uint8_t* codes, const uint16_t* scale, const uint16_t* zmin,
+                         const int32_t* idx, int64_t n_idx, int64_t total_rows, int d_c, int g,
+                         int b, void* out, bool out_bf16, hipStream_t st);
+
+}  // namespace rkv

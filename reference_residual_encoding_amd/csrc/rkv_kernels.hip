@@ -1,0 +1,719 @@
+// HIP kernels of the ResidualKV cache-write path for gfx950 (MI355X).
+//
+// Method: the ResidualKV reading notes, "ResidualKV：基于参考向量与残差的 KV Cache
+// 压缩" (notes on arXiv 2602.08005v2), cited as [RKV] with the notes' own
+// section numbers.
+//
+// Encode pipeline (one stream, in this order):
+//   pack      W1|W2 -> Wp [2 d_ff][C] (columns of W1 and W2 interleaved in
+//             blocks of 32 so one lane holds x*W1 and x*W2 of the same
+//             column), W3 -> W3p [d_c][k3] (K-contiguous rows).
+//   norms     ||kv_j||^2 of every reference.
+//   dist      distance contraction token x reference on the matrix cores,
+//             fused with a running top-KL per token and reference chunk
+//             ([RKV] §2.2 retrieval equation).  Distances are ranked as
+//             ||kv_j||^2 - 2 kv_t . kv_j, which orders references exactly
+//             as ||kv_t - kv_j||^2 does (the dropped ||kv_t||^2 is the same
+//             for every candidate of token t).
+//   merge     per token: merge chunk lists, keep k_t = min(k, |pool|),
+//             write ref_idx sorted by position.
+//   proj      P = R [W1|W2] for the reference rows, fp32.
+//   swiglu    U = kv_t [W1|W2] for non-reference tokens; epilogue forms the
+//             mean branch from P (m_t [W1|W2] = mean_j kv_j [W1|W2] because
+//             the first layer is linear and bias-free, [RKV] §2.3) and writes
+//             delta_h = Swish(u1)*u2 - Swish(mean u1)*mean u2.
+//   w3        z = delta_h W3: since W3 is linear, f_c(kv) - f_c(m) equals
+//             (h(kv) - h(m)) W3 ([RKV] §2.3).  bf16 runs feed delta_h as a
+//             hi + lo pair of bf16 (K = 2 d_ff) so the product keeps ~16
+//             mantissa bits of delta_h.
+//   quantize  per-token group min-max quantiser ([RKV] §2.4).
+// The read side is one kernel: gather-dequantise over an index list.
+#include "rkv_device.h"
+#include "rkv_gemm.h"
+#include "rkv_internal.h"
+
+#include <algorithm>
+
+namespace rkv {
+
+namespace {
+
+constexpr int kGemmBM = 128, kGemmBN = 128;   // proj / swiglu / w3 tiles
+constexpr int kDistRefs = 128;                // references per chunk (tile M)
+constexpr int kDistTok = 128;                 // tokens per tile (tile N)
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+inline int cdiv(long a, long b) { return int((a + b - 1) / b); }
+
+// ------------------------------------------------------------------ packing
+// dst[map(c) * ld + r (+ dup)] = src[r * cols + c]; map: 0 identity,
+// 1 W1 slot 64*(c/32) + c%32, 2 W2 slot 64*(c/32) + 32 + c%32.
+template <typename E>
+__global__ __launch_bounds__(256) void k_transpose_pack(const E* __restrict__ src, int rows,
+                                                        int cols, E* __restrict__ dst, int ld,
+                                                        int mode, int dup) {
+  __shared__ E tile[32][33];
+  const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  for (int i = ty; i < 32; i += 8) {
+    const int r = r0 + i, c = c0 + tx;
+    if (r < rows && c < cols) tile[i][tx] = src[size_t(r) * cols + c];
+  }
+  __syncthreads();
+  for (int i = ty; i < 32; i += 8) {
+    const int c = c0 + i, r = r0 + tx;
+    if (c < cols && r < rows) {
+      const int n = mode == 0 ? c : 64 * (c >> 5) + (mode == 2 ? 32 : 0) + (c & 31);
+      const E v = tile[tx][i];
+      dst[size_t(n) * ld + r] = v;
+      if (dup) dst[size_t(n) * ld + dup + r] = v;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ norms
+template <typename E>
+__global__ __launch_bounds__(256) void k_ref_norms(const char* __restrict__ kv, int B, int T,
+                                                   int C, int s, int nref,
+                                                   float* __restrict__ ysq) {
+  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (wid >= B * nref) return;
+  const int b = wid / nref, j = wid % nref;
+  const E* row = reinterpret_cast<const E*>(kv + (size_t(b) * T + size_t(j) * s) * C * sizeof(E));
+  float acc = 0.0f;
+  for (int c = lane * 8; c < C; c += 512) {
+    if constexpr (sizeof(E) == 2) {
+      const uint4 w = *reinterpret_cast<const uint4*>(row + c);
+      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = __uint_as_float(u[e] << 16), hi = __uint_as_float(u[e] & 0xFFFF0000u);
+        acc = fmaf(lo, lo, acc);
+        acc = fmaf(hi, hi, acc);
+      }
+    } else {
+      const float4 a = *reinterpret_cast<const float4*>(row + c);
+      const float4 d = *reinterpret_cast<const float4*>(row + c + 4);
+      acc = fmaf(a.x, a.x, acc); acc = fmaf(a.y, a.y, acc);
+      acc = fmaf(a.z, a.z, acc); acc = fmaf(a.w, a.w, acc);
+      acc = fmaf(d.x, d.x, acc); acc = fmaf(d.y, d.y, acc);
+      acc = fmaf(d.z, d.z, acc); acc = fmaf(d.w, d.w, acc);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (lane == 0) ysq[wid] = acc;
+}
+
+// ------------------------------------------------------------------ retrieval
+// One workgroup: kDistRefs references (chunk c) x kDistTok non-reference
+// tokens (tile tt) of sequence b.  Writes, per token, the KL best (d', j) of
+// the chunk restricted to the causal pool (j*s < position).
+template <typename E, int KL>
+__global__ __launch_bounds__(256) void k_dist_topk(const char* __restrict__ kv,
+                                                   const float* __restrict__ ysq,
+                                                   float2* __restrict__ part, int B, int T,
+                                                   int C, int s, int nref, int nr,
+                                                   int n_chunks, int n_tt) {
+  constexpr int BM = kDistRefs, BN = kDistTok;
+  using TL = Tile<E, BM, BN>;
+  __shared__ __attribute__((aligned(16))) char lds[TL::kLds];
+  const int item = blockIdx.x;
+  const int c = item % n_chunks;
+  const int rest = item / n_chunks;
+  const int tt = rest % n_tt, b = rest / n_tt;
+  const int n0 = tt * BN;
+  const int plast = nonref_pos(min(n0 + BN, nr) - 1, s);
+  const int npool_max = (plast + s - 1) / s;
+  const int m0 = c * BM;
+  if (m0 >= npool_max) return;  // chunk entirely after every token of the tile
+
+  const size_t rowb = size_t(C) * sizeof(E);
+  const char* base = kv + size_t(b) * T * rowb;
+  const int tid = threadIdx.x, srow = tid >> 3, scol = (tid & 7) * 16;
+  const char* pa[TL::kLdA];
+  const char* pb[TL::kLdB];
+#pragma unroll
+  for (int i = 0; i < TL::kLdA; ++i) {
+    const int j = min(m0 + srow + 32 * i, nref - 1);
+    pa[i] = base + size_t(j) * s * rowb + scol;
+  }
+#pragma unroll
+  for (int i = 0; i < TL::kLdB; ++i) {
+    const int q = min(n0 + srow + 32 * i, nr - 1);
+    pb[i] = base + size_t(nonref_pos(q, s)) * rowb + scol;
+  }
+  f32x16 acc[TL::kTM][TL::kTN];
+  gemm_mainloop<E, BM, BN>(pa, pb, int(rowb / TL::kStage), lds, acc);
+
+  const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  float* ld_d = reinterpret_cast<float*>(lds);              // [BN][4][KL]
+  int* ld_i = reinterpret_cast<int*>(lds + BN * 4 * KL * 4);  // [BN][4][KL]
+  const float* yb = ysq + size_t(b) * nref;
+#pragma unroll
+  for (int tn = 0; tn < TL::kTN; ++tn) {
+    const int tl = wn * TL::kWN + tn * 32 + (lane & 31);
+    const int q = n0 + tl;
+    const bool qv = q < nr;
+    const int pq = qv ? nonref_pos(q, s) : 0;
+    float bd[KL];
+    int bi[KL];
+#pragma unroll
+    for (int i = 0; i < KL; ++i) { bd[i] = __builtin_inff(); bi[i] = 0x7fffffff; }
+#pragma unroll
+    for (int tm = 0; tm < TL::kTM; ++tm)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = m0 + wm * TL::kWM + tm * 32 + mfma32_row(r, lane);
+        const bool v = qv && j < nref && j * s < pq;
+        const float d = yb[min(j, nref - 1)] - 2.0f * acc[tm][tn][r];
+        if (v) topk_insert<KL>(bd, bi, d, j);
+      }
+    const int src = wm * 2 + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < KL; ++i) {
+      ld_d[(tl * 4 + src) * KL + i] = bd[i];
+      ld_i[(tl * 4 + src) * KL + i] = bi[i];
+    }
+  }
+  __syncthreads();
+  if (tid < BN) {
+    const int q = n0 + tid;
+    if (q < nr) {
+      float bd[KL];
+      int bi[KL];
+#pragma unroll
+      for (int i = 0; i < KL; ++i) { bd[i] = __builtin_inff(); bi[i] = 0x7fffffff; }
+      for (int src = 0; src < 4; ++src)
+#pragma unroll
+        for (int i = 0; i < KL; ++i)
+          topk_insert<KL>(bd, bi, ld_d[(tid * 4 + src) * KL + i], ld_i[(tid * 4 + src) * KL + i]);
+      float2* out = part + ((size_t(b) * n_chunks + c) * nr + q) * KL;
+#pragma unroll
+      for (int i = 0; i < KL; ++i) out[i] = make_float2(bd[i], __int_as_float(bi[i]));
+    }
+  }
+}
+
+// Per token: merge the chunk lists, keep k_t = min(k, ceil(t/s)) references
+// ([RKV] §2.1), write their positions in ascending order, -1 pads.
+template <int KL>
+__global__ __launch_bounds__(256) void k_topk_merge(const float2* __restrict__ part,
+                                                    int32_t* __restrict__ ref_idx, int B, int T,
+                                                    int s, int k, int nr, int n_chunks) {
+  const long gid = long(blockIdx.x) * 256 + threadIdx.x;
+  if (gid >= long(B) * T) return;
+  const int b = int(gid / T), t = int(gid % T);
+  int32_t* out = ref_idx + gid * k;
+  if (t % s == 0) {
+    for (int i = 0; i < k; ++i) out[i] = -1;
+    return;
+  }
+  const int q = t - t / s - 1;
+  const int npool = (t + s - 1) / s;
+  const int kt = min(k, npool);
+  const int nch = (npool + kDistRefs - 1) / kDistRefs;
+  float bd[KL];
+  int bi[KL];
+#pragma unroll
+  for (int i = 0; i < KL; ++i) { bd[i] = __builtin_inff(); bi[i] = 0x7fffffff; }
+  for (int c = 0; c < nch; ++c) {
+    const float2* p = part + ((size_t(b) * n_chunks + c) * nr + q) * KL;
+#pragma unroll
+    for (int i = 0; i < KL; ++i) {
+      const float2 v = p[i];
+      topk_insert<KL>(bd, bi, v.x, __float_as_int(v.y));
+    }
+  }
+  int sel[KL];
+#pragma unroll
+  for (int i = 0; i < KL; ++i) sel[i] = i < kt ? bi[i] : 0x7fffffff;
+#pragma unroll
+  for (int i = 1; i < KL; ++i)
+#pragma unroll
+    for (int j = i; j > 0; --j) {
+      const int a = sel[j - 1], c2 = sel[j];
+      sel[j - 1] = min(a, c2);
+      sel[j] = max(a, c2);
+    }
+  for (int i = 0; i < k; ++i) {
+    int v = -1;
+#pragma unroll
+    for (int j = 0; j < KL; ++j)
+      if (j == i && i < kt) v = sel[j] * s;
+    out[i] = v;
+  }
+}
+
+// ------------------------------------------------------------------ reference projection
+template <typename E>
+__global__ __launch_bounds__(256) void k_ref_proj(const char* __restrict__ kv,
+                                                  const char* __restrict__ wp,
+                                                  float* __restrict__ proj, int T, int C, int s,
+                                                  int nref, int M, int N, int tiles_n) {
+  constexpr int BM = kGemmBM, BN = kGemmBN;
+  using TL = Tile<E, BM, BN>;
+  __shared__ __attribute__((aligned(16))) char lds[TL::kLds];
+  const int nt = blockIdx.x % tiles_n, mt = blockIdx.x / tiles_n;
+  const int m0 = mt * BM, n0 = nt * BN;
+  const size_t rowb = size_t(C) * sizeof(E);
+  const int tid = threadIdx.x, srow = tid >> 3, scol = (tid & 7) * 16;
+  const char* pa[TL::kLdA];
+  const char* pb[TL::kLdB];
+#pragma unroll
+  for (int i = 0; i < TL::kLdA; ++i) {
+    const int r = min(m0 + srow + 32 * i, M - 1);
+    const int b = r / nref, j = r % nref;
+    pa[i] = kv + (size_t(b) * T + size_t(j) * s) * rowb + scol;
+  }
+#pragma unroll
+  for (int i = 0; i < TL::kLdB; ++i) {
+    const int n = min(n0 + srow + 32 * i, N - 1);
+    pb[i] = wp + size_t(n) * rowb + scol;
+  }
+  f32x16 acc[TL::kTM][TL::kTN];
+  gemm_mainloop<E, BM, BN>(pa, pb, int(rowb / TL::kStage), lds, acc);
+  const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int tm = 0; tm < TL::kTM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < TL::kTN; ++tn) {
+      const int col = n0 + wn * TL::kWN + tn * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * TL::kWM + tm * 32 + mfma32_row(r, lane);
+        if (row < M && col < N) proj[size_t(row) * N + col] = acc[tm][tn][r];
+      }
+    }
+}
+
+// ------------------------------------------------------------------ SwiGLU difference
+// Rows: compact non-reference tokens Q = b*nr + q.  Columns: Wp order, pairs
+// of 32-column blocks (W1 block, W2 block) of the same d_ff columns.
+template <typename E, int KL>
+__global__ __launch_bounds__(256) void k_swiglu(const char* __restrict__ kv,
+                                                const char* __restrict__ wp,
+                                                const float* __restrict__ proj,
+                                                const int32_t* __restrict__ ref_idx,
+                                                char* __restrict__ dh, int T, int C, int s,
+                                                int nref, int nr, int k, int d_ff, int M,
+                                                int tiles_n) {
+  constexpr int BM = kGemmBM, BN = kGemmBN;
+  using TL = Tile<E, BM, BN>;
+  __shared__ __attribute__((aligned(16))) char lds[TL::kLds];
+  const int N = 2 * d_ff;
+  const int nt = blockIdx.x % tiles_n, mt = blockIdx.x / tiles_n;
+  const int m0 = mt * BM, n0 = nt * BN;
+  const size_t rowb = size_t(C) * sizeof(E);
+  const int tid = threadIdx.x, srow = tid >> 3, scol = (tid & 7) * 16;
+  const char* pa[TL::kLdA];
+  const char* pb[TL::kLdB];
+#pragma unroll
+  for (int i = 0; i < TL::kLdA; ++i) {
+    const int Q = min(m0 + srow + 32 * i, M - 1);
+    const int b = Q / nr, q = Q % nr;
+    pa[i] = kv + (size_t(b) * T + nonref_pos(q, s)) * rowb + scol;
+  }
+#pragma unroll
+  for (int i = 0; i < TL::kLdB; ++i) {
+    const int n = min(n0 + srow + 32 * i, N - 1);
+    pb[i] = wp + size_t(n) * rowb + scol;
+  }
+  f32x16 acc[TL::kTM][TL::kTN];
+  gemm_mainloop<E, BM, BN>(pa, pb, int(rowb / TL::kStage), lds, acc);
+
+  // Epilogue, row by row: one wave per token row, one lane per d_ff column
+  // of the tile (BN/2 of them), reading U back from LDS.
+  constexpr int LD = BN + 8;
+  static_assert(BN / 2 == 64, "one lane per d_ff column of the tile");
+  static_assert(BM * LD * 4 <= TL::kLds, "U tile must fit in the main-loop LDS");
+  float* u = reinterpret_cast<float*>(lds);
+  acc_to_lds<BM, BN>(acc, u, LD);
+  __syncthreads();
+  const int lane = tid & 63, wave = tid >> 6;
+  const int c = lane;                                  // tile-local d_ff column
+  const int uc1 = 64 * (c >> 5) + (c & 31);            // its x*W1 column in U
+  const int n1 = n0 + uc1, n2 = n1 + 32;
+  const int col = n0 / 2 + c;                          // global d_ff column
+  for (int rr = wave; rr < BM; rr += 4) {
+    const int Q = m0 + rr;
+    if (Q >= M || n1 >= N) break;
+    const int b = Q / nr, q = Q % nr;
+    const int32_t* ri = ref_idx + (size_t(b) * T + nonref_pos(q, s)) * k;
+    // ref_idx rows hold the k_t chosen positions first, then -1 pads.
+    float s1 = 0.0f, s2 = 0.0f;
+    int kt = 0;
+#pragma unroll
+    for (int i = 0; i < KL; ++i) {
+      const int pos = i < k ? ri[i] : -1;
+      if (pos >= 0) {
+        const size_t prow = size_t(b) * nref + pos / s;
+        s1 += proj[prow * N + n1];
+        s2 += proj[prow * N + n2];
+        ++kt;
+      }
+    }
+    const float fk = float(kt);
+    const float u1 = u[rr * LD + uc1], u2 = u[rr * LD + uc1 + 32];
+    const float delta = silu(u1) * u2 - silu(s1 / fk) * (s2 / fk);
+    if constexpr (sizeof(E) == 2) {
+      uint16_t* o = reinterpret_cast<uint16_t*>(dh) + size_t(Q) * 2 * d_ff;
+      const uint16_t hi = f32_to_bf16_rne(delta);
+      o[col] = hi;
+      o[d_ff + col] = f32_to_bf16_rne(delta - bf16_to_f32(hi));
+    } else {
+      reinterpret_cast<float*>(dh)[size_t(Q) * d_ff + col] = delta;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ W3
+template <typename E>
+__global__ __launch_bounds__(256) void k_w3(const char* __restrict__ dh,
+                                            const char* __restrict__ w3p,
+                                            float* __restrict__ zc, int K, int M, int N,
+                                            int tiles_n) {
+  constexpr int BM = kGemmBM, BN = kGemmBN;
+  using TL = Tile<E, BM, BN>;
+  __shared__ __attribute__((aligned(16))) char lds[TL::kLds];
+  const int nt = blockIdx.x % tiles_n, mt = blockIdx.x / tiles_n;
+  const int m0 = mt * BM, n0 = nt * BN;
+  const size_t rowb = size_t(K) * sizeof(E);
+  const int tid = threadIdx.x, srow = tid >> 3, scol = (tid & 7) * 16;
+  const char* pa[TL::kLdA];
+  const char* pb[TL::kLdB];
+#pragma unroll
+  for (int i = 0; i < TL::kLdA; ++i) pa[i] = dh + size_t(min(m0 + srow + 32 * i, M - 1)) * rowb + scol;
+#pragma unroll
+  for (int i = 0; i < TL::kLdB; ++i) pb[i] = w3p + size_t(min(n0 + srow + 32 * i, N - 1)) * rowb + scol;
+  f32x16 acc[TL::kTM][TL::kTN];
+  gemm_mainloop<E, BM, BN>(pa, pb, int(rowb / TL::kStage), lds, acc);
+  const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int tm = 0; tm < TL::kTM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < TL::kTN; ++tn) {
+      const int col = n0 + wn * TL::kWN + tn * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * TL::kWM + tm * 32 + mfma32_row(r, lane);
+        if (row < M && col < N) zc[size_t(row) * N + col] = acc[tm][tn][r];
+      }
+    }
+}
+
+// ------------------------------------------------------------------ quantiser
+// Lane-to-lane exchange inside groups of G8 lanes (8 latent values per lane).
+__device__ __forceinline__ float dpp_xor1(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_xor2(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float swz_xor4(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x101F));
+}
+template <int G8>
+__device__ __forceinline__ void group_minmax(float& mn, float& mx) {
+  if constexpr (G8 >= 2) { mn = fminf(mn, dpp_xor1(mn)); mx = fmaxf(mx, dpp_xor1(mx)); }
+  if constexpr (G8 >= 4) { mn = fminf(mn, dpp_xor2(mn)); mx = fmaxf(mx, dpp_xor2(mx)); }
+  if constexpr (G8 >= 8) { mn = fminf(mn, swz_xor4(mn)); mx = fmaxf(mx, swz_xor4(mx)); }
+}
+
+// One wave covers 512 consecutive latent values (whole groups, since g
+// divides 512); every lane owns 8 consecutive values of one group.
+template <int BITS, int G8>
+__global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ z, int64_t rows,
+                                                  int T, int s, int nr, int d_c,
+                                                  uint8_t* __restrict__ codes,
+                                                  uint16_t* __restrict__ scale,
+                                                  uint16_t* __restrict__ zmin,
+                                                  float* __restrict__ zout) {
+  constexpr float kLevels = float((1 << BITS) - 1);
+  const int lane = threadIdx.x & 63;
+  const int64_t units = rows * (d_c / 8);
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t base = int64_t(blockIdx.x) * blockDim.x + (threadIdx.x & ~63); base < units;
+       base += stride) {
+    const int64_t u = base + lane;
+    const bool act = u < units;
+    const int64_t f = act ? u * 8 : 0;
+    const int64_t R = f / d_c;
+    const int o = int(f - R * d_c);
+    bool have = act;
+    int64_t srow = R;
+    if (s >= 1) {  // encode layout: reference rows (t % s == 0) store zeros
+      const int t = int(R % T);
+      have = have && (t % s) != 0;
+      srow = (R / T) * nr + (t - t / s - 1);
+    }
+    float v[8];
+    if (have) {
+      const float4 a = *reinterpret_cast<const float4*>(z + srow * d_c + o);
+      const float4 c = *reinterpret_cast<const float4*>(z + srow * d_c + o + 4);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = c.x; v[5] = c.y; v[6] = c.z; v[7] = c.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+    }
+    float mn = v[0], mx = v[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) { mn = fminf(mn, v[e]); mx = fmaxf(mx, v[e]); }
+    group_minmax<G8>(mn, mx);
+    const float delta = (mx - mn) / kLevels;
+    const uint16_t dh_bits = f32_to_f16_bits(delta);
+    const uint16_t mh_bits = f32_to_f16_bits(mn);
+    const float dh = f16_bits_to_f32(dh_bits), mh = f16_bits_to_f32(mh_bits);
+    uint32_t word = 0;
+    if (dh != 0.0f) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float t = rintf((v[e] - mh) / dh);
+        const uint32_t qv = uint32_t(fminf(fmaxf(t, 0.0f), kLevels));
+        word |= qv << (BITS * e);
+      }
+    }
+    if (act) {
+      if constexpr (BITS == 4) {
+        *reinterpret_cast<uint32_t*>(codes + u * 4) = word;
+      } else {
+        *reinterpret_cast<uint16_t*>(codes + u * 2) = uint16_t(word);
+      }
+      if ((lane % G8) == 0) {
+        const int64_t grp = u / G8;
+        scale[grp] = dh_bits;
+        zmin[grp] = mh_bits;
+      }
+      if (zout) {
+        *reinterpret_cast<float4*>(zout + f) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4*>(zout + f + 4) = make_float4(v[4], v[5], v[6], v[7]);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ gather-dequantise
+template <int BITS, bool BF16>
+__global__ __launch_bounds__(256) void k_gather(const uint8_t* __restrict__ codes,
+                                                const uint16_t* __restrict__ scale,
+                                                const uint16_t* __restrict__ zmin,
+                                                const int32_t* __restrict__ idx, int64_t n_idx,
+                                                int64_t total_rows, int d_c, int g,
+                                                void* __restrict__ out) {
+  constexpr uint32_t kMask = (1u << BITS) - 1;
+  const int64_t units = n_idx * (d_c / 8);
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t u = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; u < units; u += stride) {
+    const int64_t f = u * 8;
+    const int64_t i = f / d_c;
+    const int o = int(f - i * d_c);
+    const int64_t src = idx[i];
+    float v[8];
+    if (src < 0 || src >= total_rows) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = __builtin_nanf("");
+    } else {
+      uint32_t word;
+      if constexpr (BITS == 4)
+        word = *reinterpret_cast<const uint32_t*>(codes + src * (d_c / 2) + o / 2);
+      else
+        word = *reinterpret_cast<const uint16_t*>(codes + src * (d_c / 4) + o / 4);
+      const int64_t grp = src * (d_c / g) + o / g;
+      const float dh = f16_bits_to_f32(scale[grp]), mh = f16_bits_to_f32(zmin[grp]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = fmaf(float((word >> (BITS * e)) & kMask), dh, mh);
+    }
+    if constexpr (BF16) {
+      uint16_t* o16 = reinterpret_cast<uint16_t*>(out) + f;
+      uint4 w;
+      w.x = uint32_t(f32_to_bf16_rne(v[0])) | (uint32_t(f32_to_bf16_rne(v[1])) << 16);
+      w.y = uint32_t(f32_to_bf16_rne(v[2])) | (uint32_t(f32_to_bf16_rne(v[3])) << 16);
+      w.z = uint32_t(f32_to_bf16_rne(v[4])) | (uint32_t(f32_to_bf16_rne(v[5])) << 16);
+      w.w = uint32_t(f32_to_bf16_rne(v[6])) | (uint32_t(f32_to_bf16_rne(v[7])) << 16);
+      *reinterpret_cast<uint4*>(o16) = w;
+    } else {
+      float* o32 = reinterpret_cast<float*>(out) + f;
+      *reinterpret_cast<float4*>(o32) = make_float4(v[0], v[1], v[2], v[3]);
+      *reinterpret_cast<float4*>(o32 + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    }
+  }
+}
+
+int grid_for(int64_t work_items, int per_block) {
+  const int64_t g = (work_items + per_block - 1) / per_block;
+  return int(std::min<int64_t>(std::max<int64_t>(g, 1), 256 * 64));
+}
+
+}  // namespace
+
+// ==================================================================== host
+Shape make_shape(int B, int T, int N, int D, int d_ff, int d_c, int k, int g, int b, int s,
+                 bool bf16) {
+  Shape sh{};
+  sh.B = B; sh.T = T; sh.C = 2 * N * D; sh.d_ff = d_ff; sh.d_c = d_c; sh.k = k;
+  sh.g = g; sh.b = b; sh.s = s; sh.bf16 = bf16;
+  sh.esize = bf16 ? 2 : 4;
+  sh.nref = (T + s - 1) / s;
+  sh.nr = T - sh.nref;
+  sh.kl = k <= 4 ? 4 : 8;
+  sh.n_chunks = cdiv(sh.nref, kDistRefs);
+  sh.k3 = bf16 ? 2 * d_ff : d_ff;
+  return sh;
+}
+
+Workspace plan_workspace(const Shape& sh) {
+  Workspace L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off += align256(bytes); return at; };
+  L.wp = take(size_t(2) * sh.d_ff * sh.C * sh.esize);
+  L.w3p = take(size_t(sh.d_c) * sh.k3 * sh.esize);
+  L.ysq = take(size_t(sh.B) * sh.nref * 4);
+  L.proj = take(size_t(sh.B) * sh.nref * 2 * sh.d_ff * 4);
+  L.part = take(size_t(sh.B) * sh.n_chunks * sh.nr * sh.kl * 8);
+  L.dh = take(size_t(sh.B) * sh.nr * sh.k3 * sh.esize);
+  L.zc = take(size_t(sh.B) * sh.nr * sh.d_c * 4);
+  L.total = off;
+  return L;
+}
+
+hipError_t launch_pack_weights(const Shape& sh, const void* w1, const void* w2, const void* w3,
+                               char* ws, const Workspace& L, hipStream_t st) {
+  const dim3 blk(256);
+  const dim3 g12(cdiv(sh.d_ff, 32), cdiv(sh.C, 32));
+  const dim3 g3(cdiv(sh.d_c, 32), cdiv(sh.d_ff, 32));
+  const int dup = sh.bf16 ? sh.d_ff : 0;
+  if (sh.bf16) {
+    auto* wp = reinterpret_cast<uint16_t*>(ws + L.wp);
+    k_transpose_pack<uint16_t><<<g12, blk, 0, st>>>(static_cast<const uint16_t*>(w1), sh.C, sh.d_ff, wp, sh.C, 1, 0);
+    k_transpose_pack<uint16_t><<<g12, blk, 0, st>>>(static_cast<const uint16_t*>(w2), sh.C, sh.d_ff, wp, sh.C, 2, 0);
+    k_transpose_pack<uint16_t><<<g3, blk, 0, st>>>(static_cast<const uint16_t*>(w3), sh.d_ff, sh.d_c,
+                                                   reinterpret_cast<uint16_t*>(ws + L.w3p), sh.k3, 0, dup);
+  } else {
+    auto* wp = reinterpret_cast<float*>(ws + L.wp);
+    k_transpose_pack<float><<<g12, blk, 0, st>>>(static_cast<const float*>(w1), sh.C, sh.d_ff, wp, sh.C, 1, 0);
+    k_transpose_pack<float><<<g12, blk, 0, st>>>(static_cast<const float*>(w2), sh.C, sh.d_ff, wp, sh.C, 2, 0);
+    k_transpose_pack<float><<<g3, blk, 0, st>>>(static_cast<const float*>(w3), sh.d_ff, sh.d_c,
+                                                reinterpret_cast<float*>(ws + L.w3p), sh.k3, 0, 0);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_ref_norms(const Shape& sh, const void* kv, char* ws, const Workspace& L,
+                            hipStream_t st) {
+  const int rows = sh.B * sh.nref;
+  auto* y = reinterpret_cast<float*>(ws + L.ysq);
+  const auto* p = static_cast<const char*>(kv);
+  if (sh.bf16)
+    k_ref_norms<uint16_t><<<cdiv(rows, 4), 256, 0, st>>>(p, sh.B, sh.T, sh.C, sh.s, sh.nref, y);
+  else
+    k_ref_norms<float><<<cdiv(rows, 4), 256, 0, st>>>(p, sh.B, sh.T, sh.C, sh.s, sh.nref, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_dist(const Shape& sh, const void* kv, char* ws, const Workspace& L,
+                       hipStream_t st) {
+  if (sh.nr == 0) return hipGetLastError();
+  const auto* p = static_cast<const char*>(kv);
+  const auto* y = reinterpret_cast<const float*>(ws + L.ysq);
+  auto* part = reinterpret_cast<float2*>(ws + L.part);
+  const int n_tt = cdiv(sh.nr, kDistTok);
+  const int items = sh.B * n_tt * sh.n_chunks;
+#define RKV_DIST(E, KL) \
+  k_dist_topk<E, KL><<<items, 256, 0, st>>>(p, y, part, sh.B, sh.T, sh.C, sh.s, sh.nref, sh.nr, sh.n_chunks, n_tt)
+  if (sh.bf16) { if (sh.kl == 4) RKV_DIST(uint16_t, 4); else RKV_DIST(uint16_t, 8); }
+  else { if (sh.kl == 4) RKV_DIST(float, 4); else RKV_DIST(float, 8); }
+#undef RKV_DIST
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const Shape& sh, int32_t* ref_idx, char* ws, const Workspace& L,
+                        hipStream_t st) {
+  const auto* part = reinterpret_cast<const float2*>(ws + L.part);
+  const int nb = cdiv(long(sh.B) * sh.T, 256);
+  if (sh.kl == 4)
+    k_topk_merge<4><<<nb, 256, 0, st>>>(part, ref_idx, sh.B, sh.T, sh.s, sh.k, sh.nr, sh.n_chunks);
+  else
+    k_topk_merge<8><<<nb, 256, 0, st>>>(part, ref_idx, sh.B, sh.T, sh.s, sh.k, sh.nr, sh.n_chunks);
+  return hipGetLastError();
+}
+
+hipError_t launch_ref_proj(const Shape& sh, const void* kv, char* ws, const Workspace& L,
+                           hipStream_t st) {
+  const int M = sh.B * sh.nref, N = 2 * sh.d_ff;
+  const int tn = cdiv(N, kGemmBN), tm = cdiv(M, kGemmBM);
+  const auto* p = static_cast<const char*>(kv);
+  auto* proj = reinterpret_cast<float*>(ws + L.proj);
+  if (sh.bf16)
+    k_ref_proj<uint16_t><<<tn * tm, 256, 0, st>>>(p, ws + L.wp, proj, sh.T, sh.C, sh.s, sh.nref, M, N, tn);
+  else
+    k_ref_proj<float><<<tn * tm, 256, 0, st>>>(p, ws + L.wp, proj, sh.T, sh.C, sh.s, sh.nref, M, N, tn);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu(const Shape& sh, const void* kv, const int32_t* ref_idx, char* ws,
+                         const Workspace& L, hipStream_t st) {
+  const int M = sh.B * sh.nr, N = 2 * sh.d_ff;
+  if (M == 0) return hipGetLastError();
+  const int tn = cdiv(N, kGemmBN), tm = cdiv(M, kGemmBM);
+  const auto* p = static_cast<const char*>(kv);
+  const auto* proj = reinterpret_cast<const float*>(ws + L.proj);
+#define RKV_SW(E, KL)                                                                       \
+  k_swiglu<E, KL><<<tn * tm, 256, 0, st>>>(p, ws + L.wp, proj, ref_idx, ws + L.dh, sh.T, sh.C, \
+                                           sh.s, sh.nref, sh.nr, sh.k, sh.d_ff, M, tn)
+  if (sh.bf16) { if (sh.kl == 4) RKV_SW(uint16_t, 4); else RKV_SW(uint16_t, 8); }
+  else { if (sh.kl == 4) RKV_SW(float, 4); else RKV_SW(float, 8); }
+#undef RKV_SW
+  return hipGetLastError();
+}
+
+hipError_t launch_w3(const Shape& sh, char* ws, const Workspace& L, hipStream_t st) {
+  const int M = sh.B * sh.nr, N = sh.d_c;
+  if (M == 0) return hipGetLastError();
+  const int tn = cdiv(N, kGemmBN), tm = cdiv(M, kGemmBM);
+  auto* zc = reinterpret_cast<float*>(ws + L.zc);
+  if (sh.bf16)
+    k_w3<uint16_t><<<tn * tm, 256, 0, st>>>(ws + L.dh, ws + L.w3p, zc, sh.k3, M, N, tn);
+  else
+    k_w3<float><<<tn * tm, 256, 0, st>>>(ws + L.dh, ws + L.w3p, zc, sh.k3, M, N, tn);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize(const float* z, int64_t rows, int T, int s, int d_c, int g, int b,
+                           uint8_t* codes, uint16_t* scale, uint16_t* zmin, float* zout,
+                           hipStream_t st) {
+  if (rows == 0) return hipGetLastError();
+  const int nr = s >= 1 ? T - (T + s - 1) / s : 0;
+  const int64_t units = rows * (d_c / 8);
+  const int grid = grid_for(units, 256);
+#define RKV_Q(BITS, G8) \
+  k_quantize<BITS, G8><<<grid, 256, 0, st>>>(z, rows, T, s, nr, d_c, codes, scale, zmin, zout)
+#define RKV_QG(BITS)                        \
+  switch (g) {                              \
+    case 8: RKV_Q(BITS, 1); break;          \
+    case 16: RKV_Q(BITS, 2); break;         \
+    case 32: RKV_Q(BITS, 4); break;         \
+    default: RKV_Q(BITS, 8); break;         \
+  }
+  if (b == 4) { RKV_QG(4) } else { RKV_QG(2) }
+#undef RKV_QG
+#undef RKV_Q
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const uint8_t* codes, const uint16_t* scale, const uint16_t* zmin,
+                         const int32_t* idx, int64_t n_idx, int64_t total_rows, int d_c, int g,
+                         int b, void* out, bool out_bf16, hipStream_t st) {
+  if (n_idx == 0) return hipGetLastError();
+  const int64_t units = n_idx * (d_c / 8);
+  const int grid = grid_for(units, 256);
+#define RKV_G(BITS, BF) \
+  k_gather<BITS, BF><<<grid, 256, 0, st>>>(codes, scale, zmin, idx, n_idx, total_rows, d_c, g, out)
+  if (b == 4) { if (out_bf16) RKV_G(4, true); else RKV_G(4, false); }
+  else { if (out_bf16) RKV_G(2, true); else RKV_G(2, false); }
+#undef RKV_G
+  return hipGetLastError();
+}
+
+}  // namespace rkv

@@ -1,0 +1,141 @@
+"""CPU tests of the C ABI: the library loads without a GPU, exports every
+symbol include/rkv.h declares, and rejects bad arguments on the host before
+anything is enqueued (no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import reference_residual_encoding_amd as R
+from synth.configs import CONFIGS, LLAMA32K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000          # aligned, never dereferenced: validation fails first
+FAKE_MIS = 0x10004      # misaligned
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "rkv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rkv_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = R.lib()
+    declared = header_functions()
+    assert set(declared) == set(R.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert R.rkv_abi_version() == 1
+
+
+def test_status_strings():
+    assert R.rkv_status_str(0) == "RKV_OK"
+    assert R.rkv_status_str(3) == "RKV_ERR_WORKSPACE"
+
+
+def _p(cfg, **kw):
+    d = dict(B=cfg.B, T=cfg.T, N=cfg.N, D=cfg.D, d_ff=cfg.d_ff, d_c=cfg.d_c, k=cfg.k, g=cfg.g,
+             b=cfg.b, ref_stride=cfg.stride, dtype=cfg.dtype)
+    d.update(kw)
+    return R.params(**d)
+
+
+def _encode(p, ws_bytes=1 << 40, **ptrs):
+    args = dict(kv=FAKE, w1=FAKE, w2=FAKE, w3=FAKE, ref_idx=FAKE, codes=FAKE, scale=FAKE,
+                zmin=FAKE, z=None, workspace=FAKE)
+    args.update(ptrs)
+    # Safety: these pointers are fake; a call that would pass validation must
+    # never be made (it would enqueue kernels on them).
+    valid_ptrs = all(v is not None and v % 16 == 0 for k, v in args.items() if k != "z") \
+        and (args["z"] is None or args["z"] % 16 == 0)
+    if R.rkv_encode_workspace_bytes(p) and valid_ptrs and ws_bytes >= R.rkv_encode_workspace_bytes(p):
+        pytest.fail("test would pass validation with fake pointers")
+    return R.rkv_encode(p, args["kv"], args["w1"], args["w2"], args["w3"], args["ref_idx"],
+                        args["codes"], args["scale"], args["zmin"], args["z"],
+                        args["workspace"], ws_bytes, None, check=False)
+
+
+@pytest.mark.parametrize("cfg", CONFIGS, ids=lambda c: c.name)
+def test_workspace_size_is_positive_and_grows_with_T(cfg):
+    w = R.rkv_encode_workspace_bytes(_p(cfg))
+    assert w > 0 and w % 256 == 0
+    assert R.rkv_encode_workspace_bytes(_p(cfg, T=cfg.T * 2)) > w
+
+
+def test_workspace_size_zero_for_invalid_params():
+    assert R.rkv_encode_workspace_bytes(_p(LLAMA32K, b=3)) == 0
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("B", 0, R.RKV_ERR_INVALID_ARG), ("T", -1, R.RKV_ERR_INVALID_ARG),
+    ("N", 0, R.RKV_ERR_INVALID_ARG), ("d_ff", 0, R.RKV_ERR_INVALID_ARG),
+    ("k", 0, R.RKV_ERR_INVALID_ARG), ("ref_stride", 0, R.RKV_ERR_INVALID_ARG),
+    ("b", 3, R.RKV_ERR_INVALID_ARG), ("b", 8, R.RKV_ERR_INVALID_ARG),
+    ("g", 0, R.RKV_ERR_INVALID_ARG), ("dtype", 7, R.RKV_ERR_INVALID_ARG),
+    ("g", 24, R.RKV_ERR_UNSUPPORTED), ("k", 9, R.RKV_ERR_UNSUPPORTED),
+    ("d_c", 48, R.RKV_ERR_UNSUPPORTED), ("g", 64, R.RKV_ERR_UNSUPPORTED),
+    ("d_ff", 1000, R.RKV_ERR_UNSUPPORTED), ("D", 10, R.RKV_ERR_UNSUPPORTED),
+])
+def test_encode_rejects_bad_params(field, value, status):
+    kw = {field: value}
+    if field == "g" and value == 64:
+        kw["d_c"] = 96         # 64 does not divide 96
+    st = _encode(_p(LLAMA32K, **kw))
+    assert st == status, R.rkv_last_error()
+    assert R.rkv_last_error() != ""
+
+
+@pytest.mark.parametrize("name", ["kv", "w1", "w2", "w3", "ref_idx", "codes", "scale", "zmin",
+                                  "workspace"])
+def test_encode_rejects_null_and_misaligned(name):
+    p = _p(LLAMA32K)
+    assert _encode(p, **{name: None}) == R.RKV_ERR_INVALID_ARG
+    assert name in R.rkv_last_error()
+    assert _encode(p, **{name: FAKE_MIS}) == R.RKV_ERR_INVALID_ARG
+    assert "aligned" in R.rkv_last_error()
+    assert _encode(p, z=FAKE_MIS) == R.RKV_ERR_INVALID_ARG
+
+
+def test_encode_rejects_small_workspace():
+    p = _p(LLAMA32K)
+    need = R.rkv_encode_workspace_bytes(p)
+    assert _encode(p, ws_bytes=need - 1) == R.RKV_ERR_WORKSPACE
+    assert str(need) in R.rkv_last_error()
+    st = R.rkv_select(p, FAKE, FAKE, FAKE, need - 256, None, check=False)
+    assert st == R.RKV_ERR_WORKSPACE
+
+
+def test_raising_wrapper_carries_status_and_text():
+    with pytest.raises(R.RkvError) as e:
+        R.rkv_encode(_p(LLAMA32K, b=5), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                     FAKE, 1 << 40, None)
+    assert e.value.status == R.RKV_ERR_INVALID_ARG and "b must be" in str(e.value)
+
+
+def test_gather_and_quantize_validation_and_empty_calls():
+    p = _p(LLAMA32K)
+    # zero-size calls succeed without touching the device
+    assert R.rkv_dequant_gather(p, FAKE, FAKE, FAKE, FAKE, 0, FAKE, "f32", None, check=False) == 0
+    assert R.rkv_quantize(p, FAKE, 0, FAKE, FAKE, FAKE, None, check=False) == 0
+    assert R.rkv_dequant_gather(p, FAKE, FAKE, FAKE, FAKE, -1, FAKE, "f32", None,
+                                check=False) == R.RKV_ERR_INVALID_ARG
+    assert R.rkv_dequant_gather(p, FAKE, FAKE, FAKE, None, 5, FAKE, "f32", None,
+                                check=False) == R.RKV_ERR_INVALID_ARG
+    assert R.rkv_dequant_gather(p, FAKE, FAKE, FAKE, FAKE, 5, FAKE, 9, None,
+                                check=False) == R.RKV_ERR_INVALID_ARG
+    assert R.rkv_dequant_gather(_p(LLAMA32K, b=1), FAKE, FAKE, FAKE, FAKE, 5, FAKE, "f32", None,
+                                check=False) == R.RKV_ERR_INVALID_ARG
+    assert R.rkv_quantize(p, FAKE, -3, FAKE, FAKE, FAKE, None, check=False) == R.RKV_ERR_INVALID_ARG
+    assert R.rkv_quantize(p, FAKE_MIS, 3, FAKE, FAKE, FAKE, None, check=False) == R.RKV_ERR_INVALID_ARG
+
+
+def test_product_package_never_imports_the_oracle():
+    pkg = os.path.join(ROOT, "reference_residual_encoding_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "rkv_oracle" not in text, f

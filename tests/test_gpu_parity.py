@@ -1,0 +1,167 @@
+"""GPU parity: the HIP path (called through the C ABI) against the fp64 CPU
+oracle on the same seeded inputs.  Needs an MI355X."""
+import numpy as np
+import pytest
+import torch
+
+import reference_residual_encoding_amd as R
+from reference_residual_encoding_amd import buffers as RB
+from oracle import rkv_oracle as O
+from synth import generate
+from synth.configs import LLAMA8K, LLAMA32K, MM_INT2, QWEN_LIKE, TINY
+
+import rkv_parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _gather_rows(p, out, idx_flat):
+    idx = torch.from_numpy(np.asarray(idx_flat, dtype=np.int32)).cuda()
+    rows = RB.dequant_gather(p, out, idx, "f32")
+    torch.cuda.synchronize()
+    return rows.cpu().numpy()
+
+
+def _full_parity(cfg):
+    w = generate(cfg)
+    p, out, host, _ = P.run_encode(w)
+    P.check_record_invariants(cfg, host)
+    P.check_quantizer_bit_exact(cfg, host)
+    pos = {b: np.arange(cfg.T) for b in range(cfg.B)}
+    gathered = {b: _gather_rows(p, out, b * cfg.T + pos[b]) for b in range(cfg.B)}
+    return P.compare_tokens(w, host, pos, gathered, log=_log)
+
+
+def test_tiny_f32_all_positions():
+    _log("[case] tiny_f32 full")
+    _full_parity(TINY)
+
+
+# Ragged shapes spanning several tiles, non-power-of-two stride, k > 4
+# (8-long neighbour lists), g = 16 and 64, INT2, both dtypes.
+RAGGED = [
+    LLAMA8K.with_(name="ragged_bf16_b2_k5", B=3, T=1000, N=2, D=32, d_ff=96, d_c=64, k=5, g=16,
+                  b=2, stride=7, n_protos=24),
+    LLAMA8K.with_(name="ragged_f32_k1_g64", B=2, T=777, N=1, D=64, d_ff=64, d_c=128, k=1, g=64,
+                  b=4, stride=3, dtype="f32", n_protos=12, noise=0.3),
+    LLAMA8K.with_(name="ragged_bf16_k8_g8", B=1, T=1300, N=4, D=32, d_ff=160, d_c=96, k=8, g=8,
+                  b=4, stride=16, n_protos=40),
+]
+
+
+@pytest.mark.parametrize("cfg", RAGGED, ids=lambda c: c.name)
+def test_ragged_shapes_all_positions(cfg):
+    _log(f"[case] {cfg.name} full")
+    _full_parity(cfg)
+
+
+EDGE = [
+    TINY.with_(name="edge_T1", T=1),
+    TINY.with_(name="edge_T_lt_s", T=5),
+    TINY.with_(name="edge_T_eq_s_plus1", T=9),
+    TINY.with_(name="edge_s1_all_refs", T=40, stride=1),
+    TINY.with_(name="edge_s_gt_T", T=20, stride=64),
+    TINY.with_(name="edge_bf16_T130", T=130, dtype="bf16"),
+]
+
+
+@pytest.mark.parametrize("cfg", EDGE, ids=lambda c: c.name)
+def test_edge_cases(cfg):
+    _log(f"[case] {cfg.name}")
+    _full_parity(cfg)
+
+
+@pytest.mark.parametrize("cfg,n_random", [(LLAMA8K, 800), (LLAMA32K, 500), (QWEN_LIKE, 300),
+                                          (MM_INT2, 200)], ids=lambda c: getattr(c, "name", c))
+def test_full_size_configs_sampled(cfg, n_random):
+    """Full-size workloads, in the launch configuration the benchmark times:
+    invariants and bit-exact quantiser on every token, oracle parity on a
+    sample of tokens computed one by one."""
+    _log(f"[case] {cfg.name} sampled")
+    w = generate(cfg)
+    p, out, host, _ = P.run_encode(w)
+    P.check_record_invariants(cfg, host)
+    P.check_quantizer_bit_exact(cfg, host)
+    pos = {b: P.sample_positions(cfg.T, cfg.stride, n_random, seed=100 + b) for b in range(cfg.B)}
+    gathered = {b: _gather_rows(p, out, b * cfg.T + pos[b]) for b in range(cfg.B)}
+    P.compare_tokens(w, host, pos, gathered, log=_log)
+
+
+def test_select_export_matches_encode():
+    cfg = LLAMA8K.with_(T=2048)
+    w = generate(cfg)
+    p, out, host, (kv, *_) = P.run_encode(w, with_z=False)
+    ri = torch.empty_like(out.ref_idx)
+    R.rkv_select(p, kv, ri, out.workspace, out.workspace.numel(), torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert np.array_equal(ri.cpu().numpy(), host["ref_idx"])
+
+
+def test_encode_is_deterministic():
+    cfg = LLAMA8K.with_(T=4096)
+    w = generate(cfg)
+    _, _, h1, _ = P.run_encode(w)
+    _, _, h2, _ = P.run_encode(w)
+    for key in ("ref_idx", "codes", "scale", "zmin", "z"):
+        assert np.array_equal(h1[key].view(np.uint8), h2[key].view(np.uint8)), key
+
+
+@pytest.mark.parametrize("b,g", [(4, 32), (2, 32), (4, 8), (2, 16), (4, 64)])
+def test_quantize_export_bit_exact(b, g):
+    rng = np.random.default_rng(b * 100 + g)
+    d_c = 128
+    z = np.concatenate([
+        rng.standard_normal((300, d_c)),
+        rng.standard_t(2, size=(100, d_c)) * 1e-3,
+        np.zeros((5, d_c)),                          # all-zero rows
+        np.full((5, d_c), 0.1),                      # constant groups, not fp16-exact
+        np.tile(np.arange(d_c) % g, (5, 1)) * 0.5,   # ramps with half-grid ties
+    ]).astype(np.float32)
+    z[7, :g] = 3.25                                  # one constant group inside a row
+    p = R.params(B=1, T=1, N=1, D=32, d_ff=32, d_c=d_c, k=4, g=g, b=b, ref_stride=1, dtype="f32")
+    zt = torch.from_numpy(z).cuda()
+    codes = torch.empty((len(z), d_c * b // 8), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((len(z), d_c // g), dtype=torch.float16, device="cuda")
+    zm = torch.empty_like(sc)
+    R.rkv_quantize(p, zt, len(z), codes, sc, zm, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    q, dh, mh = O.quantize(z.astype(np.float64), g, b)
+    assert np.array_equal(codes.cpu().numpy(), O.pack_codes(q, b))
+    assert np.array_equal(sc.cpu().numpy().view(np.uint16), dh.view(np.uint16))
+    assert np.array_equal(zm.cpu().numpy().view(np.uint16), mh.view(np.uint16))
+
+
+@pytest.mark.parametrize("b", [4, 2])
+def test_gather_bit_exact_f32_and_bf16(b):
+    rng = np.random.default_rng(5 + b)
+    B, T, d_c, g = 2, 300, 64, 32
+    z = rng.standard_normal((B * T, d_c))
+    z[::7] = 0.0
+    q, dh, mh = O.quantize(z, g, b)
+    codes = O.pack_codes(q, b)
+    idx = np.concatenate([rng.integers(0, B * T, 500), [0, B * T - 1, -1, B * T, 10 ** 6, 3, 3]])
+    idx = idx.astype(np.int32)
+    p = R.params(B=B, T=T, N=1, D=32, d_ff=32, d_c=d_c, k=4, g=g, b=b, ref_stride=4, dtype="f32")
+    dc = torch.from_numpy(codes).cuda()
+    ds = torch.from_numpy(dh).cuda()
+    dz = torch.from_numpy(mh).cuda()
+    di = torch.from_numpy(idx).cuda()
+    out32 = torch.empty((len(idx), d_c), dtype=torch.float32, device="cuda")
+    out16 = torch.empty((len(idx), d_c), dtype=torch.bfloat16, device="cuda")
+    st = torch.cuda.current_stream()
+    R.rkv_dequant_gather(p, dc, ds, dz, di, len(idx), out32, "f32", st)
+    R.rkv_dequant_gather(p, dc, ds, dz, di, len(idx), out16, "bf16", st)
+    R.rkv_dequant_gather(p, dc, ds, dz, di, 0, out32, "f32", st)      # empty: no-op
+    torch.cuda.synchronize()
+    want = O.gather(codes, dh, mh, idx, g=g, b=b, d_c=d_c)
+    got = out32.cpu().numpy()
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    g16 = P.bf16_bits_of(out16)
+    assert np.array_equal(g16[~nan], P.expected_bf16(want)[~nan])
+    assert np.all(np.isnan(out16.float().cpu().numpy()[nan]))
