@@ -148,8 +148,8 @@ typedef enum {
   RKV_STAGE_MERGE = 3,   /* top-k merge, ref_idx                            */
   RKV_STAGE_PROJ = 4,    /* reference projection R [W1|W2]                  */
   RKV_STAGE_SWIGLU = 5,  /* token projection + SwiGLU difference            */
-  RKV_STAGE_W3 = 6,      /* latent z = delta_h W3                           */
-  RKV_STAGE_QUANT = 7,   /* group quantiser                                 */
+  RKV_STAGE_W3 = 6,      /* latent z = delta_h W3 + group quantiser         */
+  RKV_STAGE_QUANT = 7,   /* stand-alone quantiser (rkv_quantize)            */
   RKV_STAGE_GATHER = 8,  /* gather-dequantise                               */
   RKV_STAGE_COUNT = 9
 } rkv_stage;

@@ -193,16 +193,13 @@ rkv_status rkv_encode(const rkv_params* p, const void* kv, const void* w1, const
   RKV_STAGE(RKV_STAGE_PACK, rkv::launch_pack_weights(sh, w1, w2, w3, ws, L, stream), "pack");
   RKV_STAGE(RKV_STAGE_NORMS, rkv::launch_ref_norms(sh, kv, ws, L, stream), "norms");
   RKV_STAGE(RKV_STAGE_DIST, rkv::launch_dist(sh, kv, ws, L, stream), "dist");
-  RKV_STAGE(RKV_STAGE_MERGE, rkv::launch_merge(sh, ref_idx, ws, L, stream), "merge");
+  RKV_STAGE(RKV_STAGE_MERGE, rkv::launch_merge(sh, ref_idx, ws, L, codes, scale, zmin, z, stream),
+            "merge");
   if (sh.nr > 0) {
     RKV_STAGE(RKV_STAGE_PROJ, rkv::launch_ref_proj(sh, kv, ws, L, stream), "proj");
     RKV_STAGE(RKV_STAGE_SWIGLU, rkv::launch_swiglu(sh, kv, ref_idx, ws, L, stream), "swiglu");
-    RKV_STAGE(RKV_STAGE_W3, rkv::launch_w3(sh, ws, L, stream), "w3");
+    RKV_STAGE(RKV_STAGE_W3, rkv::launch_w3_quant(sh, ws, L, codes, scale, zmin, z, stream), "w3");
   }
-  RKV_STAGE(RKV_STAGE_QUANT,
-            rkv::launch_quantize(reinterpret_cast<const float*>(ws + L.zc), int64_t(sh.B) * sh.T,
-                                 sh.T, sh.s, sh.d_c, sh.g, sh.b, codes, scale, zmin, z, stream),
-            "quantize");
   return ok();
 }
 
@@ -221,7 +218,9 @@ rkv_status rkv_select(const rkv_params* p, const void* kv, int32_t* ref_idx, voi
   hipError_t e;
   RKV_STAGE(RKV_STAGE_NORMS, rkv::launch_ref_norms(sh, kv, ws, L, stream), "norms");
   RKV_STAGE(RKV_STAGE_DIST, rkv::launch_dist(sh, kv, ws, L, stream), "dist");
-  RKV_STAGE(RKV_STAGE_MERGE, rkv::launch_merge(sh, ref_idx, ws, L, stream), "merge");
+  RKV_STAGE(RKV_STAGE_MERGE,
+            rkv::launch_merge(sh, ref_idx, ws, L, nullptr, nullptr, nullptr, nullptr, stream),
+            "merge");
   return ok();
 }
 
@@ -237,9 +236,11 @@ rkv_status rkv_quantize(const rkv_params* p, const float* z, int64_t rows, uint8
   RKV_NEED_PTR(codes);
   RKV_NEED_PTR(scale);
   RKV_NEED_PTR(zmin);
-  hipError_t e = rkv::launch_quantize(z, rows, 0, 0, p->d_c, p->g, p->b, codes, scale, zmin,
-                                      nullptr, stream);
-  return device_status(e, "quantize");
+  hipError_t e;
+  RKV_STAGE(RKV_STAGE_QUANT,
+            rkv::launch_quantize(z, rows, p->d_c, p->g, p->b, codes, scale, zmin, stream),
+            "quantize");
+  return ok();
 }
 
 rkv_status rkv_dequant_gather(const rkv_params* p, const uint8_t* codes, const uint16_t* scale,

@@ -41,23 +41,22 @@ __device__ __forceinline__ int nonref_pos(int q, int s) {
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
 
-// Keep the KL smallest (d, j) pairs in ascending (d, j) order.
+// Keep the KL smallest (d, j) pairs in ascending (d, j) order, for
+// candidates that arrive in increasing j: a newcomer then goes after every
+// kept pair of equal d, so the strict comparison d < d_i decides alone.
+// Branch-free select network (an infinite d never enters).
 template <int KL>
-__device__ __forceinline__ void topk_insert(float (&bd)[KL], int (&bi)[KL], float d, int j) {
-  if (d < bd[KL - 1] || (d == bd[KL - 1] && j < bi[KL - 1])) {
-    bd[KL - 1] = d;
-    bi[KL - 1] = j;
+__device__ __forceinline__ void topk_push(float (&bd)[KL], int (&bi)[KL], float d, int j) {
+  bool c[KL];
 #pragma unroll
-    for (int i = KL - 1; i > 0; --i) {
-      const bool sw = bd[i] < bd[i - 1] || (bd[i] == bd[i - 1] && bi[i] < bi[i - 1]);
-      const float td = sw ? bd[i - 1] : bd[i];
-      const int ti = sw ? bi[i - 1] : bi[i];
-      bd[i - 1] = sw ? bd[i] : bd[i - 1];
-      bi[i - 1] = sw ? bi[i] : bi[i - 1];
-      bd[i] = td;
-      bi[i] = ti;
-    }
+  for (int i = 0; i < KL; ++i) c[i] = d < bd[i];
+#pragma unroll
+  for (int i = KL - 1; i > 0; --i) {
+    bd[i] = c[i - 1] ? bd[i - 1] : (c[i] ? d : bd[i]);
+    bi[i] = c[i - 1] ? bi[i - 1] : (c[i] ? j : bi[i]);
   }
+  bd[0] = c[0] ? d : bd[0];
+  bi[0] = c[0] ? j : bi[0];
 }
 
 }  // namespace rkv

@@ -139,14 +139,186 @@ __device__ __forceinline__ void gemm_mainloop(const char* (&pa)[BM / 32],
   }
 }
 
-// Write a workgroup's accumulators to LDS as a row-major fp32 tile with row
-// stride `ld` floats.  With ld % 64 == 8 the two half-waves (rows 4 apart)
-// land on disjoint banks.  Callers synchronise before reading it back.
-template <int BM, int BN>
-__device__ __forceinline__ void acc_to_lds(const f32x16 (&acc)[BM / 64][BN / 64], float* tile,
-                                           int ld) {
+// ---------------------------------------------------------------------------
+// bf16 main loop: LDS-DMA ring (gfx950 global_load_lds_dwordx4).
+//
+// Same tile and accumulator layout as gemm_mainloop, but:
+//  - operands travel HBM/L2 -> LDS directly (no VGPR staging), NS stages of
+//    SB bytes of K per row in flight, so a stage is requested NS-1 stages
+//    before it is consumed;
+//  - LDS rows are SB bytes, unpadded; the 16-byte slot of each row is XOR-
+//    swizzled (swz) so the 32 rows a half-wave reads at one K offset hit
+//    distinct banks (the DMA writes 1 KB contiguous per wave instruction,
+//    so the swizzle is applied on the global side: lane l of a DMA
+//    instruction fetches slot (l % kSlots) ^ swz(row));
+//  - fragments are double-buffered: the next k-step's reads are issued
+//    between this k-step's MFMAs (sched_group_barrier keeps that order);
+//  - waits are explicit s_waitcnt vmcnt(n) + a bare s_barrier (no fence), so
+//    younger stages stay in flight across the barrier.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <int BM, int BN, int SB, int NS>
+struct DmaTile {
+  static constexpr int kSlots = SB / 16;          // 16-byte slots per LDS row
+  static constexpr int kRowsPerKB = 1024 / SB;    // rows per DMA wave instruction
+  static constexpr int kStage = (BM + BN) * SB;   // bytes per stage
+  static constexpr int kLds = NS * kStage;
+  static constexpr int kWM = BM / 2, kWN = BN / 2, kTM = kWM / 32, kTN = kWN / 32;
+  static constexpr int kSteps = SB / 32;          // 32x32x16 k-steps per stage
+  static constexpr int kLdA = BM * SB / 4096, kLdB = BN * SB / 4096;  // DMA instr. per wave per stage
+  static constexpr int kLd = kLdA + kLdB;
+  static_assert(kSteps % 2 == 0, "fragment double-buffering pairs k-steps");
+  static_assert(kLdA >= 1 && kLdB >= 1, "each wave feeds part of A and of B");
+  static_assert(kLd * (NS - 2 > 0 ? NS - 2 : 0) <= 31, "vmcnt window");
+};
+
+template <int SB>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (SB == 64) return ((r >> 1) ^ (r >> 3)) & 3;
+  else return (r ^ (r >> 3)) & 7;
+}
+
+// Tile-local row fed by DMA instruction i of this lane, and the byte offset
+// of the (swizzled) K slot it fetches within a stage.
+template <typename TL, int SB>
+__device__ __forceinline__ int dma_row(int i, int per_wave) {
+  return ((threadIdx.x >> 6) * per_wave + i) * TL::kRowsPerKB + (threadIdx.x & 63) / TL::kSlots;
+}
+template <typename TL, int SB>
+__device__ __forceinline__ int dma_slot(int row) {
+  return (((threadIdx.x & 63) % TL::kSlots) ^ swz<SB>(row)) << 4;
+}
+
+// s_waitcnt vmcnt(n) lgkmcnt(0)
+__device__ __forceinline__ void wait_vm_lgkm(int n) {
+#define RKV_WVM(N) \
+  case N: __builtin_amdgcn_s_waitcnt(((N) & 0xF) | (((N) >> 4) << 14) | (0x7 << 4)); break;
+  switch (n) {
+    RKV_WVM(0) RKV_WVM(1) RKV_WVM(2) RKV_WVM(3) RKV_WVM(4) RKV_WVM(5) RKV_WVM(6) RKV_WVM(7)
+    RKV_WVM(8) RKV_WVM(9) RKV_WVM(10) RKV_WVM(11) RKV_WVM(12) RKV_WVM(13) RKV_WVM(14)
+    RKV_WVM(15) RKV_WVM(16) RKV_WVM(17) RKV_WVM(18) RKV_WVM(19) RKV_WVM(20) RKV_WVM(21)
+    RKV_WVM(22) RKV_WVM(23) RKV_WVM(24) RKV_WVM(25) RKV_WVM(26) RKV_WVM(27) RKV_WVM(28)
+    RKV_WVM(29) RKV_WVM(30) RKV_WVM(31)
+    default: __builtin_amdgcn_s_waitcnt(0x7 << 4); break;  // vmcnt(0) lgkmcnt(0)
+  }
+#undef RKV_WVM
+}
+
+// Workgroup barrier without a memory fence (the waits above order memory);
+// the empty asm statements stop the compiler moving LDS accesses across it.
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// pa[i] / pb[i] (i < kLdA / kLdB): this lane's source address for DMA
+// instruction i at K stage 0 (row base + dma_slot); rows past the end must
+// point at a valid row.
+template <int BM, int BN, int SB, int NS>
+__device__ __forceinline__ void gemm_mainloop_dma(const char* const* pa, const char* const* pb,
+                                                  int KT, char* lds,
+                                                  f32x16 (&acc)[BM / 64][BN / 64]) {
+  using TL = DmaTile<BM, BN, SB, NS>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int i = 0; i < TL::kTM; ++i)
+#pragma unroll
+    for (int j = 0; j < TL::kTN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  auto issue = [&](int s) {
+    char* buf = lds + (s % NS) * TL::kStage;
+#pragma unroll
+    for (int i = 0; i < TL::kLdA; ++i)
+      __builtin_amdgcn_global_load_lds(pa[i] + size_t(s) * SB,
+                                       (lds_ptr_t)(buf + (wave * TL::kLdA + i) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < TL::kLdB; ++i)
+      __builtin_amdgcn_global_load_lds(pb[i] + size_t(s) * SB,
+                                       (lds_ptr_t)(buf + BM * SB + (wave * TL::kLdB + i) * 1024),
+                                       16, 0, 0);
+  };
+  int offA[TL::kTM], swA[TL::kTM], offB[TL::kTN], swB[TL::kTN];
+#pragma unroll
+  for (int i = 0; i < TL::kTM; ++i) {
+    const int r = wm * TL::kWM + i * 32 + (lane & 31);
+    offA[i] = r * SB;
+    swA[i] = swz<SB>(r);
+  }
+#pragma unroll
+  for (int j = 0; j < TL::kTN; ++j) {
+    const int r = wn * TL::kWN + j * 32 + (lane & 31);
+    offB[j] = BM * SB + r * SB;
+    swB[j] = swz<SB>(r);
+  }
+  const int hi = lane >> 5;
+  bf16x8 fa[2][TL::kTM], fb[2][TL::kTN];
+  auto load_frags = [&](int stage, int st, int p) {
+    const char* buf = lds + (stage % NS) * TL::kStage;
+    const int kc = 2 * st + hi;
+#pragma unroll
+    for (int i = 0; i < TL::kTM; ++i)
+      fa[p][i] = *reinterpret_cast<const bf16x8*>(buf + offA[i] + ((kc ^ swA[i]) << 4));
+#pragma unroll
+    for (int j = 0; j < TL::kTN; ++j)
+      fb[p][j] = *reinterpret_cast<const bf16x8*>(buf + offB[j] + ((kc ^ swB[j]) << 4));
+  };
+
+  const int pre = NS - 1 < KT ? NS - 1 : KT;
+  for (int s = 0; s < pre; ++s) issue(s);
+  wait_vm_lgkm(TL::kLd * (pre - 1));
+  block_barrier();
+  load_frags(0, 0, 0);
+  for (int kt = 0; kt < KT; ++kt) {
+    if (kt + NS - 1 < KT) issue(kt + NS - 1);
+#pragma unroll
+    for (int st = 0; st < TL::kSteps; ++st) {
+      const int p = st & 1;
+      if (st + 1 < TL::kSteps) {
+        load_frags(kt, st + 1, p ^ 1);
+      } else if (kt + 1 < KT) {
+        // stage kt+1 must have landed (younger stages may stay in flight),
+        // and every wave must be done with the buffer the next issue reuses
+        const int younger = (KT - 2 - kt) < (NS - 2) ? (KT - 2 - kt) : (NS - 2);
+        wait_vm_lgkm(TL::kLd * younger);
+        block_barrier();
+        load_frags(kt + 1, 0, p ^ 1);
+      }
+#pragma unroll
+      for (int i = 0; i < TL::kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < TL::kTN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[p][i], fb[p][j], acc[i][j], 0, 0, 0);
+      constexpr int kMfma = TL::kTM * TL::kTN, kReads = TL::kTM + TL::kTN;
+#pragma unroll
+      for (int x = 0; x < kReads; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kReads, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // leave no LDS read in flight: callers reuse the LDS right away
+  __builtin_amdgcn_s_waitcnt((0xF | (3 << 14)) | (0x7 << 4));
+  block_barrier();
+}
+
+// Write the accumulators of the waves whose wave-row is `half` (or of every
+// wave when half < 0) to LDS as a row-major fp32 tile with row stride `ld`
+// floats; tile row 0 is the first row of that half (or of the workgroup).
+// With ld % 64 == 8 the two half-waves (rows 4 apart) land on disjoint banks.
+// Callers synchronise before reading it back.
+template <int BM, int BN>
+__device__ __forceinline__ void acc_to_lds(const f32x16 (&acc)[BM / 64][BN / 64], float* tile,
+                                           int ld, int half = -1) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  if (half >= 0 && wm != half) return;
+  const int row0 = half >= 0 ? 0 : wm * (BM / 2);
 #pragma unroll
   for (int i = 0; i < BM / 64; ++i)
 #pragma unroll
@@ -154,8 +326,49 @@ __device__ __forceinline__ void acc_to_lds(const f32x16 (&acc)[BM / 64][BN / 64]
       const int col = wn * (BN / 2) + j * 32 + (lane & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        tile[(wm * (BM / 2) + i * 32 + mfma32_row(r, lane)) * ld + col] = acc[i][j][r];
+        tile[(row0 + i * 32 + mfma32_row(r, lane)) * ld + col] = acc[i][j][r];
     }
+}
+
+// ---------------------------------------------------------------------------
+// One workgroup tile of C = A * B^T: the bf16 path runs the LDS-DMA ring
+// (SB bytes of K per stage, NS stages), the fp32 path the register-staged
+// loop.  rowA(r) / rowB(r) return the first byte of tile-local row r
+// (clamped to a valid row); kbytes is the contraction length in bytes.
+template <typename E, int BM, int BN, int SB, int NS>
+constexpr int mainloop_lds() {
+  return sizeof(E) == 2 ? DmaTile<BM, BN, SB, NS>::kLds : Tile<E, BM, BN>::kLds;
+}
+
+template <typename E, int BM, int BN, int SB, int NS, class RowA, class RowB>
+__device__ __forceinline__ void tile_product(const RowA& rowA, const RowB& rowB, int kbytes,
+                                             char* lds, f32x16 (&acc)[BM / 64][BN / 64]) {
+  if constexpr (sizeof(E) == 2) {
+    using TL = DmaTile<BM, BN, SB, NS>;
+    const char* pa[TL::kLdA];
+    const char* pb[TL::kLdB];
+#pragma unroll
+    for (int i = 0; i < TL::kLdA; ++i) {
+      const int r = dma_row<TL, SB>(i, TL::kLdA);
+      pa[i] = rowA(r) + dma_slot<TL, SB>(r);
+    }
+#pragma unroll
+    for (int i = 0; i < TL::kLdB; ++i) {
+      const int r = dma_row<TL, SB>(i, TL::kLdB);
+      pb[i] = rowB(r) + dma_slot<TL, SB>(r);
+    }
+    gemm_mainloop_dma<BM, BN, SB, NS>(pa, pb, kbytes / SB, lds, acc);
+  } else {
+    using TL = Tile<E, BM, BN>;
+    const int srow = threadIdx.x >> 3, scol = (threadIdx.x & 7) * 16;
+    const char* pa[TL::kLdA];
+    const char* pb[TL::kLdB];
+#pragma unroll
+    for (int i = 0; i < TL::kLdA; ++i) pa[i] = rowA(srow + 32 * i) + scol;
+#pragma unroll
+    for (int i = 0; i < TL::kLdB; ++i) pb[i] = rowB(srow + 32 * i) + scol;
+    gemm_mainloop<E, BM, BN>(pa, pb, kbytes / TL::kStage, lds, acc);
+  }
 }
 
 }  // namespace rkv

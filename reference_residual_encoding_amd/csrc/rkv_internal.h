@@ -21,7 +21,7 @@ struct Shape {
 
 // Byte offsets of the workspace regions (each 256-byte aligned).
 struct Workspace {
-  size_t wp, w3p, ysq, proj, part, dh, zc, total;
+  size_t wp, w3p, ysq, proj, part, dh, total;
 };
 
 Shape make_shape(int B, int T, int N, int D, int d_ff, int d_c, int k, int g, int b, int s,
@@ -36,18 +36,18 @@ hipError_t launch_ref_norms(const Shape& sh, const void* kv, char* ws, const Wor
 hipError_t launch_dist(const Shape& sh, const void* kv, char* ws, const Workspace& L,
                        hipStream_t st);
 hipError_t launch_merge(const Shape& sh, int32_t* ref_idx, char* ws, const Workspace& L,
+                        uint8_t* codes, uint16_t* scale, uint16_t* zmin, float* z,
                         hipStream_t st);
 hipError_t launch_ref_proj(const Shape& sh, const void* kv, char* ws, const Workspace& L,
                            hipStream_t st);
 hipError_t launch_swiglu(const Shape& sh, const void* kv, const int32_t* ref_idx, char* ws,
                          const Workspace& L, hipStream_t st);
-hipError_t launch_w3(const Shape& sh, char* ws, const Workspace& L, hipStream_t st);
-// Quantise rows of z.  With s >= 1 rows are the B*T tokens of an encode and
-// z is the compact non-reference latent (reference rows write zeros); with
-// s == 0 rows map one to one onto z.  zout (optional) receives the latent.
-hipError_t launch_quantize(const float* z, int64_t rows, int T, int s, int d_c, int g, int b,
-                           uint8_t* codes, uint16_t* scale, uint16_t* zmin, float* zout,
-                           hipStream_t st);
+// W3 product fused with the quantiser; writes the records of non-reference tokens.
+hipError_t launch_w3_quant(const Shape& sh, char* ws, const Workspace& L, uint8_t* codes,
+                           uint16_t* scale, uint16_t* zmin, float* z, hipStream_t st);
+// Quantise rows of z [rows][d_c] one to one into records (stepwise export).
+hipError_t launch_quantize(const float* z, int64_t rows, int d_c, int g, int b, uint8_t* codes,
+                           uint16_t* scale, uint16_t* zmin, hipStream_t st);
 hipError_t launch_gather(const uint8_t* codes, const uint16_t* scale, const uint16_t* zmin,
                          const int32_t* idx, int64_t n_idx, int64_t total_rows, int d_c, int g,
                          int b, void* out, bool out_bf16, hipStream_t st);

@@ -25,8 +25,9 @@
 //   w3        z = delta_h W3: since W3 is linear, f_c(kv) - f_c(m) equals
 //             (h(kv) - h(m)) W3 ([RKV] §2.3).  bf16 runs feed delta_h as a
 //             hi + lo pair of bf16 (K = 2 d_ff) so the product keeps ~16
-//             mantissa bits of delta_h.
-//   quantize  per-token group min-max quantiser ([RKV] §2.4).
+//             mantissa bits of delta_h.  The epilogue runs the per-token
+//             group min-max quantiser ([RKV] §2.4) and writes the record.
+//   (the merge writes the all-zero records of reference tokens)
 // The read side is one kernel: gather-dequantise over an index list.
 #include "rkv_device.h"
 #include "rkv_gemm.h"
@@ -38,9 +39,16 @@ namespace rkv {
 
 namespace {
 
-constexpr int kGemmBM = 128, kGemmBN = 128;   // proj / swiglu / w3 tiles
-constexpr int kDistRefs = 128;                // references per chunk (tile M)
-constexpr int kDistTok = 128;                 // tokens per tile (tile N)
+// Workgroup tiles (4 waves in a 2 x 2 grid, each wave a quarter of the
+// tile) and, for bf16, the DMA ring: SB bytes of K per stage, NS stages.
+constexpr int kProjBM = 128, kProjBN = 128, kProjNS = 4;  // reference projection
+constexpr int kSwBM = 256, kSwBN = 256, kSwNS = 2;        // token projection + SwiGLU difference
+constexpr int kW3BM = 256, kW3BN = 256, kW3NS = 2;        // W3 product + quantiser
+constexpr int kDistRefs = 128;                            // references per chunk (tile M)
+constexpr int kDistTok = 256;                             // tokens per tile (tile N)
+constexpr int kDistNS = 2;
+constexpr int kSB = 128;
+constexpr int kEpiLd(int bn) { return bn + 8; }  // padded fp32 row of an LDS-staged tile
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 inline int cdiv(long a, long b) { return int((a + b - 1) / b); }
@@ -106,303 +114,6 @@ __global__ __launch_bounds__(256) void k_ref_norms(const char* __restrict__ kv, 
   if (lane == 0) ysq[wid] = acc;
 }
 
-// ------------------------------------------------------------------ retrieval
-// One workgroup: kDistRefs references (chunk c) x kDistTok non-reference
-// tokens (tile tt) of sequence b.  Writes, per token, the KL best (d', j) of
-// the chunk restricted to the causal pool (j*s < position).
-template <typename E, int KL>
-__global__ __launch_bounds__(256) void k_dist_topk(const char* __restrict__ kv,
-                                                   const float* __restrict__ ysq,
-                                                   float2* __restrict__ part, int B, int T,
-                                                   int C, int s, int nref, int nr,
-                                                   int n_chunks, int n_tt) {
-  constexpr int BM = kDistRefs, BN = kDistTok;
-  using TL = Tile<E, BM, BN>;
-  __shared__ __attribute__((aligned(16))) char lds[TL::kLds];
-  const int item = blockIdx.x;
-  const int c = item % n_chunks;
-  const int rest = item / n_chunks;
-  const int tt = rest % n_tt, b = rest / n_tt;
-  const int n0 = tt * BN;
-  const int plast = nonref_pos(min(n0 + BN, nr) - 1, s);
-  const int npool_max = (plast + s - 1) / s;
-  const int m0 = c * BM;
-  if (m0 >= npool_max) return;  // chunk entirely after every token of the tile
-
-  const size_t rowb = size_t(C) * sizeof(E);
-  const char* base = kv + size_t(b) * T * rowb;
-  const int tid = threadIdx.x, srow = tid >> 3, scol = (tid & 7) * 16;
-  const char* pa[TL::kLdA];
-  const char* pb[TL::kLdB];
-#pragma unroll
-  for (int i = 0; i < TL::kLdA; ++i) {
-    const int j = min(m0 + srow + 32 * i, nref - 1);
-    pa[i] = base + size_t(j) * s * rowb + scol;
-  }
-#pragma unroll
-  for (int i = 0; i < TL::kLdB; ++i) {
-    const int q = min(n0 + srow + 32 * i, nr - 1);
-    pb[i] = base + size_t(nonref_pos(q, s)) * rowb + scol;
-  }
-  f32x16 acc[TL::kTM][TL::kTN];
-  gemm_mainloop<E, BM, BN>(pa, pb, int(rowb / TL::kStage), lds, acc);
-
-  const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-  float* ld_d = reinterpret_cast<float*>(lds);              // [BN][4][KL]
-  int* ld_i = reinterpret_cast<int*>(lds + BN * 4 * KL * 4);  // [BN][4][KL]
-  const float* yb = ysq + size_t(b) * nref;
-#pragma unroll
-  for (int tn = 0; tn < TL::kTN; ++tn) {
-    const int tl = wn * TL::kWN + tn * 32 + (lane & 31);
-    const int q = n0 + tl;
-    const bool qv = q < nr;
-    const int pq = qv ? nonref_pos(q, s) : 0;
-    float bd[KL];
-    int bi[KL];
-#pragma unroll
-    for (int i = 0; i < KL; ++i) { bd[i] = __builtin_inff(); bi[i] = 0x7fffffff; }
-#pragma unroll
-    for (int tm = 0; tm < TL::kTM; ++tm)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = m0 + wm * TL::kWM + tm * 32 + mfma32_row(r, lane);
-        const bool v = qv && j < nref && j * s < pq;
-        const float d = yb[min(j, nref - 1)] - 2.0f * acc[tm][tn][r];
-        if (v) topk_insert<KL>(bd, bi, d, j);
-      }
-    const int src = wm * 2 + (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < KL; ++i) {
-      ld_d[(tl * 4 + src) * KL + i] = bd[i];
-      ld_i[(tl * 4 + src) * KL + i] = bi[i];
-    }
-  }
-  __syncthreads();
-  if (tid < BN) {
-    const int q = n0 + tid;
-    if (q < nr) {
-      float bd[KL];
-      int bi[KL];
-#pragma unroll
-      for (int i = 0; i < KL; ++i) { bd[i] = __builtin_inff(); bi[i] = 0x7fffffff; }
-      for (int src = 0; src < 4; ++src)
-#pragma unroll
-        for (int i = 0; i < KL; ++i)
-          topk_insert<KL>(bd, bi, ld_d[(tid * 4 + src) * KL + i], ld_i[(tid * 4 + src) * KL + i]);
-      float2* out = part + ((size_t(b) * n_chunks + c) * nr + q) * KL;
-#pragma unroll
-      for (int i = 0; i < KL; ++i) out[i] = make_float2(bd[i], __int_as_float(bi[i]));
-    }
-  }
-}
-
-// Per token: merge the chunk lists, keep k_t = min(k, ceil(t/s)) references
-// ([RKV] §2.1), write their positions in ascending order, -1 pads.
-template <int KL>
-__global__ __launch_bounds__(256) void k_topk_merge(const float2* __restrict__ part,
-                                                    int32_t* __restrict__ ref_idx, int B, int T,
-                                                    int s, int k, int nr, int n_chunks) {
-  const long gid = long(blockIdx.x) * 256 + threadIdx.x;
-  if (gid >= long(B) * T) return;
-  const int b = int(gid / T), t = int(gid % T);
-  int32_t* out = ref_idx + gid * k;
-  if (t % s == 0) {
-    for (int i = 0; i < k; ++i) out[i] = -1;
-    return;
-  }
-  const int q = t - t / s - 1;
-  const int npool = (t + s - 1) / s;
-  const int kt = min(k, npool);
-  const int nch = (npool + kDistRefs - 1) / kDistRefs;
-  float bd[KL];
-  int bi[KL];
-#pragma unroll
-  for (int i = 0; i < KL; ++i) { bd[i] = __builtin_inff(); bi[i] = 0x7fffffff; }
-  for (int c = 0; c < nch; ++c) {
-    const float2* p = part + ((size_t(b) * n_chunks + c) * nr + q) * KL;
-#pragma unroll
-    for (int i = 0; i < KL; ++i) {
-      const float2 v = p[i];
-      topk_insert<KL>(bd, bi, v.x, __float_as_int(v.y));
-    }
-  }
-  int sel[KL];
-#pragma unroll
-  for (int i = 0; i < KL; ++i) sel[i] = i < kt ? bi[i] : 0x7fffffff;
-#pragma unroll
-  for (int i = 1; i < KL; ++i)
-#pragma unroll
-    for (int j = i; j > 0; --j) {
-      const int a = sel[j - 1], c2 = sel[j];
-      sel[j - 1] = min(a, c2);
-      sel[j] = max(a, c2);
-    }
-  for (int i = 0; i < k; ++i) {
-    int v = -1;
-#pragma unroll
-    for (int j = 0; j < KL; ++j)
-      if (j == i && i < kt) v = sel[j] * s;
-    out[i] = v;
-  }
-}
-
-// ------------------------------------------------------------------ reference projection
-template <typename E>
-__global__ __launch_bounds__(256) void k_ref_proj(const char* __restrict__ kv,
-                                                  const char* __restrict__ wp,
-                                                  float* __restrict__ proj, int T, int C, int s,
-                                                  int nref, int M, int N, int tiles_n) {
-  constexpr int BM = kGemmBM, BN = kGemmBN;
-  using TL = Tile<E, BM, BN>;
-  __shared__ __attribute__((aligned(16))) char lds[TL::kLds];
-  const int nt = blockIdx.x % tiles_n, mt = blockIdx.x / tiles_n;
-  const int m0 = mt * BM, n0 = nt * BN;
-  const size_t rowb = size_t(C) * sizeof(E);
-  const int tid = threadIdx.x, srow = tid >> 3, scol = (tid & 7) * 16;
-  const char* pa[TL::kLdA];
-  const char* pb[TL::kLdB];
-#pragma unroll
-  for (int i = 0; i < TL::kLdA; ++i) {
-    const int r = min(m0 + srow + 32 * i, M - 1);
-    const int b = r / nref, j = r % nref;
-    pa[i] = kv + (size_t(b) * T + size_t(j) * s) * rowb + scol;
-  }
-#pragma unroll
-  for (int i = 0; i < TL::kLdB; ++i) {
-    const int n = min(n0 + srow + 32 * i, N - 1);
-    pb[i] = wp + size_t(n) * rowb + scol;
-  }
-  f32x16 acc[TL::kTM][TL::kTN];
-  gemm_mainloop<E, BM, BN>(pa, pb, int(rowb / TL::kStage), lds, acc);
-  const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-#pragma unroll
-  for (int tm = 0; tm < TL::kTM; ++tm)
-#pragma unroll
-    for (int tn = 0; tn < TL::kTN; ++tn) {
-      const int col = n0 + wn * TL::kWN + tn * 32 + (lane & 31);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * TL::kWM + tm * 32 + mfma32_row(r, lane);
-        if (row < M && col < N) proj[size_t(row) * N + col] = acc[tm][tn][r];
-      }
-    }
-}
-
-// ------------------------------------------------------------------ SwiGLU difference
-// Rows: compact non-reference tokens Q = b*nr + q.  Columns: Wp order, pairs
-// of 32-column blocks (W1 block, W2 block) of the same d_ff columns.
-template <typename E, int KL>
-__global__ __launch_bounds__(256) void k_swiglu(const char* __restrict__ kv,
-                                                const char* __restrict__ wp,
-                                                const float* __restrict__ proj,
-                                                const int32_t* __restrict__ ref_idx,
-                                                char* __restrict__ dh, int T, int C, int s,
-                                                int nref, int nr, int k, int d_ff, int M,
-                                                int tiles_n) {
-  constexpr int BM = kGemmBM, BN = kGemmBN;
-  using TL = Tile<E, BM, BN>;
-  __shared__ __attribute__((aligned(16))) char lds[TL::kLds];
-  const int N = 2 * d_ff;
-  const int nt = blockIdx.x % tiles_n, mt = blockIdx.x / tiles_n;
-  const int m0 = mt * BM, n0 = nt * BN;
-  const size_t rowb = size_t(C) * sizeof(E);
-  const int tid = threadIdx.x, srow = tid >> 3, scol = (tid & 7) * 16;
-  const char* pa[TL::kLdA];
-  const char* pb[TL::kLdB];
-#pragma unroll
-  for (int i = 0; i < TL::kLdA; ++i) {
-    const int Q = min(m0 + srow + 32 * i, M - 1);
-    const int b = Q / nr, q = Q % nr;
-    pa[i] = kv + (size_t(b) * T + nonref_pos(q, s)) * rowb + scol;
-  }
-#pragma unroll
-  for (int i = 0; i < TL::kLdB; ++i) {
-    const int n = min(n0 + srow + 32 * i, N - 1);
-    pb[i] = wp + size_t(n) * rowb + scol;
-  }
-  f32x16 acc[TL::kTM][TL::kTN];
-  gemm_mainloop<E, BM, BN>(pa, pb, int(rowb / TL::kStage), lds, acc);
-
-  // Epilogue, row by row: one wave per token row, one lane per d_ff column
-  // of the tile (BN/2 of them), reading U back from LDS.
-  constexpr int LD = BN + 8;
-  static_assert(BN / 2 == 64, "one lane per d_ff column of the tile");
-  static_assert(BM * LD * 4 <= TL::kLds, "U tile must fit in the main-loop LDS");
-  float* u = reinterpret_cast<float*>(lds);
-  acc_to_lds<BM, BN>(acc, u, LD);
-  __syncthreads();
-  const int lane = tid & 63, wave = tid >> 6;
-  const int c = lane;                                  // tile-local d_ff column
-  const int uc1 = 64 * (c >> 5) + (c & 31);            // its x*W1 column in U
-  const int n1 = n0 + uc1, n2 = n1 + 32;
-  const int col = n0 / 2 + c;                          // global d_ff column
-  for (int rr = wave; rr < BM; rr += 4) {
-    const int Q = m0 + rr;
-    if (Q >= M || n1 >= N) break;
-    const int b = Q / nr, q = Q % nr;
-    const int32_t* ri = ref_idx + (size_t(b) * T + nonref_pos(q, s)) * k;
-    // ref_idx rows hold the k_t chosen positions first, then -1 pads.
-    float s1 = 0.0f, s2 = 0.0f;
-    int kt = 0;
-#pragma unroll
-    for (int i = 0; i < KL; ++i) {
-      const int pos = i < k ? ri[i] : -1;
-      if (pos >= 0) {
-        const size_t prow = size_t(b) * nref + pos / s;
-        s1 += proj[prow * N + n1];
-        s2 += proj[prow * N + n2];
-        ++kt;
-      }
-    }
-    const float fk = float(kt);
-    const float u1 = u[rr * LD + uc1], u2 = u[rr * LD + uc1 + 32];
-    const float delta = silu(u1) * u2 - silu(s1 / fk) * (s2 / fk);
-    if constexpr (sizeof(E) == 2) {
-      uint16_t* o = reinterpret_cast<uint16_t*>(dh) + size_t(Q) * 2 * d_ff;
-      const uint16_t hi = f32_to_bf16_rne(delta);
-      o[col] = hi;
-      o[d_ff + col] = f32_to_bf16_rne(delta - bf16_to_f32(hi));
-    } else {
-      reinterpret_cast<float*>(dh)[size_t(Q) * d_ff + col] = delta;
-    }
-  }
-}
-
-// ------------------------------------------------------------------ W3
-template <typename E>
-__global__ __launch_bounds__(256) void k_w3(const char* __restrict__ dh,
-                                            const char* __restrict__ w3p,
-                                            float* __restrict__ zc, int K, int M, int N,
-                                            int tiles_n) {
-  constexpr int BM = kGemmBM, BN = kGemmBN;
-  using TL = Tile<E, BM, BN>;
-  __shared__ __attribute__((aligned(16))) char lds[TL::kLds];
-  const int nt = blockIdx.x % tiles_n, mt = blockIdx.x / tiles_n;
-  const int m0 = mt * BM, n0 = nt * BN;
-  const size_t rowb = size_t(K) * sizeof(E);
-  const int tid = threadIdx.x, srow = tid >> 3, scol = (tid & 7) * 16;
-  const char* pa[TL::kLdA];
-  const char* pb[TL::kLdB];
-#pragma unroll
-  for (int i = 0; i < TL::kLdA; ++i) pa[i] = dh + size_t(min(m0 + srow + 32 * i, M - 1)) * rowb + scol;
-#pragma unroll
-  for (int i = 0; i < TL::kLdB; ++i) pb[i] = w3p + size_t(min(n0 + srow + 32 * i, N - 1)) * rowb + scol;
-  f32x16 acc[TL::kTM][TL::kTN];
-  gemm_mainloop<E, BM, BN>(pa, pb, int(rowb / TL::kStage), lds, acc);
-  const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-#pragma unroll
-  for (int tm = 0; tm < TL::kTM; ++tm)
-#pragma unroll
-    for (int tn = 0; tn < TL::kTN; ++tn) {
-      const int col = n0 + wn * TL::kWN + tn * 32 + (lane & 31);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * TL::kWM + tm * 32 + mfma32_row(r, lane);
-        if (row < M && col < N) zc[size_t(row) * N + col] = acc[tm][tn][r];
-      }
-    }
-}
-
 // ------------------------------------------------------------------ quantiser
 // Lane-to-lane exchange inside groups of G8 lanes (8 latent values per lane).
 __device__ __forceinline__ float dpp_xor1(float x) {
@@ -421,16 +132,431 @@ __device__ __forceinline__ void group_minmax(float& mn, float& mx) {
   if constexpr (G8 >= 8) { mn = fminf(mn, swz_xor4(mn)); mx = fmaxf(mx, swz_xor4(mx)); }
 }
 
-// One wave covers 512 consecutive latent values (whole groups, since g
-// divides 512); every lane owns 8 consecutive values of one group.
+// Quantise the 8 consecutive latent values a lane owns ([RKV] §2.4); the
+// G8 lanes of a group must all call it together.  Returns the packed codes;
+// Delta_h and m_h as fp16 bits.  Integer decisions are taken in fp32:
+// Delta = (max - min) / (2^b - 1), q = clamp(rint((z - m_h) / Delta_h)),
+// q = 0 when Delta_h == 0 (a constant group keeps m_h, no division).
 template <int BITS, int G8>
-__global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ z, int64_t rows,
-                                                  int T, int s, int nr, int d_c,
+__device__ __forceinline__ uint32_t quant8(const float (&v)[8], uint16_t& dh_bits,
+                                           uint16_t& mh_bits) {
+  constexpr float kLevels = float((1 << BITS) - 1);
+  float mn = v[0], mx = v[0];
+#pragma unroll
+  for (int e = 1; e < 8; ++e) { mn = fminf(mn, v[e]); mx = fmaxf(mx, v[e]); }
+  group_minmax<G8>(mn, mx);
+  const float delta = (mx - mn) / kLevels;
+  dh_bits = f32_to_f16_bits(delta);
+  mh_bits = f32_to_f16_bits(mn);
+  const float dh = f16_bits_to_f32(dh_bits), mh = f16_bits_to_f32(mh_bits);
+  uint32_t word = 0;
+  if (dh != 0.0f) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float t = rintf((v[e] - mh) / dh);
+      word |= uint32_t(fminf(fmaxf(t, 0.0f), kLevels)) << (BITS * e);
+    }
+  }
+  return word;
+}
+
+template <int BITS>
+__device__ __forceinline__ void store_codes(uint8_t* codes, int64_t unit, uint32_t word) {
+  if constexpr (BITS == 4)
+    *reinterpret_cast<uint32_t*>(codes + unit * 4) = word;
+  else
+    *reinterpret_cast<uint16_t*>(codes + unit * 2) = uint16_t(word);
+}
+
+// ------------------------------------------------------------------ retrieval
+// One workgroup: kDistRefs references (chunk c) x kDistTok non-reference
+// tokens (tile tt) of sequence b.  Writes, per token, the KL best (d', j) of
+// the chunk restricted to the causal pool (j*s < position).
+template <typename E, int KL>
+__global__ __launch_bounds__(256) void k_dist_topk(const char* __restrict__ kv,
+                                                   const float* __restrict__ ysq,
+                                                   float2* __restrict__ part, int B, int T,
+                                                   int C, int s, int nref, int nr,
+                                                   int n_chunks, int n_tt) {
+  constexpr int BM = kDistRefs, BN = kDistTok;
+  using TL = Tile<E, BM, BN>;   // wave-tile geometry (same for both main loops)
+  constexpr int LD = kEpiLd(BN);
+  constexpr int kMain = mainloop_lds<E, BM, BN, kSB, kDistNS>();
+  constexpr int kStaged = kMain > BM * LD * 4 ? kMain : BM * LD * 4;
+  __shared__ __attribute__((aligned(1024))) char lds[kStaged + BM * 4];
+  float* ysq_l = reinterpret_cast<float*>(lds + kStaged);
+  const int item = blockIdx.x;
+  const int c = item % n_chunks;
+  const int rest = item / n_chunks;
+  const int tt = rest % n_tt, b = rest / n_tt;
+  const int n0 = tt * BN;
+  const int plast = nonref_pos(min(n0 + BN, nr) - 1, s);
+  const int npool_max = (plast + s - 1) / s;
+  const int m0 = c * BM;
+  if (m0 >= npool_max) return;  // chunk entirely after every token of the tile
+
+  const size_t rowb = size_t(C) * sizeof(E);
+  const char* base = kv + size_t(b) * T * rowb;
+  const int tid = threadIdx.x;
+  for (int r = tid; r < BM; r += 256) ysq_l[r] = ysq[size_t(b) * nref + min(m0 + r, nref - 1)];
+  auto rowA = [&](int r) { return base + size_t(min(m0 + r, nref - 1)) * s * rowb; };
+  auto rowB = [&](int r) { return base + size_t(nonref_pos(min(n0 + r, nr - 1), s)) * rowb; };
+  f32x16 acc[TL::kTM][TL::kTN];
+  tile_product<E, BM, BN, kSB, kDistNS>(rowA, rowB, int(rowb), lds, acc);
+
+  // Stage the tile of dot products; then one thread per token scans the
+  // chunk's references in order, keeping the KL best (d', j).
+  float* dot = reinterpret_cast<float*>(lds);
+  acc_to_lds<BM, BN>(acc, dot, LD);
+  __syncthreads();
+  static_assert(BN == 256, "one thread per token of the tile");
+  {
+    const int t = tid, q = n0 + t;
+    // references j < ceil(position / s) are in the pool of the token at q;
+    // the scan runs to the tile's largest pool (uniform) and masks the rest
+    const int lim = q < nr ? min((nonref_pos(q, s) + s - 1) / s - m0, BM) : 0;
+    const int lim_all = min(npool_max - m0, BM);
+    float bd[KL];
+    int bi[KL];
+#pragma unroll
+    for (int i = 0; i < KL; ++i) { bd[i] = __builtin_inff(); bi[i] = 0x7fffffff; }
+    int jl = 0;
+    for (; jl + 4 <= lim_all; jl += 4) {
+      float dd[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) dd[u] = ysq_l[jl + u] - 2.0f * dot[(jl + u) * LD + t];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        topk_push<KL>(bd, bi, jl + u < lim ? dd[u] : __builtin_inff(), m0 + jl + u);
+    }
+    for (; jl < lim_all; ++jl) {
+      const float d = ysq_l[jl] - 2.0f * dot[jl * LD + t];
+      topk_push<KL>(bd, bi, jl < lim ? d : __builtin_inff(), m0 + jl);
+    }
+    if (q < nr) {
+      float2* out = part + ((size_t(b) * n_chunks + c) * nr + q) * KL;
+#pragma unroll
+      for (int i = 0; i < KL; ++i) out[i] = make_float2(bd[i], __int_as_float(bi[i]));
+    }
+  }
+}
+
+// Per token: merge the chunk lists, keep k_t = min(k, ceil(t/s)) references
+// ([RKV] §2.1), write their positions in ascending order, -1 pads.  Chunks
+// are merged in increasing order, each list sorted by (d, j), so every
+// candidate has a larger j than the kept pairs of equal d it meets.
+// Reference tokens get an all -1 row and, when a record is given, an all-zero
+// record: references are stored as they are ([RKV] §2.4).
+template <int KL>
+__global__ __launch_bounds__(256) void k_topk_merge(const float2* __restrict__ part,
+                                                    int32_t* __restrict__ ref_idx, int B, int T,
+                                                    int s, int k, int nr, int n_chunks, int d_c,
+                                                    int g, int bits, uint8_t* __restrict__ codes,
+                                                    uint16_t* __restrict__ scale,
+                                                    uint16_t* __restrict__ zmin,
+                                                    float* __restrict__ z) {
+  const long gid = long(blockIdx.x) * 256 + threadIdx.x;
+  if (gid >= long(B) * T) return;
+  const int b = int(gid / T), t = int(gid % T);
+  int32_t* out = ref_idx + gid * k;
+  if (t % s == 0) {
+    for (int i = 0; i < k; ++i) out[i] = -1;
+    if (codes) {
+      const int cb = d_c * bits / 8, ng = d_c / g;
+      for (int i = 0; i < cb; i += 4) *reinterpret_cast<uint32_t*>(codes + gid * cb + i) = 0u;
+      for (int i = 0; i < ng; ++i) { scale[gid * ng + i] = 0; zmin[gid * ng + i] = 0; }
+      if (z)
+        for (int i = 0; i < d_c; i += 4)
+          *reinterpret_cast<float4*>(z + gid * d_c + i) = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    return;
+  }
+  const int q = t - t / s - 1;
+  const int npool = (t + s - 1) / s;
+  const int kt = min(k, npool);
+  const int nch = (npool + kDistRefs - 1) / kDistRefs;
+  float bd[KL];
+  int bi[KL];
+#pragma unroll
+  for (int i = 0; i < KL; ++i) { bd[i] = __builtin_inff(); bi[i] = 0x7fffffff; }
+  const float2* p = part + (size_t(b) * n_chunks * nr + q) * KL;
+  const size_t cstride = size_t(nr) * KL;
+  int c = 0;
+  for (; c + 2 <= nch; c += 2) {  // two chunks' loads in flight
+    float2 v0[KL], v1[KL];
+#pragma unroll
+    for (int i = 0; i < KL; ++i) { v0[i] = p[c * cstride + i]; v1[i] = p[(c + 1) * cstride + i]; }
+#pragma unroll
+    for (int i = 0; i < KL; ++i) topk_push<KL>(bd, bi, v0[i].x, __float_as_int(v0[i].y));
+#pragma unroll
+    for (int i = 0; i < KL; ++i) topk_push<KL>(bd, bi, v1[i].x, __float_as_int(v1[i].y));
+  }
+  if (c < nch) {
+#pragma unroll
+    for (int i = 0; i < KL; ++i) {
+      const float2 v = p[c * cstride + i];
+      topk_push<KL>(bd, bi, v.x, __float_as_int(v.y));
+    }
+  }
+  int sel[KL];
+#pragma unroll
+  for (int i = 0; i < KL; ++i) sel[i] = i < kt ? bi[i] : 0x7fffffff;
+#pragma unroll
+  for (int i = 1; i < KL; ++i)
+#pragma unroll
+    for (int j = i; j > 0; --j) {
+      const int a = sel[j - 1], c2 = sel[j];
+      sel[j - 1] = min(a, c2);
+      sel[j] = max(a, c2);
+    }
+#pragma unroll
+  for (int i = 0; i < KL; ++i)
+    if (i < k) out[i] = i < kt ? sel[i] * s : -1;
+}
+
+// ------------------------------------------------------------------ reference projection
+template <typename E>
+__global__ __launch_bounds__(256) void k_ref_proj(const char* __restrict__ kv,
+                                                  const char* __restrict__ wp,
+                                                  float* __restrict__ proj, int T, int C, int s,
+                                                  int nref, int M, int N, int tiles_m) {
+  constexpr int BM = kProjBM, BN = kProjBN;
+  using TL = Tile<E, BM, BN>;
+  __shared__ __attribute__((aligned(1024))) char lds[mainloop_lds<E, BM, BN, kSB, kProjNS>()];
+  const int mt = blockIdx.x % tiles_m, nt = blockIdx.x / tiles_m;
+  const int m0 = mt * BM, n0 = nt * BN;
+  const size_t rowb = size_t(C) * sizeof(E);
+  const int tid = threadIdx.x;
+  auto rowA = [&](int r) {
+    const int g = min(m0 + r, M - 1);
+    return kv + (size_t(g / nref) * T + size_t(g % nref) * s) * rowb;
+  };
+  auto rowB = [&](int r) { return wp + size_t(min(n0 + r, N - 1)) * rowb; };
+  f32x16 acc[TL::kTM][TL::kTN];
+  tile_product<E, BM, BN, kSB, kProjNS>(rowA, rowB, int(rowb), lds, acc);
+  const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int tm = 0; tm < TL::kTM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < TL::kTN; ++tn) {
+      const int col = n0 + wn * TL::kWN + tn * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * TL::kWM + tm * 32 + mfma32_row(r, lane);
+        if (row < M && col < N) proj[size_t(row) * N + col] = acc[tm][tn][r];
+      }
+    }
+}
+
+// ------------------------------------------------------------------ SwiGLU difference
+// Rows: compact non-reference tokens Q = b*nr + q.  Columns: Wp order, pairs
+// of 32-column blocks (W1 block, W2 block) of the same d_ff columns.
+// Epilogue: delta_h = Swish(u1)*u2 - Swish(mean u1)*(mean u2), where the
+// means run over the rows of P of the token's references.
+__device__ __forceinline__ float silu_fast(float x) {
+  // x * sigmoid(x) with the hardware exp2 and reciprocal (about 1e-7
+  // relative, far inside the latent tolerance)
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504f * x));
+}
+
+template <typename E, int KL>
+__global__ __launch_bounds__(256) void k_swiglu(const char* __restrict__ kv,
+                                                const char* __restrict__ wp,
+                                                const float* __restrict__ proj,
+                                                const int32_t* __restrict__ ref_idx,
+                                                char* __restrict__ dh, int T, int C, int s,
+                                                int nref, int nr, int k, int d_ff, int M,
+                                                int tiles_n) {
+  constexpr int BM = kSwBM, BN = kSwBN;
+  using TL = Tile<E, BM, BN>;
+  constexpr int LD = kEpiLd(BN);
+  constexpr int HALF = BM / 2;
+  constexpr int kMain = mainloop_lds<E, BM, BN, kSB, kSwNS>();
+  constexpr int kStaged = kMain > HALF * LD * 4 ? kMain : HALF * LD * 4;
+  __shared__ __attribute__((aligned(1024))) char lds[kStaged + BM * KL * 4];
+  int* prow_lds = reinterpret_cast<int*>(lds + kStaged);   // [BM][KL] rows of P, -1 = none
+  const int N = 2 * d_ff;
+  // column tile fastest: the dispatcher deals consecutive workgroups to the
+  // 8 XCDs in turn, so with 8 (or 4, 2) column tiles each XCD keeps to its
+  // own column tiles and its L2 holds their slices of Wp and of P
+  const int nt = blockIdx.x % tiles_n, mt = blockIdx.x / tiles_n;
+  const int m0 = mt * BM, n0 = nt * BN;
+  const size_t rowb = size_t(C) * sizeof(E);
+  const int tid = threadIdx.x;
+  // the rows of P each token of the tile needs (read back after the main
+  // loop, whose barriers publish them)
+  for (int r = tid; r < BM; r += 256) {
+    const int Q = m0 + r;
+    int pr[KL];
+#pragma unroll
+    for (int i = 0; i < KL; ++i) pr[i] = -1;
+    if (Q < M) {
+      const int b = Q / nr, q = Q % nr;
+      const int32_t* ri = ref_idx + (size_t(b) * T + nonref_pos(q, s)) * k;
+#pragma unroll
+      for (int i = 0; i < KL; ++i) {
+        const int pos = i < k ? ri[i] : -1;
+        pr[i] = pos >= 0 ? b * nref + pos / s : -1;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < KL; ++i) prow_lds[r * KL + i] = pr[i];
+  }
+  auto rowA = [&](int r) {
+    const int Q = min(m0 + r, M - 1);
+    return kv + (size_t(Q / nr) * T + nonref_pos(Q % nr, s)) * rowb;
+  };
+  auto rowB = [&](int r) { return wp + size_t(min(n0 + r, N - 1)) * rowb; };
+  f32x16 acc[TL::kTM][TL::kTN];
+  tile_product<E, BM, BN, kSB, kSwNS>(rowA, rowB, int(rowb), lds, acc);
+
+  // Epilogue in two halves of BM/2 rows staged through LDS.  A wave takes
+  // two rows at a time (one per half-wave); lane lc of a half-wave owns d_ff
+  // columns 4*lc .. 4*lc+3 of the tile, whose x*W1 values are 4 contiguous
+  // columns of U (x*W2 32 columns further), so P is read 16 bytes at a time.
+  static_assert(BN / 2 == 128, "32 lanes x 4 d_ff columns per row");
+  float* u = reinterpret_cast<float*>(lds);
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lc = lane & 31, hw = lane >> 5;
+  const int uc = 64 * (lc >> 3) + 4 * (lc & 7);        // x*W1 column (of 4) in U
+  const bool colv = n0 + uc < N;                       // all 4 or none
+  const int col = n0 / 2 + 4 * lc;                     // global d_ff column (of 4)
+  constexpr int RB = 8 / KL;                           // row steps whose loads fly together
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  for (int half = 0; half < 2; ++half) {
+    acc_to_lds<BM, BN>(acc, u, LD, half);
+    __syncthreads();
+    for (int it = 0; it < HALF / 8; it += RB) {
+      f4 p1[RB][KL], p2[RB][KL];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int rl = 8 * (it + rb) + 2 * wave + hw;   // row within the half
+        const int rt = half * HALF + rl;                 // row within the tile
+#pragma unroll
+        for (int i = 0; i < KL; ++i) {
+          const int pr = m0 + rt < M ? prow_lds[rt * KL + i] : -1;
+          const bool ok = pr >= 0 && colv;
+          const f4* src = reinterpret_cast<const f4*>(proj + size_t(ok ? pr : 0) * N + (ok ? n0 + uc : 0));
+          const f4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+          p1[rb][i] = ok ? src[0] : zero;
+          p2[rb][i] = ok ? src[8] : zero;              // +32 floats: the x*W2 column
+        }
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int rl = 8 * (it + rb) + 2 * wave + hw;
+        const int rt = half * HALF + rl;
+        const int Q = m0 + rt;
+        if (Q >= M || !colv) continue;
+        int kt = 0;
+#pragma unroll
+        for (int i = 0; i < KL; ++i) kt += prow_lds[rt * KL + i] >= 0;
+        const float inv = 1.0f / float(kt);
+        f4 s1 = p1[rb][0], s2 = p2[rb][0];
+#pragma unroll
+        for (int i = 1; i < KL; ++i) { s1 += p1[rb][i]; s2 += p2[rb][i]; }
+        const f4 u1 = *reinterpret_cast<const f4*>(u + rl * LD + uc);
+        const f4 u2 = *reinterpret_cast<const f4*>(u + rl * LD + uc + 32);
+        float dl[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          dl[e] = silu_fast(u1[e]) * u2[e] - silu_fast(s1[e] * inv) * (s2[e] * inv);
+        if constexpr (sizeof(E) == 2) {
+          uint16_t* o = reinterpret_cast<uint16_t*>(dh) + size_t(Q) * 2 * d_ff;
+          uint16_t hi[4], lo[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            hi[e] = f32_to_bf16_rne(dl[e]);
+            lo[e] = f32_to_bf16_rne(dl[e] - bf16_to_f32(hi[e]));
+          }
+          *reinterpret_cast<uint2*>(o + col) =
+              make_uint2(hi[0] | (uint32_t(hi[1]) << 16), hi[2] | (uint32_t(hi[3]) << 16));
+          *reinterpret_cast<uint2*>(o + d_ff + col) =
+              make_uint2(lo[0] | (uint32_t(lo[1]) << 16), lo[2] | (uint32_t(lo[3]) << 16));
+        } else {
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(dh) + size_t(Q) * d_ff + col) =
+              make_float4(dl[0], dl[1], dl[2], dl[3]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ W3 + quantiser
+// z = delta_h W3 for a tile of kW3BM non-reference tokens x kW3BN latent
+// columns, then the group quantiser on the tile ([RKV] §2.4), writing the
+// token's record (and z, if asked) at its place in [B][T].
+template <typename E, int BITS, int G8>
+__global__ __launch_bounds__(256) void k_w3_quant(const char* __restrict__ dh,
+                                                  const char* __restrict__ w3p, int K, int M,
+                                                  int N, int tiles_m, int T, int s, int nr,
                                                   uint8_t* __restrict__ codes,
                                                   uint16_t* __restrict__ scale,
                                                   uint16_t* __restrict__ zmin,
-                                                  float* __restrict__ zout) {
-  constexpr float kLevels = float((1 << BITS) - 1);
+                                                  float* __restrict__ z) {
+  constexpr int BM = kW3BM, BN = kW3BN;
+  using TL = Tile<E, BM, BN>;
+  constexpr int LD = kEpiLd(BN);
+  constexpr int HALF = BM / 2;
+  constexpr int kMain = mainloop_lds<E, BM, BN, kSB, kW3NS>();
+  constexpr int kLdsBytes = kMain > HALF * LD * 4 ? kMain : HALF * LD * 4;
+  __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
+  const int mt = blockIdx.x % tiles_m, nt = blockIdx.x / tiles_m;
+  const int m0 = mt * BM, n0 = nt * BN;
+  const size_t rowb = size_t(K) * sizeof(E);
+  const int tid = threadIdx.x;
+  auto rowA = [&](int r) { return dh + size_t(min(m0 + r, M - 1)) * rowb; };
+  auto rowB = [&](int r) { return w3p + size_t(min(n0 + r, N - 1)) * rowb; };
+  f32x16 acc[TL::kTM][TL::kTN];
+  tile_product<E, BM, BN, kSB, kW3NS>(rowA, rowB, int(rowb), lds, acc);
+  float* zt = reinterpret_cast<float*>(lds);
+  // 8 latent values per lane; G8 consecutive lanes hold one group (groups
+  // never straddle a row or the edge N: g divides both BN and d_c)
+  constexpr int kChunks = BN / 8;
+  const int d_c = N;
+  for (int half = 0; half < 2; ++half) {
+    acc_to_lds<BM, BN>(acc, zt, LD, half);
+    __syncthreads();
+    for (int i = 0; i < HALF * kChunks / 256; ++i) {
+      const int unit = i * 256 + tid;
+      const int row = unit / kChunks, ch = unit % kChunks;
+      const int Q = m0 + half * HALF + row, col = n0 + ch * 8;
+      const bool act = Q < M && col < N;
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = zt[row * LD + ch * 8 + e];
+      uint16_t dhb, mhb;
+      const uint32_t word = quant8<BITS, G8>(v, dhb, mhb);
+      if (act) {
+        const int bq = Q / nr, q = Q % nr;
+        const int64_t rec = int64_t(bq) * T + nonref_pos(q, s);   // record row b*T + t
+        const int64_t u = (rec * d_c + col) / 8;                    // flat 8-value unit
+        store_codes<BITS>(codes, u, word);
+        if ((tid % G8) == 0) {
+          const int64_t grp = (rec * d_c + col) / (8 * G8);
+          scale[grp] = dhb;
+          zmin[grp] = mhb;
+        }
+        if (z) {
+          float* zo = z + rec * d_c + col;
+          *reinterpret_cast<float4*>(zo) = make_float4(v[0], v[1], v[2], v[3]);
+          *reinterpret_cast<float4*>(zo + 4) = make_float4(v[4], v[5], v[6], v[7]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Stand-alone quantiser (stepwise export): rows of z map one to one onto the
+// records.  One wave covers 512 consecutive latent values (whole groups,
+// since g divides 512); every lane owns 8 consecutive values of one group.
+template <int BITS, int G8>
+__global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ z, int64_t rows,
+                                                  int d_c, uint8_t* __restrict__ codes,
+                                                  uint16_t* __restrict__ scale,
+                                                  uint16_t* __restrict__ zmin) {
   const int lane = threadIdx.x & 63;
   const int64_t units = rows * (d_c / 8);
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
@@ -438,57 +564,23 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ z, i
        base += stride) {
     const int64_t u = base + lane;
     const bool act = u < units;
-    const int64_t f = act ? u * 8 : 0;
-    const int64_t R = f / d_c;
-    const int o = int(f - R * d_c);
-    bool have = act;
-    int64_t srow = R;
-    if (s >= 1) {  // encode layout: reference rows (t % s == 0) store zeros
-      const int t = int(R % T);
-      have = have && (t % s) != 0;
-      srow = (R / T) * nr + (t - t / s - 1);
-    }
     float v[8];
-    if (have) {
-      const float4 a = *reinterpret_cast<const float4*>(z + srow * d_c + o);
-      const float4 c = *reinterpret_cast<const float4*>(z + srow * d_c + o + 4);
+    if (act) {
+      const float4 a = *reinterpret_cast<const float4*>(z + u * 8);
+      const float4 c = *reinterpret_cast<const float4*>(z + u * 8 + 4);
       v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
       v[4] = c.x; v[5] = c.y; v[6] = c.z; v[7] = c.w;
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = 0.0f;
     }
-    float mn = v[0], mx = v[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) { mn = fminf(mn, v[e]); mx = fmaxf(mx, v[e]); }
-    group_minmax<G8>(mn, mx);
-    const float delta = (mx - mn) / kLevels;
-    const uint16_t dh_bits = f32_to_f16_bits(delta);
-    const uint16_t mh_bits = f32_to_f16_bits(mn);
-    const float dh = f16_bits_to_f32(dh_bits), mh = f16_bits_to_f32(mh_bits);
-    uint32_t word = 0;
-    if (dh != 0.0f) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float t = rintf((v[e] - mh) / dh);
-        const uint32_t qv = uint32_t(fminf(fmaxf(t, 0.0f), kLevels));
-        word |= qv << (BITS * e);
-      }
-    }
+    uint16_t dhb, mhb;
+    const uint32_t word = quant8<BITS, G8>(v, dhb, mhb);
     if (act) {
-      if constexpr (BITS == 4) {
-        *reinterpret_cast<uint32_t*>(codes + u * 4) = word;
-      } else {
-        *reinterpret_cast<uint16_t*>(codes + u * 2) = uint16_t(word);
-      }
+      store_codes<BITS>(codes, u, word);
       if ((lane % G8) == 0) {
-        const int64_t grp = u / G8;
-        scale[grp] = dh_bits;
-        zmin[grp] = mh_bits;
-      }
-      if (zout) {
-        *reinterpret_cast<float4*>(zout + f) = make_float4(v[0], v[1], v[2], v[3]);
-        *reinterpret_cast<float4*>(zout + f + 4) = make_float4(v[4], v[5], v[6], v[7]);
+        scale[u / G8] = dhb;
+        zmin[u / G8] = mhb;
       }
     }
   }
@@ -573,7 +665,6 @@ Workspace plan_workspace(const Shape& sh) {
   L.proj = take(size_t(sh.B) * sh.nref * 2 * sh.d_ff * 4);
   L.part = take(size_t(sh.B) * sh.n_chunks * sh.nr * sh.kl * 8);
   L.dh = take(size_t(sh.B) * sh.nr * sh.k3 * sh.esize);
-  L.zc = take(size_t(sh.B) * sh.nr * sh.d_c * 4);
   L.total = off;
   return L;
 }
@@ -629,26 +720,28 @@ hipError_t launch_dist(const Shape& sh, const void* kv, char* ws, const Workspac
 }
 
 hipError_t launch_merge(const Shape& sh, int32_t* ref_idx, char* ws, const Workspace& L,
+                        uint8_t* codes, uint16_t* scale, uint16_t* zmin, float* z,
                         hipStream_t st) {
   const auto* part = reinterpret_cast<const float2*>(ws + L.part);
   const int nb = cdiv(long(sh.B) * sh.T, 256);
-  if (sh.kl == 4)
-    k_topk_merge<4><<<nb, 256, 0, st>>>(part, ref_idx, sh.B, sh.T, sh.s, sh.k, sh.nr, sh.n_chunks);
-  else
-    k_topk_merge<8><<<nb, 256, 0, st>>>(part, ref_idx, sh.B, sh.T, sh.s, sh.k, sh.nr, sh.n_chunks);
+#define RKV_MERGE(KL)                                                                        \
+  k_topk_merge<KL><<<nb, 256, 0, st>>>(part, ref_idx, sh.B, sh.T, sh.s, sh.k, sh.nr,        \
+                                       sh.n_chunks, sh.d_c, sh.g, sh.b, codes, scale, zmin, z)
+  if (sh.kl == 4) RKV_MERGE(4); else RKV_MERGE(8);
+#undef RKV_MERGE
   return hipGetLastError();
 }
 
 hipError_t launch_ref_proj(const Shape& sh, const void* kv, char* ws, const Workspace& L,
                            hipStream_t st) {
   const int M = sh.B * sh.nref, N = 2 * sh.d_ff;
-  const int tn = cdiv(N, kGemmBN), tm = cdiv(M, kGemmBM);
+  const int tn = cdiv(N, kProjBN), tm = cdiv(M, kProjBM);
   const auto* p = static_cast<const char*>(kv);
   auto* proj = reinterpret_cast<float*>(ws + L.proj);
   if (sh.bf16)
-    k_ref_proj<uint16_t><<<tn * tm, 256, 0, st>>>(p, ws + L.wp, proj, sh.T, sh.C, sh.s, sh.nref, M, N, tn);
+    k_ref_proj<uint16_t><<<tn * tm, 256, 0, st>>>(p, ws + L.wp, proj, sh.T, sh.C, sh.s, sh.nref, M, N, tm);
   else
-    k_ref_proj<float><<<tn * tm, 256, 0, st>>>(p, ws + L.wp, proj, sh.T, sh.C, sh.s, sh.nref, M, N, tn);
+    k_ref_proj<float><<<tn * tm, 256, 0, st>>>(p, ws + L.wp, proj, sh.T, sh.C, sh.s, sh.nref, M, N, tm);
   return hipGetLastError();
 }
 
@@ -656,7 +749,7 @@ hipError_t launch_swiglu(const Shape& sh, const void* kv, const int32_t* ref_idx
                          const Workspace& L, hipStream_t st) {
   const int M = sh.B * sh.nr, N = 2 * sh.d_ff;
   if (M == 0) return hipGetLastError();
-  const int tn = cdiv(N, kGemmBN), tm = cdiv(M, kGemmBM);
+  const int tn = cdiv(N, kSwBN), tm = cdiv(M, kSwBM);
   const auto* p = static_cast<const char*>(kv);
   const auto* proj = reinterpret_cast<const float*>(ws + L.proj);
 #define RKV_SW(E, KL)                                                                       \
@@ -668,27 +761,39 @@ hipError_t launch_swiglu(const Shape& sh, const void* kv, const int32_t* ref_idx
   return hipGetLastError();
 }
 
-hipError_t launch_w3(const Shape& sh, char* ws, const Workspace& L, hipStream_t st) {
+hipError_t launch_w3_quant(const Shape& sh, char* ws, const Workspace& L, uint8_t* codes,
+                           uint16_t* scale, uint16_t* zmin, float* z, hipStream_t st) {
   const int M = sh.B * sh.nr, N = sh.d_c;
   if (M == 0) return hipGetLastError();
-  const int tn = cdiv(N, kGemmBN), tm = cdiv(M, kGemmBM);
-  auto* zc = reinterpret_cast<float*>(ws + L.zc);
-  if (sh.bf16)
-    k_w3<uint16_t><<<tn * tm, 256, 0, st>>>(ws + L.dh, ws + L.w3p, zc, sh.k3, M, N, tn);
-  else
-    k_w3<float><<<tn * tm, 256, 0, st>>>(ws + L.dh, ws + L.w3p, zc, sh.k3, M, N, tn);
+  const int tn = cdiv(N, kW3BN), tm = cdiv(M, kW3BM);
+  const char* a = ws + L.dh;
+  const char* w = ws + L.w3p;
+#define RKV_W3(E, BITS, G8)                                                               \
+  k_w3_quant<E, BITS, G8><<<tn * tm, 256, 0, st>>>(a, w, sh.k3, M, N, tm, sh.T, sh.s, sh.nr, \
+                                                   codes, scale, zmin, z)
+#define RKV_W3G(E, BITS)                      \
+  switch (sh.g) {                             \
+    case 8: RKV_W3(E, BITS, 1); break;        \
+    case 16: RKV_W3(E, BITS, 2); break;       \
+    case 32: RKV_W3(E, BITS, 4); break;       \
+    default: RKV_W3(E, BITS, 8); break;       \
+  }
+  if (sh.bf16) {
+    if (sh.b == 4) { RKV_W3G(uint16_t, 4) } else { RKV_W3G(uint16_t, 2) }
+  } else {
+    if (sh.b == 4) { RKV_W3G(float, 4) } else { RKV_W3G(float, 2) }
+  }
+#undef RKV_W3G
+#undef RKV_W3
   return hipGetLastError();
 }
 
-hipError_t launch_quantize(const float* z, int64_t rows, int T, int s, int d_c, int g, int b,
-                           uint8_t* codes, uint16_t* scale, uint16_t* zmin, float* zout,
-                           hipStream_t st) {
+hipError_t launch_quantize(const float* z, int64_t rows, int d_c, int g, int b, uint8_t* codes,
+                           uint16_t* scale, uint16_t* zmin, hipStream_t st) {
   if (rows == 0) return hipGetLastError();
-  const int nr = s >= 1 ? T - (T + s - 1) / s : 0;
   const int64_t units = rows * (d_c / 8);
   const int grid = grid_for(units, 256);
-#define RKV_Q(BITS, G8) \
-  k_quantize<BITS, G8><<<grid, 256, 0, st>>>(z, rows, T, s, nr, d_c, codes, scale, zmin, zout)
+#define RKV_Q(BITS, G8) k_quantize<BITS, G8><<<grid, 256, 0, st>>>(z, rows, d_c, codes, scale, zmin)
 #define RKV_QG(BITS)                        \
   switch (g) {                              \
     case 8: RKV_Q(BITS, 1); break;          \
