@@ -84,6 +84,9 @@ def main():
     ap.add_argument("--workload", default="llama8b_T32k")
     ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-check-mb", type=int, default=0,
+                    help="before the timed region, run one plain device copy of this many MiB "
+                         "(a reference of known size for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -121,6 +124,13 @@ def main():
         RB.encode(p, kv, w1, w2, w3, out, stream)
         RB.dequant_gather(p, out, idx, "bf16", stream, dst=gdst)
 
+    if args.copy_check_mb:
+        src = torch.empty(args.copy_check_mb << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(max(args.warmup, 1)):
         step()
     torch.cuda.synchronize()

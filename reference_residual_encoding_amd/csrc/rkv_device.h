@@ -47,16 +47,19 @@ __device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
 // Branch-free select network (an infinite d never enters).
 template <int KL>
 __device__ __forceinline__ void topk_push(float (&bd)[KL], int (&bi)[KL], float d, int j) {
-  bool c[KL];
+  // compare-and-swap bubble: the smaller pair stays, the larger moves on
+  float x = d;
+  int xj = j;
 #pragma unroll
-  for (int i = 0; i < KL; ++i) c[i] = d < bd[i];
-#pragma unroll
-  for (int i = KL - 1; i > 0; --i) {
-    bd[i] = c[i - 1] ? bd[i - 1] : (c[i] ? d : bd[i]);
-    bi[i] = c[i - 1] ? bi[i - 1] : (c[i] ? j : bi[i]);
+  for (int i = 0; i < KL; ++i) {
+    const bool c = x < bd[i];
+    const float nd = c ? x : bd[i];
+    const int ni = c ? xj : bi[i];
+    x = c ? bd[i] : x;
+    xj = c ? bi[i] : xj;
+    bd[i] = nd;
+    bi[i] = ni;
   }
-  bd[0] = c[0] ? d : bd[0];
-  bi[0] = c[0] ? j : bi[0];
 }
 
 }  // namespace rkv

@@ -147,8 +147,8 @@ __device__ __forceinline__ void gemm_mainloop(const char* (&pa)[BM / 32],
 //    SB bytes of K per row in flight, so a stage is requested NS-1 stages
 //    before it is consumed;
 //  - LDS rows are SB bytes, unpadded; the 16-byte slot of each row is XOR-
-//    swizzled (swz) so the 32 rows a half-wave reads at one K offset hit
-//    distinct banks (the DMA writes 1 KB contiguous per wave instruction,
+//    swizzled (swz) so the rows a half-wave reads at one K offset spread
+//    over the banks (the DMA writes 1 KB contiguous per wave instruction,
 //    so the swizzle is applied on the global side: lane l of a DMA
 //    instruction fetches slot (l % kSlots) ^ swz(row));
 //  - fragments are double-buffered: the next k-step's reads are issued
@@ -172,9 +172,11 @@ struct DmaTile {
   static_assert(kLd * (NS - 2 > 0 ? NS - 2 : 0) <= 31, "vmcnt window");
 };
 
+// (chosen by measurement: SQ_LDS_BANK_CONFLICT reads zero for the fragment
+// reads of both row widths with these two maps)
 template <int SB>
 __device__ __forceinline__ int swz(int r) {
-  if constexpr (SB == 64) return ((r >> 1) ^ (r >> 3)) & 3;
+  if constexpr (SB == 64) return (r >> 2) & 3;
   else return (r ^ (r >> 3)) & 7;
 }
 

@@ -21,7 +21,7 @@ struct Shape {
 
 // Byte offsets of the workspace regions (each 256-byte aligned).
 struct Workspace {
-  size_t wp, w3p, ysq, proj, part, dh, total;
+  size_t wp, w3p, ysq, refs, proj, part, dh, total;
 };
 
 Shape make_shape(int B, int T, int N, int D, int d_ff, int d_c, int k, int g, int b, int s,

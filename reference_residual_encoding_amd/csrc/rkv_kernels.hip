@@ -8,7 +8,7 @@
 //   pack      W1|W2 -> Wp [2 d_ff][C] (columns of W1 and W2 interleaved in
 //             blocks of 32 so one lane holds x*W1 and x*W2 of the same
 //             column), W3 -> W3p [d_c][k3] (K-contiguous rows).
-//   norms     ||kv_j||^2 of every reference.
+//   norms     reference rows copied into a compact block, and ||kv_j||^2.
 //   dist      distance contraction token x reference on the matrix cores,
 //             fused with a running top-KL per token and reference chunk
 //             ([RKV] §2.2 retrieval equation).  Distances are ranked as
@@ -42,11 +42,12 @@ namespace {
 // Workgroup tiles (4 waves in a 2 x 2 grid, each wave a quarter of the
 // tile) and, for bf16, the DMA ring: SB bytes of K per stage, NS stages.
 constexpr int kProjBM = 128, kProjBN = 128, kProjNS = 4;  // reference projection
-constexpr int kSwBM = 256, kSwBN = 256, kSwNS = 2;        // token projection + SwiGLU difference
+constexpr int kSwBM = 256, kSwBN = 128, kSwNS = 3, kSwSB = 64;  // token projection + SwiGLU
+                                                                 // difference, 2 WGs per CU
 constexpr int kW3BM = 256, kW3BN = 256, kW3NS = 2;        // W3 product + quantiser
 constexpr int kDistRefs = 128;                            // references per chunk (tile M)
 constexpr int kDistTok = 256;                             // tokens per tile (tile N)
-constexpr int kDistNS = 2;
+constexpr int kDistNS = 3, kDistSB = 64;                  // two workgroups per CU
 constexpr int kSB = 128;
 constexpr int kEpiLd(int bn) { return bn + 8; }  // padded fp32 row of an LDS-staged tile
 
@@ -79,21 +80,28 @@ __global__ __launch_bounds__(256) void k_transpose_pack(const E* __restrict__ sr
   }
 }
 
-// ------------------------------------------------------------------ norms
+// ------------------------------------------------------------------ references
+// Copy the reference rows (positions j*s of each sequence) into a compact
+// [B*nref][C] block, which the distance and projection contractions stream
+// (the references sit a whole stride apart in kv), and compute ||kv_j||^2.
 template <typename E>
-__global__ __launch_bounds__(256) void k_ref_norms(const char* __restrict__ kv, int B, int T,
-                                                   int C, int s, int nref,
-                                                   float* __restrict__ ysq) {
+__global__ __launch_bounds__(256) void k_ref_gather(const char* __restrict__ kv, int B, int T,
+                                                    int C, int s, int nref,
+                                                    char* __restrict__ refs,
+                                                    float* __restrict__ ysq) {
   const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (wid >= B * nref) return;
   const int b = wid / nref, j = wid % nref;
-  const E* row = reinterpret_cast<const E*>(kv + (size_t(b) * T + size_t(j) * s) * C * sizeof(E));
+  const size_t rowb = size_t(C) * sizeof(E);
+  const char* src = kv + (size_t(b) * T + size_t(j) * s) * rowb;
+  char* dst = refs + size_t(wid) * rowb;
   float acc = 0.0f;
-  for (int c = lane * 8; c < C; c += 512) {
+  for (size_t o = size_t(lane) * 16; o < rowb; o += 64 * 16) {
+    const uint4 w = *reinterpret_cast<const uint4*>(src + o);
+    *reinterpret_cast<uint4*>(dst + o) = w;
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
     if constexpr (sizeof(E) == 2) {
-      const uint4 w = *reinterpret_cast<const uint4*>(row + c);
-      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float lo = __uint_as_float(u[e] << 16), hi = __uint_as_float(u[e] & 0xFFFF0000u);
@@ -101,12 +109,11 @@ __global__ __launch_bounds__(256) void k_ref_norms(const char* __restrict__ kv, 
         acc = fmaf(hi, hi, acc);
       }
     } else {
-      const float4 a = *reinterpret_cast<const float4*>(row + c);
-      const float4 d = *reinterpret_cast<const float4*>(row + c + 4);
-      acc = fmaf(a.x, a.x, acc); acc = fmaf(a.y, a.y, acc);
-      acc = fmaf(a.z, a.z, acc); acc = fmaf(a.w, a.w, acc);
-      acc = fmaf(d.x, d.x, acc); acc = fmaf(d.y, d.y, acc);
-      acc = fmaf(d.z, d.z, acc); acc = fmaf(d.w, d.w, acc);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float f = __uint_as_float(u[e]);
+        acc = fmaf(f, f, acc);
+      }
     }
   }
 #pragma unroll
@@ -173,7 +180,8 @@ __device__ __forceinline__ void store_codes(uint8_t* codes, int64_t unit, uint32
 // tokens (tile tt) of sequence b.  Writes, per token, the KL best (d', j) of
 // the chunk restricted to the causal pool (j*s < position).
 template <typename E, int KL>
-__global__ __launch_bounds__(256) void k_dist_topk(const char* __restrict__ kv,
+__global__ __launch_bounds__(256, 2) void k_dist_topk(const char* __restrict__ kv,
+                                                   const char* __restrict__ refs,
                                                    const float* __restrict__ ysq,
                                                    float2* __restrict__ part, int B, int T,
                                                    int C, int s, int nref, int nr,
@@ -181,63 +189,81 @@ __global__ __launch_bounds__(256) void k_dist_topk(const char* __restrict__ kv,
   constexpr int BM = kDistRefs, BN = kDistTok;
   using TL = Tile<E, BM, BN>;   // wave-tile geometry (same for both main loops)
   constexpr int LD = kEpiLd(BN);
-  constexpr int kMain = mainloop_lds<E, BM, BN, kSB, kDistNS>();
-  constexpr int kStaged = kMain > BM * LD * 4 ? kMain : BM * LD * 4;
+  constexpr int HALF = BM / 2;
+  constexpr int kMain = mainloop_lds<E, BM, BN, kDistSB, kDistNS>();
+  constexpr int kStaged = kMain > HALF * LD * 4 ? kMain : HALF * LD * 4;
   __shared__ __attribute__((aligned(1024))) char lds[kStaged + BM * 4];
   float* ysq_l = reinterpret_cast<float*>(lds + kStaged);
-  const int item = blockIdx.x;
-  const int c = item % n_chunks;
-  const int rest = item / n_chunks;
-  const int tt = rest % n_tt, b = rest / n_tt;
+  // Work items are the causal (token tile, reference chunk) pairs.  The
+  // dispatcher deals workgroups to the 8 XCDs in turn, so workgroup w runs
+  // on XCD w % 8: that XCD takes the token tiles g = x, x+8, x+16, ... and
+  // all of their chunks, one after the other, which keeps a token tile in
+  // its own L2 while the chunks stream past.
+  const int x = blockIdx.x & 7;
+  int l = blockIdx.x >> 3;
+  int g = x, c = -1, npool_max = 0;
+  for (; g < B * n_tt; g += 8) {
+    const int tt_ = g % n_tt;
+    const int pl = nonref_pos(min(tt_ * BN + BN, nr) - 1, s);
+    const int np = (pl + s - 1) / s;
+    const int nch = (np + BM - 1) / BM;
+    if (l < nch) { c = l; npool_max = np; break; }
+    l -= nch;
+  }
+  if (c < 0) return;  // this XCD has no more items
+  const int tt = g % n_tt, b = g / n_tt;
   const int n0 = tt * BN;
-  const int plast = nonref_pos(min(n0 + BN, nr) - 1, s);
-  const int npool_max = (plast + s - 1) / s;
   const int m0 = c * BM;
-  if (m0 >= npool_max) return;  // chunk entirely after every token of the tile
 
   const size_t rowb = size_t(C) * sizeof(E);
   const char* base = kv + size_t(b) * T * rowb;
   const int tid = threadIdx.x;
   for (int r = tid; r < BM; r += 256) ysq_l[r] = ysq[size_t(b) * nref + min(m0 + r, nref - 1)];
-  auto rowA = [&](int r) { return base + size_t(min(m0 + r, nref - 1)) * s * rowb; };
+  const char* rbase = refs + size_t(b) * nref * rowb;
+  auto rowA = [&](int r) { return rbase + size_t(min(m0 + r, nref - 1)) * rowb; };
   auto rowB = [&](int r) { return base + size_t(nonref_pos(min(n0 + r, nr - 1), s)) * rowb; };
   f32x16 acc[TL::kTM][TL::kTN];
-  tile_product<E, BM, BN, kSB, kDistNS>(rowA, rowB, int(rowb), lds, acc);
+  tile_product<E, BM, BN, kDistSB, kDistNS>(rowA, rowB, int(rowb), lds, acc);
 
-  // Stage the tile of dot products; then one thread per token scans the
-  // chunk's references in order, keeping the KL best (d', j).
-  float* dot = reinterpret_cast<float*>(lds);
-  acc_to_lds<BM, BN>(acc, dot, LD);
-  __syncthreads();
+  // Stage the dot products half a chunk at a time; one thread per token
+  // scans the references in increasing order, keeping the KL best (d', j).
   static_assert(BN == 256, "one thread per token of the tile");
-  {
-    const int t = tid, q = n0 + t;
-    // references j < ceil(position / s) are in the pool of the token at q;
-    // the scan runs to the tile's largest pool (uniform) and masks the rest
-    const int lim = q < nr ? min((nonref_pos(q, s) + s - 1) / s - m0, BM) : 0;
-    const int lim_all = min(npool_max - m0, BM);
-    float bd[KL];
-    int bi[KL];
+  float* dot = reinterpret_cast<float*>(lds);
+  const int t = tid, q = n0 + t;
+  // references j < ceil(position / s) are in the pool of the token at q;
+  // the scan runs to the tile's largest pool (uniform) and masks the rest
+  const int lim = q < nr ? (nonref_pos(q, s) + s - 1) / s - m0 : 0;
+  const int lim_all = min(npool_max - m0, BM);
+  float bd[KL];
+  int bi[KL];
 #pragma unroll
-    for (int i = 0; i < KL; ++i) { bd[i] = __builtin_inff(); bi[i] = 0x7fffffff; }
-    int jl = 0;
-    for (; jl + 4 <= lim_all; jl += 4) {
-      float dd[4];
+  for (int i = 0; i < KL; ++i) { bd[i] = __builtin_inff(); bi[i] = 0x7fffffff; }
+  for (int half = 0; half < 2; ++half) {
+    const int j0 = half * HALF;
+    if (j0 < lim_all) {              // uniform: the workgroup skips an empty half
+      acc_to_lds<BM, BN>(acc, dot, LD, half);
+      __syncthreads();
+      const int end = min(lim_all - j0, HALF);
+      int jl = 0;
+      for (; jl + 4 <= end; jl += 4) {
+        float dd[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) dd[u] = ysq_l[jl + u] - 2.0f * dot[(jl + u) * LD + t];
+        for (int u = 0; u < 4; ++u) dd[u] = ysq_l[j0 + jl + u] - 2.0f * dot[(jl + u) * LD + t];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        topk_push<KL>(bd, bi, jl + u < lim ? dd[u] : __builtin_inff(), m0 + jl + u);
+        for (int u = 0; u < 4; ++u)
+          topk_push<KL>(bd, bi, j0 + jl + u < lim ? dd[u] : __builtin_inff(), m0 + j0 + jl + u);
+      }
+      for (; jl < end; ++jl) {
+        const float d = ysq_l[j0 + jl] - 2.0f * dot[jl * LD + t];
+        topk_push<KL>(bd, bi, j0 + jl < lim ? d : __builtin_inff(), m0 + j0 + jl);
+      }
+      __syncthreads();
     }
-    for (; jl < lim_all; ++jl) {
-      const float d = ysq_l[jl] - 2.0f * dot[jl * LD + t];
-      topk_push<KL>(bd, bi, jl < lim ? d : __builtin_inff(), m0 + jl);
-    }
-    if (q < nr) {
-      float2* out = part + ((size_t(b) * n_chunks + c) * nr + q) * KL;
+  }
+  if (q < nr) {
+    float2* out = part + ((size_t(b) * n_chunks + c) * nr + q) * KL;
 #pragma unroll
-      for (int i = 0; i < KL; ++i) out[i] = make_float2(bd[i], __int_as_float(bi[i]));
-    }
+    for (int i = 0; i < KL; ++i) out[i] = make_float2(bd[i], __int_as_float(bi[i]));
   }
 }
 
@@ -316,10 +342,10 @@ __global__ __launch_bounds__(256) void k_topk_merge(const float2* __restrict__ p
 
 // ------------------------------------------------------------------ reference projection
 template <typename E>
-__global__ __launch_bounds__(256) void k_ref_proj(const char* __restrict__ kv,
+__global__ __launch_bounds__(256) void k_ref_proj(const char* __restrict__ refs,
                                                   const char* __restrict__ wp,
-                                                  float* __restrict__ proj, int T, int C, int s,
-                                                  int nref, int M, int N, int tiles_m) {
+                                                  float* __restrict__ proj, int C, int M, int N,
+                                                  int tiles_m) {
   constexpr int BM = kProjBM, BN = kProjBN;
   using TL = Tile<E, BM, BN>;
   __shared__ __attribute__((aligned(1024))) char lds[mainloop_lds<E, BM, BN, kSB, kProjNS>()];
@@ -327,10 +353,7 @@ __global__ __launch_bounds__(256) void k_ref_proj(const char* __restrict__ kv,
   const int m0 = mt * BM, n0 = nt * BN;
   const size_t rowb = size_t(C) * sizeof(E);
   const int tid = threadIdx.x;
-  auto rowA = [&](int r) {
-    const int g = min(m0 + r, M - 1);
-    return kv + (size_t(g / nref) * T + size_t(g % nref) * s) * rowb;
-  };
+  auto rowA = [&](int r) { return refs + size_t(min(m0 + r, M - 1)) * rowb; };
   auto rowB = [&](int r) { return wp + size_t(min(n0 + r, N - 1)) * rowb; };
   f32x16 acc[TL::kTM][TL::kTN];
   tile_product<E, BM, BN, kSB, kProjNS>(rowA, rowB, int(rowb), lds, acc);
@@ -360,7 +383,7 @@ __device__ __forceinline__ float silu_fast(float x) {
 }
 
 template <typename E, int KL>
-__global__ __launch_bounds__(256) void k_swiglu(const char* __restrict__ kv,
+__global__ __launch_bounds__(256, 2) void k_swiglu(const char* __restrict__ kv,
                                                 const char* __restrict__ wp,
                                                 const float* __restrict__ proj,
                                                 const int32_t* __restrict__ ref_idx,
@@ -371,7 +394,7 @@ __global__ __launch_bounds__(256) void k_swiglu(const char* __restrict__ kv,
   using TL = Tile<E, BM, BN>;
   constexpr int LD = kEpiLd(BN);
   constexpr int HALF = BM / 2;
-  constexpr int kMain = mainloop_lds<E, BM, BN, kSB, kSwNS>();
+  constexpr int kMain = mainloop_lds<E, BM, BN, kSwSB, kSwNS>();
   constexpr int kStaged = kMain > HALF * LD * 4 ? kMain : HALF * LD * 4;
   __shared__ __attribute__((aligned(1024))) char lds[kStaged + BM * KL * 4];
   int* prow_lds = reinterpret_cast<int*>(lds + kStaged);   // [BM][KL] rows of P, -1 = none
@@ -408,29 +431,32 @@ __global__ __launch_bounds__(256) void k_swiglu(const char* __restrict__ kv,
   };
   auto rowB = [&](int r) { return wp + size_t(min(n0 + r, N - 1)) * rowb; };
   f32x16 acc[TL::kTM][TL::kTN];
-  tile_product<E, BM, BN, kSB, kSwNS>(rowA, rowB, int(rowb), lds, acc);
+  tile_product<E, BM, BN, kSwSB, kSwNS>(rowA, rowB, int(rowb), lds, acc);
 
-  // Epilogue in two halves of BM/2 rows staged through LDS.  A wave takes
-  // two rows at a time (one per half-wave); lane lc of a half-wave owns d_ff
-  // columns 4*lc .. 4*lc+3 of the tile, whose x*W1 values are 4 contiguous
-  // columns of U (x*W2 32 columns further), so P is read 16 bytes at a time.
-  static_assert(BN / 2 == 128, "32 lanes x 4 d_ff columns per row");
+  // Epilogue in two halves of BM/2 rows staged through LDS.  Lane lc of a
+  // row group owns d_ff columns 4*lc .. 4*lc+3 of the tile, whose x*W1
+  // values are 4 contiguous columns of U (x*W2 32 columns further), so P is
+  // read 16 bytes at a time; a wave covers RPW rows per step.
+  constexpr int LPR = BN / 8;                          // lanes per row
+  constexpr int RPW = 64 / LPR;                        // rows per wave step
+  static_assert(BN % 64 == 0 && LPR <= 64, "whole column pairs per tile");
   float* u = reinterpret_cast<float*>(lds);
   const int lane = tid & 63, wave = tid >> 6;
-  const int lc = lane & 31, hw = lane >> 5;
+  const int lc = lane % LPR, hw = lane / LPR;
   const int uc = 64 * (lc >> 3) + 4 * (lc & 7);        // x*W1 column (of 4) in U
   const bool colv = n0 + uc < N;                       // all 4 or none
   const int col = n0 / 2 + 4 * lc;                     // global d_ff column (of 4)
   constexpr int RB = 8 / KL;                           // row steps whose loads fly together
+  constexpr int STEP = 4 * RPW;                        // rows per workgroup step
   typedef float f4 __attribute__((ext_vector_type(4)));
   for (int half = 0; half < 2; ++half) {
     acc_to_lds<BM, BN>(acc, u, LD, half);
     __syncthreads();
-    for (int it = 0; it < HALF / 8; it += RB) {
+    for (int it = 0; it < HALF / STEP; it += RB) {
       f4 p1[RB][KL], p2[RB][KL];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const int rl = 8 * (it + rb) + 2 * wave + hw;   // row within the half
+        const int rl = STEP * (it + rb) + RPW * wave + hw;   // row within the half
         const int rt = half * HALF + rl;                 // row within the tile
 #pragma unroll
         for (int i = 0; i < KL; ++i) {
@@ -444,7 +470,7 @@ __global__ __launch_bounds__(256) void k_swiglu(const char* __restrict__ kv,
       }
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const int rl = 8 * (it + rb) + 2 * wave + hw;
+        const int rl = STEP * (it + rb) + RPW * wave + hw;
         const int rt = half * HALF + rl;
         const int Q = m0 + rt;
         if (Q >= M || !colv) continue;
@@ -662,6 +688,7 @@ Workspace plan_workspace(const Shape& sh) {
   L.wp = take(size_t(2) * sh.d_ff * sh.C * sh.esize);
   L.w3p = take(size_t(sh.d_c) * sh.k3 * sh.esize);
   L.ysq = take(size_t(sh.B) * sh.nref * 4);
+  L.refs = take(size_t(sh.B) * sh.nref * sh.C * sh.esize);
   L.proj = take(size_t(sh.B) * sh.nref * 2 * sh.d_ff * 4);
   L.part = take(size_t(sh.B) * sh.n_chunks * sh.nr * sh.kl * 8);
   L.dh = take(size_t(sh.B) * sh.nr * sh.k3 * sh.esize);
@@ -697,9 +724,9 @@ hipError_t launch_ref_norms(const Shape& sh, const void* kv, char* ws, const Wor
   auto* y = reinterpret_cast<float*>(ws + L.ysq);
   const auto* p = static_cast<const char*>(kv);
   if (sh.bf16)
-    k_ref_norms<uint16_t><<<cdiv(rows, 4), 256, 0, st>>>(p, sh.B, sh.T, sh.C, sh.s, sh.nref, y);
+    k_ref_gather<uint16_t><<<cdiv(rows, 4), 256, 0, st>>>(p, sh.B, sh.T, sh.C, sh.s, sh.nref, ws + L.refs, y);
   else
-    k_ref_norms<float><<<cdiv(rows, 4), 256, 0, st>>>(p, sh.B, sh.T, sh.C, sh.s, sh.nref, y);
+    k_ref_gather<float><<<cdiv(rows, 4), 256, 0, st>>>(p, sh.B, sh.T, sh.C, sh.s, sh.nref, ws + L.refs, y);
   return hipGetLastError();
 }
 
@@ -710,9 +737,19 @@ hipError_t launch_dist(const Shape& sh, const void* kv, char* ws, const Workspac
   const auto* y = reinterpret_cast<const float*>(ws + L.ysq);
   auto* part = reinterpret_cast<float2*>(ws + L.part);
   const int n_tt = cdiv(sh.nr, kDistTok);
-  const int items = sh.B * n_tt * sh.n_chunks;
+  // per-XCD item counts (same enumeration as the kernel); grid = 8 x max
+  long per_xcd[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int g = 0; g < sh.B * n_tt; ++g) {
+    const int tt = g % n_tt;
+    const int q = std::min(tt * kDistTok + kDistTok, sh.nr) - 1;
+    const int pl = (q / (sh.s - 1)) * sh.s + (q % (sh.s - 1)) + 1;
+    const int np = (pl + sh.s - 1) / sh.s;
+    per_xcd[g & 7] += (np + kDistRefs - 1) / kDistRefs;
+  }
+  const long lmax = *std::max_element(per_xcd, per_xcd + 8);
+  const int items = int(8 * lmax);
 #define RKV_DIST(E, KL) \
-  k_dist_topk<E, KL><<<items, 256, 0, st>>>(p, y, part, sh.B, sh.T, sh.C, sh.s, sh.nref, sh.nr, sh.n_chunks, n_tt)
+  k_dist_topk<E, KL><<<items, 256, 0, st>>>(p, ws + L.refs, y, part, sh.B, sh.T, sh.C, sh.s, sh.nref, sh.nr, sh.n_chunks, n_tt)
   if (sh.bf16) { if (sh.kl == 4) RKV_DIST(uint16_t, 4); else RKV_DIST(uint16_t, 8); }
   else { if (sh.kl == 4) RKV_DIST(float, 4); else RKV_DIST(float, 8); }
 #undef RKV_DIST
@@ -736,12 +773,12 @@ hipError_t launch_ref_proj(const Shape& sh, const void* kv, char* ws, const Work
                            hipStream_t st) {
   const int M = sh.B * sh.nref, N = 2 * sh.d_ff;
   const int tn = cdiv(N, kProjBN), tm = cdiv(M, kProjBM);
-  const auto* p = static_cast<const char*>(kv);
+  (void)kv;
   auto* proj = reinterpret_cast<float*>(ws + L.proj);
   if (sh.bf16)
-    k_ref_proj<uint16_t><<<tn * tm, 256, 0, st>>>(p, ws + L.wp, proj, sh.T, sh.C, sh.s, sh.nref, M, N, tm);
+    k_ref_proj<uint16_t><<<tn * tm, 256, 0, st>>>(ws + L.refs, ws + L.wp, proj, sh.C, M, N, tm);
   else
-    k_ref_proj<float><<<tn * tm, 256, 0, st>>>(p, ws + L.wp, proj, sh.T, sh.C, sh.s, sh.nref, M, N, tm);
+    k_ref_proj<float><<<tn * tm, 256, 0, st>>>(ws + L.refs, ws + L.wp, proj, sh.C, M, N, tm);
   return hipGetLastError();
 }
 
