@@ -66,7 +66,8 @@ typedef struct {
 } rkv_params;
 
 /* GPU-path limits (RKV_ERR_UNSUPPORTED otherwise): C % 64 == 0,
- * d_ff % 32 == 0, d_c % 32 == 0, d_c % g == 0, B*T < 2^31. */
+ * d_ff % 32 == 0, d_ff <= 65536, d_c % 32 == 0, d_c % g == 0, B*T < 2^31,
+ * B*ceil(T/s)*2*d_ff*4 < 2^31 (the reference projections). */
 
 /* Bytes of device workspace rkv_encode / rkv_select need for *p (0 if *p is
  * invalid).  The workspace holds repacked weights, reference projections,
@@ -146,8 +147,8 @@ typedef enum {
   RKV_STAGE_NORMS = 1,   /* reference squared norms                        */
   RKV_STAGE_DIST = 2,    /* distance contraction + per-chunk top-k          */
   RKV_STAGE_MERGE = 3,   /* top-k merge, ref_idx                            */
-  RKV_STAGE_PROJ = 4,    /* reference projection R [W1|W2]                  */
-  RKV_STAGE_SWIGLU = 5,  /* token projection + SwiGLU difference            */
+  RKV_STAGE_PROJ = 4,    /* reference projection P = R [W1|W2]              */
+  RKV_STAGE_SWIGLU = 5,  /* token projection, mean branch, delta_h          */
   RKV_STAGE_W3 = 6,      /* latent z = delta_h W3 + group quantiser         */
   RKV_STAGE_QUANT = 7,   /* stand-alone quantiser (rkv_quantize)            */
   RKV_STAGE_GATHER = 8,  /* gather-dequantise                               */

@@ -42,6 +42,7 @@ EXPORTS = (
 )
 
 STAGES = ("pack", "norms", "dist", "merge", "proj", "swiglu", "w3", "quant", "gather")
+RKV_ABI_VERSION = 1
 
 
 class rkv_params(ctypes.Structure):

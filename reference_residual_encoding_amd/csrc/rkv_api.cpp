@@ -66,8 +66,12 @@ rkv_status check_params(const rkv_params* p) {
   if (C > (1LL << 20)) return fail(RKV_ERR_UNSUPPORTED, "C = 2*N*D too large (%lld)", C);
   if (C % 64 != 0) return fail(RKV_ERR_UNSUPPORTED, "C = 2*N*D must be a multiple of 64 (got %lld)", C);
   if (p->d_ff % 32 != 0) return fail(RKV_ERR_UNSUPPORTED, "d_ff must be a multiple of 32 (got %d)", p->d_ff);
+  if (p->d_ff > 65536) return fail(RKV_ERR_UNSUPPORTED, "d_ff must be at most 65536 (got %d)", p->d_ff);
   if ((long long)p->B * p->T >= (1LL << 31)) return fail(RKV_ERR_UNSUPPORTED, "B*T must be below 2^31");
   if ((long long)p->B * p->T * C >= (1LL << 40)) return fail(RKV_ERR_UNSUPPORTED, "B*T*C too large");
+  const long long nref = (p->T + p->ref_stride - 1) / p->ref_stride;
+  if ((long long)p->B * nref * 2 * p->d_ff * 4 >= (1LL << 31))
+    return fail(RKV_ERR_UNSUPPORTED, "B*ceil(T/s)*2*d_ff*4 (reference projections) must be below 2^31 bytes");
   return RKV_OK;
 }
 

@@ -24,8 +24,9 @@
 //             delta_h = Swish(u1)*u2 - Swish(mean u1)*mean u2.
 //   w3        z = delta_h W3: since W3 is linear, f_c(kv) - f_c(m) equals
 //             (h(kv) - h(m)) W3 ([RKV] §2.3).  bf16 runs feed delta_h as a
-//             hi + lo pair of bf16 (K = 2 d_ff) so the product keeps ~16
-//             mantissa bits of delta_h.  The epilogue runs the per-token
+//             hi + lo pair of bf16 per feature (K = 2 d_ff, the pair at K
+//             positions 2f, 2f + 1, W3 rows duplicated to match) so the
+//             product keeps ~16 mantissa bits of delta_h.  The epilogue runs the per-token
 //             group min-max quantiser ([RKV] §2.4) and writes the record.
 //   (the merge writes the all-zero records of reference tokens)
 // The read side is one kernel: gather-dequantise over an index list.
@@ -55,12 +56,14 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 inline int cdiv(long a, long b) { return int((a + b - 1) / b); }
 
 // ------------------------------------------------------------------ packing
-// dst[map(c) * ld + r (+ dup)] = src[r * cols + c]; map: 0 identity,
-// 1 W1 slot 64*(c/32) + c%32, 2 W2 slot 64*(c/32) + 32 + c%32.
+// dst[map(c) * ld + r] = src[r * cols + c]; map: 0 identity, 1 W1 slot
+// 64*(c/32) + c%32, 2 W2 slot 64*(c/32) + 32 + c%32.  With pair set, each
+// value is written twice, at dst[map(c) * ld + 2r] and [.. + 2r + 1]: the
+// K order of a delta_h row stored as (hi, lo) bf16 pairs.
 template <typename E>
 __global__ __launch_bounds__(256) void k_transpose_pack(const E* __restrict__ src, int rows,
                                                         int cols, E* __restrict__ dst, int ld,
-                                                        int mode, int dup) {
+                                                        int mode, int pair) {
   __shared__ E tile[32][33];
   const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
@@ -74,8 +77,12 @@ __global__ __launch_bounds__(256) void k_transpose_pack(const E* __restrict__ sr
     if (c < cols && r < rows) {
       const int n = mode == 0 ? c : 64 * (c >> 5) + (mode == 2 ? 32 : 0) + (c & 31);
       const E v = tile[tx][i];
-      dst[size_t(n) * ld + r] = v;
-      if (dup) dst[size_t(n) * ld + dup + r] = v;
+      if (pair) {
+        dst[size_t(n) * ld + 2 * r] = v;
+        dst[size_t(n) * ld + 2 * r + 1] = v;
+      } else {
+        dst[size_t(n) * ld + r] = v;
+      }
     }
   }
 }
@@ -371,33 +378,38 @@ __global__ __launch_bounds__(256) void k_ref_proj(const char* __restrict__ refs,
     }
 }
 
-// ------------------------------------------------------------------ SwiGLU difference
-// Rows: compact non-reference tokens Q = b*nr + q.  Columns: Wp order, pairs
-// of 32-column blocks (W1 block, W2 block) of the same d_ff columns.
-// Epilogue: delta_h = Swish(u1)*u2 - Swish(mean u1)*(mean u2), where the
-// means run over the rows of P of the token's references.
+// ------------------------------------------------------------------ Swish
 __device__ __forceinline__ float silu_fast(float x) {
   // x * sigmoid(x) with the hardware exp2 and reciprocal (about 1e-7
   // relative, far inside the latent tolerance)
   return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504f * x));
 }
 
+// ------------------------------------------------------------------ SwiGLU difference
+// U = kv_t [W1|W2] for a tile of kSwBM non-reference tokens x kSwBN columns
+// of Wp, then per (token, d_ff feature f)
+//   delta_h = Swish(u1) * u2 - Swish(mean_j P_j,1) * mean_j P_j,2,
+// where P = R [W1|W2] holds the projected references and j runs over the
+// token's k_t chosen references: m_t [W1|W2] = mean_j kv_j [W1|W2] because
+// the first layer of f_c is linear and bias-free ([RKV] §2.2 mean eq.,
+// §2.3).  delta_h goes to the token's 4-byte slot of f (dh float index
+// Q*d_ff + f): a (hi, lo) bf16 pair for bf16 runs, fp32 otherwise.
 template <typename E, int KL>
 __global__ __launch_bounds__(256, 2) void k_swiglu(const char* __restrict__ kv,
                                                 const char* __restrict__ wp,
                                                 const float* __restrict__ proj,
+                                                uint32_t proj_bytes,
                                                 const int32_t* __restrict__ ref_idx,
                                                 char* __restrict__ dh, int T, int C, int s,
                                                 int nref, int nr, int k, int d_ff, int M,
                                                 int tiles_n) {
   constexpr int BM = kSwBM, BN = kSwBN;
   using TL = Tile<E, BM, BN>;
-  constexpr int LD = kEpiLd(BN);
-  constexpr int HALF = BM / 2;
   constexpr int kMain = mainloop_lds<E, BM, BN, kSwSB, kSwNS>();
-  constexpr int kStaged = kMain > HALF * LD * 4 ? kMain : HALF * LD * 4;
-  __shared__ __attribute__((aligned(1024))) char lds[kStaged + BM * KL * 4];
-  int* prow_lds = reinterpret_cast<int*>(lds + kStaged);   // [BM][KL] rows of P, -1 = none
+  constexpr int kLdh = BN / 2 + 8;                       // padded fp32 row of the staged h tile
+  static_assert(BM * kLdh * 4 <= kMain, "the h tile reuses the main-loop ring");
+  __shared__ __attribute__((aligned(1024))) char lds[kMain + BM * KL * 4];
+  uint32_t* poff_lds = reinterpret_cast<uint32_t*>(lds + kMain);  // [BM][KL] P row byte offsets
   const int N = 2 * d_ff;
   // column tile fastest: the dispatcher deals consecutive workgroups to the
   // 8 XCDs in turn, so with 8 (or 4, 2) column tiles each XCD keeps to its
@@ -406,24 +418,27 @@ __global__ __launch_bounds__(256, 2) void k_swiglu(const char* __restrict__ kv,
   const int m0 = mt * BM, n0 = nt * BN;
   const size_t rowb = size_t(C) * sizeof(E);
   const int tid = threadIdx.x;
-  // the rows of P each token of the tile needs (read back after the main
-  // loop, whose barriers publish them)
+  // Per token of the tile: the byte offsets of its reference rows of P (read
+  // back after the main loop, whose barriers publish them).  A missing
+  // reference gets an offset past the end of P, which the buffer load below
+  // returns as zero.
+  constexpr uint32_t kNone = 0x80000000u;
   for (int r = tid; r < BM; r += 256) {
     const int Q = m0 + r;
-    int pr[KL];
+    uint32_t off[KL];
 #pragma unroll
-    for (int i = 0; i < KL; ++i) pr[i] = -1;
+    for (int i = 0; i < KL; ++i) off[i] = kNone;
     if (Q < M) {
       const int b = Q / nr, q = Q % nr;
       const int32_t* ri = ref_idx + (size_t(b) * T + nonref_pos(q, s)) * k;
 #pragma unroll
       for (int i = 0; i < KL; ++i) {
         const int pos = i < k ? ri[i] : -1;
-        pr[i] = pos >= 0 ? b * nref + pos / s : -1;
+        if (pos >= 0) off[i] = uint32_t(b * nref + pos / s) * uint32_t(N) * 4u;
       }
     }
 #pragma unroll
-    for (int i = 0; i < KL; ++i) prow_lds[r * KL + i] = pr[i];
+    for (int i = 0; i < KL; ++i) poff_lds[r * KL + i] = off[i];
   }
   auto rowA = [&](int r) {
     const int Q = min(m0 + r, M - 1);
@@ -433,79 +448,87 @@ __global__ __launch_bounds__(256, 2) void k_swiglu(const char* __restrict__ kv,
   f32x16 acc[TL::kTM][TL::kTN];
   tile_product<E, BM, BN, kSwSB, kSwNS>(rowA, rowB, int(rowb), lds, acc);
 
-  // Epilogue in two halves of BM/2 rows staged through LDS.  Lane lc of a
-  // row group owns d_ff columns 4*lc .. 4*lc+3 of the tile, whose x*W1
-  // values are 4 contiguous columns of U (x*W2 32 columns further), so P is
-  // read 16 bytes at a time; a wave covers RPW rows per step.
-  constexpr int LPR = BN / 8;                          // lanes per row
-  constexpr int RPW = 64 / LPR;                        // rows per wave step
-  static_assert(BN % 64 == 0 && LPR <= 64, "whole column pairs per tile");
-  float* u = reinterpret_cast<float*>(lds);
-  const int lane = tid & 63, wave = tid >> 6;
-  const int lc = lane % LPR, hw = lane / LPR;
-  const int uc = 64 * (lc >> 3) + 4 * (lc & 7);        // x*W1 column (of 4) in U
-  const bool colv = n0 + uc < N;                       // all 4 or none
-  const int col = n0 / 2 + 4 * lc;                     // global d_ff column (of 4)
-  constexpr int RB = 8 / KL;                           // row steps whose loads fly together
-  constexpr int STEP = 4 * RPW;                        // rows per workgroup step
+  // 1. h(kv) = Swish(u1) * u2 from the accumulators into LDS.  Lane l of
+  // wave (wm, wn) holds, in register r of fragment (i, j), tile row
+  // wm*BM/2 + 32i + mfma32_row(r, l) and Wp row n0 + wn*BN/2 + 32j + l%32.  Wp
+  // interleaves W1 and W2 in blocks of 32, so fragment j = 0 is x*W1 and
+  // j = 1 the x*W2 of the same feature: tile feature wn*32 + l%32.
+  static_assert(TL::kTN == 2 && BN / 2 == 64, "one W1/W2 fragment pair per wave");
+  float* h = reinterpret_cast<float*>(lds);
+  {
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+    for (int i = 0; i < TL::kTM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        h[(wm * (BM / 2) + 32 * i + mfma32_row(r, lane)) * kLdh + wn * 32 + (lane & 31)] =
+            silu_fast(acc[i][0][r]) * acc[i][1][r];
+  }
+  __syncthreads();
+
+  // 2. Four consecutive features of one row per lane: 16 lanes per row, 16
+  // rows per workgroup step.  Feature quad c holds W1 columns
+  // n0 + 64(c/8) + 4(c%8) .. +3 of P and the W2 columns 32 further.  All loads
+  // and stores are unconditional: P and the tile's rows of dh go through
+  // buffer resources (an offset past the end of a range reads zero and
+  // drops a store), which lets the compiler keep the loads in flight.
   typedef float f4 __attribute__((ext_vector_type(4)));
-  for (int half = 0; half < 2; ++half) {
-    acc_to_lds<BM, BN>(acc, u, LD, half);
-    __syncthreads();
-    for (int it = 0; it < HALF / STEP; it += RB) {
-      f4 p1[RB][KL], p2[RB][KL];
+  const int c = tid & 15, row0 = tid >> 4;
+  const bool colv = n0 + 64 * (c >> 3) < N;              // the quad's 64-column group exists
+  const uint32_t pcol = uint32_t(n0 + 64 * (c >> 3) + 4 * (c & 7)) * 4u;
+  const int f = n0 / 2 + 4 * c;
+  const __amdgpu_buffer_rsrc_t prs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(proj), 0, int(proj_bytes), 0x00020000);
+  const int rows = min(M - m0, BM);
+  const __amdgpu_buffer_rsrc_t drs = __builtin_amdgcn_make_buffer_rsrc(
+      dh + size_t(m0) * d_ff * 4, 0, rows * d_ff * 4, 0x00020000);
+  auto ld4 = [&](uint32_t off) {
+    return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(prs, int(off), 0, 0));
+  };
+  constexpr int kRB = KL <= 4 ? 4 : 2;                   // row steps whose loads fly together
+  for (int it = 0; it < BM / 16; it += kRB) {
+    f4 p1[kRB][KL], p2[kRB][KL];
+    int kt[kRB];
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const int rl = STEP * (it + rb) + RPW * wave + hw;   // row within the half
-        const int rt = half * HALF + rl;                 // row within the tile
+    for (int u = 0; u < kRB; ++u) {
+      const uint32_t* po = poff_lds + (16 * (it + u) + row0) * KL;
+      kt[u] = 0;
 #pragma unroll
-        for (int i = 0; i < KL; ++i) {
-          const int pr = m0 + rt < M ? prow_lds[rt * KL + i] : -1;
-          const bool ok = pr >= 0 && colv;
-          const f4* src = reinterpret_cast<const f4*>(proj + size_t(ok ? pr : 0) * N + (ok ? n0 + uc : 0));
-          const f4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-          p1[rb][i] = ok ? src[0] : zero;
-          p2[rb][i] = ok ? src[8] : zero;              // +32 floats: the x*W2 column
-        }
-      }
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const int rl = STEP * (it + rb) + RPW * wave + hw;
-        const int rt = half * HALF + rl;
-        const int Q = m0 + rt;
-        if (Q >= M || !colv) continue;
-        int kt = 0;
-#pragma unroll
-        for (int i = 0; i < KL; ++i) kt += prow_lds[rt * KL + i] >= 0;
-        const float inv = 1.0f / float(kt);
-        f4 s1 = p1[rb][0], s2 = p2[rb][0];
-#pragma unroll
-        for (int i = 1; i < KL; ++i) { s1 += p1[rb][i]; s2 += p2[rb][i]; }
-        const f4 u1 = *reinterpret_cast<const f4*>(u + rl * LD + uc);
-        const f4 u2 = *reinterpret_cast<const f4*>(u + rl * LD + uc + 32);
-        float dl[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          dl[e] = silu_fast(u1[e]) * u2[e] - silu_fast(s1[e] * inv) * (s2[e] * inv);
-        if constexpr (sizeof(E) == 2) {
-          uint16_t* o = reinterpret_cast<uint16_t*>(dh) + size_t(Q) * 2 * d_ff;
-          uint16_t hi[4], lo[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            hi[e] = f32_to_bf16_rne(dl[e]);
-            lo[e] = f32_to_bf16_rne(dl[e] - bf16_to_f32(hi[e]));
-          }
-          *reinterpret_cast<uint2*>(o + col) =
-              make_uint2(hi[0] | (uint32_t(hi[1]) << 16), hi[2] | (uint32_t(hi[3]) << 16));
-          *reinterpret_cast<uint2*>(o + d_ff + col) =
-              make_uint2(lo[0] | (uint32_t(lo[1]) << 16), lo[2] | (uint32_t(lo[3]) << 16));
-        } else {
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(dh) + size_t(Q) * d_ff + col) =
-              make_float4(dl[0], dl[1], dl[2], dl[3]);
-        }
+      for (int q = 0; q < KL; ++q) {
+        const uint32_t o = po[q];
+        const bool ok = o != kNone;
+        kt[u] += ok;
+        const bool go = ok && colv;
+        p1[u][q] = ld4(go ? o + pcol : kNone);
+        p2[u][q] = ld4(go ? o + pcol + 128u : kNone);   // +32 floats: the x*W2 columns
       }
     }
-    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kRB; ++u) {
+      const int rt = 16 * (it + u) + row0;
+      f4 s1 = p1[u][0], s2 = p2[u][0];
+#pragma unroll
+      for (int q = 1; q < KL; ++q) { s1 += p1[u][q]; s2 += p2[u][q]; }
+      const float inv = 1.0f / float(max(kt[u], 1));
+      const f4 hk = *reinterpret_cast<const f4*>(h + rt * kLdh + 4 * c);
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float dl = hk[e] - silu_fast(s1[e] * inv) * (s2[e] * inv);
+        if constexpr (sizeof(E) == 2) {
+          const uint16_t hi = f32_to_bf16_rne(dl);
+          const uint16_t lo = f32_to_bf16_rne(dl - bf16_to_f32(hi));
+          w[e] = hi | (uint32_t(lo) << 16);
+        } else {
+          w[e] = __float_as_uint(dl);
+        }
+      }
+      const u32x4 wv = {w[0], w[1], w[2], w[3]};
+      // a quad past the column edge, or a row past M, lands outside the range
+      const uint32_t so = colv ? uint32_t(rt * d_ff + f) * 4u : kNone;
+      __builtin_amdgcn_raw_buffer_store_b128(wv, drs, int(so), 0, 0);
+    }
   }
 }
 
@@ -701,13 +724,13 @@ hipError_t launch_pack_weights(const Shape& sh, const void* w1, const void* w2, 
   const dim3 blk(256);
   const dim3 g12(cdiv(sh.d_ff, 32), cdiv(sh.C, 32));
   const dim3 g3(cdiv(sh.d_c, 32), cdiv(sh.d_ff, 32));
-  const int dup = sh.bf16 ? sh.d_ff : 0;
+  const int pair = sh.bf16 ? 1 : 0;
   if (sh.bf16) {
     auto* wp = reinterpret_cast<uint16_t*>(ws + L.wp);
     k_transpose_pack<uint16_t><<<g12, blk, 0, st>>>(static_cast<const uint16_t*>(w1), sh.C, sh.d_ff, wp, sh.C, 1, 0);
     k_transpose_pack<uint16_t><<<g12, blk, 0, st>>>(static_cast<const uint16_t*>(w2), sh.C, sh.d_ff, wp, sh.C, 2, 0);
     k_transpose_pack<uint16_t><<<g3, blk, 0, st>>>(static_cast<const uint16_t*>(w3), sh.d_ff, sh.d_c,
-                                                   reinterpret_cast<uint16_t*>(ws + L.w3p), sh.k3, 0, dup);
+                                                   reinterpret_cast<uint16_t*>(ws + L.w3p), sh.k3, 0, pair);
   } else {
     auto* wp = reinterpret_cast<float*>(ws + L.wp);
     k_transpose_pack<float><<<g12, blk, 0, st>>>(static_cast<const float*>(w1), sh.C, sh.d_ff, wp, sh.C, 1, 0);
@@ -789,9 +812,11 @@ hipError_t launch_swiglu(const Shape& sh, const void* kv, const int32_t* ref_idx
   const int tn = cdiv(N, kSwBN), tm = cdiv(M, kSwBM);
   const auto* p = static_cast<const char*>(kv);
   const auto* proj = reinterpret_cast<const float*>(ws + L.proj);
-#define RKV_SW(E, KL)                                                                       \
-  k_swiglu<E, KL><<<tn * tm, 256, 0, st>>>(p, ws + L.wp, proj, ref_idx, ws + L.dh, sh.T, sh.C, \
-                                           sh.s, sh.nref, sh.nr, sh.k, sh.d_ff, M, tn)
+  // P is addressed with 32-bit byte offsets (its size is checked on the host)
+  const uint32_t pbytes = uint32_t(size_t(sh.B) * sh.nref * N * 4);
+#define RKV_SW(E, KL)                                                                        \
+  k_swiglu<E, KL><<<tn * tm, 256, 0, st>>>(p, ws + L.wp, proj, pbytes, ref_idx, ws + L.dh, sh.T, \
+                                           sh.C, sh.s, sh.nref, sh.nr, sh.k, sh.d_ff, M, tn)
   if (sh.bf16) { if (sh.kl == 4) RKV_SW(uint16_t, 4); else RKV_SW(uint16_t, 8); }
   else { if (sh.kl == 4) RKV_SW(float, 4); else RKV_SW(float, 8); }
 #undef RKV_SW

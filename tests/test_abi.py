@@ -27,7 +27,7 @@ def test_library_exports_every_declared_function():
     assert set(declared) == set(R.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert R.rkv_abi_version() == 1
+    assert R.rkv_abi_version() == R.RKV_ABI_VERSION
 
 
 def test_status_strings():
