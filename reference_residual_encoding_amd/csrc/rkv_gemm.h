@@ -1,11 +1,11 @@
 // MFMA main loop shared by every contraction of the encode path.
 //
-// One 256-thread workgroup computes a BM x BN tile of C = A * B^T where every
-// row of A and of B is K-contiguous in HBM (the "NT" form: token rows of kv,
-// packed weight rows, reference rows all have their contraction index
-// innermost).  The four waves form a 2 x 2 grid; wave (wm, wn) owns the
-// (BM/2) x (BN/2) sub-tile as (BM/64) x (BN/64) fragments of 32 x 32 fp32
-// accumulators.
+// One workgroup computes a BM x BN tile of C = A * B^T where every row of A
+// and of B is K-contiguous in HBM (the "NT" form: token rows of kv, packed
+// weight rows, reference rows all have their contraction index innermost).
+// Its waves form a WGM x WGN grid (2 x 2 by default; the bf16 loop also runs
+// 2 x 4); wave (wm, wn) owns the (BM/WGM) x (BN/WGN) sub-tile as fragments of
+// 32 x 32 fp32 accumulators.
 //
 //  - bf16 operands use v_mfma_f32_32x32x16_bf16 (products exact, fp32 sums);
 //    fp32 operands use v_mfma_f32_32x32x2_f32.  Both write the same 32 x 32
@@ -157,15 +157,18 @@ __device__ __forceinline__ void gemm_mainloop(const char* (&pa)[BM / 32],
 //    younger stages stay in flight across the barrier.
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-template <int BM, int BN, int SB, int NS>
+template <int BM, int BN, int SB, int NS, int WGM = 2, int WGN = 2>
 struct DmaTile {
+  static constexpr int kWaves = WGM * WGN;        // wave grid WGM x WGN
+  static constexpr int kThreads = 64 * kWaves;
   static constexpr int kSlots = SB / 16;          // 16-byte slots per LDS row
   static constexpr int kRowsPerKB = 1024 / SB;    // rows per DMA wave instruction
   static constexpr int kStage = (BM + BN) * SB;   // bytes per stage
   static constexpr int kLds = NS * kStage;
-  static constexpr int kWM = BM / 2, kWN = BN / 2, kTM = kWM / 32, kTN = kWN / 32;
+  static constexpr int kWM = BM / WGM, kWN = BN / WGN, kTM = kWM / 32, kTN = kWN / 32;
   static constexpr int kSteps = SB / 32;          // 32x32x16 k-steps per stage
-  static constexpr int kLdA = BM * SB / 4096, kLdB = BN * SB / 4096;  // DMA instr. per wave per stage
+  // DMA instructions per wave per stage
+  static constexpr int kLdA = BM * SB / (1024 * kWaves), kLdB = BN * SB / (1024 * kWaves);
   static constexpr int kLd = kLdA + kLdB;
   static_assert(kSteps % 2 == 0, "fragment double-buffering pairs k-steps");
   static_assert(kLdA >= 1 && kLdB >= 1, "each wave feeds part of A and of B");
@@ -217,13 +220,13 @@ __device__ __forceinline__ void block_barrier() {
 // pa[i] / pb[i] (i < kLdA / kLdB): this lane's source address for DMA
 // instruction i at K stage 0 (row base + dma_slot); rows past the end must
 // point at a valid row.
-template <int BM, int BN, int SB, int NS>
+template <int BM, int BN, int SB, int NS, int WGM = 2, int WGN = 2>
 __device__ __forceinline__ void gemm_mainloop_dma(const char* const* pa, const char* const* pb,
                                                   int KT, char* lds,
-                                                  f32x16 (&acc)[BM / 64][BN / 64]) {
-  using TL = DmaTile<BM, BN, SB, NS>;
+                                                  f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32]) {
+  using TL = DmaTile<BM, BN, SB, NS, WGM, WGN>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
 #pragma unroll
   for (int i = 0; i < TL::kTM; ++i)
 #pragma unroll
@@ -309,23 +312,23 @@ __device__ __forceinline__ void gemm_mainloop_dma(const char* const* pa, const c
   block_barrier();
 }
 
-// Write the accumulators of the waves whose wave-row is `half` (or of every
-// wave when half < 0) to LDS as a row-major fp32 tile with row stride `ld`
-// floats; tile row 0 is the first row of that half (or of the workgroup).
-// With ld % 64 == 8 the two half-waves (rows 4 apart) land on disjoint banks.
-// Callers synchronise before reading it back.
-template <int BM, int BN>
-__device__ __forceinline__ void acc_to_lds(const f32x16 (&acc)[BM / 64][BN / 64], float* tile,
-                                           int ld, int half = -1) {
+// Write the accumulators of the waves whose wave-row is `part` (or of every
+// wave when part < 0) to LDS as a row-major fp32 tile with row stride `ld`
+// floats; tile row 0 is the first row of that wave-row (or of the
+// workgroup).  With ld % 64 == 8 the two half-waves (rows 4 apart) land on
+// disjoint banks.  Callers synchronise before reading it back.
+template <int BM, int BN, int WGM = 2, int WGN = 2>
+__device__ __forceinline__ void acc_to_lds(const f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32],
+                                           float* tile, int ld, int part = -1) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  if (half >= 0 && wm != half) return;
-  const int row0 = half >= 0 ? 0 : wm * (BM / 2);
+  const int wm = wave / WGN, wn = wave % WGN;
+  if (part >= 0 && wm != part) return;
+  const int row0 = part >= 0 ? 0 : wm * (BM / WGM);
 #pragma unroll
-  for (int i = 0; i < BM / 64; ++i)
+  for (int i = 0; i < BM / WGM / 32; ++i)
 #pragma unroll
-    for (int j = 0; j < BN / 64; ++j) {
-      const int col = wn * (BN / 2) + j * 32 + (lane & 31);
+    for (int j = 0; j < BN / WGN / 32; ++j) {
+      const int col = wn * (BN / WGN) + j * 32 + (lane & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         tile[(row0 + i * 32 + mfma32_row(r, lane)) * ld + col] = acc[i][j][r];
@@ -337,16 +340,18 @@ __device__ __forceinline__ void acc_to_lds(const f32x16 (&acc)[BM / 64][BN / 64]
 // (SB bytes of K per stage, NS stages), the fp32 path the register-staged
 // loop.  rowA(r) / rowB(r) return the first byte of tile-local row r
 // (clamped to a valid row); kbytes is the contraction length in bytes.
-template <typename E, int BM, int BN, int SB, int NS>
+template <typename E, int BM, int BN, int SB, int NS, int WGM = 2, int WGN = 2>
 constexpr int mainloop_lds() {
-  return sizeof(E) == 2 ? DmaTile<BM, BN, SB, NS>::kLds : Tile<E, BM, BN>::kLds;
+  return sizeof(E) == 2 ? DmaTile<BM, BN, SB, NS, WGM, WGN>::kLds : Tile<E, BM, BN>::kLds;
 }
 
-template <typename E, int BM, int BN, int SB, int NS, class RowA, class RowB>
+template <typename E, int BM, int BN, int SB, int NS, int WGM = 2, int WGN = 2, class RowA,
+          class RowB>
 __device__ __forceinline__ void tile_product(const RowA& rowA, const RowB& rowB, int kbytes,
-                                             char* lds, f32x16 (&acc)[BM / 64][BN / 64]) {
+                                             char* lds,
+                                             f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32]) {
   if constexpr (sizeof(E) == 2) {
-    using TL = DmaTile<BM, BN, SB, NS>;
+    using TL = DmaTile<BM, BN, SB, NS, WGM, WGN>;
     const char* pa[TL::kLdA];
     const char* pb[TL::kLdB];
 #pragma unroll
@@ -359,8 +364,9 @@ __device__ __forceinline__ void tile_product(const RowA& rowA, const RowB& rowB,
       const int r = dma_row<TL, SB>(i, TL::kLdB);
       pb[i] = rowB(r) + dma_slot<TL, SB>(r);
     }
-    gemm_mainloop_dma<BM, BN, SB, NS>(pa, pb, kbytes / SB, lds, acc);
+    gemm_mainloop_dma<BM, BN, SB, NS, WGM, WGN>(pa, pb, kbytes / SB, lds, acc);
   } else {
+    static_assert(WGM == 2 && WGN == 2, "the fp32 loop runs a 2 x 2 wave grid");
     using TL = Tile<E, BM, BN>;
     const int srow = threadIdx.x >> 3, scol = (threadIdx.x & 7) * 16;
     const char* pa[TL::kLdA];

@@ -43,9 +43,23 @@ namespace {
 // Workgroup tiles (4 waves in a 2 x 2 grid, each wave a quarter of the
 // tile) and, for bf16, the DMA ring: SB bytes of K per stage, NS stages.
 constexpr int kProjBM = 128, kProjBN = 128, kProjNS = 4;  // reference projection
-constexpr int kSwBM = 256, kSwBN = 128, kSwNS = 3, kSwSB = 64;  // token projection + SwiGLU
+// token projection + SwiGLU, and the W3 product + quantiser: bf16 runs use
+// 256 x 256 tiles on 8 waves (2 x 4, one workgroup per CU, a 2-stage ring
+// of 128-byte K slices); fp32 runs keep the 4-wave register-staged loop
+template <typename E> struct SwCfg {
+  static constexpr int BM = 256, BN = 256, SB = 128, NS = 2, WGM = 2, WGN = 4;
+  static constexpr int kThreads = 64 * WGM * WGN;
+};
+template <> struct SwCfg<float> {
+  static constexpr int BM = 256, BN = 128, SB = 128, NS = 2, WGM = 2, WGN = 2;
+  static constexpr int kThreads = 64 * WGM * WGN;
+};
+template <typename E> struct W3Cfg : SwCfg<E> {};
+template <> struct W3Cfg<float> {
+  static constexpr int BM = 256, BN = 256, SB = 128, NS = 2, WGM = 2, WGN = 2;
+  static constexpr int kThreads = 64 * WGM * WGN;
+};
                                                                  // difference, 2 WGs per CU
-constexpr int kW3BM = 256, kW3BN = 256, kW3NS = 2;        // W3 product + quantiser
 constexpr int kDistRefs = 128;                            // references per chunk (tile M)
 constexpr int kDistTok = 256;                             // tokens per tile (tile N)
 constexpr int kDistNS = 3, kDistSB = 64;                  // two workgroups per CU
@@ -395,26 +409,26 @@ __device__ __forceinline__ float silu_fast(float x) {
 // §2.3).  delta_h goes to the token's 4-byte slot of f (dh float index
 // Q*d_ff + f): a (hi, lo) bf16 pair for bf16 runs, fp32 otherwise.
 template <typename E, int KL>
-__global__ __launch_bounds__(256, 2) void k_swiglu(const char* __restrict__ kv,
+__global__ __launch_bounds__(SwCfg<E>::kThreads) void k_swiglu(const char* __restrict__ kv,
                                                 const char* __restrict__ wp,
                                                 const float* __restrict__ proj,
                                                 uint32_t proj_bytes,
                                                 const int32_t* __restrict__ ref_idx,
                                                 char* __restrict__ dh, int T, int C, int s,
-                                                int nref, int nr, int k, int d_ff, int M,
-                                                int tiles_n) {
-  constexpr int BM = kSwBM, BN = kSwBN;
-  using TL = Tile<E, BM, BN>;
-  constexpr int kMain = mainloop_lds<E, BM, BN, kSwSB, kSwNS>();
+                                                int nref, int nr, int k, int d_ff, int M) {
+  using CF = SwCfg<E>;
+  constexpr int BM = CF::BM, BN = CF::BN, WGM = CF::WGM, WGN = CF::WGN, NT = CF::kThreads;
+  constexpr int kMain = mainloop_lds<E, BM, BN, CF::SB, CF::NS, WGM, WGN>();
   constexpr int kLdh = BN / 2 + 8;                       // padded fp32 row of the staged h tile
-  static_assert(BM * kLdh * 4 <= kMain, "the h tile reuses the main-loop ring");
-  __shared__ __attribute__((aligned(1024))) char lds[kMain + BM * KL * 4];
-  uint32_t* poff_lds = reinterpret_cast<uint32_t*>(lds + kMain);  // [BM][KL] P row byte offsets
+  constexpr int kStaged = kMain > BM * kLdh * 4 ? kMain : BM * kLdh * 4;
+  __shared__ __attribute__((aligned(1024))) char lds[kStaged + BM * KL * 4];
+  uint32_t* poff_lds = reinterpret_cast<uint32_t*>(lds + kStaged);  // [BM][KL] P row byte offsets
   const int N = 2 * d_ff;
-  // column tile fastest: the dispatcher deals consecutive workgroups to the
-  // 8 XCDs in turn, so with 8 (or 4, 2) column tiles each XCD keeps to its
-  // own column tiles and its L2 holds their slices of Wp and of P
-  const int nt = blockIdx.x % tiles_n, mt = blockIdx.x / tiles_n;
+  // row tile fastest: all XCDs work through one column tile of Wp at a time,
+  // so every L2 holds that tile's rows of Wp and the columns of P its
+  // epilogue gathers, while each token tile is read once per column tile
+  const int tiles_m = (M + BM - 1) / BM;
+  const int mt = blockIdx.x % tiles_m, nt = blockIdx.x / tiles_m;
   const int m0 = mt * BM, n0 = nt * BN;
   const size_t rowb = size_t(C) * sizeof(E);
   const int tid = threadIdx.x;
@@ -423,7 +437,7 @@ __global__ __launch_bounds__(256, 2) void k_swiglu(const char* __restrict__ kv,
   // reference gets an offset past the end of P, which the buffer load below
   // returns as zero.
   constexpr uint32_t kNone = 0x80000000u;
-  for (int r = tid; r < BM; r += 256) {
+  for (int r = tid; r < BM; r += NT) {
     const int Q = m0 + r;
     uint32_t off[KL];
 #pragma unroll
@@ -445,36 +459,39 @@ __global__ __launch_bounds__(256, 2) void k_swiglu(const char* __restrict__ kv,
     return kv + (size_t(Q / nr) * T + nonref_pos(Q % nr, s)) * rowb;
   };
   auto rowB = [&](int r) { return wp + size_t(min(n0 + r, N - 1)) * rowb; };
-  f32x16 acc[TL::kTM][TL::kTN];
-  tile_product<E, BM, BN, kSwSB, kSwNS>(rowA, rowB, int(rowb), lds, acc);
+  constexpr int kTM = BM / WGM / 32, kTN = BN / WGN / 32;
+  f32x16 acc[kTM][kTN];
+  tile_product<E, BM, BN, CF::SB, CF::NS, WGM, WGN>(rowA, rowB, int(rowb), lds, acc);
 
   // 1. h(kv) = Swish(u1) * u2 from the accumulators into LDS.  Lane l of
   // wave (wm, wn) holds, in register r of fragment (i, j), tile row
-  // wm*BM/2 + 32i + mfma32_row(r, l) and Wp row n0 + wn*BN/2 + 32j + l%32.  Wp
-  // interleaves W1 and W2 in blocks of 32, so fragment j = 0 is x*W1 and
+  // wm*BM/WGM + 32i + mfma32_row(r, l) and Wp row n0 + wn*64 + 32j + l%32.
+  // Wp interleaves W1 and W2 in blocks of 32, so fragment j = 0 is x*W1 and
   // j = 1 the x*W2 of the same feature: tile feature wn*32 + l%32.
-  static_assert(TL::kTN == 2 && BN / 2 == 64, "one W1/W2 fragment pair per wave");
+  static_assert(kTN == 2 && BN / WGN == 64, "one W1/W2 fragment pair per wave");
   float* h = reinterpret_cast<float*>(lds);
   {
     const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WGN, wn = wave % WGN;
 #pragma unroll
-    for (int i = 0; i < TL::kTM; ++i)
+    for (int i = 0; i < kTM; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        h[(wm * (BM / 2) + 32 * i + mfma32_row(r, lane)) * kLdh + wn * 32 + (lane & 31)] =
+        h[(wm * (BM / WGM) + 32 * i + mfma32_row(r, lane)) * kLdh + wn * 32 + (lane & 31)] =
             silu_fast(acc[i][0][r]) * acc[i][1][r];
   }
   __syncthreads();
 
-  // 2. Four consecutive features of one row per lane: 16 lanes per row, 16
-  // rows per workgroup step.  Feature quad c holds W1 columns
+  // 2. Four consecutive features of one row per lane: BN/8 lanes per row,
+  // 16 rows per workgroup step.  Feature quad c holds W1 columns
   // n0 + 64(c/8) + 4(c%8) .. +3 of P and the W2 columns 32 further.  All loads
   // and stores are unconditional: P and the tile's rows of dh go through
   // buffer resources (an offset past the end of a range reads zero and
   // drops a store), which lets the compiler keep the loads in flight.
   typedef float f4 __attribute__((ext_vector_type(4)));
-  const int c = tid & 15, row0 = tid >> 4;
+  constexpr int kQ = BN / 8;                             // feature quads per row
+  static_assert(NT / kQ == 16, "16 rows per workgroup step");
+  const int c = tid % kQ, row0 = tid / kQ;
   const bool colv = n0 + 64 * (c >> 3) < N;              // the quad's 64-column group exists
   const uint32_t pcol = uint32_t(n0 + 64 * (c >> 3) + 4 * (c & 7)) * 4u;
   const int f = n0 / 2 + 4 * c;
@@ -537,18 +554,19 @@ __global__ __launch_bounds__(256, 2) void k_swiglu(const char* __restrict__ kv,
 // columns, then the group quantiser on the tile ([RKV] §2.4), writing the
 // token's record (and z, if asked) at its place in [B][T].
 template <typename E, int BITS, int G8>
-__global__ __launch_bounds__(256) void k_w3_quant(const char* __restrict__ dh,
+__global__ __launch_bounds__(W3Cfg<E>::kThreads) void k_w3_quant(const char* __restrict__ dh,
                                                   const char* __restrict__ w3p, int K, int M,
                                                   int N, int tiles_m, int T, int s, int nr,
                                                   uint8_t* __restrict__ codes,
                                                   uint16_t* __restrict__ scale,
                                                   uint16_t* __restrict__ zmin,
                                                   float* __restrict__ z) {
-  constexpr int BM = kW3BM, BN = kW3BN;
-  using TL = Tile<E, BM, BN>;
+  using CF = W3Cfg<E>;
+  constexpr int BM = CF::BM, BN = CF::BN, WGM = CF::WGM, WGN = CF::WGN, NT = CF::kThreads;
+  static_assert(WGM == 2, "the epilogue stages one wave-row (half the tile) at a time");
   constexpr int LD = kEpiLd(BN);
   constexpr int HALF = BM / 2;
-  constexpr int kMain = mainloop_lds<E, BM, BN, kSB, kW3NS>();
+  constexpr int kMain = mainloop_lds<E, BM, BN, CF::SB, CF::NS, WGM, WGN>();
   constexpr int kLdsBytes = kMain > HALF * LD * 4 ? kMain : HALF * LD * 4;
   __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
   const int mt = blockIdx.x % tiles_m, nt = blockIdx.x / tiles_m;
@@ -557,18 +575,18 @@ __global__ __launch_bounds__(256) void k_w3_quant(const char* __restrict__ dh,
   const int tid = threadIdx.x;
   auto rowA = [&](int r) { return dh + size_t(min(m0 + r, M - 1)) * rowb; };
   auto rowB = [&](int r) { return w3p + size_t(min(n0 + r, N - 1)) * rowb; };
-  f32x16 acc[TL::kTM][TL::kTN];
-  tile_product<E, BM, BN, kSB, kW3NS>(rowA, rowB, int(rowb), lds, acc);
+  f32x16 acc[BM / WGM / 32][BN / WGN / 32];
+  tile_product<E, BM, BN, CF::SB, CF::NS, WGM, WGN>(rowA, rowB, int(rowb), lds, acc);
   float* zt = reinterpret_cast<float*>(lds);
   // 8 latent values per lane; G8 consecutive lanes hold one group (groups
   // never straddle a row or the edge N: g divides both BN and d_c)
   constexpr int kChunks = BN / 8;
   const int d_c = N;
   for (int half = 0; half < 2; ++half) {
-    acc_to_lds<BM, BN>(acc, zt, LD, half);
+    acc_to_lds<BM, BN, WGM, WGN>(acc, zt, LD, half);
     __syncthreads();
-    for (int i = 0; i < HALF * kChunks / 256; ++i) {
-      const int unit = i * 256 + tid;
+    for (int i = 0; i < HALF * kChunks / NT; ++i) {
+      const int unit = i * NT + tid;
       const int row = unit / kChunks, ch = unit % kChunks;
       const int Q = m0 + half * HALF + row, col = n0 + ch * 8;
       const bool act = Q < M && col < N;
@@ -809,14 +827,14 @@ hipError_t launch_swiglu(const Shape& sh, const void* kv, const int32_t* ref_idx
                          const Workspace& L, hipStream_t st) {
   const int M = sh.B * sh.nr, N = 2 * sh.d_ff;
   if (M == 0) return hipGetLastError();
-  const int tn = cdiv(N, kSwBN), tm = cdiv(M, kSwBM);
   const auto* p = static_cast<const char*>(kv);
   const auto* proj = reinterpret_cast<const float*>(ws + L.proj);
   // P is addressed with 32-bit byte offsets (its size is checked on the host)
   const uint32_t pbytes = uint32_t(size_t(sh.B) * sh.nref * N * 4);
-#define RKV_SW(E, KL)                                                                        \
-  k_swiglu<E, KL><<<tn * tm, 256, 0, st>>>(p, ws + L.wp, proj, pbytes, ref_idx, ws + L.dh, sh.T, \
-                                           sh.C, sh.s, sh.nref, sh.nr, sh.k, sh.d_ff, M, tn)
+#define RKV_SW(E, KL)                                                                           \
+  k_swiglu<E, KL><<<cdiv(N, SwCfg<E>::BN) * cdiv(M, SwCfg<E>::BM), SwCfg<E>::kThreads, 0, st>>>( \
+      p, ws + L.wp, proj, pbytes, ref_idx, ws + L.dh, sh.T, sh.C, sh.s, sh.nref, sh.nr, sh.k,    \
+      sh.d_ff, M)
   if (sh.bf16) { if (sh.kl == 4) RKV_SW(uint16_t, 4); else RKV_SW(uint16_t, 8); }
   else { if (sh.kl == 4) RKV_SW(float, 4); else RKV_SW(float, 8); }
 #undef RKV_SW
@@ -827,12 +845,12 @@ hipError_t launch_w3_quant(const Shape& sh, char* ws, const Workspace& L, uint8_
                            uint16_t* scale, uint16_t* zmin, float* z, hipStream_t st) {
   const int M = sh.B * sh.nr, N = sh.d_c;
   if (M == 0) return hipGetLastError();
-  const int tn = cdiv(N, kW3BN), tm = cdiv(M, kW3BM);
   const char* a = ws + L.dh;
   const char* w = ws + L.w3p;
-#define RKV_W3(E, BITS, G8)                                                               \
-  k_w3_quant<E, BITS, G8><<<tn * tm, 256, 0, st>>>(a, w, sh.k3, M, N, tm, sh.T, sh.s, sh.nr, \
-                                                   codes, scale, zmin, z)
+#define RKV_W3(E, BITS, G8)                                                                   \
+  k_w3_quant<E, BITS, G8><<<cdiv(N, W3Cfg<E>::BN) * cdiv(M, W3Cfg<E>::BM), W3Cfg<E>::kThreads, \
+                            0, st>>>(a, w, sh.k3, M, N, cdiv(M, W3Cfg<E>::BM), sh.T, sh.s,     \
+                                     sh.nr, codes, scale, zmin, z)
 #define RKV_W3G(E, BITS)                      \
   switch (sh.g) {                             \
     case 8: RKV_W3(E, BITS, 1); break;        \
