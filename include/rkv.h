@@ -144,9 +144,9 @@ rkv_status rkv_select(const rkv_params* p, const void* kv, int32_t* ref_idx,
  * single-threaded measurement; events are created on first use and kept. */
 typedef enum {
   RKV_STAGE_PACK = 0,    /* weight repacking                               */
-  RKV_STAGE_NORMS = 1,   /* reference squared norms                        */
-  RKV_STAGE_DIST = 2,    /* distance contraction + per-chunk top-k          */
-  RKV_STAGE_MERGE = 3,   /* top-k merge, ref_idx                            */
+  RKV_STAGE_NORMS = 1,   /* reference rows, norms, reference-token records  */
+  RKV_STAGE_DIST = 2,    /* distance contraction + partial top-k lists      */
+  RKV_STAGE_MERGE = 3,   /* top-k merge, ref_idx of non-reference tokens    */
   RKV_STAGE_PROJ = 4,    /* reference projection P = R [W1|W2]              */
   RKV_STAGE_SWIGLU = 5,  /* token projection, mean branch, delta_h          */
   RKV_STAGE_W3 = 6,      /* latent z = delta_h W3 + group quantiser         */

@@ -62,4 +62,22 @@ __device__ __forceinline__ void topk_push(float (&bd)[KL], int (&bi)[KL], float 
   }
 }
 
+// The same for candidates in any order: (d, j) pairs compare
+// lexicographically, so equal distances keep the smaller position.
+template <int KL>
+__device__ __forceinline__ void topk_push_lex(float (&bd)[KL], int (&bi)[KL], float d, int j) {
+  float x = d;
+  int xj = j;
+#pragma unroll
+  for (int i = 0; i < KL; ++i) {
+    const bool c = x < bd[i] || (x == bd[i] && xj < bi[i]);
+    const float nd = c ? x : bd[i];
+    const int ni = c ? xj : bi[i];
+    x = c ? bd[i] : x;
+    xj = c ? bi[i] : xj;
+    bd[i] = nd;
+    bi[i] = ni;
+  }
+}
+
 }  // namespace rkv

@@ -15,7 +15,7 @@ struct Shape {
   int nref;      // references per sequence, ceil(T/s)
   int nr;        // non-references per sequence, T - nref
   int kl;        // neighbour-list length kept per chunk (4 or 8, >= k)
-  int n_chunks;  // reference chunks per sequence in the distance kernel
+  int n_chunks;  // reference chunks (one partial top-k list each) per sequence
   int k3;        // contraction length of the W3 product (2*d_ff bf16 hi/lo, d_ff fp32)
 };
 
@@ -32,11 +32,11 @@ Workspace plan_workspace(const Shape& sh);
 hipError_t launch_pack_weights(const Shape& sh, const void* w1, const void* w2, const void* w3,
                                char* ws, const Workspace& L, hipStream_t st);
 hipError_t launch_ref_norms(const Shape& sh, const void* kv, char* ws, const Workspace& L,
-                            hipStream_t st);
+                            int32_t* ref_idx, uint8_t* codes, uint16_t* scale, uint16_t* zmin,
+                            float* z, hipStream_t st);
 hipError_t launch_dist(const Shape& sh, const void* kv, char* ws, const Workspace& L,
                        hipStream_t st);
 hipError_t launch_merge(const Shape& sh, int32_t* ref_idx, char* ws, const Workspace& L,
-                        uint8_t* codes, uint16_t* scale, uint16_t* zmin, float* z,
                         hipStream_t st);
 hipError_t launch_ref_proj(const Shape& sh, const void* kv, char* ws, const Workspace& L,
                            hipStream_t st);

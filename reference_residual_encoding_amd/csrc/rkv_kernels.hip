@@ -60,9 +60,16 @@ template <> struct W3Cfg<float> {
   static constexpr int kThreads = 64 * WGM * WGN;
 };
                                                                  // difference, 2 WGs per CU
-constexpr int kDistRefs = 128;                            // references per chunk (tile M)
-constexpr int kDistTok = 256;                             // tokens per tile (tile N)
-constexpr int kDistNS = 3, kDistSB = 64;                  // two workgroups per CU
+// distance contraction: BM references (a chunk) x BN tokens per workgroup;
+// SUBS = threads per token in the top-k scan, each keeping its own list
+template <typename E> struct DistCfg {
+  static constexpr int BM = 192, BN = 256, SB = 128, NS = 2, WGM = 2, WGN = 4;
+  static constexpr int kThreads = 64 * WGM * WGN, SUBS = kThreads / BN;
+};
+template <> struct DistCfg<float> {
+  static constexpr int BM = 128, BN = 256, SB = 128, NS = 2, WGM = 2, WGN = 2;
+  static constexpr int kThreads = 64 * WGM * WGN, SUBS = kThreads / BN;
+};
 constexpr int kSB = 128;
 constexpr int kEpiLd(int bn) { return bn + 8; }  // padded fp32 row of an LDS-staged tile
 
@@ -105,15 +112,32 @@ __global__ __launch_bounds__(256) void k_transpose_pack(const E* __restrict__ sr
 // Copy the reference rows (positions j*s of each sequence) into a compact
 // [B*nref][C] block, which the distance and projection contractions stream
 // (the references sit a whole stride apart in kv), and compute ||kv_j||^2.
+// A reference token is stored as it is ([RKV] §2.4): its ref_idx row is all
+// -1 and, when a record is given, its record (codes, scale, zmin, z) is all
+// zero; one wave writes each with coalesced stores.
 template <typename E>
 __global__ __launch_bounds__(256) void k_ref_gather(const char* __restrict__ kv, int B, int T,
                                                     int C, int s, int nref,
                                                     char* __restrict__ refs,
-                                                    float* __restrict__ ysq) {
+                                                    float* __restrict__ ysq,
+                                                    int32_t* __restrict__ ref_idx, int k,
+                                                    uint8_t* __restrict__ codes, int cb,
+                                                    uint16_t* __restrict__ scale,
+                                                    uint16_t* __restrict__ zmin, int ng,
+                                                    float* __restrict__ z, int d_c) {
   const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (wid >= B * nref) return;
   const int b = wid / nref, j = wid % nref;
+  const size_t rec = size_t(b) * T + size_t(j) * s;     // the reference token's flat row
+  for (int i = lane; i < k; i += 64) ref_idx[rec * k + i] = -1;
+  if (codes) {
+    for (int o = lane * 4; o < cb; o += 256) *reinterpret_cast<uint32_t*>(codes + rec * cb + o) = 0u;
+    for (int i = lane; i < ng; i += 64) { scale[rec * ng + i] = 0; zmin[rec * ng + i] = 0; }
+    if (z)
+      for (int i = lane * 4; i < d_c; i += 256)
+        *reinterpret_cast<float4*>(z + rec * d_c + i) = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   const size_t rowb = size_t(C) * sizeof(E);
   const char* src = kv + (size_t(b) * T + size_t(j) * s) * rowb;
   char* dst = refs + size_t(wid) * rowb;
@@ -197,21 +221,22 @@ __device__ __forceinline__ void store_codes(uint8_t* codes, int64_t unit, uint32
 }
 
 // ------------------------------------------------------------------ retrieval
-// One workgroup: kDistRefs references (chunk c) x kDistTok non-reference
-// tokens (tile tt) of sequence b.  Writes, per token, the KL best (d', j) of
-// the chunk restricted to the causal pool (j*s < position).
+// One workgroup: BM references (chunk c) x BN non-reference tokens (tile tt)
+// of sequence b.  Each of the SUBS threads of a token scans its own span of
+// each half chunk in increasing j; their lists are then combined into the KL
+// best (d', j) of the chunk restricted to the causal pool (j*s < position),
+// written as partial list c.
 template <typename E, int KL>
-__global__ __launch_bounds__(256, 2) void k_dist_topk(const char* __restrict__ kv,
-                                                   const char* __restrict__ refs,
-                                                   const float* __restrict__ ysq,
-                                                   float2* __restrict__ part, int B, int T,
-                                                   int C, int s, int nref, int nr,
-                                                   int n_chunks, int n_tt) {
-  constexpr int BM = kDistRefs, BN = kDistTok;
-  using TL = Tile<E, BM, BN>;   // wave-tile geometry (same for both main loops)
+__global__ __launch_bounds__(DistCfg<E>::kThreads) void k_dist_topk(
+    const char* __restrict__ kv, const char* __restrict__ refs, const float* __restrict__ ysq,
+    float2* __restrict__ part, int B, int T, int C, int s, int nref, int nr, int n_lists,
+    int n_tt) {
+  using CF = DistCfg<E>;
+  constexpr int BM = CF::BM, BN = CF::BN, WGM = CF::WGM, WGN = CF::WGN, SUBS = CF::SUBS;
   constexpr int LD = kEpiLd(BN);
-  constexpr int HALF = BM / 2;
-  constexpr int kMain = mainloop_lds<E, BM, BN, kDistSB, kDistNS>();
+  constexpr int HALF = BM / 2, SPAN = HALF / SUBS;
+  static_assert(WGM == 2 && SPAN % 4 == 0, "two wave-rows; whole groups of 4 per span");
+  constexpr int kMain = mainloop_lds<E, BM, BN, CF::SB, CF::NS, WGM, WGN>();
   constexpr int kStaged = kMain > HALF * LD * 4 ? kMain : HALF * LD * 4;
   __shared__ __attribute__((aligned(1024))) char lds[kStaged + BM * 4];
   float* ysq_l = reinterpret_cast<float*>(lds + kStaged);
@@ -239,18 +264,18 @@ __global__ __launch_bounds__(256, 2) void k_dist_topk(const char* __restrict__ k
   const size_t rowb = size_t(C) * sizeof(E);
   const char* base = kv + size_t(b) * T * rowb;
   const int tid = threadIdx.x;
-  for (int r = tid; r < BM; r += 256) ysq_l[r] = ysq[size_t(b) * nref + min(m0 + r, nref - 1)];
+  for (int r = tid; r < BM; r += CF::kThreads) ysq_l[r] = ysq[size_t(b) * nref + min(m0 + r, nref - 1)];
   const char* rbase = refs + size_t(b) * nref * rowb;
   auto rowA = [&](int r) { return rbase + size_t(min(m0 + r, nref - 1)) * rowb; };
   auto rowB = [&](int r) { return base + size_t(nonref_pos(min(n0 + r, nr - 1), s)) * rowb; };
-  f32x16 acc[TL::kTM][TL::kTN];
-  tile_product<E, BM, BN, kDistSB, kDistNS>(rowA, rowB, int(rowb), lds, acc);
+  f32x16 acc[BM / WGM / 32][BN / WGN / 32];
+  tile_product<E, BM, BN, CF::SB, CF::NS, WGM, WGN>(rowA, rowB, int(rowb), lds, acc);
 
-  // Stage the dot products half a chunk at a time; one thread per token
-  // scans the references in increasing order, keeping the KL best (d', j).
-  static_assert(BN == 256, "one thread per token of the tile");
+  // Stage the dot products half a chunk at a time (the waves of one
+  // wave-row); thread (t, sub) scans references sub*SPAN .. +SPAN of each
+  // half for token t in increasing order, keeping the KL best (d', j).
   float* dot = reinterpret_cast<float*>(lds);
-  const int t = tid, q = n0 + t;
+  const int t = tid % BN, sb = tid / BN, q = n0 + t;     // sb is uniform per wave
   // references j < ceil(position / s) are in the pool of the token at q;
   // the scan runs to the tile's largest pool (uniform) and masks the rest
   const int lim = q < nr ? (nonref_pos(q, s) + s - 1) / s - m0 : 0;
@@ -262,87 +287,111 @@ __global__ __launch_bounds__(256, 2) void k_dist_topk(const char* __restrict__ k
   for (int half = 0; half < 2; ++half) {
     const int j0 = half * HALF;
     if (j0 < lim_all) {              // uniform: the workgroup skips an empty half
-      acc_to_lds<BM, BN>(acc, dot, LD, half);
+      acc_to_lds<BM, BN, WGM, WGN>(acc, dot, LD, half);
       __syncthreads();
-      const int end = min(lim_all - j0, HALF);
+      const int js = j0 + sb * SPAN;                     // first reference of this thread's span
+      const int end = min(lim_all - js, SPAN);           // uniform per wave
+      const float* col = dot + (sb * SPAN) * LD + t;
       int jl = 0;
       for (; jl + 4 <= end; jl += 4) {
         float dd[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) dd[u] = ysq_l[j0 + jl + u] - 2.0f * dot[(jl + u) * LD + t];
+        for (int u = 0; u < 4; ++u) {
+          const float d = ysq_l[js + jl + u] - 2.0f * col[(jl + u) * LD];
+          dd[u] = js + jl + u < lim ? d : __builtin_inff();
+        }
+        // a candidate not below the current KL-th best changes nothing (a
+        // tie arrives with the larger j), so a group that no lane of the
+        // wave can use is skipped whole
+        const float mn = fminf(fminf(dd[0], dd[1]), fminf(dd[2], dd[3]));
+        if (__any(mn < bd[KL - 1])) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          topk_push<KL>(bd, bi, j0 + jl + u < lim ? dd[u] : __builtin_inff(), m0 + j0 + jl + u);
+          for (int u = 0; u < 4; ++u) topk_push<KL>(bd, bi, dd[u], m0 + js + jl + u);
+        }
       }
       for (; jl < end; ++jl) {
-        const float d = ysq_l[j0 + jl] - 2.0f * dot[jl * LD + t];
-        topk_push<KL>(bd, bi, j0 + jl < lim ? d : __builtin_inff(), m0 + j0 + jl);
+        const float d = ysq_l[js + jl] - 2.0f * col[jl * LD];
+        topk_push<KL>(bd, bi, js + jl < lim ? d : __builtin_inff(), m0 + js + jl);
       }
       __syncthreads();
     }
   }
+  if constexpr (SUBS > 1) {
+    // combine the SUBS lists of each token: the others publish theirs in LDS
+    // (free since the barrier that ended the last scanned half), thread 0
+    // of the token merges them by (d, j)
+    float2* xl = reinterpret_cast<float2*>(lds);         // [SUBS-1][BN][KL]
+    if (sb > 0) {
+#pragma unroll
+      for (int i = 0; i < KL; ++i)
+        xl[((sb - 1) * BN + t) * KL + i] = make_float2(bd[i], __int_as_float(bi[i]));
+    }
+    __syncthreads();
+    if (sb > 0) return;
+#pragma unroll
+    for (int o = 0; o < SUBS - 1; ++o)
+#pragma unroll
+      for (int i = 0; i < KL; ++i) {
+        const float2 v = xl[(o * BN + t) * KL + i];
+        topk_push_lex<KL>(bd, bi, v.x, __float_as_int(v.y));
+      }
+  }
   if (q < nr) {
-    float2* out = part + ((size_t(b) * n_chunks + c) * nr + q) * KL;
+    float2* out = part + ((size_t(b) * n_lists + c) * nr + q) * KL;
 #pragma unroll
     for (int i = 0; i < KL; ++i) out[i] = make_float2(bd[i], __int_as_float(bi[i]));
   }
 }
 
-// Per token: merge the chunk lists, keep k_t = min(k, ceil(t/s)) references
-// ([RKV] §2.1), write their positions in ascending order, -1 pads.  Chunks
-// are merged in increasing order, each list sorted by (d, j), so every
-// candidate has a larger j than the kept pairs of equal d it meets.
+// Per non-reference token: merge the partial lists, keep k_t = min(k,
+// ceil(t/s)) references ([RKV] §2.1), write their positions in ascending
+// order, -1 pads.  The lists cover disjoint reference sets; the merge orders
+// by (d, j), so equal distances keep the smaller position whatever order the
+// lists come in.  (Reference tokens' rows are written by k_ref_gather.)
 // Reference tokens get an all -1 row and, when a record is given, an all-zero
 // record: references are stored as they are ([RKV] §2.4).
 template <int KL>
-__global__ __launch_bounds__(256) void k_topk_merge(const float2* __restrict__ part,
+__global__ __launch_bounds__(64) void k_topk_merge(const float2* __restrict__ part,
                                                     int32_t* __restrict__ ref_idx, int B, int T,
-                                                    int s, int k, int nr, int n_chunks, int d_c,
-                                                    int g, int bits, uint8_t* __restrict__ codes,
-                                                    uint16_t* __restrict__ scale,
-                                                    uint16_t* __restrict__ zmin,
-                                                    float* __restrict__ z) {
-  const long gid = long(blockIdx.x) * 256 + threadIdx.x;
+                                                    int s, int k, int nr, int n_lists,
+                                                    int chunk) {
+  const long gid = long(blockIdx.x) * 64 + threadIdx.x;
   if (gid >= long(B) * T) return;
   const int b = int(gid / T), t = int(gid % T);
   int32_t* out = ref_idx + gid * k;
-  if (t % s == 0) {
-    for (int i = 0; i < k; ++i) out[i] = -1;
-    if (codes) {
-      const int cb = d_c * bits / 8, ng = d_c / g;
-      for (int i = 0; i < cb; i += 4) *reinterpret_cast<uint32_t*>(codes + gid * cb + i) = 0u;
-      for (int i = 0; i < ng; ++i) { scale[gid * ng + i] = 0; zmin[gid * ng + i] = 0; }
-      if (z)
-        for (int i = 0; i < d_c; i += 4)
-          *reinterpret_cast<float4*>(z + gid * d_c + i) = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    return;
-  }
+  if (t % s == 0) return;
   const int q = t - t / s - 1;
   const int npool = (t + s - 1) / s;
   const int kt = min(k, npool);
-  const int nch = (npool + kDistRefs - 1) / kDistRefs;
+  const int nch = (npool + chunk - 1) / chunk;          // lists that cover the pool
   float bd[KL];
   int bi[KL];
 #pragma unroll
   for (int i = 0; i < KL; ++i) { bd[i] = __builtin_inff(); bi[i] = 0x7fffffff; }
-  const float2* p = part + (size_t(b) * n_chunks * nr + q) * KL;
+  const float2* p = part + (size_t(b) * n_lists * nr + q) * KL;
   const size_t cstride = size_t(nr) * KL;
-  int c = 0;
-  for (; c + 2 <= nch; c += 2) {  // two chunks' loads in flight
-    float2 v0[KL], v1[KL];
+  // kB lists per batch (every list of a typical pool at once), 16-byte
+  // loads; every load is unconditional (a list index past the last one is
+  // clamped and its values are replaced by +inf)
+  constexpr int kB = KL <= 4 ? 12 : 6;
+  for (int c0 = 0; c0 < nch; c0 += kB) {
+    float4 v[kB][KL / 2];
 #pragma unroll
-    for (int i = 0; i < KL; ++i) { v0[i] = p[c * cstride + i]; v1[i] = p[(c + 1) * cstride + i]; }
+    for (int u = 0; u < kB; ++u) {
+      const float4* src = reinterpret_cast<const float4*>(p + min(c0 + u, nch - 1) * cstride);
 #pragma unroll
-    for (int i = 0; i < KL; ++i) topk_push<KL>(bd, bi, v0[i].x, __float_as_int(v0[i].y));
+      for (int h = 0; h < KL / 2; ++h) v[u][h] = src[h];
+    }
 #pragma unroll
-    for (int i = 0; i < KL; ++i) topk_push<KL>(bd, bi, v1[i].x, __float_as_int(v1[i].y));
-  }
-  if (c < nch) {
+    for (int u = 0; u < kB; ++u) {
+      const bool live = c0 + u < nch;
 #pragma unroll
-    for (int i = 0; i < KL; ++i) {
-      const float2 v = p[c * cstride + i];
-      topk_push<KL>(bd, bi, v.x, __float_as_int(v.y));
+      for (int h = 0; h < KL / 2; ++h) {
+        topk_push_lex<KL>(bd, bi, live ? v[u][h].x : __builtin_inff(),
+                          live ? __float_as_int(v[u][h].y) : 0x7fffffff);
+        topk_push_lex<KL>(bd, bi, live ? v[u][h].z : __builtin_inff(),
+                          live ? __float_as_int(v[u][h].w) : 0x7fffffff);
+      }
     }
   }
   int sel[KL];
@@ -717,7 +766,7 @@ Shape make_shape(int B, int T, int N, int D, int d_ff, int d_c, int k, int g, in
   sh.nref = (T + s - 1) / s;
   sh.nr = T - sh.nref;
   sh.kl = k <= 4 ? 4 : 8;
-  sh.n_chunks = cdiv(sh.nref, kDistRefs);
+  sh.n_chunks = cdiv(sh.nref, bf16 ? DistCfg<uint16_t>::BM : DistCfg<float>::BM);
   sh.k3 = bf16 ? 2 * d_ff : d_ff;
   return sh;
 }
@@ -760,15 +809,36 @@ hipError_t launch_pack_weights(const Shape& sh, const void* w1, const void* w2, 
 }
 
 hipError_t launch_ref_norms(const Shape& sh, const void* kv, char* ws, const Workspace& L,
-                            hipStream_t st) {
+                            int32_t* ref_idx, uint8_t* codes, uint16_t* scale, uint16_t* zmin,
+                            float* z, hipStream_t st) {
   const int rows = sh.B * sh.nref;
   auto* y = reinterpret_cast<float*>(ws + L.ysq);
   const auto* p = static_cast<const char*>(kv);
+  const int cb = sh.d_c * sh.b / 8, ng = sh.d_c / sh.g;
   if (sh.bf16)
-    k_ref_gather<uint16_t><<<cdiv(rows, 4), 256, 0, st>>>(p, sh.B, sh.T, sh.C, sh.s, sh.nref, ws + L.refs, y);
+    k_ref_gather<uint16_t><<<cdiv(rows, 4), 256, 0, st>>>(p, sh.B, sh.T, sh.C, sh.s, sh.nref,
+                                                          ws + L.refs, y, ref_idx, sh.k, codes, cb,
+                                                          scale, zmin, ng, z, sh.d_c);
   else
-    k_ref_gather<float><<<cdiv(rows, 4), 256, 0, st>>>(p, sh.B, sh.T, sh.C, sh.s, sh.nref, ws + L.refs, y);
+    k_ref_gather<float><<<cdiv(rows, 4), 256, 0, st>>>(p, sh.B, sh.T, sh.C, sh.s, sh.nref,
+                                                       ws + L.refs, y, ref_idx, sh.k, codes, cb,
+                                                       scale, zmin, ng, z, sh.d_c);
   return hipGetLastError();
+}
+
+template <typename E>
+static int dist_items(const Shape& sh, int n_tt) {
+  // per-XCD item counts (same enumeration as the kernel); grid = 8 x max
+  constexpr int BM = DistCfg<E>::BM, BN = DistCfg<E>::BN;
+  long per_xcd[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int g = 0; g < sh.B * n_tt; ++g) {
+    const int tt = g % n_tt;
+    const int q = std::min(tt * BN + BN, sh.nr) - 1;
+    const int pl = (q / (sh.s - 1)) * sh.s + (q % (sh.s - 1)) + 1;
+    const int np = (pl + sh.s - 1) / sh.s;
+    per_xcd[g & 7] += (np + BM - 1) / BM;
+  }
+  return int(8 * *std::max_element(per_xcd, per_xcd + 8));
 }
 
 hipError_t launch_dist(const Shape& sh, const void* kv, char* ws, const Workspace& L,
@@ -777,20 +847,12 @@ hipError_t launch_dist(const Shape& sh, const void* kv, char* ws, const Workspac
   const auto* p = static_cast<const char*>(kv);
   const auto* y = reinterpret_cast<const float*>(ws + L.ysq);
   auto* part = reinterpret_cast<float2*>(ws + L.part);
-  const int n_tt = cdiv(sh.nr, kDistTok);
-  // per-XCD item counts (same enumeration as the kernel); grid = 8 x max
-  long per_xcd[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int g = 0; g < sh.B * n_tt; ++g) {
-    const int tt = g % n_tt;
-    const int q = std::min(tt * kDistTok + kDistTok, sh.nr) - 1;
-    const int pl = (q / (sh.s - 1)) * sh.s + (q % (sh.s - 1)) + 1;
-    const int np = (pl + sh.s - 1) / sh.s;
-    per_xcd[g & 7] += (np + kDistRefs - 1) / kDistRefs;
-  }
-  const long lmax = *std::max_element(per_xcd, per_xcd + 8);
-  const int items = int(8 * lmax);
-#define RKV_DIST(E, KL) \
-  k_dist_topk<E, KL><<<items, 256, 0, st>>>(p, ws + L.refs, y, part, sh.B, sh.T, sh.C, sh.s, sh.nref, sh.nr, sh.n_chunks, n_tt)
+#define RKV_DIST(E, KL)                                                                      \
+  do {                                                                                       \
+    const int n_tt = cdiv(sh.nr, DistCfg<E>::BN);                                            \
+    k_dist_topk<E, KL><<<dist_items<E>(sh, n_tt), DistCfg<E>::kThreads, 0, st>>>(            \
+        p, ws + L.refs, y, part, sh.B, sh.T, sh.C, sh.s, sh.nref, sh.nr, sh.n_chunks, n_tt); \
+  } while (0)
   if (sh.bf16) { if (sh.kl == 4) RKV_DIST(uint16_t, 4); else RKV_DIST(uint16_t, 8); }
   else { if (sh.kl == 4) RKV_DIST(float, 4); else RKV_DIST(float, 8); }
 #undef RKV_DIST
@@ -798,13 +860,13 @@ hipError_t launch_dist(const Shape& sh, const void* kv, char* ws, const Workspac
 }
 
 hipError_t launch_merge(const Shape& sh, int32_t* ref_idx, char* ws, const Workspace& L,
-                        uint8_t* codes, uint16_t* scale, uint16_t* zmin, float* z,
                         hipStream_t st) {
   const auto* part = reinterpret_cast<const float2*>(ws + L.part);
-  const int nb = cdiv(long(sh.B) * sh.T, 256);
+  const int nb = cdiv(long(sh.B) * sh.T, 64);   // one wave per block: every CU takes part
+  const int chunk = sh.bf16 ? DistCfg<uint16_t>::BM : DistCfg<float>::BM;
 #define RKV_MERGE(KL)                                                                        \
-  k_topk_merge<KL><<<nb, 256, 0, st>>>(part, ref_idx, sh.B, sh.T, sh.s, sh.k, sh.nr,        \
-                                       sh.n_chunks, sh.d_c, sh.g, sh.b, codes, scale, zmin, z)
+  k_topk_merge<KL><<<nb, 64, 0, st>>>(part, ref_idx, sh.B, sh.T, sh.s, sh.k, sh.nr,        \
+                                      sh.n_chunks, chunk)
   if (sh.kl == 4) RKV_MERGE(4); else RKV_MERGE(8);
 #undef RKV_MERGE
   return hipGetLastError();
