@@ -26,6 +26,45 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
+# kernel behind each profiled stage
+STAGE_KERNEL = {"pack": "k_transpose_pack", "norms": "k_ref_gather", "dist": "k_dist_topk",
+                "merge": "k_topk_merge", "proj": "k_ref_proj", "swiglu": "k_swiglu",
+                "w3": "k_w3_quant", "quant": "k_quantize", "gather": "k_gather"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_{workload}.txt")
+
+
+def source_digest() -> str:
+    """sha256 over the HIP/C++ sources of librkv (file names and contents)."""
+    import hashlib
+    d = os.path.join(ROOT, "reference_residual_encoding_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            h.update(name.encode())
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel`, from the committed hardware-counter
+    summary of this workload, or None when there is none or the kernel
+    sources have changed since the counters were taken."""
+    path = TRAFFIC_FILE.format(workload=workload)
+    if not os.path.exists(path):
+        return None
+    digest, table = None, {}
+    with open(path) as f:
+        for line in f:
+            parts = line.split()
+            if len(parts) == 2 and parts[0] == "source_sha256":
+                digest = parts[1]
+            elif len(parts) == 4 and parts[0].startswith("k_"):
+                table[parts[0]] = float(parts[3])
+    if digest != source_digest():
+        return None
+    return table.get(kernel)
+
 
 def stage_work(cfg, n_gather: int):
     """Algorithmic work of one launch of each stage: (kind, amount).
@@ -167,16 +206,17 @@ def main():
 
     work = stage_work(cfg, idx.numel())
     kind, amount = work[dominant]
+    traffic = measured_traffic(cfg.name, STAGE_KERNEL[dominant])
     if kind == "flops":
         peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
         achieved = amount / (dom_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": None, "kernel": dominant,
+                "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": dominant,
                 "kernel_ms": round(dom_ms, 4), "work_per_launch": amount}
     else:
         achieved = amount / (dom_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                 "kernel": dominant, "kernel_ms": round(dom_ms, 4), "work_per_launch": amount}
 
     mfma_flops = sum(work[s][1] for s in ("dist", "proj", "swiglu", "w3"))
