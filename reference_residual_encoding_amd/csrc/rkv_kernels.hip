@@ -184,11 +184,26 @@ __device__ __forceinline__ void group_minmax(float& mn, float& mx) {
   if constexpr (G8 >= 8) { mn = fminf(mn, swz_xor4(mn)); mx = fmaxf(mx, swz_xor4(mx)); }
 }
 
+// rint(x / d) exactly as the correctly rounded fp32 division would give it,
+// for quotients below 2^4 in magnitude plus the few steps an fp16-rounded
+// step or minimum can add.  x * rcp(d) (rcp within 1 ulp) lies within
+// 2 ulp(16) < 4e-6 of the rounded quotient, so the two round alike unless
+// the product is within 1e-5 of a half-integer; only then, and only where a
+// lane of the wave needs it, is the division itself done.
+__device__ __forceinline__ float rint_div(float x, float d, float rd) {
+  const float y = x * rd;
+  const bool near_half = fabsf(y - floorf(y) - 0.5f) < 1e-5f;
+  float r = rintf(y);
+  if (__any(near_half)) r = near_half ? rintf(x / d) : r;
+  return r;
+}
+
 // Quantise the 8 consecutive latent values a lane owns ([RKV] §2.4); the
 // G8 lanes of a group must all call it together.  Returns the packed codes;
-// Delta_h and m_h as fp16 bits.  Integer decisions are taken in fp32:
-// Delta = (max - min) / (2^b - 1), q = clamp(rint((z - m_h) / Delta_h)),
-// q = 0 when Delta_h == 0 (a constant group keeps m_h, no division).
+// Delta_h and m_h as fp16 bits.  Integer decisions are those of fp32
+// arithmetic: Delta = (max - min) / (2^b - 1), q = clamp(rint((z - m_h) /
+// Delta_h)), q = 0 when Delta_h == 0 (a constant group keeps m_h, no
+// division).
 template <int BITS, int G8>
 __device__ __forceinline__ uint32_t quant8(const float (&v)[8], uint16_t& dh_bits,
                                            uint16_t& mh_bits) {
@@ -203,9 +218,10 @@ __device__ __forceinline__ uint32_t quant8(const float (&v)[8], uint16_t& dh_bit
   const float dh = f16_bits_to_f32(dh_bits), mh = f16_bits_to_f32(mh_bits);
   uint32_t word = 0;
   if (dh != 0.0f) {
+    const float rd = __builtin_amdgcn_rcpf(dh);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float t = rintf((v[e] - mh) / dh);
+      const float t = rint_div(v[e] - mh, dh, rd);
       word |= uint32_t(fminf(fmaxf(t, 0.0f), kLevels)) << (BITS * e);
     }
   }
@@ -617,11 +633,18 @@ __global__ __launch_bounds__(W3Cfg<E>::kThreads) void k_w3_quant(const char* __r
   constexpr int HALF = BM / 2;
   constexpr int kMain = mainloop_lds<E, BM, BN, CF::SB, CF::NS, WGM, WGN>();
   constexpr int kLdsBytes = kMain > HALF * LD * 4 ? kMain : HALF * LD * 4;
-  __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
+  __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes + BM * 4];
+  int* rec_lds = reinterpret_cast<int*>(lds + kLdsBytes);  // [BM] record row b*T + t, -1 past M
   const int mt = blockIdx.x % tiles_m, nt = blockIdx.x / tiles_m;
   const int m0 = mt * BM, n0 = nt * BN;
   const size_t rowb = size_t(K) * sizeof(E);
   const int tid = threadIdx.x;
+  // record row of every token of the tile (read after the main loop, whose
+  // barriers publish it)
+  for (int r = tid; r < BM; r += NT) {
+    const int Q = m0 + r;
+    rec_lds[r] = Q < M ? (Q / nr) * T + nonref_pos(Q % nr, s) : -1;
+  }
   auto rowA = [&](int r) { return dh + size_t(min(m0 + r, M - 1)) * rowb; };
   auto rowB = [&](int r) { return w3p + size_t(min(n0 + r, N - 1)) * rowb; };
   f32x16 acc[BM / WGM / 32][BN / WGN / 32];
@@ -637,16 +660,16 @@ __global__ __launch_bounds__(W3Cfg<E>::kThreads) void k_w3_quant(const char* __r
     for (int i = 0; i < HALF * kChunks / NT; ++i) {
       const int unit = i * NT + tid;
       const int row = unit / kChunks, ch = unit % kChunks;
-      const int Q = m0 + half * HALF + row, col = n0 + ch * 8;
-      const bool act = Q < M && col < N;
+      const int col = n0 + ch * 8;
+      const int recr = rec_lds[half * HALF + row];
+      const bool act = recr >= 0 && col < N;
       float v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = zt[row * LD + ch * 8 + e];
       uint16_t dhb, mhb;
       const uint32_t word = quant8<BITS, G8>(v, dhb, mhb);
       if (act) {
-        const int bq = Q / nr, q = Q % nr;
-        const int64_t rec = int64_t(bq) * T + nonref_pos(q, s);   // record row b*T + t
+        const int64_t rec = recr;                                   // record row b*T + t
         const int64_t u = (rec * d_c + col) / 8;                    // flat 8-value unit
         store_codes<BITS>(codes, u, word);
         if ((tid % G8) == 0) {
