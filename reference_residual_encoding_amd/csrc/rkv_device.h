@@ -39,6 +39,16 @@ __device__ __forceinline__ int nonref_pos(int q, int s) {
   return (q / sm1) * s + (q % sm1) + 1;
 }
 
+// x as a (hi, lo) bf16 pair, hi = bf16(x) and lo = bf16(x - hi), both
+// rounded to nearest even (gfx950 converts in hardware: v_cvt_pk_bf16_f32);
+// hi in the low 16 bits.  hi + lo carries about 16 significant bits of x.
+__device__ __forceinline__ uint32_t bf16_hi_lo(float x) {
+  const __bf16 hi = static_cast<__bf16>(x);
+  const float lo = x - static_cast<float>(hi);
+  return uint32_t(__builtin_bit_cast(uint16_t, hi)) |
+         (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(lo))) << 16);
+}
+
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
 
 // Keep the KL smallest (d, j) pairs in ascending (d, j) order, for

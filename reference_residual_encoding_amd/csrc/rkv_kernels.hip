@@ -486,8 +486,9 @@ __global__ __launch_bounds__(SwCfg<E>::kThreads) void k_swiglu(const char* __res
   constexpr int kMain = mainloop_lds<E, BM, BN, CF::SB, CF::NS, WGM, WGN>();
   constexpr int kLdh = BN / 2 + 8;                       // padded fp32 row of the staged h tile
   constexpr int kStaged = kMain > BM * kLdh * 4 ? kMain : BM * kLdh * 4;
-  __shared__ __attribute__((aligned(1024))) char lds[kStaged + BM * KL * 4];
+  __shared__ __attribute__((aligned(1024))) char lds[kStaged + BM * KL * 4 + BM * 4];
   uint32_t* poff_lds = reinterpret_cast<uint32_t*>(lds + kStaged);  // [BM][KL] P row byte offsets
+  float* inv_lds = reinterpret_cast<float*>(lds + kStaged + BM * KL * 4);  // [BM] 1 / k_t
   const int N = 2 * d_ff;
   // row tile fastest: all XCDs work through one column tile of Wp at a time,
   // so every L2 holds that tile's rows of Wp and the columns of P its
@@ -497,14 +498,16 @@ __global__ __launch_bounds__(SwCfg<E>::kThreads) void k_swiglu(const char* __res
   const int m0 = mt * BM, n0 = nt * BN;
   const size_t rowb = size_t(C) * sizeof(E);
   const int tid = threadIdx.x;
-  // Per token of the tile: the byte offsets of its reference rows of P (read
-  // back after the main loop, whose barriers publish them).  A missing
-  // reference gets an offset past the end of P, which the buffer load below
-  // returns as zero.
+  // Per token of the tile: the byte offsets of its reference rows of P and
+  // 1/k_t (read back after the main loop, whose barriers publish them).  A
+  // missing reference gets the offset 2^31, past the end of P (which is
+  // smaller than 2 GiB) also after a column offset is added: the buffer load
+  // below returns zero for it.
   constexpr uint32_t kNone = 0x80000000u;
   for (int r = tid; r < BM; r += NT) {
     const int Q = m0 + r;
     uint32_t off[KL];
+    int kt = 0;
 #pragma unroll
     for (int i = 0; i < KL; ++i) off[i] = kNone;
     if (Q < M) {
@@ -513,11 +516,15 @@ __global__ __launch_bounds__(SwCfg<E>::kThreads) void k_swiglu(const char* __res
 #pragma unroll
       for (int i = 0; i < KL; ++i) {
         const int pos = i < k ? ri[i] : -1;
-        if (pos >= 0) off[i] = uint32_t(b * nref + pos / s) * uint32_t(N) * 4u;
+        if (pos >= 0) {
+          off[i] = uint32_t(b * nref + pos / s) * uint32_t(N) * 4u;
+          ++kt;
+        }
       }
     }
 #pragma unroll
     for (int i = 0; i < KL; ++i) poff_lds[r * KL + i] = off[i];
+    inv_lds[r] = 1.0f / float(max(kt, 1));
   }
   auto rowA = [&](int r) {
     const int Q = min(m0 + r, M - 1);
@@ -571,19 +578,15 @@ __global__ __launch_bounds__(SwCfg<E>::kThreads) void k_swiglu(const char* __res
   constexpr int kRB = KL <= 4 ? 4 : 2;                   // row steps whose loads fly together
   for (int it = 0; it < BM / 16; it += kRB) {
     f4 p1[kRB][KL], p2[kRB][KL];
-    int kt[kRB];
 #pragma unroll
     for (int u = 0; u < kRB; ++u) {
       const uint32_t* po = poff_lds + (16 * (it + u) + row0) * KL;
-      kt[u] = 0;
 #pragma unroll
       for (int q = 0; q < KL; ++q) {
-        const uint32_t o = po[q];
-        const bool ok = o != kNone;
-        kt[u] += ok;
-        const bool go = ok && colv;
-        p1[u][q] = ld4(go ? o + pcol : kNone);
-        p2[u][q] = ld4(go ? o + pcol + 128u : kNone);   // +32 floats: the x*W2 columns
+        // kNone + pcol stays past the end of P; a quad past the column edge
+        // reads in-range values of no use (its store is dropped)
+        p1[u][q] = ld4(po[q] + pcol);
+        p2[u][q] = ld4(po[q] + pcol + 128u);           // +32 floats: the x*W2 columns
       }
     }
 #pragma unroll
@@ -592,19 +595,13 @@ __global__ __launch_bounds__(SwCfg<E>::kThreads) void k_swiglu(const char* __res
       f4 s1 = p1[u][0], s2 = p2[u][0];
 #pragma unroll
       for (int q = 1; q < KL; ++q) { s1 += p1[u][q]; s2 += p2[u][q]; }
-      const float inv = 1.0f / float(max(kt[u], 1));
+      const float inv = inv_lds[rt];
       const f4 hk = *reinterpret_cast<const f4*>(h + rt * kLdh + 4 * c);
       uint32_t w[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float dl = hk[e] - silu_fast(s1[e] * inv) * (s2[e] * inv);
-        if constexpr (sizeof(E) == 2) {
-          const uint16_t hi = f32_to_bf16_rne(dl);
-          const uint16_t lo = f32_to_bf16_rne(dl - bf16_to_f32(hi));
-          w[e] = hi | (uint32_t(lo) << 16);
-        } else {
-          w[e] = __float_as_uint(dl);
-        }
+        w[e] = sizeof(E) == 2 ? bf16_hi_lo(dl) : __float_as_uint(dl);
       }
       const u32x4 wv = {w[0], w[1], w[2], w[3]};
       // a quad past the column edge, or a row past M, lands outside the range
