@@ -27,7 +27,7 @@ PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 # kernel behind each profiled stage
-STAGE_KERNEL = {"pack": "k_transpose_pack", "norms": "k_ref_gather", "dist": "k_dist_topk",
+STAGE_KERNEL = {"pack": "k_pack_weights", "norms": "k_ref_gather", "dist": "k_dist_topk",
                 "merge": "k_topk_merge", "proj": "k_ref_proj", "swiglu": "k_swiglu",
                 "w3": "k_w3_quant", "quant": "k_quantize", "gather": "k_gather"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_{workload}.txt")

@@ -77,33 +77,56 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 inline int cdiv(long a, long b) { return int((a + b - 1) / b); }
 
 // ------------------------------------------------------------------ packing
-// dst[map(c) * ld + r] = src[r * cols + c]; map: 0 identity, 1 W1 slot
-// 64*(c/32) + c%32, 2 W2 slot 64*(c/32) + 32 + c%32.  With pair set, each
-// value is written twice, at dst[map(c) * ld + 2r] and [.. + 2r + 1]: the
-// K order of a delta_h row stored as (hi, lo) bf16 pairs.
+// dst[map(c) * ld + r] = src[r * cols + c] for the weight matrices, one
+// launch for all three.  map: 0 identity, 1 W1 slot 64*(c/32) + c%32, 2 W2
+// slot 64*(c/32) + 32 + c%32.  With pair set, each value is written twice,
+// at dst[map(c) * ld + 2r] and [.. + 2r + 1]: the K order of a delta_h row
+// stored as (hi, lo) bf16 pairs.  A workgroup moves one 64 x 64 tile with
+// 16-byte loads and stores (rows and columns are multiples of 32).
+struct PackJob {
+  const void* src;
+  void* dst;
+  int rows, cols, ld, mode, pair, tiles_c, first;
+};
+struct PackJobs { PackJob j[3]; };
+
 template <typename E>
-__global__ __launch_bounds__(256) void k_transpose_pack(const E* __restrict__ src, int rows,
-                                                        int cols, E* __restrict__ dst, int ld,
-                                                        int mode, int pair) {
-  __shared__ E tile[32][33];
-  const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  for (int i = ty; i < 32; i += 8) {
-    const int r = r0 + i, c = c0 + tx;
-    if (r < rows && c < cols) tile[i][tx] = src[size_t(r) * cols + c];
+__global__ __launch_bounds__(256) void k_pack_weights(PackJobs jobs) {
+  constexpr int V = 16 / int(sizeof(E));                 // elements per 16 bytes
+  constexpr int LDT = 64 + 16 / int(sizeof(E));          // padded tile row (keeps 16-byte alignment)
+  __shared__ __attribute__((aligned(16))) E tile[64][LDT];
+  const int w = blockIdx.x;
+  const int ji = w >= jobs.j[2].first ? 2 : (w >= jobs.j[1].first ? 1 : 0);
+  const PackJob& J = jobs.j[ji];
+  const int tr = (w - J.first) / J.tiles_c, tc = (w - J.first) % J.tiles_c;
+  const int r0 = tr * 64, c0 = tc * 64;
+  const E* src = static_cast<const E*>(J.src);
+  E* dst = static_cast<E*>(J.dst);
+  constexpr int kVecRow = 64 / V;                        // 16-byte vectors per tile row
+  for (int u = threadIdx.x; u < 64 * kVecRow; u += 256) {
+    const int rr = u / kVecRow, cv = (u % kVecRow) * V;
+    if (r0 + rr < J.rows && c0 + cv < J.cols)
+      *reinterpret_cast<u32x4*>(&tile[rr][cv]) =
+          *reinterpret_cast<const u32x4*>(src + size_t(r0 + rr) * J.cols + c0 + cv);
   }
   __syncthreads();
-  for (int i = ty; i < 32; i += 8) {
-    const int c = c0 + i, r = r0 + tx;
-    if (c < cols && r < rows) {
-      const int n = mode == 0 ? c : 64 * (c >> 5) + (mode == 2 ? 32 : 0) + (c & 31);
-      const E v = tile[tx][i];
-      if (pair) {
-        dst[size_t(n) * ld + 2 * r] = v;
-        dst[size_t(n) * ld + 2 * r + 1] = v;
-      } else {
-        dst[size_t(n) * ld + r] = v;
-      }
+  for (int u = threadIdx.x; u < 64 * kVecRow; u += 256) {
+    const int c = u / kVecRow, rv = (u % kVecRow) * V;   // output: column c, rows rv .. rv+V-1
+    const int cg = c0 + c, rg = r0 + rv;
+    if (cg >= J.cols || rg >= J.rows) continue;
+    const int n = J.mode == 0 ? cg : 64 * (cg >> 5) + (J.mode == 2 ? 32 : 0) + (cg & 31);
+    E v[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) v[e] = tile[rv + e][c];
+    if (J.pair) {
+      E d[2 * V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) { d[2 * e] = v[e]; d[2 * e + 1] = v[e]; }
+      u32x4* o = reinterpret_cast<u32x4*>(dst + size_t(n) * J.ld + 2 * rg);
+      o[0] = *reinterpret_cast<const u32x4*>(&d[0]);
+      o[1] = *reinterpret_cast<const u32x4*>(&d[V]);
+    } else {
+      *reinterpret_cast<u32x4*>(dst + size_t(n) * J.ld + rg) = *reinterpret_cast<const u32x4*>(&v[0]);
     }
   }
 }
@@ -808,23 +831,20 @@ Workspace plan_workspace(const Shape& sh) {
 
 hipError_t launch_pack_weights(const Shape& sh, const void* w1, const void* w2, const void* w3,
                                char* ws, const Workspace& L, hipStream_t st) {
-  const dim3 blk(256);
-  const dim3 g12(cdiv(sh.d_ff, 32), cdiv(sh.C, 32));
-  const dim3 g3(cdiv(sh.d_c, 32), cdiv(sh.d_ff, 32));
-  const int pair = sh.bf16 ? 1 : 0;
-  if (sh.bf16) {
-    auto* wp = reinterpret_cast<uint16_t*>(ws + L.wp);
-    k_transpose_pack<uint16_t><<<g12, blk, 0, st>>>(static_cast<const uint16_t*>(w1), sh.C, sh.d_ff, wp, sh.C, 1, 0);
-    k_transpose_pack<uint16_t><<<g12, blk, 0, st>>>(static_cast<const uint16_t*>(w2), sh.C, sh.d_ff, wp, sh.C, 2, 0);
-    k_transpose_pack<uint16_t><<<g3, blk, 0, st>>>(static_cast<const uint16_t*>(w3), sh.d_ff, sh.d_c,
-                                                   reinterpret_cast<uint16_t*>(ws + L.w3p), sh.k3, 0, pair);
-  } else {
-    auto* wp = reinterpret_cast<float*>(ws + L.wp);
-    k_transpose_pack<float><<<g12, blk, 0, st>>>(static_cast<const float*>(w1), sh.C, sh.d_ff, wp, sh.C, 1, 0);
-    k_transpose_pack<float><<<g12, blk, 0, st>>>(static_cast<const float*>(w2), sh.C, sh.d_ff, wp, sh.C, 2, 0);
-    k_transpose_pack<float><<<g3, blk, 0, st>>>(static_cast<const float*>(w3), sh.d_ff, sh.d_c,
-                                                reinterpret_cast<float*>(ws + L.w3p), sh.k3, 0, 0);
+  auto tiles = [](int n) { return (n + 63) / 64; };
+  PackJobs J{};
+  J.j[0] = {w1, ws + L.wp, sh.C, sh.d_ff, sh.C, 1, 0, tiles(sh.d_ff), 0};
+  J.j[1] = {w2, ws + L.wp, sh.C, sh.d_ff, sh.C, 2, 0, tiles(sh.d_ff), 0};
+  J.j[2] = {w3, ws + L.w3p, sh.d_ff, sh.d_c, sh.k3, 0, sh.bf16 ? 1 : 0, tiles(sh.d_c), 0};
+  int first = 0;
+  for (auto& j : J.j) {
+    j.first = first;
+    first += tiles(j.rows) * j.tiles_c;
   }
+  if (sh.bf16)
+    k_pack_weights<uint16_t><<<first, 256, 0, st>>>(J);
+  else
+    k_pack_weights<float><<<first, 256, 0, st>>>(J);
   return hipGetLastError();
 }
 
