@@ -46,6 +46,20 @@ the design notes of the repository):
   * dequantised values are q * Delta_h + m_h, exact in float64, then rounded
     once to float32.
 
+Restore (read side, [RKV] §2.5 and the implementation note of §2.1):
+
+  8. for a selected non-reference token: KV^ = z~ W_d + mean of its stored
+     references, W_d a bias-free linear map [d_c][2 d_k]; a reference token
+     restores to its stored row                          ([RKV] §2.5 boxed eq.)
+  9. split KV^ into K (first N*D coordinates) and V; the restored pre-RoPE
+     key is rotated at the token's own position                ([RKV] §2.1)
+
+Readings for the restore: z~ is the dequantised record of step 7; the
+references are the stored rows kv_j at input precision; RoPE pairs
+coordinate d of a head with d + D/2 ("rotate half") and turns pair i by
+position * theta^(-2i/D), with no frequency scaling; theta <= 0 leaves K
+unrotated; an index outside [0, B*T) yields a NaN row.
+
 Parity status: the selection, mean, compressor and quantiser are pinned by
 the tests in ``tests/test_oracle_pins.py`` (brute force, closed-form
 identities, special cases and hand-derived golden values).  The actual
@@ -296,4 +310,55 @@ def gather(codes: np.ndarray, scale: np.ndarray, zmin: np.ndarray, idx: np.ndarr
         sel = idx[ok]
         q = unpack_codes(codes[sel], b, d_c)
         out[ok] = dequantize(q, scale[sel], zmin[sel], g)
+    return out
+
+
+# ---------------------------------------------------------------- restore
+def rope_inv_freq(D: int, theta: float) -> np.ndarray:
+    """Rotation rate of pair i of a head, theta^(-2i/D), i < D/2 (rotary
+    position embedding applied to restored keys, [RKV] §2.1 note)."""
+    i = np.arange(D // 2, dtype=F64)
+    return np.power(F64(theta), -2.0 * i / F64(D))
+
+
+def apply_rope(k_flat: np.ndarray, pos: int, N: int, D: int, theta: float) -> np.ndarray:
+    """Rotate the N heads of one pre-RoPE key at position `pos`: coordinate d
+    and d + D/2 of a head form pair i = d, turned by the angle pos * rate_i."""
+    x = np.asarray(k_flat, F64).reshape(N, D)
+    if theta <= 0:
+        return x.reshape(-1).copy()
+    ang = F64(pos) * rope_inv_freq(D, theta)
+    c, sn = np.cos(ang), np.sin(ang)
+    x1, x2 = x[:, : D // 2], x[:, D // 2:]
+    return np.concatenate([x1 * c - x2 * sn, x2 * c + x1 * sn], axis=1).reshape(-1)
+
+
+def restore(codes: np.ndarray, scale: np.ndarray, zmin: np.ndarray, ref_idx: np.ndarray,
+            kv: np.ndarray, Wd: np.ndarray, idx: np.ndarray, *, s: int, N: int, D: int,
+            g: int, b: int, d_c: int, rope_theta: float) -> np.ndarray:
+    """Restore the selected tokens' K|V rows ([RKV] §2.5): z~ W_d plus the mean
+    of the token's stored references, reference tokens as stored; then K is
+    rotated at the token's position.
+
+    codes/scale/zmin/ref_idx are flattened over [B*T] (ref_idx rows hold
+    reference positions, -1 pads); kv is [B][T][C] (only reference rows are
+    read); idx are flat b*T + t.  Returns fp64 [len(idx)][C]; NaN rows for
+    indices outside [0, B*T)."""
+    Bn, T, C = kv.shape
+    idx = np.asarray(idx, dtype=np.int64)
+    out = np.full((len(idx), C), np.nan, dtype=F64)
+    Wd = np.asarray(Wd, F64)
+    for n, fl in enumerate(idx):
+        if fl < 0 or fl >= Bn * T:
+            continue
+        bq, t = divmod(int(fl), T)
+        if t % s == 0:
+            row = np.asarray(kv[bq, t], F64)
+        else:
+            q = unpack_codes(codes[fl:fl + 1], b, d_c)
+            zt = dequantize(q, scale[fl:fl + 1], zmin[fl:fl + 1], g)[0].astype(F64)
+            R = [int(p) for p in ref_idx[fl] if p >= 0]
+            row = zt @ Wd + reference_mean(kv[bq], R)
+        out[n, : N * D] = apply_rope(row[: N * D], t, N, D, rope_theta)
+        out[n, N * D:] = row[N * D:]
     return out

@@ -7,6 +7,7 @@ their inputs from here, so the two sides always see the same bits.
 """
 from .configs import CONFIGS, RkvConfig, config_by_name
 from .generate import (
+    decoder_weight,
     Workload,
     bf16_bits_to_f32,
     f32_to_bf16_bits,
@@ -14,6 +15,7 @@ from .generate import (
 )
 
 __all__ = [
+    "decoder_weight",
     "CONFIGS",
     "RkvConfig",
     "config_by_name",

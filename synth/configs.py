@@ -34,6 +34,7 @@ class RkvConfig:
     noise: float = 0.0         # noise scale of the clustered recipes
     gather_frac: Optional[float] = None  # None: gather every position
     seed: int = 0
+    rope_theta: float = 10000.0  # RoPE base of the model whose keys are restored
     # multimodal recipe only
     mm_blocks: int = 0
     mm_block_len: int = 0
@@ -59,21 +60,22 @@ TINY = RkvConfig(
 
 LLAMA8K = RkvConfig(
     name="llama8b_T8k", B=1, T=8192, N=8, D=128, d_ff=1024, d_c=512, k=4, g=32,
-    b=4, stride=16, dtype="bf16", kind="proto", n_protos=256, noise=0.25)
+    b=4, stride=16, dtype="bf16", kind="proto", n_protos=256, noise=0.25,
+    rope_theta=500000.0)
 
 LLAMA32K = LLAMA8K.with_(name="llama8b_T32k", T=32768, gather_frac=0.30)
 
 QWEN_LIKE = RkvConfig(
     name="qwen7b_like_B2_T32k", B=2, T=32768, N=4, D=128, d_ff=512, d_c=256,
     k=4, g=32, b=4, stride=16, dtype="bf16", kind="proto_t4", n_protos=512,
-    noise=0.25)
+    noise=0.25, rope_theta=1000000.0)
 
 MM_INT2 = RkvConfig(
     name="multimodal_int2_B4_T16k", B=4, T=16384, N=8, D=128, d_ff=1024,
     d_c=512, k=4, g=32, b=2, stride=16, dtype="bf16", kind="multimodal",
     gather_frac=0.10, mm_blocks=24, mm_block_len=576, mm_block_protos=32,
     mm_image_noise=0.2, mm_text_protos=256, mm_text_noise=0.4, mm_run_min=32,
-    mm_run_max=128)
+    mm_run_max=128, rope_theta=500000.0)
 
 CONFIGS = [TINY, LLAMA8K, LLAMA32K, QWEN_LIKE, MM_INT2]
 

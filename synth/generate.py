@@ -155,3 +155,14 @@ def generate(cfg: RkvConfig) -> Workload:
     return Workload(cfg=cfg, kv=_finish(kv, cfg.dtype), w1=_finish(w1, cfg.dtype),
                     w2=_finish(w2, cfg.dtype), w3=_finish(w3, cfg.dtype),
                     gather_idx=gidx, segments=segments)
+
+
+def decoder_weight(cfg: RkvConfig) -> np.ndarray:
+    """W_d [d_c][C] of the linear restore map z -> z W_d, N(0, 1/d_c).
+
+    Drawn from its own stream, ``default_rng((seed, 1))``, so the encode
+    workloads above keep their draws.  Rounded to bf16 for bf16 workloads
+    (uint16 bits), float32 otherwise."""
+    rng = np.random.default_rng((cfg.seed, 1))
+    wd = rng.standard_normal((cfg.d_c, cfg.C), dtype=np.float32) * np.float32(1.0 / np.sqrt(cfg.d_c))
+    return _finish(wd, cfg.dtype)

@@ -363,3 +363,121 @@ def test_zero_references_reduce_z_to_library_compressor():
     x = torch.from_numpy(kv[ts])
     want = (torch.nn.functional.silu(x @ torch.from_numpy(W1)) * (x @ torch.from_numpy(W2))) @ torch.from_numpy(W3)
     np.testing.assert_allclose(out["z"], want.numpy(), rtol=1e-12, atol=1e-13)
+
+
+# ------------------------------------------------------------------ restore
+def _rope_gold():
+    vals = {}
+    with open(os.path.join(GOLD, "rope_example.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            key, *rest = line.split()
+            vals[key] = [float(v) for v in rest]
+    return vals
+
+
+def test_rope_matches_hand_worked_example():
+    """[RKV] §2.1 note; values worked by hand in tests/golden/rope_example.txt."""
+    g = _rope_gold()
+    y = O.apply_rope(np.array(g["x"]), int(g["position"][0]), 1, int(g["D"][0]), g["theta"][0])
+    np.testing.assert_allclose(y, g["y"], rtol=0, atol=1e-15)
+
+
+def test_rope_position_zero_and_disabled_are_identity():
+    x = np.random.default_rng(3).standard_normal(2 * 16)
+    np.testing.assert_array_equal(O.apply_rope(x, 0, 2, 16, 10000.0), x)
+    np.testing.assert_array_equal(O.apply_rope(x, 77, 2, 16, 0.0), x)
+
+
+def test_rope_preserves_pair_norms_and_relative_positions():
+    """A rotation keeps each (d, d + D/2) pair's length, and the score of two
+    rotated vectors depends only on their position difference."""
+    rng = np.random.default_rng(4)
+    N, D, th = 2, 16, 500000.0
+    q, k = rng.standard_normal(N * D), rng.standard_normal(N * D)
+    rq = O.apply_rope(q, 1234, N, D, th).reshape(N, D)
+    qq = q.reshape(N, D)
+    np.testing.assert_allclose(rq[:, :D // 2] ** 2 + rq[:, D // 2:] ** 2,
+                               qq[:, :D // 2] ** 2 + qq[:, D // 2:] ** 2, rtol=1e-12)
+    s1 = O.apply_rope(q, 900, N, D, th) @ O.apply_rope(k, 250, N, D, th)
+    s2 = O.apply_rope(q, 1650, N, D, th) @ O.apply_rope(k, 1000, N, D, th)
+    assert abs(s1 - s2) < 1e-9 * (1 + abs(s1))
+
+
+@pytest.fixture(scope="module")
+def tiny_encoded(tiny):
+    w, kv, W1, W2, W3 = tiny
+    c = TINY
+    enc = O.encode(kv[None], W1, W2, W3, k=c.k, g=c.g, b=c.b, s=c.stride)
+    return enc
+
+
+def _restore(enc, kv, Wd, idx, theta):
+    c = TINY
+    flat = lambda a: a.reshape(-1, *a.shape[2:])
+    return O.restore(flat(enc["codes"]), flat(enc["scale"]), flat(enc["zmin"]), flat(enc["ref_idx"]),
+                     kv[None], Wd, np.asarray(idx), s=c.stride, N=c.N, D=c.D, g=c.g, b=c.b,
+                     d_c=c.d_c, rope_theta=theta)
+
+
+def test_restore_reference_tokens_are_their_stored_rows(tiny, tiny_encoded):
+    """[RKV] §2.4/§2.5: references are stored as they are; only their keys are rotated."""
+    w, kv, *_ = tiny
+    Wd = np.random.default_rng(5).standard_normal((TINY.d_c, TINY.C))
+    refs = np.arange(0, TINY.T, TINY.stride)
+    out = _restore(tiny_encoded, kv, Wd, refs, 0.0)
+    np.testing.assert_array_equal(out, kv[refs])
+    out_r = _restore(tiny_encoded, kv, Wd, refs, 10000.0)
+    nd = TINY.N * TINY.D
+    for n, t in enumerate(refs):
+        np.testing.assert_allclose(out_r[n, :nd], O.apply_rope(kv[t, :nd], t, TINY.N, TINY.D, 10000.0))
+        np.testing.assert_array_equal(out_r[n, nd:], kv[t, nd:])
+
+
+def test_restore_of_a_zero_record_or_zero_decoder_is_the_reference_mean(tiny, tiny_encoded):
+    """f_d(0) = 0 and a zero W_d leave exactly the mean of the stored references ([RKV] §2.5)."""
+    w, kv, *_ = tiny
+    enc = {k: v.copy() for k, v in tiny_encoded.items()}
+    t = 37
+    enc["codes"][0, t] = 0
+    enc["scale"][0, t] = 0
+    enc["zmin"][0, t] = 0
+    Wd = np.random.default_rng(6).standard_normal((TINY.d_c, TINY.C))
+    R = [int(p) for p in tiny_encoded["ref_idx"][0, t] if p >= 0]
+    mean = kv[R].mean(axis=0)
+    np.testing.assert_allclose(_restore(enc, kv, Wd, [t], 0.0)[0], mean, rtol=1e-15, atol=1e-15)
+    np.testing.assert_allclose(_restore(tiny_encoded, kv, np.zeros_like(Wd), [t], 0.0)[0], mean,
+                               rtol=1e-15, atol=1e-15)
+
+
+def test_restore_with_an_identity_decoder_returns_the_token_within_the_quantiser_bound():
+    """With d_c = 2 d_k, W_d = I and records that quantise kv_t - mean, the
+    restore is kv_t up to the quantiser's error: at most Delta_h / 2 plus the
+    fp16 slack of the record per coordinate ([RKV] §2.4, §2.5)."""
+    c = TINY.with_(d_c=TINY.C)
+    rng = np.random.default_rng(8)
+    kv = rng.standard_normal((1, 40, c.C))
+    t = 21
+    pos = O.candidate_pool(t, c.stride)
+    R, _ = O.retrieve(kv[0], t, c.stride, c.k)
+    mean = O.reference_mean(kv[0], R)
+    q, dh, mh = O.quantize((kv[0, t] - mean)[None].astype(np.float32), c.g, c.b)
+    codes = np.zeros((40, c.d_c * c.b // 8), np.uint8)
+    scale = np.zeros((40, c.d_c // c.g), np.float16)
+    zmin = np.zeros_like(scale)
+    codes[t] = O.pack_codes(q, c.b)[0]
+    scale[t], zmin[t] = dh[0], mh[0]
+    ref_idx = np.full((40, c.k), -1, np.int64)
+    ref_idx[t, :len(R)] = np.sort(R)
+    out = O.restore(codes, scale, zmin, ref_idx, kv, np.eye(c.C), np.array([t]), s=c.stride,
+                    N=c.N, D=c.D, g=c.g, b=c.b, d_c=c.d_c, rope_theta=0.0)[0]
+    step = np.repeat(dh[0].astype(np.float64), c.g)
+    assert np.all(np.abs(out - kv[0, t]) <= step / 2 + 1e-3 * step + 1e-6)
+
+
+def test_restore_out_of_range_rows_are_nan(tiny, tiny_encoded):
+    w, kv, *_ = tiny
+    Wd = np.zeros((TINY.d_c, TINY.C))
+    out = _restore(tiny_encoded, kv, Wd, [-1, TINY.T, 5], 0.0)
+    assert np.isnan(out[0]).all() and np.isnan(out[1]).all() and not np.isnan(out[2]).any()
