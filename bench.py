@@ -115,6 +115,50 @@ def cpu_baseline(w, n_tokens: int, seed: int = 0):
                       f"quantiser), numpy fp64; {dt:.2f} s"}
 
 
+def bench_restore(R, cfg, w, p, kv, out, idx, stream, args):
+    """rkv_restore of the gathered rows (decoder product z~ W_d, reference
+    mean, RoPE on K; bf16 out), timed on its own after the encode steps; the
+    records are those the timed encode wrote."""
+    import numpy as np
+    import torch
+    from synth import decoder_weight
+    dev = kv.device
+    wd = decoder_weight(cfg)
+    if cfg.dtype == "bf16":
+        d_wd = torch.from_numpy(np.ascontiguousarray(wd).view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        d_wd = torch.from_numpy(wd).to(dev)
+    n = idx.numel()
+    rout = torch.empty((n, cfg.C), dtype=torch.bfloat16, device=dev)
+    wsb = R.rkv_restore_workspace_bytes(p, n)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+    def call():
+        R.rkv_restore(p, out.codes, out.scale, out.zmin, out.ref_idx, kv, d_wd, idx, n,
+                      cfg.rope_theta, rout, "bf16", ws, wsb, stream)
+
+    for _ in range(max(args.warmup, 1)):
+        call()
+    st = R.STAGES.index("restore")
+    R.rkv_profile_begin(1 << st)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    tot, cnt = R.rkv_profile_read(st)
+    R.rkv_profile_begin(0)
+    flops = 2.0 * n * cfg.d_c * cfg.C           # z~ W_d, the method's product
+    return {"rows": n, "ms_per_call": round(ms, 4), "rows_per_s": round(n / (ms * 1e-3), 1),
+            "stage_ms": round(tot / cnt, 4),
+            "decoder_tflops_algorithmic": round(flops / (tot / cnt * 1e-3) / 1e12, 2),
+            "out_dtype": "bf16", "rope_theta": cfg.rope_theta}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -123,6 +167,8 @@ def main():
     ap.add_argument("--workload", default="llama8b_T32k")
     ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-restore", action="store_true",
+                    help="skip the separate restore measurement (rkv_restore of the gathered rows)")
     ap.add_argument("--copy-check-mb", type=int, default=0,
                     help="before the timed region, run one plain device copy of this many MiB "
                          "(a reference of known size for hardware byte counters)")
@@ -244,6 +290,8 @@ def main():
         "encode_ms_stage_sum": round(encode_ms, 4),
         "roofline": roof,
     }
+    if not args.no_restore:
+        line["restore"] = bench_restore(R, cfg, w, p, kv, out, idx, stream, args)
     if not args.no_cpu_baseline:
         print(f"[bench] cpu baseline on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens)

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define RKV_ABI_VERSION 1
+#define RKV_ABI_VERSION 2
 
 typedef enum {
   RKV_OK = 0,
@@ -134,8 +134,38 @@ rkv_status rkv_select(const rkv_params* p, const void* kv, int32_t* ref_idx,
                       void* workspace, size_t workspace_bytes,
                       hipStream_t stream);
 
+/* Read side: restore the K|V rows of selected tokens ([RKV] §2.5 boxed eq.;
+ * §2.7 decode step 3; §2.1 note on rotating restored keys).
+ *
+ * For each idx[i] = b*T + t:
+ *   non-reference t:  KV^ = z~ W_d + mean of kv_j over the token's ref_idx
+ *                     row (j >= 0), z~ = q * Delta_h + m_h of its record
+ *                     (fmaf, as rkv_dequant_gather), W_d bias-free
+ *   reference t:      KV^ = kv_t (references are stored as they are)
+ *   K = KV^[0, N*D) is then rotated at position t when rope_theta > 0:
+ *   coordinate d and d + D/2 of a head form pair i = d, turned by the angle
+ *   t * rope_theta^(-2i/D) ("rotate half"; angles reduced in fp64, sin/cos
+ *   in fp32); V = KV^[N*D, C) as is.  rope_theta <= 0 leaves K unrotated.
+ * Inputs:  codes, scale, zmin, ref_idx as rkv_encode wrote them ([B][T]...);
+ *          kv [B][T][C] in p->dtype: the stored references (only rows at
+ *          reference positions are read); wd [d_c][C] in p->dtype, used as
+ *          z * W_d; idx [n_idx] int32, any order, duplicates allowed.
+ * Output:  out [n_idx][C], float (RKV_F32) or bf16 rounded to nearest even
+ *          (RKV_BF16); an index outside [0, B*T) yields a row of NaN.
+ * workspace: at least rkv_restore_workspace_bytes(p, n_idx) bytes.
+ * Arithmetic: z~ enters the bf16 matrix cores as a (hi, lo) bf16 pair (fp32
+ * inputs use the fp32 matrix cores); products accumulate in fp32.
+ * GPU-path limit (RKV_ERR_UNSUPPORTED otherwise): D in {16, 32, 64, 128}. */
+size_t rkv_restore_workspace_bytes(const rkv_params* p, int32_t n_idx);
+rkv_status rkv_restore(const rkv_params* p, const uint8_t* codes,
+                       const uint16_t* scale, const uint16_t* zmin,
+                       const int32_t* ref_idx, const void* kv, const void* wd,
+                       const int32_t* idx, int32_t n_idx, float rope_theta,
+                       void* out, rkv_dtype out_dtype, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
 /* Observability.  Stages of the encode path, in launch order, plus the
- * gather.  rkv_profile_begin(mask) makes later rkv_encode /
+ * gather and the restore.  rkv_profile_begin(mask) makes later rkv_encode /
  * rkv_dequant_gather calls on this process record a HIP event pair around
  * every stage whose bit (1u << stage) is set in mask, and clears previous
  * records; mask 0 turns recording off (the default).  rkv_profile_read()
@@ -152,7 +182,8 @@ typedef enum {
   RKV_STAGE_W3 = 6,      /* latent z = delta_h W3 + group quantiser         */
   RKV_STAGE_QUANT = 7,   /* stand-alone quantiser (rkv_quantize)            */
   RKV_STAGE_GATHER = 8,  /* gather-dequantise                               */
-  RKV_STAGE_COUNT = 9
+  RKV_STAGE_RESTORE = 9, /* restore: dequantise, decoder product, mean, RoPE */
+  RKV_STAGE_COUNT = 10
 } rkv_stage;
 rkv_status rkv_profile_begin(uint32_t stage_mask);
 rkv_status rkv_profile_read(int32_t stage, double* total_ms, int64_t* launches);

@@ -39,10 +39,12 @@ EXPORTS = (
     "rkv_abi_version",
     "rkv_profile_begin",
     "rkv_profile_read",
+    "rkv_restore_workspace_bytes",
+    "rkv_restore",
 )
 
-STAGES = ("pack", "norms", "dist", "merge", "proj", "swiglu", "w3", "quant", "gather")
-RKV_ABI_VERSION = 1
+STAGES = ("pack", "norms", "dist", "merge", "proj", "swiglu", "w3", "quant", "gather", "restore")
+RKV_ABI_VERSION = 2
 
 
 class rkv_params(ctypes.Structure):
@@ -91,6 +93,11 @@ def lib() -> ctypes.CDLL:
         L.rkv_profile_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double),
                                        ctypes.POINTER(ctypes.c_int64)]
         L.rkv_profile_read.restype = ctypes.c_int
+        L.rkv_restore_workspace_bytes.argtypes = [P, i32]
+        L.rkv_restore_workspace_bytes.restype = sz
+        L.rkv_restore.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, i32, ctypes.c_float, vp,
+                                  ctypes.c_int, vp, sz, vp]
+        L.rkv_restore.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -187,3 +194,18 @@ def rkv_profile_read(stage: int):
     n = ctypes.c_int64()
     _check("rkv_profile_read", lib().rkv_profile_read(int(stage), ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value
+
+
+def rkv_restore_workspace_bytes(p: rkv_params, n_idx: int) -> int:
+    return int(lib().rkv_restore_workspace_bytes(ctypes.byref(p), int(n_idx)))
+
+
+def rkv_restore(p: rkv_params, codes, scale, zmin, ref_idx, kv, wd, idx, n_idx: int,
+                rope_theta: float, out, out_dtype, workspace, workspace_bytes: int, stream=None,
+                *, check: bool = True) -> int:
+    if isinstance(out_dtype, str):
+        out_dtype = {"f32": RKV_F32, "bf16": RKV_BF16}[out_dtype]
+    st = lib().rkv_restore(ctypes.byref(p), _p(codes), _p(scale), _p(zmin), _p(ref_idx), _p(kv),
+                           _p(wd), _p(idx), int(n_idx), float(rope_theta), _p(out),
+                           int(out_dtype), _p(workspace), int(workspace_bytes), _s(stream))
+    return _check("rkv_restore", st) if check else st

@@ -271,4 +271,53 @@ rkv_status rkv_dequant_gather(const rkv_params* p, const uint8_t* codes, const u
   return ok();
 }
 
+// Restore shares the encode's parameter checks and needs whole heads per
+// 128-column tile (the rotation partner d +- D/2 sits in the same tile).
+static rkv_status check_restore(const rkv_params* p, int32_t n_idx) {
+  rkv_status st = check_params(p);
+  if (st != RKV_OK) return st;
+  if (p->D % 16 != 0 || 128 % p->D != 0)
+    return fail(RKV_ERR_UNSUPPORTED, "restore needs D in {16, 32, 64, 128} (got %d)", p->D);
+  if (n_idx < 0) return fail(RKV_ERR_INVALID_ARG, "n_idx must be non-negative (got %d)", n_idx);
+  return RKV_OK;
+}
+
+size_t rkv_restore_workspace_bytes(const rkv_params* p, int32_t n_idx) {
+  if (check_restore(p, n_idx) != RKV_OK) return 0;
+  return rkv::plan_restore(shape_of(p), n_idx).total;
+}
+
+rkv_status rkv_restore(const rkv_params* p, const uint8_t* codes, const uint16_t* scale,
+                       const uint16_t* zmin, const int32_t* ref_idx, const void* kv,
+                       const void* wd, const int32_t* idx, int32_t n_idx, float rope_theta,
+                       void* out, rkv_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  rkv_status st = check_restore(p, n_idx);
+  if (st != RKV_OK) return st;
+  if (out_dtype != RKV_F32 && out_dtype != RKV_BF16)
+    return fail(RKV_ERR_INVALID_ARG, "unknown out_dtype %d", int(out_dtype));
+  if (!(rope_theta == rope_theta)) return fail(RKV_ERR_INVALID_ARG, "rope_theta is NaN");
+  if (n_idx == 0) return ok();
+  RKV_NEED_PTR(codes);
+  RKV_NEED_PTR(scale);
+  RKV_NEED_PTR(zmin);
+  RKV_NEED_PTR(ref_idx);
+  RKV_NEED_PTR(kv);
+  RKV_NEED_PTR(wd);
+  RKV_NEED_PTR(idx);
+  RKV_NEED_PTR(out);
+  RKV_NEED_PTR(workspace);
+  const rkv::Shape sh = shape_of(p);
+  const rkv::RestoreWorkspace L = rkv::plan_restore(sh, n_idx);
+  if (workspace_bytes < L.total)
+    return fail(RKV_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
+  hipError_t e;
+  RKV_STAGE(RKV_STAGE_RESTORE,
+            rkv::launch_restore(sh, p->N, p->D, codes, scale, zmin, ref_idx, kv, wd, idx, n_idx,
+                                rope_theta, out, out_dtype == RKV_BF16,
+                                static_cast<char*>(workspace), L, stream),
+            "restore");
+  return ok();
+}
+
 }  // extern "C"

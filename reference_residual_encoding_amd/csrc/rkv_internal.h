@@ -52,4 +52,16 @@ hipError_t launch_gather(const uint8_t* codes, const uint16_t* scale, const uint
                          const int32_t* idx, int64_t n_idx, int64_t total_rows, int d_c, int g,
                          int b, void* out, bool out_bf16, hipStream_t st);
 
+// Restore ([RKV] §2.5): workspace of the decoder product for n_idx rows.
+struct RestoreWorkspace {
+  int kr;               // contraction length (2*d_c bf16 hi/lo pairs, d_c fp32)
+  size_t wdp, zt, total;
+};
+RestoreWorkspace plan_restore(const Shape& sh, int64_t n_idx);
+hipError_t launch_restore(const Shape& sh, int N, int D, const uint8_t* codes,
+                          const uint16_t* scale, const uint16_t* zmin, const int32_t* ref_idx,
+                          const void* kv, const void* wd, const int32_t* idx, int n_idx,
+                          float theta, void* out, bool out_bf16, char* ws,
+                          const RestoreWorkspace& L, hipStream_t st);
+
 }  // namespace rkv

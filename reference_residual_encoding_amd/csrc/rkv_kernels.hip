@@ -745,6 +745,203 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ z, i
   }
 }
 
+// ------------------------------------------------------------------ restore
+// Read side ([RKV] §2.5): KV^ = z~ W_d + mean of the token's stored
+// references (a reference token is its own single reference, with z~ = 0),
+// split into K | V, and K rotated at the token's own position ([RKV] §2.1
+// note).  Two kernels: the selected records are dequantised into the A
+// operand of the decoder product, then the product's epilogue adds the
+// reference mean and applies the rotation.
+template <typename E> struct RsCfg {
+  static constexpr int BM = 256, BN = 256, SB = 128, NS = 2, WGM = 2, WGN = 4;
+  static constexpr int kThreads = 64 * WGM * WGN;
+};
+template <> struct RsCfg<float> {
+  static constexpr int BM = 256, BN = 128, SB = 128, NS = 2, WGM = 2, WGN = 2;
+  static constexpr int kThreads = 64 * WGM * WGN;
+};
+
+// z~ of each selected token as the decoder product's A row: bf16 runs store
+// a (hi, lo) bf16 pair per latent (K positions 2c, 2c + 1), fp32 runs the
+// float; zeros for reference tokens and indices outside [0, B*T).  z~ is
+// fmaf(q, Delta_h, m_h), as rkv_dequant_gather gives it.
+template <typename E, int BITS>
+__global__ __launch_bounds__(256) void k_restore_prep(const uint8_t* __restrict__ codes,
+                                                      const uint16_t* __restrict__ scale,
+                                                      const uint16_t* __restrict__ zmin,
+                                                      const int32_t* __restrict__ idx,
+                                                      int64_t n_idx, int64_t total_rows, int T,
+                                                      int s, int d_c, int g,
+                                                      uint32_t* __restrict__ zt) {
+  constexpr uint32_t kMask = (1u << BITS) - 1;
+  const int64_t units = n_idx * (d_c / 8);
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t u = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; u < units; u += stride) {
+    const int64_t i = u / (d_c / 8);
+    const int o = int(u - i * (d_c / 8)) * 8;
+    const int64_t src = idx[i];
+    const bool live = src >= 0 && src < total_rows && (src % T) % s != 0;
+    const int64_t sr = live ? src : 0;
+    uint32_t word;
+    if constexpr (BITS == 4)
+      word = *reinterpret_cast<const uint32_t*>(codes + sr * (d_c / 2) + o / 2);
+    else
+      word = *reinterpret_cast<const uint16_t*>(codes + sr * (d_c / 4) + o / 4);
+    const int64_t grp = sr * (d_c / g) + o / g;
+    const float dh = f16_bits_to_f32(scale[grp]), mh = f16_bits_to_f32(zmin[grp]);
+    uint32_t w[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = live ? fmaf(float((word >> (BITS * e)) & kMask), dh, mh) : 0.0f;
+      w[e] = sizeof(E) == 2 ? bf16_hi_lo(v) : __float_as_uint(v);
+    }
+    u32x4* dst = reinterpret_cast<u32x4*>(zt + i * d_c + o);
+    dst[0] = u32x4{w[0], w[1], w[2], w[3]};
+    dst[1] = u32x4{w[4], w[5], w[6], w[7]};
+  }
+}
+
+// One workgroup: BM selected tokens x BN columns of KV^.  D divides BN, so a
+// tile holds whole heads and every rotation partner (d +- D/2) is in it.
+template <typename E, int KL>
+__global__ __launch_bounds__(RsCfg<E>::kThreads) void k_restore(
+    const char* __restrict__ zt, const char* __restrict__ wdp, int K, const int32_t* __restrict__ idx,
+    int n_idx, int64_t total_rows, int T, int s, int k, const int32_t* __restrict__ ref_idx,
+    const char* __restrict__ kv, int C, int ND, int D, float theta, void* __restrict__ out,
+    int out_bf16) {
+  using CF = RsCfg<E>;
+  constexpr int BM = CF::BM, BN = CF::BN, WGM = CF::WGM, WGN = CF::WGN, NT = CF::kThreads;
+  static_assert(WGM == 2, "the epilogue stages one wave-row (half the tile) at a time");
+  constexpr int LD = kEpiLd(BN);
+  constexpr int HALF = BM / 2;
+  constexpr int kMain = mainloop_lds<E, BM, BN, CF::SB, CF::NS, WGM, WGN>();
+  constexpr int kStaged = kMain > HALF * LD * 4 ? kMain : HALF * LD * 4;
+  __shared__ __attribute__((aligned(1024))) char lds[kStaged + BM * (KL + 2) * 4 + 64 * 8];
+  int* rows_lds = reinterpret_cast<int*>(lds + kStaged);            // [BM][KL] kv rows, -1 none
+  float* inv_lds = reinterpret_cast<float*>(lds + kStaged + BM * KL * 4);  // [BM] 1 / count
+  int* pos_lds = reinterpret_cast<int*>(lds + kStaged + BM * (KL + 1) * 4);  // [BM] t, -1 invalid
+  double* rate = reinterpret_cast<double*>(lds + kStaged + BM * (KL + 2) * 4);  // [D/2] theta^(-2i/D)
+  const int tiles_m = (n_idx + BM - 1) / BM;
+  const int mt = blockIdx.x % tiles_m, nt = blockIdx.x / tiles_m;
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int tid = threadIdx.x;
+  for (int r = tid; r < BM; r += NT) {
+    const int i = m0 + r;
+    int rows[KL];
+#pragma unroll
+    for (int q = 0; q < KL; ++q) rows[q] = -1;
+    int cnt = 0, pos = -1;
+    if (i < n_idx) {
+      const int64_t fl = idx[i];
+      if (fl >= 0 && fl < total_rows) {
+        const int b = int(fl / T), t = int(fl % T);
+        pos = t;
+        if (t % s == 0) {
+          rows[0] = int(fl);
+          cnt = 1;
+        } else {
+#pragma unroll
+          for (int q = 0; q < KL; ++q) {
+            const int p = q < k ? ref_idx[fl * k + q] : -1;
+            if (p >= 0) { rows[q] = b * T + p; ++cnt; }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < KL; ++q) rows_lds[r * KL + q] = rows[q];
+    inv_lds[r] = 1.0f / float(max(cnt, 1));
+    pos_lds[r] = pos;
+  }
+  if (theta > 0.0f)
+    for (int i = tid; i < D / 2; i += NT) rate[i] = pow(double(theta), -2.0 * i / double(D));
+  const size_t rowa = size_t(K) * sizeof(E);
+  auto rowA = [&](int r) { return zt + size_t(min(m0 + r, n_idx - 1)) * rowa; };
+  auto rowB = [&](int r) { return wdp + size_t(min(n0 + r, C - 1)) * rowa; };
+  f32x16 acc[BM / WGM / 32][BN / WGN / 32];
+  tile_product<E, BM, BN, CF::SB, CF::NS, WGM, WGN>(rowA, rowB, int(rowa), lds, acc);
+
+  float* tile = reinterpret_cast<float*>(lds);
+  constexpr int kV = BN / 8;                             // 8-column vectors per row
+  const size_t kvrow = size_t(C) * sizeof(E);
+  for (int half = 0; half < 2; ++half) {
+    acc_to_lds<BM, BN, WGM, WGN>(acc, tile, LD, half);
+    __syncthreads();
+    // a. + mean of the stored reference rows (NaN for an invalid index)
+    for (int u = tid; u < HALF * kV; u += NT) {
+      const int rl = u / kV, cv = (u % kV) * 8, rt = half * HALF + rl, col = n0 + cv;
+      if (col >= C) continue;
+      float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int q = 0; q < KL; ++q) {
+        const int row = rows_lds[rt * KL + q];
+        const char* src = kv + size_t(max(row, 0)) * kvrow + size_t(col) * sizeof(E);
+        float v[8];
+        if constexpr (sizeof(E) == 2) {
+          const u32x4 w = *reinterpret_cast<const u32x4*>(src);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[2 * e] = __uint_as_float(w[e] << 16);
+            v[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+          }
+        } else {
+          const float4 a = reinterpret_cast<const float4*>(src)[0];
+          const float4 c2 = reinterpret_cast<const float4*>(src)[1];
+          v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+          v[4] = c2.x; v[5] = c2.y; v[6] = c2.z; v[7] = c2.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m[e] += row >= 0 ? v[e] : 0.0f;
+      }
+      const float inv = inv_lds[rt];
+      const bool bad = pos_lds[rt] < 0;
+      float* tr = tile + rl * LD + cv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) tr[e] = bad ? __builtin_nanf("") : tr[e] + m[e] * inv;
+    }
+    __syncthreads();
+    // b. rotate K at the token's position, write the row
+    for (int u = tid; u < HALF * kV; u += NT) {
+      const int rl = u / kV, cv = (u % kV) * 8, rt = half * HALF + rl, col = n0 + cv;
+      const int i = m0 + rt;
+      if (col >= C || i >= n_idx) continue;
+      float y[8];
+      const float* tr = tile + rl * LD + cv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = tr[e];
+      const int pos = pos_lds[rt];
+      if (theta > 0.0f && col < ND && pos >= 0) {
+        const int d0 = col % D;                          // 8 columns in one half of a head
+        const bool first = d0 < D / 2;
+        const float* pr = tr + (first ? D / 2 : -(D / 2));
+        const int i0 = first ? d0 : d0 - D / 2;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          // angle pos * rate reduced to [-pi, pi] in fp64, then sin/cos in fp32
+          const double a = double(pos) * rate[i0 + e];
+          const float ar = float(a - 6.283185307179586 * rint(a * 0.15915494309189535));
+          float sn, cs;
+          sincosf(ar, &sn, &cs);
+          y[e] = first ? tr[e] * cs - pr[e] * sn : tr[e] * cs + pr[e] * sn;
+        }
+      }
+      if (out_bf16) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w[e] = uint32_t(f32_to_bf16_rne(y[2 * e])) | (uint32_t(f32_to_bf16_rne(y[2 * e + 1])) << 16);
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + size_t(i) * C + col) =
+            u32x4{w[0], w[1], w[2], w[3]};
+      } else {
+        float4* o = reinterpret_cast<float4*>(static_cast<float*>(out) + size_t(i) * C + col);
+        o[0] = make_float4(y[0], y[1], y[2], y[3]);
+        o[1] = make_float4(y[4], y[5], y[6], y[7]);
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // ------------------------------------------------------------------ gather-dequantise
 template <int BITS, bool BF16>
 __global__ __launch_bounds__(256) void k_gather(const uint8_t* __restrict__ codes,
@@ -1000,6 +1197,51 @@ hipError_t launch_gather(const uint8_t* codes, const uint16_t* scale, const uint
   if (b == 4) { if (out_bf16) RKV_G(4, true); else RKV_G(4, false); }
   else { if (out_bf16) RKV_G(2, true); else RKV_G(2, false); }
 #undef RKV_G
+  return hipGetLastError();
+}
+
+RestoreWorkspace plan_restore(const Shape& sh, int64_t n_idx) {
+  RestoreWorkspace L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off += align256(bytes); return at; };
+  L.kr = sh.bf16 ? 2 * sh.d_c : sh.d_c;
+  L.wdp = take(size_t(sh.C) * L.kr * sh.esize);
+  L.zt = take(size_t(n_idx) * sh.d_c * 4);
+  L.total = off;
+  return L;
+}
+
+hipError_t launch_restore(const Shape& sh, int N, int D, const uint8_t* codes,
+                          const uint16_t* scale, const uint16_t* zmin, const int32_t* ref_idx,
+                          const void* kv, const void* wd, const int32_t* idx, int n_idx,
+                          float theta, void* out, bool out_bf16, char* ws,
+                          const RestoreWorkspace& L, hipStream_t st) {
+  if (n_idx == 0) return hipGetLastError();
+  // W_d [d_c][C] -> [C][K] rows (bf16: each value twice, matching the pairs)
+  PackJobs J{};
+  J.j[0] = {wd, ws + L.wdp, sh.d_c, sh.C, L.kr, 0, sh.bf16 ? 1 : 0, (sh.C + 63) / 64, 0};
+  const int tiles = (sh.d_c + 63) / 64 * J.j[0].tiles_c;
+  J.j[1].first = tiles;
+  J.j[2].first = tiles;
+  if (sh.bf16) k_pack_weights<uint16_t><<<tiles, 256, 0, st>>>(J);
+  else k_pack_weights<float><<<tiles, 256, 0, st>>>(J);
+  const int64_t total = int64_t(sh.B) * sh.T;
+  const int grid = grid_for(int64_t(n_idx) * (sh.d_c / 8), 256);
+  auto* zt = reinterpret_cast<uint32_t*>(ws + L.zt);
+#define RKV_RP(E, BITS)                                                                       \
+  k_restore_prep<E, BITS><<<grid, 256, 0, st>>>(codes, scale, zmin, idx, n_idx, total, sh.T,  \
+                                                sh.s, sh.d_c, sh.g, zt)
+  if (sh.bf16) { if (sh.b == 4) RKV_RP(uint16_t, 4); else RKV_RP(uint16_t, 2); }
+  else { if (sh.b == 4) RKV_RP(float, 4); else RKV_RP(float, 2); }
+#undef RKV_RP
+  const auto* kvp = static_cast<const char*>(kv);
+#define RKV_RS(E, KL)                                                                            \
+  k_restore<E, KL><<<cdiv(n_idx, RsCfg<E>::BM) * cdiv(sh.C, RsCfg<E>::BN), RsCfg<E>::kThreads, 0, \
+                     st>>>(ws + L.zt, ws + L.wdp, L.kr, idx, n_idx, total, sh.T, sh.s, sh.k,      \
+                           ref_idx, kvp, sh.C, N * D, D, theta, out, out_bf16 ? 1 : 0)
+  if (sh.bf16) { if (sh.kl == 4) RKV_RS(uint16_t, 4); else RKV_RS(uint16_t, 8); }
+  else { if (sh.kl == 4) RKV_RS(float, 4); else RKV_RS(float, 8); }
+#undef RKV_RS
   return hipGetLastError();
 }
 

@@ -139,3 +139,33 @@ def test_product_package_never_imports_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "rkv_oracle" not in text, f
+
+
+def _restore(p, n_idx=4, ws_bytes=1 << 40, theta=10000.0, out_dtype=R.RKV_F32, **ptrs):
+    args = dict(codes=FAKE, scale=FAKE, zmin=FAKE, ref_idx=FAKE, kv=FAKE, wd=FAKE, idx=FAKE,
+                out=FAKE, workspace=FAKE)
+    args.update(ptrs)
+    need = R.rkv_restore_workspace_bytes(p, max(n_idx, 0))
+    valid_ptrs = all(v is not None and v % 16 == 0 for v in args.values())
+    if need and n_idx > 0 and valid_ptrs and ws_bytes >= need and theta == theta \
+            and out_dtype in (R.RKV_F32, R.RKV_BF16):
+        pytest.fail("test would pass validation with fake pointers")
+    return R.rkv_restore(p, args["codes"], args["scale"], args["zmin"], args["ref_idx"], args["kv"],
+                         args["wd"], args["idx"], n_idx, theta, args["out"], out_dtype,
+                         args["workspace"], ws_bytes, None, check=False)
+
+
+def test_restore_validation():
+    p = _p(LLAMA32K)
+    assert R.rkv_restore_workspace_bytes(p, 9830) > R.rkv_restore_workspace_bytes(p, 10) > 0
+    assert R.rkv_restore_workspace_bytes(_p(LLAMA32K, D=96, N=8), 10) == 0   # D must divide 128
+    assert _restore(_p(LLAMA32K, D=96), codes=None) == R.RKV_ERR_UNSUPPORTED
+    assert _restore(p, n_idx=-1) == R.RKV_ERR_INVALID_ARG
+    assert _restore(p, out=None) == R.RKV_ERR_INVALID_ARG
+    assert _restore(p, wd=FAKE_MIS) == R.RKV_ERR_INVALID_ARG
+    assert _restore(p, ws_bytes=1024) == R.RKV_ERR_WORKSPACE
+    assert _restore(p, theta=float("nan")) == R.RKV_ERR_INVALID_ARG
+    assert _restore(p, out_dtype=5) == R.RKV_ERR_INVALID_ARG
+    # n_idx == 0 is a no-op and touches no pointer
+    assert R.rkv_restore(p, None, None, None, None, None, None, None, 0, 1.0, None, R.RKV_F32,
+                         None, 0, None, check=False) == R.RKV_OK
