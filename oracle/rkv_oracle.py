@@ -10,7 +10,8 @@ Source: the ResidualKV reading notes, "ResidualKVï¼šåŸºäºå‚è€ƒå‘é‡ä¸æ®‹å·®ç
 KV Cache å‹ç¼©" (notes on arXiv 2602.08005v2), cited below as [RKV] with the
 notes' own section numbers.  Every step follows the order of [RKV] Â§2.1-Â§2.4:
 
-  1. reference schedule: a reference every ``s`` tokens          ([RKV] Â§2.6)
+  1. reference schedule: sinks, then p_{m+1} = p_m + s0 +
+     floor(alpha (p_m - n_sink)); alpha = 0 is one every s0 tokens ([RKV] Â§2.6)
   2. candidate pool of token i: earlier references; k_i = min(k, |pool|)
                                                                  ([RKV] Â§2.1)
   3. the k_i references nearest in squared L2 over the joint vector
@@ -24,8 +25,10 @@ notes' own section numbers.  Every step follows the order of [RKV] Â§2.1-Â§2.4:
 
 Readings taken where the notes are silent (each is listed with its reason in
 the design notes of the repository):
-  * references sit at positions t with t % s == 0 of each sequence; the pool
-    of token t holds the references at positions j < t of the same sequence;
+  * the schedule starts at p_0 = n_sink after the n_sink sink tokens, which
+    are stored as references too; with the defaults (alpha = 0, no sinks)
+    references sit at t % s == 0; the pool of token t holds the references at
+    positions j < t of the same sequence;
   * distances are unweighted over all 2*d_k coordinates; ties in distance are
     broken by the smaller position;
   * Swish has beta = 1 (SiLU); f_c has no biases;
@@ -78,19 +81,39 @@ F32 = np.float32
 
 
 # ---------------------------------------------------------------- schedule
-def reference_positions(T: int, s: int) -> np.ndarray:
-    """Fixed-stride reference schedule, one reference every s tokens ([RKV] Â§2.6)."""
-    return np.arange(0, T, s, dtype=np.int64)
+def reference_schedule(T: int, s0: int, alpha: float = 0.0, n_sink: int = 0) -> np.ndarray:
+    """Reference positions of a sequence of T tokens ([RKV] Â§2.6).
+
+    The n_sink sink tokens (positions < n_sink) are stored as references;
+    then p_0 = n_sink and p_{m+1} = p_m + s0 + floor(alpha * (p_m - n_sink)),
+    the floor of the double-precision product.  alpha = 0 is the fixed
+    stride s0; with n_sink = 0 as well, the references are t % s0 == 0."""
+    pos = list(range(min(n_sink, T)))
+    p = n_sink
+    while p < T:
+        pos.append(p)
+        p = p + s0 + math.floor(alpha * (p - n_sink))
+    return np.asarray(pos, dtype=np.int64)
+
+
+def reference_positions(T: int, s: int, alpha: float = 0.0, n_sink: int = 0) -> np.ndarray:
+    """The schedule of [RKV] Â§2.6; fixed stride s by default."""
+    return reference_schedule(T, s, alpha, n_sink)
 
 
 def is_reference(t: int, s: int) -> bool:
+    """Fixed-stride schedule (alpha = 0, no sinks): t % s == 0."""
     return t % s == 0
 
 
-def candidate_pool(t: int, s: int) -> np.ndarray:
+def candidate_pool(t: int, s: int, refs: Optional[np.ndarray] = None) -> np.ndarray:
     """T_ref,t: the references already in the cache when token t is written
-    ([RKV] Â§2.1 symbol table; Â§2.2 'existing reference pool')."""
-    return np.arange(0, t, s, dtype=np.int64)
+    ([RKV] Â§2.1 symbol table; Â§2.2 'existing reference pool').  `refs` is the
+    sequence's schedule (fixed stride s when None)."""
+    if refs is None:
+        return np.arange(0, t, s, dtype=np.int64)
+    refs = np.asarray(refs, dtype=np.int64)
+    return refs[refs < t]
 
 
 def k_effective(k: int, pool_size: int) -> int:
@@ -105,13 +128,13 @@ def squared_l2(x: np.ndarray, Y: np.ndarray) -> np.ndarray:
     return np.einsum("jc,jc->j", diff, diff)
 
 
-def retrieve(kv_seq: np.ndarray, t: int, s: int, k: int):
+def retrieve(kv_seq: np.ndarray, t: int, s: int, k: int, refs: Optional[np.ndarray] = None):
     """Top-k_t nearest references of token t ([RKV] Â§2.2 retrieval equation).
 
     Returns (R, d_sorted): R are the chosen reference positions ordered by
     (distance, position); d_sorted are all pool distances in the same order.
     """
-    pool = candidate_pool(t, s)
+    pool = candidate_pool(t, s, refs)
     d = squared_l2(kv_seq[t], kv_seq[pool])
     order = np.lexsort((pool, d))            # primary key d, then position
     k_t = k_effective(k, len(pool))
@@ -242,7 +265,8 @@ def keep_ratio(beta: float, rho_ref: float, qb: float, dc_over_2dk: float,
 
 # ---------------------------------------------------------------- encode
 def encode_tokens(kv_seq: np.ndarray, W1, W2, W3, positions: Iterable[int], *,
-                  k: int, g: int, b: int, s: int, n_diag: Optional[int] = None) -> Dict:
+                  k: int, g: int, b: int, s: int, n_diag: Optional[int] = None,
+                  alpha: float = 0.0, n_sink: int = 0) -> Dict:
     """Encode the given positions of one sequence, each on its own.
 
     kv_seq: [T, C] joint vectors [K heads | V heads], pre-RoPE ([RKV] Â§2.1).
@@ -260,11 +284,14 @@ def encode_tokens(kv_seq: np.ndarray, W1, W2, W3, positions: Iterable[int], *,
     ref_idx = np.full((n, k), -1, dtype=np.int32)
     d_diag = np.full((n, n_diag), np.inf)
     z = np.zeros((n, d_c), dtype=F64)
+    refs = reference_schedule(len(kv_seq), s, alpha, n_sink)
+    ref_mask = np.zeros(len(kv_seq), dtype=bool)
+    ref_mask[refs] = True
     enc_rows, enc_kv, enc_mean = [], [], []
     for i, t in enumerate(positions):
-        if is_reference(int(t), s):
+        if ref_mask[int(t)]:
             continue                       # references are stored as they are
-        R, d_sorted = retrieve(kv_seq, int(t), s, k)
+        R, d_sorted = retrieve(kv_seq, int(t), s, k, refs)
         ref_idx[i, :len(R)] = np.sort(R)
         m = min(n_diag, len(d_sorted))
         d_diag[i, :m] = d_sorted[:m]
@@ -275,7 +302,7 @@ def encode_tokens(kv_seq: np.ndarray, W1, W2, W3, positions: Iterable[int], *,
         rows = np.asarray(enc_rows)
         z[rows] = residual_latent(np.stack(enc_kv), np.stack(enc_mean), W1, W2, W3)
     q, dh, mh = quantize(z, g, b)
-    ref_rows = np.array([is_reference(int(t), s) for t in positions], dtype=bool)
+    ref_rows = ref_mask[positions]
     q[ref_rows] = 0                        # stored directly: all-zero record
     dh[ref_rows] = 0
     mh[ref_rows] = 0
@@ -283,10 +310,12 @@ def encode_tokens(kv_seq: np.ndarray, W1, W2, W3, positions: Iterable[int], *,
                 codes=pack_codes(q, b), d_diag=d_diag, is_ref=ref_rows)
 
 
-def encode(kv: np.ndarray, W1, W2, W3, *, k: int, g: int, b: int, s: int) -> Dict:
+def encode(kv: np.ndarray, W1, W2, W3, *, k: int, g: int, b: int, s: int,
+           alpha: float = 0.0, n_sink: int = 0) -> Dict:
     """Encode every position of every sequence; kv is [B, T, C]."""
     B, T, _ = kv.shape
-    parts = [encode_tokens(kv[bi], W1, W2, W3, range(T), k=k, g=g, b=b, s=s)
+    parts = [encode_tokens(kv[bi], W1, W2, W3, range(T), k=k, g=g, b=b, s=s, alpha=alpha,
+                           n_sink=n_sink)
              for bi in range(B)]
     out = {}
     for key in ("ref_idx", "z", "q", "scale", "zmin", "codes", "d_diag", "is_ref"):
@@ -335,7 +364,8 @@ def apply_rope(k_flat: np.ndarray, pos: int, N: int, D: int, theta: float) -> np
 
 def restore(codes: np.ndarray, scale: np.ndarray, zmin: np.ndarray, ref_idx: np.ndarray,
             kv: np.ndarray, Wd: np.ndarray, idx: np.ndarray, *, s: int, N: int, D: int,
-            g: int, b: int, d_c: int, rope_theta: float) -> np.ndarray:
+            g: int, b: int, d_c: int, rope_theta: float, alpha: float = 0.0,
+            n_sink: int = 0) -> np.ndarray:
     """Restore the selected tokens' K|V rows ([RKV] Â§2.5): z~ W_d plus the mean
     of the token's stored references, reference tokens as stored; then K is
     rotated at the token's position.
@@ -345,6 +375,8 @@ def restore(codes: np.ndarray, scale: np.ndarray, zmin: np.ndarray, ref_idx: np.
     read); idx are flat b*T + t.  Returns fp64 [len(idx)][C]; NaN rows for
     indices outside [0, B*T)."""
     Bn, T, C = kv.shape
+    ref_mask = np.zeros(T, dtype=bool)
+    ref_mask[reference_schedule(T, s, alpha, n_sink)] = True
     idx = np.asarray(idx, dtype=np.int64)
     out = np.full((len(idx), C), np.nan, dtype=F64)
     Wd = np.asarray(Wd, F64)
@@ -352,7 +384,7 @@ def restore(codes: np.ndarray, scale: np.ndarray, zmin: np.ndarray, ref_idx: np.
         if fl < 0 or fl >= Bn * T:
             continue
         bq, t = divmod(int(fl), T)
-        if t % s == 0:
+        if ref_mask[t]:
             row = np.asarray(kv[bq, t], F64)
         else:
             q = unpack_codes(codes[fl:fl + 1], b, d_c)

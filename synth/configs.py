@@ -35,6 +35,8 @@ class RkvConfig:
     gather_frac: Optional[float] = None  # None: gather every position
     seed: int = 0
     rope_theta: float = 10000.0  # RoPE base of the model whose keys are restored
+    alpha: float = 0.0         # reference schedule growth ([RKV] §2.6); 0 = fixed stride
+    n_sink: int = 0            # sink tokens, stored as references before the schedule starts
     # multimodal recipe only
     mm_blocks: int = 0
     mm_block_len: int = 0
@@ -80,8 +82,19 @@ MM_INT2 = RkvConfig(
 CONFIGS = [TINY, LLAMA8K, LLAMA32K, QWEN_LIKE, MM_INT2]
 
 
+
+
+# Dynamic reference schedules ([RKV] §2.6, the notes' LongBench setting
+# alpha = 0.001 with the default initial stride 10): parity and measurement
+# cases beside the five fixed-stride workloads above.
+TINY_DYN = TINY.with_(name="tiny_f32_dynamic", alpha=0.02, n_sink=2)
+LLAMA8K_DYN = LLAMA8K.with_(name="llama8b_T8k_dynamic", stride=10, alpha=0.001, n_sink=4)
+LLAMA32K_DYN = LLAMA32K.with_(name="llama8b_T32k_dynamic", stride=10, alpha=0.001, n_sink=4)
+DYNAMIC = (TINY_DYN, LLAMA8K_DYN, LLAMA32K_DYN)
+
+
 def config_by_name(name: str) -> RkvConfig:
-    for c in CONFIGS:
+    for c in CONFIGS + DYNAMIC:
         if c.name == name:
             return c
     raise KeyError(name)

@@ -481,3 +481,52 @@ def test_restore_out_of_range_rows_are_nan(tiny, tiny_encoded):
     Wd = np.zeros((TINY.d_c, TINY.C))
     out = _restore(tiny_encoded, kv, Wd, [-1, TINY.T, 5], 0.0)
     assert np.isnan(out[0]).all() and np.isnan(out[1]).all() and not np.isnan(out[2]).any()
+
+
+# ------------------------------------------------------------------ schedule
+def test_reference_schedule_reproduces_table_vi_counts():
+    """[RKV] §4.6 Table VI, numbers printed by the notes (reading of T in the file)."""
+    with open(os.path.join(GOLD, "reference_counts.json")) as f:
+        g = json.load(f)
+    got = [len(O.reference_schedule(g["T"], g["s0"], a, g["n_sink"])) for a in g["alpha"]]
+    assert got == g["count"]
+
+
+@pytest.mark.parametrize("alpha", [0.001, 0.02, 0.05, 0.1])
+def test_reference_count_follows_the_logarithmic_approximation(alpha):
+    """[RKV] §2.6: ignoring the floor, N_ref(T) ~ log_{1+a}(1 + a (T - n_sink) / s0).
+    The floor only shortens gaps, so the exact count is at least the
+    approximation, and close to it."""
+    T, s0, ns = 262144, 10, 4
+    n = len(O.reference_schedule(T, s0, alpha, ns)) - ns
+    approx = math.log1p(alpha * (T - ns) / s0) / math.log1p(alpha)
+    assert approx <= n <= 1.02 * approx + 2
+
+
+def test_reference_schedule_special_cases():
+    """alpha = 0 without sinks is the fixed stride; sinks come first and the
+    recurrence starts right after them; gaps never shrink."""
+    np.testing.assert_array_equal(O.reference_schedule(1000, 16), np.arange(0, 1000, 16))
+    r = O.reference_schedule(5000, 10, 0.01, 4)
+    assert list(r[:5]) == [0, 1, 2, 3, 4] and r[5] == 4 + 10
+    gaps = np.diff(r[4:])
+    assert np.all(np.diff(gaps) >= 0) and gaps[0] == 10
+
+
+def test_dynamic_schedule_pool_and_selection_follow_the_schedule():
+    """Under a dynamic schedule the pool of t is the scheduled references
+    before t, and the encode's selections match brute force over that pool."""
+    rng = np.random.default_rng(21)
+    T, C = 160, 16
+    kv = rng.standard_normal((T, C))
+    refs = O.reference_schedule(T, 6, 0.05, 3)
+    W1, W2 = rng.standard_normal((C, 8)), rng.standard_normal((C, 8))
+    W3 = rng.standard_normal((8, 8))
+    pos = [t for t in range(T) if t not in set(refs.tolist())]
+    enc = O.encode_tokens(kv, W1, W2, W3, pos, k=3, g=8, b=4, s=6, alpha=0.05, n_sink=3)
+    for i, t in enumerate(pos):
+        pool = [int(p) for p in refs if p < t]
+        d = [(float(((kv[t] - kv[p]) ** 2).sum()), p) for p in pool]
+        want = sorted(p for _, p in sorted(d)[:min(3, len(pool))])
+        got = [int(p) for p in enc["ref_idx"][i] if p >= 0]
+        assert got == want, t
