@@ -94,7 +94,7 @@ DYNAMIC = (TINY_DYN, LLAMA8K_DYN, LLAMA32K_DYN)
 
 
 def config_by_name(name: str) -> RkvConfig:
-    for c in CONFIGS + DYNAMIC:
+    for c in list(CONFIGS) + list(DYNAMIC):
         if c.name == name:
             return c
     raise KeyError(name)
