@@ -198,7 +198,8 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
 
     p = R.params(B=cfg.B, T=cfg.T, N=cfg.N, D=cfg.D, d_ff=cfg.d_ff, d_c=cfg.d_c, k=cfg.k,
-                 g=cfg.g, b=cfg.b, ref_stride=cfg.stride, dtype=cfg.dtype)
+                 g=cfg.g, b=cfg.b, ref_stride=cfg.stride, dtype=cfg.dtype, n_sink=cfg.n_sink,
+                 ref_alpha=cfg.alpha)
     kv, w1, w2, w3 = (to_dev(x) for x in (w.kv, w.w1, w.w2, w.w3))
     out = RB.alloc_encode(p, dev, with_z=False)
     idx = torch.from_numpy(w.gather_idx.astype(np.int32)).to(dev)
@@ -283,7 +284,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "N": cfg.N, "D": cfg.D,
                    "C": cfg.C, "d_ff": cfg.d_ff, "d_c": cfg.d_c, "k": cfg.k, "g": cfg.g,
-                   "b": cfg.b, "ref_stride": cfg.stride, "gather_rows": int(idx.numel())},
+                   "b": cfg.b, "ref_stride": cfg.stride, "ref_alpha": cfg.alpha, "n_sink": cfg.n_sink,
+                   "gather_rows": int(idx.numel())},
         "pct_bf16_mfma_peak": round(100.0 * mfma_flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "encode_mfma_tflops_algorithmic": round(mfma_flops / 1e12, 4),
         "stages_ms": {k: round(v, 4) for k, v in stages_ms.items()},

@@ -27,10 +27,13 @@
  *  - Token layout: kv[b][t][c] with c in [0, C): the N key heads (pre-RoPE)
  *    then the N value heads, D coordinates each ([RKV] §2.1: K and V of all
  *    heads flattened into one joint vector).
- *  - Reference schedule: position t of a sequence is a reference iff
- *    t % s == 0 ([RKV] §2.6, fixed stride).  The candidate pool of a
- *    non-reference token t holds the references at positions j < t of the
- *    same sequence; k_t = min(k, ceil(t / s)) ([RKV] §2.1).
+ *  - Reference schedule ([RKV] §2.6): positions t < n_sink (sink tokens)
+ *    are references; then p_0 = n_sink and p_{m+1} = p_m + s +
+ *    floor(ref_alpha * (p_m - n_sink)) (the floor of the double product).
+ *    With ref_alpha = 0 and n_sink = 0 the references are t % s == 0 (fixed
+ *    stride).  The candidate pool of a non-reference token t holds the
+ *    references at positions j < t of the same sequence; k_t = min(k, pool
+ *    size) ([RKV] §2.1).  Position 0 is always a reference.
  */
 #ifndef RKV_H
 #define RKV_H
@@ -61,8 +64,10 @@ typedef struct {
   int32_t d_ff, d_c;  /* compressor width; latent width                        */
   int32_t k;          /* neighbours per token, 1..8 ([RKV] §2.2 uses 4)        */
   int32_t g, b;       /* quantiser group size (8,16,32,64); bits (2 or 4)      */
-  int32_t ref_stride; /* s >= 1                                                */
+  int32_t ref_stride; /* s >= 1 (s0, the initial stride, of the schedule)      */
   rkv_dtype dtype;    /* element type of kv, w1, w2, w3                        */
+  int32_t n_sink;     /* sink tokens (positions < n_sink), stored as references */
+  double ref_alpha;   /* schedule growth alpha >= 0 ([RKV] §2.6); 0: fixed     */
 } rkv_params;
 
 /* GPU-path limits (RKV_ERR_UNSUPPORTED otherwise): C % 64 == 0,

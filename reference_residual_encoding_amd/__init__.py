@@ -50,7 +50,7 @@ RKV_ABI_VERSION = 2
 class rkv_params(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("B", "T", "N", "D", "d_ff", "d_c", "k", "g", "b", "ref_stride")] + \
-               [("dtype", ctypes.c_int32)]
+               [("dtype", ctypes.c_int32), ("n_sink", ctypes.c_int32), ("ref_alpha", ctypes.c_double)]
 
 
 class RkvError(RuntimeError):
@@ -112,11 +112,12 @@ def _check(fn: str, status: int) -> int:
     return status
 
 
-def params(*, B, T, N, D, d_ff, d_c, k, g, b, ref_stride, dtype) -> rkv_params:
+def params(*, B, T, N, D, d_ff, d_c, k, g, b, ref_stride, dtype, n_sink=0,
+           ref_alpha=0.0) -> rkv_params:
     """Build an rkv_params; dtype is RKV_F32/RKV_BF16 or "f32"/"bf16"."""
     if isinstance(dtype, str):
         dtype = {"f32": RKV_F32, "bf16": RKV_BF16}[dtype]
-    return rkv_params(B, T, N, D, d_ff, d_c, k, g, b, ref_stride, dtype)
+    return rkv_params(B, T, N, D, d_ff, d_c, k, g, b, ref_stride, dtype, n_sink, ref_alpha)
 
 
 def _p(x) -> Optional[int]:

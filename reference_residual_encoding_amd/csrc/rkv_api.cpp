@@ -69,7 +69,11 @@ rkv_status check_params(const rkv_params* p) {
   if (p->d_ff > 65536) return fail(RKV_ERR_UNSUPPORTED, "d_ff must be at most 65536 (got %d)", p->d_ff);
   if ((long long)p->B * p->T >= (1LL << 31)) return fail(RKV_ERR_UNSUPPORTED, "B*T must be below 2^31");
   if ((long long)p->B * p->T * C >= (1LL << 40)) return fail(RKV_ERR_UNSUPPORTED, "B*T*C too large");
-  const long long nref = (p->T + p->ref_stride - 1) / p->ref_stride;
+  if (!(p->ref_alpha >= 0.0 && p->ref_alpha <= 1.0e6))
+    return fail(RKV_ERR_INVALID_ARG, "ref_alpha must be in [0, 1e6] (got %g)", p->ref_alpha);
+  if (p->n_sink < 0) return fail(RKV_ERR_INVALID_ARG, "n_sink must be non-negative (got %d)", p->n_sink);
+  const long long nref =
+      (long long)rkv::schedule_for(p->T, p->ref_stride, p->ref_alpha, p->n_sink).rpos.size();
   if ((long long)p->B * nref * 2 * p->d_ff * 4 >= (1LL << 31))
     return fail(RKV_ERR_UNSUPPORTED, "B*ceil(T/s)*2*d_ff*4 (reference projections) must be below 2^31 bytes");
   return RKV_OK;
@@ -77,7 +81,7 @@ rkv_status check_params(const rkv_params* p) {
 
 rkv::Shape shape_of(const rkv_params* p) {
   return rkv::make_shape(p->B, p->T, p->N, p->D, p->d_ff, p->d_c, p->k, p->g, p->b, p->ref_stride,
-                         p->dtype == RKV_BF16);
+                         p->dtype == RKV_BF16, p->ref_alpha, p->n_sink);
 }
 
 rkv_status device_status(hipError_t e, const char* where) {
@@ -195,6 +199,7 @@ rkv_status rkv_encode(const rkv_params* p, const void* kv, const void* w1, const
     if ((e = (call)) != hipSuccess) return device_status(e, name); \
   } while (0)
   RKV_STAGE(RKV_STAGE_PACK, rkv::launch_pack_weights(sh, w1, w2, w3, ws, L, stream), "pack");
+  RKV_STAGE(RKV_STAGE_NORMS, rkv::launch_schedule(sh, ws, L, stream), "schedule");
   RKV_STAGE(RKV_STAGE_NORMS,
             rkv::launch_ref_norms(sh, kv, ws, L, ref_idx, codes, scale, zmin, z, stream), "norms");
   RKV_STAGE(RKV_STAGE_DIST, rkv::launch_dist(sh, kv, ws, L, stream), "dist");
@@ -220,6 +225,7 @@ rkv_status rkv_select(const rkv_params* p, const void* kv, int32_t* ref_idx, voi
     return fail(RKV_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
   char* ws = static_cast<char*>(workspace);
   hipError_t e;
+  RKV_STAGE(RKV_STAGE_NORMS, rkv::launch_schedule(sh, ws, L, stream), "schedule");
   RKV_STAGE(RKV_STAGE_NORMS,
             rkv::launch_ref_norms(sh, kv, ws, L, ref_idx, nullptr, nullptr, nullptr, nullptr,
                                   stream),

@@ -32,13 +32,6 @@ __device__ __forceinline__ int mfma32_row(int r, int lane) {
   return (r & 3) + 8 * (r >> 2) + 4 * (lane >> 5);
 }
 
-// Position of the q-th non-reference token of a sequence whose references
-// sit at multiples of s (s >= 2): s-1 non-references follow each reference.
-__device__ __forceinline__ int nonref_pos(int q, int s) {
-  const int sm1 = s - 1;
-  return (q / sm1) * s + (q % sm1) + 1;
-}
-
 // x as a (hi, lo) bf16 pair, hi = bf16(x) and lo = bf16(x - hi), both
 // rounded to nearest even (gfx950 converts in hardware: v_cvt_pk_bf16_f32);
 // hi in the low 16 bits.  hi + lo carries about 16 significant bits of x.

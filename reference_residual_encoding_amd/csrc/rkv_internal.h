@@ -5,7 +5,19 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <vector>
+
 namespace rkv {
+
+// Reference schedule of one sequence ([RKV] §2.6), computed on the host.
+struct Schedule {
+  int T = -1, s0 = 0, n_sink = 0;
+  double alpha = 0.0;
+  std::vector<int> rpos;   // reference positions, ascending
+  std::vector<int> nrp;    // position of the q-th non-reference token
+};
+// The schedule for these parameters (cached per thread).
+const Schedule& schedule_for(int T, int s0, double alpha, int n_sink);
 
 // Derived sizes of one encode problem.
 struct Shape {
@@ -17,15 +29,22 @@ struct Shape {
   int kl;        // neighbour-list length kept per chunk (4 or 8, >= k)
   int n_chunks;  // reference chunks (one partial top-k list each) per sequence
   int k3;        // contraction length of the W3 product (2*d_ff bf16 hi/lo, d_ff fp32)
+  int n_sink;
+  double alpha;
+  const Schedule* sched;  // host copy of the schedule (planning the distance items)
 };
 
 // Byte offsets of the workspace regions (each 256-byte aligned).
 struct Workspace {
-  size_t wp, w3p, ysq, refs, proj, part, dh, total;
+  size_t wp, w3p, ysq, refs, proj, part, dh, rpos, nrp, tab, total;
 };
 
 Shape make_shape(int B, int T, int N, int D, int d_ff, int d_c, int k, int g, int b, int s,
-                 bool bf16);
+                 bool bf16, double alpha, int n_sink);
+// Device schedule tables in the workspace: reference positions, non-reference
+// positions, and per position t: ~j for the j-th reference, else the
+// non-reference index q.
+hipError_t launch_schedule(const Shape& sh, char* ws, const Workspace& L, hipStream_t st);
 Workspace plan_workspace(const Shape& sh);
 
 // Each launcher enqueues on `st` and returns hipGetLastError().

@@ -35,6 +35,7 @@
 #include "rkv_internal.h"
 
 #include <algorithm>
+#include <cmath>
 
 namespace rkv {
 
@@ -131,6 +132,52 @@ __global__ __launch_bounds__(256) void k_pack_weights(PackJobs jobs) {
   }
 }
 
+// ------------------------------------------------------------------ schedule
+// Device copies of the reference schedule ([RKV] §2.6), one per call (every
+// sequence shares it): rpos[j] = position of the j-th reference, nrp[q] =
+// position of the q-th non-reference token, tab[t] = ~j for the j-th
+// reference, else q.  The host computes the schedule exactly; the device
+// copy comes from the closed form (fixed stride) or from the host's
+// positions carried in kernel arguments, so no host buffer is involved.
+__global__ __launch_bounds__(256) void k_sched_fixed(int* __restrict__ rpos, int nref, int T,
+                                                     int s0, int n_sink, int* __restrict__ tab,
+                                                     int* __restrict__ nrp) {
+  // Fixed stride after the sinks: every table has a closed form.
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= T) return;
+  if (t < nref) rpos[t] = t < n_sink ? t : n_sink + (t - n_sink) * s0;
+  const int u = t - n_sink;
+  const bool ref = u < 0 || u % s0 == 0;
+  const int before = u < 0 ? t : n_sink + (u + s0 - 1) / s0;   // references before t
+  tab[t] = ref ? ~before : t - before;
+  if (!ref) nrp[t - before] = t;
+}
+
+constexpr int kPosChunk = 960;
+struct PosChunk {
+  int first, count;
+  int pos[kPosChunk];
+};
+
+__global__ __launch_bounds__(256) void k_sched_chunk(int* __restrict__ rpos, PosChunk c) {
+  for (int i = threadIdx.x; i < c.count; i += 256) rpos[c.first + i] = c.pos[i];
+}
+
+__global__ __launch_bounds__(256) void k_sched_tables(const int* __restrict__ rpos, int nref,
+                                                      int T, int* __restrict__ tab,
+                                                      int* __restrict__ nrp) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= T) return;
+  int lo = 0, hi = nref;                                 // references before t
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (rpos[mid] < t) lo = mid + 1; else hi = mid;
+  }
+  const bool ref = lo < nref && rpos[lo] == t;
+  tab[t] = ref ? ~lo : t - lo;
+  if (!ref) nrp[t - lo] = t;
+}
+
 // ------------------------------------------------------------------ references
 // Copy the reference rows (positions j*s of each sequence) into a compact
 // [B*nref][C] block, which the distance and projection contractions stream
@@ -140,7 +187,7 @@ __global__ __launch_bounds__(256) void k_pack_weights(PackJobs jobs) {
 // zero; one wave writes each with coalesced stores.
 template <typename E>
 __global__ __launch_bounds__(256) void k_ref_gather(const char* __restrict__ kv, int B, int T,
-                                                    int C, int s, int nref,
+                                                    int C, const int* __restrict__ rpos, int nref,
                                                     char* __restrict__ refs,
                                                     float* __restrict__ ysq,
                                                     int32_t* __restrict__ ref_idx, int k,
@@ -152,7 +199,7 @@ __global__ __launch_bounds__(256) void k_ref_gather(const char* __restrict__ kv,
   const int lane = threadIdx.x & 63;
   if (wid >= B * nref) return;
   const int b = wid / nref, j = wid % nref;
-  const size_t rec = size_t(b) * T + size_t(j) * s;     // the reference token's flat row
+  const size_t rec = size_t(b) * T + size_t(rpos[j]);   // the reference token's flat row
   for (int i = lane; i < k; i += 64) ref_idx[rec * k + i] = -1;
   if (codes) {
     for (int o = lane * 4; o < cb; o += 256) *reinterpret_cast<uint32_t*>(codes + rec * cb + o) = 0u;
@@ -162,7 +209,7 @@ __global__ __launch_bounds__(256) void k_ref_gather(const char* __restrict__ kv,
         *reinterpret_cast<float4*>(z + rec * d_c + i) = make_float4(0.f, 0.f, 0.f, 0.f);
   }
   const size_t rowb = size_t(C) * sizeof(E);
-  const char* src = kv + (size_t(b) * T + size_t(j) * s) * rowb;
+  const char* src = kv + rec * rowb;
   char* dst = refs + size_t(wid) * rowb;
   float acc = 0.0f;
   for (size_t o = size_t(lane) * 16; o < rowb; o += 64 * 16) {
@@ -268,7 +315,8 @@ __device__ __forceinline__ void store_codes(uint8_t* codes, int64_t unit, uint32
 template <typename E, int KL>
 __global__ __launch_bounds__(DistCfg<E>::kThreads) void k_dist_topk(
     const char* __restrict__ kv, const char* __restrict__ refs, const float* __restrict__ ysq,
-    float2* __restrict__ part, int B, int T, int C, int s, int nref, int nr, int n_lists,
+    float2* __restrict__ part, int B, int T, int C, const int* __restrict__ nrp, int nref,
+    int nr, int n_lists,
     int n_tt) {
   using CF = DistCfg<E>;
   constexpr int BM = CF::BM, BN = CF::BN, WGM = CF::WGM, WGN = CF::WGN, SUBS = CF::SUBS;
@@ -289,8 +337,8 @@ __global__ __launch_bounds__(DistCfg<E>::kThreads) void k_dist_topk(
   int g = x, c = -1, npool_max = 0;
   for (; g < B * n_tt; g += 8) {
     const int tt_ = g % n_tt;
-    const int pl = nonref_pos(min(tt_ * BN + BN, nr) - 1, s);
-    const int np = (pl + s - 1) / s;
+    const int ql = min(tt_ * BN + BN, nr) - 1;          // last token of the tile
+    const int np = nrp[ql] - ql;                         // its pool: references before it
     const int nch = (np + BM - 1) / BM;
     if (l < nch) { c = l; npool_max = np; break; }
     l -= nch;
@@ -306,7 +354,7 @@ __global__ __launch_bounds__(DistCfg<E>::kThreads) void k_dist_topk(
   for (int r = tid; r < BM; r += CF::kThreads) ysq_l[r] = ysq[size_t(b) * nref + min(m0 + r, nref - 1)];
   const char* rbase = refs + size_t(b) * nref * rowb;
   auto rowA = [&](int r) { return rbase + size_t(min(m0 + r, nref - 1)) * rowb; };
-  auto rowB = [&](int r) { return base + size_t(nonref_pos(min(n0 + r, nr - 1), s)) * rowb; };
+  auto rowB = [&](int r) { return base + size_t(nrp[min(n0 + r, nr - 1)]) * rowb; };
   f32x16 acc[BM / WGM / 32][BN / WGN / 32];
   tile_product<E, BM, BN, CF::SB, CF::NS, WGM, WGN>(rowA, rowB, int(rowb), lds, acc);
 
@@ -315,9 +363,9 @@ __global__ __launch_bounds__(DistCfg<E>::kThreads) void k_dist_topk(
   // half for token t in increasing order, keeping the KL best (d', j).
   float* dot = reinterpret_cast<float*>(lds);
   const int t = tid % BN, sb = tid / BN, q = n0 + t;     // sb is uniform per wave
-  // references j < ceil(position / s) are in the pool of the token at q;
-  // the scan runs to the tile's largest pool (uniform) and masks the rest
-  const int lim = q < nr ? (nonref_pos(q, s) + s - 1) / s - m0 : 0;
+  // the pool of the token at q is the t - q references before its position
+  // t; the scan runs to the tile's largest pool (uniform) and masks the rest
+  const int lim = q < nr ? nrp[q] - q - m0 : 0;
   const int lim_all = min(npool_max - m0, BM);
   float bd[KL];
   int bi[KL];
@@ -392,15 +440,16 @@ __global__ __launch_bounds__(DistCfg<E>::kThreads) void k_dist_topk(
 template <int KL>
 __global__ __launch_bounds__(64) void k_topk_merge(const float2* __restrict__ part,
                                                     int32_t* __restrict__ ref_idx, int B, int T,
-                                                    int s, int k, int nr, int n_lists,
-                                                    int chunk) {
+                                                    const int* __restrict__ tab,
+                                                    const int* __restrict__ rpos, int k, int nr,
+                                                    int n_lists, int chunk) {
   const long gid = long(blockIdx.x) * 64 + threadIdx.x;
   if (gid >= long(B) * T) return;
   const int b = int(gid / T), t = int(gid % T);
   int32_t* out = ref_idx + gid * k;
-  if (t % s == 0) return;
-  const int q = t - t / s - 1;
-  const int npool = (t + s - 1) / s;
+  const int q = tab[t];
+  if (q < 0) return;                                    // a reference
+  const int npool = t - q;
   const int kt = min(k, npool);
   const int nch = (npool + chunk - 1) / chunk;          // lists that cover the pool
   float bd[KL];
@@ -446,7 +495,7 @@ __global__ __launch_bounds__(64) void k_topk_merge(const float2* __restrict__ pa
     }
 #pragma unroll
   for (int i = 0; i < KL; ++i)
-    if (i < k) out[i] = i < kt ? sel[i] * s : -1;
+    if (i < k) out[i] = i < kt ? rpos[sel[i]] : -1;
 }
 
 // ------------------------------------------------------------------ reference projection
@@ -502,8 +551,10 @@ __global__ __launch_bounds__(SwCfg<E>::kThreads) void k_swiglu(const char* __res
                                                 const float* __restrict__ proj,
                                                 uint32_t proj_bytes,
                                                 const int32_t* __restrict__ ref_idx,
-                                                char* __restrict__ dh, int T, int C, int s,
-                                                int nref, int nr, int k, int d_ff, int M) {
+                                                char* __restrict__ dh, int T, int C,
+                                                const int* __restrict__ nrp,
+                                                const int* __restrict__ tab, int nref, int nr,
+                                                int k, int d_ff, int M) {
   using CF = SwCfg<E>;
   constexpr int BM = CF::BM, BN = CF::BN, WGM = CF::WGM, WGN = CF::WGN, NT = CF::kThreads;
   constexpr int kMain = mainloop_lds<E, BM, BN, CF::SB, CF::NS, WGM, WGN>();
@@ -535,12 +586,12 @@ __global__ __launch_bounds__(SwCfg<E>::kThreads) void k_swiglu(const char* __res
     for (int i = 0; i < KL; ++i) off[i] = kNone;
     if (Q < M) {
       const int b = Q / nr, q = Q % nr;
-      const int32_t* ri = ref_idx + (size_t(b) * T + nonref_pos(q, s)) * k;
+      const int32_t* ri = ref_idx + (size_t(b) * T + nrp[q]) * k;
 #pragma unroll
       for (int i = 0; i < KL; ++i) {
         const int pos = i < k ? ri[i] : -1;
         if (pos >= 0) {
-          off[i] = uint32_t(b * nref + pos / s) * uint32_t(N) * 4u;
+          off[i] = uint32_t(b * nref + ~tab[pos]) * uint32_t(N) * 4u;   // P row of reference ~tab
           ++kt;
         }
       }
@@ -551,7 +602,7 @@ __global__ __launch_bounds__(SwCfg<E>::kThreads) void k_swiglu(const char* __res
   }
   auto rowA = [&](int r) {
     const int Q = min(m0 + r, M - 1);
-    return kv + (size_t(Q / nr) * T + nonref_pos(Q % nr, s)) * rowb;
+    return kv + (size_t(Q / nr) * T + nrp[Q % nr]) * rowb;
   };
   auto rowB = [&](int r) { return wp + size_t(min(n0 + r, N - 1)) * rowb; };
   constexpr int kTM = BM / WGM / 32, kTN = BN / WGN / 32;
@@ -641,7 +692,8 @@ __global__ __launch_bounds__(SwCfg<E>::kThreads) void k_swiglu(const char* __res
 template <typename E, int BITS, int G8>
 __global__ __launch_bounds__(W3Cfg<E>::kThreads) void k_w3_quant(const char* __restrict__ dh,
                                                   const char* __restrict__ w3p, int K, int M,
-                                                  int N, int tiles_m, int T, int s, int nr,
+                                                  int N, int tiles_m, int T,
+                                                  const int* __restrict__ nrp, int nr,
                                                   uint8_t* __restrict__ codes,
                                                   uint16_t* __restrict__ scale,
                                                   uint16_t* __restrict__ zmin,
@@ -663,7 +715,7 @@ __global__ __launch_bounds__(W3Cfg<E>::kThreads) void k_w3_quant(const char* __r
   // barriers publish it)
   for (int r = tid; r < BM; r += NT) {
     const int Q = m0 + r;
-    rec_lds[r] = Q < M ? (Q / nr) * T + nonref_pos(Q % nr, s) : -1;
+    rec_lds[r] = Q < M ? (Q / nr) * T + nrp[Q % nr] : -1;
   }
   auto rowA = [&](int r) { return dh + size_t(min(m0 + r, M - 1)) * rowb; };
   auto rowB = [&](int r) { return w3p + size_t(min(n0 + r, N - 1)) * rowb; };
@@ -763,15 +815,17 @@ template <> struct RsCfg<float> {
 
 // z~ of each selected token as the decoder product's A row: bf16 runs store
 // a (hi, lo) bf16 pair per latent (K positions 2c, 2c + 1), fp32 runs the
-// float; zeros for reference tokens and indices outside [0, B*T).  z~ is
+// float; zeros for reference tokens (all -1 ref_idx rows) and indices
+// outside [0, B*T).  z~ is
 // fmaf(q, Delta_h, m_h), as rkv_dequant_gather gives it.
 template <typename E, int BITS>
 __global__ __launch_bounds__(256) void k_restore_prep(const uint8_t* __restrict__ codes,
                                                       const uint16_t* __restrict__ scale,
                                                       const uint16_t* __restrict__ zmin,
                                                       const int32_t* __restrict__ idx,
-                                                      int64_t n_idx, int64_t total_rows, int T,
-                                                      int s, int d_c, int g,
+                                                      int64_t n_idx, int64_t total_rows,
+                                                      const int32_t* __restrict__ ref_idx, int k,
+                                                      int d_c, int g,
                                                       uint32_t* __restrict__ zt) {
   constexpr uint32_t kMask = (1u << BITS) - 1;
   const int64_t units = n_idx * (d_c / 8);
@@ -780,7 +834,9 @@ __global__ __launch_bounds__(256) void k_restore_prep(const uint8_t* __restrict_
     const int64_t i = u / (d_c / 8);
     const int o = int(u - i * (d_c / 8)) * 8;
     const int64_t src = idx[i];
-    const bool live = src >= 0 && src < total_rows && (src % T) % s != 0;
+    // a reference token's ref_idx row is all -1 (every other token has at
+    // least one reference: position 0 always is one)
+    const bool live = src >= 0 && src < total_rows && ref_idx[src * k] >= 0;
     const int64_t sr = live ? src : 0;
     uint32_t word;
     if constexpr (BITS == 4)
@@ -806,7 +862,7 @@ __global__ __launch_bounds__(256) void k_restore_prep(const uint8_t* __restrict_
 template <typename E, int KL>
 __global__ __launch_bounds__(RsCfg<E>::kThreads) void k_restore(
     const char* __restrict__ zt, const char* __restrict__ wdp, int K, const int32_t* __restrict__ idx,
-    int n_idx, int64_t total_rows, int T, int s, int k, const int32_t* __restrict__ ref_idx,
+    int n_idx, int64_t total_rows, int T, int k, const int32_t* __restrict__ ref_idx,
     const char* __restrict__ kv, int C, int ND, int D, float theta, void* __restrict__ out,
     int out_bf16) {
   using CF = RsCfg<E>;
@@ -836,7 +892,7 @@ __global__ __launch_bounds__(RsCfg<E>::kThreads) void k_restore(
       if (fl >= 0 && fl < total_rows) {
         const int b = int(fl / T), t = int(fl % T);
         pos = t;
-        if (t % s == 0) {
+        if (ref_idx[fl * k] < 0) {                       // a reference: its own stored row
           rows[0] = int(fl);
           cnt = 1;
         } else {
@@ -997,13 +1053,37 @@ int grid_for(int64_t work_items, int per_block) {
 }  // namespace
 
 // ==================================================================== host
+const Schedule& schedule_for(int T, int s0, double alpha, int n_sink) {
+  thread_local Schedule last;
+  if (last.T == T && last.s0 == s0 && last.alpha == alpha && last.n_sink == n_sink) return last;
+  Schedule sc;
+  sc.T = T; sc.s0 = s0; sc.alpha = alpha; sc.n_sink = n_sink;
+  for (int t = 0; t < std::min(n_sink, T); ++t) sc.rpos.push_back(t);
+  // p_{m+1} = p_m + s0 + floor(alpha * (p_m - n_sink)) ([RKV] §2.6), in
+  // 64-bit integers and the floor of the double product
+  for (long long p = n_sink; p < T;) {
+    sc.rpos.push_back(int(p));
+    p += s0 + (long long)std::floor(alpha * double(p - n_sink));
+  }
+  sc.nrp.reserve(size_t(T) - sc.rpos.size());
+  size_t j = 0;
+  for (int t = 0; t < T; ++t) {
+    if (j < sc.rpos.size() && sc.rpos[j] == t) ++j;
+    else sc.nrp.push_back(t);
+  }
+  last = std::move(sc);
+  return last;
+}
+
 Shape make_shape(int B, int T, int N, int D, int d_ff, int d_c, int k, int g, int b, int s,
-                 bool bf16) {
+                 bool bf16, double alpha, int n_sink) {
   Shape sh{};
   sh.B = B; sh.T = T; sh.C = 2 * N * D; sh.d_ff = d_ff; sh.d_c = d_c; sh.k = k;
   sh.g = g; sh.b = b; sh.s = s; sh.bf16 = bf16;
+  sh.alpha = alpha; sh.n_sink = n_sink;
   sh.esize = bf16 ? 2 : 4;
-  sh.nref = (T + s - 1) / s;
+  sh.sched = &schedule_for(T, s, alpha, n_sink);
+  sh.nref = int(sh.sched->rpos.size());
   sh.nr = T - sh.nref;
   sh.kl = k <= 4 ? 4 : 8;
   sh.n_chunks = cdiv(sh.nref, bf16 ? DistCfg<uint16_t>::BM : DistCfg<float>::BM);
@@ -1022,6 +1102,9 @@ Workspace plan_workspace(const Shape& sh) {
   L.proj = take(size_t(sh.B) * sh.nref * 2 * sh.d_ff * 4);
   L.part = take(size_t(sh.B) * sh.n_chunks * sh.nr * sh.kl * 8);
   L.dh = take(size_t(sh.B) * sh.nr * sh.k3 * sh.esize);
+  L.rpos = take(size_t(sh.nref) * 4);
+  L.nrp = take(size_t(sh.nr) * 4);
+  L.tab = take(size_t(sh.T) * 4);
   L.total = off;
   return L;
 }
@@ -1045,19 +1128,39 @@ hipError_t launch_pack_weights(const Shape& sh, const void* w1, const void* w2, 
   return hipGetLastError();
 }
 
+hipError_t launch_schedule(const Shape& sh, char* ws, const Workspace& L, hipStream_t st) {
+  auto* rpos = reinterpret_cast<int*>(ws + L.rpos);
+  auto* tab = reinterpret_cast<int*>(ws + L.tab);
+  auto* nrp = reinterpret_cast<int*>(ws + L.nrp);
+  if (sh.alpha == 0.0) {                                  // nref <= T: one thread per token
+    k_sched_fixed<<<cdiv(sh.T, 256), 256, 0, st>>>(rpos, sh.nref, sh.T, sh.s, sh.n_sink, tab, nrp);
+    return hipGetLastError();
+  }
+  for (int first = 0; first < sh.nref; first += kPosChunk) {
+    PosChunk c;
+    c.first = first;
+    c.count = std::min(kPosChunk, sh.nref - first);
+    for (int i = 0; i < c.count; ++i) c.pos[i] = sh.sched->rpos[size_t(first) + i];
+    k_sched_chunk<<<1, 256, 0, st>>>(rpos, c);
+  }
+  k_sched_tables<<<cdiv(sh.T, 256), 256, 0, st>>>(rpos, sh.nref, sh.T, tab, nrp);
+  return hipGetLastError();
+}
+
 hipError_t launch_ref_norms(const Shape& sh, const void* kv, char* ws, const Workspace& L,
                             int32_t* ref_idx, uint8_t* codes, uint16_t* scale, uint16_t* zmin,
                             float* z, hipStream_t st) {
   const int rows = sh.B * sh.nref;
   auto* y = reinterpret_cast<float*>(ws + L.ysq);
+  const auto* rpos = reinterpret_cast<const int*>(ws + L.rpos);
   const auto* p = static_cast<const char*>(kv);
   const int cb = sh.d_c * sh.b / 8, ng = sh.d_c / sh.g;
   if (sh.bf16)
-    k_ref_gather<uint16_t><<<cdiv(rows, 4), 256, 0, st>>>(p, sh.B, sh.T, sh.C, sh.s, sh.nref,
+    k_ref_gather<uint16_t><<<cdiv(rows, 4), 256, 0, st>>>(p, sh.B, sh.T, sh.C, rpos, sh.nref,
                                                           ws + L.refs, y, ref_idx, sh.k, codes, cb,
                                                           scale, zmin, ng, z, sh.d_c);
   else
-    k_ref_gather<float><<<cdiv(rows, 4), 256, 0, st>>>(p, sh.B, sh.T, sh.C, sh.s, sh.nref,
+    k_ref_gather<float><<<cdiv(rows, 4), 256, 0, st>>>(p, sh.B, sh.T, sh.C, rpos, sh.nref,
                                                        ws + L.refs, y, ref_idx, sh.k, codes, cb,
                                                        scale, zmin, ng, z, sh.d_c);
   return hipGetLastError();
@@ -1071,8 +1174,7 @@ static int dist_items(const Shape& sh, int n_tt) {
   for (int g = 0; g < sh.B * n_tt; ++g) {
     const int tt = g % n_tt;
     const int q = std::min(tt * BN + BN, sh.nr) - 1;
-    const int pl = (q / (sh.s - 1)) * sh.s + (q % (sh.s - 1)) + 1;
-    const int np = (pl + sh.s - 1) / sh.s;
+    const int np = sh.sched->nrp[q] - q;               // references before the tile's last token
     per_xcd[g & 7] += (np + BM - 1) / BM;
   }
   return int(8 * *std::max_element(per_xcd, per_xcd + 8));
@@ -1084,11 +1186,12 @@ hipError_t launch_dist(const Shape& sh, const void* kv, char* ws, const Workspac
   const auto* p = static_cast<const char*>(kv);
   const auto* y = reinterpret_cast<const float*>(ws + L.ysq);
   auto* part = reinterpret_cast<float2*>(ws + L.part);
+  const auto* nrp = reinterpret_cast<const int*>(ws + L.nrp);
 #define RKV_DIST(E, KL)                                                                      \
   do {                                                                                       \
     const int n_tt = cdiv(sh.nr, DistCfg<E>::BN);                                            \
     k_dist_topk<E, KL><<<dist_items<E>(sh, n_tt), DistCfg<E>::kThreads, 0, st>>>(            \
-        p, ws + L.refs, y, part, sh.B, sh.T, sh.C, sh.s, sh.nref, sh.nr, sh.n_chunks, n_tt); \
+        p, ws + L.refs, y, part, sh.B, sh.T, sh.C, nrp, sh.nref, sh.nr, sh.n_chunks, n_tt);  \
   } while (0)
   if (sh.bf16) { if (sh.kl == 4) RKV_DIST(uint16_t, 4); else RKV_DIST(uint16_t, 8); }
   else { if (sh.kl == 4) RKV_DIST(float, 4); else RKV_DIST(float, 8); }
@@ -1101,8 +1204,10 @@ hipError_t launch_merge(const Shape& sh, int32_t* ref_idx, char* ws, const Works
   const auto* part = reinterpret_cast<const float2*>(ws + L.part);
   const int nb = cdiv(long(sh.B) * sh.T, 64);   // one wave per block: every CU takes part
   const int chunk = sh.bf16 ? DistCfg<uint16_t>::BM : DistCfg<float>::BM;
+  const auto* tab = reinterpret_cast<const int*>(ws + L.tab);
+  const auto* rpos = reinterpret_cast<const int*>(ws + L.rpos);
 #define RKV_MERGE(KL)                                                                        \
-  k_topk_merge<KL><<<nb, 64, 0, st>>>(part, ref_idx, sh.B, sh.T, sh.s, sh.k, sh.nr,        \
+  k_topk_merge<KL><<<nb, 64, 0, st>>>(part, ref_idx, sh.B, sh.T, tab, rpos, sh.k, sh.nr,    \
                                       sh.n_chunks, chunk)
   if (sh.kl == 4) RKV_MERGE(4); else RKV_MERGE(8);
 #undef RKV_MERGE
@@ -1132,7 +1237,9 @@ hipError_t launch_swiglu(const Shape& sh, const void* kv, const int32_t* ref_idx
   const uint32_t pbytes = uint32_t(size_t(sh.B) * sh.nref * N * 4);
 #define RKV_SW(E, KL)                                                                           \
   k_swiglu<E, KL><<<cdiv(N, SwCfg<E>::BN) * cdiv(M, SwCfg<E>::BM), SwCfg<E>::kThreads, 0, st>>>( \
-      p, ws + L.wp, proj, pbytes, ref_idx, ws + L.dh, sh.T, sh.C, sh.s, sh.nref, sh.nr, sh.k,    \
+      p, ws + L.wp, proj, pbytes, ref_idx, ws + L.dh, sh.T, sh.C,                                \
+      reinterpret_cast<const int*>(ws + L.nrp), reinterpret_cast<const int*>(ws + L.tab),         \
+      sh.nref, sh.nr, sh.k,                                                                        \
       sh.d_ff, M)
   if (sh.bf16) { if (sh.kl == 4) RKV_SW(uint16_t, 4); else RKV_SW(uint16_t, 8); }
   else { if (sh.kl == 4) RKV_SW(float, 4); else RKV_SW(float, 8); }
@@ -1148,7 +1255,8 @@ hipError_t launch_w3_quant(const Shape& sh, char* ws, const Workspace& L, uint8_
   const char* w = ws + L.w3p;
 #define RKV_W3(E, BITS, G8)                                                                   \
   k_w3_quant<E, BITS, G8><<<cdiv(N, W3Cfg<E>::BN) * cdiv(M, W3Cfg<E>::BM), W3Cfg<E>::kThreads, \
-                            0, st>>>(a, w, sh.k3, M, N, cdiv(M, W3Cfg<E>::BM), sh.T, sh.s,     \
+                            0, st>>>(a, w, sh.k3, M, N, cdiv(M, W3Cfg<E>::BM), sh.T,           \
+                                     reinterpret_cast<const int*>(ws + L.nrp),                 \
                                      sh.nr, codes, scale, zmin, z)
 #define RKV_W3G(E, BITS)                      \
   switch (sh.g) {                             \
@@ -1229,15 +1337,15 @@ hipError_t launch_restore(const Shape& sh, int N, int D, const uint8_t* codes,
   const int grid = grid_for(int64_t(n_idx) * (sh.d_c / 8), 256);
   auto* zt = reinterpret_cast<uint32_t*>(ws + L.zt);
 #define RKV_RP(E, BITS)                                                                       \
-  k_restore_prep<E, BITS><<<grid, 256, 0, st>>>(codes, scale, zmin, idx, n_idx, total, sh.T,  \
-                                                sh.s, sh.d_c, sh.g, zt)
+  k_restore_prep<E, BITS><<<grid, 256, 0, st>>>(codes, scale, zmin, idx, n_idx, total, ref_idx, \
+                                                sh.k, sh.d_c, sh.g, zt)
   if (sh.bf16) { if (sh.b == 4) RKV_RP(uint16_t, 4); else RKV_RP(uint16_t, 2); }
   else { if (sh.b == 4) RKV_RP(float, 4); else RKV_RP(float, 2); }
 #undef RKV_RP
   const auto* kvp = static_cast<const char*>(kv);
 #define RKV_RS(E, KL)                                                                            \
   k_restore<E, KL><<<cdiv(n_idx, RsCfg<E>::BM) * cdiv(sh.C, RsCfg<E>::BN), RsCfg<E>::kThreads, 0, \
-                     st>>>(ws + L.zt, ws + L.wdp, L.kr, idx, n_idx, total, sh.T, sh.s, sh.k,      \
+                     st>>>(ws + L.zt, ws + L.wdp, L.kr, idx, n_idx, total, sh.T, sh.k,            \
                            ref_idx, kvp, sh.C, N * D, D, theta, out, out_bf16 ? 1 : 0)
   if (sh.bf16) { if (sh.kl == 4) RKV_RS(uint16_t, 4); else RKV_RS(uint16_t, 8); }
   else { if (sh.kl == 4) RKV_RS(float, 4); else RKV_RS(float, 8); }

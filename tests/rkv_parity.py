@@ -32,7 +32,8 @@ DEQ_REL = 1e-2
 
 def params_of(cfg):
     return R.params(B=cfg.B, T=cfg.T, N=cfg.N, D=cfg.D, d_ff=cfg.d_ff, d_c=cfg.d_c, k=cfg.k,
-                    g=cfg.g, b=cfg.b, ref_stride=cfg.stride, dtype=cfg.dtype)
+                    g=cfg.g, b=cfg.b, ref_stride=cfg.stride, dtype=cfg.dtype, n_sink=cfg.n_sink,
+                    ref_alpha=cfg.alpha)
 
 
 def to_device(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
@@ -55,16 +56,27 @@ def run_encode(w, device="cuda", with_z=True):
     return p, out, host, (kv, w1, w2, w3)
 
 
-def sample_positions(T: int, s: int, n_random: int, seed: int = 123) -> np.ndarray:
+def ref_mask_of(cfg) -> np.ndarray:
+    """Boolean [T]: the positions the schedule stores as references."""
+    m = np.zeros(cfg.T, dtype=bool)
+    m[O.reference_schedule(cfg.T, cfg.stride, cfg.alpha, cfg.n_sink)] = True
+    return m
+
+
+def sample_positions(T: int, s: int, n_random: int, seed: int = 123, cfg=None) -> np.ndarray:
+    """Warm-up, tail, token-tile boundaries (tiles of 128 non-reference
+    tokens) and n_random seeded positions."""
     rng = np.random.default_rng(seed)
-    pos = set(range(min(T, 3 * s + 8)))                 # warm-up: k_t < k, references
+    mask = ref_mask_of(cfg) if cfg is not None else (np.arange(T) % s) == 0
+    refs, nonref = np.flatnonzero(mask), np.flatnonzero(~mask)
+    n_sink = cfg.n_sink if cfg is not None else 0
+    warm = int(refs[min(len(refs) - 1, n_sink + 3)]) + 8
+    pos = set(range(min(T, warm)))                      # warm-up: k_t < k, references
     pos |= set(range(max(0, T - 24), T))                # tail
-    nr = T - (T + s - 1) // s
-    for q in range(0, nr, 128):                         # token-tile boundaries
+    for q in range(0, len(nonref), 128):
         for dq in (-1, 0, 1):
-            qq = q + dq
-            if 0 <= qq < nr:
-                pos.add((qq // (s - 1)) * s + qq % (s - 1) + 1 if s > 1 else 0)
+            if 0 <= q + dq < len(nonref):
+                pos.add(int(nonref[q + dq]))
     pos |= set(int(x) for x in rng.choice(T, size=min(T, n_random), replace=False))
     return np.array(sorted(p for p in pos if p < T), dtype=np.int64)
 
@@ -85,11 +97,12 @@ def compare_tokens(w, host, positions_by_seq, gathered=None, log=print):
     deq_num2 = deq_den2 = 0.0
     for bi, pos in positions_by_seq.items():
         kvb = kv32[bi].astype(np.float64)
-        orc = O.encode_tokens(kvb, W1, W2, W3, pos, k=k, g=g, b=bb, s=s)
+        orc = O.encode_tokens(kvb, W1, W2, W3, pos, k=k, g=g, b=bb, s=s, alpha=cfg.alpha,
+                              n_sink=cfg.n_sink)
         g_ref = host["ref_idx"][bi, pos]
         z_orc = orc["z"].copy()
         for i, t in enumerate(pos):
-            if t % s == 0:
+            if orc["is_ref"][i]:
                 assert np.all(g_ref[i] == -1), (bi, t)
                 assert np.all(host["codes"][bi, t] == 0) and np.all(host["scale"][bi, t] == 0)
                 assert np.all(host["zmin"][bi, t] == 0)
@@ -171,15 +184,16 @@ def compare_tokens(w, host, positions_by_seq, gathered=None, log=print):
 
 def check_record_invariants(cfg, host):
     """Properties that hold at any size, checked on every token."""
-    B, T, k, s = cfg.B, cfg.T, cfg.k, cfg.stride
+    B, T, k = cfg.B, cfg.T, cfg.k
     t = np.arange(T)
-    is_ref = (t % s) == 0
-    want = np.where(is_ref, 0, np.minimum(k, (t + s - 1) // s))
+    is_ref = ref_mask_of(cfg)
+    pool = np.cumsum(is_ref) - is_ref                       # references before t
+    want = np.where(is_ref, 0, np.minimum(k, pool))
     ri = host["ref_idx"]
     cnt = (ri >= 0).sum(axis=2)
     assert np.array_equal(cnt, np.broadcast_to(want, (B, T)))
     valid = ri >= 0
-    assert np.all(ri[valid] % s == 0)
+    assert np.all(is_ref[ri[valid]])                        # members of the schedule
     assert np.all(np.where(valid, ri, -1) < t[None, :, None])
     assert np.all(valid[:, :, 1:] <= valid[:, :, :-1])          # chosen first, then pads
     both = valid[:, :, 1:] & valid[:, :, :-1]

@@ -37,7 +37,8 @@ def test_status_strings():
 
 def _p(cfg, **kw):
     d = dict(B=cfg.B, T=cfg.T, N=cfg.N, D=cfg.D, d_ff=cfg.d_ff, d_c=cfg.d_c, k=cfg.k, g=cfg.g,
-             b=cfg.b, ref_stride=cfg.stride, dtype=cfg.dtype)
+             b=cfg.b, ref_stride=cfg.stride, dtype=cfg.dtype, n_sink=cfg.n_sink,
+             ref_alpha=cfg.alpha)
     d.update(kw)
     return R.params(**d)
 
@@ -77,6 +78,8 @@ def test_workspace_size_zero_for_invalid_params():
     ("g", 24, R.RKV_ERR_UNSUPPORTED), ("k", 9, R.RKV_ERR_UNSUPPORTED),
     ("d_c", 48, R.RKV_ERR_UNSUPPORTED), ("g", 64, R.RKV_ERR_UNSUPPORTED),
     ("d_ff", 1000, R.RKV_ERR_UNSUPPORTED), ("D", 10, R.RKV_ERR_UNSUPPORTED),
+    ("ref_alpha", -0.5, R.RKV_ERR_INVALID_ARG), ("ref_alpha", float("nan"), R.RKV_ERR_INVALID_ARG),
+    ("n_sink", -1, R.RKV_ERR_INVALID_ARG),
 ])
 def test_encode_rejects_bad_params(field, value, status):
     kw = {field: value}
@@ -169,3 +172,10 @@ def test_restore_validation():
     # n_idx == 0 is a no-op and touches no pointer
     assert R.rkv_restore(p, None, None, None, None, None, None, None, 0, 1.0, None, R.RKV_F32,
                          None, 0, None, check=False) == R.RKV_OK
+
+
+def test_dynamic_schedule_shrinks_the_workspace():
+    """Fewer references under a growing schedule ([RKV] §2.6) need fewer
+    reference rows and projections."""
+    from synth.configs import LLAMA32K_DYN
+    assert 0 < R.rkv_encode_workspace_bytes(_p(LLAMA32K_DYN)) < R.rkv_encode_workspace_bytes(_p(LLAMA32K))

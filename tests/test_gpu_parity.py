@@ -8,7 +8,8 @@ import reference_residual_encoding_amd as R
 from reference_residual_encoding_amd import buffers as RB
 from oracle import rkv_oracle as O
 from synth import generate
-from synth.configs import LLAMA8K, LLAMA32K, MM_INT2, QWEN_LIKE, TINY
+from synth.configs import (LLAMA8K, LLAMA8K_DYN, LLAMA32K, LLAMA32K_DYN, MM_INT2, QWEN_LIKE,
+                           TINY, TINY_DYN)
 
 import rkv_parity as P
 
@@ -86,9 +87,35 @@ def test_full_size_configs_sampled(cfg, n_random):
     p, out, host, _ = P.run_encode(w)
     P.check_record_invariants(cfg, host)
     P.check_quantizer_bit_exact(cfg, host)
-    pos = {b: P.sample_positions(cfg.T, cfg.stride, n_random, seed=100 + b) for b in range(cfg.B)}
+    pos = {b: P.sample_positions(cfg.T, cfg.stride, n_random, seed=100 + b, cfg=cfg)
+           for b in range(cfg.B)}
     gathered = {b: _gather_rows(p, out, b * cfg.T + pos[b]) for b in range(cfg.B)}
     P.compare_tokens(w, host, pos, gathered, log=_log)
+
+
+# Dynamic reference schedule ([RKV] §2.6): sinks, a growing stride, a pool
+# that outgrows one candidate chunk, schedules where the sinks cover the
+# whole sequence, both dtypes.
+DYN_EDGE = [
+    TINY_DYN,
+    TINY.with_(name="dyn_sinks_cover_T", T=6, n_sink=8, alpha=0.1),
+    TINY.with_(name="dyn_sinks_fixed_stride", T=200, n_sink=5),
+    TINY.with_(name="dyn_fast_growth_bf16", T=500, alpha=0.5, n_sink=1, dtype="bf16"),
+    RAGGED[0].with_(name="dyn_ragged_bf16_k5", alpha=0.01, n_sink=3),
+    RAGGED[2].with_(name="dyn_ragged_bf16_k8", T=3000, stride=2, alpha=0.002, n_sink=16),
+]
+
+
+@pytest.mark.parametrize("cfg", DYN_EDGE, ids=lambda c: c.name)
+def test_dynamic_schedule_all_positions(cfg):
+    _log(f"[case] {cfg.name} full")
+    _full_parity(cfg)
+
+
+@pytest.mark.parametrize("cfg,n_random", [(LLAMA8K_DYN, 600), (LLAMA32K_DYN, 400)],
+                         ids=lambda c: getattr(c, "name", c))
+def test_dynamic_schedule_sampled(cfg, n_random):
+    test_full_size_configs_sampled(cfg, n_random)
 
 
 def test_select_export_matches_encode():

@@ -15,7 +15,7 @@ import torch
 import reference_residual_encoding_amd as R
 from oracle import rkv_oracle as O
 from synth import bf16_bits_to_f32, decoder_weight, generate
-from synth.configs import LLAMA8K, LLAMA32K, QWEN_LIKE, TINY
+from synth.configs import LLAMA8K, LLAMA8K_DYN, LLAMA32K, QWEN_LIKE, TINY, TINY_DYN
 
 import rkv_parity as P
 
@@ -40,7 +40,8 @@ def _oracle_records(w, positions_by_seq):
     kv = w.kv_f32().astype(np.float64)
     W1, W2, W3 = (x.astype(np.float64) for x in w.weights_f32())
     for b, pos in positions_by_seq.items():
-        enc = O.encode_tokens(kv[b], W1, W2, W3, pos, k=cfg.k, g=cfg.g, b=cfg.b, s=cfg.stride)
+        enc = O.encode_tokens(kv[b], W1, W2, W3, pos, k=cfg.k, g=cfg.g, b=cfg.b, s=cfg.stride,
+                              alpha=cfg.alpha, n_sink=cfg.n_sink)
         rows = b * cfg.T + np.asarray(enc["positions"])
         codes[rows], scale[rows], zmin[rows], ref_idx[rows] = (
             enc["codes"], enc["scale"], enc["zmin"], enc["ref_idx"])
@@ -75,7 +76,7 @@ def _oracle(w, wd, rec, idx, theta):
     return O.restore(codes, scale, zmin, ref_idx, w.kv_f32().astype(np.float64),
                      bf16_bits_to_f32(wd) if cfg.dtype == "bf16" else wd, np.asarray(idx),
                      s=cfg.stride, N=cfg.N, D=cfg.D, g=cfg.g, b=cfg.b, d_c=cfg.d_c,
-                     rope_theta=theta)
+                     rope_theta=theta, alpha=cfg.alpha, n_sink=cfg.n_sink)
 
 
 def _compare(got, ref, tol, name):
@@ -101,12 +102,25 @@ def test_restore_tiny_all_positions(out_dtype, tol):
         _compare(got, _oracle(w, wd, rec, idx, theta), tol, f"tiny theta={theta} {out_dtype}")
 
 
-@pytest.mark.parametrize("cfg", [LLAMA8K, QWEN_LIKE], ids=lambda c: c.name)
+def test_restore_dynamic_schedule_all_positions():
+    """Sinks and a growing stride ([RKV] §2.6): every reference token,
+    sinks included, restores to its own row."""
+    cfg = TINY_DYN
+    _log(f"[case] restore {cfg.name}")
+    w = generate(cfg)
+    wd = decoder_weight(cfg)
+    rec = _oracle_records(w, {0: np.arange(cfg.T)})
+    idx = np.arange(cfg.T)
+    got = _run(w, wd, rec, idx, cfg.rope_theta, "f32")
+    _compare(got, _oracle(w, wd, rec, idx, cfg.rope_theta), REL_F32, f"{cfg.name} f32")
+
+
+@pytest.mark.parametrize("cfg", [LLAMA8K, QWEN_LIKE, LLAMA8K_DYN], ids=lambda c: c.name)
 def test_restore_sampled_tokens(cfg):
     _log(f"[case] restore {cfg.name}")
     w = generate(cfg)
     wd = decoder_weight(cfg)
-    pos = {b: P.sample_positions(cfg.T, cfg.stride, 120, seed=7 + b) for b in range(cfg.B)}
+    pos = {b: P.sample_positions(cfg.T, cfg.stride, 120, seed=7 + b, cfg=cfg) for b in range(cfg.B)}
     rec = _oracle_records(w, pos)
     idx = np.concatenate([b * cfg.T + pos[b] for b in range(cfg.B)])
     rng = np.random.default_rng(11)
