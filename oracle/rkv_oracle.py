@@ -23,6 +23,10 @@ notes' own section numbers.  Every step follows the order of [RKV] §2.1-§2.4:
   7. dequantisation of selected tokens           ([RKV] §2.4 third eq.,
                                                    §2.7 decode step 3)
 
+Append (decode step 4 of [RKV] §2.7): a new token at position t is stored as
+it is when t is on the schedule, else encoded by steps 2-6 against the
+references already in the cache.
+
 Readings taken where the notes are silent (each is listed with its reason in
 the design notes of the repository):
   * the schedule starts at p_0 = n_sink after the n_sink sink tokens, which
@@ -321,6 +325,43 @@ def encode(kv: np.ndarray, W1, W2, W3, *, k: int, g: int, b: int, s: int,
     for key in ("ref_idx", "z", "q", "scale", "zmin", "codes", "d_diag", "is_ref"):
         out[key] = np.stack([p[key] for p in parts])
     return out
+
+
+def append_token(cache_seq: np.ndarray, kv_new: np.ndarray, t: int, W1, W2, W3, *, k: int,
+                 g: int, b: int, s: int, alpha: float = 0.0, n_sink: int = 0) -> Dict:
+    """Decode step 4 of [RKV] §2.7 for one sequence: the new token enters the
+    cache at position t.
+
+    When the schedule ([RKV] §2.6) makes t a reference, the token is stored
+    as it is (stored=True, all-zero record, ref_idx all -1).  Otherwise it is
+    encoded against the references already in the cache, the rows
+    cache_seq[j] at scheduled positions j < t, by retrieval (§2.2), the mean
+    (§2.2), z = f_c(kv_new) - f_c(mean) (§2.3) and the quantiser (§2.4).
+    No other row of cache_seq is read.  The cache itself is not modified:
+    the caller stores kv_new at row t when stored is True."""
+    T = len(cache_seq)
+    kv_new = np.asarray(kv_new, F64)
+    d_c = np.asarray(W3).shape[1]
+    refs = reference_schedule(T, s, alpha, n_sink)
+    ref_idx = np.full(k, -1, dtype=np.int32)
+    z = np.zeros((1, d_c), dtype=F64)
+    stored = bool(np.any(refs == t))
+    if not stored:
+        pool = refs[refs < t]
+        d = squared_l2(kv_new, np.asarray(cache_seq[pool], F64))
+        order = np.lexsort((pool, d))                 # by (distance, position)
+        R = pool[order[:k_effective(k, len(pool))]]
+        ref_idx[:len(R)] = np.sort(R)
+        mean = np.asarray(cache_seq[R], F64).sum(axis=0) / F64(len(R))
+        z = residual_latent(kv_new[None, :], mean[None, :], np.asarray(W1, F64),
+                            np.asarray(W2, F64), np.asarray(W3, F64))
+    q, dh, mh = quantize(z, g, b)
+    if stored:
+        q[:] = 0
+        dh[:] = 0
+        mh[:] = 0
+    return dict(stored=stored, ref_idx=ref_idx, z=z[0], q=q[0], scale=dh[0], zmin=mh[0],
+                codes=pack_codes(q, b)[0])
 
 
 def gather(codes: np.ndarray, scale: np.ndarray, zmin: np.ndarray, idx: np.ndarray,

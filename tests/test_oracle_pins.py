@@ -530,3 +530,76 @@ def test_dynamic_schedule_pool_and_selection_follow_the_schedule():
         want = sorted(p for _, p in sorted(d)[:min(3, len(pool))])
         got = [int(p) for p in enc["ref_idx"][i] if p >= 0]
         assert got == want, t
+
+
+# ------------------------------------------------------------ append
+
+def _append_all(kv, W1, W2, W3, *, k, g, b, s, alpha=0.0, n_sink=0):
+    """Append every position in order to a cache whose rows start as NaN."""
+    T = len(kv)
+    cache = np.full_like(kv, np.nan)
+    recs = []
+    for t in range(T):
+        r = O.append_token(cache, kv[t], t, W1, W2, W3, k=k, g=g, b=b, s=s, alpha=alpha,
+                           n_sink=n_sink)
+        if r["stored"]:
+            cache[t] = kv[t]
+        recs.append(r)
+    return cache, recs
+
+
+@pytest.mark.parametrize("alpha,n_sink", [(0.0, 0), (0.02, 2)])
+def test_append_in_order_reproduces_the_prefix_encode(tiny, alpha, n_sink):
+    """[RKV] §2.7 decode step 4: appending a sequence token by token to a cache
+    that holds nothing but the stored references gives the records of encoding
+    the whole prefix; rows that are never stored stay NaN and are never read
+    (a NaN there would poison every distance)."""
+    w, kv, W1, W2, W3 = tiny
+    c = TINY
+    cache, recs = _append_all(kv, W1, W2, W3, k=c.k, g=c.g, b=c.b, s=c.stride, alpha=alpha,
+                              n_sink=n_sink)
+    enc = O.encode(kv[None], W1, W2, W3, k=c.k, g=c.g, b=c.b, s=c.stride, alpha=alpha,
+                   n_sink=n_sink)
+    refs = O.reference_schedule(c.T, c.stride, alpha, n_sink)
+    mask = np.zeros(c.T, bool)
+    mask[refs] = True
+    np.testing.assert_array_equal(cache[mask], kv[mask])
+    assert np.isnan(cache[~mask]).all()
+    for t, r in enumerate(recs):
+        assert r["stored"] == mask[t]
+        np.testing.assert_array_equal(r["ref_idx"], enc["ref_idx"][0, t])
+        np.testing.assert_array_equal(r["codes"], enc["codes"][0, t])
+        np.testing.assert_array_equal(r["scale"], enc["scale"][0, t])
+        np.testing.assert_array_equal(r["zmin"], enc["zmin"][0, t])
+        np.testing.assert_allclose(r["z"], enc["z"][0, t], rtol=0, atol=1e-12)
+
+
+def test_append_selection_minimises_the_retrieval_radius():
+    """[RKV] §2.8: the appended token's chosen set minimises the mean squared
+    distance rho^2 to the chosen references over every k-subset of the pool
+    (brute-force enumeration)."""
+    rng = np.random.default_rng(31)
+    T, C, s, k = 60, 12, 5, 3
+    kv = rng.standard_normal((T, C))
+    W = rng.standard_normal((C, 4))
+    W3 = rng.standard_normal((4, 8))
+    cache = np.full_like(kv, np.nan)
+    cache[::s] = kv[::s]
+    for t in (7, 23, 59):
+        r = O.append_token(cache, kv[t], t, W, W, W3, k=k, g=8, b=4, s=s)
+        pool = list(range(0, t, s))
+        rho = lambda R: np.mean([((kv[t] - kv[j]) ** 2).sum() for j in R])
+        best = min(rho(R) for R in itertools.combinations(pool, min(k, len(pool))))
+        assert abs(rho([int(j) for j in r["ref_idx"] if j >= 0]) - best) <= 1e-12 * best
+
+
+def test_append_of_a_reference_position_is_stored_with_a_zero_record(tiny):
+    """[RKV] §2.4 and §2.7 step 4: a token the schedule makes a reference is stored as it is."""
+    w, kv, W1, W2, W3 = tiny
+    c = TINY
+    cache = np.full_like(kv, np.nan)
+    r = O.append_token(cache, kv[3 * c.stride], 3 * c.stride, W1, W2, W3, k=c.k, g=c.g, b=c.b,
+                       s=c.stride)
+    assert r["stored"]
+    assert np.all(r["ref_idx"] == -1) and not r["codes"].any()
+    assert not r["scale"].any() and not r["zmin"].any() and not r["z"].any()
