@@ -66,16 +66,26 @@ def measured_traffic(workload: str, kernel: str):
     return table.get(kernel)
 
 
-def stage_work(cfg, n_gather: int):
+def schedule_counts(refs, T: int):
+    """(references, non-references, causal (token, reference) pairs) of one
+    sequence, from the schedule's reference positions."""
+    import numpy as np
+    mask = np.zeros(T, dtype=bool)
+    mask[np.asarray(refs, dtype=np.int64)] = True
+    before = np.cumsum(mask) - mask                  # references before each position
+    return int(mask.sum()), int(T - mask.sum()), int(before[~mask].sum())
+
+
+def stage_work(cfg, n_gather: int, refs):
     """Algorithmic work of one launch of each stage: (kind, amount).
 
     MFMA stages count 2 flops per multiply-add of the contraction the method
     needs (the bf16 hi/lo split of the W3 input is not counted); HBM-bound
-    stages count the bytes they must move."""
-    B, T, C, s = cfg.B, cfg.T, cfg.C, cfg.stride
-    nref = -(-T // s)
-    nr = T - nref
-    pairs = sum(-(-t // s) for t in range(T) if t % s) * B        # causal (token, reference) pairs
+    stages count the bytes they must move.  `refs` are the schedule's
+    reference positions (rkv_reference_positions)."""
+    B, T, C = cfg.B, cfg.T, cfg.C
+    nref, nr, pairs = schedule_counts(refs, T)
+    pairs *= B
     esz = 2 if cfg.dtype == "bf16" else 4
     rec = cfg.d_c * cfg.b // 8 + 4 * (cfg.d_c // cfg.g)
     return {
@@ -104,10 +114,13 @@ def cpu_baseline(w, n_tokens: int, seed: int = 0):
     rng = np.random.default_rng(seed)
     kv = w.kv_f32()[0].astype(np.float64)
     W1, W2, W3 = (x.astype(np.float64) for x in w.weights_f32())
-    nonref = np.array([t for t in range(cfg.T) if t % cfg.stride], dtype=np.int64)
+    mask = np.zeros(cfg.T, dtype=bool)
+    mask[O.reference_schedule(cfg.T, cfg.stride, cfg.alpha, cfg.n_sink)] = True
+    nonref = np.flatnonzero(~mask)
     pos = np.sort(rng.choice(nonref, size=n_tokens, replace=False))
     t0 = time.perf_counter()
-    O.encode_tokens(kv, W1, W2, W3, pos, k=cfg.k, g=cfg.g, b=cfg.b, s=cfg.stride)
+    O.encode_tokens(kv, W1, W2, W3, pos, k=cfg.k, g=cfg.g, b=cfg.b, s=cfg.stride,
+                    alpha=cfg.alpha, n_sink=cfg.n_sink)
     dt = time.perf_counter() - t0
     return {"value": n_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{n_tokens} random non-reference tokens of sequence 0 of {cfg.name}, "
@@ -159,6 +172,74 @@ def bench_restore(R, cfg, w, p, kv, out, idx, stream, args):
             "out_dtype": "bf16", "rope_theta": cfg.rope_theta}
 
 
+def bench_append(R, cfg, p_enc, kv, w1, w2, w3, stream, args, batches=(1, 16)):
+    """rkv_append ([RKV] §2.7 decode step 4) at the end of the workload's
+    context: B sequences each append the token at a non-reference position
+    near T, against a pool of every reference before it.  The cache of B
+    sequences repeats the workload's sequence 0 (same shape and statistics);
+    timed with events over repeated calls (each call rewrites the same
+    records).  HBM bytes per call are algorithmic: the pool rows read by the
+    distances, the chosen rows of the mean, the new rows, W1, W2 and W3 once,
+    and the records written."""
+    import numpy as np
+    import torch
+    dev = kv.device
+    refs = R.rkv_reference_positions(p_enc)
+    mask = np.zeros(cfg.T, dtype=bool)
+    mask[refs] = True
+    nonref = np.flatnonzero(~mask)
+    esz = 2 if cfg.dtype == "bf16" else 4
+    rec = cfg.d_c * cfg.b // 8 + 4 * (cfg.d_c // cfg.g) + 4 * cfg.k
+    out = []
+    for B in batches:
+        p = R.params(B=B, T=cfg.T, N=cfg.N, D=cfg.D, d_ff=cfg.d_ff, d_c=cfg.d_c, k=cfg.k, g=cfg.g,
+                     b=cfg.b, ref_stride=cfg.stride, dtype=cfg.dtype, n_sink=cfg.n_sink,
+                     ref_alpha=cfg.alpha)
+        cache = kv[:1].expand(B, -1, -1).contiguous()
+        pos_h = nonref[len(nonref) - 1 - 3 * np.arange(B)]
+        pos = torch.from_numpy(pos_h.astype(np.int32)).to(dev)
+        kv_new = cache[torch.arange(B, device=dev), pos.long()].contiguous()
+        n = B * cfg.T
+        ref_idx = torch.empty((n, cfg.k), dtype=torch.int32, device=dev)
+        codes = torch.empty((n, cfg.d_c * cfg.b // 8), dtype=torch.uint8, device=dev)
+        scale = torch.empty((n, cfg.d_c // cfg.g), dtype=torch.float16, device=dev)
+        zmin = torch.empty_like(scale)
+        wsb = R.rkv_append_workspace_bytes(p)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+        def call():
+            R.rkv_append(p, cache, kv_new, pos, w1, w2, w3, ref_idx, codes, scale, zmin, None, ws,
+                         wsb, stream)
+
+        for _ in range(max(args.warmup, 3)):
+            call()
+        st = R.STAGES.index("append")
+        reps = max(args.steps, 50)
+        R.rkv_profile_begin(1 << st)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tot, cnt = R.rkv_profile_read(st)
+        R.rkv_profile_begin(0)
+        pools = np.searchsorted(np.asarray(refs), pos_h)          # references before each position
+        nbytes = (int(pools.sum()) * cfg.C * esz + B * (cfg.k + 1) * cfg.C * esz
+                  + (2 * cfg.C * cfg.d_ff + cfg.d_ff * cfg.d_c) * esz + B * rec)
+        us = ms * 1e3
+        out.append({"B": B, "us_per_call": round(us, 2), "tokens_per_s": round(B / (ms * 1e-3), 1),
+                    "stage_us": round(tot / cnt * 1e3, 2), "hbm_bytes_algorithmic": nbytes,
+                    "hbm_gb_s": round(nbytes / (tot / cnt * 1e-3) / 1e9, 1),
+                    "hbm_frac": round(nbytes / (tot / cnt * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                    "pool_refs": int(pools.max())})
+        del cache, kv_new, ref_idx, codes, scale, zmin, ws
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -167,6 +248,7 @@ def main():
     ap.add_argument("--workload", default="llama8b_T32k")
     ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-append", action="store_true", help="skip the append measurement")
     ap.add_argument("--no-restore", action="store_true",
                     help="skip the separate restore measurement (rkv_restore of the gathered rows)")
     ap.add_argument("--copy-check-mb", type=int, default=0,
@@ -251,7 +333,7 @@ def main():
     R.rkv_profile_begin(0)
     dom_ms = dom_total / dom_n
 
-    work = stage_work(cfg, idx.numel())
+    work = stage_work(cfg, idx.numel(), R.rkv_reference_positions(p))
     kind, amount = work[dominant]
     traffic = measured_traffic(cfg.name, STAGE_KERNEL[dominant])
     if kind == "flops":
@@ -294,6 +376,8 @@ def main():
     }
     if not args.no_restore:
         line["restore"] = bench_restore(R, cfg, w, p, kv, out, idx, stream, args)
+    if not args.no_append:
+        line["append"] = bench_append(R, cfg, p, kv, w1, w2, w3, stream, args)
     if not args.no_cpu_baseline:
         print(f"[bench] cpu baseline on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens)

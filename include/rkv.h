@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define RKV_ABI_VERSION 2
+#define RKV_ABI_VERSION 3
 
 typedef enum {
   RKV_OK = 0,
@@ -72,7 +72,8 @@ typedef struct {
 
 /* GPU-path limits (RKV_ERR_UNSUPPORTED otherwise): C % 64 == 0,
  * d_ff % 32 == 0, d_ff <= 65536, d_c % 32 == 0, d_c % g == 0, B*T < 2^31,
- * B*ceil(T/s)*2*d_ff*4 < 2^31 (the reference projections). */
+ * T <= 2^26, B*nref*2*d_ff*4 < 2^31 with nref the references per sequence
+ * (the reference projections). */
 
 /* Bytes of device workspace rkv_encode / rkv_select need for *p (0 if *p is
  * invalid).  The workspace holds repacked weights, reference projections,
@@ -169,9 +170,49 @@ rkv_status rkv_restore(const rkv_params* p, const uint8_t* codes,
                        void* out, rkv_dtype out_dtype, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
 
+/* Decode-time append ([RKV] §2.7 decode step 4): one new token per
+ * sequence enters the cache.  For sequence b the new token sits at position
+ * t = pos[b]:
+ *   reference t (the schedule above):  kv[b][t] = kv_new[b] (stored as it
+ *       is), its ref_idx row all -1 and its record zero;
+ *   non-reference t:  encoded exactly as rkv_encode encodes position t, with
+ *       the pool read from the cache: the references of sequence b at
+ *       positions j < t, rows kv[b][j] ([RKV] §2.2-§2.4); its ref_idx row
+ *       and record (and z) are written at b*T + t;
+ *   t outside [0, T):  sequence b is left untouched (nothing is written).
+ * Only reference rows of kv are read, and only row t of a sequence whose
+ * new token is a reference is written; the other rows of kv may hold
+ * anything.  Records of other positions are not touched.  Positions of
+ * different sequences are independent (continuous batching).
+ * Inputs:  kv [B][T][C] (in/out), the cache's stored rows, p->dtype;
+ *          kv_new [B][C], p->dtype, the new tokens (pre-RoPE K | V);
+ *          pos [B] int32, device memory; w1, w2, w3 as in rkv_encode.
+ * Outputs: ref_idx, codes, scale, zmin, z (optional) laid out as in
+ *          rkv_encode, one row per appended token.
+ * workspace: at least rkv_append_workspace_bytes(p) bytes (its contents are
+ *          private and need not be initialised).
+ * Arithmetic: fp32 on the vector ALUs from the stored values: distances by
+ * direct differences, the mean in fp32, the products x W1, x W2, m W1,
+ * m W2 and delta_h W3 in fp32; the quantiser as in rkv_encode. */
+size_t rkv_append_workspace_bytes(const rkv_params* p);
+rkv_status rkv_append(const rkv_params* p, void* kv, const void* kv_new,
+                      const int32_t* pos, const void* w1, const void* w2,
+                      const void* w3, int32_t* ref_idx, uint8_t* codes,
+                      uint16_t* scale, uint16_t* zmin, float* z,
+                      void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/* The reference schedule of [RKV] §2.6 for p->T, ref_stride, ref_alpha,
+ * n_sink, computed on the host (no device work): writes the first
+ * min(cap, n) reference positions, ascending, into rpos (HOST memory; may
+ * be NULL when cap == 0) and returns n, the number of references per
+ * sequence, or -1 on invalid fields (rkv_last_error() says which). */
+int32_t rkv_reference_positions(const rkv_params* p, int32_t* rpos,
+                                int32_t cap);
+
 /* Observability.  Stages of the encode path, in launch order, plus the
- * gather and the restore.  rkv_profile_begin(mask) makes later rkv_encode /
- * rkv_dequant_gather calls on this process record a HIP event pair around
+ * gather, the restore and the append.  rkv_profile_begin(mask) makes later
+ * calls of this library on this process record a HIP event pair around
  * every stage whose bit (1u << stage) is set in mask, and clears previous
  * records; mask 0 turns recording off (the default).  rkv_profile_read()
  * waits for the recorded events of one stage and returns the summed
@@ -188,7 +229,8 @@ typedef enum {
   RKV_STAGE_QUANT = 7,   /* stand-alone quantiser (rkv_quantize)            */
   RKV_STAGE_GATHER = 8,  /* gather-dequantise                               */
   RKV_STAGE_RESTORE = 9, /* restore: dequantise, decoder product, mean, RoPE */
-  RKV_STAGE_COUNT = 10
+  RKV_STAGE_APPEND = 10, /* decode-time append of one token per sequence    */
+  RKV_STAGE_COUNT = 11
 } rkv_stage;
 rkv_status rkv_profile_begin(uint32_t stage_mask);
 rkv_status rkv_profile_read(int32_t stage, double* total_ms, int64_t* launches);

@@ -41,10 +41,14 @@ EXPORTS = (
     "rkv_profile_read",
     "rkv_restore_workspace_bytes",
     "rkv_restore",
+    "rkv_append_workspace_bytes",
+    "rkv_append",
+    "rkv_reference_positions",
 )
 
-STAGES = ("pack", "norms", "dist", "merge", "proj", "swiglu", "w3", "quant", "gather", "restore")
-RKV_ABI_VERSION = 2
+STAGES = ("pack", "norms", "dist", "merge", "proj", "swiglu", "w3", "quant", "gather", "restore",
+          "append")
+RKV_ABI_VERSION = 3
 
 
 class rkv_params(ctypes.Structure):
@@ -98,6 +102,12 @@ def lib() -> ctypes.CDLL:
         L.rkv_restore.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, i32, ctypes.c_float, vp,
                                   ctypes.c_int, vp, sz, vp]
         L.rkv_restore.restype = ctypes.c_int
+        L.rkv_append_workspace_bytes.argtypes = [P]
+        L.rkv_append_workspace_bytes.restype = sz
+        L.rkv_append.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.rkv_append.restype = ctypes.c_int
+        L.rkv_reference_positions.argtypes = [P, vp, i32]
+        L.rkv_reference_positions.restype = i32
         _lib = L
     return _lib
 
@@ -210,3 +220,25 @@ def rkv_restore(p: rkv_params, codes, scale, zmin, ref_idx, kv, wd, idx, n_idx: 
                            _p(wd), _p(idx), int(n_idx), float(rope_theta), _p(out),
                            int(out_dtype), _p(workspace), int(workspace_bytes), _s(stream))
     return _check("rkv_restore", st) if check else st
+
+
+def rkv_append_workspace_bytes(p: rkv_params) -> int:
+    return int(lib().rkv_append_workspace_bytes(ctypes.byref(p)))
+
+
+def rkv_append(p: rkv_params, kv, kv_new, pos, w1, w2, w3, ref_idx, codes, scale, zmin, z,
+               workspace, workspace_bytes: int, stream=None, *, check: bool = True) -> int:
+    st = lib().rkv_append(ctypes.byref(p), _p(kv), _p(kv_new), _p(pos), _p(w1), _p(w2), _p(w3),
+                          _p(ref_idx), _p(codes), _p(scale), _p(zmin), _p(z), _p(workspace),
+                          int(workspace_bytes), _s(stream))
+    return _check("rkv_append", st) if check else st
+
+
+def rkv_reference_positions(p: rkv_params):
+    """The schedule's reference positions (host query): a list of ints."""
+    n = lib().rkv_reference_positions(ctypes.byref(p), None, 0)
+    if n < 0:
+        raise RkvError("rkv_reference_positions", RKV_ERR_INVALID_ARG, rkv_last_error())
+    buf = (ctypes.c_int32 * max(n, 1))()
+    lib().rkv_reference_positions(ctypes.byref(p), ctypes.cast(buf, ctypes.c_void_p), n)
+    return list(buf[:n])

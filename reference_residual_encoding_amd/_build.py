@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "librkv.so")
-SOURCES = ["rkv_kernels.hip", "rkv_api.cpp"]
+SOURCES = ["rkv_kernels.hip", "rkv_append.hip", "rkv_api.cpp"]
 
 FLAGS = [
     "--offload-arch=gfx950",

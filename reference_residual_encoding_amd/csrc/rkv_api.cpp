@@ -68,6 +68,7 @@ rkv_status check_params(const rkv_params* p) {
   if (p->d_ff % 32 != 0) return fail(RKV_ERR_UNSUPPORTED, "d_ff must be a multiple of 32 (got %d)", p->d_ff);
   if (p->d_ff > 65536) return fail(RKV_ERR_UNSUPPORTED, "d_ff must be at most 65536 (got %d)", p->d_ff);
   if ((long long)p->B * p->T >= (1LL << 31)) return fail(RKV_ERR_UNSUPPORTED, "B*T must be below 2^31");
+  if (p->T > (1 << 26)) return fail(RKV_ERR_UNSUPPORTED, "T must be at most 2^26 (got %d)", p->T);
   if ((long long)p->B * p->T * C >= (1LL << 40)) return fail(RKV_ERR_UNSUPPORTED, "B*T*C too large");
   if (!(p->ref_alpha >= 0.0 && p->ref_alpha <= 1.0e6))
     return fail(RKV_ERR_INVALID_ARG, "ref_alpha must be in [0, 1e6] (got %g)", p->ref_alpha);
@@ -75,7 +76,7 @@ rkv_status check_params(const rkv_params* p) {
   const long long nref =
       (long long)rkv::schedule_for(p->T, p->ref_stride, p->ref_alpha, p->n_sink).rpos.size();
   if ((long long)p->B * nref * 2 * p->d_ff * 4 >= (1LL << 31))
-    return fail(RKV_ERR_UNSUPPORTED, "B*ceil(T/s)*2*d_ff*4 (reference projections) must be below 2^31 bytes");
+    return fail(RKV_ERR_UNSUPPORTED, "B*nref*2*d_ff*4 (reference projections) must be below 2^31 bytes");
   return RKV_OK;
 }
 
@@ -324,6 +325,55 @@ rkv_status rkv_restore(const rkv_params* p, const uint8_t* codes, const uint16_t
                                 static_cast<char*>(workspace), L, stream),
             "restore");
   return ok();
+}
+
+size_t rkv_append_workspace_bytes(const rkv_params* p) {
+  if (check_params(p) != RKV_OK) return 0;
+  return rkv::plan_append(shape_of(p)).total;
+}
+
+rkv_status rkv_append(const rkv_params* p, void* kv, const void* kv_new, const int32_t* pos,
+                      const void* w1, const void* w2, const void* w3, int32_t* ref_idx,
+                      uint8_t* codes, uint16_t* scale, uint16_t* zmin, float* z, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  rkv_status st = check_params(p);
+  if (st != RKV_OK) return st;
+  RKV_NEED_PTR(kv);
+  RKV_NEED_PTR(kv_new);
+  RKV_NEED_PTR(pos);
+  RKV_NEED_PTR(w1);
+  RKV_NEED_PTR(w2);
+  RKV_NEED_PTR(w3);
+  RKV_NEED_PTR(ref_idx);
+  RKV_NEED_PTR(codes);
+  RKV_NEED_PTR(scale);
+  RKV_NEED_PTR(zmin);
+  RKV_NEED_PTR(workspace);
+  if (z != nullptr && !aligned16(z)) return fail(RKV_ERR_INVALID_ARG, "z is not 16-byte aligned");
+  const rkv::Shape sh = shape_of(p);
+  const rkv::AppendWorkspace L = rkv::plan_append(sh);
+  if (workspace_bytes < L.total)
+    return fail(RKV_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
+  hipError_t e;
+  RKV_STAGE(RKV_STAGE_APPEND,
+            rkv::launch_append(sh, kv, kv_new, pos, w1, w2, w3, ref_idx, codes, scale, zmin, z,
+                               static_cast<char*>(workspace), L, stream),
+            "append");
+  return ok();
+}
+
+int32_t rkv_reference_positions(const rkv_params* p, int32_t* rpos, int32_t cap) {
+  if (p == nullptr) { fail(RKV_ERR_INVALID_ARG, "params is NULL"); return -1; }
+  if (p->T <= 0 || p->T > (1 << 26)) { fail(RKV_ERR_INVALID_ARG, "T must be in [1, 2^26] (got %d)", p->T); return -1; }
+  if (p->ref_stride <= 0) { fail(RKV_ERR_INVALID_ARG, "ref_stride must be positive (got %d)", p->ref_stride); return -1; }
+  if (!(p->ref_alpha >= 0.0 && p->ref_alpha <= 1.0e6)) { fail(RKV_ERR_INVALID_ARG, "ref_alpha must be in [0, 1e6]"); return -1; }
+  if (p->n_sink < 0) { fail(RKV_ERR_INVALID_ARG, "n_sink must be non-negative (got %d)", p->n_sink); return -1; }
+  if (cap < 0 || (cap > 0 && rpos == nullptr)) { fail(RKV_ERR_INVALID_ARG, "rpos is NULL or cap negative"); return -1; }
+  const auto& sc = rkv::schedule_for(p->T, p->ref_stride, p->ref_alpha, p->n_sink);
+  const int32_t n = int32_t(sc.rpos.size());
+  for (int32_t i = 0; i < n && i < cap; ++i) rpos[i] = sc.rpos[size_t(i)];
+  ok();
+  return n;
 }
 
 }  // extern "C"

@@ -1,0 +1,473 @@
+// Decode-time append of the ResidualKV cache ([RKV] §2.7, decode step 4):
+// one new token per sequence is either stored as it is, when the schedule
+// of [RKV] §2.6 makes its position a reference, or encoded against the
+// references already in the cache ([RKV] §2.2-§2.4) and stored as a record.
+//
+// The work per call is a few vectors against the cache and the weights, so
+// every kernel here is a streaming kernel on the vector ALUs, in fp32 from
+// the stored values (no matrix cores: at one to a few dozen tokens the
+// products are bound by reading the weights and the references once):
+//   dist     one workgroup per 8 pool references of a sequence: squared L2
+//            by direct differences, the workgroup's best KL as a list
+//   select   per sequence: merge the lists by (distance, position), write
+//            ref_idx, form the mean of the chosen references in fp32; a
+//            reference token is copied into the cache with a zero record
+//   proj     one workgroup per 4 features: x W1, x W2, m W1, m W2 for every
+//            appended token over all C rows, reduced in LDS, then
+//            delta_h = Swish(x W1) (x W2) - Swish(m W1) (m W2) ([RKV] §2.3)
+//   w3       one workgroup per (token, 64 or 32 latent columns): z =
+//            delta_h W3 (W3 is linear, so f_c(kv) - f_c(m) = (h(kv) - h(m))
+//            W3), then the group quantiser of [RKV] §2.4 and the record
+#include "rkv_device.h"
+#include "rkv_internal.h"
+#include "rkv_quant.h"
+
+#include <cfloat>
+
+namespace rkv {
+
+namespace {
+
+constexpr int kAppCH = 8;          // pool references per distance workgroup (4 waves x 2)
+constexpr int kNoRef = 0x7fffffff;  // list padding (sorts after every reference)
+
+// Where the schedule puts its references: the closed form of a fixed
+// stride after the sinks, or the device copy of the host's positions.
+struct SchedView {
+  const int* rpos;  // nullptr: fixed stride
+  int nref, s0, n_sink;
+};
+
+__device__ __forceinline__ int ref_position(const SchedView& v, int j) {
+  if (v.rpos) return v.rpos[j];
+  return j < v.n_sink ? j : v.n_sink + (j - v.n_sink) * v.s0;
+}
+
+// Number of references before position t, and whether t is one.
+__device__ __forceinline__ int refs_before(const SchedView& v, int t, bool& is_ref) {
+  if (!v.rpos) {
+    const int u = t - v.n_sink;
+    is_ref = u < 0 || u % v.s0 == 0;
+    return u < 0 ? t : v.n_sink + (u + v.s0 - 1) / v.s0;
+  }
+  int lo = 0, hi = v.nref;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (v.rpos[mid] < t) lo = mid + 1; else hi = mid;
+  }
+  is_ref = lo < v.nref && v.rpos[lo] == t;
+  return lo;
+}
+
+template <typename E>
+__device__ __forceinline__ void load8(const E* p, float (&v)[8]) {
+  if constexpr (sizeof(E) == 2) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = __uint_as_float(w[e] << 16);
+      v[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+    }
+  } else {
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+template <typename E>
+__device__ __forceinline__ void load4(const E* p, float (&v)[4]) {
+  if constexpr (sizeof(E) == 2) {
+    const uint2 w = *reinterpret_cast<const uint2*>(p);
+    v[0] = __uint_as_float(w.x << 16);
+    v[1] = __uint_as_float(w.x & 0xFFFF0000u);
+    v[2] = __uint_as_float(w.y << 16);
+    v[3] = __uint_as_float(w.y & 0xFFFF0000u);
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  }
+}
+
+template <typename E>
+__device__ __forceinline__ float load1(const E* p) {
+  if constexpr (sizeof(E) == 2) return bf16_to_f32(*p);
+  else return *p;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+// State of sequence b's new token: -1 nothing to encode (invalid position
+// or a reference), else the size of its pool.
+__device__ __forceinline__ int pool_of(const SchedView& v, const int32_t* pos, int b, int T,
+                                       int& t) {
+  t = pos[b];
+  if (t < 0 || t >= T) return -1;
+  bool is_ref;
+  const int n = refs_before(v, t, is_ref);
+  return is_ref ? -1 : n;
+}
+
+// ---------------------------------------------------------------- distance
+// Workgroup (b, c): pool references j in [8c, 8c + 8) of sequence b, two
+// per wave with both rows' loads in flight; d = sum (x - y)^2 in fp32.
+template <typename E, int KL>
+__global__ __launch_bounds__(256) void k_app_dist(const E* __restrict__ kv,
+                                                  const E* __restrict__ kv_new,
+                                                  const int32_t* __restrict__ pos, SchedView sv,
+                                                  int T, int C, int n_lists,
+                                                  float2* __restrict__ part) {
+  const int b = blockIdx.x / n_lists, c = blockIdx.x % n_lists;
+  int t;
+  const int pool = pool_of(sv, pos, b, T, t);
+  const int j0 = c * kAppCH;
+  if (pool < 0 || j0 >= pool) return;
+  __shared__ float dl[kAppCH];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int ja = j0 + 2 * wave, jb = ja + 1;
+  const bool va = ja < pool, vb = jb < pool;
+  const E* x = kv_new + size_t(b) * C;
+  const E* ya = kv + (size_t(b) * T + ref_position(sv, va ? ja : j0)) * C;
+  const E* yb = kv + (size_t(b) * T + ref_position(sv, vb ? jb : j0)) * C;
+  float sa = 0.0f, sb = 0.0f;
+  for (int o = lane * 8; o < C; o += 512) {
+    float xv[8], av[8], bv[8];
+    load8(x + o, xv);
+    load8(ya + o, av);
+    load8(yb + o, bv);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float da = xv[e] - av[e], db = xv[e] - bv[e];
+      sa = fmaf(da, da, sa);
+      sb = fmaf(db, db, sb);
+    }
+  }
+  sa = wave_sum(sa);
+  sb = wave_sum(sb);
+  if (lane == 0) {
+    dl[2 * wave] = va ? sa : FLT_MAX;
+    dl[2 * wave + 1] = vb ? sb : FLT_MAX;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float bd[KL];
+    int bi[KL];
+#pragma unroll
+    for (int e = 0; e < KL; ++e) { bd[e] = FLT_MAX; bi[e] = kNoRef; }
+    for (int i = 0; i < kAppCH && j0 + i < pool; ++i) topk_push_lex(bd, bi, dl[i], j0 + i);
+    float2* dst = part + size_t(blockIdx.x) * KL;
+#pragma unroll
+    for (int e = 0; e < KL; ++e) dst[e] = make_float2(bd[e], __int_as_float(bi[e]));
+  }
+}
+
+// ---------------------------------------------------------------- select
+// Per sequence: store a reference token; else merge the distance lists,
+// write ref_idx (k_t positions ascending, -1 pads) and the fp32 mean of
+// the chosen rows.  act[b] = 1 when the token is to be encoded.
+template <typename E, int KL>
+__global__ __launch_bounds__(256) void k_app_select(
+    E* __restrict__ kv, const E* __restrict__ kv_new, const int32_t* __restrict__ pos,
+    SchedView sv, int T, int C, int k, int rec_bytes, int n_groups, int d_c, int n_lists,
+    const float2* __restrict__ part, int32_t* __restrict__ ref_idx, uint8_t* __restrict__ codes,
+    uint16_t* __restrict__ scale, uint16_t* __restrict__ zmin, float* __restrict__ z,
+    float* __restrict__ mean, int* __restrict__ act) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int t = pos[b];
+  if (t < 0 || t >= T) {                                 // not appended this call
+    if (tid == 0) act[b] = 0;
+    return;
+  }
+  const size_t row = size_t(b) * T + t;
+  bool is_ref;
+  const int pool = refs_before(sv, t, is_ref);
+  if (is_ref) {                                          // stored as it is ([RKV] §2.4)
+    for (int o = tid * 8; o < C; o += 256 * 8) {
+      if constexpr (sizeof(E) == 2)
+        *reinterpret_cast<u32x4*>(kv + row * C + o) =
+            *reinterpret_cast<const u32x4*>(kv_new + size_t(b) * C + o);
+      else {
+        reinterpret_cast<float4*>(kv + row * C + o)[0] =
+            reinterpret_cast<const float4*>(kv_new + size_t(b) * C + o)[0];
+        reinterpret_cast<float4*>(kv + row * C + o)[1] =
+            reinterpret_cast<const float4*>(kv_new + size_t(b) * C + o)[1];
+      }
+    }
+    for (int i = tid; i < k; i += 256) ref_idx[row * k + i] = -1;
+    for (int i = tid; i < rec_bytes; i += 256) codes[row * rec_bytes + i] = 0;
+    for (int i = tid; i < n_groups; i += 256) {
+      scale[row * n_groups + i] = 0;
+      zmin[row * n_groups + i] = 0;
+    }
+    if (z)
+      for (int i = tid; i < d_c; i += 256) z[row * d_c + i] = 0.0f;
+    if (tid == 0) act[b] = 0;
+    return;
+  }
+  const int nch = (pool + kAppCH - 1) / kAppCH;
+  float bd[KL];
+  int bi[KL];
+#pragma unroll
+  for (int e = 0; e < KL; ++e) { bd[e] = FLT_MAX; bi[e] = kNoRef; }
+  for (int l = tid; l < nch; l += 256) {
+    const float2* src = part + (size_t(b) * n_lists + l) * KL;
+#pragma unroll
+    for (int e = 0; e < KL; ++e) topk_push_lex(bd, bi, src[e].x, __float_as_int(src[e].y));
+  }
+  __shared__ float sd[256 * KL];
+  __shared__ int sj[256 * KL];
+  __shared__ int sel[KL];
+  for (int half = 128; half >= 1; half >>= 1) {        // tree merge, fixed order
+    if (tid >= half && tid < 2 * half)
+#pragma unroll
+      for (int e = 0; e < KL; ++e) { sd[tid * KL + e] = bd[e]; sj[tid * KL + e] = bi[e]; }
+    __syncthreads();
+    if (tid < half)
+#pragma unroll
+      for (int e = 0; e < KL; ++e)
+        topk_push_lex(bd, bi, sd[(tid + half) * KL + e], sj[(tid + half) * KL + e]);
+    __syncthreads();
+  }
+  const int kt = min(k, pool);                           // k_t = min(k, |pool|) ([RKV] §2.1)
+  if (tid == 0) {
+    int jj[KL];
+#pragma unroll
+    for (int e = 0; e < KL; ++e) jj[e] = e < kt ? bi[e] : kNoRef;
+    for (int a = 1; a < KL; ++a)                         // ascending position
+      for (int m = a; m > 0 && jj[m] < jj[m - 1]; --m) {
+        const int tmp = jj[m]; jj[m] = jj[m - 1]; jj[m - 1] = tmp;
+      }
+    for (int e = 0; e < k; ++e) {
+      const int p = e < kt ? ref_position(sv, jj[e]) : -1;
+      ref_idx[row * k + e] = p;
+      if (e < KL) sel[e] = p;
+    }
+    act[b] = 1;
+  }
+  __syncthreads();
+  const float inv = 1.0f / float(kt);
+  for (int o = tid * 8; o < C; o += 256 * 8) {
+    float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int i = 0; i < kt; ++i) {
+      float v[8];
+      load8(kv + (size_t(b) * T + sel[i]) * C + o, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m[e] += v[e];
+    }
+    float4* dst = reinterpret_cast<float4*>(mean + size_t(b) * C + o);
+    dst[0] = make_float4(m[0] * inv, m[1] * inv, m[2] * inv, m[3] * inv);
+    dst[1] = make_float4(m[4] * inv, m[5] * inv, m[6] * inv, m[7] * inv);
+  }
+}
+
+// ---------------------------------------------------------------- projection
+// Workgroup: features [4w, 4w + 4).  For RB tokens at a time each thread
+// accumulates x.W1, x.W2, m.W1, m.W2 over the rows c = tid + 256 i; the
+// 256 partial sums of each of the 64 values are reduced through LDS in a
+// fixed order, then delta_h is formed for the 4 features.
+template <typename E>
+__global__ __launch_bounds__(256) void k_app_proj(const E* __restrict__ kv_new,
+                                                  const float* __restrict__ mean,
+                                                  const int* __restrict__ act,
+                                                  const E* __restrict__ w1,
+                                                  const E* __restrict__ w2, int B, int C, int d_ff,
+                                                  float* __restrict__ dh) {
+  constexpr int RB = 4, NV = RB * 16;                    // [token][x|m][W1|W2][feature]
+  const int f0 = blockIdx.x * 4, tid = threadIdx.x;
+  __shared__ float red[NV * 257];
+  __shared__ float part4[4 * NV];
+  __shared__ float tot[NV];
+  for (int b0 = 0; b0 < B; b0 += RB) {
+    float acc[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) acc[v] = 0.0f;
+    bool live[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) live[r] = b0 + r < B && act[b0 + r] == 1;
+    for (int c = tid; c < C; c += 256) {
+      float a1[4], a2[4];
+      load4(w1 + size_t(c) * d_ff + f0, a1);
+      load4(w2 + size_t(c) * d_ff + f0, a2);
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        if (!live[r]) continue;
+        const float xv = load1(kv_new + size_t(b0 + r) * C + c);
+        const float mv = mean[size_t(b0 + r) * C + c];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          acc[r * 16 + 0 + f] = fmaf(xv, a1[f], acc[r * 16 + 0 + f]);
+          acc[r * 16 + 4 + f] = fmaf(xv, a2[f], acc[r * 16 + 4 + f]);
+          acc[r * 16 + 8 + f] = fmaf(mv, a1[f], acc[r * 16 + 8 + f]);
+          acc[r * 16 + 12 + f] = fmaf(mv, a2[f], acc[r * 16 + 12 + f]);
+        }
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < NV; ++v) red[v * 257 + tid] = acc[v];
+    __syncthreads();
+    {
+      const int v = tid % NV, q = tid / NV;              // 4 quarters of 64 threads
+      float s = 0.0f;
+      for (int i = 0; i < 64; ++i) s += red[v * 257 + q * 64 + i];
+      part4[q * NV + v] = s;
+    }
+    __syncthreads();
+    if (tid < NV)
+      tot[tid] = ((part4[tid] + part4[NV + tid]) + part4[2 * NV + tid]) + part4[3 * NV + tid];
+    __syncthreads();
+    if (tid < RB * 4) {
+      const int r = tid / 4, f = tid % 4;
+      if (live[r]) {
+        const float* u = tot + r * 16;
+        const float hk = silu(u[0 + f]) * u[4 + f];
+        const float hm = silu(u[8 + f]) * u[12 + f];
+        dh[size_t(b0 + r) * d_ff + f0 + f] = hk - hm;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- W3 + quantiser
+// Workgroup (token b, columns [CB*w, CB*w + CB)), CB = 64 or 32: thread
+// (rs, cg) sums delta_h[f] W3[f][8 cg .. 8 cg + 7] over f = rs + 32 i; the
+// 32 partial rows are reduced in LDS; the first CB/8 lanes then hold 8
+// consecutive latents each and run the group quantiser ([RKV] §2.4).
+template <typename E, int BITS, int G8>
+__global__ __launch_bounds__(256) void k_app_w3(const float* __restrict__ dh,
+                                                const int* __restrict__ act,
+                                                const int32_t* __restrict__ pos,
+                                                const E* __restrict__ w3, int T, int d_ff,
+                                                int d_c, int CB, uint8_t* __restrict__ codes,
+                                                uint16_t* __restrict__ scale,
+                                                uint16_t* __restrict__ zmin,
+                                                float* __restrict__ z) {
+  const int nblk = d_c / CB;
+  const int b = blockIdx.x / nblk, c0 = (blockIdx.x % nblk) * CB;
+  if (act[b] != 1) return;
+  const int tid = threadIdx.x, cg = tid % 8, rs = tid / 8;
+  __shared__ float red[32 * 65];
+  __shared__ float zl[64];
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (cg * 8 < CB) {
+    for (int f = rs; f < d_ff; f += 32) {
+      const float d = dh[size_t(b) * d_ff + f];
+      float w[8];
+      load8(w3 + size_t(f) * d_c + c0 + cg * 8, w);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(d, w[e], acc[e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[rs * 65 + cg * 8 + e] = acc[e];
+  __syncthreads();
+  if (tid < 64) {
+    float s = 0.0f;
+    for (int r = 0; r < 32; ++r) s += red[r * 65 + tid];
+    zl[tid] = s;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int lanes = CB / 8;
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = tid < lanes ? zl[tid * 8 + e] : 0.0f;
+    uint16_t dhb, mhb;
+    const uint32_t word = quant8<BITS, G8>(v, dhb, mhb);
+    if (tid < lanes) {
+      const size_t row = size_t(b) * T + pos[b];
+      const int64_t unit = int64_t(row) * (d_c / 8) + c0 / 8 + tid;
+      store_codes<BITS>(codes, unit, word);
+      if ((tid % G8) == 0) {
+        scale[unit / G8] = dhb;
+        zmin[unit / G8] = mhb;
+      }
+      if (z) {
+        float4* dst = reinterpret_cast<float4*>(z + unit * 8);
+        dst[0] = make_float4(v[0], v[1], v[2], v[3]);
+        dst[1] = make_float4(v[4], v[5], v[6], v[7]);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+AppendWorkspace plan_append(const Shape& sh) {
+  AppendWorkspace L{};
+  L.n_lists = cdiv(std::max(sh.nref, 1), kAppCH);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off += align256(bytes); return at; };
+  L.rpos = take(size_t(sh.nref) * 4);
+  L.part = take(size_t(sh.B) * L.n_lists * sh.kl * 8);
+  L.mean = take(size_t(sh.B) * sh.C * 4);
+  L.dh = take(size_t(sh.B) * sh.d_ff * 4);
+  L.act = take(size_t(sh.B) * 4);
+  L.total = off;
+  return L;
+}
+
+hipError_t launch_append(const Shape& sh, void* kv, const void* kv_new, const int32_t* pos,
+                         const void* w1, const void* w2, const void* w3, int32_t* ref_idx,
+                         uint8_t* codes, uint16_t* scale, uint16_t* zmin, float* z, char* ws,
+                         const AppendWorkspace& L, hipStream_t st) {
+  SchedView sv{nullptr, sh.nref, sh.s, sh.n_sink};
+  if (sh.alpha != 0.0) {
+    int* rpos = reinterpret_cast<int*>(ws + L.rpos);
+    const hipError_t e = launch_ref_positions(sh, rpos, st);
+    if (e != hipSuccess) return e;
+    sv.rpos = rpos;
+  }
+  auto* part = reinterpret_cast<float2*>(ws + L.part);
+  auto* mean = reinterpret_cast<float*>(ws + L.mean);
+  auto* dh = reinterpret_cast<float*>(ws + L.dh);
+  auto* act = reinterpret_cast<int*>(ws + L.act);
+  const int rec_bytes = sh.d_c * sh.b / 8, n_groups = sh.d_c / sh.g;
+  const int cb = sh.d_c % 64 == 0 ? 64 : 32;
+  const int n_dist = sh.B * L.n_lists;
+
+#define RKV_APP(E, KL)                                                                            \
+  k_app_dist<E, KL><<<n_dist, 256, 0, st>>>(static_cast<const E*>(kv),                           \
+                                            static_cast<const E*>(kv_new), pos, sv, sh.T, sh.C,   \
+                                            L.n_lists, part);                                     \
+  k_app_select<E, KL><<<sh.B, 256, 0, st>>>(static_cast<E*>(kv), static_cast<const E*>(kv_new),  \
+                                            pos, sv, sh.T, sh.C, sh.k, rec_bytes, n_groups,       \
+                                            sh.d_c, L.n_lists, part, ref_idx, codes, scale, zmin, \
+                                            z, mean, act);                                        \
+  k_app_proj<E><<<sh.d_ff / 4, 256, 0, st>>>(static_cast<const E*>(kv_new), mean, act,           \
+                                             static_cast<const E*>(w1), static_cast<const E*>(w2), \
+                                             sh.B, sh.C, sh.d_ff, dh)
+  if (sh.bf16) {
+    if (sh.kl == 4) { RKV_APP(uint16_t, 4); } else { RKV_APP(uint16_t, 8); }
+  } else {
+    if (sh.kl == 4) { RKV_APP(float, 4); } else { RKV_APP(float, 8); }
+  }
+#undef RKV_APP
+
+  const int n_w3 = sh.B * (sh.d_c / cb);
+#define RKV_W3(E, BITS, G8)                                                                        \
+  k_app_w3<E, BITS, G8><<<n_w3, 256, 0, st>>>(dh, act, pos, static_cast<const E*>(w3), sh.T,      \
+                                              sh.d_ff, sh.d_c, cb, codes, scale, zmin, z)
+#define RKV_W3G(E, BITS)                   \
+  switch (sh.g) {                          \
+    case 8: RKV_W3(E, BITS, 1); break;     \
+    case 16: RKV_W3(E, BITS, 2); break;    \
+    case 32: RKV_W3(E, BITS, 4); break;    \
+    default: RKV_W3(E, BITS, 8); break;    \
+  }
+  if (sh.bf16) {
+    if (sh.b == 4) { RKV_W3G(uint16_t, 4) } else { RKV_W3G(uint16_t, 2) }
+  } else {
+    if (sh.b == 4) { RKV_W3G(float, 4) } else { RKV_W3G(float, 2) }
+  }
+#undef RKV_W3G
+#undef RKV_W3
+  return hipGetLastError();
+}
+
+}  // namespace rkv

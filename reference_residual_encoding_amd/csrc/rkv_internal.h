@@ -9,6 +9,9 @@
 
 namespace rkv {
 
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+inline int cdiv(long a, long b) { return int((a + b - 1) / b); }
+
 // Reference schedule of one sequence ([RKV] §2.6), computed on the host.
 struct Schedule {
   int T = -1, s0 = 0, n_sink = 0;
@@ -24,7 +27,7 @@ struct Shape {
   int B, T, C, d_ff, d_c, k, g, b, s;
   bool bf16;
   int esize;     // bytes per kv / weight element
-  int nref;      // references per sequence, ceil(T/s)
+  int nref;      // references per sequence under the schedule
   int nr;        // non-references per sequence, T - nref
   int kl;        // neighbour-list length kept per chunk (4 or 8, >= k)
   int n_chunks;  // reference chunks (one partial top-k list each) per sequence
@@ -45,6 +48,9 @@ Shape make_shape(int B, int T, int N, int D, int d_ff, int d_c, int k, int g, in
 // positions, and per position t: ~j for the j-th reference, else the
 // non-reference index q.
 hipError_t launch_schedule(const Shape& sh, char* ws, const Workspace& L, hipStream_t st);
+// The reference positions alone, rpos[nref], copied from the host schedule
+// through kernel arguments (no host buffer).
+hipError_t launch_ref_positions(const Shape& sh, int* rpos, hipStream_t st);
 Workspace plan_workspace(const Shape& sh);
 
 // Each launcher enqueues on `st` and returns hipGetLastError().
@@ -82,5 +88,16 @@ hipError_t launch_restore(const Shape& sh, int N, int D, const uint8_t* codes,
                           const void* kv, const void* wd, const int32_t* idx, int n_idx,
                           float theta, void* out, bool out_bf16, char* ws,
                           const RestoreWorkspace& L, hipStream_t st);
+
+// Append ([RKV] §2.7 decode step 4): one new token per sequence.
+struct AppendWorkspace {
+  int n_lists;          // distance workgroups (partial lists) per sequence
+  size_t rpos, part, mean, dh, act, total;
+};
+AppendWorkspace plan_append(const Shape& sh);
+hipError_t launch_append(const Shape& sh, void* kv, const void* kv_new, const int32_t* pos,
+                         const void* w1, const void* w2, const void* w3, int32_t* ref_idx,
+                         uint8_t* codes, uint16_t* scale, uint16_t* zmin, float* z, char* ws,
+                         const AppendWorkspace& L, hipStream_t st);
 
 }  // namespace rkv

@@ -33,6 +33,7 @@
 #include "rkv_device.h"
 #include "rkv_gemm.h"
 #include "rkv_internal.h"
+#include "rkv_quant.h"
 
 #include <algorithm>
 #include <cmath>
@@ -74,8 +75,6 @@ template <> struct DistCfg<float> {
 constexpr int kSB = 128;
 constexpr int kEpiLd(int bn) { return bn + 8; }  // padded fp32 row of an LDS-staged tile
 
-inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-inline int cdiv(long a, long b) { return int((a + b - 1) / b); }
 
 // ------------------------------------------------------------------ packing
 // dst[map(c) * ld + r] = src[r * cols + c] for the weight matrices, one
@@ -234,76 +233,6 @@ __global__ __launch_bounds__(256) void k_ref_gather(const char* __restrict__ kv,
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if (lane == 0) ysq[wid] = acc;
-}
-
-// ------------------------------------------------------------------ quantiser
-// Lane-to-lane exchange inside groups of G8 lanes (8 latent values per lane).
-__device__ __forceinline__ float dpp_xor1(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float dpp_xor2(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float swz_xor4(float x) {
-  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x101F));
-}
-template <int G8>
-__device__ __forceinline__ void group_minmax(float& mn, float& mx) {
-  if constexpr (G8 >= 2) { mn = fminf(mn, dpp_xor1(mn)); mx = fmaxf(mx, dpp_xor1(mx)); }
-  if constexpr (G8 >= 4) { mn = fminf(mn, dpp_xor2(mn)); mx = fmaxf(mx, dpp_xor2(mx)); }
-  if constexpr (G8 >= 8) { mn = fminf(mn, swz_xor4(mn)); mx = fmaxf(mx, swz_xor4(mx)); }
-}
-
-// rint(x / d) exactly as the correctly rounded fp32 division would give it,
-// for quotients below 2^4 in magnitude plus the few steps an fp16-rounded
-// step or minimum can add.  x * rcp(d) (rcp within 1 ulp) lies within
-// 2 ulp(16) < 4e-6 of the rounded quotient, so the two round alike unless
-// the product is within 1e-5 of a half-integer; only then, and only where a
-// lane of the wave needs it, is the division itself done.
-__device__ __forceinline__ float rint_div(float x, float d, float rd) {
-  const float y = x * rd;
-  const bool near_half = fabsf(y - floorf(y) - 0.5f) < 1e-5f;
-  float r = rintf(y);
-  if (__any(near_half)) r = near_half ? rintf(x / d) : r;
-  return r;
-}
-
-// Quantise the 8 consecutive latent values a lane owns ([RKV] §2.4); the
-// G8 lanes of a group must all call it together.  Returns the packed codes;
-// Delta_h and m_h as fp16 bits.  Integer decisions are those of fp32
-// arithmetic: Delta = (max - min) / (2^b - 1), q = clamp(rint((z - m_h) /
-// Delta_h)), q = 0 when Delta_h == 0 (a constant group keeps m_h, no
-// division).
-template <int BITS, int G8>
-__device__ __forceinline__ uint32_t quant8(const float (&v)[8], uint16_t& dh_bits,
-                                           uint16_t& mh_bits) {
-  constexpr float kLevels = float((1 << BITS) - 1);
-  float mn = v[0], mx = v[0];
-#pragma unroll
-  for (int e = 1; e < 8; ++e) { mn = fminf(mn, v[e]); mx = fmaxf(mx, v[e]); }
-  group_minmax<G8>(mn, mx);
-  const float delta = (mx - mn) / kLevels;
-  dh_bits = f32_to_f16_bits(delta);
-  mh_bits = f32_to_f16_bits(mn);
-  const float dh = f16_bits_to_f32(dh_bits), mh = f16_bits_to_f32(mh_bits);
-  uint32_t word = 0;
-  if (dh != 0.0f) {
-    const float rd = __builtin_amdgcn_rcpf(dh);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float t = rint_div(v[e] - mh, dh, rd);
-      word |= uint32_t(fminf(fmaxf(t, 0.0f), kLevels)) << (BITS * e);
-    }
-  }
-  return word;
-}
-
-template <int BITS>
-__device__ __forceinline__ void store_codes(uint8_t* codes, int64_t unit, uint32_t word) {
-  if constexpr (BITS == 4)
-    *reinterpret_cast<uint32_t*>(codes + unit * 4) = word;
-  else
-    *reinterpret_cast<uint16_t*>(codes + unit * 2) = uint16_t(word);
 }
 
 // ------------------------------------------------------------------ retrieval
@@ -1128,6 +1057,17 @@ hipError_t launch_pack_weights(const Shape& sh, const void* w1, const void* w2, 
   return hipGetLastError();
 }
 
+hipError_t launch_ref_positions(const Shape& sh, int* rpos, hipStream_t st) {
+  for (int first = 0; first < sh.nref; first += kPosChunk) {
+    PosChunk c;
+    c.first = first;
+    c.count = std::min(kPosChunk, sh.nref - first);
+    for (int i = 0; i < c.count; ++i) c.pos[i] = sh.sched->rpos[size_t(first) + i];
+    k_sched_chunk<<<1, 256, 0, st>>>(rpos, c);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_schedule(const Shape& sh, char* ws, const Workspace& L, hipStream_t st) {
   auto* rpos = reinterpret_cast<int*>(ws + L.rpos);
   auto* tab = reinterpret_cast<int*>(ws + L.tab);
@@ -1136,13 +1076,8 @@ hipError_t launch_schedule(const Shape& sh, char* ws, const Workspace& L, hipStr
     k_sched_fixed<<<cdiv(sh.T, 256), 256, 0, st>>>(rpos, sh.nref, sh.T, sh.s, sh.n_sink, tab, nrp);
     return hipGetLastError();
   }
-  for (int first = 0; first < sh.nref; first += kPosChunk) {
-    PosChunk c;
-    c.first = first;
-    c.count = std::min(kPosChunk, sh.nref - first);
-    for (int i = 0; i < c.count; ++i) c.pos[i] = sh.sched->rpos[size_t(first) + i];
-    k_sched_chunk<<<1, 256, 0, st>>>(rpos, c);
-  }
+  const hipError_t e = launch_ref_positions(sh, rpos, st);
+  if (e != hipSuccess) return e;
   k_sched_tables<<<cdiv(sh.T, 256), 256, 0, st>>>(rpos, sh.nref, sh.T, tab, nrp);
   return hipGetLastError();
 }

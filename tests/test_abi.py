@@ -179,3 +179,47 @@ def test_dynamic_schedule_shrinks_the_workspace():
     reference rows and projections."""
     from synth.configs import LLAMA32K_DYN
     assert 0 < R.rkv_encode_workspace_bytes(_p(LLAMA32K_DYN)) < R.rkv_encode_workspace_bytes(_p(LLAMA32K))
+
+
+def _append(p, ws_bytes=1 << 40, **ptrs):
+    args = dict(kv=FAKE, kv_new=FAKE, pos=FAKE, w1=FAKE, w2=FAKE, w3=FAKE, ref_idx=FAKE,
+                codes=FAKE, scale=FAKE, zmin=FAKE, z=None, workspace=FAKE)
+    args.update(ptrs)
+    valid_ptrs = all(v is not None and v % 16 == 0 for k, v in args.items() if k != "z") \
+        and (args["z"] is None or args["z"] % 16 == 0)
+    need = R.rkv_append_workspace_bytes(p)
+    if need and valid_ptrs and ws_bytes >= need:
+        pytest.fail("test would pass validation with fake pointers")
+    return R.rkv_append(p, args["kv"], args["kv_new"], args["pos"], args["w1"], args["w2"],
+                        args["w3"], args["ref_idx"], args["codes"], args["scale"], args["zmin"],
+                        args["z"], args["workspace"], ws_bytes, None, check=False)
+
+
+@pytest.mark.parametrize("name", ["kv", "kv_new", "pos", "w1", "w2", "w3", "ref_idx", "codes",
+                                  "scale", "zmin", "workspace"])
+def test_append_rejects_null_and_misaligned(name):
+    p = _p(LLAMA32K)
+    assert _append(p, **{name: None}) == R.RKV_ERR_INVALID_ARG
+    assert _append(p, **{name: FAKE_MIS}) == R.RKV_ERR_INVALID_ARG
+
+
+def test_append_validation_and_workspace():
+    p = _p(LLAMA32K)
+    need = R.rkv_append_workspace_bytes(p)
+    # a few vectors per sequence and one partial list per 8 pool references
+    assert 0 < need < 1 << 20
+    assert R.rkv_append_workspace_bytes(_p(LLAMA32K, B=16)) > need
+    assert _append(p, ws_bytes=need - 1) == R.RKV_ERR_WORKSPACE
+    assert _append(_p(LLAMA32K, k=9)) == R.RKV_ERR_UNSUPPORTED
+    assert _append(_p(LLAMA32K, ref_alpha=-1.0)) == R.RKV_ERR_INVALID_ARG
+    assert _append(p, z=FAKE_MIS) == R.RKV_ERR_INVALID_ARG
+
+
+def test_reference_positions_host_query():
+    """The schedule of [RKV] §2.6 as host data, with no device work."""
+    assert R.rkv_reference_positions(_p(LLAMA32K, T=100)) == list(range(0, 100, 16))
+    got = R.rkv_reference_positions(_p(LLAMA32K, T=80, ref_stride=10, ref_alpha=0.1, n_sink=3))
+    # sinks 0..2, then p0 = 3, gaps 10 + floor(0.1 (p - 3))
+    assert got == [0, 1, 2, 3, 13, 24, 36, 49, 63, 79]
+    with pytest.raises(R.RkvError):
+        R.rkv_reference_positions(_p(LLAMA32K, ref_stride=0))

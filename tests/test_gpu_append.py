@@ -1,0 +1,157 @@
+"""GPU parity of the decode-time append (rkv_append, [RKV] §2.7 decode step 4),
+through the C ABI, against the fp64 oracle's encoding of the same positions
+(the oracle's append_token is pinned to reproduce it token by token).
+
+The cache's kv rows that are not references hold NaN, so a kernel that read
+one would poison the result; records start as a byte pattern that rkv_append
+must overwrite on appended rows and leave alone elsewhere.  The records are
+compared with the same bars as the encode (rkv_parity).  Needs an MI355X."""
+import numpy as np
+import pytest
+import torch
+
+import reference_residual_encoding_amd as R
+from synth import generate
+from synth.configs import LLAMA8K, LLAMA8K_DYN, TINY, TINY_DYN
+
+import rkv_parity as P
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 0xA5
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+class Cache:
+    """Device cache of one configuration: kv rows + records, in the
+    layouts of include/rkv.h.  Non-reference kv rows hold NaN, and so do
+    the reference rows unless prefill_refs."""
+
+    def __init__(self, w, prefill_refs: bool, device="cuda"):
+        cfg = self.cfg = w.cfg
+        self.w = w
+        self.p = P.params_of(cfg)
+        n = cfg.B * cfg.T
+        self.ref_mask = P.ref_mask_of(cfg)
+        kv = np.array(w.kv, copy=True)
+        nan = np.uint16(0x7FC0) if cfg.dtype == "bf16" else np.float32(np.nan)
+        kv[:, ~self.ref_mask] = nan
+        if not prefill_refs:
+            kv[:, self.ref_mask] = nan
+        self.expected_kv = kv                     # host copy of what the cache must hold
+        self.kv = P.to_device(kv, cfg.dtype, device)
+        self.w1, self.w2, self.w3 = (P.to_device(x, cfg.dtype, device) for x in (w.w1, w.w2, w.w3))
+        u8 = lambda nbytes: torch.full((nbytes,), SENTINEL, dtype=torch.uint8, device=device)
+        self.ref_idx = u8(n * cfg.k * 4).view(torch.int32).view(cfg.B, cfg.T, cfg.k)
+        self.codes = u8(n * cfg.d_c * cfg.b // 8).view(cfg.B, cfg.T, -1)
+        self.scale = u8(n * (cfg.d_c // cfg.g) * 2).view(torch.float16).view(cfg.B, cfg.T, -1)
+        self.zmin = u8(n * (cfg.d_c // cfg.g) * 2).view(torch.float16).view(cfg.B, cfg.T, -1)
+        self.z = u8(n * cfg.d_c * 4).view(torch.float32).view(cfg.B, cfg.T, cfg.d_c)
+        self.ws_bytes = R.rkv_append_workspace_bytes(self.p)
+        assert self.ws_bytes > 0
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        self.appended = np.zeros((cfg.B, cfg.T), bool)
+
+    def append(self, pos):
+        cfg = self.cfg
+        pos = np.asarray(pos, dtype=np.int64)
+        assert pos.shape == (cfg.B,)
+        rows = np.zeros((cfg.B, cfg.C), dtype=self.w.kv.dtype)
+        for b, t in enumerate(pos):
+            if 0 <= t < cfg.T:
+                rows[b] = self.w.kv[b, t]
+                self.appended[b, t] = True
+                if self.ref_mask[t]:
+                    self.expected_kv[b, t] = self.w.kv[b, t]
+        kv_new = P.to_device(rows, cfg.dtype)
+        d_pos = torch.from_numpy(pos.astype(np.int32)).cuda()
+        R.rkv_append(self.p, self.kv, kv_new, d_pos, self.w1, self.w2, self.w3, self.ref_idx,
+                     self.codes, self.scale, self.zmin, self.z, self.ws, self.ws_bytes,
+                     torch.cuda.current_stream())
+
+    def check(self, name):
+        """Parity of every appended row; untouched records keep the pattern;
+        the cache holds exactly the appended (and prefilled) references."""
+        cfg = self.cfg
+        torch.cuda.synchronize()
+        h = dict(ref_idx=self.ref_idx.cpu().numpy(), codes=self.codes.cpu().numpy(),
+                 scale=self.scale.cpu().numpy(), zmin=self.zmin.cpu().numpy(),
+                 z=self.z.cpu().numpy())
+        pos = {b: np.flatnonzero(self.appended[b]) for b in range(cfg.B)}
+        summary = P.compare_tokens(self.w, h, {b: v for b, v in pos.items() if v.size}, log=_log)
+        untouched = ~self.appended
+        assert (h["codes"][untouched] == SENTINEL).all(), f"{name}: a record outside the appended rows changed"
+        assert (h["ref_idx"].view(np.uint8).reshape(cfg.B, cfg.T, -1)[untouched] == SENTINEL).all()
+        assert (h["scale"].view(np.uint8).reshape(cfg.B, cfg.T, -1)[untouched] == SENTINEL).all()
+        kv = self.kv.cpu()
+        kv = kv.view(torch.int16).numpy().view(np.uint16) if cfg.dtype == "bf16" else kv.numpy()
+        assert np.array_equal(kv.view(np.uint8), self.expected_kv.view(np.uint8)), \
+            f"{name}: the cache's kv rows differ from the appended references"
+        return summary
+
+
+def _make(cfg, prefill):
+    return Cache(generate(cfg), prefill)
+
+
+@pytest.mark.parametrize("cfg", [TINY, TINY_DYN], ids=lambda c: c.name)
+def test_append_every_position_in_order(cfg):
+    """An empty cache (all NaN) filled token by token reaches the same records
+    as the oracle's encode of the prefix; reference rows land in the cache."""
+    _log(f"[case] append {cfg.name} in order")
+    c = _make(cfg, prefill=False)
+    for t in range(cfg.T):
+        c.append(np.full(cfg.B, t))
+    c.check(cfg.name)
+
+
+RAGGED_BF16 = LLAMA8K.with_(name="append_ragged_bf16_b2_k5", B=3, T=1000, N=2, D=32, d_ff=96,
+                            d_c=64, k=5, g=16, b=2, stride=7, n_protos=24)
+RAGGED_F32 = LLAMA8K.with_(name="append_ragged_f32_k8_g64", B=2, T=700, N=1, D=64, d_ff=64,
+                           d_c=128, k=8, g=64, b=4, stride=3, dtype="f32", n_protos=12, noise=0.3)
+
+
+@pytest.mark.parametrize("cfg", [RAGGED_BF16, RAGGED_F32], ids=lambda c: c.name)
+def test_append_independent_positions_per_sequence(cfg):
+    """Continuous batching: every call appends a different position in each
+    sequence, in random order, with some sequences skipped (pos -1 or T)."""
+    _log(f"[case] append {cfg.name} random positions")
+    c = _make(cfg, prefill=True)
+    rng = np.random.default_rng(17)
+    perms = [rng.permutation(cfg.T) for _ in range(cfg.B)]
+    for i in range(60):
+        pos = np.array([perms[b][i] for b in range(cfg.B)])
+        if i % 7 == 3:
+            pos[i % cfg.B] = -1
+        if i % 11 == 5:
+            pos[(i + 1) % cfg.B] = cfg.T
+        c.append(pos)
+    c.check(cfg.name)
+
+
+@pytest.mark.parametrize("cfg", [LLAMA8K.with_(B=2), LLAMA8K_DYN], ids=lambda c: c.name)
+def test_append_full_size_sampled(cfg):
+    """The Llama layer shape at 8k context: sampled positions (warm-up, tail,
+    random), one per sequence per call."""
+    _log(f"[case] append {cfg.name} sampled")
+    c = _make(cfg, prefill=True)
+    pos = [P.sample_positions(cfg.T, cfg.stride, 150, seed=40 + b, cfg=cfg) for b in range(cfg.B)]
+    n = min(len(p) for p in pos)
+    for i in range(n):
+        c.append(np.array([pos[b][i] for b in range(cfg.B)]))
+    c.check(cfg.name)
+
+
+def test_append_bench_shape():
+    """The benchmark's append launch: 16 sequences at the end of a 32k
+    context (pool of 2,048 references each), compared with the oracle."""
+    from synth.configs import LLAMA32K
+    cfg = LLAMA32K.with_(B=16, gather_frac=None)
+    _log("[case] append bench shape B=16 T=32k")
+    c = _make(cfg, prefill=True)
+    pos = np.array([cfg.T - 1 - 3 * b for b in range(cfg.B)])
+    c.append(pos)
+    c.check("bench shape")
