@@ -15,7 +15,7 @@
 //   proj     one workgroup per 4 features: x W1, x W2, m W1, m W2 for every
 //            appended token over all C rows, reduced in LDS, then
 //            delta_h = Swish(x W1) (x W2) - Swish(m W1) (m W2) ([RKV] §2.3)
-//   w3       one workgroup per (token, 64 or 32 latent columns): z =
+//   w3       one workgroup per (token, 32 or 64 latent columns): z =
 //            delta_h W3 (W3 is linear, so f_c(kv) - f_c(m) = (h(kv) - h(m))
 //            W3), then the group quantiser of [RKV] §2.4 and the record
 #include "rkv_device.h"
@@ -135,6 +135,7 @@ __global__ __launch_bounds__(256) void k_app_dist(const E* __restrict__ kv,
   const E* ya = kv + (size_t(b) * T + ref_position(sv, va ? ja : j0)) * C;
   const E* yb = kv + (size_t(b) * T + ref_position(sv, vb ? jb : j0)) * C;
   float sa = 0.0f, sb = 0.0f;
+#pragma unroll 4
   for (int o = lane * 8; o < C; o += 512) {
     float xv[8], av[8], bv[8];
     load8(x + o, xv);
@@ -252,13 +253,16 @@ __global__ __launch_bounds__(256) void k_app_select(
   __syncthreads();
   const float inv = 1.0f / float(kt);
   for (int o = tid * 8; o < C; o += 256 * 8) {
-    float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int i = 0; i < kt; ++i) {
-      float v[8];
-      load8(kv + (size_t(b) * T + sel[i]) * C + o, v);
+    float v[KL][8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) m[e] += v[e];
-    }
+    for (int i = 0; i < KL; ++i)                         // every row's loads in flight together
+      load8(kv + (size_t(b) * T + sel[min(i, kt - 1)]) * C + o, v[i]);
+    float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < KL; ++i)
+      if (i < kt)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m[e] += v[i][e];
     float4* dst = reinterpret_cast<float4*>(mean + size_t(b) * C + o);
     dst[0] = make_float4(m[0] * inv, m[1] * inv, m[2] * inv, m[3] * inv);
     dst[1] = make_float4(m[4] * inv, m[5] * inv, m[6] * inv, m[7] * inv);
@@ -266,10 +270,13 @@ __global__ __launch_bounds__(256) void k_app_select(
 }
 
 // ---------------------------------------------------------------- projection
-// Workgroup: features [4w, 4w + 4).  For RB tokens at a time each thread
-// accumulates x.W1, x.W2, m.W1, m.W2 over the rows c = tid + 256 i; the
-// 256 partial sums of each of the 64 values are reduced through LDS in a
-// fixed order, then delta_h is formed for the 4 features.
+// Workgroup: features [4w, 4w + 4).  Thread tid owns the rows c = c0 + tid +
+// 256 i (i < 8) of W1 and W2 in registers (loaded once when C <= 2048),
+// and for RB tokens at a time accumulates x.W1, x.W2, m.W1, m.W2 over its
+// rows; the 256 partial sums of each of the 64 values are reduced through
+// LDS in a fixed order, then delta_h is formed for the 4 features.  All of
+// a thread's loads of one step are issued together (the path is bound by
+// memory latency at a few tokens).
 template <typename E>
 __global__ __launch_bounds__(256) void k_app_proj(const E* __restrict__ kv_new,
                                                   const float* __restrict__ mean,
@@ -277,11 +284,22 @@ __global__ __launch_bounds__(256) void k_app_proj(const E* __restrict__ kv_new,
                                                   const E* __restrict__ w1,
                                                   const E* __restrict__ w2, int B, int C, int d_ff,
                                                   float* __restrict__ dh) {
-  constexpr int RB = 4, NV = RB * 16;                    // [token][x|m][W1|W2][feature]
+  constexpr int RB = 4, NV = RB * 16, RPT = 8;           // [token][x|m][W1|W2][feature]
   const int f0 = blockIdx.x * 4, tid = threadIdx.x;
   __shared__ float red[NV * 257];
   __shared__ float part4[4 * NV];
   __shared__ float tot[NV];
+  float a1[RPT][4], a2[RPT][4];
+  auto load_w = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int c = min(c0 + tid + 256 * i, C - 1);
+      load4(w1 + size_t(c) * d_ff + f0, a1[i]);
+      load4(w2 + size_t(c) * d_ff + f0, a2[i]);
+    }
+  };
+  const bool one_chunk = C <= 256 * RPT;
+  if (one_chunk) load_w(0);
   for (int b0 = 0; b0 < B; b0 += RB) {
     float acc[NV];
 #pragma unroll
@@ -289,22 +307,30 @@ __global__ __launch_bounds__(256) void k_app_proj(const E* __restrict__ kv_new,
     bool live[RB];
 #pragma unroll
     for (int r = 0; r < RB; ++r) live[r] = b0 + r < B && act[b0 + r] == 1;
-    for (int c = tid; c < C; c += 256) {
-      float a1[4], a2[4];
-      load4(w1 + size_t(c) * d_ff + f0, a1);
-      load4(w2 + size_t(c) * d_ff + f0, a2);
+    for (int c0 = 0; c0 < C; c0 += 256 * RPT) {
+      if (!one_chunk) load_w(c0);
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
         if (!live[r]) continue;
-        const float xv = load1(kv_new + size_t(b0 + r) * C + c);
-        const float mv = mean[size_t(b0 + r) * C + c];
+        float xv[RPT], mv[RPT];
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
-          acc[r * 16 + 0 + f] = fmaf(xv, a1[f], acc[r * 16 + 0 + f]);
-          acc[r * 16 + 4 + f] = fmaf(xv, a2[f], acc[r * 16 + 4 + f]);
-          acc[r * 16 + 8 + f] = fmaf(mv, a1[f], acc[r * 16 + 8 + f]);
-          acc[r * 16 + 12 + f] = fmaf(mv, a2[f], acc[r * 16 + 12 + f]);
+        for (int i = 0; i < RPT; ++i) {
+          const int c = c0 + tid + 256 * i;
+          const int cc = min(c, C - 1);
+          const float x = load1(kv_new + size_t(b0 + r) * C + cc);
+          const float m = mean[size_t(b0 + r) * C + cc];
+          xv[i] = c < C ? x : 0.0f;
+          mv[i] = c < C ? m : 0.0f;
         }
+#pragma unroll
+        for (int i = 0; i < RPT; ++i)
+#pragma unroll
+          for (int f = 0; f < 4; ++f) {
+            acc[r * 16 + 0 + f] = fmaf(xv[i], a1[i][f], acc[r * 16 + 0 + f]);
+            acc[r * 16 + 4 + f] = fmaf(xv[i], a2[i][f], acc[r * 16 + 4 + f]);
+            acc[r * 16 + 8 + f] = fmaf(mv[i], a1[i][f], acc[r * 16 + 8 + f]);
+            acc[r * 16 + 12 + f] = fmaf(mv[i], a2[i][f], acc[r * 16 + 12 + f]);
+          }
       }
     }
 #pragma unroll
@@ -334,58 +360,66 @@ __global__ __launch_bounds__(256) void k_app_proj(const E* __restrict__ kv_new,
 }
 
 // ---------------------------------------------------------------- W3 + quantiser
-// Workgroup (token b, columns [CB*w, CB*w + CB)), CB = 64 or 32: thread
-// (rs, cg) sums delta_h[f] W3[f][8 cg .. 8 cg + 7] over f = rs + 32 i; the
-// 32 partial rows are reduced in LDS; the first CB/8 lanes then hold 8
-// consecutive latents each and run the group quantiser ([RKV] §2.4).
-template <typename E, int BITS, int G8>
+// Workgroup (token b, columns [CB*w, CB*w + CB)), CB = 32 (g <= 32) or 64:
+// LPR = CB/8 lanes cover a row of the block, 8 columns each; the 256/LPR
+// row groups sum delta_h[f] W3[f][.] over f = rg + (256/LPR) i, 16 rows'
+// loads in flight at a time; the partial rows are reduced in LDS; the first
+// LPR lanes then hold 8 consecutive latents each and run the group
+// quantiser ([RKV] §2.4).
+template <typename E, int BITS, int G8, int CB>
 __global__ __launch_bounds__(256) void k_app_w3(const float* __restrict__ dh,
                                                 const int* __restrict__ act,
                                                 const int32_t* __restrict__ pos,
                                                 const E* __restrict__ w3, int T, int d_ff,
-                                                int d_c, int CB, uint8_t* __restrict__ codes,
+                                                int d_c, uint8_t* __restrict__ codes,
                                                 uint16_t* __restrict__ scale,
                                                 uint16_t* __restrict__ zmin,
                                                 float* __restrict__ z) {
+  constexpr int LPR = CB / 8, RG = 256 / LPR, UN = 16;
   const int nblk = d_c / CB;
   const int b = blockIdx.x / nblk, c0 = (blockIdx.x % nblk) * CB;
   if (act[b] != 1) return;
-  const int tid = threadIdx.x, cg = tid % 8, rs = tid / 8;
-  __shared__ float red[32 * 65];
-  __shared__ float zl[64];
+  const int tid = threadIdx.x, cg = tid % LPR, rg = tid / LPR;
+  __shared__ float red[RG * (CB + 1)];
+  __shared__ float zl[CB];
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (cg * 8 < CB) {
-    for (int f = rs; f < d_ff; f += 32) {
-      const float d = dh[size_t(b) * d_ff + f];
-      float w[8];
-      load8(w3 + size_t(f) * d_c + c0 + cg * 8, w);
+  const float* dhb = dh + size_t(b) * d_ff;
+  const E* wcol = w3 + c0 + cg * 8;
+  for (int f1 = rg; f1 < d_ff; f1 += RG * UN) {
+    float d[UN], w[UN][8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = fmaf(d, w[e], acc[e]);
+    for (int u = 0; u < UN; ++u) {
+      const int f = min(f1 + RG * u, d_ff - 1);
+      d[u] = f1 + RG * u < d_ff ? dhb[f] : 0.0f;
+      load8(wcol + size_t(f) * d_c, w[u]);
     }
+#pragma unroll
+    for (int u = 0; u < UN; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(d[u], w[u][e], acc[e]);
   }
 #pragma unroll
-  for (int e = 0; e < 8; ++e) red[rs * 65 + cg * 8 + e] = acc[e];
+  for (int e = 0; e < 8; ++e) red[rg * (CB + 1) + cg * 8 + e] = acc[e];
   __syncthreads();
-  if (tid < 64) {
+  if (tid < CB) {
     float s = 0.0f;
-    for (int r = 0; r < 32; ++r) s += red[r * 65 + tid];
+    for (int r = 0; r < RG; ++r) s += red[r * (CB + 1) + tid];
     zl[tid] = s;
   }
   __syncthreads();
   if (tid < 64) {
-    const int lanes = CB / 8;
     float v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = tid < lanes ? zl[tid * 8 + e] : 0.0f;
-    uint16_t dhb, mhb;
-    const uint32_t word = quant8<BITS, G8>(v, dhb, mhb);
-    if (tid < lanes) {
+    for (int e = 0; e < 8; ++e) v[e] = tid < LPR ? zl[min(tid, LPR - 1) * 8 + e] : 0.0f;
+    uint16_t dhq, mhq;
+    const uint32_t word = quant8<BITS, G8>(v, dhq, mhq);
+    if (tid < LPR) {
       const size_t row = size_t(b) * T + pos[b];
       const int64_t unit = int64_t(row) * (d_c / 8) + c0 / 8 + tid;
       store_codes<BITS>(codes, unit, word);
       if ((tid % G8) == 0) {
-        scale[unit / G8] = dhb;
-        zmin[unit / G8] = mhb;
+        scale[unit / G8] = dhq;
+        zmin[unit / G8] = mhq;
       }
       if (z) {
         float4* dst = reinterpret_cast<float4*>(z + unit * 8);
@@ -428,7 +462,7 @@ hipError_t launch_append(const Shape& sh, void* kv, const void* kv_new, const in
   auto* dh = reinterpret_cast<float*>(ws + L.dh);
   auto* act = reinterpret_cast<int*>(ws + L.act);
   const int rec_bytes = sh.d_c * sh.b / 8, n_groups = sh.d_c / sh.g;
-  const int cb = sh.d_c % 64 == 0 ? 64 : 32;
+  const int cb = sh.g <= 32 ? 32 : 64;                  // a block holds whole groups
   const int n_dist = sh.B * L.n_lists;
 
 #define RKV_APP(E, KL)                                                                            \
@@ -451,8 +485,12 @@ hipError_t launch_append(const Shape& sh, void* kv, const void* kv_new, const in
 
   const int n_w3 = sh.B * (sh.d_c / cb);
 #define RKV_W3(E, BITS, G8)                                                                        \
-  k_app_w3<E, BITS, G8><<<n_w3, 256, 0, st>>>(dh, act, pos, static_cast<const E*>(w3), sh.T,      \
-                                              sh.d_ff, sh.d_c, cb, codes, scale, zmin, z)
+  if (cb == 32)                                                                                    \
+    k_app_w3<E, BITS, G8, 32><<<n_w3, 256, 0, st>>>(dh, act, pos, static_cast<const E*>(w3),      \
+                                                    sh.T, sh.d_ff, sh.d_c, codes, scale, zmin, z); \
+  else                                                                                             \
+    k_app_w3<E, BITS, G8, 64><<<n_w3, 256, 0, st>>>(dh, act, pos, static_cast<const E*>(w3),      \
+                                                    sh.T, sh.d_ff, sh.d_c, codes, scale, zmin, z)
 #define RKV_W3G(E, BITS)                   \
   switch (sh.g) {                          \
     case 8: RKV_W3(E, BITS, 1); break;     \
