@@ -51,7 +51,10 @@ the design notes of the repository):
   * codes are packed little-endian inside a byte: coordinate r of a byte
     holds bits [r*b, (r+1)*b);
   * dequantised values are q * Delta_h + m_h, exact in float64, then rounded
-    once to float32.
+    once to float32;
+  * with quantisation off (b = 16), Q is the identity ([RKV] §2.4): each
+    latent is stored as fp16, rounded to nearest even from its float32
+    value, and the record holds no group numbers.
 
 Restore (read side, [RKV] §2.5 and the implementation note of §2.1):
 
@@ -82,6 +85,7 @@ import numpy as np
 
 F64 = np.float64
 F32 = np.float32
+IDENTITY_BITS = 16      # b = 16: quantisation off, the latent stored as fp16
 
 
 # ---------------------------------------------------------------- schedule
@@ -178,12 +182,20 @@ def quantize(z: np.ndarray, g: int, b: int):
 
     z: [n, d_c] latents.  Returns q [n, d_c] (int64 codes), Delta_h and m_h
     [n, n_groups] as float16.  Integer decisions are taken in float32 (see
-    the module docstring).
+    the module docstring).  b = 16 is the identity mode: q holds the fp16
+    bits of each latent.
     """
     z32 = np.asarray(z, F64).astype(F32)
     n, d_c = z32.shape
-    levels = F32(2 ** b - 1)
     bounds = group_bounds(d_c, g)
+    if b == IDENTITY_BITS:
+        # quantisation off: Q is the identity map ([RKV] §2.4); the latent is
+        # stored as fp16 (round to nearest even from its float32 value) and
+        # the record holds no group numbers (zeros here)
+        q = z32.astype(np.float16).view(np.uint16).astype(np.int64)
+        zeros = np.zeros((n, len(bounds)), dtype=np.float16)
+        return q, zeros, zeros.copy()
+    levels = F32(2 ** b - 1)
     q = np.zeros((n, d_c), dtype=np.int64)
     dh = np.zeros((n, len(bounds)), dtype=np.float16)
     mh = np.zeros((n, len(bounds)), dtype=np.float16)
@@ -204,12 +216,15 @@ def quantize(z: np.ndarray, g: int, b: int):
     return q, dh, mh
 
 
-def dequantize(q: np.ndarray, dh: np.ndarray, mh: np.ndarray, g: int) -> np.ndarray:
+def dequantize(q: np.ndarray, dh: np.ndarray, mh: np.ndarray, g: int, b: int = 0) -> np.ndarray:
     """z~ = q * Delta + z_min per group ([RKV] §2.4 third equation).
 
     Exact in float64 for fp16 (Delta_h, m_h) and b <= 8, then one rounding to
-    float32.  Returns float32 [n, d_c].
+    float32.  Returns float32 [n, d_c].  b = 16 (identity mode): the fp16
+    value the code holds.
     """
+    if b == IDENTITY_BITS:
+        return np.asarray(q).astype(np.uint16).view(np.float16).astype(F32)
     n, d_c = q.shape
     out = np.empty((n, d_c), dtype=F64)
     for gi, (a, e) in enumerate(group_bounds(d_c, g)):
@@ -221,6 +236,8 @@ def dequantize(q: np.ndarray, dh: np.ndarray, mh: np.ndarray, g: int) -> np.ndar
 def pack_codes(q: np.ndarray, b: int) -> np.ndarray:
     """Little-endian packing: coordinate per*j + r -> bits [r*b, (r+1)*b) of byte j."""
     n, d_c = q.shape
+    if b == IDENTITY_BITS:                               # two bytes per latent, little-endian
+        return np.ascontiguousarray(q.astype(np.uint16).astype("<u2")).view(np.uint8).reshape(n, 2 * d_c)
     per = 8 // b
     assert d_c % per == 0
     qq = q.astype(np.uint32).reshape(n, d_c // per, per)
@@ -232,6 +249,8 @@ def pack_codes(q: np.ndarray, b: int) -> np.ndarray:
 
 def unpack_codes(codes: np.ndarray, b: int, d_c: int) -> np.ndarray:
     n = codes.shape[0]
+    if b == IDENTITY_BITS:
+        return np.ascontiguousarray(codes).view("<u2").reshape(n, d_c).astype(np.int64)
     per = 8 // b
     mask = (1 << b) - 1
     c = codes.astype(np.int64)
@@ -243,6 +262,8 @@ def unpack_codes(codes: np.ndarray, b: int, d_c: int) -> np.ndarray:
 
 def record_bytes_per_token(d_c: int, g: int, b: int) -> int:
     """b-bit payload plus two fp16 numbers per group ([RKV] §2.4, §3.3)."""
+    if b == IDENTITY_BITS:
+        return 2 * d_c
     n_groups = -(-d_c // g)
     return d_c * b // 8 + 4 * n_groups
 
@@ -379,7 +400,7 @@ def gather(codes: np.ndarray, scale: np.ndarray, zmin: np.ndarray, idx: np.ndarr
     if ok.any():
         sel = idx[ok]
         q = unpack_codes(codes[sel], b, d_c)
-        out[ok] = dequantize(q, scale[sel], zmin[sel], g)
+        out[ok] = dequantize(q, scale[sel], zmin[sel], g, b)
     return out
 
 
@@ -429,7 +450,7 @@ def restore(codes: np.ndarray, scale: np.ndarray, zmin: np.ndarray, ref_idx: np.
             row = np.asarray(kv[bq, t], F64)
         else:
             q = unpack_codes(codes[fl:fl + 1], b, d_c)
-            zt = dequantize(q, scale[fl:fl + 1], zmin[fl:fl + 1], g)[0].astype(F64)
+            zt = dequantize(q, scale[fl:fl + 1], zmin[fl:fl + 1], g, b)[0].astype(F64)
             R = [int(p) for p in ref_idx[fl] if p >= 0]
             row = zt @ Wd + reference_mean(kv[bq], R)
         out[n, : N * D] = apply_rope(row[: N * D], t, N, D, rope_theta)

@@ -26,14 +26,15 @@ class EncodeBuffers:
 
 def alloc_encode(p: rkv_params, device="cuda", with_z: bool = True) -> EncodeBuffers:
     B, T = p.B, p.T
+    ng = 0 if p.b == 16 else p.d_c // p.g          # identity mode stores no group numbers
     ws = rkv_encode_workspace_bytes(p)
     if ws == 0:
         raise ValueError("invalid rkv_params")
     return EncodeBuffers(
         ref_idx=torch.empty((B, T, p.k), dtype=torch.int32, device=device),
         codes=torch.empty((B, T, p.d_c * p.b // 8), dtype=torch.uint8, device=device),
-        scale=torch.empty((B, T, p.d_c // p.g), dtype=torch.float16, device=device),
-        zmin=torch.empty((B, T, p.d_c // p.g), dtype=torch.float16, device=device),
+        scale=torch.empty((B, T, ng), dtype=torch.float16, device=device),
+        zmin=torch.empty((B, T, ng), dtype=torch.float16, device=device),
         z=torch.empty((B, T, p.d_c), dtype=torch.float32, device=device) if with_z else None,
         workspace=torch.empty(ws, dtype=torch.uint8, device=device),
     )

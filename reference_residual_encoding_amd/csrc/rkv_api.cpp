@@ -31,6 +31,12 @@ rkv_status ok() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// scale / zmin: not read or written in identity mode (b = 16), may be NULL there
+#define RKV_NEED_GROUP_PTR(ptr)                                                        \
+  do {                                                                                 \
+    if (p->b != 16) RKV_NEED_PTR(ptr);                                                 \
+  } while (0)
+
 #define RKV_NEED_PTR(ptr)                                                              \
   do {                                                                                 \
     if ((ptr) == nullptr) return fail(RKV_ERR_INVALID_ARG, "%s is NULL", #ptr);        \
@@ -40,7 +46,13 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Fields read by the quantiser and the gather.
 rkv_status check_record(const rkv_params* p) {
   if (p->d_c <= 0) return fail(RKV_ERR_INVALID_ARG, "d_c must be positive (got %d)", p->d_c);
-  if (p->b != 2 && p->b != 4) return fail(RKV_ERR_INVALID_ARG, "b must be 2 or 4 (got %d)", p->b);
+  if (p->b != 2 && p->b != 4 && p->b != 16)
+    return fail(RKV_ERR_INVALID_ARG, "b must be 2, 4 or 16 (identity) (got %d)", p->b);
+  if (p->b == 16) {                       // identity: no groups; g is not read
+    if (p->d_c % 32 != 0)
+      return fail(RKV_ERR_UNSUPPORTED, "d_c must be a multiple of 32 (got %d)", p->d_c);
+    return RKV_OK;
+  }
   if (p->g <= 0) return fail(RKV_ERR_INVALID_ARG, "g must be positive (got %d)", p->g);
   if (p->g != 8 && p->g != 16 && p->g != 32 && p->g != 64)
     return fail(RKV_ERR_UNSUPPORTED, "g must be 8, 16, 32 or 64 on the GPU path (got %d)", p->g);
@@ -184,8 +196,8 @@ rkv_status rkv_encode(const rkv_params* p, const void* kv, const void* w1, const
   RKV_NEED_PTR(w3);
   RKV_NEED_PTR(ref_idx);
   RKV_NEED_PTR(codes);
-  RKV_NEED_PTR(scale);
-  RKV_NEED_PTR(zmin);
+  RKV_NEED_GROUP_PTR(scale);
+  RKV_NEED_GROUP_PTR(zmin);
   RKV_NEED_PTR(workspace);
   if (z != nullptr && !aligned16(z)) return fail(RKV_ERR_INVALID_ARG, "z is not 16-byte aligned");
   const rkv::Shape sh = shape_of(p);
@@ -246,8 +258,8 @@ rkv_status rkv_quantize(const rkv_params* p, const float* z, int64_t rows, uint8
   if (rows == 0) return ok();
   RKV_NEED_PTR(z);
   RKV_NEED_PTR(codes);
-  RKV_NEED_PTR(scale);
-  RKV_NEED_PTR(zmin);
+  RKV_NEED_GROUP_PTR(scale);
+  RKV_NEED_GROUP_PTR(zmin);
   hipError_t e;
   RKV_STAGE(RKV_STAGE_QUANT,
             rkv::launch_quantize(z, rows, p->d_c, p->g, p->b, codes, scale, zmin, stream),
@@ -266,8 +278,8 @@ rkv_status rkv_dequant_gather(const rkv_params* p, const uint8_t* codes, const u
   if (out_dtype != RKV_F32 && out_dtype != RKV_BF16) return fail(RKV_ERR_INVALID_ARG, "unknown out_dtype %d", int(out_dtype));
   if (n_idx == 0) return ok();
   RKV_NEED_PTR(codes);
-  RKV_NEED_PTR(scale);
-  RKV_NEED_PTR(zmin);
+  RKV_NEED_GROUP_PTR(scale);
+  RKV_NEED_GROUP_PTR(zmin);
   RKV_NEED_PTR(idx);
   RKV_NEED_PTR(out);
   hipError_t e;
@@ -306,8 +318,8 @@ rkv_status rkv_restore(const rkv_params* p, const uint8_t* codes, const uint16_t
   if (!(rope_theta == rope_theta)) return fail(RKV_ERR_INVALID_ARG, "rope_theta is NaN");
   if (n_idx == 0) return ok();
   RKV_NEED_PTR(codes);
-  RKV_NEED_PTR(scale);
-  RKV_NEED_PTR(zmin);
+  RKV_NEED_GROUP_PTR(scale);
+  RKV_NEED_GROUP_PTR(zmin);
   RKV_NEED_PTR(ref_idx);
   RKV_NEED_PTR(kv);
   RKV_NEED_PTR(wd);
@@ -346,8 +358,8 @@ rkv_status rkv_append(const rkv_params* p, void* kv, const void* kv_new, const i
   RKV_NEED_PTR(w3);
   RKV_NEED_PTR(ref_idx);
   RKV_NEED_PTR(codes);
-  RKV_NEED_PTR(scale);
-  RKV_NEED_PTR(zmin);
+  RKV_NEED_GROUP_PTR(scale);
+  RKV_NEED_GROUP_PTR(zmin);
   RKV_NEED_PTR(workspace);
   if (z != nullptr && !aligned16(z)) return fail(RKV_ERR_INVALID_ARG, "z is not 16-byte aligned");
   const rkv::Shape sh = shape_of(p);

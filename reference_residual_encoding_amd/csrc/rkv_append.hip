@@ -411,16 +411,10 @@ __global__ __launch_bounds__(256) void k_app_w3(const float* __restrict__ dh,
     float v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = tid < LPR ? zl[min(tid, LPR - 1) * 8 + e] : 0.0f;
-    uint16_t dhq, mhq;
-    const uint32_t word = quant8<BITS, G8>(v, dhq, mhq);
+    const size_t row = size_t(b) * T + pos[b];
+    const int64_t unit = int64_t(row) * (d_c / 8) + c0 / 8 + tid;
+    write_record8<BITS, G8>(v, tid < LPR, tid, unit, codes, scale, zmin);
     if (tid < LPR) {
-      const size_t row = size_t(b) * T + pos[b];
-      const int64_t unit = int64_t(row) * (d_c / 8) + c0 / 8 + tid;
-      store_codes<BITS>(codes, unit, word);
-      if ((tid % G8) == 0) {
-        scale[unit / G8] = dhq;
-        zmin[unit / G8] = mhq;
-      }
       if (z) {
         float4* dst = reinterpret_cast<float4*>(z + unit * 8);
         dst[0] = make_float4(v[0], v[1], v[2], v[3]);
@@ -461,8 +455,9 @@ hipError_t launch_append(const Shape& sh, void* kv, const void* kv_new, const in
   auto* mean = reinterpret_cast<float*>(ws + L.mean);
   auto* dh = reinterpret_cast<float*>(ws + L.dh);
   auto* act = reinterpret_cast<int*>(ws + L.act);
-  const int rec_bytes = sh.d_c * sh.b / 8, n_groups = sh.d_c / sh.g;
-  const int cb = sh.g <= 32 ? 32 : 64;                  // a block holds whole groups
+  const int rec_bytes = sh.d_c * sh.b / 8;
+  const int n_groups = sh.b == kIdentityBits ? 0 : sh.d_c / sh.g;   // identity: no group numbers
+  const int cb = sh.g <= 32 || sh.b == kIdentityBits ? 32 : 64;   // a block holds whole groups
   const int n_dist = sh.B * L.n_lists;
 
 #define RKV_APP(E, KL)                                                                            \
@@ -499,9 +494,11 @@ hipError_t launch_append(const Shape& sh, void* kv, const void* kv_new, const in
     default: RKV_W3(E, BITS, 8); break;    \
   }
   if (sh.bf16) {
-    if (sh.b == 4) { RKV_W3G(uint16_t, 4) } else { RKV_W3G(uint16_t, 2) }
+    if (sh.b == 4) { RKV_W3G(uint16_t, 4) } else if (sh.b == 2) { RKV_W3G(uint16_t, 2) }
+    else { RKV_W3(uint16_t, kIdentityBits, 1); }
   } else {
-    if (sh.b == 4) { RKV_W3G(float, 4) } else { RKV_W3G(float, 2) }
+    if (sh.b == 4) { RKV_W3G(float, 4) } else if (sh.b == 2) { RKV_W3G(float, 2) }
+    else { RKV_W3(float, kIdentityBits, 1); }
   }
 #undef RKV_W3G
 #undef RKV_W3

@@ -667,17 +667,10 @@ __global__ __launch_bounds__(W3Cfg<E>::kThreads) void k_w3_quant(const char* __r
       float v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = zt[row * LD + ch * 8 + e];
-      uint16_t dhb, mhb;
-      const uint32_t word = quant8<BITS, G8>(v, dhb, mhb);
+      const int64_t rec = recr;                                     // record row b*T + t
+      const int64_t u = (rec * d_c + col) / 8;                      // flat 8-value unit
+      write_record8<BITS, G8>(v, act, tid, u, codes, scale, zmin);
       if (act) {
-        const int64_t rec = recr;                                   // record row b*T + t
-        const int64_t u = (rec * d_c + col) / 8;                    // flat 8-value unit
-        store_codes<BITS>(codes, u, word);
-        if ((tid % G8) == 0) {
-          const int64_t grp = (rec * d_c + col) / (8 * G8);
-          scale[grp] = dhb;
-          zmin[grp] = mhb;
-        }
         if (z) {
           float* zo = z + rec * d_c + col;
           *reinterpret_cast<float4*>(zo) = make_float4(v[0], v[1], v[2], v[3]);
@@ -714,15 +707,7 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ z, i
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = 0.0f;
     }
-    uint16_t dhb, mhb;
-    const uint32_t word = quant8<BITS, G8>(v, dhb, mhb);
-    if (act) {
-      store_codes<BITS>(codes, u, word);
-      if ((lane % G8) == 0) {
-        scale[u / G8] = dhb;
-        zmin[u / G8] = mhb;
-      }
-    }
+    write_record8<BITS, G8>(v, act, lane, u, codes, scale, zmin);
   }
 }
 
@@ -756,7 +741,6 @@ __global__ __launch_bounds__(256) void k_restore_prep(const uint8_t* __restrict_
                                                       const int32_t* __restrict__ ref_idx, int k,
                                                       int d_c, int g,
                                                       uint32_t* __restrict__ zt) {
-  constexpr uint32_t kMask = (1u << BITS) - 1;
   const int64_t units = n_idx * (d_c / 8);
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
   for (int64_t u = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; u < units; u += stride) {
@@ -767,17 +751,12 @@ __global__ __launch_bounds__(256) void k_restore_prep(const uint8_t* __restrict_
     // least one reference: position 0 always is one)
     const bool live = src >= 0 && src < total_rows && ref_idx[src * k] >= 0;
     const int64_t sr = live ? src : 0;
-    uint32_t word;
-    if constexpr (BITS == 4)
-      word = *reinterpret_cast<const uint32_t*>(codes + sr * (d_c / 2) + o / 2);
-    else
-      word = *reinterpret_cast<const uint16_t*>(codes + sr * (d_c / 4) + o / 4);
-    const int64_t grp = sr * (d_c / g) + o / g;
-    const float dh = f16_bits_to_f32(scale[grp]), mh = f16_bits_to_f32(zmin[grp]);
+    float zv[8];
+    read_record8<BITS>(codes, scale, zmin, sr, o, d_c, g, zv);
     uint32_t w[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float v = live ? fmaf(float((word >> (BITS * e)) & kMask), dh, mh) : 0.0f;
+      const float v = live ? zv[e] : 0.0f;
       w[e] = sizeof(E) == 2 ? bf16_hi_lo(v) : __float_as_uint(v);
     }
     u32x4* dst = reinterpret_cast<u32x4*>(zt + i * d_c + o);
@@ -935,7 +914,6 @@ __global__ __launch_bounds__(256) void k_gather(const uint8_t* __restrict__ code
                                                 const int32_t* __restrict__ idx, int64_t n_idx,
                                                 int64_t total_rows, int d_c, int g,
                                                 void* __restrict__ out) {
-  constexpr uint32_t kMask = (1u << BITS) - 1;
   const int64_t units = n_idx * (d_c / 8);
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
   for (int64_t u = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; u < units; u += stride) {
@@ -948,15 +926,7 @@ __global__ __launch_bounds__(256) void k_gather(const uint8_t* __restrict__ code
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = __builtin_nanf("");
     } else {
-      uint32_t word;
-      if constexpr (BITS == 4)
-        word = *reinterpret_cast<const uint32_t*>(codes + src * (d_c / 2) + o / 2);
-      else
-        word = *reinterpret_cast<const uint16_t*>(codes + src * (d_c / 4) + o / 4);
-      const int64_t grp = src * (d_c / g) + o / g;
-      const float dh = f16_bits_to_f32(scale[grp]), mh = f16_bits_to_f32(zmin[grp]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = fmaf(float((word >> (BITS * e)) & kMask), dh, mh);
+      read_record8<BITS>(codes, scale, zmin, src, o, d_c, g, v);
     }
     if constexpr (BF16) {
       uint16_t* o16 = reinterpret_cast<uint16_t*>(out) + f;
@@ -1089,7 +1059,8 @@ hipError_t launch_ref_norms(const Shape& sh, const void* kv, char* ws, const Wor
   auto* y = reinterpret_cast<float*>(ws + L.ysq);
   const auto* rpos = reinterpret_cast<const int*>(ws + L.rpos);
   const auto* p = static_cast<const char*>(kv);
-  const int cb = sh.d_c * sh.b / 8, ng = sh.d_c / sh.g;
+  // identity mode stores no group numbers
+  const int cb = sh.d_c * sh.b / 8, ng = sh.b == kIdentityBits ? 0 : sh.d_c / sh.g;
   if (sh.bf16)
     k_ref_gather<uint16_t><<<cdiv(rows, 4), 256, 0, st>>>(p, sh.B, sh.T, sh.C, rpos, sh.nref,
                                                           ws + L.refs, y, ref_idx, sh.k, codes, cb,
@@ -1201,9 +1172,11 @@ hipError_t launch_w3_quant(const Shape& sh, char* ws, const Workspace& L, uint8_
     default: RKV_W3(E, BITS, 8); break;       \
   }
   if (sh.bf16) {
-    if (sh.b == 4) { RKV_W3G(uint16_t, 4) } else { RKV_W3G(uint16_t, 2) }
+    if (sh.b == 4) { RKV_W3G(uint16_t, 4) } else if (sh.b == 2) { RKV_W3G(uint16_t, 2) }
+    else { RKV_W3(uint16_t, kIdentityBits, 1); }
   } else {
-    if (sh.b == 4) { RKV_W3G(float, 4) } else { RKV_W3G(float, 2) }
+    if (sh.b == 4) { RKV_W3G(float, 4) } else if (sh.b == 2) { RKV_W3G(float, 2) }
+    else { RKV_W3(float, kIdentityBits, 1); }
   }
 #undef RKV_W3G
 #undef RKV_W3
@@ -1223,7 +1196,7 @@ hipError_t launch_quantize(const float* z, int64_t rows, int d_c, int g, int b, 
     case 32: RKV_Q(BITS, 4); break;         \
     default: RKV_Q(BITS, 8); break;         \
   }
-  if (b == 4) { RKV_QG(4) } else { RKV_QG(2) }
+  if (b == 4) { RKV_QG(4) } else if (b == 2) { RKV_QG(2) } else { RKV_Q(kIdentityBits, 1); }
 #undef RKV_QG
 #undef RKV_Q
   return hipGetLastError();
@@ -1238,7 +1211,8 @@ hipError_t launch_gather(const uint8_t* codes, const uint16_t* scale, const uint
 #define RKV_G(BITS, BF) \
   k_gather<BITS, BF><<<grid, 256, 0, st>>>(codes, scale, zmin, idx, n_idx, total_rows, d_c, g, out)
   if (b == 4) { if (out_bf16) RKV_G(4, true); else RKV_G(4, false); }
-  else { if (out_bf16) RKV_G(2, true); else RKV_G(2, false); }
+  else if (b == 2) { if (out_bf16) RKV_G(2, true); else RKV_G(2, false); }
+  else { if (out_bf16) RKV_G(kIdentityBits, true); else RKV_G(kIdentityBits, false); }
 #undef RKV_G
   return hipGetLastError();
 }
@@ -1274,8 +1248,13 @@ hipError_t launch_restore(const Shape& sh, int N, int D, const uint8_t* codes,
 #define RKV_RP(E, BITS)                                                                       \
   k_restore_prep<E, BITS><<<grid, 256, 0, st>>>(codes, scale, zmin, idx, n_idx, total, ref_idx, \
                                                 sh.k, sh.d_c, sh.g, zt)
-  if (sh.bf16) { if (sh.b == 4) RKV_RP(uint16_t, 4); else RKV_RP(uint16_t, 2); }
-  else { if (sh.b == 4) RKV_RP(float, 4); else RKV_RP(float, 2); }
+  if (sh.bf16) {
+    if (sh.b == 4) RKV_RP(uint16_t, 4); else if (sh.b == 2) RKV_RP(uint16_t, 2);
+    else RKV_RP(uint16_t, kIdentityBits);
+  } else {
+    if (sh.b == 4) RKV_RP(float, 4); else if (sh.b == 2) RKV_RP(float, 2);
+    else RKV_RP(float, kIdentityBits);
+  }
 #undef RKV_RP
   const auto* kvp = static_cast<const char*>(kv);
 #define RKV_RS(E, KL)                                                                            \

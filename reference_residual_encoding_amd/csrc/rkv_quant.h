@@ -76,4 +76,66 @@ __device__ __forceinline__ void store_codes(uint8_t* codes, int64_t unit, uint32
     *reinterpret_cast<uint16_t*>(codes + unit * 2) = uint16_t(word);
 }
 
+// Quantisation off ([RKV] §2.4: Q is the identity): the 8 latents as fp16
+// bits, rounded to nearest even, little-endian, 16 bytes per lane.
+constexpr int kIdentityBits = 16;
+__device__ __forceinline__ u32x4 fp16x8(const float (&v)[8]) {
+  u32x4 w;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    w[e] = uint32_t(f32_to_f16_bits(v[2 * e])) | (uint32_t(f32_to_f16_bits(v[2 * e + 1])) << 16);
+  return w;
+}
+
+// The record of the 8 consecutive latents of flat unit `unit` (latent
+// index 8*unit over [rows][d_c]): codes, and Delta_h / m_h once per group
+// (by the first of its G8 lanes).  Every lane of a group calls it (the
+// quantiser exchanges min and max between them); only lanes with `act`
+// write.  Identity mode writes the fp16 latents and no group numbers.
+template <int BITS, int G8>
+__device__ __forceinline__ void write_record8(const float (&v)[8], bool act, int lane,
+                                              int64_t unit, uint8_t* codes, uint16_t* scale,
+                                              uint16_t* zmin) {
+  if constexpr (BITS == kIdentityBits) {
+    if (act) *reinterpret_cast<u32x4*>(codes + unit * 16) = fp16x8(v);
+  } else {
+    uint16_t dhb, mhb;
+    const uint32_t word = quant8<BITS, G8>(v, dhb, mhb);
+    if (act) {
+      store_codes<BITS>(codes, unit, word);
+      if ((lane % G8) == 0) {
+        scale[unit / G8] = dhb;
+        zmin[unit / G8] = mhb;
+      }
+    }
+  }
+}
+
+// The 8 dequantised latents of flat unit `unit` of record row `row`
+// (z~ = fmaf(q, Delta_h, m_h), or the stored fp16 values in identity mode).
+template <int BITS>
+__device__ __forceinline__ void read_record8(const uint8_t* codes, const uint16_t* scale,
+                                             const uint16_t* zmin, int64_t row, int o, int d_c,
+                                             int g, float (&v)[8]) {
+  if constexpr (BITS == kIdentityBits) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(codes + row * (d_c * 2) + o * 2);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = f16_bits_to_f32(uint16_t(w[e] & 0xFFFFu));
+      v[2 * e + 1] = f16_bits_to_f32(uint16_t(w[e] >> 16));
+    }
+  } else {
+    constexpr uint32_t kMask = (1u << BITS) - 1;
+    uint32_t word;
+    if constexpr (BITS == 4)
+      word = *reinterpret_cast<const uint32_t*>(codes + row * (d_c / 2) + o / 2);
+    else
+      word = *reinterpret_cast<const uint16_t*>(codes + row * (d_c / 4) + o / 4);
+    const int64_t grp = row * (d_c / g) + o / g;
+    const float dh = f16_bits_to_f32(scale[grp]), mh = f16_bits_to_f32(zmin[grp]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = fmaf(float((word >> (BITS * e)) & kMask), dh, mh);
+  }
+}
+
 }  // namespace rkv

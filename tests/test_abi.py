@@ -223,3 +223,15 @@ def test_reference_positions_host_query():
     assert got == [0, 1, 2, 3, 13, 24, 36, 49, 63, 79]
     with pytest.raises(R.RkvError):
         R.rkv_reference_positions(_p(LLAMA32K, ref_stride=0))
+
+
+def test_identity_mode_validation():
+    """b = 16 is the identity mode ([RKV] §2.4): larger records, no group numbers."""
+    p16 = _p(LLAMA32K, b=16)
+    assert R.rkv_encode_workspace_bytes(p16) > 0
+    assert R.rkv_encode_workspace_bytes(_p(LLAMA32K, b=8)) == 0
+    assert R.rkv_encode_workspace_bytes(_p(LLAMA32K, b=16, g=0)) > 0       # g is not read
+    assert _encode(_p(LLAMA32K, b=3)) == R.RKV_ERR_INVALID_ARG
+    # scale / zmin may be NULL in identity mode: validation then stops at the next pointer
+    assert _encode(p16, scale=None, zmin=None, workspace=None) == R.RKV_ERR_INVALID_ARG
+    assert "workspace" in R.rkv_last_error()

@@ -47,8 +47,9 @@ class Cache:
         u8 = lambda nbytes: torch.full((nbytes,), SENTINEL, dtype=torch.uint8, device=device)
         self.ref_idx = u8(n * cfg.k * 4).view(torch.int32).view(cfg.B, cfg.T, cfg.k)
         self.codes = u8(n * cfg.d_c * cfg.b // 8).view(cfg.B, cfg.T, -1)
-        self.scale = u8(n * (cfg.d_c // cfg.g) * 2).view(torch.float16).view(cfg.B, cfg.T, -1)
-        self.zmin = u8(n * (cfg.d_c // cfg.g) * 2).view(torch.float16).view(cfg.B, cfg.T, -1)
+        ng = 1 if cfg.b == 16 else cfg.d_c // cfg.g      # identity: no group numbers (not read)
+        self.scale = u8(n * ng * 2).view(torch.float16).view(cfg.B, cfg.T, -1)
+        self.zmin = u8(n * ng * 2).view(torch.float16).view(cfg.B, cfg.T, -1)
         self.z = u8(n * cfg.d_c * 4).view(torch.float32).view(cfg.B, cfg.T, cfg.d_c)
         self.ws_bytes = R.rkv_append_workspace_bytes(self.p)
         assert self.ws_bytes > 0
@@ -114,7 +115,9 @@ RAGGED_F32 = LLAMA8K.with_(name="append_ragged_f32_k8_g64", B=2, T=700, N=1, D=6
                            d_c=128, k=8, g=64, b=4, stride=3, dtype="f32", n_protos=12, noise=0.3)
 
 
-@pytest.mark.parametrize("cfg", [RAGGED_BF16, RAGGED_F32], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [RAGGED_BF16, RAGGED_F32,
+                                 RAGGED_BF16.with_(name="append_ragged_bf16_identity", b=16)],
+                         ids=lambda c: c.name)
 def test_append_independent_positions_per_sequence(cfg):
     """Continuous batching: every call appends a different position in each
     sequence, in random order, with some sequences skipped (pos -1 or T)."""

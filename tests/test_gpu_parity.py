@@ -118,6 +118,23 @@ def test_dynamic_schedule_sampled(cfg, n_random):
     test_full_size_configs_sampled(cfg, n_random)
 
 
+# Quantisation off ([RKV] §2.4: Q is the identity; the latent stored as fp16).
+IDENTITY = [
+    TINY.with_(name="tiny_f32_identity", b=16),
+    RAGGED[0].with_(name="ragged_bf16_identity_dynamic", b=16, alpha=0.01, n_sink=3),
+]
+
+
+@pytest.mark.parametrize("cfg", IDENTITY, ids=lambda c: c.name)
+def test_identity_mode_all_positions(cfg):
+    _log(f"[case] {cfg.name} full")
+    _full_parity(cfg)
+
+
+def test_identity_mode_sampled():
+    test_full_size_configs_sampled(LLAMA8K.with_(name="llama8b_T8k_identity", b=16), 400)
+
+
 def test_select_export_matches_encode():
     cfg = LLAMA8K.with_(T=2048)
     w = generate(cfg)
@@ -137,7 +154,7 @@ def test_encode_is_deterministic():
         assert np.array_equal(h1[key].view(np.uint8), h2[key].view(np.uint8)), key
 
 
-@pytest.mark.parametrize("b,g", [(4, 32), (2, 32), (4, 8), (2, 16), (4, 64)])
+@pytest.mark.parametrize("b,g", [(4, 32), (2, 32), (4, 8), (2, 16), (4, 64), (16, 32)])
 def test_quantize_export_bit_exact(b, g):
     rng = np.random.default_rng(b * 100 + g)
     d_c = 128
@@ -158,11 +175,13 @@ def test_quantize_export_bit_exact(b, g):
     torch.cuda.synchronize()
     q, dh, mh = O.quantize(z.astype(np.float64), g, b)
     assert np.array_equal(codes.cpu().numpy(), O.pack_codes(q, b))
+    if b == O.IDENTITY_BITS:                         # no group numbers in identity mode
+        return
     assert np.array_equal(sc.cpu().numpy().view(np.uint16), dh.view(np.uint16))
     assert np.array_equal(zm.cpu().numpy().view(np.uint16), mh.view(np.uint16))
 
 
-@pytest.mark.parametrize("b", [4, 2])
+@pytest.mark.parametrize("b", [4, 2, 16])
 def test_gather_bit_exact_f32_and_bf16(b):
     rng = np.random.default_rng(5 + b)
     B, T, d_c, g = 2, 300, 64, 32

@@ -115,7 +115,9 @@ def test_restore_dynamic_schedule_all_positions():
     _compare(got, _oracle(w, wd, rec, idx, cfg.rope_theta), REL_F32, f"{cfg.name} f32")
 
 
-@pytest.mark.parametrize("cfg", [LLAMA8K, QWEN_LIKE, LLAMA8K_DYN], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [LLAMA8K, QWEN_LIKE, LLAMA8K_DYN,
+                                 LLAMA8K.with_(name="llama8b_T8k_identity", b=16)],
+                         ids=lambda c: c.name)
 def test_restore_sampled_tokens(cfg):
     _log(f"[case] restore {cfg.name}")
     w = generate(cfg)

@@ -603,3 +603,28 @@ def test_append_of_a_reference_position_is_stored_with_a_zero_record(tiny):
     assert r["stored"]
     assert np.all(r["ref_idx"] == -1) and not r["codes"].any()
     assert not r["scale"].any() and not r["zmin"].any() and not r["z"].any()
+
+
+# ------------------------------------------------------------ identity mode
+
+def test_identity_mode_stores_the_latent_as_fp16():
+    """[RKV] §2.4: with quantisation off Q is the identity; the record is the
+    latent in fp16 (2 bytes per coordinate, no group numbers), so z~ is z
+    within half an fp16 ulp, and exactly z when z is an fp16 value."""
+    rng = np.random.default_rng(8)
+    z = rng.standard_normal((50, 64)) * np.exp(rng.uniform(-6, 3, (50, 1)))
+    q, dh, mh = O.quantize(z, 32, 16)
+    codes = O.pack_codes(q, 16)
+    assert codes.shape == (50, 128) and not dh.any() and not mh.any()
+    assert O.record_bytes_per_token(64, 32, 16) == 128
+    back = O.dequantize(O.unpack_codes(codes, 16, 64), dh, mh, 32, 16).astype(np.float64)
+    z32 = z.astype(np.float32).astype(np.float64)
+    # fp16 normal range: |error| <= 2^-11 |z| (half an ulp, relative)
+    normal = np.abs(z32) >= 2.0 ** -14
+    assert np.all(np.abs(back - z32)[normal] <= 2.0 ** -11 * np.abs(z32)[normal])
+    assert np.all(np.abs(back - z32)[~normal] <= 2.0 ** -25)
+    exact = np.array([[0.0, 1.0, -2.5, 0.099975586, 65504.0, -6.1035156e-05, 3.0, 0.5]])
+    qe, dhe, mhe = O.quantize(exact, 8, 16)
+    np.testing.assert_array_equal(O.dequantize(qe, dhe, mhe, 8, 16), exact.astype(np.float32))
+    # byte order: little-endian fp16 bits (1.0 = 0x3C00 -> 00 3C)
+    assert O.pack_codes(O.quantize(np.array([[1.0]]), 1, 16)[0], 16).tolist() == [[0x00, 0x3C]]
