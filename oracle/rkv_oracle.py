@@ -64,6 +64,12 @@ Restore (read side, [RKV] §2.5 and the implementation note of §2.1):
   9. split KV^ into K (first N*D coordinates) and V; the restored pre-RoPE
      key is rotated at the token's own position                ([RKV] §2.1)
 
+FP8 references ([RKV] §2.4 last paragraph; §2.5: encoder and decoder use
+the references as stored): reading, OCP E4M3 (bias 7, 3 mantissa bits,
+largest finite 448), round to nearest even, saturating at +-448, no scale
+factor; retrieval distances, the mean and the restore all read the FP8
+values, the token being encoded its own input row.
+
 Readings for the restore: z~ is the dequantised record of step 7; the
 references are the stored rows kv_j at input precision; RoPE pairs
 coordinate d of a head with d + D/2 ("rotate half") and turns pair i by
@@ -130,20 +136,75 @@ def k_effective(k: int, pool_size: int) -> int:
 
 
 # ---------------------------------------------------------------- retrieval
+# ---------------------------------------------------------------- FP8 references
+FP8_MAX = 448.0
+
+
+def fp8_e4m3(x: np.ndarray) -> np.ndarray:
+    """Stored value of a reference coordinate kept in FP8 ([RKV] §2.4 last
+    paragraph: references are stored in FP8 in deployment).  Reading: the
+    OCP E4M3 format (4 exponent bits, bias 7, 3 mantissa bits, subnormals
+    down to 2^-9, largest finite 448, no infinities), round to nearest even,
+    saturating at +-448.  Returns float64 values on that grid."""
+    x = np.asarray(x, F64)
+    a = np.abs(x)
+    _, ex = np.frexp(np.maximum(a, 2.0 ** -6))       # a = m * 2^ex, m in [0.5, 1)
+    spacing = np.ldexp(1.0, ex - 1 - 3)               # 3 mantissa bits below the leading one
+    r = np.minimum(np.rint(a / spacing) * spacing, FP8_MAX)
+    return np.copysign(r, x)
+
+
+def fp8_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """The E4M3 byte of each value of fp8_e4m3(x): sign, 4-bit biased
+    exponent (0 for subnormals), 3-bit mantissa."""
+    r = fp8_e4m3(x)
+    a = np.abs(r)
+    sign = np.where(np.signbit(r), 0x80, 0)
+    sub = a < 2.0 ** -6
+    _, ex = np.frexp(np.where(sub, 1.0, a))
+    e = ex - 1
+    mant = np.where(sub, a / 2.0 ** -9, (a / np.ldexp(1.0, e) - 1.0) * 8.0)
+    expf = np.where(sub, 0, e + 7)
+    return (sign | (expf.astype(np.int64) << 3) | np.rint(mant).astype(np.int64)).astype(np.uint8)
+
+
+def fp8_e4m3_value(bits: np.ndarray) -> np.ndarray:
+    """Value of E4M3 bytes (the inverse of fp8_e4m3_bits on its range)."""
+    bits = np.asarray(bits, np.int64)
+    sign = np.where(bits & 0x80, -1.0, 1.0)
+    e = (bits >> 3) & 0xF
+    m = bits & 7
+    val = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.ldexp(1.0, e - 7))
+    return sign * val
+
+
+def stored_references(kv_seq: np.ndarray, refs: np.ndarray, ref_fp8: bool) -> np.ndarray:
+    """The cache's view of a sequence: reference rows as stored (FP8 values
+    when ref_fp8, else the input rows), every other row as given (never read
+    by retrieval or the mean)."""
+    out = np.array(kv_seq, dtype=F64, copy=True)
+    if ref_fp8 and len(refs):
+        out[refs] = fp8_e4m3(out[refs])
+    return out
+
+
 def squared_l2(x: np.ndarray, Y: np.ndarray) -> np.ndarray:
     """||x - y_j||_2^2 for every row y_j of Y, by direct differences."""
     diff = np.asarray(Y, F64) - np.asarray(x, F64)[None, :]
     return np.einsum("jc,jc->j", diff, diff)
 
 
-def retrieve(kv_seq: np.ndarray, t: int, s: int, k: int, refs: Optional[np.ndarray] = None):
+def retrieve(kv_seq: np.ndarray, t: int, s: int, k: int, refs: Optional[np.ndarray] = None,
+             stored: Optional[np.ndarray] = None):
     """Top-k_t nearest references of token t ([RKV] §2.2 retrieval equation).
 
     Returns (R, d_sorted): R are the chosen reference positions ordered by
     (distance, position); d_sorted are all pool distances in the same order.
+    `stored` holds the references' stored rows (default: kv_seq itself).
     """
     pool = candidate_pool(t, s, refs)
-    d = squared_l2(kv_seq[t], kv_seq[pool])
+    Y = kv_seq if stored is None else stored
+    d = squared_l2(kv_seq[t], Y[pool])
     order = np.lexsort((pool, d))            # primary key d, then position
     k_t = k_effective(k, len(pool))
     return pool[order[:k_t]], d[order]
@@ -291,7 +352,7 @@ def keep_ratio(beta: float, rho_ref: float, qb: float, dc_over_2dk: float,
 # ---------------------------------------------------------------- encode
 def encode_tokens(kv_seq: np.ndarray, W1, W2, W3, positions: Iterable[int], *,
                   k: int, g: int, b: int, s: int, n_diag: Optional[int] = None,
-                  alpha: float = 0.0, n_sink: int = 0) -> Dict:
+                  alpha: float = 0.0, n_sink: int = 0, ref_fp8: bool = False) -> Dict:
     """Encode the given positions of one sequence, each on its own.
 
     kv_seq: [T, C] joint vectors [K heads | V heads], pre-RoPE ([RKV] §2.1).
@@ -312,17 +373,21 @@ def encode_tokens(kv_seq: np.ndarray, W1, W2, W3, positions: Iterable[int], *,
     refs = reference_schedule(len(kv_seq), s, alpha, n_sink)
     ref_mask = np.zeros(len(kv_seq), dtype=bool)
     ref_mask[refs] = True
+    # encoder and decoder use the references as stored ([RKV] §2.5), FP8
+    # values when they are kept in FP8; the token itself is encoded from its
+    # own input row
+    stored = stored_references(kv_seq, refs, ref_fp8)
     enc_rows, enc_kv, enc_mean = [], [], []
     for i, t in enumerate(positions):
         if ref_mask[int(t)]:
             continue                       # references are stored as they are
-        R, d_sorted = retrieve(kv_seq, int(t), s, k, refs)
+        R, d_sorted = retrieve(kv_seq, int(t), s, k, refs, stored)
         ref_idx[i, :len(R)] = np.sort(R)
         m = min(n_diag, len(d_sorted))
         d_diag[i, :m] = d_sorted[:m]
         enc_rows.append(i)
         enc_kv.append(kv_seq[t])
-        enc_mean.append(reference_mean(kv_seq, R))
+        enc_mean.append(reference_mean(stored, R))
     if enc_rows:
         rows = np.asarray(enc_rows)
         z[rows] = residual_latent(np.stack(enc_kv), np.stack(enc_mean), W1, W2, W3)
@@ -336,11 +401,11 @@ def encode_tokens(kv_seq: np.ndarray, W1, W2, W3, positions: Iterable[int], *,
 
 
 def encode(kv: np.ndarray, W1, W2, W3, *, k: int, g: int, b: int, s: int,
-           alpha: float = 0.0, n_sink: int = 0) -> Dict:
+           alpha: float = 0.0, n_sink: int = 0, ref_fp8: bool = False) -> Dict:
     """Encode every position of every sequence; kv is [B, T, C]."""
     B, T, _ = kv.shape
     parts = [encode_tokens(kv[bi], W1, W2, W3, range(T), k=k, g=g, b=b, s=s, alpha=alpha,
-                           n_sink=n_sink)
+                           n_sink=n_sink, ref_fp8=ref_fp8)
              for bi in range(B)]
     out = {}
     for key in ("ref_idx", "z", "q", "scale", "zmin", "codes", "d_diag", "is_ref"):
@@ -349,7 +414,8 @@ def encode(kv: np.ndarray, W1, W2, W3, *, k: int, g: int, b: int, s: int,
 
 
 def append_token(cache_seq: np.ndarray, kv_new: np.ndarray, t: int, W1, W2, W3, *, k: int,
-                 g: int, b: int, s: int, alpha: float = 0.0, n_sink: int = 0) -> Dict:
+                 g: int, b: int, s: int, alpha: float = 0.0, n_sink: int = 0,
+                 ref_fp8: bool = False) -> Dict:
     """Decode step 4 of [RKV] §2.7 for one sequence: the new token enters the
     cache at position t.
 
@@ -359,7 +425,8 @@ def append_token(cache_seq: np.ndarray, kv_new: np.ndarray, t: int, W1, W2, W3, 
     cache_seq[j] at scheduled positions j < t, by retrieval (§2.2), the mean
     (§2.2), z = f_c(kv_new) - f_c(mean) (§2.3) and the quantiser (§2.4).
     No other row of cache_seq is read.  The cache itself is not modified:
-    the caller stores kv_new at row t when stored is True."""
+    the caller stores stored_row (kv_new, or its FP8 value when ref_fp8) at
+    row t when stored is True."""
     T = len(cache_seq)
     kv_new = np.asarray(kv_new, F64)
     d_c = np.asarray(W3).shape[1]
@@ -382,7 +449,8 @@ def append_token(cache_seq: np.ndarray, kv_new: np.ndarray, t: int, W1, W2, W3, 
         dh[:] = 0
         mh[:] = 0
     return dict(stored=stored, ref_idx=ref_idx, z=z[0], q=q[0], scale=dh[0], zmin=mh[0],
-                codes=pack_codes(q, b)[0])
+                codes=pack_codes(q, b)[0],
+                stored_row=fp8_e4m3(kv_new) if ref_fp8 else kv_new)
 
 
 def gather(codes: np.ndarray, scale: np.ndarray, zmin: np.ndarray, idx: np.ndarray,
@@ -427,7 +495,7 @@ def apply_rope(k_flat: np.ndarray, pos: int, N: int, D: int, theta: float) -> np
 def restore(codes: np.ndarray, scale: np.ndarray, zmin: np.ndarray, ref_idx: np.ndarray,
             kv: np.ndarray, Wd: np.ndarray, idx: np.ndarray, *, s: int, N: int, D: int,
             g: int, b: int, d_c: int, rope_theta: float, alpha: float = 0.0,
-            n_sink: int = 0) -> np.ndarray:
+            n_sink: int = 0, ref_fp8: bool = False) -> np.ndarray:
     """Restore the selected tokens' K|V rows ([RKV] §2.5): z~ W_d plus the mean
     of the token's stored references, reference tokens as stored; then K is
     rotated at the token's position.
@@ -435,10 +503,13 @@ def restore(codes: np.ndarray, scale: np.ndarray, zmin: np.ndarray, ref_idx: np.
     codes/scale/zmin/ref_idx are flattened over [B*T] (ref_idx rows hold
     reference positions, -1 pads); kv is [B][T][C] (only reference rows are
     read); idx are flat b*T + t.  Returns fp64 [len(idx)][C]; NaN rows for
-    indices outside [0, B*T)."""
+    indices outside [0, B*T).  With ref_fp8 the references are read as their
+    FP8 stored values."""
     Bn, T, C = kv.shape
+    refs = reference_schedule(T, s, alpha, n_sink)
     ref_mask = np.zeros(T, dtype=bool)
-    ref_mask[reference_schedule(T, s, alpha, n_sink)] = True
+    ref_mask[refs] = True
+    kv = np.stack([stored_references(kv[bq], refs, ref_fp8) for bq in range(Bn)])
     idx = np.asarray(idx, dtype=np.int64)
     out = np.full((len(idx), C), np.nan, dtype=F64)
     Wd = np.asarray(Wd, F64)

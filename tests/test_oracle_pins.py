@@ -628,3 +628,93 @@ def test_identity_mode_stores_the_latent_as_fp16():
     np.testing.assert_array_equal(O.dequantize(qe, dhe, mhe, 8, 16), exact.astype(np.float32))
     # byte order: little-endian fp16 bits (1.0 = 0x3C00 -> 00 3C)
     assert O.pack_codes(O.quantize(np.array([[1.0]]), 1, 16)[0], 16).tolist() == [[0x00, 0x3C]]
+
+
+# ------------------------------------------------------------ FP8 references
+
+def test_fp8_storage_matches_hand_derived_values():
+    """Every line of tests/golden/fp8_e4m3.txt was derived by hand from the format."""
+    rows = []
+    with open(os.path.join(GOLD, "fp8_e4m3.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                x, v, byte = line.split()[:3]
+                rows.append((float(x), float(v), int(byte, 16)))
+    x = np.array([r[0] for r in rows])
+    np.testing.assert_array_equal(O.fp8_e4m3(x), [r[1] for r in rows])
+    assert O.fp8_e4m3_bits(x).tolist() == [r[2] for r in rows]
+
+
+def test_fp8_storage_matches_the_library_cast_and_round_trips():
+    """torch's float8_e4m3fn cast (round to nearest even) agrees wherever it
+    does not overflow (|x| <= 464); every finite byte decodes and re-encodes
+    to itself."""
+    rng = np.random.default_rng(12)
+    x = np.concatenate([rng.standard_normal(20000) * np.exp(rng.uniform(-9, 6, 20000)),
+                        np.ldexp(np.arange(-16, 17) / 16.0 + 1.0, rng.integers(-10, 8, 33))])
+    x = x.astype(np.float32).astype(np.float64)
+    x = x[np.abs(x) <= 464.0]
+    lib = torch.from_numpy(x.astype(np.float32)).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.fp8_e4m3(x), lib)
+    finite = np.array([b for b in range(256) if (b & 0x7F) != 0x7F], dtype=np.uint8)
+    vals = O.fp8_e4m3_value(finite)
+    assert O.fp8_e4m3_bits(vals).tolist() == finite.tolist()
+    assert np.abs(vals).max() == 448.0
+
+
+def test_fp8_references_select_by_their_stored_values(tiny):
+    """[RKV] §2.5: the encoder uses the references as stored.  With FP8
+    references the selection is brute force over the FP8 values of the pool
+    (rounded here by the library cast), and the mean is theirs."""
+    w, kv, W1, W2, W3 = tiny
+    c = TINY
+    enc = O.encode_tokens(kv, W1, W2, W3, range(c.T), k=c.k, g=c.g, b=c.b, s=c.stride,
+                          ref_fp8=True)
+    kv8 = torch.from_numpy(kv.astype(np.float32)).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for t in range(1, c.T):
+        if t % c.stride == 0:
+            continue
+        pool = list(range(0, t, c.stride))
+        d = sorted((float(((kv[t] - kv8[j]) ** 2).sum()), j) for j in pool)
+        want = sorted(j for _, j in d[:min(c.k, len(pool))])
+        assert [int(j) for j in enc["ref_idx"][t] if j >= 0] == want, t
+    t = 201
+    mean8 = kv8[[int(j) for j in enc["ref_idx"][t] if j >= 0]].mean(axis=0)
+    np.testing.assert_allclose(enc["z"][t], O.residual_latent(kv[t], mean8, W1, W2, W3),
+                               rtol=0, atol=1e-12)
+
+
+def test_fp8_append_in_order_reproduces_the_fp8_encode(tiny):
+    """Appending token by token with FP8 references stores their FP8 values
+    and reproduces the FP8-reference encode of the prefix."""
+    w, kv, W1, W2, W3 = tiny
+    c = TINY
+    cache = np.full_like(kv, np.nan)
+    enc = O.encode(kv[None], W1, W2, W3, k=c.k, g=c.g, b=c.b, s=c.stride, ref_fp8=True)
+    for t in range(c.T):
+        r = O.append_token(cache, kv[t], t, W1, W2, W3, k=c.k, g=c.g, b=c.b, s=c.stride,
+                           ref_fp8=True)
+        if r["stored"]:
+            cache[t] = r["stored_row"]
+        np.testing.assert_array_equal(r["codes"], enc["codes"][0, t])
+        np.testing.assert_array_equal(r["ref_idx"], enc["ref_idx"][0, t])
+    np.testing.assert_array_equal(cache[::c.stride], O.fp8_e4m3(kv[::c.stride]))
+
+
+def test_fp8_restore_reads_the_stored_references(tiny):
+    """[RKV] §2.5: the decoder adds the mean of the references as stored; a
+    reference token restores to its FP8 stored row (unrotated), and a zero
+    record restores to the mean of the FP8 rows."""
+    w, kv, W1, W2, W3 = tiny
+    c = TINY
+    enc = O.encode(kv[None], W1, W2, W3, k=c.k, g=c.g, b=c.b, s=c.stride, ref_fp8=True)
+    flat = lambda a: a.reshape(-1, *a.shape[2:])
+    Wd = np.random.default_rng(9).standard_normal((c.d_c, c.C))
+    refs = np.arange(0, c.T, c.stride)
+    zero = np.zeros_like(flat(enc["codes"]))
+    out = O.restore(zero, np.zeros_like(flat(enc["scale"])), np.zeros_like(flat(enc["zmin"])),
+                    flat(enc["ref_idx"]), kv[None], Wd, np.array([*refs[:5], 201]), s=c.stride,
+                    N=c.N, D=c.D, g=c.g, b=c.b, d_c=c.d_c, rope_theta=0.0, ref_fp8=True)
+    np.testing.assert_array_equal(out[:5], O.fp8_e4m3(kv[refs[:5]]))
+    R = [int(j) for j in enc["ref_idx"][0, 201] if j >= 0]
+    np.testing.assert_allclose(out[5], O.fp8_e4m3(kv[R]).mean(axis=0), rtol=0, atol=1e-12)
