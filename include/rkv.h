@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define RKV_ABI_VERSION 3
+#define RKV_ABI_VERSION 4
 
 typedef enum {
   RKV_OK = 0,
@@ -58,16 +58,34 @@ typedef enum {
 
 typedef enum { RKV_F32 = 0, RKV_BF16 = 1 } rkv_dtype;
 
+/* How the cache keeps its references ([RKV] §2.4 last paragraph: stored
+ * as they are, in FP8 in deployment; §2.5: encoder and decoder use them as
+ * stored).
+ *   RKV_REF_INPUT: at input precision, the rows kv[b][t] at reference
+ *                  positions t (p->dtype).
+ *   RKV_REF_FP8:   as OCP FP8 E4M3 bytes (bias 7, 3 mantissa bits, largest
+ *                  finite 448; round to nearest even, saturating at +-448,
+ *                  no scale factor) in a compact store ref_store[b][j][C],
+ *                  j the index of the reference in the schedule.  The
+ *                  encode computes with the FP8 values of kv's reference
+ *                  rows; rkv_store_refs writes the store; rkv_restore and
+ *                  rkv_append read (and append writes) the store. */
+typedef enum { RKV_REF_INPUT = 0, RKV_REF_FP8 = 1 } rkv_ref_format;
+
 typedef struct {
   int32_t B, T;       /* sequences; tokens per sequence                        */
   int32_t N, D;       /* KV heads; head dimension.  C = 2*N*D                  */
   int32_t d_ff, d_c;  /* compressor width; latent width                        */
   int32_t k;          /* neighbours per token, 1..8 ([RKV] §2.2 uses 4)        */
-  int32_t g, b;       /* quantiser group size (8,16,32,64); bits (2 or 4)      */
+  int32_t g, b;       /* quantiser group size (8,16,32,64); bits 2 or 4, or 16:
+                         quantisation off ([RKV] §2.4: Q is the identity), the
+                         latent stored as fp16 and no group numbers (scale,
+                         zmin neither read nor written, may be NULL; g unused) */
   int32_t ref_stride; /* s >= 1 (s0, the initial stride, of the schedule)      */
   rkv_dtype dtype;    /* element type of kv, w1, w2, w3                        */
   int32_t n_sink;     /* sink tokens (positions < n_sink), stored as references */
   double ref_alpha;   /* schedule growth alpha >= 0 ([RKV] §2.6); 0: fixed     */
+  int32_t ref_format; /* rkv_ref_format of the stored references             */
 } rkv_params;
 
 /* GPU-path limits (RKV_ERR_UNSUPPORTED otherwise): C % 64 == 0,
@@ -153,9 +171,11 @@ rkv_status rkv_select(const rkv_params* p, const void* kv, int32_t* ref_idx,
  *   t * rope_theta^(-2i/D) ("rotate half"; angles reduced in fp64, sin/cos
  *   in fp32); V = KV^[N*D, C) as is.  rope_theta <= 0 leaves K unrotated.
  * Inputs:  codes, scale, zmin, ref_idx as rkv_encode wrote them ([B][T]...);
- *          kv [B][T][C] in p->dtype: the stored references (only rows at
- *          reference positions are read); wd [d_c][C] in p->dtype, used as
- *          z * W_d; idx [n_idx] int32, any order, duplicates allowed.
+ *          kv: the stored references: with RKV_REF_INPUT kv [B][T][C] in
+ *          p->dtype (only rows at reference positions are read), with
+ *          RKV_REF_FP8 the store [B][n_ref][C] of E4M3 bytes;
+ *          wd [d_c][C] in p->dtype, used as z * W_d; idx [n_idx] int32, any
+ *          order, duplicates allowed.
  * Output:  out [n_idx][C], float (RKV_F32) or bf16 rounded to nearest even
  *          (RKV_BF16); an index outside [0, B*T) yields a row of NaN.
  * workspace: at least rkv_restore_workspace_bytes(p, n_idx) bytes.
@@ -180,11 +200,14 @@ rkv_status rkv_restore(const rkv_params* p, const uint8_t* codes,
  *       positions j < t, rows kv[b][j] ([RKV] §2.2-§2.4); its ref_idx row
  *       and record (and z) are written at b*T + t;
  *   t outside [0, T):  sequence b is left untouched (nothing is written).
- * Only reference rows of kv are read, and only row t of a sequence whose
+ * Only reference rows of kv are read, and only the row of a sequence whose
  * new token is a reference is written; the other rows of kv may hold
  * anything.  Records of other positions are not touched.  Positions of
  * different sequences are independent (continuous batching).
- * Inputs:  kv [B][T][C] (in/out), the cache's stored rows, p->dtype;
+ * Inputs:  kv (in/out), the cache's stored references: with RKV_REF_INPUT
+ *          [B][T][C] in p->dtype, rows at positions; with RKV_REF_FP8 the
+ *          store [B][n_ref][C] of E4M3 bytes, row j the j-th reference (a
+ *          new reference is written there as its E4M3 bytes);
  *          kv_new [B][C], p->dtype, the new tokens (pre-RoPE K | V);
  *          pos [B] int32, device memory; w1, w2, w3 as in rkv_encode.
  * Outputs: ref_idx, codes, scale, zmin, z (optional) laid out as in
@@ -201,6 +224,15 @@ rkv_status rkv_append(const rkv_params* p, void* kv, const void* kv_new,
                       uint16_t* scale, uint16_t* zmin, float* z,
                       void* workspace, size_t workspace_bytes,
                       hipStream_t stream);
+
+/* The FP8 reference store of a prefix (p->ref_format == RKV_REF_FP8,
+ * [RKV] §2.4 last paragraph): ref_store[b][j][c] = E4M3 byte of
+ * kv[b][p_j][c] for the j-th reference position p_j of the schedule, the
+ * same values rkv_encode computes with.  kv [B][T][C] in p->dtype (only
+ * reference rows are read); ref_store [B][n_ref][C] bytes, n_ref =
+ * rkv_reference_positions(p, NULL, 0). */
+rkv_status rkv_store_refs(const rkv_params* p, const void* kv, uint8_t* ref_store,
+                          hipStream_t stream);
 
 /* The reference schedule of [RKV] §2.6 for p->T, ref_stride, ref_alpha,
  * n_sink, computed on the host (no device work): writes the first
@@ -230,7 +262,8 @@ typedef enum {
   RKV_STAGE_GATHER = 8,  /* gather-dequantise                               */
   RKV_STAGE_RESTORE = 9, /* restore: dequantise, decoder product, mean, RoPE */
   RKV_STAGE_APPEND = 10, /* decode-time append of one token per sequence    */
-  RKV_STAGE_COUNT = 11
+  RKV_STAGE_STORE = 11,  /* FP8 reference store (rkv_store_refs)            */
+  RKV_STAGE_COUNT = 12
 } rkv_stage;
 rkv_status rkv_profile_begin(uint32_t stage_mask);
 rkv_status rkv_profile_read(int32_t stage, double* total_ms, int64_t* launches);

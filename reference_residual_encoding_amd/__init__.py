@@ -44,17 +44,21 @@ EXPORTS = (
     "rkv_append_workspace_bytes",
     "rkv_append",
     "rkv_reference_positions",
+    "rkv_store_refs",
 )
 
 STAGES = ("pack", "norms", "dist", "merge", "proj", "swiglu", "w3", "quant", "gather", "restore",
-          "append")
-RKV_ABI_VERSION = 3
+          "append", "store")
+RKV_ABI_VERSION = 4
+RKV_REF_INPUT = 0
+RKV_REF_FP8 = 1
 
 
 class rkv_params(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("B", "T", "N", "D", "d_ff", "d_c", "k", "g", "b", "ref_stride")] + \
-               [("dtype", ctypes.c_int32), ("n_sink", ctypes.c_int32), ("ref_alpha", ctypes.c_double)]
+               [("dtype", ctypes.c_int32), ("n_sink", ctypes.c_int32), ("ref_alpha", ctypes.c_double),
+                ("ref_format", ctypes.c_int32)]
 
 
 class RkvError(RuntimeError):
@@ -108,6 +112,8 @@ def lib() -> ctypes.CDLL:
         L.rkv_append.restype = ctypes.c_int
         L.rkv_reference_positions.argtypes = [P, vp, i32]
         L.rkv_reference_positions.restype = i32
+        L.rkv_store_refs.argtypes = [P, vp, vp, vp]
+        L.rkv_store_refs.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -123,11 +129,15 @@ def _check(fn: str, status: int) -> int:
 
 
 def params(*, B, T, N, D, d_ff, d_c, k, g, b, ref_stride, dtype, n_sink=0,
-           ref_alpha=0.0) -> rkv_params:
-    """Build an rkv_params; dtype is RKV_F32/RKV_BF16 or "f32"/"bf16"."""
+           ref_alpha=0.0, ref_format=RKV_REF_INPUT) -> rkv_params:
+    """Build an rkv_params; dtype is RKV_F32/RKV_BF16 or "f32"/"bf16";
+    ref_format RKV_REF_INPUT/RKV_REF_FP8 or "input"/"fp8"."""
     if isinstance(dtype, str):
         dtype = {"f32": RKV_F32, "bf16": RKV_BF16}[dtype]
-    return rkv_params(B, T, N, D, d_ff, d_c, k, g, b, ref_stride, dtype, n_sink, ref_alpha)
+    if isinstance(ref_format, str):
+        ref_format = {"input": RKV_REF_INPUT, "fp8": RKV_REF_FP8}[ref_format]
+    return rkv_params(B, T, N, D, d_ff, d_c, k, g, b, ref_stride, dtype, n_sink, ref_alpha,
+                      ref_format)
 
 
 def _p(x) -> Optional[int]:
@@ -242,3 +252,8 @@ def rkv_reference_positions(p: rkv_params):
     buf = (ctypes.c_int32 * max(n, 1))()
     lib().rkv_reference_positions(ctypes.byref(p), ctypes.cast(buf, ctypes.c_void_p), n)
     return list(buf[:n])
+
+
+def rkv_store_refs(p: rkv_params, kv, ref_store, stream=None, *, check: bool = True) -> int:
+    st = lib().rkv_store_refs(ctypes.byref(p), _p(kv), _p(ref_store), _s(stream))
+    return _check("rkv_store_refs", st) if check else st

@@ -85,6 +85,8 @@ rkv_status check_params(const rkv_params* p) {
   if (!(p->ref_alpha >= 0.0 && p->ref_alpha <= 1.0e6))
     return fail(RKV_ERR_INVALID_ARG, "ref_alpha must be in [0, 1e6] (got %g)", p->ref_alpha);
   if (p->n_sink < 0) return fail(RKV_ERR_INVALID_ARG, "n_sink must be non-negative (got %d)", p->n_sink);
+  if (p->ref_format != RKV_REF_INPUT && p->ref_format != RKV_REF_FP8)
+    return fail(RKV_ERR_INVALID_ARG, "unknown ref_format %d", int(p->ref_format));
   const long long nref =
       (long long)rkv::schedule_for(p->T, p->ref_stride, p->ref_alpha, p->n_sink).rpos.size();
   if ((long long)p->B * nref * 2 * p->d_ff * 4 >= (1LL << 31))
@@ -94,7 +96,8 @@ rkv_status check_params(const rkv_params* p) {
 
 rkv::Shape shape_of(const rkv_params* p) {
   return rkv::make_shape(p->B, p->T, p->N, p->D, p->d_ff, p->d_c, p->k, p->g, p->b, p->ref_stride,
-                         p->dtype == RKV_BF16, p->ref_alpha, p->n_sink);
+                         p->dtype == RKV_BF16, p->ref_alpha, p->n_sink,
+                         p->ref_format == RKV_REF_FP8);
 }
 
 rkv_status device_status(hipError_t e, const char* where) {
@@ -371,6 +374,20 @@ rkv_status rkv_append(const rkv_params* p, void* kv, const void* kv_new, const i
             rkv::launch_append(sh, kv, kv_new, pos, w1, w2, w3, ref_idx, codes, scale, zmin, z,
                                static_cast<char*>(workspace), L, stream),
             "append");
+  return ok();
+}
+
+rkv_status rkv_store_refs(const rkv_params* p, const void* kv, uint8_t* ref_store,
+                          hipStream_t stream) {
+  rkv_status st = check_params(p);
+  if (st != RKV_OK) return st;
+  if (p->ref_format != RKV_REF_FP8)
+    return fail(RKV_ERR_INVALID_ARG, "rkv_store_refs needs ref_format RKV_REF_FP8");
+  RKV_NEED_PTR(kv);
+  RKV_NEED_PTR(ref_store);
+  const rkv::Shape sh = shape_of(p);
+  hipError_t e;
+  RKV_STAGE(RKV_STAGE_STORE, rkv::launch_store_refs(sh, kv, ref_store, stream), "store");
   return ok();
 }
 

@@ -31,34 +31,6 @@ namespace {
 constexpr int kAppCH = 8;          // pool references per distance workgroup (4 waves x 2)
 constexpr int kNoRef = 0x7fffffff;  // list padding (sorts after every reference)
 
-// Where the schedule puts its references: the closed form of a fixed
-// stride after the sinks, or the device copy of the host's positions.
-struct SchedView {
-  const int* rpos;  // nullptr: fixed stride
-  int nref, s0, n_sink;
-};
-
-__device__ __forceinline__ int ref_position(const SchedView& v, int j) {
-  if (v.rpos) return v.rpos[j];
-  return j < v.n_sink ? j : v.n_sink + (j - v.n_sink) * v.s0;
-}
-
-// Number of references before position t, and whether t is one.
-__device__ __forceinline__ int refs_before(const SchedView& v, int t, bool& is_ref) {
-  if (!v.rpos) {
-    const int u = t - v.n_sink;
-    is_ref = u < 0 || u % v.s0 == 0;
-    return u < 0 ? t : v.n_sink + (u + v.s0 - 1) / v.s0;
-  }
-  int lo = 0, hi = v.nref;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (v.rpos[mid] < t) lo = mid + 1; else hi = mid;
-  }
-  is_ref = lo < v.nref && v.rpos[lo] == t;
-  return lo;
-}
-
 template <typename E>
 __device__ __forceinline__ void load8(const E* p, float (&v)[8]) {
   if constexpr (sizeof(E) == 2) {
@@ -96,6 +68,31 @@ __device__ __forceinline__ float load1(const E* p) {
   else return *p;
 }
 
+// Stored reference j of sequence b: the row at its position in kv
+// [B][T][C] (input precision), or row j of the FP8 store [B][nref][C].
+template <typename E, bool FP8>
+struct RefRows {
+  const void* base;
+  SchedView sv;
+  int T, C;
+  __device__ __forceinline__ size_t row(int b, int j) const {
+    return FP8 ? size_t(b) * sv.nref + j : size_t(b) * T + ref_position(sv, j);
+  }
+  // 8 coordinates [o, o + 8) of stored row `r` (from row())
+  __device__ __forceinline__ void load(size_t r, int o, float (&v)[8]) const {
+    if constexpr (FP8) {
+      const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(base) + r * C + o);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = fp8_e4m3_to_f32((w.x >> (8 * e)) & 0xFFu);
+        v[4 + e] = fp8_e4m3_to_f32((w.y >> (8 * e)) & 0xFFu);
+      }
+    } else {
+      load8(static_cast<const E*>(base) + r * C + o, v);
+    }
+  }
+};
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
@@ -116,12 +113,13 @@ __device__ __forceinline__ int pool_of(const SchedView& v, const int32_t* pos, i
 // ---------------------------------------------------------------- distance
 // Workgroup (b, c): pool references j in [8c, 8c + 8) of sequence b, two
 // per wave with both rows' loads in flight; d = sum (x - y)^2 in fp32.
-template <typename E, int KL>
-__global__ __launch_bounds__(256) void k_app_dist(const E* __restrict__ kv,
+template <typename E, int KL, bool FP8>
+__global__ __launch_bounds__(256) void k_app_dist(const void* __restrict__ kv,
                                                   const E* __restrict__ kv_new,
                                                   const int32_t* __restrict__ pos, SchedView sv,
                                                   int T, int C, int n_lists,
                                                   float2* __restrict__ part) {
+  const RefRows<E, FP8> refs{kv, sv, T, C};
   const int b = blockIdx.x / n_lists, c = blockIdx.x % n_lists;
   int t;
   const int pool = pool_of(sv, pos, b, T, t);
@@ -132,15 +130,14 @@ __global__ __launch_bounds__(256) void k_app_dist(const E* __restrict__ kv,
   const int ja = j0 + 2 * wave, jb = ja + 1;
   const bool va = ja < pool, vb = jb < pool;
   const E* x = kv_new + size_t(b) * C;
-  const E* ya = kv + (size_t(b) * T + ref_position(sv, va ? ja : j0)) * C;
-  const E* yb = kv + (size_t(b) * T + ref_position(sv, vb ? jb : j0)) * C;
+  const size_t ya = refs.row(b, va ? ja : j0), yb = refs.row(b, vb ? jb : j0);
   float sa = 0.0f, sb = 0.0f;
 #pragma unroll 4
   for (int o = lane * 8; o < C; o += 512) {
     float xv[8], av[8], bv[8];
     load8(x + o, xv);
-    load8(ya + o, av);
-    load8(yb + o, bv);
+    refs.load(ya, o, av);
+    refs.load(yb, o, bv);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float da = xv[e] - av[e], db = xv[e] - bv[e];
@@ -171,9 +168,9 @@ __global__ __launch_bounds__(256) void k_app_dist(const E* __restrict__ kv,
 // Per sequence: store a reference token; else merge the distance lists,
 // write ref_idx (k_t positions ascending, -1 pads) and the fp32 mean of
 // the chosen rows.  act[b] = 1 when the token is to be encoded.
-template <typename E, int KL>
+template <typename E, int KL, bool FP8>
 __global__ __launch_bounds__(256) void k_app_select(
-    E* __restrict__ kv, const E* __restrict__ kv_new, const int32_t* __restrict__ pos,
+    void* __restrict__ kv, const E* __restrict__ kv_new, const int32_t* __restrict__ pos,
     SchedView sv, int T, int C, int k, int rec_bytes, int n_groups, int d_c, int n_lists,
     const float2* __restrict__ part, int32_t* __restrict__ ref_idx, uint8_t* __restrict__ codes,
     uint16_t* __restrict__ scale, uint16_t* __restrict__ zmin, float* __restrict__ z,
@@ -187,15 +184,25 @@ __global__ __launch_bounds__(256) void k_app_select(
   const size_t row = size_t(b) * T + t;
   bool is_ref;
   const int pool = refs_before(sv, t, is_ref);
+  const RefRows<E, FP8> refs{kv, sv, T, C};
   if (is_ref) {                                          // stored as it is ([RKV] §2.4)
     for (int o = tid * 8; o < C; o += 256 * 8) {
-      if constexpr (sizeof(E) == 2)
-        *reinterpret_cast<u32x4*>(kv + row * C + o) =
+      if constexpr (FP8) {                               // its E4M3 bytes, row j = pool
+        float v[8];
+        load8(kv_new + size_t(b) * C + o, v);
+        uint2 w;
+        w.x = f32_to_fp8_e4m3(v[0]) | (f32_to_fp8_e4m3(v[1]) << 8) |
+              (f32_to_fp8_e4m3(v[2]) << 16) | (f32_to_fp8_e4m3(v[3]) << 24);
+        w.y = f32_to_fp8_e4m3(v[4]) | (f32_to_fp8_e4m3(v[5]) << 8) |
+              (f32_to_fp8_e4m3(v[6]) << 16) | (f32_to_fp8_e4m3(v[7]) << 24);
+        *reinterpret_cast<uint2*>(static_cast<uint8_t*>(kv) + refs.row(b, pool) * C + o) = w;
+      } else if constexpr (sizeof(E) == 2) {
+        *reinterpret_cast<u32x4*>(static_cast<E*>(kv) + row * C + o) =
             *reinterpret_cast<const u32x4*>(kv_new + size_t(b) * C + o);
-      else {
-        reinterpret_cast<float4*>(kv + row * C + o)[0] =
+      } else {
+        reinterpret_cast<float4*>(static_cast<E*>(kv) + row * C + o)[0] =
             reinterpret_cast<const float4*>(kv_new + size_t(b) * C + o)[0];
-        reinterpret_cast<float4*>(kv + row * C + o)[1] =
+        reinterpret_cast<float4*>(static_cast<E*>(kv) + row * C + o)[1] =
             reinterpret_cast<const float4*>(kv_new + size_t(b) * C + o)[1];
       }
     }
@@ -244,9 +251,8 @@ __global__ __launch_bounds__(256) void k_app_select(
         const int tmp = jj[m]; jj[m] = jj[m - 1]; jj[m - 1] = tmp;
       }
     for (int e = 0; e < k; ++e) {
-      const int p = e < kt ? ref_position(sv, jj[e]) : -1;
-      ref_idx[row * k + e] = p;
-      if (e < KL) sel[e] = p;
+      ref_idx[row * k + e] = e < kt ? ref_position(sv, jj[e]) : -1;
+      if (e < KL) sel[e] = e < kt ? int(refs.row(b, jj[e])) : -1;   // stored row
     }
     act[b] = 1;
   }
@@ -256,7 +262,7 @@ __global__ __launch_bounds__(256) void k_app_select(
     float v[KL][8];
 #pragma unroll
     for (int i = 0; i < KL; ++i)                         // every row's loads in flight together
-      load8(kv + (size_t(b) * T + sel[min(i, kt - 1)]) * C + o, v[i]);
+      refs.load(size_t(sel[min(i, kt - 1)]), o, v[i]);
     float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < KL; ++i)
@@ -460,22 +466,24 @@ hipError_t launch_append(const Shape& sh, void* kv, const void* kv_new, const in
   const int cb = sh.g <= 32 || sh.b == kIdentityBits ? 32 : 64;   // a block holds whole groups
   const int n_dist = sh.B * L.n_lists;
 
-#define RKV_APP(E, KL)                                                                            \
-  k_app_dist<E, KL><<<n_dist, 256, 0, st>>>(static_cast<const E*>(kv),                           \
-                                            static_cast<const E*>(kv_new), pos, sv, sh.T, sh.C,   \
-                                            L.n_lists, part);                                     \
-  k_app_select<E, KL><<<sh.B, 256, 0, st>>>(static_cast<E*>(kv), static_cast<const E*>(kv_new),  \
-                                            pos, sv, sh.T, sh.C, sh.k, rec_bytes, n_groups,       \
-                                            sh.d_c, L.n_lists, part, ref_idx, codes, scale, zmin, \
-                                            z, mean, act);                                        \
+#define RKV_APP(E, KL, F8)                                                                        \
+  k_app_dist<E, KL, F8><<<n_dist, 256, 0, st>>>(kv, static_cast<const E*>(kv_new), pos, sv, sh.T, \
+                                                sh.C, L.n_lists, part);                          \
+  k_app_select<E, KL, F8><<<sh.B, 256, 0, st>>>(kv, static_cast<const E*>(kv_new), pos, sv, sh.T, \
+                                                sh.C, sh.k, rec_bytes, n_groups, sh.d_c,         \
+                                                L.n_lists, part, ref_idx, codes, scale, zmin, z, \
+                                                mean, act);                                      \
   k_app_proj<E><<<sh.d_ff / 4, 256, 0, st>>>(static_cast<const E*>(kv_new), mean, act,           \
                                              static_cast<const E*>(w1), static_cast<const E*>(w2), \
                                              sh.B, sh.C, sh.d_ff, dh)
+#define RKV_APPK(E, F8) \
+  if (sh.kl == 4) { RKV_APP(E, 4, F8); } else { RKV_APP(E, 8, F8); }
   if (sh.bf16) {
-    if (sh.kl == 4) { RKV_APP(uint16_t, 4); } else { RKV_APP(uint16_t, 8); }
+    if (sh.ref_fp8) { RKV_APPK(uint16_t, true) } else { RKV_APPK(uint16_t, false) }
   } else {
-    if (sh.kl == 4) { RKV_APP(float, 4); } else { RKV_APP(float, 8); }
+    if (sh.ref_fp8) { RKV_APPK(float, true) } else { RKV_APPK(float, false) }
   }
+#undef RKV_APPK
 #undef RKV_APP
 
   const int n_w3 = sh.B * (sh.d_c / cb);

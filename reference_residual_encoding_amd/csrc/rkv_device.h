@@ -44,6 +44,60 @@ __device__ __forceinline__ uint32_t bf16_hi_lo(float x) {
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
 
+// FP8 reference storage: OCP E4M3 (bias 7, 3 mantissa bits, subnormals
+// k * 2^-9, largest finite 448, no infinities), round to nearest even,
+// saturating at +-448.  Every E4M3 value is exact in bf16 and fp32.
+__device__ __forceinline__ uint32_t f32_to_fp8_e4m3(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fabsf(x);
+  uint32_t r;
+  if (!(a < 448.0f)) {
+    r = a != a ? 0x7Fu : 0x7Eu;                          // NaN stays NaN, the rest saturates
+  } else if (a < 0.015625f) {
+    r = uint32_t(rintf(a * 512.0f));                     // k * 2^-9; k = 8 is 2^-6 (field 1)
+  } else {
+    const uint32_t ua = __float_as_uint(a);              // 3 mantissa bits, ties to even
+    r = ((ua + 0x7FFFFu + ((ua >> 20) & 1u)) >> 20) - (120u << 3);
+    r = r > 0x7Eu ? 0x7Eu : r;                           // rounding past 448 saturates
+  }
+  return sign | r;
+}
+__device__ __forceinline__ float fp8_e4m3_to_f32(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  const float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : float(m) * 0.001953125f;
+  return (b & 0x80u) ? -v : v;
+}
+__device__ __forceinline__ float fp8_round(float x) { return fp8_e4m3_to_f32(f32_to_fp8_e4m3(x)); }
+
+// Where the schedule ([RKV] §2.6) puts its references: the closed form of a
+// fixed stride after the sinks, or a device copy of the host's positions.
+struct SchedView {
+  const int* rpos;  // nullptr: fixed stride
+  int nref, s0, n_sink;
+};
+
+__device__ __forceinline__ int ref_position(const SchedView& v, int j) {
+  if (v.rpos) return v.rpos[j];
+  return j < v.n_sink ? j : v.n_sink + (j - v.n_sink) * v.s0;
+}
+
+// Number of references before position t (the index of t when t is one),
+// and whether t is one.
+__device__ __forceinline__ int refs_before(const SchedView& v, int t, bool& is_ref) {
+  if (!v.rpos) {
+    const int u = t - v.n_sink;
+    is_ref = u < 0 || u % v.s0 == 0;
+    return u < 0 ? t : v.n_sink + (u + v.s0 - 1) / v.s0;
+  }
+  int lo = 0, hi = v.nref;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (v.rpos[mid] < t) lo = mid + 1; else hi = mid;
+  }
+  is_ref = lo < v.nref && v.rpos[lo] == t;
+  return lo;
+}
+
 // Keep the KL smallest (d, j) pairs in ascending (d, j) order, for
 // candidates that arrive in increasing j: a newcomer then goes after every
 // kept pair of equal d, so the strict comparison d < d_i decides alone.

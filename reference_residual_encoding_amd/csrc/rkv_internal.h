@@ -34,6 +34,7 @@ struct Shape {
   int k3;        // contraction length of the W3 product (2*d_ff bf16 hi/lo, d_ff fp32)
   int n_sink;
   double alpha;
+  bool ref_fp8;           // references kept as FP8 E4M3 (compact store [B][nref][C])
   const Schedule* sched;  // host copy of the schedule (planning the distance items)
 };
 
@@ -43,7 +44,7 @@ struct Workspace {
 };
 
 Shape make_shape(int B, int T, int N, int D, int d_ff, int d_c, int k, int g, int b, int s,
-                 bool bf16, double alpha, int n_sink);
+                 bool bf16, double alpha, int n_sink, bool ref_fp8);
 // Device schedule tables in the workspace: reference positions, non-reference
 // positions, and per position t: ~j for the j-th reference, else the
 // non-reference index q.
@@ -51,6 +52,8 @@ hipError_t launch_schedule(const Shape& sh, char* ws, const Workspace& L, hipStr
 // The reference positions alone, rpos[nref], copied from the host schedule
 // through kernel arguments (no host buffer).
 hipError_t launch_ref_positions(const Shape& sh, int* rpos, hipStream_t st);
+// FP8 reference store [B][nref][C] of the prefix kv.
+hipError_t launch_store_refs(const Shape& sh, const void* kv, uint8_t* store, hipStream_t st);
 Workspace plan_workspace(const Shape& sh);
 
 // Each launcher enqueues on `st` and returns hipGetLastError().
@@ -80,7 +83,8 @@ hipError_t launch_gather(const uint8_t* codes, const uint16_t* scale, const uint
 // Restore ([RKV] §2.5): workspace of the decoder product for n_idx rows.
 struct RestoreWorkspace {
   int kr;               // contraction length (2*d_c bf16 hi/lo pairs, d_c fp32)
-  size_t wdp, zt, total;
+  bool tables;          // schedule tables present (FP8 store of a dynamic schedule)
+  size_t wdp, zt, rpos, nrp, tab, total;
 };
 RestoreWorkspace plan_restore(const Shape& sh, int64_t n_idx);
 hipError_t launch_restore(const Shape& sh, int N, int D, const uint8_t* codes,

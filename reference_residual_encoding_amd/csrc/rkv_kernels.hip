@@ -193,7 +193,7 @@ __global__ __launch_bounds__(256) void k_ref_gather(const char* __restrict__ kv,
                                                     uint8_t* __restrict__ codes, int cb,
                                                     uint16_t* __restrict__ scale,
                                                     uint16_t* __restrict__ zmin, int ng,
-                                                    float* __restrict__ z, int d_c) {
+                                                    float* __restrict__ z, int d_c, int fp8) {
   const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (wid >= B * nref) return;
@@ -212,7 +212,20 @@ __global__ __launch_bounds__(256) void k_ref_gather(const char* __restrict__ kv,
   char* dst = refs + size_t(wid) * rowb;
   float acc = 0.0f;
   for (size_t o = size_t(lane) * 16; o < rowb; o += 64 * 16) {
-    const uint4 w = *reinterpret_cast<const uint4*>(src + o);
+    uint4 w = *reinterpret_cast<const uint4*>(src + o);
+    if (fp8) {                                           // the values the FP8 store holds
+      uint32_t* u = reinterpret_cast<uint32_t*>(&w);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (sizeof(E) == 2) {
+          const float lo = fp8_round(__uint_as_float(u[e] << 16));
+          const float hi = fp8_round(__uint_as_float(u[e] & 0xFFFF0000u));
+          u[e] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);  // exact in bf16
+        } else {
+          u[e] = __float_as_uint(fp8_round(__uint_as_float(u[e])));
+        }
+      }
+    }
     *reinterpret_cast<uint4*>(dst + o) = w;
     const uint32_t u[4] = {w.x, w.y, w.z, w.w};
     if constexpr (sizeof(E) == 2) {
@@ -233,6 +246,48 @@ __global__ __launch_bounds__(256) void k_ref_gather(const char* __restrict__ kv,
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if (lane == 0) ysq[wid] = acc;
+}
+
+// FP8 reference store ([RKV] §2.4 last paragraph): store[b][j][c] = E4M3 of
+// kv[b][p_j][c], one wave per reference row, 8 coordinates per lane and
+// step.  Positions come from the closed form of a fixed stride (sv), or,
+// with use_chunk, from the chunk of host positions in the kernel arguments
+// (references chunk.first .. chunk.first + chunk.count - 1).
+template <typename E>
+__global__ __launch_bounds__(256) void k_ref_store(const E* __restrict__ kv, int B, int T, int C,
+                                                   SchedView sv, PosChunk chunk, int use_chunk,
+                                                   int nref, uint8_t* __restrict__ store) {
+  const int rows = use_chunk ? chunk.count : nref;
+  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (wid >= B * rows) return;
+  const int b = wid / rows, jj = wid % rows;
+  const int j = use_chunk ? chunk.first + jj : jj;
+  const int t = use_chunk ? chunk.pos[jj] : ref_position(sv, j);
+  const E* src = kv + (size_t(b) * T + t) * C;
+  uint8_t* dst = store + (size_t(b) * nref + j) * C;
+  for (int o = lane * 8; o < C; o += 512) {
+    float v[8];
+    if constexpr (sizeof(E) == 2) {
+      const uint4 w = *reinterpret_cast<const uint4*>(src + o);
+      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] = __uint_as_float(u[e] << 16);
+        v[2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
+      }
+    } else {
+      const float4 a0 = reinterpret_cast<const float4*>(src + o)[0];
+      const float4 a1 = reinterpret_cast<const float4*>(src + o)[1];
+      v[0] = a0.x; v[1] = a0.y; v[2] = a0.z; v[3] = a0.w;
+      v[4] = a1.x; v[5] = a1.y; v[6] = a1.z; v[7] = a1.w;
+    }
+    uint2 out;
+    out.x = f32_to_fp8_e4m3(v[0]) | (f32_to_fp8_e4m3(v[1]) << 8) | (f32_to_fp8_e4m3(v[2]) << 16) |
+            (f32_to_fp8_e4m3(v[3]) << 24);
+    out.y = f32_to_fp8_e4m3(v[4]) | (f32_to_fp8_e4m3(v[5]) << 8) | (f32_to_fp8_e4m3(v[6]) << 16) |
+            (f32_to_fp8_e4m3(v[7]) << 24);
+    *reinterpret_cast<uint2*>(dst + o) = out;
+  }
 }
 
 // ------------------------------------------------------------------ retrieval
@@ -767,12 +822,15 @@ __global__ __launch_bounds__(256) void k_restore_prep(const uint8_t* __restrict_
 
 // One workgroup: BM selected tokens x BN columns of KV^.  D divides BN, so a
 // tile holds whole heads and every rotation partner (d +- D/2) is in it.
-template <typename E, int KL>
+// FP8: the stored references are the E4M3 store [B][nref][C]; row of a
+// reference position p = its index j in the schedule (closed form, or
+// ~tab[p] from the schedule tables).
+template <typename E, int KL, bool FP8>
 __global__ __launch_bounds__(RsCfg<E>::kThreads) void k_restore(
     const char* __restrict__ zt, const char* __restrict__ wdp, int K, const int32_t* __restrict__ idx,
     int n_idx, int64_t total_rows, int T, int k, const int32_t* __restrict__ ref_idx,
     const char* __restrict__ kv, int C, int ND, int D, float theta, void* __restrict__ out,
-    int out_bf16) {
+    int out_bf16, SchedView sv, const int* __restrict__ tab) {
   using CF = RsCfg<E>;
   constexpr int BM = CF::BM, BN = CF::BN, WGM = CF::WGM, WGN = CF::WGN, NT = CF::kThreads;
   static_assert(WGM == 2, "the epilogue stages one wave-row (half the tile) at a time");
@@ -800,14 +858,23 @@ __global__ __launch_bounds__(RsCfg<E>::kThreads) void k_restore(
       if (fl >= 0 && fl < total_rows) {
         const int b = int(fl / T), t = int(fl % T);
         pos = t;
+        auto store_row = [&](int p) {
+          if constexpr (FP8) {
+            bool is_ref;
+            const int j = tab ? ~tab[p] : refs_before(sv, p, is_ref);
+            return b * sv.nref + min(max(j, 0), sv.nref - 1);   // records from rkv_encode: in range
+          } else {
+            return b * T + p;
+          }
+        };
         if (ref_idx[fl * k] < 0) {                       // a reference: its own stored row
-          rows[0] = int(fl);
+          rows[0] = store_row(t);
           cnt = 1;
         } else {
 #pragma unroll
           for (int q = 0; q < KL; ++q) {
             const int p = q < k ? ref_idx[fl * k + q] : -1;
-            if (p >= 0) { rows[q] = b * T + p; ++cnt; }
+            if (p >= 0) { rows[q] = store_row(p); ++cnt; }
           }
         }
       }
@@ -827,7 +894,7 @@ __global__ __launch_bounds__(RsCfg<E>::kThreads) void k_restore(
 
   float* tile = reinterpret_cast<float*>(lds);
   constexpr int kV = BN / 8;                             // 8-column vectors per row
-  const size_t kvrow = size_t(C) * sizeof(E);
+  const size_t kvrow = size_t(C) * (FP8 ? 1 : sizeof(E));
   for (int half = 0; half < 2; ++half) {
     acc_to_lds<BM, BN, WGM, WGN>(acc, tile, LD, half);
     __syncthreads();
@@ -839,9 +906,16 @@ __global__ __launch_bounds__(RsCfg<E>::kThreads) void k_restore(
 #pragma unroll
       for (int q = 0; q < KL; ++q) {
         const int row = rows_lds[rt * KL + q];
-        const char* src = kv + size_t(max(row, 0)) * kvrow + size_t(col) * sizeof(E);
+        const char* src = kv + size_t(max(row, 0)) * kvrow + size_t(col) * (FP8 ? 1 : sizeof(E));
         float v[8];
-        if constexpr (sizeof(E) == 2) {
+        if constexpr (FP8) {
+          const uint2 w = *reinterpret_cast<const uint2*>(src);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[e] = fp8_e4m3_to_f32((w.x >> (8 * e)) & 0xFFu);
+            v[4 + e] = fp8_e4m3_to_f32((w.y >> (8 * e)) & 0xFFu);
+          }
+        } else if constexpr (sizeof(E) == 2) {
           const u32x4 w = *reinterpret_cast<const u32x4*>(src);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -975,11 +1049,11 @@ const Schedule& schedule_for(int T, int s0, double alpha, int n_sink) {
 }
 
 Shape make_shape(int B, int T, int N, int D, int d_ff, int d_c, int k, int g, int b, int s,
-                 bool bf16, double alpha, int n_sink) {
+                 bool bf16, double alpha, int n_sink, bool ref_fp8) {
   Shape sh{};
   sh.B = B; sh.T = T; sh.C = 2 * N * D; sh.d_ff = d_ff; sh.d_c = d_c; sh.k = k;
   sh.g = g; sh.b = b; sh.s = s; sh.bf16 = bf16;
-  sh.alpha = alpha; sh.n_sink = n_sink;
+  sh.alpha = alpha; sh.n_sink = n_sink; sh.ref_fp8 = ref_fp8;
   sh.esize = bf16 ? 2 : 4;
   sh.sched = &schedule_for(T, s, alpha, n_sink);
   sh.nref = int(sh.sched->rpos.size());
@@ -1027,6 +1101,35 @@ hipError_t launch_pack_weights(const Shape& sh, const void* w1, const void* w2, 
   return hipGetLastError();
 }
 
+hipError_t launch_store_refs(const Shape& sh, const void* kv, uint8_t* store, hipStream_t st) {
+  const SchedView fixed{nullptr, sh.nref, sh.s, sh.n_sink};
+  auto go = [&](const PosChunk& c, int use_chunk, int rows) {
+    const int grid = cdiv(long(sh.B) * rows, 4);
+    if (sh.bf16)
+      k_ref_store<uint16_t><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(kv), sh.B, sh.T,
+                                                  sh.C, fixed, c, use_chunk, sh.nref, store);
+    else
+      k_ref_store<float><<<grid, 256, 0, st>>>(static_cast<const float*>(kv), sh.B, sh.T, sh.C,
+                                               fixed, c, use_chunk, sh.nref, store);
+  };
+  if (sh.alpha == 0.0) {
+    PosChunk none;
+    none.first = 0;
+    none.count = 0;
+    go(none, 0, sh.nref);
+    return hipGetLastError();
+  }
+  // positions of a dynamic schedule ride in the kernel arguments, 960 at a time
+  for (int first = 0; first < sh.nref; first += kPosChunk) {
+    PosChunk c;
+    c.first = first;
+    c.count = std::min(kPosChunk, sh.nref - first);
+    for (int i = 0; i < c.count; ++i) c.pos[i] = sh.sched->rpos[size_t(first) + i];
+    go(c, 1, c.count);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_ref_positions(const Shape& sh, int* rpos, hipStream_t st) {
   for (int first = 0; first < sh.nref; first += kPosChunk) {
     PosChunk c;
@@ -1064,11 +1167,11 @@ hipError_t launch_ref_norms(const Shape& sh, const void* kv, char* ws, const Wor
   if (sh.bf16)
     k_ref_gather<uint16_t><<<cdiv(rows, 4), 256, 0, st>>>(p, sh.B, sh.T, sh.C, rpos, sh.nref,
                                                           ws + L.refs, y, ref_idx, sh.k, codes, cb,
-                                                          scale, zmin, ng, z, sh.d_c);
+                                                          scale, zmin, ng, z, sh.d_c, sh.ref_fp8);
   else
     k_ref_gather<float><<<cdiv(rows, 4), 256, 0, st>>>(p, sh.B, sh.T, sh.C, rpos, sh.nref,
                                                        ws + L.refs, y, ref_idx, sh.k, codes, cb,
-                                                       scale, zmin, ng, z, sh.d_c);
+                                                       scale, zmin, ng, z, sh.d_c, sh.ref_fp8);
   return hipGetLastError();
 }
 
@@ -1224,6 +1327,12 @@ RestoreWorkspace plan_restore(const Shape& sh, int64_t n_idx) {
   L.kr = sh.bf16 ? 2 * sh.d_c : sh.d_c;
   L.wdp = take(size_t(sh.C) * L.kr * sh.esize);
   L.zt = take(size_t(n_idx) * sh.d_c * 4);
+  L.tables = sh.ref_fp8 && sh.alpha != 0.0;        // FP8 rows of a dynamic schedule: tab[p]
+  if (L.tables) {
+    L.rpos = take(size_t(sh.nref) * 4);
+    L.nrp = take(size_t(sh.nr) * 4);
+    L.tab = take(size_t(sh.T) * 4);
+  }
   L.total = off;
   return L;
 }
@@ -1257,12 +1366,25 @@ hipError_t launch_restore(const Shape& sh, int N, int D, const uint8_t* codes,
   }
 #undef RKV_RP
   const auto* kvp = static_cast<const char*>(kv);
-#define RKV_RS(E, KL)                                                                            \
-  k_restore<E, KL><<<cdiv(n_idx, RsCfg<E>::BM) * cdiv(sh.C, RsCfg<E>::BN), RsCfg<E>::kThreads, 0, \
-                     st>>>(ws + L.zt, ws + L.wdp, L.kr, idx, n_idx, total, sh.T, sh.k,            \
-                           ref_idx, kvp, sh.C, N * D, D, theta, out, out_bf16 ? 1 : 0)
-  if (sh.bf16) { if (sh.kl == 4) RKV_RS(uint16_t, 4); else RKV_RS(uint16_t, 8); }
-  else { if (sh.kl == 4) RKV_RS(float, 4); else RKV_RS(float, 8); }
+  const SchedView sv{nullptr, sh.nref, sh.s, sh.n_sink};
+  const int* tab = nullptr;
+  if (L.tables) {
+    Workspace T{};
+    T.rpos = L.rpos; T.nrp = L.nrp; T.tab = L.tab;
+    const hipError_t e = launch_schedule(sh, ws, T, st);
+    if (e != hipSuccess) return e;
+    tab = reinterpret_cast<const int*>(ws + L.tab);
+  }
+#define RKV_RS(E, KL, F8)                                                                        \
+  k_restore<E, KL, F8><<<cdiv(n_idx, RsCfg<E>::BM) * cdiv(sh.C, RsCfg<E>::BN), RsCfg<E>::kThreads, \
+                         0, st>>>(ws + L.zt, ws + L.wdp, L.kr, idx, n_idx, total, sh.T, sh.k,     \
+                                  ref_idx, kvp, sh.C, N * D, D, theta, out, out_bf16 ? 1 : 0, sv, \
+                                  tab)
+#define RKV_RSK(E, F8) \
+  if (sh.kl == 4) RKV_RS(E, 4, F8); else RKV_RS(E, 8, F8)
+  if (sh.bf16) { if (sh.ref_fp8) { RKV_RSK(uint16_t, true); } else { RKV_RSK(uint16_t, false); } }
+  else { if (sh.ref_fp8) { RKV_RSK(float, true); } else { RKV_RSK(float, false); } }
+#undef RKV_RSK
 #undef RKV_RS
   return hipGetLastError();
 }

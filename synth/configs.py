@@ -37,6 +37,7 @@ class RkvConfig:
     rope_theta: float = 10000.0  # RoPE base of the model whose keys are restored
     alpha: float = 0.0         # reference schedule growth ([RKV] §2.6); 0 = fixed stride
     n_sink: int = 0            # sink tokens, stored as references before the schedule starts
+    ref_fp8: bool = False      # references stored as FP8 E4M3 ([RKV] §2.4 last paragraph)
     # multimodal recipe only
     mm_blocks: int = 0
     mm_block_len: int = 0

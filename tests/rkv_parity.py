@@ -38,7 +38,7 @@ DEQ_REL = 1e-2
 def params_of(cfg):
     return R.params(B=cfg.B, T=cfg.T, N=cfg.N, D=cfg.D, d_ff=cfg.d_ff, d_c=cfg.d_c, k=cfg.k,
                     g=cfg.g, b=cfg.b, ref_stride=cfg.stride, dtype=cfg.dtype, n_sink=cfg.n_sink,
-                    ref_alpha=cfg.alpha)
+                    ref_alpha=cfg.alpha, ref_format="fp8" if cfg.ref_fp8 else "input")
 
 
 def to_device(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
@@ -59,6 +59,20 @@ def run_encode(w, device="cuda", with_z=True):
                 scale=out.scale.cpu().numpy(), zmin=out.zmin.cpu().numpy(),
                 z=out.z.cpu().numpy() if with_z else None)
     return p, out, host, (kv, w1, w2, w3)
+
+
+def fp8_store(cfg, kv_bits: np.ndarray) -> np.ndarray:
+    """The FP8 reference store [B][nref][C] of a prefix, built on the host
+    from the format (the oracle's E4M3 rounding)."""
+    refs = O.reference_schedule(cfg.T, cfg.stride, cfg.alpha, cfg.n_sink)
+    kv = kv_bits_to_f64(cfg, kv_bits)
+    return O.fp8_e4m3_bits(kv[:, refs])
+
+
+def kv_bits_to_f64(cfg, kv_bits: np.ndarray) -> np.ndarray:
+    if cfg.dtype == "bf16":
+        return (kv_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return kv_bits.astype(np.float64)
 
 
 def ref_mask_of(cfg) -> np.ndarray:
@@ -103,7 +117,9 @@ def compare_tokens(w, host, positions_by_seq, gathered=None, log=print):
     for bi, pos in positions_by_seq.items():
         kvb = kv32[bi].astype(np.float64)
         orc = O.encode_tokens(kvb, W1, W2, W3, pos, k=k, g=g, b=bb, s=s, alpha=cfg.alpha,
-                              n_sink=cfg.n_sink)
+                              n_sink=cfg.n_sink, ref_fp8=cfg.ref_fp8)
+        stored = O.stored_references(kvb, O.reference_schedule(cfg.T, s, cfg.alpha, cfg.n_sink),
+                                     cfg.ref_fp8)
         g_ref = host["ref_idx"][bi, pos]
         z_orc = orc["z"].copy()
         for i, t in enumerate(pos):
@@ -126,9 +142,9 @@ def compare_tokens(w, host, positions_by_seq, gathered=None, log=print):
                 dk, dk1 = orc["d_diag"][i, k_t - 1], orc["d_diag"][i, k_t]
                 excused = np.isfinite(dk1) and abs(dk1 - dk) <= TIE_REL * abs(dk)
                 assert excused, f"seq {bi} token {t}: GPU set {gs} vs oracle {o_set} (d_k={dk}, d_k+1={dk1})"
-                d_gpu = O.squared_l2(kvb[t], kvb[gs[:k_t]])
+                d_gpu = O.squared_l2(kvb[t], stored[gs[:k_t]])
                 assert np.all(d_gpu <= dk * (1 + TIE_REL)), (bi, t, d_gpu, dk)
-                z_orc[i] = O.residual_latent(kvb[t], O.reference_mean(kvb, gs[:k_t]), W1, W2, W3)
+                z_orc[i] = O.residual_latent(kvb[t], O.reference_mean(stored, gs[:k_t]), W1, W2, W3)
                 n_excused += 1
         q_orc, dh_orc, mh_orc = O.quantize(z_orc, g, bb)
         q_orc[orc["is_ref"]] = 0

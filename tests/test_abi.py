@@ -38,7 +38,7 @@ def test_status_strings():
 def _p(cfg, **kw):
     d = dict(B=cfg.B, T=cfg.T, N=cfg.N, D=cfg.D, d_ff=cfg.d_ff, d_c=cfg.d_c, k=cfg.k, g=cfg.g,
              b=cfg.b, ref_stride=cfg.stride, dtype=cfg.dtype, n_sink=cfg.n_sink,
-             ref_alpha=cfg.alpha)
+             ref_alpha=cfg.alpha, ref_format="fp8" if cfg.ref_fp8 else "input")
     d.update(kw)
     return R.params(**d)
 
@@ -235,3 +235,15 @@ def test_identity_mode_validation():
     # scale / zmin may be NULL in identity mode: validation then stops at the next pointer
     assert _encode(p16, scale=None, zmin=None, workspace=None) == R.RKV_ERR_INVALID_ARG
     assert "workspace" in R.rkv_last_error()
+
+
+def test_fp8_reference_format_validation():
+    """ref_format selects how the cache keeps its references ([RKV] §2.4)."""
+    assert R.rkv_encode_workspace_bytes(_p(LLAMA32K, ref_format="fp8")) > 0
+    assert _encode(_p(LLAMA32K, ref_format=7)) == R.RKV_ERR_INVALID_ARG
+    st = R.rkv_store_refs(_p(LLAMA32K), FAKE, FAKE, None, check=False)
+    assert st == R.RKV_ERR_INVALID_ARG and "RKV_REF_FP8" in R.rkv_last_error()
+    assert R.rkv_store_refs(_p(LLAMA32K, ref_format="fp8"), FAKE, None, None,
+                            check=False) == R.RKV_ERR_INVALID_ARG
+    assert R.rkv_store_refs(_p(LLAMA32K, ref_format="fp8"), FAKE_MIS, FAKE, None,
+                            check=False) == R.RKV_ERR_INVALID_ARG

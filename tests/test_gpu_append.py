@@ -36,13 +36,22 @@ class Cache:
         self.p = P.params_of(cfg)
         n = cfg.B * cfg.T
         self.ref_mask = P.ref_mask_of(cfg)
-        kv = np.array(w.kv, copy=True)
-        nan = np.uint16(0x7FC0) if cfg.dtype == "bf16" else np.float32(np.nan)
-        kv[:, ~self.ref_mask] = nan
-        if not prefill_refs:
-            kv[:, self.ref_mask] = nan
-        self.expected_kv = kv                     # host copy of what the cache must hold
-        self.kv = P.to_device(kv, cfg.dtype, device)
+        if cfg.ref_fp8:
+            # the E4M3 store [B][nref][C]; 0x7F (NaN) where nothing is stored yet
+            self.store_bytes = P.fp8_store(cfg, w.kv)
+            kv = np.full_like(self.store_bytes, 0x7F)
+            if prefill_refs:
+                kv[:] = self.store_bytes
+            self.expected_kv = kv
+            self.kv = torch.from_numpy(kv.copy()).to(device)
+        else:
+            kv = np.array(w.kv, copy=True)
+            nan = np.uint16(0x7FC0) if cfg.dtype == "bf16" else np.float32(np.nan)
+            kv[:, ~self.ref_mask] = nan
+            if not prefill_refs:
+                kv[:, self.ref_mask] = nan
+            self.expected_kv = kv                 # host copy of what the cache must hold
+            self.kv = P.to_device(kv, cfg.dtype, device)
         self.w1, self.w2, self.w3 = (P.to_device(x, cfg.dtype, device) for x in (w.w1, w.w2, w.w3))
         u8 = lambda nbytes: torch.full((nbytes,), SENTINEL, dtype=torch.uint8, device=device)
         self.ref_idx = u8(n * cfg.k * 4).view(torch.int32).view(cfg.B, cfg.T, cfg.k)
@@ -65,7 +74,10 @@ class Cache:
             if 0 <= t < cfg.T:
                 rows[b] = self.w.kv[b, t]
                 self.appended[b, t] = True
-                if self.ref_mask[t]:
+                if self.ref_mask[t] and cfg.ref_fp8:
+                    j = int(np.cumsum(self.ref_mask)[t]) - 1
+                    self.expected_kv[b, j] = self.store_bytes[b, j]
+                elif self.ref_mask[t]:
                     self.expected_kv[b, t] = self.w.kv[b, t]
         kv_new = P.to_device(rows, cfg.dtype)
         d_pos = torch.from_numpy(pos.astype(np.int32)).cuda()
@@ -88,7 +100,10 @@ class Cache:
         assert (h["ref_idx"].view(np.uint8).reshape(cfg.B, cfg.T, -1)[untouched] == SENTINEL).all()
         assert (h["scale"].view(np.uint8).reshape(cfg.B, cfg.T, -1)[untouched] == SENTINEL).all()
         kv = self.kv.cpu()
-        kv = kv.view(torch.int16).numpy().view(np.uint16) if cfg.dtype == "bf16" else kv.numpy()
+        if cfg.ref_fp8:
+            kv = kv.numpy()
+        else:
+            kv = kv.view(torch.int16).numpy().view(np.uint16) if cfg.dtype == "bf16" else kv.numpy()
         assert np.array_equal(kv.view(np.uint8), self.expected_kv.view(np.uint8)), \
             f"{name}: the cache's kv rows differ from the appended references"
         return summary
@@ -98,7 +113,9 @@ def _make(cfg, prefill):
     return Cache(generate(cfg), prefill)
 
 
-@pytest.mark.parametrize("cfg", [TINY, TINY_DYN], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [TINY, TINY_DYN,
+                                 TINY_DYN.with_(name="tiny_f32_dynamic_fp8ref", ref_fp8=True)],
+                         ids=lambda c: c.name)
 def test_append_every_position_in_order(cfg):
     """An empty cache (all NaN) filled token by token reaches the same records
     as the oracle's encode of the prefix; reference rows land in the cache."""
@@ -116,7 +133,8 @@ RAGGED_F32 = LLAMA8K.with_(name="append_ragged_f32_k8_g64", B=2, T=700, N=1, D=6
 
 
 @pytest.mark.parametrize("cfg", [RAGGED_BF16, RAGGED_F32,
-                                 RAGGED_BF16.with_(name="append_ragged_bf16_identity", b=16)],
+                                 RAGGED_BF16.with_(name="append_ragged_bf16_identity", b=16),
+                                 RAGGED_BF16.with_(name="append_ragged_bf16_fp8ref", ref_fp8=True)],
                          ids=lambda c: c.name)
 def test_append_independent_positions_per_sequence(cfg):
     """Continuous batching: every call appends a different position in each
@@ -135,7 +153,9 @@ def test_append_independent_positions_per_sequence(cfg):
     c.check(cfg.name)
 
 
-@pytest.mark.parametrize("cfg", [LLAMA8K.with_(B=2), LLAMA8K_DYN], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [LLAMA8K.with_(B=2), LLAMA8K_DYN,
+                                 LLAMA8K.with_(name="llama8b_T8k_fp8ref", B=2, ref_fp8=True)],
+                         ids=lambda c: c.name)
 def test_append_full_size_sampled(cfg):
     """The Llama layer shape at 8k context: sampled positions (warm-up, tail,
     random), one per sequence per call."""

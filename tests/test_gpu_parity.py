@@ -135,6 +135,47 @@ def test_identity_mode_sampled():
     test_full_size_configs_sampled(LLAMA8K.with_(name="llama8b_T8k_identity", b=16), 400)
 
 
+# FP8 references ([RKV] §2.4 last paragraph; §2.5: the encoder uses them as
+# stored): retrieval and the mean read their E4M3 values.
+FP8 = [
+    TINY.with_(name="tiny_f32_fp8ref", ref_fp8=True),
+    RAGGED[0].with_(name="ragged_bf16_fp8ref_dynamic", ref_fp8=True, alpha=0.01, n_sink=3),
+    RAGGED[2].with_(name="ragged_bf16_fp8ref_k8_identity", ref_fp8=True, b=16),
+]
+
+
+@pytest.mark.parametrize("cfg", FP8, ids=lambda c: c.name)
+def test_fp8_references_all_positions(cfg):
+    _log(f"[case] {cfg.name} full")
+    _full_parity(cfg)
+
+
+def test_fp8_references_sampled():
+    test_full_size_configs_sampled(LLAMA8K.with_(name="llama8b_T8k_fp8ref", ref_fp8=True), 400)
+
+
+@pytest.mark.parametrize("cfg", [
+    TINY.with_(name="store_f32", ref_fp8=True),
+    LLAMA8K.with_(name="store_bf16_B2", B=2, T=2048, ref_fp8=True),
+    # a growing schedule (still stride 2 below 5,005) with 2,003 references:
+    # three chunks of host positions in the kernel arguments
+    LLAMA8K.with_(name="store_bf16_dynamic", T=4000, stride=2, alpha=0.0002, n_sink=5,
+                  ref_fp8=True),
+], ids=lambda c: c.name)
+def test_fp8_store_is_bit_exact(cfg):
+    """rkv_store_refs writes the E4M3 bytes of every reference row, as the
+    format rounds them (the oracle's rounding), in schedule order."""
+    _log(f"[case] store {cfg.name}")
+    w = generate(cfg)
+    p = P.params_of(cfg)
+    refs = R.rkv_reference_positions(p)
+    kv = P.to_device(w.kv, cfg.dtype)
+    store = torch.full((cfg.B, len(refs), cfg.C), 0xAB, dtype=torch.uint8, device="cuda")
+    R.rkv_store_refs(p, kv, store, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert np.array_equal(store.cpu().numpy(), P.fp8_store(cfg, w.kv))
+
+
 def test_select_export_matches_encode():
     cfg = LLAMA8K.with_(T=2048)
     w = generate(cfg)

@@ -41,7 +41,7 @@ def _oracle_records(w, positions_by_seq):
     W1, W2, W3 = (x.astype(np.float64) for x in w.weights_f32())
     for b, pos in positions_by_seq.items():
         enc = O.encode_tokens(kv[b], W1, W2, W3, pos, k=cfg.k, g=cfg.g, b=cfg.b, s=cfg.stride,
-                              alpha=cfg.alpha, n_sink=cfg.n_sink)
+                              alpha=cfg.alpha, n_sink=cfg.n_sink, ref_fp8=cfg.ref_fp8)
         rows = b * cfg.T + np.asarray(enc["positions"])
         codes[rows], scale[rows], zmin[rows], ref_idx[rows] = (
             enc["codes"], enc["scale"], enc["zmin"], enc["ref_idx"])
@@ -56,7 +56,10 @@ def _run(w, wd, rec, idx, theta, out_dtype):
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     d_codes, d_ref = t(codes), t(ref_idx)
     d_scale, d_zmin = t(scale.view(np.int16)), t(zmin.view(np.int16))
-    kv = P.to_device(w.kv, cfg.dtype, dev)
+    if cfg.ref_fp8:                                  # the E4M3 store [B][nref][C]
+        kv = t(P.fp8_store(cfg, w.kv))
+    else:
+        kv = P.to_device(w.kv, cfg.dtype, dev)
     d_wd = P.to_device(wd, cfg.dtype, dev)
     d_idx = t(np.asarray(idx, np.int32))
     n = len(idx)
@@ -76,7 +79,7 @@ def _oracle(w, wd, rec, idx, theta):
     return O.restore(codes, scale, zmin, ref_idx, w.kv_f32().astype(np.float64),
                      bf16_bits_to_f32(wd) if cfg.dtype == "bf16" else wd, np.asarray(idx),
                      s=cfg.stride, N=cfg.N, D=cfg.D, g=cfg.g, b=cfg.b, d_c=cfg.d_c,
-                     rope_theta=theta, alpha=cfg.alpha, n_sink=cfg.n_sink)
+                     rope_theta=theta, alpha=cfg.alpha, n_sink=cfg.n_sink, ref_fp8=cfg.ref_fp8)
 
 
 def _compare(got, ref, tol, name):
@@ -102,10 +105,12 @@ def test_restore_tiny_all_positions(out_dtype, tol):
         _compare(got, _oracle(w, wd, rec, idx, theta), tol, f"tiny theta={theta} {out_dtype}")
 
 
-def test_restore_dynamic_schedule_all_positions():
+@pytest.mark.parametrize("fp8", [False, True])
+def test_restore_dynamic_schedule_all_positions(fp8):
     """Sinks and a growing stride ([RKV] §2.6): every reference token,
-    sinks included, restores to its own row."""
-    cfg = TINY_DYN
+    sinks included, restores to its own stored row (its FP8 value when the
+    references are kept in FP8)."""
+    cfg = TINY_DYN.with_(ref_fp8=fp8)
     _log(f"[case] restore {cfg.name}")
     w = generate(cfg)
     wd = decoder_weight(cfg)
@@ -116,7 +121,9 @@ def test_restore_dynamic_schedule_all_positions():
 
 
 @pytest.mark.parametrize("cfg", [LLAMA8K, QWEN_LIKE, LLAMA8K_DYN,
-                                 LLAMA8K.with_(name="llama8b_T8k_identity", b=16)],
+                                 LLAMA8K.with_(name="llama8b_T8k_identity", b=16),
+                                 LLAMA8K.with_(name="llama8b_T8k_fp8ref", ref_fp8=True),
+                                 LLAMA8K_DYN.with_(name="llama8b_T8k_dynamic_fp8ref", ref_fp8=True)],
                          ids=lambda c: c.name)
 def test_restore_sampled_tokens(cfg):
     _log(f"[case] restore {cfg.name}")
