@@ -240,6 +240,42 @@ def bench_append(R, cfg, p_enc, kv, w1, w2, w3, stream, args, batches=(1, 16)):
     return out
 
 
+def bench_variants(R, RB, cfg, kv, w1, w2, w3, idx, stream, args):
+    """The same step (encode + gather of the workload) with the references
+    kept in FP8 ([RKV] §2.4 last paragraph) and with quantisation off
+    (identity, b = 16), each timed like the main line."""
+    import torch
+    out = {}
+    for name, kw in (("fp8_refs", dict(ref_format="fp8")), ("identity", dict(b=16))):
+        d = dict(B=cfg.B, T=cfg.T, N=cfg.N, D=cfg.D, d_ff=cfg.d_ff, d_c=cfg.d_c, k=cfg.k, g=cfg.g,
+                 b=cfg.b, ref_stride=cfg.stride, dtype=cfg.dtype, n_sink=cfg.n_sink,
+                 ref_alpha=cfg.alpha)
+        d.update(kw)
+        p = R.params(**d)
+        buf = RB.alloc_encode(p, kv.device, with_z=False)
+        gdst = torch.empty((idx.numel(), cfg.d_c), dtype=torch.bfloat16, device=kv.device)
+
+        def step():
+            RB.encode(p, kv, w1, w2, w3, buf, stream)
+            RB.dequant_gather(p, buf, idx, "bf16", stream, dst=gdst)
+
+        for _ in range(max(args.warmup, 1)):
+            step()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        out[name] = {"ms_per_step": round(ms, 4),
+                     "tokens_per_s": round(cfg.B * cfg.T / (ms * 1e-3), 1)}
+        del buf, gdst
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -249,6 +285,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-append", action="store_true", help="skip the append measurement")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the FP8-reference and identity-mode encode measurements")
     ap.add_argument("--no-restore", action="store_true",
                     help="skip the separate restore measurement (rkv_restore of the gathered rows)")
     ap.add_argument("--copy-check-mb", type=int, default=0,
@@ -378,6 +416,8 @@ def main():
         line["restore"] = bench_restore(R, cfg, w, p, kv, out, idx, stream, args)
     if not args.no_append:
         line["append"] = bench_append(R, cfg, p, kv, w1, w2, w3, stream, args)
+    if not args.no_variants:
+        line["variants"] = bench_variants(R, RB, cfg, kv, w1, w2, w3, idx, stream, args)
     if not args.no_cpu_baseline:
         print(f"[bench] cpu baseline on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens)
