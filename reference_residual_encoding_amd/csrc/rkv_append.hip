@@ -12,7 +12,7 @@
 //   select   per sequence: merge the lists by (distance, position), write
 //            ref_idx, form the mean of the chosen references in fp32; a
 //            reference token is copied into the cache with a zero record
-//   proj     one workgroup per 4 features: x W1, x W2, m W1, m W2 for every
+//   proj     one workgroup per 16 features: x W1, x W2, m W1, m W2 for every
 //            appended token over all C rows, reduced in LDS, then
 //            delta_h = Swish(x W1) (x W2) - Swish(m W1) (m W2) ([RKV] §2.3)
 //   w3       one workgroup per (token, 32 or 64 latent columns): z =
@@ -223,9 +223,15 @@ __global__ __launch_bounds__(256) void k_app_select(
 #pragma unroll
   for (int e = 0; e < KL; ++e) { bd[e] = FLT_MAX; bi[e] = kNoRef; }
   for (int l = tid; l < nch; l += 256) {
-    const float2* src = part + (size_t(b) * n_lists + l) * KL;
+    const float4* src = reinterpret_cast<const float4*>(part + (size_t(b) * n_lists + l) * KL);
+    float4 w[KL / 2];
 #pragma unroll
-    for (int e = 0; e < KL; ++e) topk_push_lex(bd, bi, src[e].x, __float_as_int(src[e].y));
+    for (int e = 0; e < KL / 2; ++e) w[e] = src[e];      // the whole list in flight at once
+#pragma unroll
+    for (int e = 0; e < KL / 2; ++e) {
+      topk_push_lex(bd, bi, w[e].x, __float_as_int(w[e].y));
+      topk_push_lex(bd, bi, w[e].z, __float_as_int(w[e].w));
+    }
   }
   __shared__ float sd[256 * KL];
   __shared__ int sj[256 * KL];
@@ -276,13 +282,15 @@ __global__ __launch_bounds__(256) void k_app_select(
 }
 
 // ---------------------------------------------------------------- projection
-// Workgroup: features [4w, 4w + 4).  Thread tid owns the rows c = c0 + tid +
-// 256 i (i < 8) of W1 and W2 in registers (loaded once when C <= 2048),
-// and for RB tokens at a time accumulates x.W1, x.W2, m.W1, m.W2 over its
-// rows; the 256 partial sums of each of the 64 values are reduced through
-// LDS in a fixed order, then delta_h is formed for the 4 features.  All of
-// a thread's loads of one step are issued together (the path is bound by
-// memory latency at a few tokens).
+// Workgroup: features [16w, 16w + 16) of RB appended tokens (the feature
+// block runs fastest, so the workgroups of one block of W share it in L2).
+// Four consecutive lanes cover the 16
+// features of one row of W1 and of W2 (32 contiguous bytes each at bf16),
+// so a wave's load touches 16 rows; the 64 row groups of the workgroup take
+// rows c = c0 + rg + 64 i (i < 8) of each 512-row chunk, all 16 loads of a
+// chunk in flight together.  For its RB tokens a thread accumulates x.W1,
+// x.W2, m.W1, m.W2 for its 4 features; the 64 partial sums of each
+// value are reduced through LDS in a fixed order, then delta_h is formed.
 template <typename E>
 __global__ __launch_bounds__(256) void k_app_proj(const E* __restrict__ kv_new,
                                                   const float* __restrict__ mean,
@@ -290,38 +298,35 @@ __global__ __launch_bounds__(256) void k_app_proj(const E* __restrict__ kv_new,
                                                   const E* __restrict__ w1,
                                                   const E* __restrict__ w2, int B, int C, int d_ff,
                                                   float* __restrict__ dh) {
-  constexpr int RB = 4, NV = RB * 16, RPT = 8;           // [token][x|m][W1|W2][feature]
-  const int f0 = blockIdx.x * 4, tid = threadIdx.x;
-  __shared__ float red[NV * 257];
-  __shared__ float part4[4 * NV];
-  __shared__ float tot[NV];
-  float a1[RPT][4], a2[RPT][4];
-  auto load_w = [&](int c0) {
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int c = min(c0 + tid + 256 * i, C - 1);
-      load4(w1 + size_t(c) * d_ff + f0, a1[i]);
-      load4(w2 + size_t(c) * d_ff + f0, a2[i]);
-    }
-  };
-  const bool one_chunk = C <= 256 * RPT;
-  if (one_chunk) load_w(0);
-  for (int b0 = 0; b0 < B; b0 += RB) {
+  constexpr int RB = 4, NV = RB * 16, RPT = 8, RG = 64;  // values: [token][x|m][W1|W2][feature]
+  const int nfb = d_ff / 16;                             // feature blocks; tokens RB at a time
+  const int fb = blockIdx.x % nfb, b0 = (blockIdx.x / nfb) * RB;
+  const int tid = threadIdx.x, fq = tid & 3, rg = tid >> 2;
+  const int f0 = fb * 16 + fq * 4;                       // this lane's 4 features
+  __shared__ float red[NV * (256 + 1)];
+  __shared__ float tot[4 * NV];
+  {
     float acc[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v) acc[v] = 0.0f;
     bool live[RB];
 #pragma unroll
     for (int r = 0; r < RB; ++r) live[r] = b0 + r < B && act[b0 + r] == 1;
-    for (int c0 = 0; c0 < C; c0 += 256 * RPT) {
-      if (!one_chunk) load_w(c0);
+    for (int c0 = 0; c0 < C; c0 += RG * RPT) {
+      float a1[RPT][4], a2[RPT][4];
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const int c = min(c0 + rg + RG * i, C - 1);
+        load4(w1 + size_t(c) * d_ff + f0, a1[i]);
+        load4(w2 + size_t(c) * d_ff + f0, a2[i]);
+      }
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
         if (!live[r]) continue;
         float xv[RPT], mv[RPT];
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
-          const int c = c0 + tid + 256 * i;
+          const int c = c0 + rg + RG * i;
           const int cc = min(c, C - 1);
           const float x = load1(kv_new + size_t(b0 + r) * C + cc);
           const float m = mean[size_t(b0 + r) * C + cc];
@@ -343,25 +348,23 @@ __global__ __launch_bounds__(256) void k_app_proj(const E* __restrict__ kv_new,
     for (int v = 0; v < NV; ++v) red[v * 257 + tid] = acc[v];
     __syncthreads();
     {
-      const int v = tid % NV, q = tid / NV;              // 4 quarters of 64 threads
+      // output (v, q): value v of the lanes with fq == q, summed over the
+      // 64 row groups in order
+      const int q = tid & 3, v = tid >> 2;
       float s = 0.0f;
-      for (int i = 0; i < 64; ++i) s += red[v * 257 + q * 64 + i];
-      part4[q * NV + v] = s;
+      for (int g = 0; g < RG; ++g) s += red[v * 257 + g * 4 + q];
+      tot[q * NV + v] = s;
     }
     __syncthreads();
-    if (tid < NV)
-      tot[tid] = ((part4[tid] + part4[NV + tid]) + part4[2 * NV + tid]) + part4[3 * NV + tid];
-    __syncthreads();
-    if (tid < RB * 4) {
-      const int r = tid / 4, f = tid % 4;
+    if (tid < RB * 16) {                                 // (token r, lane group q, feature f)
+      const int r = tid / 16, q = (tid / 4) & 3, f = tid & 3;
       if (live[r]) {
-        const float* u = tot + r * 16;
+        const float* u = tot + q * NV + r * 16;
         const float hk = silu(u[0 + f]) * u[4 + f];
         const float hm = silu(u[8 + f]) * u[12 + f];
-        dh[size_t(b0 + r) * d_ff + f0 + f] = hk - hm;
+        dh[size_t(b0 + r) * d_ff + fb * 16 + q * 4 + f] = hk - hm;
       }
     }
-    __syncthreads();
   }
 }
 
@@ -473,7 +476,8 @@ hipError_t launch_append(const Shape& sh, void* kv, const void* kv_new, const in
                                                 sh.C, sh.k, rec_bytes, n_groups, sh.d_c,         \
                                                 L.n_lists, part, ref_idx, codes, scale, zmin, z, \
                                                 mean, act);                                      \
-  k_app_proj<E><<<sh.d_ff / 4, 256, 0, st>>>(static_cast<const E*>(kv_new), mean, act,           \
+  k_app_proj<E><<<sh.d_ff / 16 * cdiv(sh.B, 4), 256, 0, st>>>(                                     \
+      static_cast<const E*>(kv_new), mean, act,                                                    \
                                              static_cast<const E*>(w1), static_cast<const E*>(w2), \
                                              sh.B, sh.C, sh.d_ff, dh)
 #define RKV_APPK(E, F8) \

@@ -127,7 +127,8 @@ __device__ __forceinline__ void topk_push_lex(float (&bd)[KL], int (&bi)[KL], fl
   int xj = j;
 #pragma unroll
   for (int i = 0; i < KL; ++i) {
-    const bool c = x < bd[i] || (x == bd[i] && xj < bi[i]);
+    // bitwise, not short-circuit: no branch per comparison
+    const bool c = (x < bd[i]) | ((x == bd[i]) & (xj < bi[i]));
     const float nd = c ? x : bd[i];
     const int ni = c ? xj : bi[i];
     x = c ? bd[i] : x;
