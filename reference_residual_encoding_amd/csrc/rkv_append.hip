@@ -287,8 +287,8 @@ __global__ __launch_bounds__(256) void k_app_select(
 // Four consecutive lanes cover the 16
 // features of one row of W1 and of W2 (32 contiguous bytes each at bf16),
 // so a wave's load touches 16 rows; the 64 row groups of the workgroup take
-// rows c = c0 + rg + 64 i (i < 8) of each 512-row chunk, all 16 loads of a
-// chunk in flight together.  For its RB tokens a thread accumulates x.W1,
+// 8 consecutive rows each of every 512-row chunk, the loads of a chunk in
+// flight together.  For its RB tokens a thread accumulates x.W1,
 // x.W2, m.W1, m.W2 for its 4 features; the 64 partial sums of each
 // value are reduced through LDS in a fixed order, then delta_h is formed.
 template <typename E>
@@ -313,34 +313,40 @@ __global__ __launch_bounds__(256) void k_app_proj(const E* __restrict__ kv_new,
 #pragma unroll
     for (int r = 0; r < RB; ++r) live[r] = b0 + r < B && act[b0 + r] == 1;
     for (int c0 = 0; c0 < C; c0 += RG * RPT) {
+      // rows c1 .. c1 + 7 of this thread: W1 and W2 for its 4 features, and
+      // every token's x and m there as two or three vector loads, all in
+      // flight together and none under a branch (C is a multiple of 8, so
+      // a thread's 8 rows are all in range or all past the end)
+      const int c1 = c0 + rg * RPT;
+      const bool in = c1 < C;
+      const int cb = in ? c1 : 0;
       float a1[RPT][4], a2[RPT][4];
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
-        const int c = min(c0 + rg + RG * i, C - 1);
-        load4(w1 + size_t(c) * d_ff + f0, a1[i]);
-        load4(w2 + size_t(c) * d_ff + f0, a2[i]);
+        load4(w1 + size_t(cb + i) * d_ff + f0, a1[i]);
+        load4(w2 + size_t(cb + i) * d_ff + f0, a2[i]);
+      }
+      float xv[RB][RPT], mv[RB][RPT];
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        const size_t rowx = size_t(min(b0 + r, B - 1)) * C + cb;  // a token past B is not summed
+        load8(kv_new + rowx, xv[r]);
+        const float4 m0 = *reinterpret_cast<const float4*>(mean + rowx);
+        const float4 m1 = *reinterpret_cast<const float4*>(mean + rowx + 4);
+        mv[r][0] = m0.x; mv[r][1] = m0.y; mv[r][2] = m0.z; mv[r][3] = m0.w;
+        mv[r][4] = m1.x; mv[r][5] = m1.y; mv[r][6] = m1.z; mv[r][7] = m1.w;
       }
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
-        if (!live[r]) continue;
-        float xv[RPT], mv[RPT];
-#pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-          const int c = c0 + rg + RG * i;
-          const int cc = min(c, C - 1);
-          const float x = load1(kv_new + size_t(b0 + r) * C + cc);
-          const float m = mean[size_t(b0 + r) * C + cc];
-          xv[i] = c < C ? x : 0.0f;
-          mv[i] = c < C ? m : 0.0f;
-        }
+        if (!live[r] || !in) continue;
 #pragma unroll
         for (int i = 0; i < RPT; ++i)
 #pragma unroll
           for (int f = 0; f < 4; ++f) {
-            acc[r * 16 + 0 + f] = fmaf(xv[i], a1[i][f], acc[r * 16 + 0 + f]);
-            acc[r * 16 + 4 + f] = fmaf(xv[i], a2[i][f], acc[r * 16 + 4 + f]);
-            acc[r * 16 + 8 + f] = fmaf(mv[i], a1[i][f], acc[r * 16 + 8 + f]);
-            acc[r * 16 + 12 + f] = fmaf(mv[i], a2[i][f], acc[r * 16 + 12 + f]);
+            acc[r * 16 + 0 + f] = fmaf(xv[r][i], a1[i][f], acc[r * 16 + 0 + f]);
+            acc[r * 16 + 4 + f] = fmaf(xv[r][i], a2[i][f], acc[r * 16 + 4 + f]);
+            acc[r * 16 + 8 + f] = fmaf(mv[r][i], a1[i][f], acc[r * 16 + 8 + f]);
+            acc[r * 16 + 12 + f] = fmaf(mv[r][i], a2[i][f], acc[r * 16 + 12 + f]);
           }
       }
     }
