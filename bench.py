@@ -276,11 +276,16 @@ def bench_variants(R, RB, cfg, kv, w1, w2, w3, idx, stream, args):
     return out
 
 
+STAGE_PASS_STEPS = 20   # untimed steps with every stage bracketed (the stage breakdown)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # the GPU reaches its steady clocks after a few tens of steps (about
+    # 7% faster than right after start): warm up past that by default
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="llama8b_T32k")
     ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -343,7 +348,7 @@ def main():
     # a short pass with every stage bracketed by events: the stage breakdown
     # and the dominant kernel
     R.rkv_profile_begin((1 << len(R.STAGES)) - 1)
-    for _ in range(3):
+    for _ in range(STAGE_PASS_STEPS):
         step()
     torch.cuda.synchronize()
     stages_ms = {}
