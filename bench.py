@@ -27,7 +27,7 @@ PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 # kernel behind each profiled stage
-STAGE_KERNEL = {"pack": "k_pack_weights", "norms": "k_ref_gather", "dist": "k_dist_topk",
+STAGE_KERNEL = {"pack": "k_pack_weights", "norms": "k_setup", "dist": "k_dist_topk",
                 "merge": "k_topk_merge", "proj": "k_ref_proj", "swiglu": "k_swiglu",
                 "w3": "k_w3_quant", "quant": "k_quantize", "gather": "k_gather"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_{workload}.txt")
@@ -90,7 +90,9 @@ def stage_work(cfg, n_gather: int, refs):
     rec = cfg.d_c * cfg.b // 8 + 4 * (cfg.d_c // cfg.g)
     return {
         "pack": ("bytes", 2 * (2 * C * cfg.d_ff + cfg.d_ff * cfg.d_c) * esz),
-        "norms": ("bytes", B * nref * C * esz),
+        # set-up: weight repacking, schedule tables, reference rows and norms
+        "norms": ("bytes", 2 * (2 * C * cfg.d_ff + cfg.d_ff * cfg.d_c) * esz + 3 * 4 * T
+                  + 2 * B * nref * C * esz),
         "dist": ("flops", 2.0 * C * pairs),
         "merge": ("bytes", B * T * cfg.k * 4),
         "proj": ("flops", 2.0 * C * 2 * cfg.d_ff * B * nref),

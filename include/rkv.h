@@ -251,8 +251,10 @@ int32_t rkv_reference_positions(const rkv_params* p, int32_t* rpos,
  * duration in milliseconds and the number of launches.  Meant for
  * single-threaded measurement; events are created on first use and kept. */
 typedef enum {
-  RKV_STAGE_PACK = 0,    /* weight repacking                               */
-  RKV_STAGE_NORMS = 1,   /* reference rows, norms, reference-token records  */
+  RKV_STAGE_PACK = 0,    /* weight repacking on its own (none in rkv_encode) */
+  RKV_STAGE_NORMS = 1,   /* set-up, one launch: weight repacking, schedule
+                            tables, reference rows, norms, reference-token
+                            records                                         */
   RKV_STAGE_DIST = 2,    /* distance contraction + partial top-k lists      */
   RKV_STAGE_MERGE = 3,   /* top-k merge, ref_idx of non-reference tokens    */
   RKV_STAGE_PROJ = 4,    /* reference projection P = R [W1|W2]              */

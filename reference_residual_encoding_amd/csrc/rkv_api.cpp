@@ -214,10 +214,9 @@ rkv_status rkv_encode(const rkv_params* p, const void* kv, const void* w1, const
     StageScope scope_(stage, stream);                         \
     if ((e = (call)) != hipSuccess) return device_status(e, name); \
   } while (0)
-  RKV_STAGE(RKV_STAGE_PACK, rkv::launch_pack_weights(sh, w1, w2, w3, ws, L, stream), "pack");
-  RKV_STAGE(RKV_STAGE_NORMS, rkv::launch_schedule(sh, ws, L, stream), "schedule");
   RKV_STAGE(RKV_STAGE_NORMS,
-            rkv::launch_ref_norms(sh, kv, ws, L, ref_idx, codes, scale, zmin, z, stream), "norms");
+            rkv::launch_setup(sh, w1, w2, w3, kv, ws, L, ref_idx, codes, scale, zmin, z, stream),
+            "setup");
   RKV_STAGE(RKV_STAGE_DIST, rkv::launch_dist(sh, kv, ws, L, stream), "dist");
   RKV_STAGE(RKV_STAGE_MERGE, rkv::launch_merge(sh, ref_idx, ws, L, stream), "merge");
   if (sh.nr > 0) {
@@ -241,11 +240,10 @@ rkv_status rkv_select(const rkv_params* p, const void* kv, int32_t* ref_idx, voi
     return fail(RKV_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
   char* ws = static_cast<char*>(workspace);
   hipError_t e;
-  RKV_STAGE(RKV_STAGE_NORMS, rkv::launch_schedule(sh, ws, L, stream), "schedule");
   RKV_STAGE(RKV_STAGE_NORMS,
-            rkv::launch_ref_norms(sh, kv, ws, L, ref_idx, nullptr, nullptr, nullptr, nullptr,
-                                  stream),
-            "norms");
+            rkv::launch_setup(sh, nullptr, nullptr, nullptr, kv, ws, L, ref_idx, nullptr, nullptr,
+                              nullptr, nullptr, stream),
+            "setup");
   RKV_STAGE(RKV_STAGE_DIST, rkv::launch_dist(sh, kv, ws, L, stream), "dist");
   RKV_STAGE(RKV_STAGE_MERGE, rkv::launch_merge(sh, ref_idx, ws, L, stream), "merge");
   return ok();

@@ -57,11 +57,14 @@ hipError_t launch_store_refs(const Shape& sh, const void* kv, uint8_t* store, hi
 Workspace plan_workspace(const Shape& sh);
 
 // Each launcher enqueues on `st` and returns hipGetLastError().
-hipError_t launch_pack_weights(const Shape& sh, const void* w1, const void* w2, const void* w3,
-                               char* ws, const Workspace& L, hipStream_t st);
-hipError_t launch_ref_norms(const Shape& sh, const void* kv, char* ws, const Workspace& L,
-                            int32_t* ref_idx, uint8_t* codes, uint16_t* scale, uint16_t* zmin,
-                            float* z, hipStream_t st);
+// Set-up of an encode in one launch (after the positions of a growing
+// schedule): weight repacking (skipped when w1 is null), schedule tables,
+// compact reference rows and their norms, and the reference tokens'
+// ref_idx rows and zero records (records skipped when codes is null).
+hipError_t launch_setup(const Shape& sh, const void* w1, const void* w2, const void* w3,
+                        const void* kv, char* ws, const Workspace& L, int32_t* ref_idx,
+                        uint8_t* codes, uint16_t* scale, uint16_t* zmin, float* z,
+                        hipStream_t st);
 hipError_t launch_dist(const Shape& sh, const void* kv, char* ws, const Workspace& L,
                        hipStream_t st);
 hipError_t launch_merge(const Shape& sh, int32_t* ref_idx, char* ws, const Workspace& L,

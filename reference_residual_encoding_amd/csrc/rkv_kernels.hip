@@ -91,11 +91,11 @@ struct PackJob {
 struct PackJobs { PackJob j[3]; };
 
 template <typename E>
-__global__ __launch_bounds__(256) void k_pack_weights(PackJobs jobs) {
+constexpr int kPackLdt = 64 + 16 / int(sizeof(E));       // padded tile row (keeps 16-byte alignment)
+
+template <typename E>
+__device__ __forceinline__ void pack_tile(const PackJobs& jobs, int w, E (*tile)[kPackLdt<E>]) {
   constexpr int V = 16 / int(sizeof(E));                 // elements per 16 bytes
-  constexpr int LDT = 64 + 16 / int(sizeof(E));          // padded tile row (keeps 16-byte alignment)
-  __shared__ __attribute__((aligned(16))) E tile[64][LDT];
-  const int w = blockIdx.x;
   const int ji = w >= jobs.j[2].first ? 2 : (w >= jobs.j[1].first ? 1 : 0);
   const PackJob& J = jobs.j[ji];
   const int tr = (w - J.first) / J.tiles_c, tc = (w - J.first) % J.tiles_c;
@@ -131,6 +131,12 @@ __global__ __launch_bounds__(256) void k_pack_weights(PackJobs jobs) {
   }
 }
 
+template <typename E>
+__global__ __launch_bounds__(256) void k_pack_weights(PackJobs jobs) {
+  __shared__ __attribute__((aligned(16))) E tile[64][kPackLdt<E>];
+  pack_tile<E>(jobs, blockIdx.x, tile);
+}
+
 // ------------------------------------------------------------------ schedule
 // Device copies of the reference schedule ([RKV] §2.6), one per call (every
 // sequence shares it): rpos[j] = position of the j-th reference, nrp[q] =
@@ -138,6 +144,40 @@ __global__ __launch_bounds__(256) void k_pack_weights(PackJobs jobs) {
 // reference, else q.  The host computes the schedule exactly; the device
 // copy comes from the closed form (fixed stride) or from the host's
 // positions carried in kernel arguments, so no host buffer is involved.
+// Tables for the 256 positions of block `blk`.  Fixed stride after the
+// sinks (rpos_in == null): every table has a closed form, and rpos is
+// written too; otherwise the positions rpos_in (already on the device) are
+// searched.
+struct SchedArgs {
+  const int* rpos_in;
+  int* rpos;
+  int* tab;
+  int* nrp;
+  int nref, T, s0, n_sink;
+};
+__device__ __forceinline__ void sched_block(const SchedArgs& a, int blk) {
+  const int t = blk * 256 + threadIdx.x;
+  if (t >= a.T) return;
+  int before;
+  bool ref;
+  if (a.rpos_in == nullptr) {
+    if (t < a.nref) a.rpos[t] = t < a.n_sink ? t : a.n_sink + (t - a.n_sink) * a.s0;
+    const int u = t - a.n_sink;
+    ref = u < 0 || u % a.s0 == 0;
+    before = u < 0 ? t : a.n_sink + (u + a.s0 - 1) / a.s0;   // references before t
+  } else {
+    int lo = 0, hi = a.nref;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (a.rpos_in[mid] < t) lo = mid + 1; else hi = mid;
+    }
+    ref = lo < a.nref && a.rpos_in[lo] == t;
+    before = lo;
+  }
+  a.tab[t] = ref ? ~before : t - before;
+  if (!ref) a.nrp[t - before] = t;
+}
+
 __global__ __launch_bounds__(256) void k_sched_fixed(int* __restrict__ rpos, int nref, int T,
                                                      int s0, int n_sink, int* __restrict__ tab,
                                                      int* __restrict__ nrp) {
@@ -184,21 +224,34 @@ __global__ __launch_bounds__(256) void k_sched_tables(const int* __restrict__ rp
 // A reference token is stored as it is ([RKV] §2.4): its ref_idx row is all
 // -1 and, when a record is given, its record (codes, scale, zmin, z) is all
 // zero; one wave writes each with coalesced stores.
+struct RefArgs {
+  const char* kv;
+  char* refs;
+  float* ysq;
+  int32_t* ref_idx;
+  uint8_t* codes;
+  uint16_t* scale;
+  uint16_t* zmin;
+  float* z;
+  SchedView sv;                                          // positions of the references
+  int B, T, C, nref, k, cb, ng, d_c, fp8;
+};
 template <typename E>
-__global__ __launch_bounds__(256) void k_ref_gather(const char* __restrict__ kv, int B, int T,
-                                                    int C, const int* __restrict__ rpos, int nref,
-                                                    char* __restrict__ refs,
-                                                    float* __restrict__ ysq,
-                                                    int32_t* __restrict__ ref_idx, int k,
-                                                    uint8_t* __restrict__ codes, int cb,
-                                                    uint16_t* __restrict__ scale,
-                                                    uint16_t* __restrict__ zmin, int ng,
-                                                    float* __restrict__ z, int d_c, int fp8) {
-  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+__device__ __forceinline__ void ref_rows(const RefArgs& a, int blk) {
+  const char* __restrict__ kv = a.kv;
+  char* __restrict__ refs = a.refs;
+  int32_t* __restrict__ ref_idx = a.ref_idx;
+  uint8_t* __restrict__ codes = a.codes;
+  uint16_t* __restrict__ scale = a.scale;
+  uint16_t* __restrict__ zmin = a.zmin;
+  float* __restrict__ z = a.z;
+  const int T = a.T, C = a.C, nref = a.nref, k = a.k, cb = a.cb, ng = a.ng, d_c = a.d_c;
+  const int fp8 = a.fp8;
+  const int wid = blk * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (wid >= B * nref) return;
+  if (wid >= a.B * nref) return;
   const int b = wid / nref, j = wid % nref;
-  const size_t rec = size_t(b) * T + size_t(rpos[j]);   // the reference token's flat row
+  const size_t rec = size_t(b) * T + size_t(ref_position(a.sv, j));   // the reference token's row
   for (int i = lane; i < k; i += 64) ref_idx[rec * k + i] = -1;
   if (codes) {
     for (int o = lane * 4; o < cb; o += 256) *reinterpret_cast<uint32_t*>(codes + rec * cb + o) = 0u;
@@ -245,7 +298,27 @@ __global__ __launch_bounds__(256) void k_ref_gather(const char* __restrict__ kv,
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (lane == 0) ysq[wid] = acc;
+  if (lane == 0) a.ysq[wid] = acc;
+}
+
+// One launch for the set-up of an encode, three independent parts by block
+// range: weight repacking (pack tiles), schedule tables (256 positions per
+// block) and the reference rows (4 per block).
+template <typename E>
+__global__ __launch_bounds__(256) void k_setup(PackJobs jobs, int n_pack, SchedArgs sa, int n_tab,
+                                               RefArgs ra) {
+  __shared__ __attribute__((aligned(16))) E tile[64][kPackLdt<E>];
+  int w = blockIdx.x;
+  if (w < n_pack) {
+    pack_tile<E>(jobs, w, tile);
+    return;
+  }
+  w -= n_pack;
+  if (w < n_tab) {
+    sched_block(sa, w);
+    return;
+  }
+  ref_rows<E>(ra, w - n_tab);
 }
 
 // FP8 reference store ([RKV] §2.4 last paragraph): store[b][j][c] = E4M3 of
@@ -1082,24 +1155,6 @@ Workspace plan_workspace(const Shape& sh) {
   return L;
 }
 
-hipError_t launch_pack_weights(const Shape& sh, const void* w1, const void* w2, const void* w3,
-                               char* ws, const Workspace& L, hipStream_t st) {
-  auto tiles = [](int n) { return (n + 63) / 64; };
-  PackJobs J{};
-  J.j[0] = {w1, ws + L.wp, sh.C, sh.d_ff, sh.C, 1, 0, tiles(sh.d_ff), 0};
-  J.j[1] = {w2, ws + L.wp, sh.C, sh.d_ff, sh.C, 2, 0, tiles(sh.d_ff), 0};
-  J.j[2] = {w3, ws + L.w3p, sh.d_ff, sh.d_c, sh.k3, 0, sh.bf16 ? 1 : 0, tiles(sh.d_c), 0};
-  int first = 0;
-  for (auto& j : J.j) {
-    j.first = first;
-    first += tiles(j.rows) * j.tiles_c;
-  }
-  if (sh.bf16)
-    k_pack_weights<uint16_t><<<first, 256, 0, st>>>(J);
-  else
-    k_pack_weights<float><<<first, 256, 0, st>>>(J);
-  return hipGetLastError();
-}
 
 hipError_t launch_store_refs(const Shape& sh, const void* kv, uint8_t* store, hipStream_t st) {
   const SchedView fixed{nullptr, sh.nref, sh.s, sh.n_sink};
@@ -1155,23 +1210,54 @@ hipError_t launch_schedule(const Shape& sh, char* ws, const Workspace& L, hipStr
   return hipGetLastError();
 }
 
-hipError_t launch_ref_norms(const Shape& sh, const void* kv, char* ws, const Workspace& L,
-                            int32_t* ref_idx, uint8_t* codes, uint16_t* scale, uint16_t* zmin,
-                            float* z, hipStream_t st) {
-  const int rows = sh.B * sh.nref;
-  auto* y = reinterpret_cast<float*>(ws + L.ysq);
-  const auto* rpos = reinterpret_cast<const int*>(ws + L.rpos);
-  const auto* p = static_cast<const char*>(kv);
-  // identity mode stores no group numbers
-  const int cb = sh.d_c * sh.b / 8, ng = sh.b == kIdentityBits ? 0 : sh.d_c / sh.g;
+hipError_t launch_setup(const Shape& sh, const void* w1, const void* w2, const void* w3,
+                        const void* kv, char* ws, const Workspace& L, int32_t* ref_idx,
+                        uint8_t* codes, uint16_t* scale, uint16_t* zmin, float* z,
+                        hipStream_t st) {
+  auto* rpos = reinterpret_cast<int*>(ws + L.rpos);
+  const bool dynamic = sh.alpha != 0.0;
+  if (dynamic) {                                         // positions first (kernel arguments)
+    const hipError_t e = launch_ref_positions(sh, rpos, st);
+    if (e != hipSuccess) return e;
+  }
+  PackJobs J{};
+  int n_pack = 0;
+  if (w1) {
+    auto tiles = [](int n) { return (n + 63) / 64; };
+    J.j[0] = {w1, ws + L.wp, sh.C, sh.d_ff, sh.C, 1, 0, tiles(sh.d_ff), 0};
+    J.j[1] = {w2, ws + L.wp, sh.C, sh.d_ff, sh.C, 2, 0, tiles(sh.d_ff), 0};
+    J.j[2] = {w3, ws + L.w3p, sh.d_ff, sh.d_c, sh.k3, 0, sh.bf16 ? 1 : 0, tiles(sh.d_c), 0};
+    for (auto& j : J.j) {
+      j.first = n_pack;
+      n_pack += tiles(j.rows) * j.tiles_c;
+    }
+  } else {
+    J.j[1].first = J.j[2].first = 0;
+  }
+  SchedArgs sa{dynamic ? rpos : nullptr, rpos, reinterpret_cast<int*>(ws + L.tab),
+               reinterpret_cast<int*>(ws + L.nrp), sh.nref, sh.T, sh.s, sh.n_sink};
+  const int n_tab = cdiv(sh.T, 256);
+  RefArgs ra{};
+  ra.kv = static_cast<const char*>(kv);
+  ra.refs = ws + L.refs;
+  ra.ysq = reinterpret_cast<float*>(ws + L.ysq);
+  ra.ref_idx = ref_idx;
+  ra.codes = codes;
+  ra.scale = scale;
+  ra.zmin = zmin;
+  ra.z = z;
+  ra.sv = SchedView{dynamic ? rpos : nullptr, sh.nref, sh.s, sh.n_sink};
+  ra.B = sh.B; ra.T = sh.T; ra.C = sh.C; ra.nref = sh.nref; ra.k = sh.k;
+  ra.cb = sh.d_c * sh.b / 8;
+  ra.ng = sh.b == kIdentityBits ? 0 : sh.d_c / sh.g;     // identity mode stores no group numbers
+  ra.d_c = sh.d_c;
+  ra.fp8 = sh.ref_fp8;
+  const int n_ref = cdiv(long(sh.B) * sh.nref, 4);
+  const int grid = n_pack + n_tab + n_ref;
   if (sh.bf16)
-    k_ref_gather<uint16_t><<<cdiv(rows, 4), 256, 0, st>>>(p, sh.B, sh.T, sh.C, rpos, sh.nref,
-                                                          ws + L.refs, y, ref_idx, sh.k, codes, cb,
-                                                          scale, zmin, ng, z, sh.d_c, sh.ref_fp8);
+    k_setup<uint16_t><<<grid, 256, 0, st>>>(J, n_pack, sa, n_tab, ra);
   else
-    k_ref_gather<float><<<cdiv(rows, 4), 256, 0, st>>>(p, sh.B, sh.T, sh.C, rpos, sh.nref,
-                                                       ws + L.refs, y, ref_idx, sh.k, codes, cb,
-                                                       scale, zmin, ng, z, sh.d_c, sh.ref_fp8);
+    k_setup<float><<<grid, 256, 0, st>>>(J, n_pack, sa, n_tab, ra);
   return hipGetLastError();
 }
 
