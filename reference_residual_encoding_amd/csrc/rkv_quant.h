@@ -32,8 +32,10 @@ __device__ __forceinline__ void group_minmax(float& mn, float& mx) {
 // lane of the wave needs it, is the division itself done.
 __device__ __forceinline__ float rint_div(float x, float d, float rd) {
   const float y = x * rd;
-  const bool near_half = fabsf(y - floorf(y) - 0.5f) < 1e-5f;
   float r = rintf(y);
+  // |y - rint(y)| <= 0.5; within 1e-5 of 0.5 means y is within 1e-5 of a
+  // half-integer
+  const bool near_half = fabsf(y - r) > 0.5f - 1e-5f;
   if (__any(near_half)) r = near_half ? rintf(x / d) : r;
   return r;
 }
@@ -62,7 +64,7 @@ __device__ __forceinline__ uint32_t quant8(const float (&v)[8], uint16_t& dh_bit
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float t = rint_div(v[e] - mh, dh, rd);
-      word |= uint32_t(fminf(fmaxf(t, 0.0f), kLevels)) << (BITS * e);
+      word |= uint32_t(__builtin_amdgcn_fmed3f(t, 0.0f, kLevels)) << (BITS * e);   // clamp
     }
   }
   return word;
