@@ -289,7 +289,7 @@ def main():
     # 7% faster than right after start): warm up past that by default
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="llama8b_T32k")
-    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-tokens", type=int, default=4096)   # about 15 s of oracle work
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-append", action="store_true", help="skip the append measurement")
     ap.add_argument("--no-variants", action="store_true",
