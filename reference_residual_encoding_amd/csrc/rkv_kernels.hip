@@ -666,6 +666,49 @@ __global__ __launch_bounds__(SwCfg<E>::kThreads) void k_swiglu(const char* __res
   f32x16 acc[kTM][kTN];
   tile_product<E, BM, BN, CF::SB, CF::NS, WGM, WGN>(rowA, rowB, int(rowb), lds, acc);
 
+  // 2 (set-up). Four consecutive features of one row per lane: BN/8 lanes
+  // per row, 16 rows per workgroup step.  Feature quad c holds W1 columns
+  // n0 + 64(c/8) + 4(c%8) .. +3 of P and the W2 columns 32 further.  All
+  // loads and stores are unconditional: P and the tile's rows of dh go
+  // through buffer resources (an offset past the end of a range reads zero
+  // and drops a store), which lets the compiler keep the loads in flight.
+  // The P rows of the first row steps are requested before h is staged,
+  // and each group's loads are in flight while the previous group is
+  // consumed (two register buffers).
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  constexpr int kQ = BN / 8;                             // feature quads per row
+  static_assert(NT / kQ == 16, "16 rows per workgroup step");
+  const int c = tid % kQ, row0 = tid / kQ;
+  const bool colv = n0 + 64 * (c >> 3) < N;              // the quad's 64-column group exists
+  const uint32_t pcol = uint32_t(n0 + 64 * (c >> 3) + 4 * (c & 7)) * 4u;
+  const int f = n0 / 2 + 4 * c;
+  const __amdgpu_buffer_rsrc_t prs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(proj), 0, int(proj_bytes), 0x00020000);
+  const int rows = min(M - m0, BM);
+  const __amdgpu_buffer_rsrc_t drs = __builtin_amdgcn_make_buffer_rsrc(
+      dh + size_t(m0) * d_ff * 4, 0, rows * d_ff * 4, 0x00020000);
+  auto ld4 = [&](uint32_t off) {
+    return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(prs, int(off), 0, 0));
+  };
+  constexpr int kRB = KL <= 4 ? 2 : 1;                   // row steps per group
+  constexpr int kGroups = BM / 16 / kRB;
+  static_assert(kGroups % 2 == 0, "groups alternate between two buffers");
+  f4 pa1[kRB][KL], pa2[kRB][KL], pb1[kRB][KL], pb2[kRB][KL];
+  auto issue = [&](int g, f4 (&q1)[kRB][KL], f4 (&q2)[kRB][KL]) {
+#pragma unroll
+    for (int u = 0; u < kRB; ++u) {
+      const uint32_t* po = poff_lds + (16 * (g * kRB + u) + row0) * KL;
+#pragma unroll
+      for (int q = 0; q < KL; ++q) {
+        // kNone + pcol stays past the end of P; a quad past the column edge
+        // reads in-range values of no use (its store is dropped)
+        q1[u][q] = ld4(po[q] + pcol);
+        q2[u][q] = ld4(po[q] + pcol + 128u);             // +32 floats: the x*W2 columns
+      }
+    }
+  };
+  issue(0, pa1, pa2);
+
   // 1. h(kv) = Swish(u1) * u2 from the accumulators into LDS.  Lane l of
   // wave (wm, wn) holds, in register r of fragment (i, j), tile row
   // wm*BM/WGM + 32i + mfma32_row(r, l) and Wp row n0 + wn*64 + 32j + l%32.
@@ -685,47 +728,15 @@ __global__ __launch_bounds__(SwCfg<E>::kThreads) void k_swiglu(const char* __res
   }
   __syncthreads();
 
-  // 2. Four consecutive features of one row per lane: BN/8 lanes per row,
-  // 16 rows per workgroup step.  Feature quad c holds W1 columns
-  // n0 + 64(c/8) + 4(c%8) .. +3 of P and the W2 columns 32 further.  All loads
-  // and stores are unconditional: P and the tile's rows of dh go through
-  // buffer resources (an offset past the end of a range reads zero and
-  // drops a store), which lets the compiler keep the loads in flight.
-  typedef float f4 __attribute__((ext_vector_type(4)));
-  constexpr int kQ = BN / 8;                             // feature quads per row
-  static_assert(NT / kQ == 16, "16 rows per workgroup step");
-  const int c = tid % kQ, row0 = tid / kQ;
-  const bool colv = n0 + 64 * (c >> 3) < N;              // the quad's 64-column group exists
-  const uint32_t pcol = uint32_t(n0 + 64 * (c >> 3) + 4 * (c & 7)) * 4u;
-  const int f = n0 / 2 + 4 * c;
-  const __amdgpu_buffer_rsrc_t prs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(proj), 0, int(proj_bytes), 0x00020000);
-  const int rows = min(M - m0, BM);
-  const __amdgpu_buffer_rsrc_t drs = __builtin_amdgcn_make_buffer_rsrc(
-      dh + size_t(m0) * d_ff * 4, 0, rows * d_ff * 4, 0x00020000);
-  auto ld4 = [&](uint32_t off) {
-    return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(prs, int(off), 0, 0));
-  };
-  constexpr int kRB = KL <= 4 ? 4 : 2;                   // row steps whose loads fly together
-  for (int it = 0; it < BM / 16; it += kRB) {
-    f4 p1[kRB][KL], p2[kRB][KL];
+  // 2. delta_h = h(kv) - Swish(mean u1) * mean u2 per row, stored as (hi, lo)
+  // bf16 pairs (or fp32)
+  auto consume = [&](int g, const f4 (&q1)[kRB][KL], const f4 (&q2)[kRB][KL]) {
 #pragma unroll
     for (int u = 0; u < kRB; ++u) {
-      const uint32_t* po = poff_lds + (16 * (it + u) + row0) * KL;
+      const int rt = 16 * (g * kRB + u) + row0;
+      f4 s1 = q1[u][0], s2 = q2[u][0];
 #pragma unroll
-      for (int q = 0; q < KL; ++q) {
-        // kNone + pcol stays past the end of P; a quad past the column edge
-        // reads in-range values of no use (its store is dropped)
-        p1[u][q] = ld4(po[q] + pcol);
-        p2[u][q] = ld4(po[q] + pcol + 128u);           // +32 floats: the x*W2 columns
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kRB; ++u) {
-      const int rt = 16 * (it + u) + row0;
-      f4 s1 = p1[u][0], s2 = p2[u][0];
-#pragma unroll
-      for (int q = 1; q < KL; ++q) { s1 += p1[u][q]; s2 += p2[u][q]; }
+      for (int q = 1; q < KL; ++q) { s1 += q1[u][q]; s2 += q2[u][q]; }
       const float inv = inv_lds[rt];
       const f4 hk = *reinterpret_cast<const f4*>(h + rt * kLdh + 4 * c);
       uint32_t w[4];
@@ -739,6 +750,13 @@ __global__ __launch_bounds__(SwCfg<E>::kThreads) void k_swiglu(const char* __res
       const uint32_t so = colv ? uint32_t(rt * d_ff + f) * 4u : kNone;
       __builtin_amdgcn_raw_buffer_store_b128(wv, drs, int(so), 0, 0);
     }
+  };
+#pragma unroll
+  for (int g = 0; g < kGroups; g += 2) {
+    issue(g + 1, pb1, pb2);
+    consume(g, pa1, pa2);
+    if (g + 2 < kGroups) issue(g + 2, pa1, pa2);
+    consume(g + 1, pb1, pb2);
   }
 }
 
