@@ -221,7 +221,7 @@ rkv_status rkv_encode(const rkv_params* p, const void* kv, const void* w1, const
   RKV_STAGE(RKV_STAGE_MERGE, rkv::launch_merge(sh, ref_idx, ws, L, stream), "merge");
   if (sh.nr > 0) {
     RKV_STAGE(RKV_STAGE_PROJ, rkv::launch_ref_proj(sh, kv, ws, L, stream), "proj");
-    RKV_STAGE(RKV_STAGE_SWIGLU, rkv::launch_swiglu(sh, kv, ref_idx, ws, L, stream), "swiglu");
+    RKV_STAGE(RKV_STAGE_SWIGLU, rkv::launch_swiglu(sh, kv, ws, L, stream), "swiglu");
     RKV_STAGE(RKV_STAGE_W3, rkv::launch_w3_quant(sh, ws, L, codes, scale, zmin, z, stream), "w3");
   }
   return ok();

@@ -40,7 +40,9 @@ struct Shape {
 
 // Byte offsets of the workspace regions (each 256-byte aligned).
 struct Workspace {
-  size_t wp, w3p, ysq, refs, proj, part, dh, rpos, nrp, tab, total;
+  size_t wp, w3p, ysq, refs, proj, part, dh, rpos, nrp, tab,
+      selj,   // [B*nr][kl] chosen reference indices of each non-reference token, -1 pads
+      total;
 };
 
 Shape make_shape(int B, int T, int N, int D, int d_ff, int d_c, int k, int g, int b, int s,
@@ -71,7 +73,7 @@ hipError_t launch_merge(const Shape& sh, int32_t* ref_idx, char* ws, const Works
                         hipStream_t st);
 hipError_t launch_ref_proj(const Shape& sh, const void* kv, char* ws, const Workspace& L,
                            hipStream_t st);
-hipError_t launch_swiglu(const Shape& sh, const void* kv, const int32_t* ref_idx, char* ws,
+hipError_t launch_swiglu(const Shape& sh, const void* kv, char* ws,
                          const Workspace& L, hipStream_t st);
 // W3 product fused with the quantiser; writes the records of non-reference tokens.
 hipError_t launch_w3_quant(const Shape& sh, char* ws, const Workspace& L, uint8_t* codes,

@@ -389,16 +389,38 @@ __global__ __launch_bounds__(DistCfg<E>::kThreads) void k_dist_topk(
   // on XCD w % 8: that XCD takes the token tiles g = x, x+8, x+16, ... and
   // all of their chunks, one after the other, which keeps a token tile in
   // its own L2 while the chunks stream past.
+  // Every wave finds the item alike: its 64 lanes take 64 of the XCD's token
+  // tiles at once (one load each, not a chain of dependent loads), and a
+  // prefix sum of their chunk counts over the lanes locates item l.
   const int x = blockIdx.x & 7;
-  int l = blockIdx.x >> 3;
-  int g = x, c = -1, npool_max = 0;
-  for (; g < B * n_tt; g += 8) {
-    const int tt_ = g % n_tt;
-    const int ql = min(tt_ * BN + BN, nr) - 1;          // last token of the tile
-    const int np = nrp[ql] - ql;                         // its pool: references before it
-    const int nch = (np + BM - 1) / BM;
-    if (l < nch) { c = l; npool_max = np; break; }
-    l -= nch;
+  const int l = blockIdx.x >> 3;
+  const int lane = threadIdx.x & 63;
+  int g = -1, c = -1, npool_max = 0;
+  for (int g0 = x, before = 0; g0 < B * n_tt; g0 += 8 * 64) {
+    const int gl = g0 + 8 * lane;
+    int np = 0, nch = 0;
+    if (gl < B * n_tt) {
+      const int tt_ = gl % n_tt;
+      const int ql = min(tt_ * BN + BN, nr) - 1;        // last token of the tile
+      np = nrp[ql] - ql;                                 // its pool: references before it
+      nch = (np + BM - 1) / BM;
+    }
+    int incl = nch;                                      // inclusive scan over the lanes
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    const int want = l - before;
+    const unsigned long long hit = __ballot(want >= incl - nch && want < incl);
+    if (hit) {
+      const int src = __ffsll(hit) - 1;
+      g = __shfl(gl, src);
+      c = want - (__shfl(incl, src) - __shfl(nch, src));
+      npool_max = __shfl(np, src);
+      break;
+    }
+    before += __shfl(incl, 63);
   }
   if (c < 0) return;  // this XCD has no more items
   const int tt = g % n_tt, b = g / n_tt;
@@ -487,19 +509,20 @@ __global__ __launch_bounds__(DistCfg<E>::kThreads) void k_dist_topk(
   }
 }
 
-// Per non-reference token: merge the partial lists, keep k_t = min(k,
-// ceil(t/s)) references ([RKV] §2.1), write their positions in ascending
-// order, -1 pads.  The lists cover disjoint reference sets; the merge orders
-// by (d, j), so equal distances keep the smaller position whatever order the
-// lists come in.  (Reference tokens' rows are written by k_ref_gather.)
-// Reference tokens get an all -1 row and, when a record is given, an all-zero
-// record: references are stored as they are ([RKV] §2.4).
+// Per non-reference token: merge the partial lists, keep k_t = min(k, pool
+// size) references ([RKV] §2.1), write their positions in ascending order,
+// -1 pads.  The lists cover disjoint reference sets; the merge orders by
+// (d, j), so equal distances keep the smaller position whatever order the
+// lists come in.  (Reference tokens' all -1 rows and zero records are
+// written by the set-up kernel: references are stored as they are, [RKV]
+// §2.4.)
 template <int KL>
 __global__ __launch_bounds__(64) void k_topk_merge(const float2* __restrict__ part,
                                                     int32_t* __restrict__ ref_idx, int B, int T,
                                                     const int* __restrict__ tab,
                                                     const int* __restrict__ rpos, int k, int nr,
-                                                    int n_lists, int chunk) {
+                                                    int n_lists, int chunk,
+                                                    int* __restrict__ selj) {
   const long gid = long(blockIdx.x) * 64 + threadIdx.x;
   if (gid >= long(B) * T) return;
   const int b = int(gid / T), t = int(gid % T);
@@ -553,6 +576,12 @@ __global__ __launch_bounds__(64) void k_topk_merge(const float2* __restrict__ pa
 #pragma unroll
   for (int i = 0; i < KL; ++i)
     if (i < k) out[i] = i < kt ? rpos[sel[i]] : -1;
+  // the same choice as reference indices, for the SwiGLU's mean branch
+  int4* sj = reinterpret_cast<int4*>(selj + (size_t(b) * nr + q) * KL);
+#pragma unroll
+  for (int h = 0; h < KL / 4; ++h)
+    sj[h] = make_int4(4 * h + 0 < kt ? sel[4 * h + 0] : -1, 4 * h + 1 < kt ? sel[4 * h + 1] : -1,
+                      4 * h + 2 < kt ? sel[4 * h + 2] : -1, 4 * h + 3 < kt ? sel[4 * h + 3] : -1);
 }
 
 // ------------------------------------------------------------------ reference projection
@@ -607,11 +636,10 @@ __global__ __launch_bounds__(SwCfg<E>::kThreads) void k_swiglu(const char* __res
                                                 const char* __restrict__ wp,
                                                 const float* __restrict__ proj,
                                                 uint32_t proj_bytes,
-                                                const int32_t* __restrict__ ref_idx,
+                                                const int* __restrict__ selj,
                                                 char* __restrict__ dh, int T, int C,
-                                                const int* __restrict__ nrp,
-                                                const int* __restrict__ tab, int nref, int nr,
-                                                int k, int d_ff, int M) {
+                                                const int* __restrict__ nrp, int nref, int nr,
+                                                int d_ff, int M) {
   using CF = SwCfg<E>;
   constexpr int BM = CF::BM, BN = CF::BN, WGM = CF::WGM, WGN = CF::WGN, NT = CF::kThreads;
   constexpr int kMain = mainloop_lds<E, BM, BN, CF::SB, CF::NS, WGM, WGN>();
@@ -642,13 +670,19 @@ __global__ __launch_bounds__(SwCfg<E>::kThreads) void k_swiglu(const char* __res
 #pragma unroll
     for (int i = 0; i < KL; ++i) off[i] = kNone;
     if (Q < M) {
-      const int b = Q / nr, q = Q % nr;
-      const int32_t* ri = ref_idx + (size_t(b) * T + nrp[q]) * k;
+      // the chosen references' indices (one 16-byte load per 4), -1 pads
+      const int b = Q / nr;
+      const int4* sj = reinterpret_cast<const int4*>(selj + size_t(Q) * KL);
+      int j[KL];
+#pragma unroll
+      for (int h = 0; h < KL / 4; ++h) {
+        const int4 v = sj[h];
+        j[4 * h] = v.x; j[4 * h + 1] = v.y; j[4 * h + 2] = v.z; j[4 * h + 3] = v.w;
+      }
 #pragma unroll
       for (int i = 0; i < KL; ++i) {
-        const int pos = i < k ? ri[i] : -1;
-        if (pos >= 0) {
-          off[i] = uint32_t(b * nref + ~tab[pos]) * uint32_t(N) * 4u;   // P row of reference ~tab
+        if (j[i] >= 0) {
+          off[i] = uint32_t(b * nref + j[i]) * uint32_t(N) * 4u;    // P row of reference j
           ++kt;
         }
       }
@@ -1169,6 +1203,7 @@ Workspace plan_workspace(const Shape& sh) {
   L.rpos = take(size_t(sh.nref) * 4);
   L.nrp = take(size_t(sh.nr) * 4);
   L.tab = take(size_t(sh.T) * 4);
+  L.selj = take(size_t(sh.B) * sh.nr * sh.kl * 4);
   L.total = off;
   return L;
 }
@@ -1321,7 +1356,7 @@ hipError_t launch_merge(const Shape& sh, int32_t* ref_idx, char* ws, const Works
   const auto* rpos = reinterpret_cast<const int*>(ws + L.rpos);
 #define RKV_MERGE(KL)                                                                        \
   k_topk_merge<KL><<<nb, 64, 0, st>>>(part, ref_idx, sh.B, sh.T, tab, rpos, sh.k, sh.nr,    \
-                                      sh.n_chunks, chunk)
+                                      sh.n_chunks, chunk, reinterpret_cast<int*>(ws + L.selj))
   if (sh.kl == 4) RKV_MERGE(4); else RKV_MERGE(8);
 #undef RKV_MERGE
   return hipGetLastError();
@@ -1340,7 +1375,7 @@ hipError_t launch_ref_proj(const Shape& sh, const void* kv, char* ws, const Work
   return hipGetLastError();
 }
 
-hipError_t launch_swiglu(const Shape& sh, const void* kv, const int32_t* ref_idx, char* ws,
+hipError_t launch_swiglu(const Shape& sh, const void* kv, char* ws,
                          const Workspace& L, hipStream_t st) {
   const int M = sh.B * sh.nr, N = 2 * sh.d_ff;
   if (M == 0) return hipGetLastError();
@@ -1350,10 +1385,8 @@ hipError_t launch_swiglu(const Shape& sh, const void* kv, const int32_t* ref_idx
   const uint32_t pbytes = uint32_t(size_t(sh.B) * sh.nref * N * 4);
 #define RKV_SW(E, KL)                                                                           \
   k_swiglu<E, KL><<<cdiv(N, SwCfg<E>::BN) * cdiv(M, SwCfg<E>::BM), SwCfg<E>::kThreads, 0, st>>>( \
-      p, ws + L.wp, proj, pbytes, ref_idx, ws + L.dh, sh.T, sh.C,                                \
-      reinterpret_cast<const int*>(ws + L.nrp), reinterpret_cast<const int*>(ws + L.tab),         \
-      sh.nref, sh.nr, sh.k,                                                                        \
-      sh.d_ff, M)
+      p, ws + L.wp, proj, pbytes, reinterpret_cast<const int*>(ws + L.selj), ws + L.dh, sh.T,     \
+      sh.C, reinterpret_cast<const int*>(ws + L.nrp), sh.nref, sh.nr, sh.d_ff, M)
   if (sh.bf16) { if (sh.kl == 4) RKV_SW(uint16_t, 4); else RKV_SW(uint16_t, 8); }
   else { if (sh.kl == 4) RKV_SW(float, 4); else RKV_SW(float, 8); }
 #undef RKV_SW
