@@ -22,6 +22,8 @@
 // a matrix must point at any valid row (their results are masked by the
 // epilogue).
 #pragma once
+#include <type_traits>
+
 #include "rkv_device.h"
 
 namespace rkv {
@@ -171,6 +173,7 @@ struct DmaTile {
   static constexpr int kLdA = BM * SB / (1024 * kWaves), kLdB = BN * SB / (1024 * kWaves);
   static constexpr int kLd = kLdA + kLdB;
   static_assert(kSteps % 2 == 0, "fragment double-buffering pairs k-steps");
+  static_assert(NS >= 2, "a stage is requested at least one stage ahead");
   static_assert(kLdA >= 1 && kLdB >= 1, "each wave feeds part of A and of B");
   static_assert(kLd * (NS - 2 > 0 ? NS - 2 : 0) <= 31, "vmcnt window");
 };
@@ -272,22 +275,24 @@ __device__ __forceinline__ void gemm_mainloop_dma(const char* const* pa, const c
       fb[p][j] = *reinterpret_cast<const bf16x8*>(buf + offB[j] + ((kc ^ swB[j]) << 4));
   };
 
-  const int pre = NS - 1 < KT ? NS - 1 : KT;
-  for (int s = 0; s < pre; ++s) issue(s);
-  wait_vm_lgkm(TL::kLd * (pre - 1));
-  block_barrier();
-  load_frags(0, 0, 0);
-  for (int kt = 0; kt < KT; ++kt) {
-    if (kt + NS - 1 < KT) issue(kt + NS - 1);
+  // One stage: its MFMAs, with the next k-step's fragment reads between
+  // them.  ISSUE: the stage NS-1 ahead is requested first; NEXT: a later
+  // stage exists, so the last k-step waits for it, syncs and reads its first
+  // fragments before its own MFMAs (whose fragments are already in
+  // registers).  Both are compile-time, so no branch makes the compiler
+  // drain those reads before the MFMAs.
+  auto stage = [&](int kt, auto issue_c, auto next_c, int younger) {
+    constexpr bool kIssue = decltype(issue_c)::value, kNext = decltype(next_c)::value;
+    if constexpr (kIssue) issue(kt + NS - 1);
 #pragma unroll
     for (int st = 0; st < TL::kSteps; ++st) {
       const int p = st & 1;
       if (st + 1 < TL::kSteps) {
         load_frags(kt, st + 1, p ^ 1);
-      } else if (kt + 1 < KT) {
-        // stage kt+1 must have landed (younger stages may stay in flight),
-        // and every wave must be done with the buffer the next issue reuses
-        const int younger = (KT - 2 - kt) < (NS - 2) ? (KT - 2 - kt) : (NS - 2);
+      } else if constexpr (kNext) {
+        // stage kt+1 must have landed (`younger` later stages may stay in
+        // flight), and every wave must be done with the buffer the next
+        // issue reuses
         wait_vm_lgkm(TL::kLd * younger);
         block_barrier();
         load_frags(kt + 1, 0, p ^ 1);
@@ -306,7 +311,21 @@ __device__ __forceinline__ void gemm_mainloop_dma(const char* const* pa, const c
       __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kReads, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-  }
+  };
+  using yes = std::true_type;
+  using no = std::false_type;
+
+  const int pre = NS - 1 < KT ? NS - 1 : KT;
+  for (int s = 0; s < pre; ++s) issue(s);
+  wait_vm_lgkm(TL::kLd * (pre - 1));
+  block_barrier();
+  load_frags(0, 0, 0);
+  int kt = 0;
+  // stages that request a later one (then NS-2 younger stages stay in flight)
+  for (; kt + NS - 1 < KT; ++kt) stage(kt, yes{}, yes{}, NS - 2);
+  // the last NS-2 stages but one: nothing left to request
+  for (; kt + 1 < KT; ++kt) stage(kt, no{}, yes{}, KT - 2 - kt);
+  if (kt < KT) stage(kt, no{}, no{}, 0);
   // leave no LDS read in flight: callers reuse the LDS right away
   __builtin_amdgcn_s_waitcnt((0xF | (3 << 14)) | (0x7 << 4));
   block_barrier();
