@@ -91,7 +91,13 @@ typedef struct {
 /* GPU-path limits (RKV_ERR_UNSUPPORTED otherwise): C % 64 == 0,
  * d_ff % 32 == 0, d_ff <= 65536, d_c % 32 == 0, d_c % g == 0, B*T < 2^31,
  * T <= 2^26, B*nref*2*d_ff*4 < 2^31 with nref the references per sequence
- * (the reference projections). */
+ * (the reference projections).
+ *
+ * Environment: RKV_DMA_GLOBAL=1 (read at every call) makes the contractions
+ * over kv rows copy their operands to LDS with 64-bit lane addresses instead
+ * of 32-bit offsets from a buffer resource.  Results are bit-identical; the
+ * library takes that form by itself where a tile's kv rows span 2 GB or
+ * more. */
 
 /* Bytes of device workspace rkv_encode / rkv_select need for *p (0 if *p is
  * invalid).  The workspace holds repacked weights, reference projections,

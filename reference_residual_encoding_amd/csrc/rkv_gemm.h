@@ -220,12 +220,19 @@ __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// pa[i] / pb[i] (i < kLdA / kLdB): this lane's source address for DMA
-// instruction i at K stage 0 (row base + dma_slot); rows past the end must
-// point at a valid row.
-template <int BM, int BN, int SB, int NS, int WGM = 2, int WGN = 2>
+// Where DMA instruction i of this lane reads at K stage 0 (row base +
+// dma_slot; rows past the end must point at a valid row), in one of two
+// forms chosen by BUF:
+//  - global form (global_load_lds): pa[i] / pb[i], a 64-bit lane address;
+//  - buffer form (buffer_load ... lds): va[i] / vb[i], a 32-bit byte offset
+//    in the buffer resource ra / rb, with the stage offset in an SGPR, so a
+//    stage costs no vector address arithmetic (measured 4-5% faster on the
+//    token-projection shape).
+template <int BM, int BN, int SB, int NS, int WGM, int WGN, bool BUF>
 __device__ __forceinline__ void gemm_mainloop_dma(const char* const* pa, const char* const* pb,
-                                                  int KT, char* lds,
+                                                  const uint32_t* va, const uint32_t* vb,
+                                                  __amdgpu_buffer_rsrc_t ra,
+                                                  __amdgpu_buffer_rsrc_t rb, int KT, char* lds,
                                                   f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32]) {
   using TL = DmaTile<BM, BN, SB, NS, WGM, WGN>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -240,14 +247,21 @@ __device__ __forceinline__ void gemm_mainloop_dma(const char* const* pa, const c
   auto issue = [&](int s) {
     char* buf = lds + (s % NS) * TL::kStage;
 #pragma unroll
-    for (int i = 0; i < TL::kLdA; ++i)
-      __builtin_amdgcn_global_load_lds(pa[i] + size_t(s) * SB,
-                                       (lds_ptr_t)(buf + (wave * TL::kLdA + i) * 1024), 16, 0, 0);
+    for (int i = 0; i < TL::kLdA; ++i) {
+      lds_ptr_t dst = (lds_ptr_t)(buf + (wave * TL::kLdA + i) * 1024);
+      if constexpr (BUF)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, va[i], s * SB, 0, 0);
+      else
+        __builtin_amdgcn_global_load_lds(pa[i] + size_t(s) * SB, dst, 16, 0, 0);
+    }
 #pragma unroll
-    for (int i = 0; i < TL::kLdB; ++i)
-      __builtin_amdgcn_global_load_lds(pb[i] + size_t(s) * SB,
-                                       (lds_ptr_t)(buf + BM * SB + (wave * TL::kLdB + i) * 1024),
-                                       16, 0, 0);
+    for (int i = 0; i < TL::kLdB; ++i) {
+      lds_ptr_t dst = (lds_ptr_t)(buf + BM * SB + (wave * TL::kLdB + i) * 1024);
+      if constexpr (BUF)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, vb[i], s * SB, 0, 0);
+      else
+        __builtin_amdgcn_global_load_lds(pb[i] + size_t(s) * SB, dst, 16, 0, 0);
+    }
   };
   int offA[TL::kTM], swA[TL::kTM], offB[TL::kTN], swB[TL::kTN];
 #pragma unroll
@@ -355,17 +369,21 @@ __device__ __forceinline__ void acc_to_lds(const f32x16 (&acc)[BM / WGM / 32][BN
 }
 
 // ---------------------------------------------------------------------------
-// One workgroup tile of C = A * B^T: the bf16 path runs the LDS-DMA ring
-// (SB bytes of K per stage, NS stages), the fp32 path the register-staged
-// loop.  rowA(r) / rowB(r) return the first byte of tile-local row r
-// (clamped to a valid row); kbytes is the contraction length in bytes.
 template <typename E, int BM, int BN, int SB, int NS, int WGM = 2, int WGN = 2>
 constexpr int mainloop_lds() {
   return sizeof(E) == 2 ? DmaTile<BM, BN, SB, NS, WGM, WGN>::kLds : Tile<E, BM, BN>::kLds;
 }
 
-template <typename E, int BM, int BN, int SB, int NS, int WGM = 2, int WGN = 2, class RowA,
-          class RowB>
+// One workgroup tile of C = A * B^T: the bf16 path runs the LDS-DMA ring
+// (SB bytes of K per stage, NS stages), the fp32 path the register-staged
+// loop.  rowA(r) / rowB(r) return the first byte of tile-local row r
+// (clamped to a valid row); kbytes is the contraction length in bytes.
+// BUF (bf16 only): the buffer form of the DMA, whose resources start at the
+// tile's row 0 and reach its last row plus kbytes.  It needs rowA / rowB
+// non-decreasing in r and that reach below 2^31 bytes; the host picks the
+// global form where a tile of kv rows could span more.
+template <typename E, int BM, int BN, int SB, int NS, int WGM = 2, int WGN = 2, bool BUF = true,
+          class RowA, class RowB>
 __device__ __forceinline__ void tile_product(const RowA& rowA, const RowB& rowB, int kbytes,
                                              char* lds,
                                              f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32]) {
@@ -373,6 +391,7 @@ __device__ __forceinline__ void tile_product(const RowA& rowA, const RowB& rowB,
     using TL = DmaTile<BM, BN, SB, NS, WGM, WGN>;
     const char* pa[TL::kLdA];
     const char* pb[TL::kLdB];
+    uint32_t va[TL::kLdA], vb[TL::kLdB];
 #pragma unroll
     for (int i = 0; i < TL::kLdA; ++i) {
       const int r = dma_row<TL, SB>(i, TL::kLdA);
@@ -383,7 +402,29 @@ __device__ __forceinline__ void tile_product(const RowA& rowA, const RowB& rowB,
       const int r = dma_row<TL, SB>(i, TL::kLdB);
       pb[i] = rowB(r) + dma_slot<TL, SB>(r);
     }
-    gemm_mainloop_dma<BM, BN, SB, NS, WGM, WGN>(pa, pb, kbytes / SB, lds, acc);
+    // (unused by the global form)
+    __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(nullptr, 0, 0, 0x00020000);
+    __amdgpu_buffer_rsrc_t rb = ra;
+    if constexpr (BUF) {
+      // wave-uniform by construction; readfirstlane keeps them in SGPRs
+      auto uniform = [](const char* p) {
+        const uint64_t u = reinterpret_cast<uint64_t>(p);
+        const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(u));
+        const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(u >> 32));
+        return reinterpret_cast<const char*>((uint64_t(hi) << 32) | lo);
+      };
+      const char* a0 = uniform(rowA(0));
+      const char* b0 = uniform(rowB(0));
+      const int na = __builtin_amdgcn_readfirstlane(int(rowA(BM - 1) - a0) + kbytes);
+      const int nb = __builtin_amdgcn_readfirstlane(int(rowB(BN - 1) - b0) + kbytes);
+#pragma unroll
+      for (int i = 0; i < TL::kLdA; ++i) va[i] = uint32_t(pa[i] - a0);
+#pragma unroll
+      for (int i = 0; i < TL::kLdB; ++i) vb[i] = uint32_t(pb[i] - b0);
+      ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(a0), 0, na, 0x00020000);
+      rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(b0), 0, nb, 0x00020000);
+    }
+    gemm_mainloop_dma<BM, BN, SB, NS, WGM, WGN, BUF>(pa, pb, va, vb, ra, rb, kbytes / SB, lds, acc);
   } else {
     static_assert(WGM == 2 && WGN == 2, "the fp32 loop runs a 2 x 2 wave grid");
     using TL = Tile<E, BM, BN>;

@@ -37,6 +37,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 
 namespace rkv {
 
@@ -369,7 +370,9 @@ __global__ __launch_bounds__(256) void k_ref_store(const E* __restrict__ kv, int
 // each half chunk in increasing j; their lists are then combined into the KL
 // best (d', j) of the chunk restricted to the causal pool (j*s < position),
 // written as partial list c.
-template <typename E, int KL>
+// BUF: the buffer form of the operand DMA (the host checks that a token
+// tile's rows lie within 2^31 bytes).
+template <typename E, int KL, bool BUF>
 __global__ __launch_bounds__(DistCfg<E>::kThreads) void k_dist_topk(
     const char* __restrict__ kv, const char* __restrict__ refs, const float* __restrict__ ysq,
     float2* __restrict__ part, int B, int T, int C, const int* __restrict__ nrp, int nref,
@@ -435,7 +438,7 @@ __global__ __launch_bounds__(DistCfg<E>::kThreads) void k_dist_topk(
   auto rowA = [&](int r) { return rbase + size_t(min(m0 + r, nref - 1)) * rowb; };
   auto rowB = [&](int r) { return base + size_t(nrp[min(n0 + r, nr - 1)]) * rowb; };
   f32x16 acc[BM / WGM / 32][BN / WGN / 32];
-  tile_product<E, BM, BN, CF::SB, CF::NS, WGM, WGN>(rowA, rowB, int(rowb), lds, acc);
+  tile_product<E, BM, BN, CF::SB, CF::NS, WGM, WGN, BUF>(rowA, rowB, int(rowb), lds, acc);
 
   // Stage the dot products half a chunk at a time (the waves of one
   // wave-row); thread (t, sub) scans references sub*SPAN .. +SPAN of each
@@ -631,7 +634,7 @@ __device__ __forceinline__ float silu_fast(float x) {
 // the first layer of f_c is linear and bias-free ([RKV] §2.2 mean eq.,
 // §2.3).  delta_h goes to the token's 4-byte slot of f (dh float index
 // Q*d_ff + f): a (hi, lo) bf16 pair for bf16 runs, fp32 otherwise.
-template <typename E, int KL>
+template <typename E, int KL, bool BUF>
 __global__ __launch_bounds__(SwCfg<E>::kThreads) void k_swiglu(const char* __restrict__ kv,
                                                 const char* __restrict__ wp,
                                                 const float* __restrict__ proj,
@@ -698,7 +701,7 @@ __global__ __launch_bounds__(SwCfg<E>::kThreads) void k_swiglu(const char* __res
   auto rowB = [&](int r) { return wp + size_t(min(n0 + r, N - 1)) * rowb; };
   constexpr int kTM = BM / WGM / 32, kTN = BN / WGN / 32;
   f32x16 acc[kTM][kTN];
-  tile_product<E, BM, BN, CF::SB, CF::NS, WGM, WGN>(rowA, rowB, int(rowb), lds, acc);
+  tile_product<E, BM, BN, CF::SB, CF::NS, WGM, WGN, BUF>(rowA, rowB, int(rowb), lds, acc);
 
   // 2 (set-up). Four consecutive features of one row per lane: BN/8 lanes
   // per row, 16 rows per workgroup step.  Feature quad c holds W1 columns
@@ -1328,6 +1331,26 @@ static int dist_items(const Shape& sh, int n_tt) {
   return int(8 * *std::max_element(per_xcd, per_xcd + 8));
 }
 
+// Whether every tile of `rows` consecutive non-reference tokens (counted
+// over all sequences when `flat`, within each sequence otherwise) has its kv
+// rows, first to last, within 2^31 bytes: the reach of the buffer form of
+// the main loop's DMA.  Rows between them are references; the host schedule
+// gives the exact span.
+// RKV_DMA_GLOBAL=1 in the environment (read at every launch) selects the
+// global form everywhere; both forms compute the same bits.
+static bool kv_tiles_fit_buffer(const Shape& sh, int rows, bool flat) {
+  const char* force = std::getenv("RKV_DMA_GLOBAL");
+  if (force && force[0] == '1') return false;
+  const std::vector<int>& nrp = sh.sched->nrp;
+  const int64_t nr = sh.nr, M = flat ? int64_t(sh.B) * nr : nr;
+  auto pos = [&](int64_t q) { return (q / nr) * sh.T + nrp[size_t(q % nr)]; };
+  int64_t span = 0;
+  for (int64_t q0 = 0; q0 < M; q0 += rows)
+    span = std::max(span, pos(std::min(q0 + rows - 1, M - 1)) - pos(q0));
+  const int64_t rowb = int64_t(sh.C) * sh.esize;
+  return (span + 1) * rowb < (int64_t(1) << 31);
+}
+
 hipError_t launch_dist(const Shape& sh, const void* kv, char* ws, const Workspace& L,
                        hipStream_t st) {
   if (sh.nr == 0) return hipGetLastError();
@@ -1335,14 +1358,19 @@ hipError_t launch_dist(const Shape& sh, const void* kv, char* ws, const Workspac
   const auto* y = reinterpret_cast<const float*>(ws + L.ysq);
   auto* part = reinterpret_cast<float2*>(ws + L.part);
   const auto* nrp = reinterpret_cast<const int*>(ws + L.nrp);
-#define RKV_DIST(E, KL)                                                                      \
+#define RKV_DIST(E, KL, BUF)                                                                 \
   do {                                                                                       \
     const int n_tt = cdiv(sh.nr, DistCfg<E>::BN);                                            \
-    k_dist_topk<E, KL><<<dist_items<E>(sh, n_tt), DistCfg<E>::kThreads, 0, st>>>(            \
+    k_dist_topk<E, KL, BUF><<<dist_items<E>(sh, n_tt), DistCfg<E>::kThreads, 0, st>>>(       \
         p, ws + L.refs, y, part, sh.B, sh.T, sh.C, nrp, sh.nref, sh.nr, sh.n_chunks, n_tt);  \
   } while (0)
-  if (sh.bf16) { if (sh.kl == 4) RKV_DIST(uint16_t, 4); else RKV_DIST(uint16_t, 8); }
-  else { if (sh.kl == 4) RKV_DIST(float, 4); else RKV_DIST(float, 8); }
+  if (sh.bf16) {
+    const bool buf = kv_tiles_fit_buffer(sh, DistCfg<uint16_t>::BN, false);
+    if (sh.kl == 4) { if (buf) RKV_DIST(uint16_t, 4, true); else RKV_DIST(uint16_t, 4, false); }
+    else { if (buf) RKV_DIST(uint16_t, 8, true); else RKV_DIST(uint16_t, 8, false); }
+  } else {
+    if (sh.kl == 4) RKV_DIST(float, 4, false); else RKV_DIST(float, 8, false);
+  }
 #undef RKV_DIST
   return hipGetLastError();
 }
@@ -1383,12 +1411,18 @@ hipError_t launch_swiglu(const Shape& sh, const void* kv, char* ws,
   const auto* proj = reinterpret_cast<const float*>(ws + L.proj);
   // P is addressed with 32-bit byte offsets (its size is checked on the host)
   const uint32_t pbytes = uint32_t(size_t(sh.B) * sh.nref * N * 4);
-#define RKV_SW(E, KL)                                                                           \
-  k_swiglu<E, KL><<<cdiv(N, SwCfg<E>::BN) * cdiv(M, SwCfg<E>::BM), SwCfg<E>::kThreads, 0, st>>>( \
+#define RKV_SW(E, KL, BUF)                                                                      \
+  k_swiglu<E, KL, BUF><<<cdiv(N, SwCfg<E>::BN) * cdiv(M, SwCfg<E>::BM), SwCfg<E>::kThreads, 0,    \
+                         st>>>(                                                                 \
       p, ws + L.wp, proj, pbytes, reinterpret_cast<const int*>(ws + L.selj), ws + L.dh, sh.T,     \
       sh.C, reinterpret_cast<const int*>(ws + L.nrp), sh.nref, sh.nr, sh.d_ff, M)
-  if (sh.bf16) { if (sh.kl == 4) RKV_SW(uint16_t, 4); else RKV_SW(uint16_t, 8); }
-  else { if (sh.kl == 4) RKV_SW(float, 4); else RKV_SW(float, 8); }
+  if (sh.bf16) {
+    const bool buf = kv_tiles_fit_buffer(sh, SwCfg<uint16_t>::BM, true);
+    if (sh.kl == 4) { if (buf) RKV_SW(uint16_t, 4, true); else RKV_SW(uint16_t, 4, false); }
+    else { if (buf) RKV_SW(uint16_t, 8, true); else RKV_SW(uint16_t, 8, false); }
+  } else {
+    if (sh.kl == 4) RKV_SW(float, 4, false); else RKV_SW(float, 8, false);
+  }
 #undef RKV_SW
   return hipGetLastError();
 }

@@ -1,5 +1,6 @@
 """GPU parity: the HIP path (called through the C ABI) against the fp64 CPU
 oracle on the same seeded inputs.  Needs an MI355X."""
+import os
 import numpy as np
 import pytest
 import torch
@@ -191,6 +192,26 @@ def test_encode_is_deterministic():
     w = generate(cfg)
     _, _, h1, _ = P.run_encode(w)
     _, _, h2, _ = P.run_encode(w)
+    for key in ("ref_idx", "codes", "scale", "zmin", "z"):
+        assert np.array_equal(h1[key].view(np.uint8), h2[key].view(np.uint8)), key
+
+
+@pytest.mark.parametrize("cfg", [LLAMA8K.with_(name="llama_B3_T1500", B=3, T=1500),
+                                 LLAMA8K_DYN.with_(name="llama_dyn_B2_T3000", B=2, T=3000)],
+                         ids=lambda c: c.name)
+def test_encode_dma_forms_bit_identical(cfg):
+    """The contractions over kv rows copy operands to LDS through buffer
+    resources (32-bit offsets from each tile's first row) unless a tile spans
+    2 GB; RKV_DMA_GLOBAL=1 forces the 64-bit-address form.  Both must give
+    the same bits, including token tiles that cross from one sequence into
+    the next (B > 1, nr not a multiple of the tile)."""
+    w = generate(cfg)
+    _, _, h1, _ = P.run_encode(w)
+    os.environ["RKV_DMA_GLOBAL"] = "1"
+    try:
+        _, _, h2, _ = P.run_encode(w)
+    finally:
+        del os.environ["RKV_DMA_GLOBAL"]
     for key in ("ref_idx", "codes", "scale", "zmin", "z"):
         assert np.array_equal(h1[key].view(np.uint8), h2[key].view(np.uint8)), key
 
