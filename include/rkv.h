@@ -89,7 +89,7 @@ typedef struct {
 } rkv_params;
 
 /* GPU-path limits (RKV_ERR_UNSUPPORTED otherwise): C % 64 == 0,
- * d_ff % 32 == 0, d_ff <= 65536, d_c % 32 == 0, d_c % g == 0, B*T < 2^31,
+ * d_ff % 32 == 0, d_ff <= 65536, d_c % 32 == 0, d_c <= 65536, d_c % g == 0, B*T < 2^31,
  * T <= 2^26, B*nref*2*d_ff*4 < 2^31 with nref the references per sequence
  * (the reference projections).
  *

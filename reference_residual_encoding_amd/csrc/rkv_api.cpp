@@ -79,6 +79,8 @@ rkv_status check_params(const rkv_params* p) {
   if (C % 64 != 0) return fail(RKV_ERR_UNSUPPORTED, "C = 2*N*D must be a multiple of 64 (got %lld)", C);
   if (p->d_ff % 32 != 0) return fail(RKV_ERR_UNSUPPORTED, "d_ff must be a multiple of 32 (got %d)", p->d_ff);
   if (p->d_ff > 65536) return fail(RKV_ERR_UNSUPPORTED, "d_ff must be at most 65536 (got %d)", p->d_ff);
+  // (keeps a 256-row tile of the latent operands within a buffer resource)
+  if (p->d_c > 65536) return fail(RKV_ERR_UNSUPPORTED, "d_c must be at most 65536 (got %d)", p->d_c);
   if ((long long)p->B * p->T >= (1LL << 31)) return fail(RKV_ERR_UNSUPPORTED, "B*T must be below 2^31");
   if (p->T > (1 << 26)) return fail(RKV_ERR_UNSUPPORTED, "T must be at most 2^26 (got %d)", p->T);
   if ((long long)p->B * p->T * C >= (1LL << 40)) return fail(RKV_ERR_UNSUPPORTED, "B*T*C too large");

@@ -78,6 +78,7 @@ def test_workspace_size_zero_for_invalid_params():
     ("g", 24, R.RKV_ERR_UNSUPPORTED), ("k", 9, R.RKV_ERR_UNSUPPORTED),
     ("d_c", 48, R.RKV_ERR_UNSUPPORTED), ("g", 64, R.RKV_ERR_UNSUPPORTED),
     ("d_ff", 1000, R.RKV_ERR_UNSUPPORTED), ("D", 10, R.RKV_ERR_UNSUPPORTED),
+    ("d_c", 65536 + 32, R.RKV_ERR_UNSUPPORTED), ("d_ff", 65536 + 32, R.RKV_ERR_UNSUPPORTED),
     ("ref_alpha", -0.5, R.RKV_ERR_INVALID_ARG), ("ref_alpha", float("nan"), R.RKV_ERR_INVALID_ARG),
     ("n_sink", -1, R.RKV_ERR_INVALID_ARG),
 ])
