@@ -101,21 +101,30 @@ __device__ __forceinline__ int refs_before(const SchedView& v, int t, bool& is_r
 // Keep the KL smallest (d, j) pairs in ascending (d, j) order, for
 // candidates that arrive in increasing j: a newcomer then goes after every
 // kept pair of equal d, so the strict comparison d < d_i decides alone.
-// Branch-free select network (an infinite d never enters).
+// Every slot takes its new pair from the compares with the old list: it
+// keeps its own, takes the newcomer, or takes the pair of the slot before
+// it (the distances through min / med3), so no slot waits on another and a
+// pair displaced into a run of equal distances moves down with the run
+// instead of dropping out.  Branch-free; d must not be NaN (an infinite d
+// never enters).
 template <int KL>
 __device__ __forceinline__ void topk_push(float (&bd)[KL], int (&bi)[KL], float d, int j) {
-  // compare-and-swap bubble: the smaller pair stays, the larger moves on
-  float x = d;
-  int xj = j;
+  bool c[KL];
+#pragma unroll
+  for (int i = 0; i < KL; ++i) c[i] = d < bd[i];
+  float nd[KL];
+  int ni[KL];
+  nd[0] = fminf(bd[0], d);
+  ni[0] = c[0] ? j : bi[0];
+#pragma unroll
+  for (int i = 1; i < KL; ++i) {
+    nd[i] = __builtin_amdgcn_fmed3f(bd[i - 1], bd[i], d);
+    ni[i] = c[i - 1] ? bi[i - 1] : (c[i] ? j : bi[i]);
+  }
 #pragma unroll
   for (int i = 0; i < KL; ++i) {
-    const bool c = x < bd[i];
-    const float nd = c ? x : bd[i];
-    const int ni = c ? xj : bi[i];
-    x = c ? bd[i] : x;
-    xj = c ? bi[i] : xj;
-    bd[i] = nd;
-    bi[i] = ni;
+    bd[i] = nd[i];
+    bi[i] = ni[i];
   }
 }
 

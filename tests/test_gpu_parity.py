@@ -216,6 +216,51 @@ def test_encode_dma_forms_bit_identical(cfg):
         assert np.array_equal(h1[key].view(np.uint8), h2[key].view(np.uint8)), key
 
 
+def _bf16_bits(x):
+    u = np.asarray(x, dtype=np.float32).view(np.uint32)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_encode_exact_ties_keep_smaller_positions(dtype):
+    """Equal distances go to the smaller position ([RKV] §2.1, the (d, j)
+    order).  Six references are one identical row, a later reference equals
+    the probe tokens, and the probes sit near the duplicate row: each probe's
+    distances to the six are exactly equal on both sides, and the later,
+    closer reference arrives after four of them fill a list.  The kept set
+    must be that reference and the three smallest duplicate positions, with
+    no tie excused."""
+    cfg = LLAMA8K.with_(name=f"ties_{dtype}", B=1, T=1024, N=2, D=32, d_ff=64, d_c=64, k=4,
+                        g=32, b=4, stride=8, n_protos=8, dtype=dtype)
+    w = generate(cfg)
+    kv = w.kv_f32()[0].astype(np.float32)              # [T, C]
+    s = cfg.stride
+    dup = [s * m for m in (3, 5, 9, 12, 20, 21)]       # reference positions
+    close, probes = s * 30, [250, 301, 517, 1001]      # a later reference; non-reference tokens
+    rng = np.random.default_rng(5)
+    base = kv[dup[0]].copy()
+    probe = base + 0.1 * np.abs(base).mean() * rng.standard_normal(cfg.C).astype(np.float32)
+    rows = {t: base for t in dup}
+    rows[close] = probe
+    rows.update({t: probe for t in probes})
+    for t, r in rows.items():
+        kv[t] = r
+    if dtype == "bf16":
+        w.kv[0] = _bf16_bits(kv)
+    else:
+        w.kv[0] = kv
+    _, _, h, _ = P.run_encode(w)
+    kvb = w.kv_f32()[0].astype(np.float64)
+    W1, W2, W3 = (x.astype(np.float64) for x in w.weights_f32())
+    orc = O.encode_tokens(kvb, W1, W2, W3, np.array(probes), k=cfg.k, g=cfg.g, b=cfg.b, s=s)
+    want = np.sort(np.array([close] + dup[:3]))
+    for i, t in enumerate(probes):
+        assert np.array_equal(np.sort(orc["ref_idx"][i]), want), (t, orc["ref_idx"][i])
+        assert np.array_equal(h["ref_idx"][0, t], orc["ref_idx"][i]), (t, h["ref_idx"][0, t], want)
+    # every other token: the usual bars
+    P.compare_tokens(w, h, {0: np.arange(cfg.T)}, log=print)
+
+
 @pytest.mark.parametrize("b,g", [(4, 32), (2, 32), (4, 8), (2, 16), (4, 64), (16, 32)])
 def test_quantize_export_bit_exact(b, g):
     rng = np.random.default_rng(b * 100 + g)
