@@ -178,3 +178,43 @@ def test_append_bench_shape():
     pos = np.array([cfg.T - 1 - 3 * b for b in range(cfg.B)])
     c.append(pos)
     c.check("bench shape")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_append_exact_ties_keep_smaller_positions(dtype):
+    """The encode's exact-tie case on the append path: six references are
+    one identical row, a later reference equals the appended tokens, so each
+    token keeps that reference and the three smallest duplicate positions
+    ([RKV] §2.1, the (d, j) order), with no tie excused."""
+    from synth.configs import LLAMA8K
+    from oracle import rkv_oracle as O
+    cfg = LLAMA8K.with_(name=f"append_ties_{dtype}", B=1, T=1024, N=2, D=32, d_ff=64, d_c=64,
+                        k=4, g=32, b=4, stride=8, n_protos=8, dtype=dtype)
+    w = generate(cfg)
+    kv = w.kv_f32()[0].astype(np.float32)
+    s = cfg.stride
+    dup = [s * m for m in (3, 5, 9, 12, 20, 21)]
+    close, probes = s * 30, [250, 301, 517, 1001]
+    rng = np.random.default_rng(5)
+    base = kv[dup[0]].copy()
+    probe = base + 0.1 * np.abs(base).mean() * rng.standard_normal(cfg.C).astype(np.float32)
+    for t in dup:
+        kv[t] = base
+    for t in [close] + probes:
+        kv[t] = probe
+    if dtype == "bf16":
+        u = kv.view(np.uint32)
+        w.kv[0] = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    else:
+        w.kv[0] = kv
+    _log(f"[case] append exact ties {dtype}")
+    c = Cache(w, prefill_refs=True)
+    for t in probes:
+        c.append(np.array([t]))
+    torch.cuda.synchronize()
+    got = c.ref_idx.cpu().numpy()[0]
+    want = np.sort(np.array([close] + dup[:3]))
+    for t in probes:
+        assert np.array_equal(got[t], want), (t, got[t], want)
+    c.check(cfg.name)
+
