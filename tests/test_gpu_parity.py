@@ -221,8 +221,19 @@ def _bf16_bits(x):
     return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
 
 
+TIE_LAYOUTS = {
+    # one chunk, one scan span: the displaced pair meets the run of ties
+    "one_chunk": dict(T=1024, dup=(3, 5, 9, 12, 20, 21), close=30, probes=(250, 301, 517, 1001)),
+    # duplicates in both halves of chunk 0 and in chunk 1 (192 references
+    # per chunk): the two-list combine and the chunk merge see the ties
+    "across_chunks": dict(T=2560, dup=(100, 150, 191, 192, 200, 250), close=300,
+                          probes=(2405, 2466, 2559)),
+}
+
+
+@pytest.mark.parametrize("layout", list(TIE_LAYOUTS))
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_encode_exact_ties_keep_smaller_positions(dtype):
+def test_encode_exact_ties_keep_smaller_positions(dtype, layout):
     """Equal distances go to the smaller position ([RKV] §2.1, the (d, j)
     order).  Six references are one identical row, a later reference equals
     the probe tokens, and the probes sit near the duplicate row: each probe's
@@ -230,13 +241,14 @@ def test_encode_exact_ties_keep_smaller_positions(dtype):
     closer reference arrives after four of them fill a list.  The kept set
     must be that reference and the three smallest duplicate positions, with
     no tie excused."""
-    cfg = LLAMA8K.with_(name=f"ties_{dtype}", B=1, T=1024, N=2, D=32, d_ff=64, d_c=64, k=4,
-                        g=32, b=4, stride=8, n_protos=8, dtype=dtype)
+    lay = TIE_LAYOUTS[layout]
+    cfg = LLAMA8K.with_(name=f"ties_{dtype}_{layout}", B=1, T=lay["T"], N=2, D=32, d_ff=64,
+                        d_c=64, k=4, g=32, b=4, stride=8, n_protos=8, dtype=dtype)
     w = generate(cfg)
     kv = w.kv_f32()[0].astype(np.float32)              # [T, C]
     s = cfg.stride
-    dup = [s * m for m in (3, 5, 9, 12, 20, 21)]       # reference positions
-    close, probes = s * 30, [250, 301, 517, 1001]      # a later reference; non-reference tokens
+    dup = [s * m for m in lay["dup"]]                  # reference positions
+    close, probes = s * lay["close"], list(lay["probes"])  # a later reference; non-references
     rng = np.random.default_rng(5)
     base = kv[dup[0]].copy()
     probe = base + 0.1 * np.abs(base).mean() * rng.standard_normal(cfg.C).astype(np.float32)
