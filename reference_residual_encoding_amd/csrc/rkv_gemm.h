@@ -10,17 +10,18 @@
 //  - bf16 operands use v_mfma_f32_32x32x16_bf16 (products exact, fp32 sums);
 //    fp32 operands use v_mfma_f32_32x32x2_f32.  Both write the same 32 x 32
 //    accumulator layout, so every epilogue serves both element types.
-//  - K advances 128 bytes per stage (64 bf16 or 32 fp32).  Stages are
-//    double-buffered in LDS; each thread stages 16-byte chunks through
-//    registers, so the next stage's global loads are in flight while the
-//    current stage feeds the matrix cores.  One barrier per stage.
-//  - LDS rows are padded by 16 bytes: the 32 lanes of a half-wave that read
-//    32 consecutive rows at the same K offset hit distinct banks.
+//  - bf16: an LDS-DMA ring (gemm_mainloop_dma below): the operands go from
+//    HBM/L2 straight into NS stages of LDS, no register staging.
+//  - fp32 (gemm_mainloop, next): K advances 128 bytes (32 values) per stage;
+//    stages are double-buffered in LDS and each thread stages 16-byte chunks
+//    through registers, so the next stage's global loads are in flight
+//    while the current stage feeds the matrix cores.  One barrier per
+//    stage.  LDS rows are padded by 16 bytes: the 32 lanes of a half-wave
+//    that read 32 consecutive rows at the same K offset hit distinct banks.
 //
-// Callers hand in, per thread, the address of the 16-byte chunk it stages for
-// each of its rows (row = tid/8 + 32*i, chunk = tid%8); rows past the end of
-// a matrix must point at any valid row (their results are masked by the
-// epilogue).
+// tile_product (at the end) is the entry: callers give the first byte of
+// each tile row (rows past the end of a matrix clamped to a valid row,
+// their results masked by the epilogue).
 #pragma once
 #include <type_traits>
 
@@ -142,7 +143,8 @@ __device__ __forceinline__ void gemm_mainloop(const char* (&pa)[BM / 32],
 }
 
 // ---------------------------------------------------------------------------
-// bf16 main loop: LDS-DMA ring (gfx950 global_load_lds_dwordx4).
+// bf16 main loop: LDS-DMA ring (gfx950 buffer_load_dwordx4 ... lds, or
+// global_load_lds_dwordx4 where a tile spans more than a buffer reaches).
 //
 // Same tile and accumulator layout as gemm_mainloop, but:
 //  - operands travel HBM/L2 -> LDS directly (no VGPR staging), NS stages of
