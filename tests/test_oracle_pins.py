@@ -125,6 +125,13 @@ def test_fc_matches_torch_fp64(tiny):
     want = (torch.nn.functional.silu(torch.from_numpy(x) @ torch.from_numpy(W1))
             * (torch.from_numpy(x) @ torch.from_numpy(W2))) @ torch.from_numpy(W3)
     np.testing.assert_allclose(O.f_c(x, W1, W2, W3), want.numpy(), rtol=1e-12, atol=1e-14)
+    # square weights, so a transposed W1, W2 or W3 would still multiply
+    rng = np.random.default_rng(5)
+    Ws = [rng.standard_normal((16, 16)) / 4 for _ in range(3)]
+    xs = rng.standard_normal((7, 16))
+    t = [torch.from_numpy(a) for a in (xs, *Ws)]
+    want = (torch.nn.functional.silu(t[0] @ t[1]) * (t[0] @ t[2])) @ t[3]
+    np.testing.assert_allclose(O.f_c(xs, *Ws), want.numpy(), rtol=1e-12, atol=1e-14)
 
 
 def test_z_is_zero_when_token_equals_its_references():
@@ -279,6 +286,35 @@ def test_quantiser_error_bounds(b):
     exact2 = sum((e - a) * (zf[:, a:e].max(1) - zf[:, a:e].min(1)) ** 2
                  for a, e in O.group_bounds(128, g))
     assert np.all(np.sqrt(exact2) / (2 * L) <= math.sqrt(g / 2) / L * np.linalg.norm(zf, axis=1) + 1e-12)
+
+
+def test_quantiser_codes_use_the_stored_fp16_grid():
+    """[RKV] §2.4 with reading: codes against the stored Delta_h and m_h.
+    tests/golden/quant_stored_grid.txt derives by hand a group whose fp16
+    minimum moves off min and one whose fp16 step moves off Delta; against the
+    unrounded numbers four codes of each group would differ."""
+    gd = _read_kv(os.path.join(GOLD, "quant_stored_grid.txt"))
+    z = np.array([[int(v) / 4096.0 for v in gd["z_num_4096"]]])
+    q, dh, mh = O.quantize(z, 8, 4)
+    assert dh[0].astype(np.float64).tolist() == [float(v) for v in gd["delta_h"]]
+    assert mh[0].astype(np.float64).tolist() == [float(v) for v in gd["zmin_h"]]
+    assert q[0].tolist() == [int(v) for v in gd["codes"]]
+    deq = O.dequantize(q, dh, mh, 8)[0].astype(np.float64)
+    want = [float(mh[0, j // 8]) + q[0, j] * float(dh[0, j // 8]) for j in range(16)]
+    assert deq.tolist() == want
+
+
+def test_quantiser_decides_codes_on_the_float32_latent():
+    """Reading: the integer decision is taken in float32.  The group
+    {0, 15} fixes Delta_h = 1, m_h = 0.  3.5 - 2^-30 lies below the half-way
+    point in float64 (code 3), but float32 has spacing 2^-22 near 3.5, so the
+    latent rounds to 3.5 and half-to-even gives code 4; 5.5 + 2^-30 rounds to
+    5.5 and gives 6 (float64: 6 as well); 6.5 - 2^-30 gives 6 either way."""
+    z = np.array([[0.0, 15.0, 3.5 - 2.0 ** -30, 5.5 + 2.0 ** -30, 6.5 - 2.0 ** -30,
+                   1.0, 2.0, 3.0]])
+    q, dh, mh = O.quantize(z, 8, 4)
+    assert float(dh[0, 0]) == 1.0 and float(mh[0, 0]) == 0.0
+    assert q[0].tolist() == [0, 15, 4, 6, 6, 1, 2, 3]
 
 
 def test_short_last_group():
@@ -492,15 +528,29 @@ def test_reference_schedule_reproduces_table_vi_counts():
     assert got == g["count"]
 
 
+@pytest.mark.parametrize("ns", [4, 1000])
 @pytest.mark.parametrize("alpha", [0.001, 0.02, 0.05, 0.1])
-def test_reference_count_follows_the_logarithmic_approximation(alpha):
-    """[RKV] §2.6: ignoring the floor, N_ref(T) ~ log_{1+a}(1 + a (T - n_sink) / s0).
-    The floor only shortens gaps, so the exact count is at least the
-    approximation, and close to it."""
-    T, s0, ns = 262144, 10, 4
+def test_reference_count_follows_the_logarithmic_approximation(alpha, ns):
+    """[RKV] §2.6: ignoring the floor, N_ref(T) ~ log_{1+a}(1 + a (T - n_sink) / s0)
+    references after the sinks.  The floor only shortens gaps, so the exact
+    count is at least the approximation, and close to it.  A thousand sinks
+    make the n_sink offset inside the floor visible in the count."""
+    T, s0 = 262144, 10
     n = len(O.reference_schedule(T, s0, alpha, ns)) - ns
     approx = math.log1p(alpha * (T - ns) / s0) / math.log1p(alpha)
     assert approx <= n <= 1.02 * approx + 2
+
+
+def test_dynamic_schedule_with_sinks_matches_hand_derivation():
+    """[RKV] §2.6 recurrence with n_sink = 1000, alpha = 0.02, s0 = 10: the
+    first sixteen positions after the sinks, derived by hand in
+    tests/golden/dynamic_schedule_sinks.txt (the gap grows with p - n_sink)."""
+    gd = _read_kv(os.path.join(GOLD, "dynamic_schedule_sinks.txt"))
+    ns, alpha, s0 = int(gd["n_sink"][0]), float(gd["alpha"][0]), int(gd["s0"][0])
+    want = [int(v) for v in gd["after_sinks"]]
+    r = O.reference_schedule(want[-1] + 1, s0, alpha, ns)
+    assert r[:ns].tolist() == list(range(ns))
+    assert r[ns:].tolist() == want
 
 
 def test_reference_schedule_special_cases():
@@ -606,6 +656,18 @@ def test_append_of_a_reference_position_is_stored_with_a_zero_record(tiny):
 
 
 # ------------------------------------------------------------ identity mode
+
+def test_identity_mode_rounds_the_float32_latent_to_fp16():
+    """Reading: in identity mode the stored fp16 value is rounded from the
+    latent's float32 value.  1 + 2^-11 + 2^-40 lies just above the half-way
+    point between the fp16 values 1 and 1 + 2^-10, but float32 (spacing
+    2^-23 there) drops the 2^-40, leaving an exact tie that goes to the even
+    value 1.0 (bits 0x3c00); 1 + 3*2^-11 rounds up to 1 + 2^-9 (0x3c02)
+    either way."""
+    z = np.array([[1.0 + 2.0 ** -11 + 2.0 ** -40, 1.0 + 3 * 2.0 ** -11]])
+    q, _, _ = O.quantize(z, 32, 16)
+    assert q[0].tolist() == [0x3C00, 0x3C02]
+
 
 def test_identity_mode_stores_the_latent_as_fp16():
     """[RKV] §2.4: with quantisation off Q is the identity; the record is the
