@@ -140,13 +140,66 @@ def params(*, B, T, N, D, d_ff, d_c, k, g, b, ref_stride, dtype, n_sink=0,
                       ref_format)
 
 
-def _p(x) -> Optional[int]:
-    """Device pointer of a tensor (or an int / None)."""
+_BF16 = ("torch.bfloat16",)
+_F32 = ("torch.float32",)
+_I32 = ("torch.int32",)
+_U8 = ("torch.uint8",)
+_HALF = ("torch.float16", "torch.int16", "torch.uint16")   # fp16 bits of Delta_h, m_h
+
+
+def _p(x, name: str = "pointer", dtypes=None, nbytes: int = 0) -> Optional[int]:
+    """Device pointer of a tensor (or an int / None), checked before any call.
+
+    A tensor must live on the GPU, be contiguous, have one of `dtypes`
+    (names as ``str(tensor.dtype)``) when given, and hold at least `nbytes`
+    bytes; otherwise ValueError, so that no host address, strided view or
+    short buffer reaches a kernel.  A plain int is passed through as a raw
+    device address (the caller's responsibility)."""
     if x is None:
         return None
     if isinstance(x, int):
         return x
+    if not getattr(x, "is_cuda", False):
+        raise ValueError(f"{name}: tensor must be on the GPU (device {getattr(x, 'device', '?')})")
+    if not x.is_contiguous():
+        raise ValueError(f"{name}: tensor must be contiguous")
+    if dtypes is not None and str(x.dtype) not in dtypes:
+        raise ValueError(f"{name}: dtype {x.dtype} not one of {', '.join(dtypes)}")
+    have = x.numel() * x.element_size()
+    if have < nbytes:
+        raise ValueError(f"{name}: {have} bytes, needs at least {nbytes}")
     return x.data_ptr()
+
+
+def _elem(p: "rkv_params"):
+    """(dtype names, bytes per element) of kv / weights for p.dtype."""
+    return (_BF16, 2) if p.dtype == RKV_BF16 else (_F32, 4)
+
+
+def _out_elem(out_dtype: int):
+    return (_BF16, 2) if out_dtype == RKV_BF16 else (_F32, 4)
+
+
+def _record_sizes(p: "rkv_params", rows: int):
+    """Bytes of codes, and of scale / zmin each, for `rows` records."""
+    codes = rows * p.d_c * p.b // 8 if p.b > 0 else 0
+    groups = 0 if p.b == 16 or p.g <= 0 else p.d_c // p.g
+    return max(codes, 0), max(rows * groups * 2, 0)
+
+
+def _n_ref(p: "rkv_params") -> int:
+    n = lib().rkv_reference_positions(ctypes.byref(p), None, 0)
+    return max(int(n), 0)
+
+
+def _ref_store(p: "rkv_params", kv, name="kv"):
+    """The stored references: kv [B][T][C] at input precision, or the FP8
+    store [B][n_ref][C] of bytes."""
+    C = 2 * p.N * p.D
+    if p.ref_format == RKV_REF_FP8:
+        return _p(kv, name, _U8, p.B * _n_ref(p) * C)
+    dt, es = _elem(p)
+    return _p(kv, name, dt, p.B * p.T * C * es)
 
 
 def _s(stream) -> Optional[int]:
@@ -176,9 +229,15 @@ def rkv_encode_workspace_bytes(p: rkv_params) -> int:
 
 def rkv_encode(p: rkv_params, kv, w1, w2, w3, ref_idx, codes, scale, zmin, z, workspace,
                workspace_bytes: int, stream=None, *, check: bool = True) -> int:
-    st = lib().rkv_encode(ctypes.byref(p), _p(kv), _p(w1), _p(w2), _p(w3), _p(ref_idx),
-                          _p(codes), _p(scale), _p(zmin), _p(z), _p(workspace),
-                          int(workspace_bytes), _s(stream))
+    dt, es = _elem(p)
+    C, rows = 2 * p.N * p.D, p.B * p.T
+    cb, sb = _record_sizes(p, rows)
+    args = (_p(kv, "kv", dt, rows * C * es), _p(w1, "w1", dt, C * p.d_ff * es),
+            _p(w2, "w2", dt, C * p.d_ff * es), _p(w3, "w3", dt, p.d_ff * p.d_c * es),
+            _p(ref_idx, "ref_idx", _I32, rows * p.k * 4), _p(codes, "codes", _U8, cb),
+            _p(scale, "scale", _HALF, sb), _p(zmin, "zmin", _HALF, sb),
+            _p(z, "z", _F32, rows * p.d_c * 4), _p(workspace, "workspace", None, workspace_bytes))
+    st = lib().rkv_encode(ctypes.byref(p), *args, int(workspace_bytes), _s(stream))
     return _check("rkv_encode", st) if check else st
 
 
@@ -186,21 +245,34 @@ def rkv_dequant_gather(p: rkv_params, codes, scale, zmin, idx, n_idx: int, out, 
                        stream=None, *, check: bool = True) -> int:
     if isinstance(out_dtype, str):
         out_dtype = {"f32": RKV_F32, "bf16": RKV_BF16}[out_dtype]
-    st = lib().rkv_dequant_gather(ctypes.byref(p), _p(codes), _p(scale), _p(zmin), _p(idx),
-                                  int(n_idx), _p(out), int(out_dtype), _s(stream))
+    rows, n = p.B * p.T, max(int(n_idx), 0)
+    cb, sb = _record_sizes(p, rows)
+    odt, oes = _out_elem(out_dtype)
+    st = lib().rkv_dequant_gather(ctypes.byref(p), _p(codes, "codes", _U8, cb),
+                                  _p(scale, "scale", _HALF, sb), _p(zmin, "zmin", _HALF, sb),
+                                  _p(idx, "idx", _I32, n * 4), int(n_idx),
+                                  _p(out, "out", odt, n * p.d_c * oes), int(out_dtype),
+                                  _s(stream))
     return _check("rkv_dequant_gather", st) if check else st
 
 
 def rkv_quantize(p: rkv_params, z, rows: int, codes, scale, zmin, stream=None, *,
                  check: bool = True) -> int:
-    st = lib().rkv_quantize(ctypes.byref(p), _p(z), int(rows), _p(codes), _p(scale), _p(zmin),
-                            _s(stream))
+    n = max(int(rows), 0)
+    cb, sb = _record_sizes(p, n)
+    st = lib().rkv_quantize(ctypes.byref(p), _p(z, "z", _F32, n * p.d_c * 4), int(rows),
+                            _p(codes, "codes", _U8, cb), _p(scale, "scale", _HALF, sb),
+                            _p(zmin, "zmin", _HALF, sb), _s(stream))
     return _check("rkv_quantize", st) if check else st
 
 
 def rkv_select(p: rkv_params, kv, ref_idx, workspace, workspace_bytes: int, stream=None, *,
                check: bool = True) -> int:
-    st = lib().rkv_select(ctypes.byref(p), _p(kv), _p(ref_idx), _p(workspace),
+    dt, es = _elem(p)
+    rows = p.B * p.T
+    st = lib().rkv_select(ctypes.byref(p), _p(kv, "kv", dt, rows * 2 * p.N * p.D * es),
+                          _p(ref_idx, "ref_idx", _I32, rows * p.k * 4),
+                          _p(workspace, "workspace", None, workspace_bytes),
                           int(workspace_bytes), _s(stream))
     return _check("rkv_select", st) if check else st
 
@@ -226,9 +298,17 @@ def rkv_restore(p: rkv_params, codes, scale, zmin, ref_idx, kv, wd, idx, n_idx: 
                 *, check: bool = True) -> int:
     if isinstance(out_dtype, str):
         out_dtype = {"f32": RKV_F32, "bf16": RKV_BF16}[out_dtype]
-    st = lib().rkv_restore(ctypes.byref(p), _p(codes), _p(scale), _p(zmin), _p(ref_idx), _p(kv),
-                           _p(wd), _p(idx), int(n_idx), float(rope_theta), _p(out),
-                           int(out_dtype), _p(workspace), int(workspace_bytes), _s(stream))
+    dt, es = _elem(p)
+    C, rows, n = 2 * p.N * p.D, p.B * p.T, max(int(n_idx), 0)
+    cb, sb = _record_sizes(p, rows)
+    odt, oes = _out_elem(out_dtype)
+    st = lib().rkv_restore(ctypes.byref(p), _p(codes, "codes", _U8, cb),
+                           _p(scale, "scale", _HALF, sb), _p(zmin, "zmin", _HALF, sb),
+                           _p(ref_idx, "ref_idx", _I32, rows * p.k * 4), _ref_store(p, kv),
+                           _p(wd, "wd", dt, p.d_c * C * es), _p(idx, "idx", _I32, n * 4),
+                           int(n_idx), float(rope_theta), _p(out, "out", odt, n * C * oes),
+                           int(out_dtype), _p(workspace, "workspace", None, workspace_bytes),
+                           int(workspace_bytes), _s(stream))
     return _check("rkv_restore", st) if check else st
 
 
@@ -238,8 +318,16 @@ def rkv_append_workspace_bytes(p: rkv_params) -> int:
 
 def rkv_append(p: rkv_params, kv, kv_new, pos, w1, w2, w3, ref_idx, codes, scale, zmin, z,
                workspace, workspace_bytes: int, stream=None, *, check: bool = True) -> int:
-    st = lib().rkv_append(ctypes.byref(p), _p(kv), _p(kv_new), _p(pos), _p(w1), _p(w2), _p(w3),
-                          _p(ref_idx), _p(codes), _p(scale), _p(zmin), _p(z), _p(workspace),
+    dt, es = _elem(p)
+    C, rows = 2 * p.N * p.D, p.B * p.T
+    cb, sb = _record_sizes(p, rows)
+    st = lib().rkv_append(ctypes.byref(p), _ref_store(p, kv), _p(kv_new, "kv_new", dt, p.B * C * es),
+                          _p(pos, "pos", _I32, p.B * 4), _p(w1, "w1", dt, C * p.d_ff * es),
+                          _p(w2, "w2", dt, C * p.d_ff * es), _p(w3, "w3", dt, p.d_ff * p.d_c * es),
+                          _p(ref_idx, "ref_idx", _I32, rows * p.k * 4), _p(codes, "codes", _U8, cb),
+                          _p(scale, "scale", _HALF, sb), _p(zmin, "zmin", _HALF, sb),
+                          _p(z, "z", _F32, rows * p.d_c * 4),
+                          _p(workspace, "workspace", None, workspace_bytes),
                           int(workspace_bytes), _s(stream))
     return _check("rkv_append", st) if check else st
 
@@ -255,5 +343,8 @@ def rkv_reference_positions(p: rkv_params):
 
 
 def rkv_store_refs(p: rkv_params, kv, ref_store, stream=None, *, check: bool = True) -> int:
-    st = lib().rkv_store_refs(ctypes.byref(p), _p(kv), _p(ref_store), _s(stream))
+    dt, es = _elem(p)
+    C = 2 * p.N * p.D
+    st = lib().rkv_store_refs(ctypes.byref(p), _p(kv, "kv", dt, p.B * p.T * C * es),
+                              _p(ref_store, "ref_store", _U8, p.B * _n_ref(p) * C), _s(stream))
     return _check("rkv_store_refs", st) if check else st

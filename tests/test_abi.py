@@ -248,3 +248,66 @@ def test_fp8_reference_format_validation():
                             check=False) == R.RKV_ERR_INVALID_ARG
     assert R.rkv_store_refs(_p(LLAMA32K, ref_format="fp8"), FAKE_MIS, FAKE, None,
                             check=False) == R.RKV_ERR_INVALID_ARG
+
+
+class _FakeGpuTensor:
+    """Stands in for a GPU tensor on this CPU-only host: the binding reads only
+    is_cuda, is_contiguous(), dtype, numel(), element_size() before a call, and
+    every case below fails those checks, so data_ptr() is never reached."""
+
+    def __init__(self, dtype="torch.bfloat16", numel=1 << 40, esize=2, contiguous=True):
+        self.is_cuda, self.dtype, self._n, self._e, self._c = True, dtype, numel, esize, contiguous
+        self.device = "cuda:0"
+
+    def is_contiguous(self):
+        return self._c
+
+    def numel(self):
+        return self._n
+
+    def element_size(self):
+        return self._e
+
+    def data_ptr(self):
+        raise AssertionError("validation should have failed before data_ptr()")
+
+
+def test_binding_rejects_host_strided_mistyped_and_short_tensors():
+    """The binding checks every tensor before the library is called: a CPU
+    tensor, a non-contiguous view, the wrong dtype for kv / weights, or a
+    buffer shorter than the call's layout raise ValueError, so no such
+    pointer can reach a kernel."""
+    import torch
+    p = _p(LLAMA32K)
+    good = _FakeGpuTensor()
+    cases = {
+        "host": torch.zeros(4, dtype=torch.bfloat16),
+        "strided": _FakeGpuTensor(contiguous=False),
+        "dtype": _FakeGpuTensor(dtype="torch.float32", esize=4),
+        "short": _FakeGpuTensor(numel=100),
+    }
+    for what, bad in cases.items():
+        with pytest.raises(ValueError):
+            R.rkv_encode(p, bad, good, good, good, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None)
+        with pytest.raises(ValueError):
+            R.rkv_encode(p, FAKE, FAKE, FAKE, bad, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None)
+        with pytest.raises(ValueError):
+            R.rkv_select(p, bad, FAKE, FAKE, 1 << 40, None)
+        with pytest.raises(ValueError):
+            R.rkv_restore(p, FAKE, FAKE, FAKE, FAKE, bad, FAKE, FAKE, 10, 1.0, FAKE, "f32", FAKE,
+                          1 << 40, None)
+        with pytest.raises(ValueError):
+            R.rkv_append(p, FAKE, bad, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                         1 << 40, None)
+        with pytest.raises(ValueError):
+            R.rkv_store_refs(_p(LLAMA32K, ref_format="fp8"), bad, FAKE, None)
+    # index and output buffers: dtype and size follow n_idx and out_dtype
+    with pytest.raises(ValueError):
+        R.rkv_dequant_gather(p, FAKE, FAKE, FAKE, _FakeGpuTensor("torch.int64", esize=8), 5, FAKE,
+                             "f32", None)
+    with pytest.raises(ValueError):
+        R.rkv_dequant_gather(p, FAKE, FAKE, FAKE, FAKE, 1000, _FakeGpuTensor("torch.float32", 1000, 4),
+                             "f32", None)
+    with pytest.raises(ValueError):
+        R.rkv_dequant_gather(p, FAKE, FAKE, FAKE, FAKE, 5, _FakeGpuTensor("torch.float32", esize=4),
+                             "bf16", None)

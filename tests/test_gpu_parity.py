@@ -92,6 +92,26 @@ def test_full_size_configs_sampled(cfg, n_random):
            for b in range(cfg.B)}
     gathered = {b: _gather_rows(p, out, b * cfg.T + pos[b]) for b in range(cfg.B)}
     P.compare_tokens(w, host, pos, gathered, log=_log)
+    if cfg.gather_frac is not None:
+        _check_configured_gather(w, p, out, host)
+
+
+def _check_configured_gather(w, p, out, host):
+    """The workload's own gather (a random 30 % or 10 % of the flat token
+    indices, sorted): every row bit-exact in f32 and bf16 against the
+    oracle's dequantisation of the GPU's records ([RKV] §2.4 third eq.)."""
+    cfg = w.cfg
+    idx = np.asarray(w.gather_idx, dtype=np.int32)
+    d_idx = torch.from_numpy(idx).cuda()
+    got32 = RB.dequant_gather(p, out, d_idx, "f32")
+    got16 = RB.dequant_gather(p, out, d_idx, "bf16")
+    torch.cuda.synchronize()
+    flat = lambda a: a.reshape(cfg.B * cfg.T, -1)
+    want = O.gather(flat(host["codes"]), flat(host["scale"]), flat(host["zmin"]), idx,
+                    g=cfg.g, b=cfg.b, d_c=cfg.d_c)
+    _log(f"[gather] {cfg.name}: {len(idx)} rows")
+    assert np.array_equal(got32.cpu().numpy(), want)
+    assert np.array_equal(P.bf16_bits_of(got16), P.expected_bf16(want))
 
 
 # Dynamic reference schedule ([RKV] §2.6): sinks, a growing stride, a pool
