@@ -231,6 +231,26 @@ rkv_status rkv_append(const rkv_params* p, void* kv, const void* kv_new,
                       void* workspace, size_t workspace_bytes,
                       hipStream_t stream);
 
+/* rkv_append without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, semantics, outputs
+ * and kernels as rkv_append; the workspace is a fixed 4 MiB array of device
+ * memory inside the library (one copy per GPU, loaded with the library and
+ * held until the process ends; its address is looked up on the first call
+ * on each device).  Nothing is allocated or freed and no allocating routine
+ * is called.  Returns RKV_ERR_WORKSPACE, with nothing enqueued, when the
+ * call needs more than 4 MiB (rkv_append_workspace_bytes(p) > 4 MiB, e.g.
+ * more than about 190 sequences at C = 2048, d_ff = 1024): use rkv_append
+ * there.  Every call on a GPU shares that GPU's array, so calls that
+ * overlap on one GPU (on different streams, or from different threads) race
+ * and give undefined results; serialise them on one stream.  The array keeps
+ * the last call's contents; nothing in it needs to start at zero. */
+rkv_status rkv_append_noalloc(const rkv_params* p, void* kv, const void* kv_new,
+                              const int32_t* pos, const void* w1, const void* w2,
+                              const void* w3, int32_t* ref_idx, uint8_t* codes,
+                              uint16_t* scale, uint16_t* zmin, float* z,
+                              hipStream_t stream);
+
 /* The FP8 reference store of a prefix (p->ref_format == RKV_REF_FP8,
  * [RKV] §2.4 last paragraph): ref_store[b][j][c] = E4M3 byte of
  * kv[b][p_j][c] for the j-th reference position p_j of the schedule, the

@@ -43,6 +43,7 @@ EXPORTS = (
     "rkv_restore",
     "rkv_append_workspace_bytes",
     "rkv_append",
+    "rkv_append_noalloc",
     "rkv_reference_positions",
     "rkv_store_refs",
 )
@@ -110,6 +111,8 @@ def lib() -> ctypes.CDLL:
         L.rkv_append_workspace_bytes.restype = sz
         L.rkv_append.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.rkv_append.restype = ctypes.c_int
+        L.rkv_append_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.rkv_append_noalloc.restype = ctypes.c_int
         L.rkv_reference_positions.argtypes = [P, vp, i32]
         L.rkv_reference_positions.restype = i32
         L.rkv_store_refs.argtypes = [P, vp, vp, vp]
@@ -330,6 +333,22 @@ def rkv_append(p: rkv_params, kv, kv_new, pos, w1, w2, w3, ref_idx, codes, scale
                           _p(workspace, "workspace", None, workspace_bytes),
                           int(workspace_bytes), _s(stream))
     return _check("rkv_append", st) if check else st
+
+
+def rkv_append_noalloc(p: rkv_params, kv, kv_new, pos, w1, w2, w3, ref_idx, codes, scale, zmin,
+                       z, stream=None, *, check: bool = True) -> int:
+    """rkv_append on the library's fixed device scratch (no workspace)."""
+    dt, es = _elem(p)
+    C, rows = 2 * p.N * p.D, p.B * p.T
+    cb, sb = _record_sizes(p, rows)
+    st = lib().rkv_append_noalloc(
+        ctypes.byref(p), _ref_store(p, kv), _p(kv_new, "kv_new", dt, p.B * C * es),
+        _p(pos, "pos", _I32, p.B * 4), _p(w1, "w1", dt, C * p.d_ff * es),
+        _p(w2, "w2", dt, C * p.d_ff * es), _p(w3, "w3", dt, p.d_ff * p.d_c * es),
+        _p(ref_idx, "ref_idx", _I32, rows * p.k * 4), _p(codes, "codes", _U8, cb),
+        _p(scale, "scale", _HALF, sb), _p(zmin, "zmin", _HALF, sb),
+        _p(z, "z", _F32, rows * p.d_c * 4), _s(stream))
+    return _check("rkv_append_noalloc", st) if check else st
 
 
 def rkv_reference_positions(p: rkv_params):

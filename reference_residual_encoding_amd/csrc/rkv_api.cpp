@@ -377,6 +377,41 @@ rkv_status rkv_append(const rkv_params* p, void* kv, const void* kv_new, const i
   return ok();
 }
 
+rkv_status rkv_append_noalloc(const rkv_params* p, void* kv, const void* kv_new,
+                              const int32_t* pos, const void* w1, const void* w2, const void* w3,
+                              int32_t* ref_idx, uint8_t* codes, uint16_t* scale, uint16_t* zmin,
+                              float* z, hipStream_t stream) {
+  rkv_status st = check_params(p);
+  if (st != RKV_OK) return st;
+  RKV_NEED_PTR(kv);
+  RKV_NEED_PTR(kv_new);
+  RKV_NEED_PTR(pos);
+  RKV_NEED_PTR(w1);
+  RKV_NEED_PTR(w2);
+  RKV_NEED_PTR(w3);
+  RKV_NEED_PTR(ref_idx);
+  RKV_NEED_PTR(codes);
+  RKV_NEED_GROUP_PTR(scale);
+  RKV_NEED_GROUP_PTR(zmin);
+  if (z != nullptr && !aligned16(z)) return fail(RKV_ERR_INVALID_ARG, "z is not 16-byte aligned");
+  const rkv::Shape sh = shape_of(p);
+  const rkv::AppendWorkspace L = rkv::plan_append(sh);
+  if (L.total > rkv::kAppendScratchBytes)
+    return fail(RKV_ERR_WORKSPACE,
+                "rkv_append_noalloc needs %zu bytes of scratch, more than its fixed %zu; "
+                "use rkv_append with a workspace",
+                L.total, rkv::kAppendScratchBytes);
+  char* ws = nullptr;
+  hipError_t e = rkv::append_scratch(&ws);
+  if (e != hipSuccess)
+    return fail(RKV_ERR_DEVICE, "scratch address: %s", hipGetErrorString(e));
+  RKV_STAGE(RKV_STAGE_APPEND,
+            rkv::launch_append(sh, kv, kv_new, pos, w1, w2, w3, ref_idx, codes, scale, zmin, z,
+                               ws, L, stream),
+            "append");
+  return ok();
+}
+
 rkv_status rkv_store_refs(const rkv_params* p, const void* kv, uint8_t* ref_store,
                           hipStream_t stream) {
   rkv_status st = check_params(p);

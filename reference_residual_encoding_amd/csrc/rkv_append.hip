@@ -23,6 +23,7 @@
 #include "rkv_quant.h"
 
 #include <cfloat>
+#include <mutex>
 
 namespace rkv {
 
@@ -440,6 +441,36 @@ __global__ __launch_bounds__(256) void k_app_w3(const float* __restrict__ dh,
 }
 
 }  // namespace
+
+// Fixed device scratch of the allocation-free append (rkv_append_noalloc):
+// the same regions plan_append lays out, in a module array instead of a
+// caller's workspace.  Each GPU that loads the library holds its own copy
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not device memory: only the address hipGetSymbolAddress returns for the
+// current device may reach a kernel.
+static __device__ __align__(256) char scratch[kAppendScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t append_scratch(char** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {               // once per device, with it current
+    void* addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<char*>(addr);
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 AppendWorkspace plan_append(const Shape& sh) {
   AppendWorkspace L{};

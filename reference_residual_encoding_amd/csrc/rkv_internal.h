@@ -104,6 +104,11 @@ struct AppendWorkspace {
   size_t rpos, part, mean, dh, act, total;
 };
 AppendWorkspace plan_append(const Shape& sh);
+// Size of the fixed device scratch the allocation-free append works in.
+constexpr size_t kAppendScratchBytes = size_t(4) << 20;
+// Device address of that scratch on the current device (looked up once per
+// device, then cached); no allocation.
+hipError_t append_scratch(char** ptr);
 hipError_t launch_append(const Shape& sh, void* kv, const void* kv_new, const int32_t* pos,
                          const void* w1, const void* w2, const void* w3, int32_t* ref_idx,
                          uint8_t* codes, uint16_t* scale, uint16_t* zmin, float* z, char* ws,

@@ -311,3 +311,18 @@ def test_binding_rejects_host_strided_mistyped_and_short_tensors():
     with pytest.raises(ValueError):
         R.rkv_dequant_gather(p, FAKE, FAKE, FAKE, FAKE, 5, _FakeGpuTensor("torch.float32", esize=4),
                              "bf16", None)
+
+
+def test_noalloc_append_rejects_calls_beyond_its_fixed_scratch():
+    """rkv_append_noalloc works in a fixed 4 MiB device array: a call that
+    needs more is refused on the host (RKV_ERR_WORKSPACE) before any device
+    call, with a message naming the alternative."""
+    from synth.configs import LLAMA8K
+    p = _p(LLAMA8K, B=400)
+    assert R.rkv_append_workspace_bytes(p) > 4 << 20      # so validation cannot pass
+    st = R.rkv_append_noalloc(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                              None, check=False)
+    assert st == R.RKV_ERR_WORKSPACE
+    assert "rkv_append with a workspace" in R.rkv_last_error()
+    assert R.rkv_append_noalloc(p, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                None, None, check=False) == R.RKV_ERR_INVALID_ARG
