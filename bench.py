@@ -103,15 +103,23 @@ def stage_work(cfg, n_gather: int, refs):
     }
 
 
-def cpu_baseline(w, n_tokens: int, seed: int = 0):
-    """The CPU oracle, as it stands, on a bounded sample of the workload."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
+def _oracle_encode_time(w, n_tokens: int, seed: int = 0):
+    """Wall time of the oracle encoding n_tokens random non-reference tokens
+    of sequence 0 (each on its own: retrieval over its causal pool, mean, two
+    f_c, quantiser); n_tokens <= 0 takes every non-reference token."""
     import numpy as np
     from oracle import rkv_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = 1
     cfg = w.cfg
     rng = np.random.default_rng(seed)
     kv = w.kv_f32()[0].astype(np.float64)
@@ -119,15 +127,54 @@ def cpu_baseline(w, n_tokens: int, seed: int = 0):
     mask = np.zeros(cfg.T, dtype=bool)
     mask[O.reference_schedule(cfg.T, cfg.stride, cfg.alpha, cfg.n_sink)] = True
     nonref = np.flatnonzero(~mask)
-    pos = np.sort(rng.choice(nonref, size=n_tokens, replace=False))
+    pos = nonref if n_tokens <= 0 else np.sort(rng.choice(nonref, size=n_tokens, replace=False))
     t0 = time.perf_counter()
-    O.encode_tokens(kv, W1, W2, W3, pos, k=cfg.k, g=cfg.g, b=cfg.b, s=cfg.stride,
-                    alpha=cfg.alpha, n_sink=cfg.n_sink)
-    dt = time.perf_counter() - t0
-    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n_tokens} random non-reference tokens of sequence 0 of {cfg.name}, "
-                      f"each encoded on its own (retrieval over its causal pool, mean, two f_c, "
-                      f"quantiser), numpy fp64; {dt:.2f} s"}
+    enc = O.encode_tokens(kv, W1, W2, W3, pos, k=cfg.k, g=cfg.g, b=cfg.b, s=cfg.stride,
+                          alpha=cfg.alpha, n_sink=cfg.n_sink)
+    return len(pos), time.perf_counter() - t0, enc
+
+
+def cpu_baseline(w, n_tokens: int, seed: int = 0):
+    """The CPU oracle, as it stands, on a bounded sample of the workload,
+    with all of the host's BLAS threads; then the same oracle on one thread
+    (the tiny workload in full, and a sample of the 8k Llama shape), and the
+    oracle's dequantise-gather of the workload's selected rows."""
+    import numpy as np
+    from oracle import rkv_oracle as O
+    from synth import generate
+    from synth.configs import LLAMA8K, TINY
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threadpool_limits, threads = None, 1
+    cfg = w.cfg
+    n, dt, enc = _oracle_encode_time(w, n_tokens, seed)
+    out = {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"{n} random non-reference tokens of sequence 0 of {cfg.name}, "
+                     f"each encoded on its own (retrieval over its causal pool, mean, two f_c, "
+                     f"quantiser), numpy fp64; {dt:.2f} s",
+           "cpu_model": cpu_model(), "host_threads_visible": len(os.sched_getaffinity(0))}
+    # the oracle's gather of the workload's rows (records of random latents
+    # of the workload's shape: the gather's cost does not depend on values)
+    rows = cfg.B * cfg.T
+    rng = np.random.default_rng(seed + 1)
+    q, dh, mh = O.quantize(rng.standard_normal((rows, cfg.d_c)), cfg.g, cfg.b)
+    codes = O.pack_codes(q, cfg.b)
+    t0 = time.perf_counter()
+    O.gather(codes, dh, mh, w.gather_idx, g=cfg.g, b=cfg.b, d_c=cfg.d_c)
+    gdt = time.perf_counter() - t0
+    out["gather"] = {"rows": int(len(w.gather_idx)), "seconds": round(gdt, 4),
+                     "rows_per_s": round(len(w.gather_idx) / gdt, 1)}
+    if threadpool_limits is not None:
+        one = {}
+        with threadpool_limits(limits=1):
+            for c, k in ((TINY, 0), (LLAMA8K, 256)):
+                n1, dt1, _ = _oracle_encode_time(generate(c), k, seed)
+                one[c.name] = {"tokens": n1, "seconds": round(dt1, 3),
+                               "tokens_per_s": round(n1 / dt1, 1)}
+        out["one_thread"] = one
+    return out
 
 
 def bench_restore(R, cfg, w, p, kv, out, idx, stream, args):
@@ -279,6 +326,46 @@ def bench_variants(R, RB, cfg, kv, w1, w2, w3, idx, stream, args):
 
 
 STAGE_PASS_STEPS = 20   # untimed steps with every stage bracketed (the stage breakdown)
+FLUSH_MB = 512          # written before every cold gather call: twice the 256 MB MALL
+
+
+def bench_gather_cold(R, RB, cfg, p, out, idx, stream, reps: int = 20):
+    """rkv_dequant_gather of the workload's rows with cold caches: before
+    every timed call a 512 MB buffer is written (evicting the 256 MB MALL and
+    every L2), then the call alone is bracketed by events; median of `reps`.
+    GB/s counts the algorithmic bytes (each row's record read, its bf16 row
+    written).  The launch floor is the same measurement for a single row."""
+    import numpy as np
+    import torch
+    dev = idx.device
+    flush = torch.empty(FLUSH_MB << 20, dtype=torch.uint8, device=dev)
+    rec = cfg.d_c * cfg.b // 8 + (0 if cfg.b == 16 else 4 * (cfg.d_c // cfg.g))
+
+    def timed(ix):
+        dst = torch.empty((ix.numel(), cfg.d_c), dtype=torch.bfloat16, device=dev)
+        ms = []
+        for i in range(reps + 2):
+            flush.fill_(i & 0xFF)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            RB.dequant_gather(p, out, ix, "bf16", stream, dst=dst)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if i >= 2:
+                ms.append(e0.elapsed_time(e1))
+        return float(np.median(ms))
+
+    ms = timed(idx)
+    floor = timed(idx[:1])
+    nbytes = idx.numel() * (rec + 2 * cfg.d_c)
+    del flush
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"rows": int(idx.numel()), "bytes_algorithmic": int(nbytes), "us": round(ms * 1e3, 2),
+            "gb_s": round(gbs, 1), "frac_of_hbm": round(gbs / PEAK_HBM_GBS, 4),
+            "launch_floor_us": round(floor * 1e3, 2),
+            "gb_s_above_floor": round(nbytes / (max(ms - floor, 1e-6) * 1e-3) / 1e9, 1),
+            "flush_mb": FLUSH_MB, "reps": reps}
 
 
 def main():
@@ -299,6 +386,12 @@ def main():
     ap.add_argument("--copy-check-mb", type=int, default=0,
                     help="before the timed region, run one plain device copy of this many MiB "
                          "(a reference of known size for hardware byte counters)")
+    ap.add_argument("--mfma-check", type=int, default=0,
+                    help="before the timed region, run one torch bf16 matmul of this size "
+                         "(n x n times n x n, 2 n^3 flops): a reference of known work for the "
+                         "matrix-core op counters")
+    ap.add_argument("--no-gather-cold", action="store_true",
+                    help="skip the cold-cache gather measurement")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -344,6 +437,13 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.mfma_check:
+        n = args.mfma_check
+        a = torch.ones((n, n), dtype=torch.bfloat16, device=dev)
+        torch.cuda.synchronize()
+        c = a @ a
+        torch.cuda.synchronize()
+        del a, c
     for _ in range(max(args.warmup, 1)):
         step()
     torch.cuda.synchronize()
@@ -363,17 +463,24 @@ def main():
     print(f"[bench] stage ms: { {k: round(v, 4) for k, v in stages_ms.items()} }",
           file=sys.stderr, flush=True)
 
-    # timed region: only the dominant stage keeps its event pair
+    def timed_steps():
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    # timed region: K whole steps, no event inside a step
+    R.rkv_profile_begin(0)
+    ms_per_step = timed_steps()
+    # the same K steps again, now with the dominant stage bracketed by an
+    # event pair on the stream its kernel runs on: its launch duration
     R.rkv_profile_begin(1 << dom_i)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = e0.elapsed_time(e1) / args.steps
+    ms_per_step_bracketed = timed_steps()
     dom_total, dom_n = R.rkv_profile_read(dom_i)
     R.rkv_profile_begin(0)
     dom_ms = dom_total / dom_n
@@ -414,11 +521,17 @@ def main():
                    "b": cfg.b, "ref_stride": cfg.stride, "ref_alpha": cfg.alpha, "n_sink": cfg.n_sink,
                    "gather_rows": int(idx.numel())},
         "pct_bf16_mfma_peak": round(100.0 * mfma_flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
-        "encode_mfma_tflops_algorithmic": round(mfma_flops / 1e12, 4),
+        "encode_mfma_tflop_per_step": round(mfma_flops / 1e12, 4),
+        "encode_mfma_tflops_achieved": round(mfma_flops / (ms_per_step * 1e-3) / 1e12, 1),
+        "non_reference_tokens_per_s": round(cfg.B * schedule_counts(R.rkv_reference_positions(p), cfg.T)[1]
+                                            / (ms_per_step * 1e-3), 1),
+        "ms_per_step_with_kernel_events": round(ms_per_step_bracketed, 4),
         "stages_ms": {k: round(v, 4) for k, v in stages_ms.items()},
         "encode_ms_stage_sum": round(encode_ms, 4),
         "roofline": roof,
     }
+    if not args.no_gather_cold:
+        line["gather"] = bench_gather_cold(R, RB, cfg, p, out, idx, stream)
     if not args.no_restore:
         line["restore"] = bench_restore(R, cfg, w, p, kv, out, idx, stream, args)
     if not args.no_append:

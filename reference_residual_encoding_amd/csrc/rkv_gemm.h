@@ -177,6 +177,8 @@ struct DmaTile {
   static_assert(kSteps % 2 == 0, "fragment double-buffering pairs k-steps");
   static_assert(NS >= 2, "a stage is requested at least one stage ahead");
   static_assert(kLdA >= 1 && kLdB >= 1, "each wave feeds part of A and of B");
+  static_assert(BM * SB == kLdA * 1024 * kWaves && BN * SB == kLdB * 1024 * kWaves,
+                "the DMA instructions of a stage cover every row of A and of B");
   static_assert(kLd * (NS - 2 > 0 ? NS - 2 : 0) <= 31, "vmcnt window");
 };
 

@@ -57,21 +57,25 @@ template <> struct SwCfg<float> {
   static constexpr int BM = 256, BN = 128, SB = 128, NS = 2, WGM = 2, WGN = 2;
   static constexpr int kThreads = 64 * WGM * WGN;
 };
-template <typename E> struct W3Cfg : SwCfg<E> {};
+// the W3 product streams delta_h from beyond L2: a deeper ring of shorter
+// stages (4 x 64 bytes; measured about 2-4% faster than 2 x 128 bytes)
+template <typename E> struct W3Cfg {
+  static constexpr int BM = 256, BN = 256, SB = 64, NS = 4, WGM = 2, WGN = 4;
+  static constexpr int kThreads = 64 * WGM * WGN;
+};
 template <> struct W3Cfg<float> {
   static constexpr int BM = 256, BN = 256, SB = 128, NS = 2, WGM = 2, WGN = 2;
   static constexpr int kThreads = 64 * WGM * WGN;
 };
                                                                  // difference, 2 WGs per CU
-// distance contraction: BM references (a chunk) x BN tokens per workgroup;
-// SUBS = threads per token in the top-k scan, each keeping its own list
+// distance contraction: BM references (a chunk) x BN tokens per workgroup
 template <typename E> struct DistCfg {
   static constexpr int BM = 192, BN = 256, SB = 128, NS = 2, WGM = 2, WGN = 4;
-  static constexpr int kThreads = 64 * WGM * WGN, SUBS = kThreads / BN;
+  static constexpr int kThreads = 64 * WGM * WGN;
 };
 template <> struct DistCfg<float> {
   static constexpr int BM = 128, BN = 256, SB = 128, NS = 2, WGM = 2, WGN = 2;
-  static constexpr int kThreads = 64 * WGM * WGN, SUBS = kThreads / BN;
+  static constexpr int kThreads = 64 * WGM * WGN;
 };
 constexpr int kSB = 128;
 constexpr int kEpiLd(int bn) { return bn + 8; }  // padded fp32 row of an LDS-staged tile
@@ -366,10 +370,12 @@ __global__ __launch_bounds__(256) void k_ref_store(const E* __restrict__ kv, int
 
 // ------------------------------------------------------------------ retrieval
 // One workgroup: BM references (chunk c) x BN non-reference tokens (tile tt)
-// of sequence b.  Each of the SUBS threads of a token scans its own span of
-// each half chunk in increasing j; their lists are then combined into the KL
-// best (d', j) of the chunk restricted to the causal pool (j*s < position),
-// written as partial list c.
+// of sequence b.  Every lane scans the dot products its own accumulators
+// hold (its kTN tokens against its kTM*16 references, in increasing j),
+// keeping a top-KL list per token; the 2*WGM lists of a token (two lane
+// halves of each of the WGM waves that share its columns) are then
+// combined in LDS into the KL best (d', j) of the chunk restricted to the
+// causal pool, written as partial list c.
 // BUF: the buffer form of the operand DMA (the host checks that a token
 // tile's rows lie within 2^31 bytes).
 template <typename E, int KL, bool BUF>
@@ -379,12 +385,11 @@ __global__ __launch_bounds__(DistCfg<E>::kThreads) void k_dist_topk(
     int nr, int n_lists,
     int n_tt) {
   using CF = DistCfg<E>;
-  constexpr int BM = CF::BM, BN = CF::BN, WGM = CF::WGM, WGN = CF::WGN, SUBS = CF::SUBS;
-  constexpr int LD = kEpiLd(BN);
-  constexpr int HALF = BM / 2, SPAN = HALF / SUBS;
-  static_assert(WGM == 2 && SPAN % 4 == 0, "two wave-rows; whole groups of 4 per span");
+  constexpr int BM = CF::BM, BN = CF::BN, WGM = CF::WGM, WGN = CF::WGN;
+  constexpr int kLists = 2 * WGM;                        // partial lists per token
   constexpr int kMain = mainloop_lds<E, BM, BN, CF::SB, CF::NS, WGM, WGN>();
-  constexpr int kStaged = kMain > HALF * LD * 4 ? kMain : HALF * LD * 4;
+  constexpr int kComb = BN * kLists * KL * 8;            // the lists, as (d', j) pairs
+  constexpr int kStaged = kMain > kComb ? kMain : kComb;
   __shared__ __attribute__((aligned(1024))) char lds[kStaged + BM * 4];
   float* ysq_l = reinterpret_cast<float*>(lds + kStaged);
   // Work items are the causal (token tile, reference chunk) pairs.  The
@@ -398,7 +403,7 @@ __global__ __launch_bounds__(DistCfg<E>::kThreads) void k_dist_topk(
   const int x = blockIdx.x & 7;
   const int l = blockIdx.x >> 3;
   const int lane = threadIdx.x & 63;
-  int g = -1, c = -1, npool_max = 0;
+  int g = -1, c = -1;
   for (int g0 = x, before = 0; g0 < B * n_tt; g0 += 8 * 64) {
     const int gl = g0 + 8 * lane;
     int np = 0, nch = 0;
@@ -420,7 +425,6 @@ __global__ __launch_bounds__(DistCfg<E>::kThreads) void k_dist_topk(
       const int src = __ffsll(hit) - 1;
       g = __shfl(gl, src);
       c = want - (__shfl(incl, src) - __shfl(nch, src));
-      npool_max = __shfl(np, src);
       break;
     }
     before += __shfl(incl, 63);
@@ -440,75 +444,98 @@ __global__ __launch_bounds__(DistCfg<E>::kThreads) void k_dist_topk(
   f32x16 acc[BM / WGM / 32][BN / WGN / 32];
   tile_product<E, BM, BN, CF::SB, CF::NS, WGM, WGN, BUF>(rowA, rowB, int(rowb), lds, acc);
 
-  // Stage the dot products half a chunk at a time (the waves of one
-  // wave-row); thread (t, sub) scans references sub*SPAN .. +SPAN of each
-  // half for token t in increasing order, keeping the KL best (d', j).
-  float* dot = reinterpret_cast<float*>(lds);
-  const int t = tid % BN, sb = tid / BN, q = n0 + t;     // sb is uniform per wave
-  // the pool of the token at q is the t - q references before its position
-  // t; the scan runs to the tile's largest pool (uniform) and masks the rest
-  const int lim = q < nr ? nrp[q] - q - m0 : 0;
-  const int lim_all = min(npool_max - m0, BM);
-  float bd[KL];
-  int bi[KL];
+  // Lane l of wave (wm, wn) holds in register r of fragment (i, j) the dot
+  // product of token column wn*kWN + 32j + l%32 with chunk reference
+  // wm*kWM + 32i + mfma32_row(r, l): for each of its tokens it sees kTM*16
+  // references, in increasing j as i, then r, increase.  d' = ||y||^2 -
+  // 2 x.y ranks them as the distance does ([RKV] §2.2).  Candidates outside
+  // the token's causal pool (j at or past the references before its
+  // position) are masked, unless the whole item lies inside every pool.
+  constexpr int kWM = BM / WGM, kWN = BN / WGN, kTM = kWM / 32, kTN = kWN / 32;
+  const int wave = tid >> 6, hi = lane >> 5;
+  const int wm = wave / WGN, wn = wave % WGN;
+  int lim[kTN];
 #pragma unroll
-  for (int i = 0; i < KL; ++i) { bd[i] = __builtin_inff(); bi[i] = 0x7fffffff; }
-  for (int half = 0; half < 2; ++half) {
-    const int j0 = half * HALF;
-    if (j0 < lim_all) {              // uniform: the workgroup skips an empty half
-      acc_to_lds<BM, BN, WGM, WGN>(acc, dot, LD, half);
-      __syncthreads();
-      const int js = j0 + sb * SPAN;                     // first reference of this thread's span
-      const int end = min(lim_all - js, SPAN);           // uniform per wave
-      const float* col = dot + (sb * SPAN) * LD + t;
-      int jl = 0;
-      for (; jl + 4 <= end; jl += 4) {
-        float dd[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float d = ysq_l[js + jl + u] - 2.0f * col[(jl + u) * LD];
-          dd[u] = js + jl + u < lim ? d : __builtin_inff();
-        }
-        // a candidate not below the current KL-th best changes nothing (a
-        // tie arrives with the larger j), so a group that no lane of the
-        // wave can use is skipped whole
-        const float mn = fminf(fminf(dd[0], dd[1]), fminf(dd[2], dd[3]));
-        if (__any(mn < bd[KL - 1])) {
-#pragma unroll
-          for (int u = 0; u < 4; ++u) topk_push<KL>(bd, bi, dd[u], m0 + js + jl + u);
-        }
-      }
-      for (; jl < end; ++jl) {
-        const float d = ysq_l[js + jl] - 2.0f * col[jl * LD];
-        topk_push<KL>(bd, bi, js + jl < lim ? d : __builtin_inff(), m0 + js + jl);
-      }
-      __syncthreads();
-    }
+  for (int j = 0; j < kTN; ++j) {
+    const int q = n0 + wn * kWN + 32 * j + (lane & 31);
+    lim[j] = q < nr ? nrp[q] - q - m0 : 0;               // references of this chunk in its pool
   }
-  if constexpr (SUBS > 1) {
-    // combine the SUBS lists of each token: the others publish theirs in LDS
-    // (free since the barrier that ended the last scanned half), thread 0
-    // of the token merges them by (d, j)
-    float2* xl = reinterpret_cast<float2*>(lds);         // [SUBS-1][BN][KL]
-    if (sb > 0) {
+  // the tile's first token has the smallest pool: the whole item is causal
+  // when it covers all BM references of the chunk
+  const bool full = nrp[n0] - n0 - m0 >= BM;
+  float bd[kTN][KL];
+  int bi[kTN][KL];
 #pragma unroll
-      for (int i = 0; i < KL; ++i)
-        xl[((sb - 1) * BN + t) * KL + i] = make_float2(bd[i], __int_as_float(bi[i]));
-    }
-    __syncthreads();
-    if (sb > 0) return;
+  for (int j = 0; j < kTN; ++j)
 #pragma unroll
-    for (int o = 0; o < SUBS - 1; ++o)
+    for (int i = 0; i < KL; ++i) { bd[j][i] = __builtin_inff(); bi[j][i] = 0x7fffffff; }
+  auto scan = [&](auto masked_c) {
+    constexpr bool kMasked = decltype(masked_c)::value;
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        // four consecutive references: rows base .. base + 3 of the chunk
+        const int base = wm * kWM + 32 * i + 8 * r4 + 4 * hi;
+        const float4 y4 = *reinterpret_cast<const float4*>(ysq_l + base);
+        const float yv[4] = {y4.x, y4.y, y4.z, y4.w};
+        float dd[kTN][4];
+        bool use = false;
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float d = yv[u] - 2.0f * acc[i][j][4 * r4 + u];
+            dd[j][u] = (!kMasked || base + u < lim[j]) ? d : __builtin_inff();
+          }
+          // a candidate not below the current KL-th best changes nothing (a
+          // tie arrives with the larger j)
+          const float mn = fminf(fminf(dd[j][0], dd[j][1]), fminf(dd[j][2], dd[j][3]));
+          use |= mn < bd[j][KL - 1];
+        }
+        // a group no lane of the wave can use is skipped whole; otherwise the
+        // lane's tokens take their candidates in turn (independent chains)
+        if (__any(use)) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int j = 0; j < kTN; ++j) topk_push<KL>(bd[j], bi[j], dd[j][u], m0 + base + u);
+        }
+      }
+  };
+  if (full)
+    scan(std::false_type{});
+  else
+    scan(std::true_type{});
+
+  // Combine: every lane publishes its lists (slot wm*2 + hi of its
+  // tokens), then one thread per token merges the kLists lists by (d, j).
+  float2* xl = reinterpret_cast<float2*>(lds);           // [BN][kLists][KL]
+#pragma unroll
+  for (int j = 0; j < kTN; ++j) {
+    const int t = wn * kWN + 32 * j + (lane & 31);
+    float2* dst = xl + (t * kLists + wm * 2 + hi) * KL;
+#pragma unroll
+    for (int i = 0; i < KL; ++i) dst[i] = make_float2(bd[j][i], __int_as_float(bi[j][i]));
+  }
+  __syncthreads();
+  for (int t = tid; t < BN; t += CF::kThreads) {
+    const int q = n0 + t;
+    if (q >= nr) continue;
+    float md[KL];
+    int mi[KL];
+#pragma unroll
+    for (int i = 0; i < KL; ++i) { md[i] = __builtin_inff(); mi[i] = 0x7fffffff; }
+#pragma unroll
+    for (int o = 0; o < kLists; ++o)
 #pragma unroll
       for (int i = 0; i < KL; ++i) {
-        const float2 v = xl[(o * BN + t) * KL + i];
-        topk_push_lex<KL>(bd, bi, v.x, __float_as_int(v.y));
+        const float2 v = xl[(t * kLists + o) * KL + i];
+        topk_push_lex<KL>(md, mi, v.x, __float_as_int(v.y));
       }
-  }
-  if (q < nr) {
     float2* out = part + ((size_t(b) * n_lists + c) * nr + q) * KL;
 #pragma unroll
-    for (int i = 0; i < KL; ++i) out[i] = make_float2(bd[i], __int_as_float(bi[i]));
+    for (int i = 0; i < KL; ++i) out[i] = make_float2(md[i], __int_as_float(mi[i]));
   }
 }
 
