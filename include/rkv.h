@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define RKV_ABI_VERSION 4
+#define RKV_ABI_VERSION 5
 
 typedef enum {
   RKV_OK = 0,
@@ -137,6 +137,30 @@ rkv_status rkv_encode(const rkv_params* p, const void* kv, const void* w1,
                       uint8_t* codes, uint16_t* scale, uint16_t* zmin,
                       float* z, void* workspace, size_t workspace_bytes,
                       hipStream_t stream);
+
+/* Pre-packed compressor weights.  The compressor f_c's weights W1, W2, W3
+ * are fixed once the codec is trained ([RKV] §2.3; §2.5: every token is
+ * compressed once, when it is written), so a caller can lay them out once
+ * in the operand form the encode's matrix-core products read, instead of
+ * rkv_encode repacking them at every call:
+ *   rkv_packed_weights_bytes(p): bytes of that buffer for p's C, d_ff, d_c
+ *     and dtype (0 if *p is invalid);
+ *   rkv_pack_weights: writes it from w1, w2 [C][d_ff] and w3 [d_ff][d_c]
+ *     (layouts as rkv_encode; `packed` is caller-owned device memory of at
+ *     least rkv_packed_weights_bytes(p) bytes; its layout is private);
+ *   rkv_encode_packed: exactly rkv_encode (same outputs, bit for bit, and
+ *     the same workspace size) with the weights taken from `packed`.
+ * The packed buffer depends only on the weights, C, d_ff, d_c and dtype; it
+ * may be shared by any number of calls, including concurrent ones. */
+size_t rkv_packed_weights_bytes(const rkv_params* p);
+rkv_status rkv_pack_weights(const rkv_params* p, const void* w1, const void* w2,
+                            const void* w3, void* packed, size_t packed_bytes,
+                            hipStream_t stream);
+rkv_status rkv_encode_packed(const rkv_params* p, const void* kv,
+                             const void* packed, size_t packed_bytes,
+                             int32_t* ref_idx, uint8_t* codes, uint16_t* scale,
+                             uint16_t* zmin, float* z, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
 
 /* Selective dequantisation: out[i][:] = q * Delta_h + m_h (one fp32 FMA per
  * coordinate) for the record of flat token idx[i] = b*T + t
@@ -277,7 +301,8 @@ int32_t rkv_reference_positions(const rkv_params* p, int32_t* rpos,
  * duration in milliseconds and the number of launches.  Meant for
  * single-threaded measurement; events are created on first use and kept. */
 typedef enum {
-  RKV_STAGE_PACK = 0,    /* weight repacking on its own (none in rkv_encode) */
+  RKV_STAGE_PACK = 0,    /* weight repacking on its own (rkv_pack_weights;
+                            the restore's decoder weights); none in rkv_encode */
   RKV_STAGE_NORMS = 1,   /* set-up, one launch: weight repacking, schedule
                             tables, reference rows, norms, reference-token
                             records                                         */

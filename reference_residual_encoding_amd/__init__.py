@@ -31,6 +31,9 @@ RKV_BF16 = 1
 EXPORTS = (
     "rkv_encode_workspace_bytes",
     "rkv_encode",
+    "rkv_packed_weights_bytes",
+    "rkv_pack_weights",
+    "rkv_encode_packed",
     "rkv_dequant_gather",
     "rkv_quantize",
     "rkv_select",
@@ -50,7 +53,7 @@ EXPORTS = (
 
 STAGES = ("pack", "norms", "dist", "merge", "proj", "swiglu", "w3", "quant", "gather", "restore",
           "append", "store")
-RKV_ABI_VERSION = 4
+RKV_ABI_VERSION = 5
 RKV_REF_INPUT = 0
 RKV_REF_FP8 = 1
 
@@ -85,6 +88,12 @@ def lib() -> ctypes.CDLL:
         L.rkv_encode_workspace_bytes.restype = sz
         L.rkv_encode.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.rkv_encode.restype = ctypes.c_int
+        L.rkv_packed_weights_bytes.argtypes = [P]
+        L.rkv_packed_weights_bytes.restype = sz
+        L.rkv_pack_weights.argtypes = [P, vp, vp, vp, vp, sz, vp]
+        L.rkv_pack_weights.restype = ctypes.c_int
+        L.rkv_encode_packed.argtypes = [P, vp, vp, sz, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.rkv_encode_packed.restype = ctypes.c_int
         L.rkv_dequant_gather.argtypes = [P, vp, vp, vp, vp, i32, vp, ctypes.c_int, vp]
         L.rkv_dequant_gather.restype = ctypes.c_int
         L.rkv_quantize.argtypes = [P, vp, i64, vp, vp, vp, vp]
@@ -242,6 +251,37 @@ def rkv_encode(p: rkv_params, kv, w1, w2, w3, ref_idx, codes, scale, zmin, z, wo
             _p(z, "z", _F32, rows * p.d_c * 4), _p(workspace, "workspace", None, workspace_bytes))
     st = lib().rkv_encode(ctypes.byref(p), *args, int(workspace_bytes), _s(stream))
     return _check("rkv_encode", st) if check else st
+
+
+def rkv_packed_weights_bytes(p: rkv_params) -> int:
+    return int(lib().rkv_packed_weights_bytes(ctypes.byref(p)))
+
+
+def rkv_pack_weights(p: rkv_params, w1, w2, w3, packed, packed_bytes: int, stream=None, *,
+                     check: bool = True) -> int:
+    dt, es = _elem(p)
+    C = 2 * p.N * p.D
+    st = lib().rkv_pack_weights(ctypes.byref(p), _p(w1, "w1", dt, C * p.d_ff * es),
+                                _p(w2, "w2", dt, C * p.d_ff * es),
+                                _p(w3, "w3", dt, p.d_ff * p.d_c * es),
+                                _p(packed, "packed", None, packed_bytes), int(packed_bytes),
+                                _s(stream))
+    return _check("rkv_pack_weights", st) if check else st
+
+
+def rkv_encode_packed(p: rkv_params, kv, packed, packed_bytes: int, ref_idx, codes, scale, zmin,
+                      z, workspace, workspace_bytes: int, stream=None, *,
+                      check: bool = True) -> int:
+    dt, es = _elem(p)
+    C, rows = 2 * p.N * p.D, p.B * p.T
+    cb, sb = _record_sizes(p, rows)
+    args = (_p(kv, "kv", dt, rows * C * es), _p(packed, "packed", None, packed_bytes),
+            int(packed_bytes), _p(ref_idx, "ref_idx", _I32, rows * p.k * 4),
+            _p(codes, "codes", _U8, cb), _p(scale, "scale", _HALF, sb),
+            _p(zmin, "zmin", _HALF, sb), _p(z, "z", _F32, rows * p.d_c * 4),
+            _p(workspace, "workspace", None, workspace_bytes))
+    st = lib().rkv_encode_packed(ctypes.byref(p), *args, int(workspace_bytes), _s(stream))
+    return _check("rkv_encode_packed", st) if check else st
 
 
 def rkv_dequant_gather(p: rkv_params, codes, scale, zmin, idx, n_idx: int, out, out_dtype,

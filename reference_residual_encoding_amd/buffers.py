@@ -10,8 +10,8 @@ from typing import Optional
 
 import torch
 
-from . import (RKV_BF16, RKV_F32, rkv_dequant_gather, rkv_encode, rkv_encode_workspace_bytes,
-               rkv_params)
+from . import (RKV_BF16, RKV_F32, rkv_dequant_gather, rkv_encode, rkv_encode_packed,
+               rkv_encode_workspace_bytes, rkv_pack_weights, rkv_packed_weights_bytes, rkv_params)
 
 
 @dataclasses.dataclass
@@ -45,6 +45,28 @@ def encode(p: rkv_params, kv, w1, w2, w3, out: EncodeBuffers, stream=None) -> En
         stream = torch.cuda.current_stream(kv.device)
     rkv_encode(p, kv, w1, w2, w3, out.ref_idx, out.codes, out.scale, out.zmin, out.z,
                out.workspace, out.workspace.numel(), stream)
+    return out
+
+
+def pack_weights(p: rkv_params, w1, w2, w3, stream=None) -> torch.Tensor:
+    """The compressor weights in the encode's operand layout (pack once,
+    encode many times with encode_packed)."""
+    n = rkv_packed_weights_bytes(p)
+    if n == 0:
+        raise ValueError("invalid rkv_params")
+    packed = torch.empty(n, dtype=torch.uint8, device=w1.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(w1.device)
+    rkv_pack_weights(p, w1, w2, w3, packed, n, stream)
+    return packed
+
+
+def encode_packed(p: rkv_params, kv, packed: torch.Tensor, out: EncodeBuffers,
+                  stream=None) -> EncodeBuffers:
+    if stream is None:
+        stream = torch.cuda.current_stream(kv.device)
+    rkv_encode_packed(p, kv, packed, packed.numel(), out.ref_idx, out.codes, out.scale, out.zmin,
+                      out.z, out.workspace, out.workspace.numel(), stream)
     return out
 
 

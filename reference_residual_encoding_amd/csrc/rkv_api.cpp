@@ -222,9 +222,74 @@ rkv_status rkv_encode(const rkv_params* p, const void* kv, const void* w1, const
   RKV_STAGE(RKV_STAGE_DIST, rkv::launch_dist(sh, kv, ws, L, stream), "dist");
   RKV_STAGE(RKV_STAGE_MERGE, rkv::launch_merge(sh, ref_idx, ws, L, stream), "merge");
   if (sh.nr > 0) {
-    RKV_STAGE(RKV_STAGE_PROJ, rkv::launch_ref_proj(sh, kv, ws, L, stream), "proj");
-    RKV_STAGE(RKV_STAGE_SWIGLU, rkv::launch_swiglu(sh, kv, ws, L, stream), "swiglu");
-    RKV_STAGE(RKV_STAGE_W3, rkv::launch_w3_quant(sh, ws, L, codes, scale, zmin, z, stream), "w3");
+    RKV_STAGE(RKV_STAGE_PROJ, rkv::launch_ref_proj(sh, kv, ws, L, ws + L.wp, stream), "proj");
+    RKV_STAGE(RKV_STAGE_SWIGLU, rkv::launch_swiglu(sh, kv, ws, L, ws + L.wp, stream), "swiglu");
+    RKV_STAGE(RKV_STAGE_W3,
+              rkv::launch_w3_quant(sh, ws, L, ws + L.w3p, codes, scale, zmin, z, stream), "w3");
+  }
+  return ok();
+}
+
+size_t rkv_packed_weights_bytes(const rkv_params* p) {
+  if (check_params(p) != RKV_OK) return 0;
+  return rkv::plan_packed(shape_of(p)).total;
+}
+
+rkv_status rkv_pack_weights(const rkv_params* p, const void* w1, const void* w2, const void* w3,
+                            void* packed, size_t packed_bytes, hipStream_t stream) {
+  rkv_status st = check_params(p);
+  if (st != RKV_OK) return st;
+  RKV_NEED_PTR(w1);
+  RKV_NEED_PTR(w2);
+  RKV_NEED_PTR(w3);
+  RKV_NEED_PTR(packed);
+  const rkv::Shape sh = shape_of(p);
+  const rkv::PackedLayout P = rkv::plan_packed(sh);
+  if (packed_bytes < P.total)
+    return fail(RKV_ERR_WORKSPACE, "packed buffer has %zu bytes, needs %zu", packed_bytes, P.total);
+  hipError_t e;
+  RKV_STAGE(RKV_STAGE_PACK,
+            rkv::launch_pack_weights(sh, w1, w2, w3, static_cast<char*>(packed), stream), "pack");
+  return ok();
+}
+
+rkv_status rkv_encode_packed(const rkv_params* p, const void* kv, const void* packed,
+                             size_t packed_bytes, int32_t* ref_idx, uint8_t* codes,
+                             uint16_t* scale, uint16_t* zmin, float* z, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  rkv_status st = check_params(p);
+  if (st != RKV_OK) return st;
+  RKV_NEED_PTR(kv);
+  RKV_NEED_PTR(packed);
+  RKV_NEED_PTR(ref_idx);
+  RKV_NEED_PTR(codes);
+  RKV_NEED_GROUP_PTR(scale);
+  RKV_NEED_GROUP_PTR(zmin);
+  RKV_NEED_PTR(workspace);
+  if (z != nullptr && !aligned16(z)) return fail(RKV_ERR_INVALID_ARG, "z is not 16-byte aligned");
+  const rkv::Shape sh = shape_of(p);
+  const rkv::PackedLayout P = rkv::plan_packed(sh);
+  if (packed_bytes < P.total)
+    return fail(RKV_ERR_WORKSPACE, "packed buffer has %zu bytes, needs %zu", packed_bytes, P.total);
+  const rkv::Workspace L = rkv::plan_workspace(sh);
+  if (workspace_bytes < L.total)
+    return fail(RKV_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
+  char* ws = static_cast<char*>(workspace);
+  const char* wp = static_cast<const char*>(packed) + P.wp;
+  const char* w3p = static_cast<const char*>(packed) + P.w3p;
+  hipError_t e;
+  // the set-up without the weight repacking (w1 null)
+  RKV_STAGE(RKV_STAGE_NORMS,
+            rkv::launch_setup(sh, nullptr, nullptr, nullptr, kv, ws, L, ref_idx, codes, scale,
+                              zmin, z, stream),
+            "setup");
+  RKV_STAGE(RKV_STAGE_DIST, rkv::launch_dist(sh, kv, ws, L, stream), "dist");
+  RKV_STAGE(RKV_STAGE_MERGE, rkv::launch_merge(sh, ref_idx, ws, L, stream), "merge");
+  if (sh.nr > 0) {
+    RKV_STAGE(RKV_STAGE_PROJ, rkv::launch_ref_proj(sh, kv, ws, L, wp, stream), "proj");
+    RKV_STAGE(RKV_STAGE_SWIGLU, rkv::launch_swiglu(sh, kv, ws, L, wp, stream), "swiglu");
+    RKV_STAGE(RKV_STAGE_W3, rkv::launch_w3_quant(sh, ws, L, w3p, codes, scale, zmin, z, stream),
+              "w3");
   }
   return ok();
 }

@@ -71,13 +71,25 @@ hipError_t launch_dist(const Shape& sh, const void* kv, char* ws, const Workspac
                        hipStream_t st);
 hipError_t launch_merge(const Shape& sh, int32_t* ref_idx, char* ws, const Workspace& L,
                         hipStream_t st);
+// The contractions read the packed weights at wp ([2 d_ff][C], W1 and W2
+// columns interleaved in blocks of 32) and w3p ([d_c][k3]): in the
+// workspace (packed by the set-up) or in a caller's pre-packed buffer.
 hipError_t launch_ref_proj(const Shape& sh, const void* kv, char* ws, const Workspace& L,
-                           hipStream_t st);
+                           const char* wp, hipStream_t st);
 hipError_t launch_swiglu(const Shape& sh, const void* kv, char* ws,
-                         const Workspace& L, hipStream_t st);
+                         const Workspace& L, const char* wp, hipStream_t st);
 // W3 product fused with the quantiser; writes the records of non-reference tokens.
-hipError_t launch_w3_quant(const Shape& sh, char* ws, const Workspace& L, uint8_t* codes,
-                           uint16_t* scale, uint16_t* zmin, float* z, hipStream_t st);
+hipError_t launch_w3_quant(const Shape& sh, char* ws, const Workspace& L, const char* w3p,
+                           uint8_t* codes, uint16_t* scale, uint16_t* zmin, float* z,
+                           hipStream_t st);
+// A pre-packed weight buffer: the same two operands the set-up writes into
+// the workspace, at byte offsets wp and w3p.
+struct PackedLayout {
+  size_t wp, w3p, total;
+};
+PackedLayout plan_packed(const Shape& sh);
+hipError_t launch_pack_weights(const Shape& sh, const void* w1, const void* w2, const void* w3,
+                               char* packed, hipStream_t st);
 // Quantise rows of z [rows][d_c] one to one into records (stepwise export).
 hipError_t launch_quantize(const float* z, int64_t rows, int d_c, int g, int b, uint8_t* codes,
                            uint16_t* scale, uint16_t* zmin, hipStream_t st);

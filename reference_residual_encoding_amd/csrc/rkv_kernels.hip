@@ -1344,6 +1344,32 @@ hipError_t launch_setup(const Shape& sh, const void* w1, const void* w2, const v
   return hipGetLastError();
 }
 
+PackedLayout plan_packed(const Shape& sh) {
+  PackedLayout P{};
+  P.wp = 0;
+  P.w3p = align256(size_t(2) * sh.d_ff * sh.C * sh.esize);
+  P.total = P.w3p + align256(size_t(sh.d_c) * sh.k3 * sh.esize);
+  return P;
+}
+
+hipError_t launch_pack_weights(const Shape& sh, const void* w1, const void* w2, const void* w3,
+                               char* packed, hipStream_t st) {
+  const PackedLayout P = plan_packed(sh);
+  auto tiles = [](int n) { return (n + 63) / 64; };
+  PackJobs J{};
+  J.j[0] = {w1, packed + P.wp, sh.C, sh.d_ff, sh.C, 1, 0, tiles(sh.d_ff), 0};
+  J.j[1] = {w2, packed + P.wp, sh.C, sh.d_ff, sh.C, 2, 0, tiles(sh.d_ff), 0};
+  J.j[2] = {w3, packed + P.w3p, sh.d_ff, sh.d_c, sh.k3, 0, sh.bf16 ? 1 : 0, tiles(sh.d_c), 0};
+  int n_pack = 0;
+  for (auto& j : J.j) {
+    j.first = n_pack;
+    n_pack += tiles(j.rows) * j.tiles_c;
+  }
+  if (sh.bf16) k_pack_weights<uint16_t><<<n_pack, 256, 0, st>>>(J);
+  else k_pack_weights<float><<<n_pack, 256, 0, st>>>(J);
+  return hipGetLastError();
+}
+
 template <typename E>
 static int dist_items(const Shape& sh, int n_tt) {
   // per-XCD item counts (same enumeration as the kernel); grid = 8 x max
@@ -1418,20 +1444,20 @@ hipError_t launch_merge(const Shape& sh, int32_t* ref_idx, char* ws, const Works
 }
 
 hipError_t launch_ref_proj(const Shape& sh, const void* kv, char* ws, const Workspace& L,
-                           hipStream_t st) {
+                           const char* wp, hipStream_t st) {
   const int M = sh.B * sh.nref, N = 2 * sh.d_ff;
   const int tn = cdiv(N, kProjBN), tm = cdiv(M, kProjBM);
   (void)kv;
   auto* proj = reinterpret_cast<float*>(ws + L.proj);
   if (sh.bf16)
-    k_ref_proj<uint16_t><<<tn * tm, 256, 0, st>>>(ws + L.refs, ws + L.wp, proj, sh.C, M, N, tm);
+    k_ref_proj<uint16_t><<<tn * tm, 256, 0, st>>>(ws + L.refs, wp, proj, sh.C, M, N, tm);
   else
-    k_ref_proj<float><<<tn * tm, 256, 0, st>>>(ws + L.refs, ws + L.wp, proj, sh.C, M, N, tm);
+    k_ref_proj<float><<<tn * tm, 256, 0, st>>>(ws + L.refs, wp, proj, sh.C, M, N, tm);
   return hipGetLastError();
 }
 
 hipError_t launch_swiglu(const Shape& sh, const void* kv, char* ws,
-                         const Workspace& L, hipStream_t st) {
+                         const Workspace& L, const char* wp, hipStream_t st) {
   const int M = sh.B * sh.nr, N = 2 * sh.d_ff;
   if (M == 0) return hipGetLastError();
   const auto* p = static_cast<const char*>(kv);
@@ -1441,7 +1467,7 @@ hipError_t launch_swiglu(const Shape& sh, const void* kv, char* ws,
 #define RKV_SW(E, KL, BUF)                                                                      \
   k_swiglu<E, KL, BUF><<<cdiv(N, SwCfg<E>::BN) * cdiv(M, SwCfg<E>::BM), SwCfg<E>::kThreads, 0,    \
                          st>>>(                                                                 \
-      p, ws + L.wp, proj, pbytes, reinterpret_cast<const int*>(ws + L.selj), ws + L.dh, sh.T,     \
+      p, wp, proj, pbytes, reinterpret_cast<const int*>(ws + L.selj), ws + L.dh, sh.T,          \
       sh.C, reinterpret_cast<const int*>(ws + L.nrp), sh.nref, sh.nr, sh.d_ff, M)
   if (sh.bf16) {
     const bool buf = kv_tiles_fit_buffer(sh, SwCfg<uint16_t>::BM, true);
@@ -1454,12 +1480,13 @@ hipError_t launch_swiglu(const Shape& sh, const void* kv, char* ws,
   return hipGetLastError();
 }
 
-hipError_t launch_w3_quant(const Shape& sh, char* ws, const Workspace& L, uint8_t* codes,
-                           uint16_t* scale, uint16_t* zmin, float* z, hipStream_t st) {
+hipError_t launch_w3_quant(const Shape& sh, char* ws, const Workspace& L, const char* w3p,
+                           uint8_t* codes, uint16_t* scale, uint16_t* zmin, float* z,
+                           hipStream_t st) {
   const int M = sh.B * sh.nr, N = sh.d_c;
   if (M == 0) return hipGetLastError();
   const char* a = ws + L.dh;
-  const char* w = ws + L.w3p;
+  const char* w = w3p;
 #define RKV_W3(E, BITS, G8)                                                                   \
   k_w3_quant<E, BITS, G8><<<cdiv(N, W3Cfg<E>::BN) * cdiv(M, W3Cfg<E>::BM), W3Cfg<E>::kThreads, \
                             0, st>>>(a, w, sh.k3, M, N, cdiv(M, W3Cfg<E>::BM), sh.T,           \

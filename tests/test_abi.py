@@ -326,3 +326,24 @@ def test_noalloc_append_rejects_calls_beyond_its_fixed_scratch():
     assert "rkv_append with a workspace" in R.rkv_last_error()
     assert R.rkv_append_noalloc(p, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                 None, None, check=False) == R.RKV_ERR_INVALID_ARG
+
+
+def test_packed_weights_calls_check_sizes_on_the_host():
+    """rkv_pack_weights / rkv_encode_packed refuse a packed buffer (or a
+    workspace) smaller than their layout before anything is enqueued."""
+    p = _p(LLAMA32K)
+    need = R.rkv_packed_weights_bytes(p)
+    # W1|W2 interleaved (2 d_ff x C) plus W3 with each value twice (d_c x 2 d_ff), bf16
+    assert need == 2 * 1024 * 2048 * 2 + 512 * 2048 * 2
+    assert R.rkv_packed_weights_bytes(_p(LLAMA32K, b=5)) == 0
+    st = R.rkv_pack_weights(p, FAKE, FAKE, FAKE, FAKE, need - 1, None, check=False)
+    assert st == R.RKV_ERR_WORKSPACE and str(need) in R.rkv_last_error()
+    st = R.rkv_encode_packed(p, FAKE, FAKE, need - 256, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                             1 << 40, None, check=False)
+    assert st == R.RKV_ERR_WORKSPACE
+    ws = R.rkv_encode_workspace_bytes(p)
+    st = R.rkv_encode_packed(p, FAKE, FAKE, need, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws - 256,
+                             None, check=False)
+    assert st == R.RKV_ERR_WORKSPACE
+    assert R.rkv_encode_packed(p, FAKE, None, need, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws, None,
+                               check=False) == R.RKV_ERR_INVALID_ARG

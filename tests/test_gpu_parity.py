@@ -197,6 +197,28 @@ def test_fp8_store_is_bit_exact(cfg):
     assert np.array_equal(store.cpu().numpy(), P.fp8_store(cfg, w.kv))
 
 
+@pytest.mark.parametrize("cfg", [TINY, RAGGED[0], RAGGED[1], LLAMA8K.with_(T=4096),
+                                 LLAMA8K_DYN.with_(name="llama_dyn_fp8_identity", T=3000,
+                                                   ref_fp8=True, b=16)],
+                         ids=lambda c: c.name)
+def test_encode_packed_matches_encode(cfg):
+    """rkv_encode_packed with weights packed once by rkv_pack_weights gives
+    rkv_encode's outputs bit for bit, on two calls with one packed buffer."""
+    _log(f"[case] packed {cfg.name}")
+    w = generate(cfg)
+    p, _, h1, (kv, w1, w2, w3) = P.run_encode(w)
+    packed = RB.pack_weights(p, w1, w2, w3)
+    for rep in range(2):
+        out = RB.alloc_encode(p, "cuda", True)
+        RB.encode_packed(p, kv, packed, out)
+        torch.cuda.synchronize()
+        h2 = dict(ref_idx=out.ref_idx.cpu().numpy(), codes=out.codes.cpu().numpy(),
+                  scale=out.scale.cpu().numpy(), zmin=out.zmin.cpu().numpy(),
+                  z=out.z.cpu().numpy())
+        for key in ("ref_idx", "codes", "scale", "zmin", "z"):
+            assert np.array_equal(h1[key].view(np.uint8), h2[key].view(np.uint8)), (rep, key)
+
+
 def test_select_export_matches_encode():
     cfg = LLAMA8K.with_(T=2048)
     w = generate(cfg)
