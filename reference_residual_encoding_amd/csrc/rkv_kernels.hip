@@ -45,7 +45,15 @@ namespace {
 
 // Workgroup tiles (4 waves in a 2 x 2 grid, each wave a quarter of the
 // tile) and, for bf16, the DMA ring: SB bytes of K per stage, NS stages.
-constexpr int kProjBM = 128, kProjBN = 128, kProjNS = 4;  // reference projection
+// reference projection: BM references x BN columns of [W1|W2] per workgroup
+template <typename E> struct ProjCfg {
+  static constexpr int BM = 128, BN = 128, SB = 128, NS = 4, WGM = 2, WGN = 2;
+  static constexpr int kThreads = 64 * WGM * WGN;
+};
+template <> struct ProjCfg<float> {
+  static constexpr int BM = 128, BN = 128, SB = 128, NS = 4, WGM = 2, WGN = 2;
+  static constexpr int kThreads = 64 * WGM * WGN;
+};
 // token projection + SwiGLU, and the W3 product + quantiser: bf16 runs use
 // 256 x 256 tiles on 8 waves (2 x 4, one workgroup per CU, a 2-stage ring
 // of 128-byte K slices); fp32 runs keep the 4-wave register-staged loop
@@ -77,7 +85,6 @@ template <> struct DistCfg<float> {
   static constexpr int BM = 128, BN = 256, SB = 128, NS = 2, WGM = 2, WGN = 2;
   static constexpr int kThreads = 64 * WGM * WGN;
 };
-constexpr int kSB = 128;
 constexpr int kEpiLd(int bn) { return bn + 8; }  // padded fp32 row of an LDS-staged tile
 
 
@@ -616,30 +623,32 @@ __global__ __launch_bounds__(64) void k_topk_merge(const float2* __restrict__ pa
 
 // ------------------------------------------------------------------ reference projection
 template <typename E>
-__global__ __launch_bounds__(256) void k_ref_proj(const char* __restrict__ refs,
+__global__ __launch_bounds__(ProjCfg<E>::kThreads) void k_ref_proj(const char* __restrict__ refs,
                                                   const char* __restrict__ wp,
                                                   float* __restrict__ proj, int C, int M, int N,
                                                   int tiles_m) {
-  constexpr int BM = kProjBM, BN = kProjBN;
-  using TL = Tile<E, BM, BN>;
-  __shared__ __attribute__((aligned(1024))) char lds[mainloop_lds<E, BM, BN, kSB, kProjNS>()];
+  using CF = ProjCfg<E>;
+  constexpr int BM = CF::BM, BN = CF::BN, WGM = CF::WGM, WGN = CF::WGN;
+  constexpr int kWM = BM / WGM, kWN = BN / WGN, kTM = kWM / 32, kTN = kWN / 32;
+  __shared__ __attribute__((aligned(1024)))
+  char lds[mainloop_lds<E, BM, BN, CF::SB, CF::NS, WGM, WGN>()];
   const int mt = blockIdx.x % tiles_m, nt = blockIdx.x / tiles_m;
   const int m0 = mt * BM, n0 = nt * BN;
   const size_t rowb = size_t(C) * sizeof(E);
   const int tid = threadIdx.x;
   auto rowA = [&](int r) { return refs + size_t(min(m0 + r, M - 1)) * rowb; };
   auto rowB = [&](int r) { return wp + size_t(min(n0 + r, N - 1)) * rowb; };
-  f32x16 acc[TL::kTM][TL::kTN];
-  tile_product<E, BM, BN, kSB, kProjNS>(rowA, rowB, int(rowb), lds, acc);
-  const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  f32x16 acc[kTM][kTN];
+  tile_product<E, BM, BN, CF::SB, CF::NS, WGM, WGN>(rowA, rowB, int(rowb), lds, acc);
+  const int lane = tid & 63, wave = tid >> 6, wm = wave / WGN, wn = wave % WGN;
 #pragma unroll
-  for (int tm = 0; tm < TL::kTM; ++tm)
+  for (int tm = 0; tm < kTM; ++tm)
 #pragma unroll
-    for (int tn = 0; tn < TL::kTN; ++tn) {
-      const int col = n0 + wn * TL::kWN + tn * 32 + (lane & 31);
+    for (int tn = 0; tn < kTN; ++tn) {
+      const int col = n0 + wn * kWN + tn * 32 + (lane & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * TL::kWM + tm * 32 + mfma32_row(r, lane);
+        const int row = m0 + wm * kWM + tm * 32 + mfma32_row(r, lane);
         if (row < M && col < N) proj[size_t(row) * N + col] = acc[tm][tn][r];
       }
     }
@@ -1446,13 +1455,15 @@ hipError_t launch_merge(const Shape& sh, int32_t* ref_idx, char* ws, const Works
 hipError_t launch_ref_proj(const Shape& sh, const void* kv, char* ws, const Workspace& L,
                            const char* wp, hipStream_t st) {
   const int M = sh.B * sh.nref, N = 2 * sh.d_ff;
-  const int tn = cdiv(N, kProjBN), tm = cdiv(M, kProjBM);
   (void)kv;
   auto* proj = reinterpret_cast<float*>(ws + L.proj);
-  if (sh.bf16)
-    k_ref_proj<uint16_t><<<tn * tm, 256, 0, st>>>(ws + L.refs, wp, proj, sh.C, M, N, tm);
-  else
-    k_ref_proj<float><<<tn * tm, 256, 0, st>>>(ws + L.refs, wp, proj, sh.C, M, N, tm);
+  auto go = [&](auto e) {
+    using E = decltype(e);
+    using CF = ProjCfg<E>;
+    const int tn = cdiv(N, CF::BN), tm = cdiv(M, CF::BM);
+    k_ref_proj<E><<<tn * tm, CF::kThreads, 0, st>>>(ws + L.refs, wp, proj, sh.C, M, N, tm);
+  };
+  if (sh.bf16) go(uint16_t{}); else go(float{});
   return hipGetLastError();
 }
 
