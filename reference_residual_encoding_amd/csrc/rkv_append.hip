@@ -9,12 +9,13 @@
 // products are bound by reading the weights and the references once):
 //   dist     one workgroup per 8 pool references of a sequence: squared L2
 //            by direct differences, the workgroup's best KL as a list
-//   select   per sequence: merge the lists by (distance, position), write
-//            ref_idx, form the mean of the chosen references in fp32; a
-//            reference token is copied into the cache with a zero record
-//   proj     one workgroup per 16 features: x W1, x W2, m W1, m W2 for every
-//            appended token over all C rows, reduced in LDS, then
-//            delta_h = Swish(x W1) (x W2) - Swish(m W1) (m W2) ([RKV] §2.3)
+//   sel_proj one workgroup per 16 features (and 4 tokens): each merges its
+//            tokens' lists by (distance, position) itself, then x W1, x W2,
+//            m W1, m W2 over all C rows (the mean m of the chosen references
+//            formed in fp32 at the rows it needs), reduced in LDS, then
+//            delta_h = Swish(x W1) (x W2) - Swish(m W1) (m W2) ([RKV] §2.3);
+//            the first feature block writes ref_idx, and stores a reference
+//            token in the cache with a zero record
 //   w3       one workgroup per (token, 32 or 64 latent columns): z =
 //            delta_h W3 (W3 is linear, so f_c(kv) - f_c(m) = (h(kv) - h(m))
 //            W3), then the group quantiser of [RKV] §2.4 and the record
@@ -165,29 +166,40 @@ __global__ __launch_bounds__(256) void k_app_dist(const void* __restrict__ kv,
   }
 }
 
-// ---------------------------------------------------------------- select
-// Per sequence: store a reference token; else merge the distance lists,
-// write ref_idx (k_t positions ascending, -1 pads) and the fp32 mean of
-// the chosen rows.  act[b] = 1 when the token is to be encoded.
+// ---------------------------------------------------------------- select + projection
+// One launch does both: every workgroup (16 features of RB appended tokens)
+// first chooses its tokens' references itself, from the distance lists
+// (they are small and L2-resident), so no launch waits for a separate
+// selection.  Workgroups with fb == 0 also write the token's ref_idx, store
+// a reference token as it is (with a zero record) and set act[b] = 1 when
+// the token is to be encoded.
+//
+// Selection of sequence b's token by one wave: every lane merges the lists
+// l, l + 64, ... of the ceil(pool/8) lists, then the lanes' lists are merged
+// by a butterfly over the wave; by (distance, position), which orders every
+// candidate uniquely, so the kept k_t = min(k, |pool|) ([RKV] §2.1) do not
+// depend on the merge order.  Writes the chosen stored rows (ascending
+// position) to sel[0..KL) and returns k_t; -1 when the token is not encoded
+// (no append this call, or a reference).  With `writer`, also writes
+// ref_idx and act[b], and stores a reference token as it is.
 template <typename E, int KL, bool FP8>
-__global__ __launch_bounds__(256) void k_app_select(
-    void* __restrict__ kv, const E* __restrict__ kv_new, const int32_t* __restrict__ pos,
-    SchedView sv, int T, int C, int k, int rec_bytes, int n_groups, int d_c, int n_lists,
-    const float2* __restrict__ part, int32_t* __restrict__ ref_idx, uint8_t* __restrict__ codes,
-    uint16_t* __restrict__ scale, uint16_t* __restrict__ zmin, float* __restrict__ z,
-    float* __restrict__ mean, int* __restrict__ act) {
-  const int b = blockIdx.x, tid = threadIdx.x;
+__device__ int select_token(void* kv, const E* kv_new, const int32_t* pos, SchedView sv, int T,
+                            int C, int k, int rec_bytes, int n_groups, int d_c, int n_lists,
+                            const float2* part, int32_t* ref_idx, uint8_t* codes, uint16_t* scale,
+                            uint16_t* zmin, float* z, int* act, int b, bool writer, int* sel) {
+  const int lane = threadIdx.x & 63;
   const int t = pos[b];
   if (t < 0 || t >= T) {                                 // not appended this call
-    if (tid == 0) act[b] = 0;
-    return;
+    if (writer && lane == 0) act[b] = 0;
+    return -1;
   }
   const size_t row = size_t(b) * T + t;
   bool is_ref;
   const int pool = refs_before(sv, t, is_ref);
   const RefRows<E, FP8> refs{kv, sv, T, C};
   if (is_ref) {                                          // stored as it is ([RKV] §2.4)
-    for (int o = tid * 8; o < C; o += 256 * 8) {
+    if (!writer) return -1;
+    for (int o = lane * 8; o < C; o += 64 * 8) {
       if constexpr (FP8) {                               // its E4M3 bytes, row j = pool
         float v[8];
         load8(kv_new + size_t(b) * C + o, v);
@@ -207,23 +219,23 @@ __global__ __launch_bounds__(256) void k_app_select(
             reinterpret_cast<const float4*>(kv_new + size_t(b) * C + o)[1];
       }
     }
-    for (int i = tid; i < k; i += 256) ref_idx[row * k + i] = -1;
-    for (int i = tid; i < rec_bytes; i += 256) codes[row * rec_bytes + i] = 0;
-    for (int i = tid; i < n_groups; i += 256) {
+    for (int i = lane; i < k; i += 64) ref_idx[row * k + i] = -1;
+    for (int i = lane; i < rec_bytes; i += 64) codes[row * rec_bytes + i] = 0;
+    for (int i = lane; i < n_groups; i += 64) {
       scale[row * n_groups + i] = 0;
       zmin[row * n_groups + i] = 0;
     }
     if (z)
-      for (int i = tid; i < d_c; i += 256) z[row * d_c + i] = 0.0f;
-    if (tid == 0) act[b] = 0;
-    return;
+      for (int i = lane; i < d_c; i += 64) z[row * d_c + i] = 0.0f;
+    if (lane == 0) act[b] = 0;
+    return -1;
   }
   const int nch = (pool + kAppCH - 1) / kAppCH;
   float bd[KL];
   int bi[KL];
 #pragma unroll
   for (int e = 0; e < KL; ++e) { bd[e] = FLT_MAX; bi[e] = kNoRef; }
-  for (int l = tid; l < nch; l += 256) {
+  for (int l = lane; l < nch; l += 64) {
     const float4* src = reinterpret_cast<const float4*>(part + (size_t(b) * n_lists + l) * KL);
     float4 w[KL / 2];
 #pragma unroll
@@ -234,71 +246,57 @@ __global__ __launch_bounds__(256) void k_app_select(
       topk_push_lex(bd, bi, w[e].z, __float_as_int(w[e].w));
     }
   }
-  __shared__ float sd[256 * KL];
-  __shared__ int sj[256 * KL];
-  __shared__ int sel[KL];
-  for (int half = 128; half >= 1; half >>= 1) {        // tree merge, fixed order
-    if (tid >= half && tid < 2 * half)
 #pragma unroll
-      for (int e = 0; e < KL; ++e) { sd[tid * KL + e] = bd[e]; sj[tid * KL + e] = bi[e]; }
-    __syncthreads();
-    if (tid < half)
+  for (int off = 32; off >= 1; off >>= 1) {             // butterfly over the wave
+    float od[KL];
+    int oi[KL];
 #pragma unroll
-      for (int e = 0; e < KL; ++e)
-        topk_push_lex(bd, bi, sd[(tid + half) * KL + e], sj[(tid + half) * KL + e]);
-    __syncthreads();
+    for (int e = 0; e < KL; ++e) { od[e] = __shfl_xor(bd[e], off); oi[e] = __shfl_xor(bi[e], off); }
+#pragma unroll
+    for (int e = 0; e < KL; ++e) topk_push_lex(bd, bi, od[e], oi[e]);
   }
   const int kt = min(k, pool);                           // k_t = min(k, |pool|) ([RKV] §2.1)
-  if (tid == 0) {
-    int jj[KL];
+  int jj[KL];
 #pragma unroll
-    for (int e = 0; e < KL; ++e) jj[e] = e < kt ? bi[e] : kNoRef;
-    for (int a = 1; a < KL; ++a)                         // ascending position
-      for (int m = a; m > 0 && jj[m] < jj[m - 1]; --m) {
-        const int tmp = jj[m]; jj[m] = jj[m - 1]; jj[m - 1] = tmp;
-      }
+  for (int e = 0; e < KL; ++e) jj[e] = e < kt ? bi[e] : kNoRef;
+#pragma unroll
+  for (int a = 1; a < KL; ++a)                           // ascending position
+#pragma unroll
+    for (int m = a; m > 0; --m) {
+      const int lo = min(jj[m - 1], jj[m]), hi = max(jj[m - 1], jj[m]);
+      jj[m - 1] = lo;
+      jj[m] = hi;
+    }
+  if (lane == 0) {
     for (int e = 0; e < k; ++e) {
-      ref_idx[row * k + e] = e < kt ? ref_position(sv, jj[e]) : -1;
+      if (writer) ref_idx[row * k + e] = e < kt ? ref_position(sv, jj[e]) : -1;
       if (e < KL) sel[e] = e < kt ? int(refs.row(b, jj[e])) : -1;   // stored row
     }
-    act[b] = 1;
+    if (writer) act[b] = 1;
   }
-  __syncthreads();
-  const float inv = 1.0f / float(kt);
-  for (int o = tid * 8; o < C; o += 256 * 8) {
-    float v[KL][8];
-#pragma unroll
-    for (int i = 0; i < KL; ++i)                         // every row's loads in flight together
-      refs.load(size_t(sel[min(i, kt - 1)]), o, v[i]);
-    float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-    for (int i = 0; i < KL; ++i)
-      if (i < kt)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) m[e] += v[i][e];
-    float4* dst = reinterpret_cast<float4*>(mean + size_t(b) * C + o);
-    dst[0] = make_float4(m[0] * inv, m[1] * inv, m[2] * inv, m[3] * inv);
-    dst[1] = make_float4(m[4] * inv, m[5] * inv, m[6] * inv, m[7] * inv);
-  }
+  return kt;
 }
 
-// ---------------------------------------------------------------- projection
 // Workgroup: features [16w, 16w + 16) of RB appended tokens (the feature
 // block runs fastest, so the workgroups of one block of W share it in L2).
-// Four consecutive lanes cover the 16
-// features of one row of W1 and of W2 (32 contiguous bytes each at bf16),
-// so a wave's load touches 16 rows; the 64 row groups of the workgroup take
-// 8 consecutive rows each of every 512-row chunk, the loads of a chunk in
-// flight together.  For its RB tokens a thread accumulates x.W1,
-// x.W2, m.W1, m.W2 for its 4 features; the 64 partial sums of each
-// value are reduced through LDS in a fixed order, then delta_h is formed.
-template <typename E>
-__global__ __launch_bounds__(256) void k_app_proj(const E* __restrict__ kv_new,
-                                                  const float* __restrict__ mean,
-                                                  const int* __restrict__ act,
-                                                  const E* __restrict__ w1,
-                                                  const E* __restrict__ w2, int B, int C, int d_ff,
-                                                  float* __restrict__ dh) {
+// After choosing the tokens' references, four consecutive lanes cover the
+// 16 features of one row of W1 and of W2 (32 contiguous bytes each at
+// bf16), so a wave's load touches 16 rows; the 64 row groups of the
+// workgroup take 8 consecutive rows each of every 512-row chunk, the loads
+// of a chunk in flight together.  The mean of the chosen references is
+// formed at the rows a thread needs, in fp32 from the stored rows (sum in
+// order, times 1/k_t).  For its RB tokens a thread accumulates x.W1, x.W2,
+// m.W1, m.W2 for its 4 features; the 64 partial sums of each value are
+// reduced through LDS in a fixed order, then
+// delta_h = Swish(x W1) (x W2) - Swish(m W1) (m W2) ([RKV] §2.3).
+template <typename E, int KL, bool FP8>
+__global__ __launch_bounds__(256) void k_app_sel_proj(
+    void* __restrict__ kv, const E* __restrict__ kv_new, const int32_t* __restrict__ pos,
+    SchedView sv, int T, int C, int k, int rec_bytes, int n_groups, int d_c, int n_lists,
+    const float2* __restrict__ part, int32_t* __restrict__ ref_idx, uint8_t* __restrict__ codes,
+    uint16_t* __restrict__ scale, uint16_t* __restrict__ zmin, float* __restrict__ z,
+    const E* __restrict__ w1, const E* __restrict__ w2, int B, int d_ff,
+    float* __restrict__ dh, int* __restrict__ act) {
   constexpr int RB = 4, NV = RB * 16, RPT = 8, RG = 64;  // values: [token][x|m][W1|W2][feature]
   const int nfb = d_ff / 16;                             // feature blocks; tokens RB at a time
   const int fb = blockIdx.x % nfb, b0 = (blockIdx.x / nfb) * RB;
@@ -306,18 +304,41 @@ __global__ __launch_bounds__(256) void k_app_proj(const E* __restrict__ kv_new,
   const int f0 = fb * 16 + fq * 4;                       // this lane's 4 features
   __shared__ float red[NV * (256 + 1)];
   __shared__ float tot[4 * NV];
+  __shared__ int sel_l[RB][KL];
+  __shared__ int kt_l[RB];
+  static_assert(RB == 4, "one wave selects each of the workgroup's tokens");
+  {
+    const int r = tid >> 6, b = b0 + r;                  // wave r selects token r
+    int kt = -1;
+    if (b < B)
+      kt = select_token<E, KL, FP8>(kv, kv_new, pos, sv, T, C, k, rec_bytes, n_groups, d_c,
+                                    n_lists, part, ref_idx, codes, scale, zmin, z, act, b,
+                                    fb == 0, sel_l[r]);
+    if ((tid & 63) == 0) kt_l[r] = kt;
+  }
+  __syncthreads();
+  const RefRows<E, FP8> refs{kv, sv, T, C};
   {
     float acc[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v) acc[v] = 0.0f;
     bool live[RB];
+    int kt[RB];
+    float inv[RB];
+    size_t srow[RB][KL];
 #pragma unroll
-    for (int r = 0; r < RB; ++r) live[r] = b0 + r < B && act[b0 + r] == 1;
+    for (int r = 0; r < RB; ++r) {
+      kt[r] = kt_l[r];
+      live[r] = kt[r] > 0;
+      inv[r] = 1.0f / float(max(kt[r], 1));
+#pragma unroll
+      for (int i = 0; i < KL; ++i) srow[r][i] = size_t(max(sel_l[r][min(i, max(kt[r], 1) - 1)], 0));
+    }
     for (int c0 = 0; c0 < C; c0 += RG * RPT) {
       // rows c1 .. c1 + 7 of this thread: W1 and W2 for its 4 features, and
-      // every token's x and m there as two or three vector loads, all in
-      // flight together and none under a branch (C is a multiple of 8, so
-      // a thread's 8 rows are all in range or all past the end)
+      // every token's x and its references' values there, all in flight
+      // together and none under a branch (C is a multiple of 8, so a
+      // thread's 8 rows are all in range or all past the end)
       const int c1 = c0 + rg * RPT;
       const bool in = c1 < C;
       const int cb = in ? c1 : 0;
@@ -327,27 +348,29 @@ __global__ __launch_bounds__(256) void k_app_proj(const E* __restrict__ kv_new,
         load4(w1 + size_t(cb + i) * d_ff + f0, a1[i]);
         load4(w2 + size_t(cb + i) * d_ff + f0, a2[i]);
       }
-      float xv[RB][RPT], mv[RB][RPT];
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
-        const size_t rowx = size_t(min(b0 + r, B - 1)) * C + cb;  // a token past B is not summed
-        load8(kv_new + rowx, xv[r]);
-        const float4 m0 = *reinterpret_cast<const float4*>(mean + rowx);
-        const float4 m1 = *reinterpret_cast<const float4*>(mean + rowx + 4);
-        mv[r][0] = m0.x; mv[r][1] = m0.y; mv[r][2] = m0.z; mv[r][3] = m0.w;
-        mv[r][4] = m1.x; mv[r][5] = m1.y; mv[r][6] = m1.z; mv[r][7] = m1.w;
-      }
+        if (!live[r] || !in) continue;                   // uniform per workgroup
+        float xv[RPT], mv[RPT], v[KL][RPT];
+        load8(kv_new + size_t(b0 + r) * C + cb, xv);
 #pragma unroll
-      for (int r = 0; r < RB; ++r) {
-        if (!live[r] || !in) continue;
+        for (int i = 0; i < KL; ++i) refs.load(srow[r][i], cb, v[i]);
+#pragma unroll
+        for (int e = 0; e < RPT; ++e) {
+          float m = 0.0f;
+#pragma unroll
+          for (int i = 0; i < KL; ++i)
+            if (i < kt[r]) m += v[i][e];
+          mv[e] = m * inv[r];
+        }
 #pragma unroll
         for (int i = 0; i < RPT; ++i)
 #pragma unroll
           for (int f = 0; f < 4; ++f) {
-            acc[r * 16 + 0 + f] = fmaf(xv[r][i], a1[i][f], acc[r * 16 + 0 + f]);
-            acc[r * 16 + 4 + f] = fmaf(xv[r][i], a2[i][f], acc[r * 16 + 4 + f]);
-            acc[r * 16 + 8 + f] = fmaf(mv[r][i], a1[i][f], acc[r * 16 + 8 + f]);
-            acc[r * 16 + 12 + f] = fmaf(mv[r][i], a2[i][f], acc[r * 16 + 12 + f]);
+            acc[r * 16 + 0 + f] = fmaf(xv[i], a1[i][f], acc[r * 16 + 0 + f]);
+            acc[r * 16 + 4 + f] = fmaf(xv[i], a2[i][f], acc[r * 16 + 4 + f]);
+            acc[r * 16 + 8 + f] = fmaf(mv[i], a1[i][f], acc[r * 16 + 8 + f]);
+            acc[r * 16 + 12 + f] = fmaf(mv[i], a2[i][f], acc[r * 16 + 12 + f]);
           }
       }
     }
@@ -479,7 +502,6 @@ AppendWorkspace plan_append(const Shape& sh) {
   auto take = [&](size_t bytes) { size_t at = off; off += align256(bytes); return at; };
   L.rpos = take(size_t(sh.nref) * 4);
   L.part = take(size_t(sh.B) * L.n_lists * sh.kl * 8);
-  L.mean = take(size_t(sh.B) * sh.C * 4);
   L.dh = take(size_t(sh.B) * sh.d_ff * 4);
   L.act = take(size_t(sh.B) * 4);
   L.total = off;
@@ -498,7 +520,6 @@ hipError_t launch_append(const Shape& sh, void* kv, const void* kv_new, const in
     sv.rpos = rpos;
   }
   auto* part = reinterpret_cast<float2*>(ws + L.part);
-  auto* mean = reinterpret_cast<float*>(ws + L.mean);
   auto* dh = reinterpret_cast<float*>(ws + L.dh);
   auto* act = reinterpret_cast<int*>(ws + L.act);
   const int rec_bytes = sh.d_c * sh.b / 8;
@@ -509,14 +530,10 @@ hipError_t launch_append(const Shape& sh, void* kv, const void* kv_new, const in
 #define RKV_APP(E, KL, F8)                                                                        \
   k_app_dist<E, KL, F8><<<n_dist, 256, 0, st>>>(kv, static_cast<const E*>(kv_new), pos, sv, sh.T, \
                                                 sh.C, L.n_lists, part);                          \
-  k_app_select<E, KL, F8><<<sh.B, 256, 0, st>>>(kv, static_cast<const E*>(kv_new), pos, sv, sh.T, \
-                                                sh.C, sh.k, rec_bytes, n_groups, sh.d_c,         \
-                                                L.n_lists, part, ref_idx, codes, scale, zmin, z, \
-                                                mean, act);                                      \
-  k_app_proj<E><<<sh.d_ff / 16 * cdiv(sh.B, 4), 256, 0, st>>>(                                     \
-      static_cast<const E*>(kv_new), mean, act,                                                    \
-                                             static_cast<const E*>(w1), static_cast<const E*>(w2), \
-                                             sh.B, sh.C, sh.d_ff, dh)
+  k_app_sel_proj<E, KL, F8><<<sh.d_ff / 16 * cdiv(sh.B, 4), 256, 0, st>>>(                         \
+      kv, static_cast<const E*>(kv_new), pos, sv, sh.T, sh.C, sh.k, rec_bytes, n_groups, sh.d_c, \
+      L.n_lists, part, ref_idx, codes, scale, zmin, z, static_cast<const E*>(w1),              \
+      static_cast<const E*>(w2), sh.B, sh.d_ff, dh, act)
 #define RKV_APPK(E, F8) \
   if (sh.kl == 4) { RKV_APP(E, 4, F8); } else { RKV_APP(E, 8, F8); }
   if (sh.bf16) {

@@ -318,7 +318,7 @@ def test_noalloc_append_rejects_calls_beyond_its_fixed_scratch():
     needs more is refused on the host (RKV_ERR_WORKSPACE) before any device
     call, with a message naming the alternative."""
     from synth.configs import LLAMA8K
-    p = _p(LLAMA8K, B=400)
+    p = _p(LLAMA8K, B=900, T=4096)
     assert R.rkv_append_workspace_bytes(p) > 4 << 20      # so validation cannot pass
     st = R.rkv_append_noalloc(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
                               None, check=False)
