@@ -76,11 +76,15 @@ coordinate d of a head with d + D/2 ("rotate half") and turns pair i by
 position * theta^(-2i/D), with no frequency scaling; theta <= 0 leaves K
 unrotated; an index outside [0, B*T) yields a NaN row.
 
-Parity status: the selection, mean, compressor and quantiser are pinned by
-the tests in ``tests/test_oracle_pins.py`` (brute force, closed-form
-identities, special cases and hand-derived golden values).  The actual
-numbers of z and of the codes at the synthetic workloads have no printed
-counterpart in the pages: beyond those pins they are "parity unpinned".
+Parity status: the schedule, selection, mean, compressor, quantiser,
+packing, FP8 rounding, restore and append are pinned by the tests in
+``tests/test_oracle_pins.py`` (brute force, closed-form identities, special
+cases, a library routine and hand-derived golden values; the readings taken
+above each have one: the n_sink offset of the schedule, the stored fp16 grid
+of the codes, float32 integer decisions, identity-mode rounding).  The
+actual numbers of z and of the codes at the synthetic workloads have no
+printed counterpart in the pages: beyond those pins they are "parity
+unpinned".
 """
 from __future__ import annotations
 
