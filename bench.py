@@ -31,7 +31,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 # kernel behind each profiled stage
 STAGE_KERNEL = {"pack": "k_pack_weights", "norms": "k_setup", "dist": "k_dist_topk",
-                "merge": "k_topk_merge", "proj": "k_ref_proj", "swiglu": "k_swiglu",
+                "merge": "k_topk_merge", "swiglu": "k_swiglu",
                 "w3": "k_w3_quant", "quant": "k_quantize", "gather": "k_gather"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_{workload}.txt")
 
@@ -96,9 +96,10 @@ def stage_work(cfg, n_gather: int, refs):
         # set-up: weight repacking, schedule tables, reference rows and norms
         "norms": ("bytes", 2 * (2 * C * cfg.d_ff + cfg.d_ff * cfg.d_c) * esz + 3 * 4 * T
                   + 2 * B * nref * C * esz),
-        "dist": ("flops", 2.0 * C * pairs),
+        # the distance scan, plus the reference projection P = R[W1|W2] whose
+        # tiles run at the end of the same launch
+        "dist": ("flops", 2.0 * C * pairs + 2.0 * C * 2 * cfg.d_ff * B * nref),
         "merge": ("bytes", B * T * cfg.k * 4),
-        "proj": ("flops", 2.0 * C * 2 * cfg.d_ff * B * nref),
         "swiglu": ("flops", 2.0 * C * 2 * cfg.d_ff * B * nr),
         "w3": ("flops", 2.0 * cfg.d_ff * cfg.d_c * B * nr),
         "quant": ("bytes", B * nr * cfg.d_c * 4 + B * T * rec),
@@ -518,7 +519,7 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                 "kernel": dominant, "kernel_ms": round(dom_ms, 4), "work_per_launch": amount}
 
-    mfma_flops = sum(work[s][1] for s in ("dist", "proj", "swiglu", "w3"))
+    mfma_flops = sum(work[s][1] for s in ("dist", "swiglu", "w3"))
     encode_ms = sum(v for k, v in stages_ms.items() if k != "gather")
     tokens = cfg.B * cfg.T
     line = {

@@ -97,7 +97,10 @@ typedef struct {
  * over kv rows copy their operands to LDS with 64-bit lane addresses instead
  * of 32-bit offsets from a buffer resource.  Results are bit-identical; the
  * library takes that form by itself where a tile's kv rows span 2 GB or
- * more. */
+ * more.  RKV_SWIGLU_ORDER=row or =col (read at every call) forces the order
+ * in which the SwiGLU product visits its tiles (row tile fastest, or column
+ * tile fastest, which the library takes by itself once B*T*C*esize exceeds
+ * 192 MiB); results are bit-identical. */
 
 /* Bytes of device workspace rkv_encode / rkv_select need for *p (0 if *p is
  * invalid).  The workspace holds repacked weights, reference projections,
@@ -307,9 +310,12 @@ typedef enum {
   RKV_STAGE_NORMS = 1,   /* set-up, one launch: weight repacking, schedule
                             tables, reference rows, norms, reference-token
                             records                                         */
-  RKV_STAGE_DIST = 2,    /* distance contraction + partial top-k lists      */
+  RKV_STAGE_DIST = 2,    /* distance contraction + partial top-k lists; in
+                            the encodes the same launch also computes the
+                            reference projection P = R [W1|W2]              */
   RKV_STAGE_MERGE = 3,   /* top-k merge, ref_idx of non-reference tokens    */
-  RKV_STAGE_PROJ = 4,    /* reference projection P = R [W1|W2]              */
+  RKV_STAGE_PROJ = 4,    /* reserved: the reference projection now runs in
+                            the RKV_STAGE_DIST launch; records nothing      */
   RKV_STAGE_SWIGLU = 5,  /* token projection, mean branch, delta_h          */
   RKV_STAGE_W3 = 6,      /* latent z = delta_h W3 + group quantiser         */
   RKV_STAGE_QUANT = 7,   /* stand-alone quantiser (rkv_quantize)            */

@@ -139,6 +139,31 @@ struct StageScope {
   }
 };
 
+// One stage on `stream`, with its profiling events; a failed launch returns.
+#define RKV_STAGE(stage, call, name)                          \
+  do {                                                        \
+    StageScope scope_(stage, stream);                         \
+    if ((e = (call)) != hipSuccess) return device_status(e, name); \
+  } while (0)
+
+// The encode after its set-up launch: the distance scan (whose launch also
+// computes the reference projection from the packed weights wp), the top-k
+// merge, the SwiGLU product, and W3 with the quantiser.
+rkv_status encode_after_setup(const rkv::Shape& sh, const void* kv, char* ws,
+                              const rkv::Workspace& L, const char* wp, const char* w3p,
+                              int32_t* ref_idx, uint8_t* codes, uint16_t* scale, uint16_t* zmin,
+                              float* z, hipStream_t stream) {
+  hipError_t e;
+  RKV_STAGE(RKV_STAGE_DIST, rkv::launch_dist(sh, kv, ws, L, wp, stream), "dist");
+  RKV_STAGE(RKV_STAGE_MERGE, rkv::launch_merge(sh, ref_idx, ws, L, stream), "merge");
+  if (sh.nr > 0) {
+    RKV_STAGE(RKV_STAGE_SWIGLU, rkv::launch_swiglu(sh, kv, ws, L, wp, stream), "swiglu");
+    RKV_STAGE(RKV_STAGE_W3, rkv::launch_w3_quant(sh, ws, L, w3p, codes, scale, zmin, z, stream),
+              "w3");
+  }
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -211,23 +236,11 @@ rkv_status rkv_encode(const rkv_params* p, const void* kv, const void* w1, const
     return fail(RKV_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
   char* ws = static_cast<char*>(workspace);
   hipError_t e;
-#define RKV_STAGE(stage, call, name)                          \
-  do {                                                        \
-    StageScope scope_(stage, stream);                         \
-    if ((e = (call)) != hipSuccess) return device_status(e, name); \
-  } while (0)
   RKV_STAGE(RKV_STAGE_NORMS,
             rkv::launch_setup(sh, w1, w2, w3, kv, ws, L, ref_idx, codes, scale, zmin, z, stream),
             "setup");
-  RKV_STAGE(RKV_STAGE_DIST, rkv::launch_dist(sh, kv, ws, L, stream), "dist");
-  RKV_STAGE(RKV_STAGE_MERGE, rkv::launch_merge(sh, ref_idx, ws, L, stream), "merge");
-  if (sh.nr > 0) {
-    RKV_STAGE(RKV_STAGE_PROJ, rkv::launch_ref_proj(sh, kv, ws, L, ws + L.wp, stream), "proj");
-    RKV_STAGE(RKV_STAGE_SWIGLU, rkv::launch_swiglu(sh, kv, ws, L, ws + L.wp, stream), "swiglu");
-    RKV_STAGE(RKV_STAGE_W3,
-              rkv::launch_w3_quant(sh, ws, L, ws + L.w3p, codes, scale, zmin, z, stream), "w3");
-  }
-  return ok();
+  return encode_after_setup(sh, kv, ws, L, ws + L.wp, ws + L.w3p, ref_idx, codes, scale, zmin,
+                            z, stream);
 }
 
 size_t rkv_packed_weights_bytes(const rkv_params* p) {
@@ -283,15 +296,7 @@ rkv_status rkv_encode_packed(const rkv_params* p, const void* kv, const void* pa
             rkv::launch_setup(sh, nullptr, nullptr, nullptr, kv, ws, L, ref_idx, codes, scale,
                               zmin, z, stream),
             "setup");
-  RKV_STAGE(RKV_STAGE_DIST, rkv::launch_dist(sh, kv, ws, L, stream), "dist");
-  RKV_STAGE(RKV_STAGE_MERGE, rkv::launch_merge(sh, ref_idx, ws, L, stream), "merge");
-  if (sh.nr > 0) {
-    RKV_STAGE(RKV_STAGE_PROJ, rkv::launch_ref_proj(sh, kv, ws, L, wp, stream), "proj");
-    RKV_STAGE(RKV_STAGE_SWIGLU, rkv::launch_swiglu(sh, kv, ws, L, wp, stream), "swiglu");
-    RKV_STAGE(RKV_STAGE_W3, rkv::launch_w3_quant(sh, ws, L, w3p, codes, scale, zmin, z, stream),
-              "w3");
-  }
-  return ok();
+  return encode_after_setup(sh, kv, ws, L, wp, w3p, ref_idx, codes, scale, zmin, z, stream);
 }
 
 rkv_status rkv_select(const rkv_params* p, const void* kv, int32_t* ref_idx, void* workspace,
@@ -311,7 +316,7 @@ rkv_status rkv_select(const rkv_params* p, const void* kv, int32_t* ref_idx, voi
             rkv::launch_setup(sh, nullptr, nullptr, nullptr, kv, ws, L, ref_idx, nullptr, nullptr,
                               nullptr, nullptr, stream),
             "setup");
-  RKV_STAGE(RKV_STAGE_DIST, rkv::launch_dist(sh, kv, ws, L, stream), "dist");
+  RKV_STAGE(RKV_STAGE_DIST, rkv::launch_dist(sh, kv, ws, L, nullptr, stream), "dist");
   RKV_STAGE(RKV_STAGE_MERGE, rkv::launch_merge(sh, ref_idx, ws, L, stream), "merge");
   return ok();
 }

@@ -67,15 +67,15 @@ hipError_t launch_setup(const Shape& sh, const void* w1, const void* w2, const v
                         const void* kv, char* ws, const Workspace& L, int32_t* ref_idx,
                         uint8_t* codes, uint16_t* scale, uint16_t* zmin, float* z,
                         hipStream_t st);
+// The distance scan; with wp (the packed [W1|W2]) non-null, the same launch
+// also writes the reference projection P = R[W1|W2] (ws + L.proj).
 hipError_t launch_dist(const Shape& sh, const void* kv, char* ws, const Workspace& L,
-                       hipStream_t st);
+                       const char* wp, hipStream_t st);
 hipError_t launch_merge(const Shape& sh, int32_t* ref_idx, char* ws, const Workspace& L,
                         hipStream_t st);
 // The contractions read the packed weights at wp ([2 d_ff][C], W1 and W2
 // columns interleaved in blocks of 32) and w3p ([d_c][k3]): in the
 // workspace (packed by the set-up) or in a caller's pre-packed buffer.
-hipError_t launch_ref_proj(const Shape& sh, const void* kv, char* ws, const Workspace& L,
-                           const char* wp, hipStream_t st);
 hipError_t launch_swiglu(const Shape& sh, const void* kv, char* ws,
                          const Workspace& L, const char* wp, hipStream_t st);
 // W3 product fused with the quantiser; writes the records of non-reference tokens.

@@ -38,6 +38,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdlib>
+#include <cstring>
 
 namespace rkv {
 
@@ -46,14 +47,6 @@ namespace {
 // Workgroup tiles (4 waves in a 2 x 2 grid, each wave a quarter of the
 // tile) and, for bf16, the DMA ring: SB bytes of K per stage, NS stages.
 // reference projection: BM references x BN columns of [W1|W2] per workgroup
-template <typename E> struct ProjCfg {
-  static constexpr int BM = 128, BN = 128, SB = 128, NS = 4, WGM = 2, WGN = 2;
-  static constexpr int kThreads = 64 * WGM * WGN;
-};
-template <> struct ProjCfg<float> {
-  static constexpr int BM = 128, BN = 128, SB = 128, NS = 4, WGM = 2, WGN = 2;
-  static constexpr int kThreads = 64 * WGM * WGN;
-};
 // token projection + SwiGLU, and the W3 product + quantiser: bf16 runs use
 // 256 x 256 tiles on 8 waves (2 x 4, one workgroup per CU, a 2-stage ring
 // of 128-byte K slices); fp32 runs keep the 4-wave register-staged loop
@@ -84,6 +77,16 @@ template <typename E> struct DistCfg {
 template <> struct DistCfg<float> {
   static constexpr int BM = 128, BN = 256, SB = 128, NS = 2, WGM = 2, WGN = 2;
   static constexpr int kThreads = 64 * WGM * WGN;
+};
+// the reference projection's tiles, which run at the end of the distance
+// launch: the distance workgroup's wave grid, on a ring that fits its LDS
+template <typename E> struct ProjCfg {
+  static constexpr int BM = 128, BN = 256, SB = 128, NS = 2, WGM = DistCfg<E>::WGM,
+                       WGN = DistCfg<E>::WGN;
+};
+template <> struct ProjCfg<float> {
+  static constexpr int BM = 128, BN = 128, SB = 128, NS = 2, WGM = DistCfg<float>::WGM,
+                       WGN = DistCfg<float>::WGN;
 };
 constexpr int kEpiLd(int bn) { return bn + 8; }  // padded fp32 row of an LDS-staged tile
 
@@ -376,6 +379,42 @@ __global__ __launch_bounds__(256) void k_ref_store(const E* __restrict__ kv, int
 }
 
 // ------------------------------------------------------------------ retrieval
+// ------------------------------------------------------------------ reference projection
+// One tile of P = R [W1|W2] in fp32 ([RKV] §2.2 mean eq.: the first layer of
+// f_c is linear, so the mean of the chosen references' rows of P is the
+// first layer applied to their mean).  R is the compact reference rows
+// (M = B * nref), wp the packed [W1|W2] (N = 2 d_ff rows of C).  Tile `tile`
+// of tiles_m x tiles_n, row tile fastest.
+template <typename E>
+__device__ __forceinline__ void ref_proj_tile(const char* __restrict__ refs,
+                                              const char* __restrict__ wp,
+                                              float* __restrict__ proj, int C, int M, int N,
+                                              int tiles_m, int tile, char* lds) {
+  using CF = ProjCfg<E>;
+  constexpr int BM = CF::BM, BN = CF::BN, WGM = CF::WGM, WGN = CF::WGN;
+  constexpr int kWM = BM / WGM, kWN = BN / WGN, kTM = kWM / 32, kTN = kWN / 32;
+  const int mt = tile % tiles_m, nt = tile / tiles_m;
+  const int m0 = mt * BM, n0 = nt * BN;
+  const size_t rowb = size_t(C) * sizeof(E);
+  const int tid = threadIdx.x;
+  auto rowA = [&](int r) { return refs + size_t(min(m0 + r, M - 1)) * rowb; };
+  auto rowB = [&](int r) { return wp + size_t(min(n0 + r, N - 1)) * rowb; };
+  f32x16 acc[kTM][kTN];
+  tile_product<E, BM, BN, CF::SB, CF::NS, WGM, WGN>(rowA, rowB, int(rowb), lds, acc);
+  const int lane = tid & 63, wave = tid >> 6, wm = wave / WGN, wn = wave % WGN;
+#pragma unroll
+  for (int tm = 0; tm < kTM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < kTN; ++tn) {
+      const int col = n0 + wn * kWN + tn * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * kWM + tm * 32 + mfma32_row(r, lane);
+        if (row < M && col < N) proj[size_t(row) * N + col] = acc[tm][tn][r];
+      }
+    }
+}
+
 // One workgroup: BM references (chunk c) x BN non-reference tokens (tile tt)
 // of sequence b.  Every lane scans the dot products its own accumulators
 // hold (its kTN tokens against its kTM*16 references, in increasing j),
@@ -385,19 +424,31 @@ __global__ __launch_bounds__(256) void k_ref_store(const E* __restrict__ kv, int
 // causal pool, written as partial list c.
 // BUF: the buffer form of the operand DMA (the host checks that a token
 // tile's rows lie within 2^31 bytes).
+// Workgroups n_dist and beyond compute tiles of the reference projection
+// (ref_proj_tile) instead: that product reads only the compact reference
+// rows and the packed weights, and after every distance item has been
+// dealt its tiles fill the CUs the last round of items leaves idle.
 template <typename E, int KL, bool BUF>
 __global__ __launch_bounds__(DistCfg<E>::kThreads) void k_dist_topk(
     const char* __restrict__ kv, const char* __restrict__ refs, const float* __restrict__ ysq,
     float2* __restrict__ part, int B, int T, int C, const int* __restrict__ nrp, int nref,
-    int nr, int n_lists,
-    int n_tt) {
+    int nr, int n_lists, int n_tt, int n_dist, const char* __restrict__ wp,
+    float* __restrict__ proj, int proj_n, int proj_tiles_m) {
   using CF = DistCfg<E>;
+  using PF = ProjCfg<E>;
   constexpr int BM = CF::BM, BN = CF::BN, WGM = CF::WGM, WGN = CF::WGN;
   constexpr int kLists = 2 * WGM;                        // partial lists per token
   constexpr int kMain = mainloop_lds<E, BM, BN, CF::SB, CF::NS, WGM, WGN>();
   constexpr int kComb = BN * kLists * KL * 8;            // the lists, as (d', j) pairs
+  constexpr int kProj = mainloop_lds<E, PF::BM, PF::BN, PF::SB, PF::NS, PF::WGM, PF::WGN>();
+  static_assert(kProj <= (kMain > kComb ? kMain : kComb), "the projection tile fits the LDS");
   constexpr int kStaged = kMain > kComb ? kMain : kComb;
   __shared__ __attribute__((aligned(1024))) char lds[kStaged + BM * 4];
+  if (int(blockIdx.x) >= n_dist) {
+    ref_proj_tile<E>(refs, wp, proj, C, B * nref, proj_n, proj_tiles_m,
+                     int(blockIdx.x) - n_dist, lds);
+    return;
+  }
   float* ysq_l = reinterpret_cast<float*>(lds + kStaged);
   // Work items are the causal (token tile, reference chunk) pairs.  The
   // dispatcher deals workgroups to the 8 XCDs in turn, so workgroup w runs
@@ -621,39 +672,6 @@ __global__ __launch_bounds__(64) void k_topk_merge(const float2* __restrict__ pa
                       4 * h + 2 < kt ? sel[4 * h + 2] : -1, 4 * h + 3 < kt ? sel[4 * h + 3] : -1);
 }
 
-// ------------------------------------------------------------------ reference projection
-template <typename E>
-__global__ __launch_bounds__(ProjCfg<E>::kThreads) void k_ref_proj(const char* __restrict__ refs,
-                                                  const char* __restrict__ wp,
-                                                  float* __restrict__ proj, int C, int M, int N,
-                                                  int tiles_m) {
-  using CF = ProjCfg<E>;
-  constexpr int BM = CF::BM, BN = CF::BN, WGM = CF::WGM, WGN = CF::WGN;
-  constexpr int kWM = BM / WGM, kWN = BN / WGN, kTM = kWM / 32, kTN = kWN / 32;
-  __shared__ __attribute__((aligned(1024)))
-  char lds[mainloop_lds<E, BM, BN, CF::SB, CF::NS, WGM, WGN>()];
-  const int mt = blockIdx.x % tiles_m, nt = blockIdx.x / tiles_m;
-  const int m0 = mt * BM, n0 = nt * BN;
-  const size_t rowb = size_t(C) * sizeof(E);
-  const int tid = threadIdx.x;
-  auto rowA = [&](int r) { return refs + size_t(min(m0 + r, M - 1)) * rowb; };
-  auto rowB = [&](int r) { return wp + size_t(min(n0 + r, N - 1)) * rowb; };
-  f32x16 acc[kTM][kTN];
-  tile_product<E, BM, BN, CF::SB, CF::NS, WGM, WGN>(rowA, rowB, int(rowb), lds, acc);
-  const int lane = tid & 63, wave = tid >> 6, wm = wave / WGN, wn = wave % WGN;
-#pragma unroll
-  for (int tm = 0; tm < kTM; ++tm)
-#pragma unroll
-    for (int tn = 0; tn < kTN; ++tn) {
-      const int col = n0 + wn * kWN + tn * 32 + (lane & 31);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * kWM + tm * 32 + mfma32_row(r, lane);
-        if (row < M && col < N) proj[size_t(row) * N + col] = acc[tm][tn][r];
-      }
-    }
-}
-
 // ------------------------------------------------------------------ Swish
 __device__ __forceinline__ float silu_fast(float x) {
   // x * sigmoid(x) with the hardware exp2 and reciprocal (about 1e-7
@@ -678,7 +696,7 @@ __global__ __launch_bounds__(SwCfg<E>::kThreads) void k_swiglu(const char* __res
                                                 const int* __restrict__ selj,
                                                 char* __restrict__ dh, int T, int C,
                                                 const int* __restrict__ nrp, int nref, int nr,
-                                                int d_ff, int M) {
+                                                int d_ff, int M, int col_order) {
   using CF = SwCfg<E>;
   constexpr int BM = CF::BM, BN = CF::BN, WGM = CF::WGM, WGN = CF::WGN, NT = CF::kThreads;
   constexpr int kMain = mainloop_lds<E, BM, BN, CF::SB, CF::NS, WGM, WGN>();
@@ -688,11 +706,15 @@ __global__ __launch_bounds__(SwCfg<E>::kThreads) void k_swiglu(const char* __res
   uint32_t* poff_lds = reinterpret_cast<uint32_t*>(lds + kStaged);  // [BM][KL] P row byte offsets
   float* inv_lds = reinterpret_cast<float*>(lds + kStaged + BM * KL * 4);  // [BM] 1 / k_t
   const int N = 2 * d_ff;
-  // row tile fastest: all XCDs work through one column tile of Wp at a time,
-  // so every L2 holds that tile's rows of Wp and the columns of P its
-  // epilogue gathers, while each token tile is read once per column tile
-  const int tiles_m = (M + BM - 1) / BM;
-  const int mt = blockIdx.x % tiles_m, nt = blockIdx.x / tiles_m;
+  // Row tile fastest (col_order 0): all XCDs work through one column tile of
+  // Wp at a time, so every L2 holds that tile's rows of Wp and the columns of
+  // P its epilogue gathers, while each token tile is read once per column
+  // tile.  Column tile fastest (col_order 1): the column tiles of a token tile
+  // run together, so its kv rows leave HBM about once (the host picks this
+  // order when the kv rows outgrow the MALL).
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int mt = col_order ? int(blockIdx.x) / tiles_n : int(blockIdx.x) % tiles_m;
+  const int nt = col_order ? int(blockIdx.x) % tiles_n : int(blockIdx.x) / tiles_m;
   const int m0 = mt * BM, n0 = nt * BN;
   const size_t rowb = size_t(C) * sizeof(E);
   const int tid = threadIdx.x;
@@ -1414,17 +1436,23 @@ static bool kv_tiles_fit_buffer(const Shape& sh, int rows, bool flat) {
 }
 
 hipError_t launch_dist(const Shape& sh, const void* kv, char* ws, const Workspace& L,
-                       hipStream_t st) {
+                       const char* wp, hipStream_t st) {
   if (sh.nr == 0) return hipGetLastError();
   const auto* p = static_cast<const char*>(kv);
   const auto* y = reinterpret_cast<const float*>(ws + L.ysq);
   auto* part = reinterpret_cast<float2*>(ws + L.part);
   const auto* nrp = reinterpret_cast<const int*>(ws + L.nrp);
+  auto* proj = reinterpret_cast<float*>(ws + L.proj);
+  const int pM = sh.B * sh.nref, pN = 2 * sh.d_ff;
 #define RKV_DIST(E, KL, BUF)                                                                 \
   do {                                                                                       \
     const int n_tt = cdiv(sh.nr, DistCfg<E>::BN);                                            \
-    k_dist_topk<E, KL, BUF><<<dist_items<E>(sh, n_tt), DistCfg<E>::kThreads, 0, st>>>(       \
-        p, ws + L.refs, y, part, sh.B, sh.T, sh.C, nrp, sh.nref, sh.nr, sh.n_chunks, n_tt);  \
+    const int n_dist = dist_items<E>(sh, n_tt);                                              \
+    const int ptm = cdiv(pM, ProjCfg<E>::BM);                                                \
+    const int n_proj = wp != nullptr && pM > 0 ? ptm * cdiv(pN, ProjCfg<E>::BN) : 0;         \
+    k_dist_topk<E, KL, BUF><<<n_dist + n_proj, DistCfg<E>::kThreads, 0, st>>>(               \
+        p, ws + L.refs, y, part, sh.B, sh.T, sh.C, nrp, sh.nref, sh.nr, sh.n_chunks, n_tt,   \
+        n_dist, wp, proj, pN, ptm);                                                          \
   } while (0)
   if (sh.bf16) {
     const bool buf = kv_tiles_fit_buffer(sh, DistCfg<uint16_t>::BN, false);
@@ -1452,25 +1480,27 @@ hipError_t launch_merge(const Shape& sh, int32_t* ref_idx, char* ws, const Works
   return hipGetLastError();
 }
 
-hipError_t launch_ref_proj(const Shape& sh, const void* kv, char* ws, const Workspace& L,
-                           const char* wp, hipStream_t st) {
-  const int M = sh.B * sh.nref, N = 2 * sh.d_ff;
-  (void)kv;
-  auto* proj = reinterpret_cast<float*>(ws + L.proj);
-  auto go = [&](auto e) {
-    using E = decltype(e);
-    using CF = ProjCfg<E>;
-    const int tn = cdiv(N, CF::BN), tm = cdiv(M, CF::BM);
-    k_ref_proj<E><<<tn * tm, CF::kThreads, 0, st>>>(ws + L.refs, wp, proj, sh.C, M, N, tm);
-  };
-  if (sh.bf16) go(uint16_t{}); else go(float{});
-  return hipGetLastError();
+// k_swiglu's tile order.  With the row tile fastest, the kv rows are
+// streamed once per column tile; the passes after the first find them in the
+// 256 MB MALL while they fit there, and that order measured best at 128 MiB of
+// kv rows (it also leaves them there for whatever reads kv next).  Once they
+// outgrow it, every pass would fetch them from HBM again, and the column tile
+// fastest order, which runs the column tiles of a token tile together, measured
+// 6% faster at 256 MiB.  RKV_SWIGLU_ORDER=row or =col in the environment (read
+// at every launch) forces one order; both compute the same bits.
+static int swiglu_col_order(const Shape& sh) {
+  const char* force = std::getenv("RKV_SWIGLU_ORDER");
+  if (force && !std::strcmp(force, "row")) return 0;
+  if (force && !std::strcmp(force, "col")) return 1;
+  const double kv_bytes = double(sh.B) * sh.T * sh.C * (sh.bf16 ? 2.0 : 4.0);
+  return kv_bytes > 192.0 * (1 << 20) ? 1 : 0;
 }
 
 hipError_t launch_swiglu(const Shape& sh, const void* kv, char* ws,
                          const Workspace& L, const char* wp, hipStream_t st) {
   const int M = sh.B * sh.nr, N = 2 * sh.d_ff;
   if (M == 0) return hipGetLastError();
+  const int col_order = swiglu_col_order(sh);
   const auto* p = static_cast<const char*>(kv);
   const auto* proj = reinterpret_cast<const float*>(ws + L.proj);
   // P is addressed with 32-bit byte offsets (its size is checked on the host)
@@ -1479,7 +1509,7 @@ hipError_t launch_swiglu(const Shape& sh, const void* kv, char* ws,
   k_swiglu<E, KL, BUF><<<cdiv(N, SwCfg<E>::BN) * cdiv(M, SwCfg<E>::BM), SwCfg<E>::kThreads, 0,    \
                          st>>>(                                                                 \
       p, wp, proj, pbytes, reinterpret_cast<const int*>(ws + L.selj), ws + L.dh, sh.T,          \
-      sh.C, reinterpret_cast<const int*>(ws + L.nrp), sh.nref, sh.nr, sh.d_ff, M)
+      sh.C, reinterpret_cast<const int*>(ws + L.nrp), sh.nref, sh.nr, sh.d_ff, M, col_order)
   if (sh.bf16) {
     const bool buf = kv_tiles_fit_buffer(sh, SwCfg<uint16_t>::BM, true);
     if (sh.kl == 4) { if (buf) RKV_SW(uint16_t, 4, true); else RKV_SW(uint16_t, 4, false); }

@@ -258,6 +258,25 @@ def test_encode_dma_forms_bit_identical(cfg):
         assert np.array_equal(h1[key].view(np.uint8), h2[key].view(np.uint8)), key
 
 
+
+@pytest.mark.parametrize("cfg", [LLAMA8K.with_(name="llama_B3_T1500", B=3, T=1500), RAGGED[0],
+                                 RAGGED[1]], ids=lambda c: c.name)
+def test_swiglu_tile_orders_bit_identical(cfg):
+    """k_swiglu runs its tiles row tile fastest, or column tile fastest once
+    the kv rows outgrow the MALL; RKV_SWIGLU_ORDER forces either.  The order
+    only moves work between workgroups, so both give the same bits, with
+    ragged column tiles (d_ff = 96, 64) and token tiles that cross sequences."""
+    outs = []
+    for order in ("row", "col"):
+        os.environ["RKV_SWIGLU_ORDER"] = order
+        try:
+            _, _, h, _ = P.run_encode(generate(cfg))
+        finally:
+            del os.environ["RKV_SWIGLU_ORDER"]
+        outs.append(h)
+    for key in ("ref_idx", "codes", "scale", "zmin", "z"):
+        assert np.array_equal(outs[0][key].view(np.uint8), outs[1][key].view(np.uint8)), key
+
 def _bf16_bits(x):
     u = np.asarray(x, dtype=np.float32).view(np.uint32)
     return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)

@@ -43,15 +43,18 @@ def test_library_schedule_special_cases(T, s0, alpha, n_sink):
 
 def test_benchmark_work_counts():
     """Algorithmic work of the long-context workload: the causal pair count
-    (every non-reference token against the references before it) and the
-    token projection's flops, from the schedule by brute force."""
+    (every non-reference token against the references before it), the
+    distance launch's flops (those pairs, plus the reference projection that
+    runs in the same launch) and the token projection's flops, from the
+    schedule by brute force."""
     cfg = LLAMA32K
     refs = O.reference_schedule(cfg.T, cfg.stride)
     nref, nr, pairs = bench.schedule_counts(refs, cfg.T)
     assert (nref, nr) == (2048, 30720)
     assert pairs == sum(-(-t // cfg.stride) for t in range(cfg.T) if t % cfg.stride)
     work = bench.stage_work(cfg, 9830, refs)
-    assert work["dist"] == ("flops", 2.0 * cfg.C * pairs)
+    assert work["dist"] == ("flops", 2.0 * cfg.C * pairs + 2.0 * cfg.C * 2 * cfg.d_ff * nref)
+    assert "proj" not in work
     assert work["swiglu"] == ("flops", 2.0 * cfg.C * 2 * cfg.d_ff * nr)
     assert work["swiglu"][1] == 257698037760.0
 
