@@ -100,7 +100,11 @@ typedef struct {
  * more.  RKV_SWIGLU_ORDER=row or =col (read at every call) forces the order
  * in which the SwiGLU product visits its tiles (row tile fastest, or column
  * tile fastest, which the library takes by itself once B*T*C*esize exceeds
- * 192 MiB); results are bit-identical. */
+ * 192 MiB); results are bit-identical.  RKV_DIST_TILE=wide or =narrow (read
+ * at every call) forces the distance launch's tiling (8 waves on 256 tokens,
+ * or 4 waves on 128 tokens two workgroups to a CU, which the library takes
+ * for bf16 where the wide tiles give under two rounds of work items or
+ * C <= 1024); results are bit-identical. */
 
 /* Bytes of device workspace rkv_encode / rkv_select need for *p (0 if *p is
  * invalid).  The workspace holds repacked weights, reference projections,

@@ -69,25 +69,38 @@ template <> struct W3Cfg<float> {
   static constexpr int kThreads = 64 * WGM * WGN;
 };
                                                                  // difference, 2 WGs per CU
-// distance contraction: BM references (a chunk) x BN tokens per workgroup
-template <typename E> struct DistCfg {
-  static constexpr int BM = 192, BN = 256, SB = 128, NS = 2, WGM = 2, WGN = 4;
+// a workgroup tile of a contraction: BM x BN outputs on a WGM x WGN wave
+// grid, SB bytes of K per ring stage, NS stages
+template <int BM_, int BN_, int SB_, int NS_, int WGM_, int WGN_>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_, SB = SB_, NS = NS_, WGM = WGM_, WGN = WGN_;
   static constexpr int kThreads = 64 * WGM * WGN;
+};
+// distance contraction: BM references (a chunk) x BN tokens per workgroup.
+// Proj is the tile of the reference projection, whose workgroups run at the
+// end of the same launch: the distance tile's wave grid, on a ring that fits
+// its LDS.  kMinWaves: waves per SIMD the registers must leave room for.
+// bf16 runs take the wide tiles (8 waves, one workgroup per CU), or the
+// narrow ones (4 waves on 128 tokens and a three-stage ring of 64-byte
+// slices, two workgroups per CU, so that one scans its lists while the other
+// runs its main loop) where the host finds the wide ones short of work.
+template <typename E> struct DistCfg {
+  static constexpr int BM = 192, BN = 256, SB = 128, NS = 2, WGM = 2, WGN = 4, kMinWaves = 1;
+  static constexpr int kThreads = 64 * WGM * WGN;
+  using Proj = TileCfg<128, 256, 128, 2, WGM, WGN>;
+};
+struct DistCfgNarrow {
+  static constexpr int BM = 192, BN = 128, SB = 64, NS = 3, WGM = 2, WGN = 2, kMinWaves = 2;
+  static constexpr int kThreads = 64 * WGM * WGN;
+  using Proj = TileCfg<128, 128, 64, 3, WGM, WGN>;
 };
 template <> struct DistCfg<float> {
-  static constexpr int BM = 128, BN = 256, SB = 128, NS = 2, WGM = 2, WGN = 2;
+  static constexpr int BM = 128, BN = 256, SB = 128, NS = 2, WGM = 2, WGN = 2, kMinWaves = 1;
   static constexpr int kThreads = 64 * WGM * WGN;
+  using Proj = TileCfg<128, 128, 128, 2, WGM, WGN>;
 };
-// the reference projection's tiles, which run at the end of the distance
-// launch: the distance workgroup's wave grid, on a ring that fits its LDS
-template <typename E> struct ProjCfg {
-  static constexpr int BM = 128, BN = 256, SB = 128, NS = 2, WGM = DistCfg<E>::WGM,
-                       WGN = DistCfg<E>::WGN;
-};
-template <> struct ProjCfg<float> {
-  static constexpr int BM = 128, BN = 128, SB = 128, NS = 2, WGM = DistCfg<float>::WGM,
-                       WGN = DistCfg<float>::WGN;
-};
+static_assert(DistCfgNarrow::BM == DistCfg<uint16_t>::BM,
+              "both bf16 tilings cut the references into the same chunks (the merge's lists)");
 constexpr int kEpiLd(int bn) { return bn + 8; }  // padded fp32 row of an LDS-staged tile
 
 
@@ -385,12 +398,11 @@ __global__ __launch_bounds__(256) void k_ref_store(const E* __restrict__ kv, int
 // first layer applied to their mean).  R is the compact reference rows
 // (M = B * nref), wp the packed [W1|W2] (N = 2 d_ff rows of C).  Tile `tile`
 // of tiles_m x tiles_n, row tile fastest.
-template <typename E>
+template <typename E, typename CF>
 __device__ __forceinline__ void ref_proj_tile(const char* __restrict__ refs,
                                               const char* __restrict__ wp,
                                               float* __restrict__ proj, int C, int M, int N,
                                               int tiles_m, int tile, char* lds) {
-  using CF = ProjCfg<E>;
   constexpr int BM = CF::BM, BN = CF::BN, WGM = CF::WGM, WGN = CF::WGN;
   constexpr int kWM = BM / WGM, kWN = BN / WGN, kTM = kWM / 32, kTN = kWN / 32;
   const int mt = tile % tiles_m, nt = tile / tiles_m;
@@ -428,14 +440,13 @@ __device__ __forceinline__ void ref_proj_tile(const char* __restrict__ refs,
 // (ref_proj_tile) instead: that product reads only the compact reference
 // rows and the packed weights, and after every distance item has been
 // dealt its tiles fill the CUs the last round of items leaves idle.
-template <typename E, int KL, bool BUF>
-__global__ __launch_bounds__(DistCfg<E>::kThreads) void k_dist_topk(
+template <typename E, typename CF, int KL, bool BUF>
+__global__ __launch_bounds__(CF::kThreads, CF::kMinWaves) void k_dist_topk(
     const char* __restrict__ kv, const char* __restrict__ refs, const float* __restrict__ ysq,
     float2* __restrict__ part, int B, int T, int C, const int* __restrict__ nrp, int nref,
     int nr, int n_lists, int n_tt, int n_dist, const char* __restrict__ wp,
     float* __restrict__ proj, int proj_n, int proj_tiles_m) {
-  using CF = DistCfg<E>;
-  using PF = ProjCfg<E>;
+  using PF = typename CF::Proj;
   constexpr int BM = CF::BM, BN = CF::BN, WGM = CF::WGM, WGN = CF::WGN;
   constexpr int kLists = 2 * WGM;                        // partial lists per token
   constexpr int kMain = mainloop_lds<E, BM, BN, CF::SB, CF::NS, WGM, WGN>();
@@ -445,8 +456,8 @@ __global__ __launch_bounds__(DistCfg<E>::kThreads) void k_dist_topk(
   constexpr int kStaged = kMain > kComb ? kMain : kComb;
   __shared__ __attribute__((aligned(1024))) char lds[kStaged + BM * 4];
   if (int(blockIdx.x) >= n_dist) {
-    ref_proj_tile<E>(refs, wp, proj, C, B * nref, proj_n, proj_tiles_m,
-                     int(blockIdx.x) - n_dist, lds);
+    ref_proj_tile<E, PF>(refs, wp, proj, C, B * nref, proj_n, proj_tiles_m,
+                         int(blockIdx.x) - n_dist, lds);
     return;
   }
   float* ysq_l = reinterpret_cast<float*>(lds + kStaged);
@@ -1401,10 +1412,10 @@ hipError_t launch_pack_weights(const Shape& sh, const void* w1, const void* w2, 
   return hipGetLastError();
 }
 
-template <typename E>
+template <typename CF>
 static int dist_items(const Shape& sh, int n_tt) {
   // per-XCD item counts (same enumeration as the kernel); grid = 8 x max
-  constexpr int BM = DistCfg<E>::BM, BN = DistCfg<E>::BN;
+  constexpr int BM = CF::BM, BN = CF::BN;
   long per_xcd[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int g = 0; g < sh.B * n_tt; ++g) {
     const int tt = g % n_tt;
@@ -1435,6 +1446,26 @@ static bool kv_tiles_fit_buffer(const Shape& sh, int rows, bool flat) {
   return (span + 1) * rowb < (int64_t(1) << 31);
 }
 
+// The narrow bf16 distance tiles where the wide ones would give the chip
+// fewer than two rounds of items, or where K = C <= 1024 makes the list scan
+// (which a second workgroup per CU overlaps with matrix-core work) weigh
+// most.  Measured in one process: llama8b_T8k 0.047 -> 0.038 ms for the
+// launch, qwen7b_like_B2_T32k (C = 1024) 1% faster per step, llama8b_T32k 1.4%
+// slower per step with narrow tiles (so wide there).  RKV_DIST_TILE=wide or
+// =narrow in the environment (read at every launch) forces one; both give
+// the same bits (every list sees the same references in the same order).
+static bool dist_narrow(const Shape& sh) {
+  if (!sh.bf16) return false;
+  const char* force = std::getenv("RKV_DIST_TILE");
+  if (force && !std::strcmp(force, "wide")) return false;
+  if (force && !std::strcmp(force, "narrow")) return true;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  using W = DistCfg<uint16_t>;
+  return sh.C <= 1024 || dist_items<W>(sh, cdiv(sh.nr, W::BN)) < 2 * cus;
+}
+
 hipError_t launch_dist(const Shape& sh, const void* kv, char* ws, const Workspace& L,
                        const char* wp, hipStream_t st) {
   if (sh.nr == 0) return hipGetLastError();
@@ -1444,24 +1475,30 @@ hipError_t launch_dist(const Shape& sh, const void* kv, char* ws, const Workspac
   const auto* nrp = reinterpret_cast<const int*>(ws + L.nrp);
   auto* proj = reinterpret_cast<float*>(ws + L.proj);
   const int pM = sh.B * sh.nref, pN = 2 * sh.d_ff;
-#define RKV_DIST(E, KL, BUF)                                                                 \
-  do {                                                                                       \
-    const int n_tt = cdiv(sh.nr, DistCfg<E>::BN);                                            \
-    const int n_dist = dist_items<E>(sh, n_tt);                                              \
-    const int ptm = cdiv(pM, ProjCfg<E>::BM);                                                \
-    const int n_proj = wp != nullptr && pM > 0 ? ptm * cdiv(pN, ProjCfg<E>::BN) : 0;         \
-    k_dist_topk<E, KL, BUF><<<n_dist + n_proj, DistCfg<E>::kThreads, 0, st>>>(               \
+  auto go = [&](auto e, auto cf) {
+    using E = decltype(e);
+    using CF = decltype(cf);
+    using PF = typename CF::Proj;
+    const int n_tt = cdiv(sh.nr, CF::BN);
+    const int n_dist = dist_items<CF>(sh, n_tt);
+    const int ptm = cdiv(pM, PF::BM);
+    const int n_proj = wp != nullptr && pM > 0 ? ptm * cdiv(pN, PF::BN) : 0;
+    const bool buf = sizeof(E) == 2 && kv_tiles_fit_buffer(sh, CF::BN, false);
+#define RKV_DIST(KL, BUF)                                                                    \
+    k_dist_topk<E, CF, KL, BUF><<<n_dist + n_proj, CF::kThreads, 0, st>>>(                   \
         p, ws + L.refs, y, part, sh.B, sh.T, sh.C, nrp, sh.nref, sh.nr, sh.n_chunks, n_tt,   \
-        n_dist, wp, proj, pN, ptm);                                                          \
-  } while (0)
-  if (sh.bf16) {
-    const bool buf = kv_tiles_fit_buffer(sh, DistCfg<uint16_t>::BN, false);
-    if (sh.kl == 4) { if (buf) RKV_DIST(uint16_t, 4, true); else RKV_DIST(uint16_t, 4, false); }
-    else { if (buf) RKV_DIST(uint16_t, 8, true); else RKV_DIST(uint16_t, 8, false); }
-  } else {
-    if (sh.kl == 4) RKV_DIST(float, 4, false); else RKV_DIST(float, 8, false);
-  }
+        n_dist, wp, proj, pN, ptm)
+    if constexpr (sizeof(E) == 2) {
+      if (sh.kl == 4) { if (buf) RKV_DIST(4, true); else RKV_DIST(4, false); }
+      else { if (buf) RKV_DIST(8, true); else RKV_DIST(8, false); }
+    } else {
+      if (sh.kl == 4) RKV_DIST(4, false); else RKV_DIST(8, false);
+    }
 #undef RKV_DIST
+  };
+  if (!sh.bf16) go(float{}, DistCfg<float>{});
+  else if (dist_narrow(sh)) go(uint16_t{}, DistCfgNarrow{});
+  else go(uint16_t{}, DistCfg<uint16_t>{});
   return hipGetLastError();
 }
 

@@ -277,6 +277,29 @@ def test_swiglu_tile_orders_bit_identical(cfg):
     for key in ("ref_idx", "codes", "scale", "zmin", "z"):
         assert np.array_equal(outs[0][key].view(np.uint8), outs[1][key].view(np.uint8)), key
 
+
+@pytest.mark.parametrize("cfg", [LLAMA8K.with_(name="llama_B3_T1500", B=3, T=1500), RAGGED[0],
+                                 RAGGED[2], LLAMA8K_DYN.with_(name="llama_dyn_B2_T3000", B=2,
+                                                              T=3000)],
+                         ids=lambda c: c.name)
+def test_distance_tilings_bit_identical(cfg):
+    """The distance launch runs wide tiles (8 waves, 256 tokens) or narrow
+    ones (4 waves, 128 tokens, two workgroups per CU) as the shape asks;
+    RKV_DIST_TILE forces either.  Every per-token list sees the same
+    references in the same order under both, so all outputs (and the
+    reference projection that rides in the same launch) are the same bits,
+    for k = 4 and k > 4 lists, a growing schedule and several sequences."""
+    outs = []
+    for tiling in ("wide", "narrow"):
+        os.environ["RKV_DIST_TILE"] = tiling
+        try:
+            _, _, h, _ = P.run_encode(generate(cfg))
+        finally:
+            del os.environ["RKV_DIST_TILE"]
+        outs.append(h)
+    for key in ("ref_idx", "codes", "scale", "zmin", "z"):
+        assert np.array_equal(outs[0][key].view(np.uint8), outs[1][key].view(np.uint8)), key
+
 def _bf16_bits(x):
     u = np.asarray(x, dtype=np.float32).view(np.uint32)
     return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
