@@ -104,7 +104,10 @@ typedef struct {
  * at every call) forces the distance launch's tiling (8 waves on 256 tokens,
  * or 4 waves on 128 tokens two workgroups to a CU, which the library takes
  * for bf16 where the wide tiles give under two rounds of work items or
- * C <= 1024); results are bit-identical. */
+ * C <= 1024); results are bit-identical.  RKV_W3_TILE=wide or =narrow
+ * likewise forces the tiling of the W3 product with the quantiser (256 x 256,
+ * or 128 x 128 two workgroups to a CU, which the library takes for bf16 where
+ * the wide tiles would number fewer than half the CUs). */
 
 /* Bytes of device workspace rkv_encode / rkv_select need for *p (0 if *p is
  * invalid).  The workspace holds repacked weights, reference projections,

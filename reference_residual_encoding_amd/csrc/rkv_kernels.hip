@@ -61,11 +61,18 @@ template <> struct SwCfg<float> {
 // the W3 product streams delta_h from beyond L2: a deeper ring of shorter
 // stages (4 x 64 bytes; measured about 2-4% faster than 2 x 128 bytes)
 template <typename E> struct W3Cfg {
-  static constexpr int BM = 256, BN = 256, SB = 64, NS = 4, WGM = 2, WGN = 4;
+  static constexpr int BM = 256, BN = 256, SB = 64, NS = 4, WGM = 2, WGN = 4, kMinWaves = 1;
   static constexpr int kThreads = 64 * WGM * WGN;
 };
 template <> struct W3Cfg<float> {
-  static constexpr int BM = 256, BN = 256, SB = 128, NS = 2, WGM = 2, WGN = 2;
+  static constexpr int BM = 256, BN = 256, SB = 128, NS = 2, WGM = 2, WGN = 2, kMinWaves = 1;
+  static constexpr int kThreads = 64 * WGM * WGN;
+};
+// bf16 W3 tiles for shapes whose 256 x 256 tiles would leave most CUs idle:
+// 128 x 128 on 4 waves, the same ring, two workgroups per CU (g <= 64
+// divides 128, so groups stay whole)
+struct W3CfgNarrow {
+  static constexpr int BM = 128, BN = 128, SB = 64, NS = 4, WGM = 2, WGN = 2, kMinWaves = 2;
   static constexpr int kThreads = 64 * WGM * WGN;
 };
                                                                  // difference, 2 WGs per CU
@@ -870,8 +877,8 @@ __global__ __launch_bounds__(SwCfg<E>::kThreads) void k_swiglu(const char* __res
 // z = delta_h W3 for a tile of kW3BM non-reference tokens x kW3BN latent
 // columns, then the group quantiser on the tile ([RKV] §2.4), writing the
 // token's record (and z, if asked) at its place in [B][T].
-template <typename E, int BITS, int G8>
-__global__ __launch_bounds__(W3Cfg<E>::kThreads) void k_w3_quant(const char* __restrict__ dh,
+template <typename E, typename CF, int BITS, int G8>
+__global__ __launch_bounds__(CF::kThreads, CF::kMinWaves) void k_w3_quant(const char* __restrict__ dh,
                                                   const char* __restrict__ w3p, int K, int M,
                                                   int N, int tiles_m, int T,
                                                   const int* __restrict__ nrp, int nr,
@@ -879,9 +886,10 @@ __global__ __launch_bounds__(W3Cfg<E>::kThreads) void k_w3_quant(const char* __r
                                                   uint16_t* __restrict__ scale,
                                                   uint16_t* __restrict__ zmin,
                                                   float* __restrict__ z) {
-  using CF = W3Cfg<E>;
   constexpr int BM = CF::BM, BN = CF::BN, WGM = CF::WGM, WGN = CF::WGN, NT = CF::kThreads;
   static_assert(WGM == 2, "the epilogue stages one wave-row (half the tile) at a time");
+  static_assert(BN % 64 == 0 && (BM / 2) * (BN / 8) % NT == 0,
+                "whole groups (g <= 64) per tile row; every thread takes the same units");
   constexpr int LD = kEpiLd(BN);
   constexpr int HALF = BM / 2;
   constexpr int kMain = mainloop_lds<E, BM, BN, CF::SB, CF::NS, WGM, WGN>();
@@ -1558,6 +1566,23 @@ hipError_t launch_swiglu(const Shape& sh, const void* kv, char* ws,
   return hipGetLastError();
 }
 
+// The narrow bf16 W3 tiles where the wide ones would number fewer than half
+// the CUs (llama8b_T8k: 60 wide tiles).  RKV_W3_TILE=wide or =narrow in the
+// environment (read at every launch) forces one; the tile shape changes no
+// output's accumulation order, so both give the same bits.
+static bool w3_narrow(const Shape& sh) {
+  if (!sh.bf16) return false;
+  const char* force = std::getenv("RKV_W3_TILE");
+  if (force && !std::strcmp(force, "wide")) return false;
+  if (force && !std::strcmp(force, "narrow")) return true;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  using W = W3Cfg<uint16_t>;
+  const long wide = long(cdiv(sh.d_c, W::BN)) * cdiv(long(sh.B) * sh.nr, W::BM);
+  return 2 * wide < cus;
+}
+
 hipError_t launch_w3_quant(const Shape& sh, char* ws, const Workspace& L, const char* w3p,
                            uint8_t* codes, uint16_t* scale, uint16_t* zmin, float* z,
                            hipStream_t st) {
@@ -1565,27 +1590,29 @@ hipError_t launch_w3_quant(const Shape& sh, char* ws, const Workspace& L, const 
   if (M == 0) return hipGetLastError();
   const char* a = ws + L.dh;
   const char* w = w3p;
-#define RKV_W3(E, BITS, G8)                                                                   \
-  k_w3_quant<E, BITS, G8><<<cdiv(N, W3Cfg<E>::BN) * cdiv(M, W3Cfg<E>::BM), W3Cfg<E>::kThreads, \
-                            0, st>>>(a, w, sh.k3, M, N, cdiv(M, W3Cfg<E>::BM), sh.T,           \
-                                     reinterpret_cast<const int*>(ws + L.nrp),                 \
-                                     sh.nr, codes, scale, zmin, z)
-#define RKV_W3G(E, BITS)                      \
-  switch (sh.g) {                             \
-    case 8: RKV_W3(E, BITS, 1); break;        \
-    case 16: RKV_W3(E, BITS, 2); break;       \
-    case 32: RKV_W3(E, BITS, 4); break;       \
-    default: RKV_W3(E, BITS, 8); break;       \
-  }
-  if (sh.bf16) {
-    if (sh.b == 4) { RKV_W3G(uint16_t, 4) } else if (sh.b == 2) { RKV_W3G(uint16_t, 2) }
-    else { RKV_W3(uint16_t, kIdentityBits, 1); }
-  } else {
-    if (sh.b == 4) { RKV_W3G(float, 4) } else if (sh.b == 2) { RKV_W3G(float, 2) }
-    else { RKV_W3(float, kIdentityBits, 1); }
-  }
+  auto go = [&](auto e, auto cf) {
+    using E = decltype(e);
+    using CF = decltype(cf);
+    const int tm = cdiv(M, CF::BM);
+#define RKV_W3(BITS, G8)                                                                      \
+    k_w3_quant<E, CF, BITS, G8><<<cdiv(N, CF::BN) * tm, CF::kThreads, 0, st>>>(               \
+        a, w, sh.k3, M, N, tm, sh.T, reinterpret_cast<const int*>(ws + L.nrp), sh.nr, codes,  \
+        scale, zmin, z)
+#define RKV_W3G(BITS)                         \
+    switch (sh.g) {                           \
+      case 8: RKV_W3(BITS, 1); break;         \
+      case 16: RKV_W3(BITS, 2); break;        \
+      case 32: RKV_W3(BITS, 4); break;        \
+      default: RKV_W3(BITS, 8); break;        \
+    }
+    if (sh.b == 4) { RKV_W3G(4) } else if (sh.b == 2) { RKV_W3G(2) }
+    else { RKV_W3(kIdentityBits, 1); }
 #undef RKV_W3G
 #undef RKV_W3
+  };
+  if (!sh.bf16) go(float{}, W3Cfg<float>{});
+  else if (w3_narrow(sh)) go(uint16_t{}, W3CfgNarrow{});
+  else go(uint16_t{}, W3Cfg<uint16_t>{});
   return hipGetLastError();
 }
 

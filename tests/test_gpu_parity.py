@@ -300,6 +300,29 @@ def test_distance_tilings_bit_identical(cfg):
     for key in ("ref_idx", "codes", "scale", "zmin", "z"):
         assert np.array_equal(outs[0][key].view(np.uint8), outs[1][key].view(np.uint8)), key
 
+
+@pytest.mark.parametrize("cfg", [LLAMA8K.with_(name="llama_B3_T1500", B=3, T=1500), RAGGED[0],
+                                 RAGGED[2], LLAMA8K.with_(name="llama_g64_B2_T1200", B=2, T=1200,
+                                                          g=64),
+                                 LLAMA8K.with_(name="llama_identity_T1200", T=1200, b=16)],
+                         ids=lambda c: c.name)
+def test_w3_tilings_bit_identical(cfg):
+    """The W3 product with the quantiser runs 256 x 256 tiles, or 128 x 128
+    tiles two to a CU where the wide ones would leave most CUs idle;
+    RKV_W3_TILE forces either.  The tile shape changes no output's
+    accumulation order, so records and z are the same bits: g = 8 to 64,
+    INT2, INT4 and identity mode, d_c = 96 (a ragged column tile)."""
+    outs = []
+    for tiling in ("wide", "narrow"):
+        os.environ["RKV_W3_TILE"] = tiling
+        try:
+            _, _, h, _ = P.run_encode(generate(cfg))
+        finally:
+            del os.environ["RKV_W3_TILE"]
+        outs.append(h)
+    for key in ("ref_idx", "codes", "scale", "zmin", "z"):
+        assert np.array_equal(outs[0][key].view(np.uint8), outs[1][key].view(np.uint8)), key
+
 def _bf16_bits(x):
     u = np.asarray(x, dtype=np.float32).view(np.uint32)
     return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
