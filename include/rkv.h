@@ -107,7 +107,10 @@ typedef struct {
  * C <= 1024); results are bit-identical.  RKV_W3_TILE=wide or =narrow
  * likewise forces the tiling of the W3 product with the quantiser (256 x 256,
  * or 128 x 128 two workgroups to a CU, which the library takes for bf16 where
- * the wide tiles would number fewer than half the CUs). */
+ * the wide tiles would number fewer than half the CUs).  RKV_RESTORE_TILE=wide
+ * or =narrow likewise forces the tiling of rkv_restore's decoder product
+ * (256 x 256, or 128 x 128 two workgroups to a CU, which the library takes
+ * for bf16 where the wide tiles would fill at most half the CUs). */
 
 /* Bytes of device workspace rkv_encode / rkv_select need for *p (0 if *p is
  * invalid).  The workspace holds repacked weights, reference projections,

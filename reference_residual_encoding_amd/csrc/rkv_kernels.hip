@@ -979,11 +979,19 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ z, i
 // operand of the decoder product, then the product's epilogue adds the
 // reference mean and applies the rotation.
 template <typename E> struct RsCfg {
-  static constexpr int BM = 256, BN = 256, SB = 128, NS = 2, WGM = 2, WGN = 4;
+  static constexpr int BM = 256, BN = 256, SB = 128, NS = 2, WGM = 2, WGN = 4, kMinWaves = 1;
   static constexpr int kThreads = 64 * WGM * WGN;
 };
 template <> struct RsCfg<float> {
-  static constexpr int BM = 256, BN = 128, SB = 128, NS = 2, WGM = 2, WGN = 2;
+  static constexpr int BM = 256, BN = 128, SB = 128, NS = 2, WGM = 2, WGN = 2, kMinWaves = 1;
+  static constexpr int kThreads = 64 * WGM * WGN;
+};
+// bf16 restore tiles two to a CU, so that one workgroup's epilogue (mean
+// loads, rotation, stores) runs beside the other's main loop: 128 x 128 on
+// 4 waves, a four-stage ring of 64-byte slices (128 columns hold whole heads:
+// D divides 128)
+struct RsCfgNarrow {
+  static constexpr int BM = 128, BN = 128, SB = 64, NS = 4, WGM = 2, WGN = 2, kMinWaves = 2;
   static constexpr int kThreads = 64 * WGM * WGN;
 };
 
@@ -1030,13 +1038,13 @@ __global__ __launch_bounds__(256) void k_restore_prep(const uint8_t* __restrict_
 // FP8: the stored references are the E4M3 store [B][nref][C]; row of a
 // reference position p = its index j in the schedule (closed form, or
 // ~tab[p] from the schedule tables).
-template <typename E, int KL, bool FP8>
-__global__ __launch_bounds__(RsCfg<E>::kThreads) void k_restore(
+template <typename E, typename CF, int KL, bool FP8>
+__global__ __launch_bounds__(CF::kThreads, CF::kMinWaves) void k_restore(
     const char* __restrict__ zt, const char* __restrict__ wdp, int K, const int32_t* __restrict__ idx,
     int n_idx, int64_t total_rows, int T, int k, const int32_t* __restrict__ ref_idx,
     const char* __restrict__ kv, int C, int ND, int D, float theta, void* __restrict__ out,
     int out_bf16, SchedView sv, const int* __restrict__ tab) {
-  using CF = RsCfg<E>;
+  static_assert(CF::BN % 128 == 0, "a column tile holds whole heads (D divides 128)");
   constexpr int BM = CF::BM, BN = CF::BN, WGM = CF::WGM, WGN = CF::WGN, NT = CF::kThreads;
   static_assert(WGM == 2, "the epilogue stages one wave-row (half the tile) at a time");
   constexpr int LD = kEpiLd(BN);
@@ -1667,6 +1675,26 @@ RestoreWorkspace plan_restore(const Shape& sh, int64_t n_idx) {
   return L;
 }
 
+// The restore's tiling (bf16): narrow tiles where the wide ones would fill at
+// most half the CUs.  Measured in one process at C = 2048 (calls of
+// rkv_restore): 1,024 rows 72.5 -> 40.8 us, 4,096 rows 75.1 -> 49.4 us; at
+// 9,830 rows (1.2 rounds of wide tiles) narrow tiles lost, 118 against 104
+// us, as they did at 32,768 rows (312 against 265 us), on twice the operand
+// traffic per flop.  RKV_RESTORE_TILE=wide or =narrow in the environment
+// (read at every launch) forces one; both give the same bits.
+static bool restore_narrow(const Shape& sh, int n_idx) {
+  if (!sh.bf16) return false;
+  const char* force = std::getenv("RKV_RESTORE_TILE");
+  if (force && !std::strcmp(force, "wide")) return false;
+  if (force && !std::strcmp(force, "narrow")) return true;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  using W = RsCfg<uint16_t>;
+  const long wide = long(cdiv(n_idx, W::BM)) * cdiv(sh.C, W::BN);
+  return 2 * wide <= cus;
+}
+
 hipError_t launch_restore(const Shape& sh, int N, int D, const uint8_t* codes,
                           const uint16_t* scale, const uint16_t* zmin, const int32_t* ref_idx,
                           const void* kv, const void* wd, const int32_t* idx, int n_idx,
@@ -1705,17 +1733,21 @@ hipError_t launch_restore(const Shape& sh, int N, int D, const uint8_t* codes,
     if (e != hipSuccess) return e;
     tab = reinterpret_cast<const int*>(ws + L.tab);
   }
-#define RKV_RS(E, KL, F8)                                                                        \
-  k_restore<E, KL, F8><<<cdiv(n_idx, RsCfg<E>::BM) * cdiv(sh.C, RsCfg<E>::BN), RsCfg<E>::kThreads, \
-                         0, st>>>(ws + L.zt, ws + L.wdp, L.kr, idx, n_idx, total, sh.T, sh.k,     \
-                                  ref_idx, kvp, sh.C, N * D, D, theta, out, out_bf16 ? 1 : 0, sv, \
-                                  tab)
-#define RKV_RSK(E, F8) \
-  if (sh.kl == 4) RKV_RS(E, 4, F8); else RKV_RS(E, 8, F8)
-  if (sh.bf16) { if (sh.ref_fp8) { RKV_RSK(uint16_t, true); } else { RKV_RSK(uint16_t, false); } }
-  else { if (sh.ref_fp8) { RKV_RSK(float, true); } else { RKV_RSK(float, false); } }
-#undef RKV_RSK
+  auto go = [&](auto e, auto cf) {
+    using E = decltype(e);
+    using CF = decltype(cf);
+#define RKV_RS(KL, F8)                                                                          \
+    k_restore<E, CF, KL, F8><<<cdiv(n_idx, CF::BM) * cdiv(sh.C, CF::BN), CF::kThreads, 0,     \
+                               st>>>(ws + L.zt, ws + L.wdp, L.kr, idx, n_idx, total, sh.T, sh.k, \
+                                     ref_idx, kvp, sh.C, N * D, D, theta, out,                 \
+                                     out_bf16 ? 1 : 0, sv, tab)
+    if (sh.ref_fp8) { if (sh.kl == 4) RKV_RS(4, true); else RKV_RS(8, true); }
+    else { if (sh.kl == 4) RKV_RS(4, false); else RKV_RS(8, false); }
 #undef RKV_RS
+  };
+  if (!sh.bf16) go(float{}, RsCfg<float>{});
+  else if (restore_narrow(sh, n_idx)) go(uint16_t{}, RsCfgNarrow{});
+  else go(uint16_t{}, RsCfg<uint16_t>{});
   return hipGetLastError();
 }
 

@@ -140,6 +140,32 @@ def test_restore_sampled_tokens(cfg):
         _compare(got, _oracle(w, wd, rec, idx, cfg.rope_theta), tol, f"{cfg.name} {out_dtype}")
 
 
+@pytest.mark.parametrize("cfg", [LLAMA8K, LLAMA8K_DYN.with_(name="llama8b_T8k_dynamic_fp8ref",
+                                                            ref_fp8=True),
+                                 LLAMA8K.with_(name="llama8b_T8k_k5", k=5)],
+                         ids=lambda c: c.name)
+def test_restore_tilings_bit_identical(cfg):
+    """The restore runs 256 x 256 tiles, or 128 x 128 tiles two to a CU
+    where the wide ones would fill at most half the CUs; RKV_RESTORE_TILE
+    forces either.  The tile shape changes no output's arithmetic, so both
+    give the same bits, in f32 and bf16, with FP8 references and k > 4."""
+    import os
+    w = generate(cfg)
+    wd = decoder_weight(cfg)
+    pos = {b: P.sample_positions(cfg.T, cfg.stride, 150, seed=3 + b, cfg=cfg) for b in range(cfg.B)}
+    rec = _oracle_records(w, pos)
+    idx = np.concatenate([b * cfg.T + pos[b] for b in range(cfg.B)] + [[-1, 5]])
+    for out_dtype in ("f32", "bf16"):
+        got = {}
+        for tiling in ("wide", "narrow"):
+            os.environ["RKV_RESTORE_TILE"] = tiling
+            try:
+                got[tiling] = _run(w, wd, rec, idx, cfg.rope_theta, out_dtype)
+            finally:
+                del os.environ["RKV_RESTORE_TILE"]
+        assert np.array_equal(got["wide"].view(np.uint32), got["narrow"].view(np.uint32)), out_dtype
+
+
 def test_restore_reference_rows_exact_without_rotation():
     """References are stored as they are ([RKV] §2.4): unrotated, their
     restore is the stored row, bit for bit."""
