@@ -513,12 +513,17 @@ __global__ __launch_bounds__(CF::kThreads, CF::kMinWaves) void k_dist_topk(
   const size_t rowb = size_t(C) * sizeof(E);
   const char* base = kv + size_t(b) * T * rowb;
   const int tid = threadIdx.x;
-  for (int r = tid; r < BM; r += CF::kThreads) ysq_l[r] = ysq[size_t(b) * nref + min(m0 + r, nref - 1)];
+  // the chunk's reference norms: loaded before the main loop (their latency
+  // passes under the first stages' copies), published after it
+  static_assert(BM <= CF::kThreads, "one norm per thread");
+  const float ysq_r = tid < BM ? ysq[size_t(b) * nref + min(m0 + tid, nref - 1)] : 0.0f;
   const char* rbase = refs + size_t(b) * nref * rowb;
   auto rowA = [&](int r) { return rbase + size_t(min(m0 + r, nref - 1)) * rowb; };
   auto rowB = [&](int r) { return base + size_t(nrp[min(n0 + r, nr - 1)]) * rowb; };
   f32x16 acc[BM / WGM / 32][BN / WGN / 32];
   tile_product<E, BM, BN, CF::SB, CF::NS, WGM, WGN, BUF>(rowA, rowB, int(rowb), lds, acc);
+  if (tid < BM) ysq_l[tid] = ysq_r;
+  __syncthreads();
 
   // Lane l of wave (wm, wn) holds in register r of fragment (i, j) the dot
   // product of token column wn*kWN + 32j + l%32 with chunk reference
@@ -741,34 +746,22 @@ __global__ __launch_bounds__(SwCfg<E>::kThreads) void k_swiglu(const char* __res
   // missing reference gets the offset 2^31, past the end of P (which is
   // smaller than 2 GiB) also after a column offset is added: the buffer load
   // below returns zero for it.
+  // The chosen references' indices (one 16-byte load per 4, -1 pads) are
+  // loaded before the main loop, whose first stages' copies cover their
+  // latency, and turned into offsets after it.
   constexpr uint32_t kNone = 0x80000000u;
-  for (int r = tid; r < BM; r += NT) {
-    const int Q = m0 + r;
-    uint32_t off[KL];
-    int kt = 0;
+  static_assert(BM <= NT, "one token per thread");
+  const int Qr = m0 + tid;
+  int jr[KL];
 #pragma unroll
-    for (int i = 0; i < KL; ++i) off[i] = kNone;
-    if (Q < M) {
-      // the chosen references' indices (one 16-byte load per 4), -1 pads
-      const int b = Q / nr;
-      const int4* sj = reinterpret_cast<const int4*>(selj + size_t(Q) * KL);
-      int j[KL];
+  for (int i = 0; i < KL; ++i) jr[i] = -1;
+  if (tid < BM && Qr < M) {
+    const int4* sj = reinterpret_cast<const int4*>(selj + size_t(Qr) * KL);
 #pragma unroll
-      for (int h = 0; h < KL / 4; ++h) {
-        const int4 v = sj[h];
-        j[4 * h] = v.x; j[4 * h + 1] = v.y; j[4 * h + 2] = v.z; j[4 * h + 3] = v.w;
-      }
-#pragma unroll
-      for (int i = 0; i < KL; ++i) {
-        if (j[i] >= 0) {
-          off[i] = uint32_t(b * nref + j[i]) * uint32_t(N) * 4u;    // P row of reference j
-          ++kt;
-        }
-      }
+    for (int h = 0; h < KL / 4; ++h) {
+      const int4 v = sj[h];
+      jr[4 * h] = v.x; jr[4 * h + 1] = v.y; jr[4 * h + 2] = v.z; jr[4 * h + 3] = v.w;
     }
-#pragma unroll
-    for (int i = 0; i < KL; ++i) poff_lds[r * KL + i] = off[i];
-    inv_lds[r] = 1.0f / float(max(kt, 1));
   }
   auto rowA = [&](int r) {
     const int Q = min(m0 + r, M - 1);
@@ -778,6 +771,21 @@ __global__ __launch_bounds__(SwCfg<E>::kThreads) void k_swiglu(const char* __res
   constexpr int kTM = BM / WGM / 32, kTN = BN / WGN / 32;
   f32x16 acc[kTM][kTN];
   tile_product<E, BM, BN, CF::SB, CF::NS, WGM, WGN, BUF>(rowA, rowB, int(rowb), lds, acc);
+  if (tid < BM) {
+    const int b = Qr / nr;
+    int kt = 0;
+#pragma unroll
+    for (int i = 0; i < KL; ++i) {
+      uint32_t off = kNone;
+      if (jr[i] >= 0) {
+        off = uint32_t(b * nref + jr[i]) * uint32_t(N) * 4u;      // P row of reference jr[i]
+        ++kt;
+      }
+      poff_lds[tid * KL + i] = off;
+    }
+    inv_lds[tid] = 1.0f / float(max(kt, 1));
+  }
+  __syncthreads();
 
   // 2 (set-up). Four consecutive features of one row per lane: BN/8 lanes
   // per row, 16 rows per workgroup step.  Feature quad c holds W1 columns
@@ -900,16 +908,16 @@ __global__ __launch_bounds__(CF::kThreads, CF::kMinWaves) void k_w3_quant(const 
   const int m0 = mt * BM, n0 = nt * BN;
   const size_t rowb = size_t(K) * sizeof(E);
   const int tid = threadIdx.x;
-  // record row of every token of the tile (read after the main loop, whose
-  // barriers publish it)
-  for (int r = tid; r < BM; r += NT) {
-    const int Q = m0 + r;
-    rec_lds[r] = Q < M ? (Q / nr) * T + nrp[Q % nr] : -1;
-  }
+  // record row of every token of the tile: loaded before the main loop,
+  // written to LDS after it (the epilogue's first barrier publishes it)
+  static_assert(BM <= NT, "one token per thread");
+  int rec_r = -1;
+  if (tid < BM && m0 + tid < M) rec_r = ((m0 + tid) / nr) * T + nrp[(m0 + tid) % nr];
   auto rowA = [&](int r) { return dh + size_t(min(m0 + r, M - 1)) * rowb; };
   auto rowB = [&](int r) { return w3p + size_t(min(n0 + r, N - 1)) * rowb; };
   f32x16 acc[BM / WGM / 32][BN / WGN / 32];
   tile_product<E, BM, BN, CF::SB, CF::NS, WGM, WGN>(rowA, rowB, int(rowb), lds, acc);
+  if (tid < BM) rec_lds[tid] = rec_r;
   float* zt = reinterpret_cast<float*>(lds);
   // 8 latent values per lane; G8 consecutive lanes hold one group (groups
   // never straddle a row or the edge N: g divides both BN and d_c)
