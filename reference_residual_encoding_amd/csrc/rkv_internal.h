@@ -101,7 +101,10 @@ hipError_t launch_gather(const uint8_t* codes, const uint16_t* scale, const uint
 struct RestoreWorkspace {
   int kr;               // contraction length (2*d_c bf16 hi/lo pairs, d_c fp32)
   bool tables;          // schedule tables present (FP8 store of a dynamic schedule)
-  size_t wdp, zt, rpos, nrp, tab, total;
+  size_t wdp, zt,
+      rinfo,            // [n_idx][kl + 4] per selected row: its kl stored reference rows
+                        // (-1 none), 1/count (float bits), its position (-1 invalid)
+      rpos, nrp, tab, total;
 };
 RestoreWorkspace plan_restore(const Shape& sh, int64_t n_idx);
 hipError_t launch_restore(const Shape& sh, int N, int D, const uint8_t* codes,

@@ -39,6 +39,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <type_traits>
 
 namespace rkv {
 
@@ -998,6 +999,13 @@ template <> struct RsCfg<float> {
 // loads, rotation, stores) runs beside the other's main loop: 128 x 128 on
 // 4 waves, a four-stage ring of 64-byte slices (128 columns hold whole heads:
 // D divides 128)
+// the 8-wave restore's tiles for the rows after its last whole round:
+// 128 x 256, half the work of a 256 x 256 tile (measured better than 8-wave
+// 128 x 128 tiles, whose rounds took about 0.9 of a wide round)
+struct RsCfgTail {
+  static constexpr int BM = 128, BN = 256, SB = 128, NS = 2, WGM = 2, WGN = 4, kMinWaves = 1;
+  static constexpr int kThreads = 64 * WGM * WGN;
+};
 struct RsCfgNarrow {
   static constexpr int BM = 128, BN = 128, SB = 64, NS = 4, WGM = 2, WGN = 2, kMinWaves = 2;
   static constexpr int kThreads = 64 * WGM * WGN;
@@ -1008,7 +1016,14 @@ struct RsCfgNarrow {
 // float; zeros for reference tokens (all -1 ref_idx rows) and indices
 // outside [0, B*T).  z~ is
 // fmaf(q, Delta_h, m_h), as rkv_dequant_gather gives it.
-template <typename E, int BITS>
+// The unit at o = 0 of each row also writes the row's entry of rinfo
+// ([kl + 4] ints): the stored rows of the references whose mean the restore
+// adds (a reference token: its own row), 1/count as float bits, and the
+// token's position, or all -1 and position -1 for an index outside
+// [0, B*T), whose restored row is NaN.  FP8: the stored references are the
+// E4M3 store [B][nref][C]; row of a reference position p = its index j in
+// the schedule (closed form, or ~tab[p] from the schedule tables).
+template <typename E, int BITS, int KL, bool FP8>
 __global__ __launch_bounds__(256) void k_restore_prep(const uint8_t* __restrict__ codes,
                                                       const uint16_t* __restrict__ scale,
                                                       const uint16_t* __restrict__ zmin,
@@ -1016,13 +1031,49 @@ __global__ __launch_bounds__(256) void k_restore_prep(const uint8_t* __restrict_
                                                       int64_t n_idx, int64_t total_rows,
                                                       const int32_t* __restrict__ ref_idx, int k,
                                                       int d_c, int g,
-                                                      uint32_t* __restrict__ zt) {
+                                                      uint32_t* __restrict__ zt, int T,
+                                                      SchedView sv, const int* __restrict__ tab,
+                                                      int* __restrict__ rinfo) {
   const int64_t units = n_idx * (d_c / 8);
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
   for (int64_t u = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; u < units; u += stride) {
     const int64_t i = u / (d_c / 8);
     const int o = int(u - i * (d_c / 8)) * 8;
     const int64_t src = idx[i];
+    if (o == 0) {
+      int rows[KL];
+#pragma unroll
+      for (int q = 0; q < KL; ++q) rows[q] = -1;
+      int cnt = 0, pos = -1;
+      if (src >= 0 && src < total_rows) {
+        const int b = int(src / T), t = int(src % T);
+        pos = t;
+        auto store_row = [&](int p) {
+          if constexpr (FP8) {
+            bool is_ref;
+            const int j = tab ? ~tab[p] : refs_before(sv, p, is_ref);
+            return b * sv.nref + min(max(j, 0), sv.nref - 1);   // records from rkv_encode: in range
+          } else {
+            return b * T + p;
+          }
+        };
+        if (ref_idx[src * k] < 0) {                      // a reference: its own stored row
+          rows[0] = store_row(t);
+          cnt = 1;
+        } else {
+#pragma unroll
+          for (int q = 0; q < KL; ++q) {
+            const int p = q < k ? ref_idx[src * k + q] : -1;
+            if (p >= 0) { rows[q] = store_row(p); ++cnt; }
+          }
+        }
+      }
+      int* ri = rinfo + i * (KL + 4);
+#pragma unroll
+      for (int q = 0; q < KL; ++q) ri[q] = rows[q];
+      ri[KL] = __float_as_int(1.0f / float(max(cnt, 1)));
+      ri[KL + 1] = pos;
+    }
     // a reference token's ref_idx row is all -1 (every other token has at
     // least one reference: position 0 always is one)
     const bool live = src >= 0 && src < total_rows && ref_idx[src * k] >= 0;
@@ -1043,15 +1094,30 @@ __global__ __launch_bounds__(256) void k_restore_prep(const uint8_t* __restrict_
 
 // One workgroup: BM selected tokens x BN columns of KV^.  D divides BN, so a
 // tile holds whole heads and every rotation partner (d +- D/2) is in it.
-// FP8: the stored references are the E4M3 store [B][nref][C]; row of a
-// reference position p = its index j in the schedule (closed form, or
-// ~tab[p] from the schedule tables).
+// The rows of the stored references whose mean it adds come from the prep
+// kernel's table (FP8: rows of the E4M3 store).
+// theta^(-2i/D) for the D/2 <= 64 rotation pairs of a head, computed in
+// fp64 on the host once per call (a kernel argument)
+struct RateTable {
+  double r[64];
+};
+
+template <typename E, typename CF, int KL>
+constexpr int restore_lds() {
+  constexpr int LD = kEpiLd(CF::BN), HALF = CF::BM / 2;
+  constexpr int kMain = mainloop_lds<E, CF::BM, CF::BN, CF::SB, CF::NS, CF::WGM, CF::WGN>();
+  constexpr int kStaged = kMain > HALF * LD * 4 ? kMain : HALF * LD * 4;
+  return kStaged + CF::BM * (KL + 2) * 4 + 64 * 8;
+}
+
+// The tile at rows m0 .., columns n0 .. of KV^ (lds: restore_lds<E, CF, KL>()
+// bytes, 1024-byte aligned).
 template <typename E, typename CF, int KL, bool FP8>
-__global__ __launch_bounds__(CF::kThreads, CF::kMinWaves) void k_restore(
-    const char* __restrict__ zt, const char* __restrict__ wdp, int K, const int32_t* __restrict__ idx,
-    int n_idx, int64_t total_rows, int T, int k, const int32_t* __restrict__ ref_idx,
-    const char* __restrict__ kv, int C, int ND, int D, float theta, void* __restrict__ out,
-    int out_bf16, SchedView sv, const int* __restrict__ tab) {
+__device__ __forceinline__ void restore_tile(
+    char* lds, int m0, int n0,
+    const char* __restrict__ zt, const char* __restrict__ wdp, int K, int n_idx,
+    const int* __restrict__ rinfo, const char* __restrict__ kv, int C, int ND, int D,
+    float theta, const RateTable& rt, void* __restrict__ out, int out_bf16) {
   static_assert(CF::BN % 128 == 0, "a column tile holds whole heads (D divides 128)");
   constexpr int BM = CF::BM, BN = CF::BN, WGM = CF::WGM, WGN = CF::WGN, NT = CF::kThreads;
   static_assert(WGM == 2, "the epilogue stages one wave-row (half the tile) at a time");
@@ -1059,59 +1125,37 @@ __global__ __launch_bounds__(CF::kThreads, CF::kMinWaves) void k_restore(
   constexpr int HALF = BM / 2;
   constexpr int kMain = mainloop_lds<E, BM, BN, CF::SB, CF::NS, WGM, WGN>();
   constexpr int kStaged = kMain > HALF * LD * 4 ? kMain : HALF * LD * 4;
-  __shared__ __attribute__((aligned(1024))) char lds[kStaged + BM * (KL + 2) * 4 + 64 * 8];
   int* rows_lds = reinterpret_cast<int*>(lds + kStaged);            // [BM][KL] kv rows, -1 none
   float* inv_lds = reinterpret_cast<float*>(lds + kStaged + BM * KL * 4);  // [BM] 1 / count
   int* pos_lds = reinterpret_cast<int*>(lds + kStaged + BM * (KL + 1) * 4);  // [BM] t, -1 invalid
   double* rate = reinterpret_cast<double*>(lds + kStaged + BM * (KL + 2) * 4);  // [D/2] theta^(-2i/D)
-  const int tiles_m = (n_idx + BM - 1) / BM;
-  const int mt = blockIdx.x % tiles_m, nt = blockIdx.x / tiles_m;
-  const int m0 = mt * BM, n0 = nt * BN;
   const int tid = threadIdx.x;
-  for (int r = tid; r < BM; r += NT) {
-    const int i = m0 + r;
-    int rows[KL];
+  // The row's entry of the prep kernel's table: loaded before the main loop
+  // (its latency passes under the first stages' copies), written to LDS
+  // after it, where the epilogue's first barrier publishes it.  Rows past
+  // n_idx repeat the last row; their results are not stored.
+  static_assert(BM <= NT, "one row per thread");
+  constexpr int kRI = (KL + 4) / 4;
+  int4 ri[kRI];
+  if (tid < BM) {
+    const int4* src = reinterpret_cast<const int4*>(rinfo + size_t(min(m0 + tid, n_idx - 1)) * (KL + 4));
 #pragma unroll
-    for (int q = 0; q < KL; ++q) rows[q] = -1;
-    int cnt = 0, pos = -1;
-    if (i < n_idx) {
-      const int64_t fl = idx[i];
-      if (fl >= 0 && fl < total_rows) {
-        const int b = int(fl / T), t = int(fl % T);
-        pos = t;
-        auto store_row = [&](int p) {
-          if constexpr (FP8) {
-            bool is_ref;
-            const int j = tab ? ~tab[p] : refs_before(sv, p, is_ref);
-            return b * sv.nref + min(max(j, 0), sv.nref - 1);   // records from rkv_encode: in range
-          } else {
-            return b * T + p;
-          }
-        };
-        if (ref_idx[fl * k] < 0) {                       // a reference: its own stored row
-          rows[0] = store_row(t);
-          cnt = 1;
-        } else {
-#pragma unroll
-          for (int q = 0; q < KL; ++q) {
-            const int p = q < k ? ref_idx[fl * k + q] : -1;
-            if (p >= 0) { rows[q] = store_row(p); ++cnt; }
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < KL; ++q) rows_lds[r * KL + q] = rows[q];
-    inv_lds[r] = 1.0f / float(max(cnt, 1));
-    pos_lds[r] = pos;
+    for (int h = 0; h < kRI; ++h) ri[h] = src[h];
   }
   if (theta > 0.0f)
-    for (int i = tid; i < D / 2; i += NT) rate[i] = pow(double(theta), -2.0 * i / double(D));
+    for (int i = tid; i < D / 2; i += NT) rate[i] = rt.r[i];
   const size_t rowa = size_t(K) * sizeof(E);
   auto rowA = [&](int r) { return zt + size_t(min(m0 + r, n_idx - 1)) * rowa; };
   auto rowB = [&](int r) { return wdp + size_t(min(n0 + r, C - 1)) * rowa; };
   f32x16 acc[BM / WGM / 32][BN / WGN / 32];
   tile_product<E, BM, BN, CF::SB, CF::NS, WGM, WGN>(rowA, rowB, int(rowa), lds, acc);
+  if (tid < BM) {
+    const int* v = reinterpret_cast<const int*>(ri);
+#pragma unroll
+    for (int q = 0; q < KL; ++q) rows_lds[tid * KL + q] = v[q];
+    inv_lds[tid] = __int_as_float(v[KL]);
+    pos_lds[tid] = v[KL + 1];
+  }
 
   float* tile = reinterpret_cast<float*>(lds);
   constexpr int kV = BN / 8;                             // 8-column vectors per row
@@ -1198,6 +1242,34 @@ __global__ __launch_bounds__(CF::kThreads, CF::kMinWaves) void k_restore(
       }
     }
     __syncthreads();
+  }
+}
+
+// One launch of the restore: workgroups below n_wide take CF tiles over the
+// rows [0, rows_wide) (whole rounds of the chip, or every row), the rest
+// take CT tiles (the same wave count) over the rows [rows_wide, n_idx), so
+// the part of the call that does not fill a round of CF tiles runs in
+// smaller ones.  rows_wide is a multiple of CF::BM or n_idx; n_wide = 0,
+// rows_wide = 0 gives a launch of CT tiles alone.
+template <typename E, typename CF, typename CT, int KL, bool FP8>
+__global__ __launch_bounds__(CF::kThreads, CF::kMinWaves) void k_restore(
+    int n_wide, int rows_wide,
+    const char* __restrict__ zt, const char* __restrict__ wdp, int K, int n_idx,
+    const int* __restrict__ rinfo, const char* __restrict__ kv, int C, int ND, int D,
+    float theta, RateTable rt, void* __restrict__ out, int out_bf16) {
+  static_assert(CF::kThreads == CT::kThreads, "one block size");
+  constexpr int kW = restore_lds<E, CF, KL>(), kT = restore_lds<E, CT, KL>();
+  __shared__ __attribute__((aligned(1024))) char lds[kW > kT ? kW : kT];
+  const int w = int(blockIdx.x);
+  if (w < n_wide) {
+    const int tm = (rows_wide + CF::BM - 1) / CF::BM;   // row tile fastest
+    restore_tile<E, CF, KL, FP8>(lds, (w % tm) * CF::BM, (w / tm) * CF::BN, zt, wdp, K, n_idx,
+                                 rinfo, kv, C, ND, D, theta, rt, out, out_bf16);
+  } else {
+    const int tm = (n_idx - rows_wide + CT::BM - 1) / CT::BM;
+    const int u = w - n_wide;
+    restore_tile<E, CT, KL, FP8>(lds, rows_wide + (u % tm) * CT::BM, (u / tm) * CT::BN, zt, wdp,
+                                 K, n_idx, rinfo, kv, C, ND, D, theta, rt, out, out_bf16);
   }
 }
 
@@ -1673,6 +1745,7 @@ RestoreWorkspace plan_restore(const Shape& sh, int64_t n_idx) {
   L.kr = sh.bf16 ? 2 * sh.d_c : sh.d_c;
   L.wdp = take(size_t(sh.C) * L.kr * sh.esize);
   L.zt = take(size_t(n_idx) * sh.d_c * 4);
+  L.rinfo = take(size_t(n_idx) * (sh.kl + 4) * 4);
   L.tables = sh.ref_fp8 && sh.alpha != 0.0;        // FP8 rows of a dynamic schedule: tab[p]
   if (L.tables) {
     L.rpos = take(size_t(sh.nref) * 4);
@@ -1688,19 +1761,45 @@ RestoreWorkspace plan_restore(const Shape& sh, int64_t n_idx) {
 // rkv_restore): 1,024 rows 72.5 -> 40.8 us, 4,096 rows 75.1 -> 49.4 us; at
 // 9,830 rows (1.2 rounds of wide tiles) narrow tiles lost, 118 against 104
 // us, as they did at 32,768 rows (312 against 265 us), on twice the operand
-// traffic per flop.  RKV_RESTORE_TILE=wide or =narrow in the environment
-// (read at every launch) forces one; both give the same bits.
+// traffic per flop.  RKV_RESTORE_TILE=narrow in the environment (read at
+// every launch) forces them, any other value the 8-wave tiles
+// (restore_wide_rows); every tiling gives the same bits.
 static bool restore_narrow(const Shape& sh, int n_idx) {
   if (!sh.bf16) return false;
   const char* force = std::getenv("RKV_RESTORE_TILE");
-  if (force && !std::strcmp(force, "wide")) return false;
   if (force && !std::strcmp(force, "narrow")) return true;
+  if (force) return false;                             // a forced 8-wave split
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess)
     (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   using W = RsCfg<uint16_t>;
   const long wide = long(cdiv(n_idx, W::BM)) * cdiv(sh.C, W::BN);
   return 2 * wide <= cus;
+}
+
+// Rows of a bf16 restore that go to 256 x 256 tiles: the whole rounds of
+// them (one tile per CU) when there is at least one and the rows after fit
+// in one round of 128 x 256 tiles; else every row.  In one process at
+// C = 2048, per call: 9,830 rows 102.8 -> 98.9 us (8,192 rows in one round
+// of 256 wide tiles, then 104 half tiles), 12,000 rows 124.3 -> 111.1 us,
+// 20,000 rows 176.7 -> 168.0 us; at 6,000 rows (no whole round) half tiles
+// alone lost, 78.4 against 71.9 us.  RKV_RESTORE_TILE (read at every launch)
+// forces the split: =wide every row in wide tiles, =tail none, =<rows> that
+// many rows (rounded down to a multiple of 256).
+static int restore_wide_rows(const Shape& sh, int n_idx) {
+  constexpr int WBM = RsCfg<uint16_t>::BM;
+  const char* force = std::getenv("RKV_RESTORE_TILE");
+  if (force && !std::strcmp(force, "wide")) return n_idx;
+  if (force && !std::strcmp(force, "tail")) return 0;
+  if (force && force[0] >= '0' && force[0] <= '9')
+    return std::min(std::atoi(force) / WBM * WBM, n_idx / WBM * WBM);
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int per_round = std::max(1, cus / cdiv(sh.C, RsCfg<uint16_t>::BN)) * WBM;
+  const int full = n_idx / per_round * per_round;
+  const int tail_tiles = cdiv(n_idx - full, RsCfgTail::BM) * cdiv(sh.C, RsCfgTail::BN);
+  return full > 0 && tail_tiles <= cus ? full : n_idx;
 }
 
 hipError_t launch_restore(const Shape& sh, int N, int D, const uint8_t* codes,
@@ -1718,20 +1817,6 @@ hipError_t launch_restore(const Shape& sh, int N, int D, const uint8_t* codes,
   if (sh.bf16) k_pack_weights<uint16_t><<<tiles, 256, 0, st>>>(J);
   else k_pack_weights<float><<<tiles, 256, 0, st>>>(J);
   const int64_t total = int64_t(sh.B) * sh.T;
-  const int grid = grid_for(int64_t(n_idx) * (sh.d_c / 8), 256);
-  auto* zt = reinterpret_cast<uint32_t*>(ws + L.zt);
-#define RKV_RP(E, BITS)                                                                       \
-  k_restore_prep<E, BITS><<<grid, 256, 0, st>>>(codes, scale, zmin, idx, n_idx, total, ref_idx, \
-                                                sh.k, sh.d_c, sh.g, zt)
-  if (sh.bf16) {
-    if (sh.b == 4) RKV_RP(uint16_t, 4); else if (sh.b == 2) RKV_RP(uint16_t, 2);
-    else RKV_RP(uint16_t, kIdentityBits);
-  } else {
-    if (sh.b == 4) RKV_RP(float, 4); else if (sh.b == 2) RKV_RP(float, 2);
-    else RKV_RP(float, kIdentityBits);
-  }
-#undef RKV_RP
-  const auto* kvp = static_cast<const char*>(kv);
   const SchedView sv{nullptr, sh.nref, sh.s, sh.n_sink};
   const int* tab = nullptr;
   if (L.tables) {
@@ -1741,21 +1826,52 @@ hipError_t launch_restore(const Shape& sh, int N, int D, const uint8_t* codes,
     if (e != hipSuccess) return e;
     tab = reinterpret_cast<const int*>(ws + L.tab);
   }
-  auto go = [&](auto e, auto cf) {
+  const int grid = grid_for(int64_t(n_idx) * (sh.d_c / 8), 256);
+  auto* zt = reinterpret_cast<uint32_t*>(ws + L.zt);
+  auto* rinfo = reinterpret_cast<int*>(ws + L.rinfo);
+  auto prep = [&](auto e, auto bits_c) {
+    using E = decltype(e);
+    constexpr int BITS = decltype(bits_c)::value;
+#define RKV_RP(KL, F8)                                                                        \
+    k_restore_prep<E, BITS, KL, F8><<<grid, 256, 0, st>>>(codes, scale, zmin, idx, n_idx, total, \
+                                                          ref_idx, sh.k, sh.d_c, sh.g, zt, sh.T, \
+                                                          sv, tab, rinfo)
+    if (sh.ref_fp8) { if (sh.kl == 4) RKV_RP(4, true); else RKV_RP(8, true); }
+    else { if (sh.kl == 4) RKV_RP(4, false); else RKV_RP(8, false); }
+#undef RKV_RP
+  };
+  using B4 = std::integral_constant<int, 4>;
+  using B2 = std::integral_constant<int, 2>;
+  using BI = std::integral_constant<int, kIdentityBits>;
+  if (sh.bf16) {
+    if (sh.b == 4) prep(uint16_t{}, B4{}); else if (sh.b == 2) prep(uint16_t{}, B2{});
+    else prep(uint16_t{}, BI{});
+  } else {
+    if (sh.b == 4) prep(float{}, B4{}); else if (sh.b == 2) prep(float{}, B2{});
+    else prep(float{}, BI{});
+  }
+  const auto* kvp = static_cast<const char*>(kv);
+  RateTable rt{};
+  if (theta > 0.0f)
+    for (int i = 0; i < D / 2; ++i) rt.r[i] = std::pow(double(theta), -2.0 * i / double(D));
+  // n_wide CF tiles over rows [0, rows_wide), then CT tiles over the rest
+  auto go = [&](auto e, auto cf, auto ct, int rows_wide) {
     using E = decltype(e);
     using CF = decltype(cf);
+    using CT = decltype(ct);
+    const int n_wide = cdiv(rows_wide, CF::BM) * cdiv(sh.C, CF::BN);
+    const int grid = n_wide + cdiv(n_idx - rows_wide, CT::BM) * cdiv(sh.C, CT::BN);
 #define RKV_RS(KL, F8)                                                                          \
-    k_restore<E, CF, KL, F8><<<cdiv(n_idx, CF::BM) * cdiv(sh.C, CF::BN), CF::kThreads, 0,     \
-                               st>>>(ws + L.zt, ws + L.wdp, L.kr, idx, n_idx, total, sh.T, sh.k, \
-                                     ref_idx, kvp, sh.C, N * D, D, theta, out,                 \
-                                     out_bf16 ? 1 : 0, sv, tab)
+    k_restore<E, CF, CT, KL, F8><<<grid, CF::kThreads, 0, st>>>(                              \
+        n_wide, rows_wide, ws + L.zt, ws + L.wdp, L.kr, n_idx, rinfo, kvp, sh.C, N * D, D,    \
+        theta, rt, out, out_bf16 ? 1 : 0)
     if (sh.ref_fp8) { if (sh.kl == 4) RKV_RS(4, true); else RKV_RS(8, true); }
     else { if (sh.kl == 4) RKV_RS(4, false); else RKV_RS(8, false); }
 #undef RKV_RS
   };
-  if (!sh.bf16) go(float{}, RsCfg<float>{});
-  else if (restore_narrow(sh, n_idx)) go(uint16_t{}, RsCfgNarrow{});
-  else go(uint16_t{}, RsCfg<uint16_t>{});
+  if (!sh.bf16) go(float{}, RsCfg<float>{}, RsCfg<float>{}, 0);
+  else if (restore_narrow(sh, n_idx)) go(uint16_t{}, RsCfgNarrow{}, RsCfgNarrow{}, 0);
+  else go(uint16_t{}, RsCfg<uint16_t>{}, RsCfgTail{}, restore_wide_rows(sh, n_idx));
   return hipGetLastError();
 }
 

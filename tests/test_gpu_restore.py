@@ -145,25 +145,31 @@ def test_restore_sampled_tokens(cfg):
                                  LLAMA8K.with_(name="llama8b_T8k_k5", k=5)],
                          ids=lambda c: c.name)
 def test_restore_tilings_bit_identical(cfg):
-    """The restore runs 256 x 256 tiles, or 128 x 128 tiles two to a CU
-    where the wide ones would fill at most half the CUs; RKV_RESTORE_TILE
-    forces either.  The tile shape changes no output's arithmetic, so both
-    give the same bits, in f32 and bf16, with FP8 references and k > 4."""
+    """The restore runs 256 x 256 tiles (with the rows after their last whole
+    round in 128 x 256 tiles of the same launch), or 128 x 128 tiles two to
+    a CU where the wide ones would fill at most half the CUs;
+    RKV_RESTORE_TILE forces every row into wide tiles, into the small 8-wave
+    tiles, into the 4-wave ones, or a split after 256 rows.  The tile shape
+    changes no output's arithmetic, so all give the same bits, in f32 and
+    bf16, with FP8 references and k > 4."""
     import os
     w = generate(cfg)
     wd = decoder_weight(cfg)
-    pos = {b: P.sample_positions(cfg.T, cfg.stride, 150, seed=3 + b, cfg=cfg) for b in range(cfg.B)}
+    pos = {b: P.sample_positions(cfg.T, cfg.stride, 200, seed=3 + b, cfg=cfg) for b in range(cfg.B)}
     rec = _oracle_records(w, pos)
     idx = np.concatenate([b * cfg.T + pos[b] for b in range(cfg.B)] + [[-1, 5]])
+    assert len(idx) > 256
     for out_dtype in ("f32", "bf16"):
         got = {}
-        for tiling in ("wide", "narrow"):
+        for tiling in ("wide", "tail", "narrow", "256"):
             os.environ["RKV_RESTORE_TILE"] = tiling
             try:
                 got[tiling] = _run(w, wd, rec, idx, cfg.rope_theta, out_dtype)
             finally:
                 del os.environ["RKV_RESTORE_TILE"]
-        assert np.array_equal(got["wide"].view(np.uint32), got["narrow"].view(np.uint32)), out_dtype
+        for tiling in ("tail", "narrow", "256"):
+            assert np.array_equal(got["wide"].view(np.uint32), got[tiling].view(np.uint32)), \
+                (out_dtype, tiling)
 
 
 def test_restore_reference_rows_exact_without_rotation():
