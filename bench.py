@@ -182,9 +182,11 @@ def cpu_baseline(w, n_tokens: int, seed: int = 0):
 
 
 def bench_restore(R, cfg, w, p, kv, out, idx, stream, args):
-    """rkv_restore of the gathered rows (decoder product z~ W_d, reference
-    mean, RoPE on K; bf16 out), timed on its own after the encode steps; the
-    records are those the timed encode wrote."""
+    """rkv_restore_packed of the gathered rows (decoder product z~ W_d,
+    reference mean, RoPE on K; bf16 out) with W_d packed once by
+    rkv_pack_decoder, timed on its own after the encode steps; the records
+    are those the timed encode wrote.  rkv_restore, which repacks W_d at
+    every call, is timed the same way beside it."""
     import numpy as np
     import torch
     from synth import decoder_weight
@@ -198,28 +200,44 @@ def bench_restore(R, cfg, w, p, kv, out, idx, stream, args):
     rout = torch.empty((n, cfg.C), dtype=torch.bfloat16, device=dev)
     wsb = R.rkv_restore_workspace_bytes(p, n)
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    pkb = R.rkv_packed_decoder_bytes(p)
+    packed = torch.empty(pkb, dtype=torch.uint8, device=dev)
+    R.rkv_pack_decoder(p, d_wd, packed, pkb, stream)
 
-    def call():
+    def call_packed():
+        R.rkv_restore_packed(p, out.codes, out.scale, out.zmin, out.ref_idx, kv, packed, pkb, idx,
+                             n, cfg.rope_theta, rout, "bf16", ws, wsb, stream)
+
+    def call_repack():
         R.rkv_restore(p, out.codes, out.scale, out.zmin, out.ref_idx, kv, d_wd, idx, n,
                       cfg.rope_theta, rout, "bf16", ws, wsb, stream)
 
-    for _ in range(max(args.warmup, 1)):
-        call()
+    def timed(call):
+        for _ in range(max(args.warmup, 1)):
+            call()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms_repack = timed(call_repack)
+    ms = timed(call_packed)
     st = R.STAGES.index("restore")
     R.rkv_profile_begin(1 << st)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
     for _ in range(args.steps):
-        call()
-    e1.record(stream)
+        call_packed()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
     tot, cnt = R.rkv_profile_read(st)
     R.rkv_profile_begin(0)
     flops = 2.0 * n * cfg.d_c * cfg.C           # z~ W_d, the method's product
-    return {"rows": n, "ms_per_call": round(ms, 4), "rows_per_s": round(n / (ms * 1e-3), 1),
+    return {"rows": n, "call": "rkv_restore_packed (W_d packed once by rkv_pack_decoder)",
+            "ms_per_call": round(ms, 4), "rows_per_s": round(n / (ms * 1e-3), 1),
+            "ms_per_call_rkv_restore_repacking": round(ms_repack, 4),
             "stage_ms": round(tot / cnt, 4),
             "decoder_tflops_algorithmic": round(flops / (tot / cnt * 1e-3) / 1e12, 2),
             "out_dtype": "bf16", "rope_theta": cfg.rope_theta}

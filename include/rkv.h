@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define RKV_ABI_VERSION 5
+#define RKV_ABI_VERSION 6
 
 typedef enum {
   RKV_OK = 0,
@@ -232,6 +232,29 @@ rkv_status rkv_restore(const rkv_params* p, const uint8_t* codes,
                        const int32_t* idx, int32_t n_idx, float rope_theta,
                        void* out, rkv_dtype out_dtype, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
+
+/* The restore with a pre-packed decoder weight ([RKV] §2.5: W_d is fixed,
+ * so the layout the matrix cores read need not be rebuilt at every call):
+ *   rkv_packed_decoder_bytes(p): bytes of that buffer for p's C, d_c and
+ *     dtype (0 for invalid p);
+ *   rkv_pack_decoder: writes it from wd [d_c][C] in p->dtype (packed: a
+ *     caller-owned device buffer of at least rkv_packed_decoder_bytes(p)
+ *     bytes, 16-byte aligned; its layout is private);
+ *   rkv_restore_packed: exactly rkv_restore (the same outputs, bit for
+ *     bit) with the packed buffer in place of wd; its workspace is
+ *     rkv_restore_workspace_bytes(p, n_idx) as well.
+ * Errors as rkv_restore, and RKV_ERR_WORKSPACE when packed_bytes is short.
+ * The buffer stays valid for any p with the same C, d_c and dtype. */
+size_t rkv_packed_decoder_bytes(const rkv_params* p);
+rkv_status rkv_pack_decoder(const rkv_params* p, const void* wd, void* packed,
+                            size_t packed_bytes, hipStream_t stream);
+rkv_status rkv_restore_packed(const rkv_params* p, const uint8_t* codes,
+                              const uint16_t* scale, const uint16_t* zmin,
+                              const int32_t* ref_idx, const void* kv,
+                              const void* packed, size_t packed_bytes,
+                              const int32_t* idx, int32_t n_idx, float rope_theta,
+                              void* out, rkv_dtype out_dtype, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
 
 /* Decode-time append ([RKV] §2.7 decode step 4): one new token per
  * sequence enters the cache.  For sequence b the new token sits at position

@@ -44,6 +44,9 @@ EXPORTS = (
     "rkv_profile_read",
     "rkv_restore_workspace_bytes",
     "rkv_restore",
+    "rkv_packed_decoder_bytes",
+    "rkv_pack_decoder",
+    "rkv_restore_packed",
     "rkv_append_workspace_bytes",
     "rkv_append",
     "rkv_append_noalloc",
@@ -53,7 +56,7 @@ EXPORTS = (
 
 STAGES = ("pack", "norms", "dist", "merge", "proj", "swiglu", "w3", "quant", "gather", "restore",
           "append", "store")
-RKV_ABI_VERSION = 5
+RKV_ABI_VERSION = 6
 RKV_REF_INPUT = 0
 RKV_REF_FP8 = 1
 
@@ -116,6 +119,13 @@ def lib() -> ctypes.CDLL:
         L.rkv_restore.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, i32, ctypes.c_float, vp,
                                   ctypes.c_int, vp, sz, vp]
         L.rkv_restore.restype = ctypes.c_int
+        L.rkv_packed_decoder_bytes.argtypes = [P]
+        L.rkv_packed_decoder_bytes.restype = sz
+        L.rkv_pack_decoder.argtypes = [P, vp, vp, sz, vp]
+        L.rkv_pack_decoder.restype = ctypes.c_int
+        L.rkv_restore_packed.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp, i32, ctypes.c_float,
+                                         vp, ctypes.c_int, vp, sz, vp]
+        L.rkv_restore_packed.restype = ctypes.c_int
         L.rkv_append_workspace_bytes.argtypes = [P]
         L.rkv_append_workspace_bytes.restype = sz
         L.rkv_append.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -353,6 +363,41 @@ def rkv_restore(p: rkv_params, codes, scale, zmin, ref_idx, kv, wd, idx, n_idx: 
                            int(out_dtype), _p(workspace, "workspace", None, workspace_bytes),
                            int(workspace_bytes), _s(stream))
     return _check("rkv_restore", st) if check else st
+
+
+def rkv_packed_decoder_bytes(p: rkv_params) -> int:
+    return int(lib().rkv_packed_decoder_bytes(ctypes.byref(p)))
+
+
+def rkv_pack_decoder(p: rkv_params, wd, packed, packed_bytes: int, stream=None, *,
+                     check: bool = True) -> int:
+    dt, es = _elem(p)
+    C = 2 * p.N * p.D
+    st = lib().rkv_pack_decoder(ctypes.byref(p), _p(wd, "wd", dt, p.d_c * C * es),
+                                _p(packed, "packed", None, packed_bytes), int(packed_bytes),
+                                _s(stream))
+    return _check("rkv_pack_decoder", st) if check else st
+
+
+def rkv_restore_packed(p: rkv_params, codes, scale, zmin, ref_idx, kv, packed,
+                       packed_bytes: int, idx, n_idx: int, rope_theta: float, out, out_dtype,
+                       workspace, workspace_bytes: int, stream=None, *,
+                       check: bool = True) -> int:
+    if isinstance(out_dtype, str):
+        out_dtype = {"f32": RKV_F32, "bf16": RKV_BF16}[out_dtype]
+    C, rows, n = 2 * p.N * p.D, p.B * p.T, max(int(n_idx), 0)
+    cb, sb = _record_sizes(p, rows)
+    odt, oes = _out_elem(out_dtype)
+    st = lib().rkv_restore_packed(ctypes.byref(p), _p(codes, "codes", _U8, cb),
+                                  _p(scale, "scale", _HALF, sb), _p(zmin, "zmin", _HALF, sb),
+                                  _p(ref_idx, "ref_idx", _I32, rows * p.k * 4),
+                                  _ref_store(p, kv), _p(packed, "packed", None, packed_bytes),
+                                  int(packed_bytes), _p(idx, "idx", _I32, n * 4), int(n_idx),
+                                  float(rope_theta), _p(out, "out", odt, n * C * oes),
+                                  int(out_dtype),
+                                  _p(workspace, "workspace", None, workspace_bytes),
+                                  int(workspace_bytes), _s(stream))
+    return _check("rkv_restore_packed", st) if check else st
 
 
 def rkv_append_workspace_bytes(p: rkv_params) -> int:

@@ -379,11 +379,15 @@ size_t rkv_restore_workspace_bytes(const rkv_params* p, int32_t n_idx) {
   return rkv::plan_restore(shape_of(p), n_idx).total;
 }
 
-rkv_status rkv_restore(const rkv_params* p, const uint8_t* codes, const uint16_t* scale,
-                       const uint16_t* zmin, const int32_t* ref_idx, const void* kv,
-                       const void* wd, const int32_t* idx, int32_t n_idx, float rope_theta,
-                       void* out, rkv_dtype out_dtype, void* workspace, size_t workspace_bytes,
-                       hipStream_t stream) {
+// The checks and launches of rkv_restore (is_packed false: wd the unpacked
+// weight, packed into the workspace first) and rkv_restore_packed
+// (is_packed true: the caller's packed buffer of packed_bytes).
+static rkv_status restore_common(const rkv_params* p, const uint8_t* codes, const uint16_t* scale,
+                                 const uint16_t* zmin, const int32_t* ref_idx, const void* kv,
+                                 bool is_packed, const void* wd, const void* packed, size_t packed_bytes,
+                                 const int32_t* idx, int32_t n_idx, float rope_theta, void* out,
+                                 rkv_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
   rkv_status st = check_restore(p, n_idx);
   if (st != RKV_OK) return st;
   if (out_dtype != RKV_F32 && out_dtype != RKV_BF16)
@@ -395,7 +399,7 @@ rkv_status rkv_restore(const rkv_params* p, const uint8_t* codes, const uint16_t
   RKV_NEED_GROUP_PTR(zmin);
   RKV_NEED_PTR(ref_idx);
   RKV_NEED_PTR(kv);
-  RKV_NEED_PTR(wd);
+  if (is_packed) RKV_NEED_PTR(packed); else RKV_NEED_PTR(wd);
   RKV_NEED_PTR(idx);
   RKV_NEED_PTR(out);
   RKV_NEED_PTR(workspace);
@@ -403,13 +407,59 @@ rkv_status rkv_restore(const rkv_params* p, const uint8_t* codes, const uint16_t
   const rkv::RestoreWorkspace L = rkv::plan_restore(sh, n_idx);
   if (workspace_bytes < L.total)
     return fail(RKV_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
+  if (is_packed && packed_bytes < rkv::packed_decoder_bytes(sh))
+    return fail(RKV_ERR_WORKSPACE, "packed decoder has %zu bytes, needs %zu", packed_bytes,
+                rkv::packed_decoder_bytes(sh));
+  char* ws = static_cast<char*>(workspace);
   hipError_t e;
+  if (!is_packed)
+    RKV_STAGE(RKV_STAGE_PACK, rkv::launch_pack_decoder(sh, wd, ws + L.wdp, stream), "pack");
+  const char* w = is_packed ? static_cast<const char*>(packed) : ws + L.wdp;
   RKV_STAGE(RKV_STAGE_RESTORE,
-            rkv::launch_restore(sh, p->N, p->D, codes, scale, zmin, ref_idx, kv, wd, idx, n_idx,
-                                rope_theta, out, out_dtype == RKV_BF16,
-                                static_cast<char*>(workspace), L, stream),
+            rkv::launch_restore(sh, p->N, p->D, codes, scale, zmin, ref_idx, kv, w, idx, n_idx,
+                                rope_theta, out, out_dtype == RKV_BF16, ws, L, stream),
             "restore");
   return ok();
+}
+
+rkv_status rkv_restore(const rkv_params* p, const uint8_t* codes, const uint16_t* scale,
+                       const uint16_t* zmin, const int32_t* ref_idx, const void* kv,
+                       const void* wd, const int32_t* idx, int32_t n_idx, float rope_theta,
+                       void* out, rkv_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  return restore_common(p, codes, scale, zmin, ref_idx, kv, false, wd, nullptr, 0, idx, n_idx,
+                        rope_theta, out, out_dtype, workspace, workspace_bytes, stream);
+}
+
+size_t rkv_packed_decoder_bytes(const rkv_params* p) {
+  if (check_restore(p, 0) != RKV_OK) return 0;
+  return rkv::packed_decoder_bytes(shape_of(p));
+}
+
+rkv_status rkv_pack_decoder(const rkv_params* p, const void* wd, void* packed,
+                            size_t packed_bytes, hipStream_t stream) {
+  rkv_status st = check_restore(p, 0);
+  if (st != RKV_OK) return st;
+  RKV_NEED_PTR(wd);
+  RKV_NEED_PTR(packed);
+  const rkv::Shape sh = shape_of(p);
+  if (packed_bytes < rkv::packed_decoder_bytes(sh))
+    return fail(RKV_ERR_WORKSPACE, "packed decoder has %zu bytes, needs %zu", packed_bytes,
+                rkv::packed_decoder_bytes(sh));
+  hipError_t e;
+  RKV_STAGE(RKV_STAGE_PACK,
+            rkv::launch_pack_decoder(sh, wd, static_cast<char*>(packed), stream), "pack");
+  return ok();
+}
+
+rkv_status rkv_restore_packed(const rkv_params* p, const uint8_t* codes, const uint16_t* scale,
+                              const uint16_t* zmin, const int32_t* ref_idx, const void* kv,
+                              const void* packed, size_t packed_bytes, const int32_t* idx,
+                              int32_t n_idx, float rope_theta, void* out, rkv_dtype out_dtype,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return restore_common(p, codes, scale, zmin, ref_idx, kv, true, nullptr, packed, packed_bytes,
+                        idx, n_idx, rope_theta, out, out_dtype, workspace, workspace_bytes,
+                        stream);
 }
 
 size_t rkv_append_workspace_bytes(const rkv_params* p) {

@@ -107,9 +107,15 @@ struct RestoreWorkspace {
       rpos, nrp, tab, total;
 };
 RestoreWorkspace plan_restore(const Shape& sh, int64_t n_idx);
+// The decoder weight packed for the restore's matrix cores ([C][kr] rows):
+// its bytes, and the launch that writes it from wd [d_c][C].
+size_t packed_decoder_bytes(const Shape& sh);
+hipError_t launch_pack_decoder(const Shape& sh, const void* wd, char* wdp, hipStream_t st);
+// The restore from the packed decoder weight wdp (in the workspace at L.wdp,
+// packed by rkv_restore, or a caller's buffer from rkv_pack_decoder).
 hipError_t launch_restore(const Shape& sh, int N, int D, const uint8_t* codes,
                           const uint16_t* scale, const uint16_t* zmin, const int32_t* ref_idx,
-                          const void* kv, const void* wd, const int32_t* idx, int n_idx,
+                          const void* kv, const char* wdp, const int32_t* idx, int n_idx,
                           float theta, void* out, bool out_bf16, char* ws,
                           const RestoreWorkspace& L, hipStream_t st);
 

@@ -1802,20 +1802,30 @@ static int restore_wide_rows(const Shape& sh, int n_idx) {
   return full > 0 && tail_tiles <= cus ? full : n_idx;
 }
 
-hipError_t launch_restore(const Shape& sh, int N, int D, const uint8_t* codes,
-                          const uint16_t* scale, const uint16_t* zmin, const int32_t* ref_idx,
-                          const void* kv, const void* wd, const int32_t* idx, int n_idx,
-                          float theta, void* out, bool out_bf16, char* ws,
-                          const RestoreWorkspace& L, hipStream_t st) {
-  if (n_idx == 0) return hipGetLastError();
+size_t packed_decoder_bytes(const Shape& sh) {
+  const int kr = sh.bf16 ? 2 * sh.d_c : sh.d_c;
+  return size_t(sh.C) * kr * sh.esize;
+}
+
+hipError_t launch_pack_decoder(const Shape& sh, const void* wd, char* wdp, hipStream_t st) {
   // W_d [d_c][C] -> [C][K] rows (bf16: each value twice, matching the pairs)
+  const int kr = sh.bf16 ? 2 * sh.d_c : sh.d_c;
   PackJobs J{};
-  J.j[0] = {wd, ws + L.wdp, sh.d_c, sh.C, L.kr, 0, sh.bf16 ? 1 : 0, (sh.C + 63) / 64, 0};
+  J.j[0] = {wd, wdp, sh.d_c, sh.C, kr, 0, sh.bf16 ? 1 : 0, (sh.C + 63) / 64, 0};
   const int tiles = (sh.d_c + 63) / 64 * J.j[0].tiles_c;
   J.j[1].first = tiles;
   J.j[2].first = tiles;
   if (sh.bf16) k_pack_weights<uint16_t><<<tiles, 256, 0, st>>>(J);
   else k_pack_weights<float><<<tiles, 256, 0, st>>>(J);
+  return hipGetLastError();
+}
+
+hipError_t launch_restore(const Shape& sh, int N, int D, const uint8_t* codes,
+                          const uint16_t* scale, const uint16_t* zmin, const int32_t* ref_idx,
+                          const void* kv, const char* wdp, const int32_t* idx, int n_idx,
+                          float theta, void* out, bool out_bf16, char* ws,
+                          const RestoreWorkspace& L, hipStream_t st) {
+  if (n_idx == 0) return hipGetLastError();
   const int64_t total = int64_t(sh.B) * sh.T;
   const SchedView sv{nullptr, sh.nref, sh.s, sh.n_sink};
   const int* tab = nullptr;
@@ -1863,7 +1873,7 @@ hipError_t launch_restore(const Shape& sh, int N, int D, const uint8_t* codes,
     const int grid = n_wide + cdiv(n_idx - rows_wide, CT::BM) * cdiv(sh.C, CT::BN);
 #define RKV_RS(KL, F8)                                                                          \
     k_restore<E, CF, CT, KL, F8><<<grid, CF::kThreads, 0, st>>>(                              \
-        n_wide, rows_wide, ws + L.zt, ws + L.wdp, L.kr, n_idx, rinfo, kvp, sh.C, N * D, D,    \
+        n_wide, rows_wide, ws + L.zt, wdp, L.kr, n_idx, rinfo, kvp, sh.C, N * D, D,           \
         theta, rt, out, out_bf16 ? 1 : 0)
     if (sh.ref_fp8) { if (sh.kl == 4) RKV_RS(4, true); else RKV_RS(8, true); }
     else { if (sh.kl == 4) RKV_RS(4, false); else RKV_RS(8, false); }

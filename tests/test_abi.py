@@ -347,3 +347,29 @@ def test_packed_weights_calls_check_sizes_on_the_host():
     assert st == R.RKV_ERR_WORKSPACE
     assert R.rkv_encode_packed(p, FAKE, None, need, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws, None,
                                check=False) == R.RKV_ERR_INVALID_ARG
+
+
+def test_packed_decoder_calls_check_sizes_on_the_host():
+    """rkv_pack_decoder / rkv_restore_packed refuse a packed decoder buffer
+    (or a workspace) smaller than their layout, and a NULL packed buffer,
+    before anything is enqueued."""
+    p = _p(LLAMA32K)
+    need = R.rkv_packed_decoder_bytes(p)
+    # W_d as C rows of the d_c latents, each value twice (the hi/lo pairs), bf16
+    assert need == 2048 * 2 * 512 * 2
+    assert R.rkv_packed_decoder_bytes(_p(LLAMA32K, D=96)) == 0      # restore needs D | 128
+    st = R.rkv_pack_decoder(p, FAKE, FAKE, need - 1, None, check=False)
+    assert st == R.RKV_ERR_WORKSPACE and str(need) in R.rkv_last_error()
+    n = 100
+    ws = R.rkv_restore_workspace_bytes(p, n)
+    st = R.rkv_restore_packed(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 256, FAKE, n, 1e4,
+                              FAKE, "bf16", FAKE, ws, None, check=False)
+    assert st == R.RKV_ERR_WORKSPACE
+    st = R.rkv_restore_packed(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, FAKE, n, 1e4, FAKE,
+                              "bf16", FAKE, ws - 256, None, check=False)
+    assert st == R.RKV_ERR_WORKSPACE
+    st = R.rkv_restore_packed(p, FAKE, FAKE, FAKE, FAKE, FAKE, None, need, FAKE, n, 1e4, FAKE,
+                              "bf16", FAKE, ws, None, check=False)
+    assert st == R.RKV_ERR_INVALID_ARG and "packed" in R.rkv_last_error()
+    assert R.rkv_restore_packed(p, None, None, None, None, None, None, 0, None, 0, 1e4, None,
+                                "bf16", None, 0, None) == R.RKV_OK             # nothing to do

@@ -48,7 +48,7 @@ def _oracle_records(w, positions_by_seq):
     return codes, scale, zmin, ref_idx
 
 
-def _run(w, wd, rec, idx, theta, out_dtype):
+def _run(w, wd, rec, idx, theta, out_dtype, packed=None):
     cfg = w.cfg
     p = P.params_of(cfg)
     codes, scale, zmin, ref_idx = rec
@@ -67,8 +67,13 @@ def _run(w, wd, rec, idx, theta, out_dtype):
                       device=dev)
     ws_bytes = R.rkv_restore_workspace_bytes(p, n)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    R.rkv_restore(p, d_codes, d_scale, d_zmin, d_ref, kv, d_wd, d_idx, n, theta, out, out_dtype,
-                  ws, ws_bytes, torch.cuda.current_stream().cuda_stream)
+    stream = torch.cuda.current_stream().cuda_stream
+    if packed is None:
+        R.rkv_restore(p, d_codes, d_scale, d_zmin, d_ref, kv, d_wd, d_idx, n, theta, out,
+                      out_dtype, ws, ws_bytes, stream)
+    else:                                   # (buffer, bytes) from rkv_pack_decoder
+        R.rkv_restore_packed(p, d_codes, d_scale, d_zmin, d_ref, kv, packed[0], packed[1], d_idx,
+                             n, theta, out, out_dtype, ws, ws_bytes, stream)
     torch.cuda.synchronize()
     return out[:n].float().cpu().numpy()
 
@@ -170,6 +175,29 @@ def test_restore_tilings_bit_identical(cfg):
         for tiling in ("tail", "narrow", "256"):
             assert np.array_equal(got["wide"].view(np.uint32), got[tiling].view(np.uint32)), \
                 (out_dtype, tiling)
+
+
+@pytest.mark.parametrize("cfg", [LLAMA8K, LLAMA8K_DYN.with_(name="llama8b_T8k_dynamic_fp8ref",
+                                                            ref_fp8=True)],
+                         ids=lambda c: c.name)
+def test_restore_packed_matches_restore(cfg):
+    """rkv_restore_packed with the buffer rkv_pack_decoder writes gives
+    exactly rkv_restore's rows (f32 and bf16 output), across two calls that
+    reuse the packed buffer."""
+    w = generate(cfg)
+    wd = decoder_weight(cfg)
+    pos = {b: P.sample_positions(cfg.T, cfg.stride, 150, seed=21 + b, cfg=cfg) for b in range(cfg.B)}
+    rec = _oracle_records(w, pos)
+    idx = np.concatenate([b * cfg.T + pos[b] for b in range(cfg.B)] + [[-1, 7]])
+    p = P.params_of(cfg)
+    d_wd = P.to_device(wd, cfg.dtype, "cuda")
+    nbytes = R.rkv_packed_decoder_bytes(p)
+    packed = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    R.rkv_pack_decoder(p, d_wd, packed, nbytes, torch.cuda.current_stream().cuda_stream)
+    for out_dtype in ("f32", "bf16"):
+        want = _run(w, wd, rec, idx, cfg.rope_theta, out_dtype)
+        got = _run(w, wd, rec, idx, cfg.rope_theta, out_dtype, packed=(packed, nbytes))
+        assert np.array_equal(want.view(np.uint32), got.view(np.uint32)), out_dtype
 
 
 def test_restore_reference_rows_exact_without_rotation():
