@@ -418,9 +418,9 @@ def main():
                     help="skip the cold-cache gather measurement")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the encode shards by sequence / token range, see the design notes).",
-              file=sys.stderr)
+        print("bench.py measures one GPU only: librkv has no multi-GPU path (the encode "
+              "would shard by sequence or by token range, with the reference rows exchanged "
+              "once).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
