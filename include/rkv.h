@@ -100,11 +100,13 @@ typedef struct {
  * more.  RKV_SWIGLU_ORDER=row or =col (read at every call) forces the order
  * in which the SwiGLU product visits its tiles (row tile fastest, or column
  * tile fastest, which the library takes by itself once B*T*C*esize exceeds
- * 192 MiB); results are bit-identical.  RKV_DIST_TILE=wide or =narrow (read
- * at every call) forces the distance launch's tiling (8 waves on 256 tokens,
- * or 4 waves on 128 tokens two workgroups to a CU, which the library takes
- * for bf16 where the wide tiles give under two rounds of work items or
- * C <= 1024); results are bit-identical.  RKV_W3_TILE=wide or =narrow
+ * 192 MiB); results are bit-identical.  RKV_DIST_TILE=wide, =narrow or
+ * =short (read at every call) forces the distance launch's tiling (8 waves
+ * on 256 tokens; 4 waves on 128 tokens two workgroups to a CU, which the
+ * library takes for bf16 where C <= 1024; the same on chunks of 128
+ * references, which it takes where the wide tiles give under two rounds of
+ * work items); results are bit-identical, and the workspace size does not
+ * depend on the tiling.  RKV_W3_TILE=wide or =narrow
  * likewise forces the tiling of the W3 product with the quantiser (256 x 256,
  * or 128 x 128 two workgroups to a CU, which the library takes for bf16 where
  * the wide tiles would number fewer than half the CUs).  RKV_RESTORE_TILE=wide

@@ -30,7 +30,9 @@ struct Shape {
   int nref;      // references per sequence under the schedule
   int nr;        // non-references per sequence, T - nref
   int kl;        // neighbour-list length kept per chunk (4 or 8, >= k)
-  int n_chunks;  // reference chunks (one partial top-k list each) per sequence
+  int dist_tiling;  // the distance launch's tiling: 0 wide, 1 narrow, 2 narrow on 128-reference chunks
+  int dist_bm;     // references per chunk of that tiling
+  int n_chunks;    // reference chunks (one partial top-k list each) per sequence
   int k3;        // contraction length of the W3 product (2*d_ff bf16 hi/lo, d_ff fp32)
   int n_sink;
   double alpha;

@@ -91,7 +91,8 @@ struct TileCfg {
 // bf16 runs take the wide tiles (8 waves, one workgroup per CU), or the
 // narrow ones (4 waves on 128 tokens and a three-stage ring of 64-byte
 // slices, two workgroups per CU, so that one scans its lists while the other
-// runs its main loop) where the host finds the wide ones short of work.
+// runs its main loop) where the host finds the wide ones short of work, on
+// chunks of 128 references where the wide tiles would not fill two rounds.
 template <typename E> struct DistCfg {
   static constexpr int BM = 192, BN = 256, SB = 128, NS = 2, WGM = 2, WGN = 4, kMinWaves = 1;
   static constexpr int kThreads = 64 * WGM * WGN;
@@ -107,8 +108,16 @@ template <> struct DistCfg<float> {
   static constexpr int kThreads = 64 * WGM * WGN;
   using Proj = TileCfg<128, 128, 128, 2, WGM, WGN>;
 };
-static_assert(DistCfgNarrow::BM == DistCfg<uint16_t>::BM,
-              "both bf16 tilings cut the references into the same chunks (the merge's lists)");
+struct DistCfgShort {
+  static constexpr int BM = 128, BN = 128, SB = 64, NS = 3, WGM = 2, WGN = 2, kMinWaves = 2;
+  static constexpr int kThreads = 64 * WGM * WGN;
+  using Proj = TileCfg<128, 128, 64, 3, WGM, WGN>;
+};
+// the smallest chunk of any tiling: the partial lists' buffer is sized for it
+constexpr int kMinChunk = 128;
+static_assert(DistCfgShort::BM == kMinChunk && DistCfg<float>::BM == kMinChunk &&
+              DistCfg<uint16_t>::BM >= kMinChunk && DistCfgNarrow::BM >= kMinChunk,
+              "no tiling cuts more chunks than kMinChunk gives");
 constexpr int kEpiLd(int bn) { return bn + 8; }  // padded fp32 row of an LDS-staged tile
 
 
@@ -1341,6 +1350,35 @@ const Schedule& schedule_for(int T, int s0, double alpha, int n_sink) {
   return last;
 }
 
+template <typename CF>
+static int dist_items(const Shape& sh, int n_tt);
+
+// The distance launch's tiling for bf16 runs (fp32 runs: 0): narrow tiles
+// (1) where the wide ones would give the chip fewer than two rounds of
+// items, or where K = C <= 1024 makes the list scan (which a second
+// workgroup per CU overlaps with matrix-core work) weigh most, on 128-
+// reference chunks (2) in the first case.  Measured in one process, per
+// step: llama8b_T8k 0.184 ms wide, 0.175 narrow, 0.137 narrow on 128-
+// reference chunks; qwen7b_like_B2_T32k (C = 1024) 0.469 wide, 0.461 narrow
+// (128-reference chunks tied, with a longer merge); llama8b_T32k wide
+// (narrow 1.4% and 128-reference chunks 4% slower).  RKV_DIST_TILE=wide,
+// =narrow or =short in the environment (read at every call) forces one; all
+// give the same bits (the chunks only group the candidates of each token's
+// lists, which the merge orders by (d, j)).
+static int choose_dist_tiling(const Shape& sh) {
+  if (!sh.bf16 || sh.nr == 0) return 0;
+  const char* force = std::getenv("RKV_DIST_TILE");
+  if (force && !std::strcmp(force, "wide")) return 0;
+  if (force && !std::strcmp(force, "narrow")) return 1;
+  if (force && !std::strcmp(force, "short")) return 2;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  using W = DistCfg<uint16_t>;
+  if (dist_items<W>(sh, cdiv(sh.nr, W::BN)) < 2 * cus) return 2;
+  return sh.C <= 1024 ? 1 : 0;
+}
+
 Shape make_shape(int B, int T, int N, int D, int d_ff, int d_c, int k, int g, int b, int s,
                  bool bf16, double alpha, int n_sink, bool ref_fp8) {
   Shape sh{};
@@ -1352,7 +1390,11 @@ Shape make_shape(int B, int T, int N, int D, int d_ff, int d_c, int k, int g, in
   sh.nref = int(sh.sched->rpos.size());
   sh.nr = T - sh.nref;
   sh.kl = k <= 4 ? 4 : 8;
-  sh.n_chunks = cdiv(sh.nref, bf16 ? DistCfg<uint16_t>::BM : DistCfg<float>::BM);
+  sh.dist_tiling = choose_dist_tiling(sh);
+  sh.dist_bm = !bf16 ? DistCfg<float>::BM
+             : sh.dist_tiling == 2 ? DistCfgShort::BM
+             : sh.dist_tiling == 1 ? DistCfgNarrow::BM : DistCfg<uint16_t>::BM;
+  sh.n_chunks = cdiv(sh.nref, sh.dist_bm);
   sh.k3 = bf16 ? 2 * d_ff : d_ff;
   return sh;
 }
@@ -1366,7 +1408,7 @@ Workspace plan_workspace(const Shape& sh) {
   L.ysq = take(size_t(sh.B) * sh.nref * 4);
   L.refs = take(size_t(sh.B) * sh.nref * sh.C * sh.esize);
   L.proj = take(size_t(sh.B) * sh.nref * 2 * sh.d_ff * 4);
-  L.part = take(size_t(sh.B) * sh.n_chunks * sh.nr * sh.kl * 8);
+  L.part = take(size_t(sh.B) * cdiv(sh.nref, kMinChunk) * sh.nr * sh.kl * 8);
   L.dh = take(size_t(sh.B) * sh.nr * sh.k3 * sh.esize);
   L.rpos = take(size_t(sh.nref) * 4);
   L.nrp = take(size_t(sh.nr) * 4);
@@ -1542,26 +1584,6 @@ static bool kv_tiles_fit_buffer(const Shape& sh, int rows, bool flat) {
   return (span + 1) * rowb < (int64_t(1) << 31);
 }
 
-// The narrow bf16 distance tiles where the wide ones would give the chip
-// fewer than two rounds of items, or where K = C <= 1024 makes the list scan
-// (which a second workgroup per CU overlaps with matrix-core work) weigh
-// most.  Measured in one process: llama8b_T8k 0.047 -> 0.038 ms for the
-// launch, qwen7b_like_B2_T32k (C = 1024) 1% faster per step, llama8b_T32k 1.4%
-// slower per step with narrow tiles (so wide there).  RKV_DIST_TILE=wide or
-// =narrow in the environment (read at every launch) forces one; both give
-// the same bits (every list sees the same references in the same order).
-static bool dist_narrow(const Shape& sh) {
-  if (!sh.bf16) return false;
-  const char* force = std::getenv("RKV_DIST_TILE");
-  if (force && !std::strcmp(force, "wide")) return false;
-  if (force && !std::strcmp(force, "narrow")) return true;
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess)
-    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  using W = DistCfg<uint16_t>;
-  return sh.C <= 1024 || dist_items<W>(sh, cdiv(sh.nr, W::BN)) < 2 * cus;
-}
-
 hipError_t launch_dist(const Shape& sh, const void* kv, char* ws, const Workspace& L,
                        const char* wp, hipStream_t st) {
   if (sh.nr == 0) return hipGetLastError();
@@ -1593,7 +1615,8 @@ hipError_t launch_dist(const Shape& sh, const void* kv, char* ws, const Workspac
 #undef RKV_DIST
   };
   if (!sh.bf16) go(float{}, DistCfg<float>{});
-  else if (dist_narrow(sh)) go(uint16_t{}, DistCfgNarrow{});
+  else if (sh.dist_tiling == 2) go(uint16_t{}, DistCfgShort{});
+  else if (sh.dist_tiling == 1) go(uint16_t{}, DistCfgNarrow{});
   else go(uint16_t{}, DistCfg<uint16_t>{});
   return hipGetLastError();
 }
@@ -1602,7 +1625,7 @@ hipError_t launch_merge(const Shape& sh, int32_t* ref_idx, char* ws, const Works
                         hipStream_t st) {
   const auto* part = reinterpret_cast<const float2*>(ws + L.part);
   const int nb = cdiv(long(sh.B) * sh.T, 64);   // one wave per block: every CU takes part
-  const int chunk = sh.bf16 ? DistCfg<uint16_t>::BM : DistCfg<float>::BM;
+  const int chunk = sh.dist_bm;
   const auto* tab = reinterpret_cast<const int*>(ws + L.tab);
   const auto* rpos = reinterpret_cast<const int*>(ws + L.rpos);
 #define RKV_MERGE(KL)                                                                        \

@@ -283,14 +283,15 @@ def test_swiglu_tile_orders_bit_identical(cfg):
                                                               T=3000)],
                          ids=lambda c: c.name)
 def test_distance_tilings_bit_identical(cfg):
-    """The distance launch runs wide tiles (8 waves, 256 tokens) or narrow
-    ones (4 waves, 128 tokens, two workgroups per CU) as the shape asks;
-    RKV_DIST_TILE forces either.  Every per-token list sees the same
-    references in the same order under both, so all outputs (and the
-    reference projection that rides in the same launch) are the same bits,
-    for k = 4 and k > 4 lists, a growing schedule and several sequences."""
+    """The distance launch runs wide tiles (8 waves, 256 tokens), narrow
+    ones (4 waves, 128 tokens, two workgroups per CU), or narrow ones on
+    128-reference chunks, as the shape asks; RKV_DIST_TILE forces any.  The
+    tilings only group each token's candidates into lists differently, and
+    the merge orders them by (d, j), so all outputs (and the reference
+    projection that rides in the same launch) are the same bits, for k = 4
+    and k > 4 lists, a growing schedule and several sequences."""
     outs = []
-    for tiling in ("wide", "narrow"):
+    for tiling in ("wide", "narrow", "short"):
         os.environ["RKV_DIST_TILE"] = tiling
         try:
             _, _, h, _ = P.run_encode(generate(cfg))
@@ -298,7 +299,8 @@ def test_distance_tilings_bit_identical(cfg):
             del os.environ["RKV_DIST_TILE"]
         outs.append(h)
     for key in ("ref_idx", "codes", "scale", "zmin", "z"):
-        assert np.array_equal(outs[0][key].view(np.uint8), outs[1][key].view(np.uint8)), key
+        for other in outs[1:]:
+            assert np.array_equal(outs[0][key].view(np.uint8), other[key].view(np.uint8)), key
 
 
 @pytest.mark.parametrize("cfg", [LLAMA8K.with_(name="llama_B3_T1500", B=3, T=1500), RAGGED[0],
