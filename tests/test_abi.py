@@ -373,3 +373,21 @@ def test_packed_decoder_calls_check_sizes_on_the_host():
     assert st == R.RKV_ERR_INVALID_ARG and "packed" in R.rkv_last_error()
     assert R.rkv_restore_packed(p, None, None, None, None, None, None, 0, None, 0, 1e4, None,
                                 "bf16", None, 0, None) == R.RKV_OK             # nothing to do
+
+
+def test_encode_workspace_size_does_not_depend_on_the_tiling(monkeypatch):
+    """The distance launch's tiling (wide, narrow, or narrow on 128-reference
+    chunks) is chosen per shape, or forced by RKV_DIST_TILE; the list buffer
+    is sized for the smallest chunk, so a workspace sized once fits every
+    tiling."""
+    from synth.configs import LLAMA8K
+    for cfg in (LLAMA32K, LLAMA8K):
+        p = _p(cfg)
+        sizes = set()
+        for tiling in ("wide", "narrow", "short", None):
+            if tiling is None:
+                monkeypatch.delenv("RKV_DIST_TILE", raising=False)
+            else:
+                monkeypatch.setenv("RKV_DIST_TILE", tiling)
+            sizes.add(R.rkv_encode_workspace_bytes(p))
+        assert len(sizes) == 1 and sizes.pop() > 0
