@@ -1004,10 +1004,6 @@ template <> struct RsCfg<float> {
   static constexpr int BM = 256, BN = 128, SB = 128, NS = 2, WGM = 2, WGN = 2, kMinWaves = 1;
   static constexpr int kThreads = 64 * WGM * WGN;
 };
-// bf16 restore tiles two to a CU, so that one workgroup's epilogue (mean
-// loads, rotation, stores) runs beside the other's main loop: 128 x 128 on
-// 4 waves, a four-stage ring of 64-byte slices (128 columns hold whole heads:
-// D divides 128)
 // the 8-wave restore's tiles for the rows after its last whole round:
 // 128 x 256, half the work of a 256 x 256 tile (measured better than 8-wave
 // 128 x 128 tiles, whose rounds took about 0.9 of a wide round)
@@ -1015,6 +1011,10 @@ struct RsCfgTail {
   static constexpr int BM = 128, BN = 256, SB = 128, NS = 2, WGM = 2, WGN = 4, kMinWaves = 1;
   static constexpr int kThreads = 64 * WGM * WGN;
 };
+// bf16 restore tiles two to a CU, so that one workgroup's epilogue (mean
+// loads, rotation, stores) runs beside the other's main loop: 128 x 128 on
+// 4 waves, a four-stage ring of 64-byte slices (128 columns hold whole heads:
+// D divides 128)
 struct RsCfgNarrow {
   static constexpr int BM = 128, BN = 128, SB = 64, NS = 4, WGM = 2, WGN = 2, kMinWaves = 2;
   static constexpr int kThreads = 64 * WGM * WGN;
@@ -1121,6 +1121,44 @@ constexpr int restore_lds() {
 
 // The tile at rows m0 .., columns n0 .. of KV^ (lds: restore_lds<E, CF, KL>()
 // bytes, 1024-byte aligned).
+// Eight consecutive stored values of a kv row (FP8 e4m3 references, bf16 or
+// fp32), loaded as raw words and decoded to float separately, so that loads
+// of several rows can be in flight before the first is used.
+template <typename E, bool FP8> struct KvRaw {
+  static constexpr int kBytes = FP8 ? 8 : 8 * int(sizeof(E));
+  uint32_t w[kBytes / 4];
+  __device__ __forceinline__ void load(const char* src) {
+    if constexpr (kBytes == 8) {
+      const uint2 x = *reinterpret_cast<const uint2*>(src);
+      w[0] = x.x; w[1] = x.y;
+    } else {
+#pragma unroll
+      for (int h = 0; h < kBytes / 16; ++h) {
+        const u32x4 x = reinterpret_cast<const u32x4*>(src)[h];
+        w[4 * h] = x[0]; w[4 * h + 1] = x[1]; w[4 * h + 2] = x[2]; w[4 * h + 3] = x[3];
+      }
+    }
+  }
+  __device__ __forceinline__ void decode(float* v) const {
+    if constexpr (FP8) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = fp8_e4m3_to_f32((w[0] >> (8 * e)) & 0xFFu);
+        v[4 + e] = fp8_e4m3_to_f32((w[1] >> (8 * e)) & 0xFFu);
+      }
+    } else if constexpr (sizeof(E) == 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] = __uint_as_float(w[e] << 16);
+        v[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = __uint_as_float(w[e]);
+    }
+  }
+};
+
 template <typename E, typename CF, int KL, bool FP8>
 __device__ __forceinline__ void restore_tile(
     char* lds, int m0, int n0,
@@ -1169,47 +1207,52 @@ __device__ __forceinline__ void restore_tile(
   float* tile = reinterpret_cast<float*>(lds);
   constexpr int kV = BN / 8;                             // 8-column vectors per row
   const size_t kvrow = size_t(C) * (FP8 ? 1 : sizeof(E));
+  constexpr int kUnits = HALF * kV;                      // 8-column units per half tile
+  static_assert(kUnits % NT == 0, "every thread takes the same number of units");
+  // units whose row loads are in flight together: at most 16 loads and 256
+  // bytes per thread, 8 loads for eight FP8 rows a unit (whose e4m3 decode
+  // would spill registers in the 8-wave tile)
+  constexpr int kLoads = (FP8 && KL == 8) ? 8 : 16;
+  constexpr int kB1 = 256 / (KL * KvRaw<E, FP8>::kBytes);
+  constexpr int kB0 = kLoads / KL < kB1 ? kLoads / KL : kB1;
+  constexpr int kB = kB0 < kUnits / NT ? kB0 : kUnits / NT;
+  static_assert(kB >= 1 && (kUnits / NT) % kB == 0, "whole batches of units");
   for (int half = 0; half < 2; ++half) {
     acc_to_lds<BM, BN, WGM, WGN>(acc, tile, LD, half);
     __syncthreads();
-    // a. + mean of the stored reference rows (NaN for an invalid index)
-    for (int u = tid; u < HALF * kV; u += NT) {
-      const int rl = u / kV, cv = (u % kV) * 8, rt = half * HALF + rl, col = n0 + cv;
-      if (col >= C) continue;
-      float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    // a. + mean of the stored reference rows (NaN for an invalid index).
+    // The row loads of kB units are issued before any is summed, so their
+    // L2 round trips overlap; each unit's sum keeps the order q = 0..KL-1.
+    // Columns past C load column 0 and store nothing.
+    for (int u0 = 0; u0 < kUnits; u0 += kB * NT) {
+      KvRaw<E, FP8> raw[kB][KL];
 #pragma unroll
-      for (int q = 0; q < KL; ++q) {
-        const int row = rows_lds[rt * KL + q];
-        const char* src = kv + size_t(max(row, 0)) * kvrow + size_t(col) * (FP8 ? 1 : sizeof(E));
-        float v[8];
-        if constexpr (FP8) {
-          const uint2 w = *reinterpret_cast<const uint2*>(src);
+      for (int j = 0; j < kB; ++j) {
+        const int u = u0 + j * NT + tid, rt = half * HALF + u / kV, col = n0 + (u % kV) * 8;
+        const size_t off = size_t(col < C ? col : 0) * (FP8 ? 1 : sizeof(E));
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v[e] = fp8_e4m3_to_f32((w.x >> (8 * e)) & 0xFFu);
-            v[4 + e] = fp8_e4m3_to_f32((w.y >> (8 * e)) & 0xFFu);
-          }
-        } else if constexpr (sizeof(E) == 2) {
-          const u32x4 w = *reinterpret_cast<const u32x4*>(src);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v[2 * e] = __uint_as_float(w[e] << 16);
-            v[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
-          }
-        } else {
-          const float4 a = reinterpret_cast<const float4*>(src)[0];
-          const float4 c2 = reinterpret_cast<const float4*>(src)[1];
-          v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-          v[4] = c2.x; v[5] = c2.y; v[6] = c2.z; v[7] = c2.w;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) m[e] += row >= 0 ? v[e] : 0.0f;
+        for (int q = 0; q < KL; ++q)
+          raw[j][q].load(kv + size_t(max(rows_lds[rt * KL + q], 0)) * kvrow + off);
       }
-      const float inv = inv_lds[rt];
-      const bool bad = pos_lds[rt] < 0;
-      float* tr = tile + rl * LD + cv;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) tr[e] = bad ? __builtin_nanf("") : tr[e] + m[e] * inv;
+      for (int j = 0; j < kB; ++j) {
+        const int u = u0 + j * NT + tid, rl = u / kV, cv = (u % kV) * 8, rt = half * HALF + rl;
+        if (n0 + cv >= C) continue;
+        float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int q = 0; q < KL; ++q) {
+          float v[8];
+          raw[j][q].decode(v);
+          const bool ok = rows_lds[rt * KL + q] >= 0;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) m[e] += ok ? v[e] : 0.0f;
+        }
+        const float inv = inv_lds[rt];
+        const bool bad = pos_lds[rt] < 0;
+        float* tr = tile + rl * LD + cv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tr[e] = bad ? __builtin_nanf("") : tr[e] + m[e] * inv;
+      }
     }
     __syncthreads();
     // b. rotate K at the token's position, write the row
