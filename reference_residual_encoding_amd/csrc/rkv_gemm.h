@@ -349,6 +349,233 @@ __device__ __forceinline__ void gemm_mainloop_dma(const char* const* pa, const c
   block_barrier();
 }
 
+// ---------------------------------------------------------------------------
+// bf16 main loop for an A operand carried as (hi, lo) bf16 pairs, x = hi +
+// lo to about 16 significant bits.  An A row holds, for every 8 consecutive
+// K features, 16 bytes of hi values followed by 16 bytes of lo values; a B
+// row holds each feature once.  One B fragment then feeds two MFMAs, hi * b
+// and lo * b, into the same accumulator, so B moves half the bytes that a
+// B row with every value duplicated would, and is read from LDS half as
+// often.
+//  - a stage carries SB bytes of every A row (SB/4 features) and SB/2 bytes
+//    of every B row, both through the LDS-DMA ring as in gemm_mainloop_dma;
+//  - a k-step covers 16 features: lane half h reads the A slots 4st + 2h
+//    (hi) and 4st + 2h + 1 (lo) and the B slot 2st + h;
+//  - each k-step runs as two phases, hi then lo, whose A fragments alternate
+//    between two register buffers (the next phase's reads are issued between
+//    this phase's MFMAs); B fragments are double-buffered across k-steps.
+//    The hi and lo MFMAs of one accumulator lie kTM*kTN MFMAs apart.
+template <int BM, int BN, int SB, int NS, int WGM = 2, int WGN = 2>
+struct DmaTileHL {
+  static constexpr int SBB = SB / 2;              // B bytes per row per stage
+  static constexpr int kWaves = WGM * WGN;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kSlotsA = SB / 16, kSlotsB = SBB / 16;
+  static constexpr int kRowsPerKBA = 1024 / SB, kRowsPerKBB = 1024 / SBB;
+  static constexpr int kStageA = BM * SB;
+  static constexpr int kStage = BM * SB + BN * SBB;
+  static constexpr int kLds = NS * kStage;
+  static constexpr int kWM = BM / WGM, kWN = BN / WGN, kTM = kWM / 32, kTN = kWN / 32;
+  static constexpr int kSteps = SB / 64;          // 16-feature k-steps per stage
+  static constexpr int kLdA = BM * SB / (1024 * kWaves), kLdB = BN * SBB / (1024 * kWaves);
+  static constexpr int kLd = kLdA + kLdB;
+  static_assert(SB == 128, "A stages of 128 bytes, B of 64 (the swizzles measured conflict-free)");
+  static_assert(NS >= 2, "a stage is requested at least one stage ahead");
+  static_assert(kLdA >= 1 && kLdB >= 1, "each wave feeds part of A and of B");
+  static_assert(BM * SB == kLdA * 1024 * kWaves && BN * SBB == kLdB * 1024 * kWaves,
+                "the DMA instructions of a stage cover every row of A and of B");
+  static_assert(kTM + kTN <= kTM * kTN, "a phase's reads fit between its MFMAs");
+  static_assert(kLd * (NS - 2 > 0 ? NS - 2 : 0) <= 31, "vmcnt window");
+};
+
+template <int BM, int BN, int SB, int NS, int WGM, int WGN, bool BUF>
+__device__ __forceinline__ void gemm_mainloop_dma_hl(const char* const* pa, const char* const* pb,
+                                                     const uint32_t* va, const uint32_t* vb,
+                                                     __amdgpu_buffer_rsrc_t ra,
+                                                     __amdgpu_buffer_rsrc_t rb, int KT, char* lds,
+                                                     f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32]) {
+  using TL = DmaTileHL<BM, BN, SB, NS, WGM, WGN>;
+  constexpr int SBB = TL::SBB;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+#pragma unroll
+  for (int i = 0; i < TL::kTM; ++i)
+#pragma unroll
+    for (int j = 0; j < TL::kTN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  auto issue = [&](int s) {
+    char* buf = lds + (s % NS) * TL::kStage;
+#pragma unroll
+    for (int i = 0; i < TL::kLdA; ++i) {
+      lds_ptr_t dst = (lds_ptr_t)(buf + (wave * TL::kLdA + i) * 1024);
+      if constexpr (BUF)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, va[i], s * SB, 0, 0);
+      else
+        __builtin_amdgcn_global_load_lds(pa[i] + size_t(s) * SB, dst, 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < TL::kLdB; ++i) {
+      lds_ptr_t dst = (lds_ptr_t)(buf + TL::kStageA + (wave * TL::kLdB + i) * 1024);
+      if constexpr (BUF)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, vb[i], s * SBB, 0, 0);
+      else
+        __builtin_amdgcn_global_load_lds(pb[i] + size_t(s) * SBB, dst, 16, 0, 0);
+    }
+  };
+  int offA[TL::kTM], swA[TL::kTM], offB[TL::kTN], swB[TL::kTN];
+#pragma unroll
+  for (int i = 0; i < TL::kTM; ++i) {
+    const int r = wm * TL::kWM + i * 32 + (lane & 31);
+    offA[i] = r * SB;
+    swA[i] = swz<SB>(r);
+  }
+#pragma unroll
+  for (int j = 0; j < TL::kTN; ++j) {
+    const int r = wn * TL::kWN + j * 32 + (lane & 31);
+    offB[j] = TL::kStageA + r * SBB;
+    swB[j] = swz<SBB>(r);
+  }
+  const int hi = lane >> 5;
+  bf16x8 fa[2][TL::kTM], fb[2][TL::kTN];
+  // A fragments of k-step st, hi (part 0) or lo (part 1) values, into fa[part]
+  auto load_a = [&](int stage, int st, int part) {
+    const char* buf = lds + (stage % NS) * TL::kStage;
+    const int kc = 4 * st + 2 * hi + part;
+#pragma unroll
+    for (int i = 0; i < TL::kTM; ++i)
+      fa[part][i] = *reinterpret_cast<const bf16x8*>(buf + offA[i] + ((kc ^ swA[i]) << 4));
+  };
+  auto load_b = [&](int stage, int st, int p) {
+    const char* buf = lds + (stage % NS) * TL::kStage;
+    const int kc = 2 * st + hi;
+#pragma unroll
+    for (int j = 0; j < TL::kTN; ++j)
+      fb[p][j] = *reinterpret_cast<const bf16x8*>(buf + offB[j] + ((kc ^ swB[j]) << 4));
+  };
+  constexpr int kMfma = TL::kTM * TL::kTN;
+  auto mfmas = [&](int part, int p) {
+#pragma unroll
+    for (int i = 0; i < TL::kTM; ++i)
+#pragma unroll
+      for (int j = 0; j < TL::kTN; ++j)
+        acc[i][j] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[part][i], fb[p][j], acc[i][j], 0, 0, 0);
+  };
+  // one MFMA, one LDS read, ... then the phase's remaining MFMAs
+  auto order = [](auto reads_c) {
+    constexpr int kReads = decltype(reads_c)::value;
+#pragma unroll
+    for (int x = 0; x < kReads; ++x) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    if constexpr (kMfma > kReads) __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kReads, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  using kReadsHi = std::integral_constant<int, TL::kTM>;
+  using kReadsLo = std::integral_constant<int, TL::kTM + TL::kTN>;
+  using kReadsNone = std::integral_constant<int, 0>;
+
+  // One stage, as in gemm_mainloop_dma: ISSUE requests the stage NS-1
+  // ahead first; NEXT (a later stage exists) makes the last phase wait for
+  // it, sync and read its first fragments before its own MFMAs.
+  auto stage = [&](int kt, auto issue_c, auto next_c, int younger) {
+    constexpr bool kIssue = decltype(issue_c)::value, kNext = decltype(next_c)::value;
+    if constexpr (kIssue) issue(kt + NS - 1);
+#pragma unroll
+    for (int st = 0; st < TL::kSteps; ++st) {
+      const int p = st & 1;
+      // hi phase: the lo fragments of this k-step are read meanwhile
+      load_a(kt, st, 1);
+      mfmas(0, p);
+      order(kReadsHi{});
+      // lo phase: the next k-step's hi and B fragments are read meanwhile
+      if (st + 1 < TL::kSteps) {
+        load_a(kt, st + 1, 0);
+        load_b(kt, st + 1, p ^ 1);
+        mfmas(1, p);
+        order(kReadsLo{});
+      } else if constexpr (kNext) {
+        wait_vm_lgkm(TL::kLd * younger);
+        block_barrier();
+        load_a(kt + 1, 0, 0);
+        load_b(kt + 1, 0, p ^ 1);
+        mfmas(1, p);
+        order(kReadsLo{});
+      } else {
+        mfmas(1, p);
+        order(kReadsNone{});
+      }
+    }
+  };
+  static_assert(TL::kSteps % 2 == 0 || TL::kSteps == 1, "B buffers alternate across stages");
+  using yes = std::true_type;
+  using no = std::false_type;
+
+  const int pre = NS - 1 < KT ? NS - 1 : KT;
+  for (int s = 0; s < pre; ++s) issue(s);
+  wait_vm_lgkm(TL::kLd * (pre - 1));
+  block_barrier();
+  load_a(0, 0, 0);
+  load_b(0, 0, 0);
+  int kt = 0;
+  for (; kt + NS - 1 < KT; ++kt) stage(kt, yes{}, yes{}, NS - 2);
+  for (; kt + 1 < KT; ++kt) stage(kt, no{}, yes{}, KT - 2 - kt);
+  if (kt < KT) stage(kt, no{}, no{}, 0);
+  __builtin_amdgcn_s_waitcnt((0xF | (3 << 14)) | (0x7 << 4));
+  block_barrier();
+}
+
+// One workgroup tile of C = A * B^T with A as (hi, lo) pairs (layout above):
+// rowA(r) / rowB(r) return the first byte of tile-local row r (clamped to a
+// valid row, non-decreasing in r for the buffer form); kfeat is the number
+// of K features (A rows carry 4 bytes per feature, B rows 2).
+template <int BM, int BN, int SB, int NS, int WGM = 2, int WGN = 2, bool BUF = true,
+          class RowA, class RowB>
+__device__ __forceinline__ void tile_product_hl(const RowA& rowA, const RowB& rowB, int kfeat,
+                                                char* lds,
+                                                f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32]) {
+  using TL = DmaTileHL<BM, BN, SB, NS, WGM, WGN>;
+  const char* pa[TL::kLdA];
+  const char* pb[TL::kLdB];
+  uint32_t va[TL::kLdA], vb[TL::kLdB];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < TL::kLdA; ++i) {
+    const int r = (wave * TL::kLdA + i) * TL::kRowsPerKBA + lane / TL::kSlotsA;
+    pa[i] = rowA(r) + (((lane % TL::kSlotsA) ^ swz<SB>(r)) << 4);
+  }
+#pragma unroll
+  for (int i = 0; i < TL::kLdB; ++i) {
+    const int r = (wave * TL::kLdB + i) * TL::kRowsPerKBB + lane / TL::kSlotsB;
+    pb[i] = rowB(r) + (((lane % TL::kSlotsB) ^ swz<TL::SBB>(r)) << 4);
+  }
+  __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(nullptr, 0, 0, 0x00020000);
+  __amdgpu_buffer_rsrc_t rb = ra;
+  if constexpr (BUF) {
+    auto uniform = [](const char* p) {
+      const uint64_t u = reinterpret_cast<uint64_t>(p);
+      const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(u));
+      const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(u >> 32));
+      return reinterpret_cast<const char*>((uint64_t(hi) << 32) | lo);
+    };
+    const char* a0 = uniform(rowA(0));
+    const char* b0 = uniform(rowB(0));
+    const int na = __builtin_amdgcn_readfirstlane(int(rowA(BM - 1) - a0) + 4 * kfeat);
+    const int nb = __builtin_amdgcn_readfirstlane(int(rowB(BN - 1) - b0) + 2 * kfeat);
+#pragma unroll
+    for (int i = 0; i < TL::kLdA; ++i) va[i] = uint32_t(pa[i] - a0);
+#pragma unroll
+    for (int i = 0; i < TL::kLdB; ++i) vb[i] = uint32_t(pb[i] - b0);
+    ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(a0), 0, na, 0x00020000);
+    rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(b0), 0, nb, 0x00020000);
+  }
+  gemm_mainloop_dma_hl<BM, BN, SB, NS, WGM, WGN, BUF>(pa, pb, va, vb, ra, rb, 4 * kfeat / SB, lds,
+                                                      acc);
+}
+
 // Write the accumulators of the waves whose wave-row is `part` (or of every
 // wave when part < 0) to LDS as a row-major fp32 tile with row stride `ld`
 // floats; tile row 0 is the first row of that wave-row (or of the

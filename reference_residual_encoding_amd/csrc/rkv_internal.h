@@ -33,7 +33,8 @@ struct Shape {
   int dist_tiling;  // the distance launch's tiling: 0 wide, 1 narrow, 2 narrow on 128-reference chunks
   int dist_bm;     // references per chunk of that tiling
   int n_chunks;    // reference chunks (one partial top-k list each) per sequence
-  int k3;        // contraction length of the W3 product (2*d_ff bf16 hi/lo, d_ff fp32)
+  int k3;        // K features of the W3 product (d_ff): the packed W3 rows hold k3 values
+  int kdh;       // elements per delta_h row: 2*d_ff bf16 (hi and lo), d_ff fp32
   int n_sink;
   double alpha;
   bool ref_fp8;           // references kept as FP8 E4M3 (compact store [B][nref][C])
@@ -76,7 +77,7 @@ hipError_t launch_dist(const Shape& sh, const void* kv, char* ws, const Workspac
 hipError_t launch_merge(const Shape& sh, int32_t* ref_idx, char* ws, const Workspace& L,
                         hipStream_t st);
 // The contractions read the packed weights at wp ([2 d_ff][C], W1 and W2
-// columns interleaved in blocks of 32) and w3p ([d_c][k3]): in the
+// columns interleaved in blocks of 32) and w3p ([d_c][d_ff]): in the
 // workspace (packed by the set-up) or in a caller's pre-packed buffer.
 hipError_t launch_swiglu(const Shape& sh, const void* kv, char* ws,
                          const Workspace& L, const char* wp, hipStream_t st);

@@ -7,7 +7,7 @@
 // Encode pipeline (one stream, in this order):
 //   pack      W1|W2 -> Wp [2 d_ff][C] (columns of W1 and W2 interleaved in
 //             blocks of 32 so one lane holds x*W1 and x*W2 of the same
-//             column), W3 -> W3p [d_c][k3] (K-contiguous rows).
+//             column), W3 -> W3p [d_c][d_ff] (K-contiguous rows).
 //   norms     reference rows copied into a compact block, and ||kv_j||^2.
 //   dist      distance contraction token x reference on the matrix cores,
 //             fused with a running top-KL per token and reference chunk
@@ -24,10 +24,11 @@
 //             delta_h = Swish(u1)*u2 - Swish(mean u1)*mean u2.
 //   w3        z = delta_h W3: since W3 is linear, f_c(kv) - f_c(m) equals
 //             (h(kv) - h(m)) W3 ([RKV] §2.3).  bf16 runs feed delta_h as a
-//             hi + lo pair of bf16 per feature (K = 2 d_ff, the pair at K
-//             positions 2f, 2f + 1, W3 rows duplicated to match) so the
-//             product keeps ~16 mantissa bits of delta_h.  The epilogue runs the per-token
-//             group min-max quantiser ([RKV] §2.4) and writes the record.
+//             hi + lo pair of bf16 per feature (every 8 features: 16 bytes
+//             of hi, then 16 of lo), each W3 fragment multiplying both, so
+//             the product keeps ~16 mantissa bits of delta_h.  The epilogue
+//             runs the per-token group min-max quantiser ([RKV] §2.4) and
+//             writes the record.
 //   (the merge writes the all-zero records of reference tokens)
 // The read side is one kernel: gather-dequantise over an index list.
 #include "rkv_device.h"
@@ -59,10 +60,11 @@ template <> struct SwCfg<float> {
   static constexpr int BM = 256, BN = 128, SB = 128, NS = 2, WGM = 2, WGN = 2;
   static constexpr int kThreads = 64 * WGM * WGN;
 };
-// the W3 product streams delta_h from beyond L2: a deeper ring of shorter
-// stages (4 x 64 bytes; measured about 2-4% faster than 2 x 128 bytes)
+// the W3 product streams delta_h from beyond L2 as (hi, lo) pairs against
+// W3 rows that hold each value once (gemm_mainloop_dma_hl): three stages of
+// 128 bytes of delta_h and 64 bytes of W3 per row
 template <typename E> struct W3Cfg {
-  static constexpr int BM = 256, BN = 256, SB = 64, NS = 4, WGM = 2, WGN = 4, kMinWaves = 1;
+  static constexpr int BM = 256, BN = 256, SB = 128, NS = 3, WGM = 2, WGN = 4, kMinWaves = 1;
   static constexpr int kThreads = 64 * WGM * WGN;
 };
 template <> struct W3Cfg<float> {
@@ -73,7 +75,7 @@ template <> struct W3Cfg<float> {
 // 128 x 128 on 4 waves, the same ring, two workgroups per CU (g <= 64
 // divides 128, so groups stay whole)
 struct W3CfgNarrow {
-  static constexpr int BM = 128, BN = 128, SB = 64, NS = 4, WGM = 2, WGN = 2, kMinWaves = 2;
+  static constexpr int BM = 128, BN = 128, SB = 128, NS = 3, WGM = 2, WGN = 2, kMinWaves = 2;
   static constexpr int kThreads = 64 * WGM * WGN;
 };
                                                                  // difference, 2 WGs per CU
@@ -706,6 +708,11 @@ __global__ __launch_bounds__(64) void k_topk_merge(const float2* __restrict__ pa
 }
 
 // ------------------------------------------------------------------ Swish
+// the value lane l ^ 1 holds (DPP quad permutation 1, 0, 3, 2)
+__device__ __forceinline__ uint32_t lane_xor1(uint32_t x) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0xB1, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ float silu_fast(float x) {
   // x * sigmoid(x) with the hardware exp2 and reciprocal (about 1e-7
   // relative, far inside the latent tolerance)
@@ -719,8 +726,10 @@ __device__ __forceinline__ float silu_fast(float x) {
 // where P = R [W1|W2] holds the projected references and j runs over the
 // token's k_t chosen references: m_t [W1|W2] = mean_j kv_j [W1|W2] because
 // the first layer of f_c is linear and bias-free ([RKV] §2.2 mean eq.,
-// §2.3).  delta_h goes to the token's 4-byte slot of f (dh float index
-// Q*d_ff + f): a (hi, lo) bf16 pair for bf16 runs, fp32 otherwise.
+// §2.3).  delta_h goes to row Q of dh, 4 bytes per feature: for bf16 runs
+// a (hi, lo) bf16 pair, each granule of 8 features as 16 bytes of hi values
+// then 16 bytes of lo values (the A layout of gemm_mainloop_dma_hl); fp32
+// otherwise, feature f at float index Q*d_ff + f.
 template <typename E, int KL, bool BUF>
 __global__ __launch_bounds__(SwCfg<E>::kThreads) void k_swiglu(const char* __restrict__ kv,
                                                 const char* __restrict__ wp,
@@ -876,10 +885,25 @@ __global__ __launch_bounds__(SwCfg<E>::kThreads) void k_swiglu(const char* __res
         const float dl = hk[e] - silu_fast(s1[e] * inv) * (s2[e] * inv);
         w[e] = sizeof(E) == 2 ? bf16_hi_lo(dl) : __float_as_uint(dl);
       }
-      const u32x4 wv = {w[0], w[1], w[2], w[3]};
       // a quad past the column edge, or a row past M, lands outside the range
-      const uint32_t so = colv ? uint32_t(rt * d_ff + f) * 4u : kNone;
-      __builtin_amdgcn_raw_buffer_store_b128(wv, drs, int(so), 0, 0);
+      if constexpr (sizeof(E) == 2) {
+        // The row's 8-feature granule holds 16 bytes of hi values, then 16
+        // of lo values.  Lanes c (even) and c + 1 hold its two quads: they
+        // swap halves (DPP, lanes l and l ^ 1), the even lane then stores
+        // the granule's hi values and the odd lane its lo values.
+        const uint32_t hi01 = (w[0] & 0xFFFFu) | (w[1] << 16), hi23 = (w[2] & 0xFFFFu) | (w[3] << 16);
+        const uint32_t lo01 = (w[0] >> 16) | (w[1] & 0xFFFF0000u), lo23 = (w[2] >> 16) | (w[3] & 0xFFFF0000u);
+        const bool odd = c & 1;
+        const uint32_t r0 = lane_xor1(odd ? hi01 : lo01), r1 = lane_xor1(odd ? hi23 : lo23);
+        const u32x4 wv = odd ? u32x4{r0, r1, lo01, lo23} : u32x4{hi01, hi23, r0, r1};
+        const uint32_t so =
+            colv ? uint32_t(rt * d_ff + (f & ~7)) * 4u + (odd ? 16u : 0u) : kNone;
+        __builtin_amdgcn_raw_buffer_store_b128(wv, drs, int(so), 0, 0);
+      } else {
+        const u32x4 wv = {w[0], w[1], w[2], w[3]};
+        const uint32_t so = colv ? uint32_t(rt * d_ff + f) * 4u : kNone;
+        __builtin_amdgcn_raw_buffer_store_b128(wv, drs, int(so), 0, 0);
+      }
     }
   };
 #pragma unroll
@@ -910,23 +934,30 @@ __global__ __launch_bounds__(CF::kThreads, CF::kMinWaves) void k_w3_quant(const 
                 "whole groups (g <= 64) per tile row; every thread takes the same units");
   constexpr int LD = kEpiLd(BN);
   constexpr int HALF = BM / 2;
-  constexpr int kMain = mainloop_lds<E, BM, BN, CF::SB, CF::NS, WGM, WGN>();
+  constexpr bool kHL = sizeof(E) == 2;                   // bf16: delta_h as (hi, lo) pairs
+  constexpr int kMain = kHL ? DmaTileHL<BM, BN, CF::SB, CF::NS, WGM, WGN>::kLds
+                            : mainloop_lds<E, BM, BN, CF::SB, CF::NS, WGM, WGN>();
   constexpr int kLdsBytes = kMain > HALF * LD * 4 ? kMain : HALF * LD * 4;
   __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes + BM * 4];
   int* rec_lds = reinterpret_cast<int*>(lds + kLdsBytes);  // [BM] record row b*T + t, -1 past M
   const int mt = blockIdx.x % tiles_m, nt = blockIdx.x / tiles_m;
   const int m0 = mt * BM, n0 = nt * BN;
-  const size_t rowb = size_t(K) * sizeof(E);
+  // K features: a delta_h row carries 4 bytes each (bf16 hi and lo, or
+  // fp32), a packed W3 row one element each
+  const size_t rowa = size_t(K) * 4, rowb = size_t(K) * sizeof(E);
   const int tid = threadIdx.x;
   // record row of every token of the tile: loaded before the main loop,
   // written to LDS after it (the epilogue's first barrier publishes it)
   static_assert(BM <= NT, "one token per thread");
   int rec_r = -1;
   if (tid < BM && m0 + tid < M) rec_r = ((m0 + tid) / nr) * T + nrp[(m0 + tid) % nr];
-  auto rowA = [&](int r) { return dh + size_t(min(m0 + r, M - 1)) * rowb; };
+  auto rowA = [&](int r) { return dh + size_t(min(m0 + r, M - 1)) * rowa; };
   auto rowB = [&](int r) { return w3p + size_t(min(n0 + r, N - 1)) * rowb; };
   f32x16 acc[BM / WGM / 32][BN / WGN / 32];
-  tile_product<E, BM, BN, CF::SB, CF::NS, WGM, WGN>(rowA, rowB, int(rowb), lds, acc);
+  if constexpr (kHL)
+    tile_product_hl<BM, BN, CF::SB, CF::NS, WGM, WGN>(rowA, rowB, K, lds, acc);
+  else
+    tile_product<E, BM, BN, CF::SB, CF::NS, WGM, WGN>(rowA, rowB, int(rowb), lds, acc);
   if (tid < BM) rec_lds[tid] = rec_r;
   float* zt = reinterpret_cast<float*>(lds);
   // 8 latent values per lane; G8 consecutive lanes hold one group (groups
@@ -1438,7 +1469,8 @@ Shape make_shape(int B, int T, int N, int D, int d_ff, int d_c, int k, int g, in
              : sh.dist_tiling == 2 ? DistCfgShort::BM
              : sh.dist_tiling == 1 ? DistCfgNarrow::BM : DistCfg<uint16_t>::BM;
   sh.n_chunks = cdiv(sh.nref, sh.dist_bm);
-  sh.k3 = bf16 ? 2 * d_ff : d_ff;
+  sh.k3 = d_ff;
+  sh.kdh = bf16 ? 2 * d_ff : d_ff;
   return sh;
 }
 
@@ -1452,7 +1484,7 @@ Workspace plan_workspace(const Shape& sh) {
   L.refs = take(size_t(sh.B) * sh.nref * sh.C * sh.esize);
   L.proj = take(size_t(sh.B) * sh.nref * 2 * sh.d_ff * 4);
   L.part = take(size_t(sh.B) * cdiv(sh.nref, kMinChunk) * sh.nr * sh.kl * 8);
-  L.dh = take(size_t(sh.B) * sh.nr * sh.k3 * sh.esize);
+  L.dh = take(size_t(sh.B) * sh.nr * sh.kdh * sh.esize);
   L.rpos = take(size_t(sh.nref) * 4);
   L.nrp = take(size_t(sh.nr) * 4);
   L.tab = take(size_t(sh.T) * 4);
@@ -1532,7 +1564,7 @@ hipError_t launch_setup(const Shape& sh, const void* w1, const void* w2, const v
     auto tiles = [](int n) { return (n + 63) / 64; };
     J.j[0] = {w1, ws + L.wp, sh.C, sh.d_ff, sh.C, 1, 0, tiles(sh.d_ff), 0};
     J.j[1] = {w2, ws + L.wp, sh.C, sh.d_ff, sh.C, 2, 0, tiles(sh.d_ff), 0};
-    J.j[2] = {w3, ws + L.w3p, sh.d_ff, sh.d_c, sh.k3, 0, sh.bf16 ? 1 : 0, tiles(sh.d_c), 0};
+    J.j[2] = {w3, ws + L.w3p, sh.d_ff, sh.d_c, sh.k3, 0, 0, tiles(sh.d_c), 0};
     for (auto& j : J.j) {
       j.first = n_pack;
       n_pack += tiles(j.rows) * j.tiles_c;
@@ -1582,7 +1614,7 @@ hipError_t launch_pack_weights(const Shape& sh, const void* w1, const void* w2, 
   PackJobs J{};
   J.j[0] = {w1, packed + P.wp, sh.C, sh.d_ff, sh.C, 1, 0, tiles(sh.d_ff), 0};
   J.j[1] = {w2, packed + P.wp, sh.C, sh.d_ff, sh.C, 2, 0, tiles(sh.d_ff), 0};
-  J.j[2] = {w3, packed + P.w3p, sh.d_ff, sh.d_c, sh.k3, 0, sh.bf16 ? 1 : 0, tiles(sh.d_c), 0};
+  J.j[2] = {w3, packed + P.w3p, sh.d_ff, sh.d_c, sh.k3, 0, 0, tiles(sh.d_c), 0};
   int n_pack = 0;
   for (auto& j : J.j) {
     j.first = n_pack;

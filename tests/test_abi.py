@@ -333,8 +333,8 @@ def test_packed_weights_calls_check_sizes_on_the_host():
     workspace) smaller than their layout before anything is enqueued."""
     p = _p(LLAMA32K)
     need = R.rkv_packed_weights_bytes(p)
-    # W1|W2 interleaved (2 d_ff x C) plus W3 with each value twice (d_c x 2 d_ff), bf16
-    assert need == 2 * 1024 * 2048 * 2 + 512 * 2048 * 2
+    # W1|W2 interleaved (2 d_ff x C) plus W3 as K-contiguous rows (d_c x d_ff), bf16
+    assert need == 2 * 1024 * 2048 * 2 + 512 * 1024 * 2
     assert R.rkv_packed_weights_bytes(_p(LLAMA32K, b=5)) == 0
     st = R.rkv_pack_weights(p, FAKE, FAKE, FAKE, FAKE, need - 1, None, check=False)
     assert st == R.RKV_ERR_WORKSPACE and str(need) in R.rkv_last_error()
