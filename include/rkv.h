@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define RKV_ABI_VERSION 6
+#define RKV_ABI_VERSION 7
 
 typedef enum {
   RKV_OK = 0,

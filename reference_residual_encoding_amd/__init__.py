@@ -56,7 +56,7 @@ EXPORTS = (
 
 STAGES = ("pack", "norms", "dist", "merge", "proj", "swiglu", "w3", "quant", "gather", "restore",
           "append", "store")
-RKV_ABI_VERSION = 6
+RKV_ABI_VERSION = 7
 RKV_REF_INPUT = 0
 RKV_REF_FP8 = 1
 

@@ -102,7 +102,7 @@ hipError_t launch_gather(const uint8_t* codes, const uint16_t* scale, const uint
 
 // Restore ([RKV] §2.5): workspace of the decoder product for n_idx rows.
 struct RestoreWorkspace {
-  int kr;               // contraction length (2*d_c bf16 hi/lo pairs, d_c fp32)
+  int kr;               // K latents of the decoder product (d_c)
   bool tables;          // schedule tables present (FP8 store of a dynamic schedule)
   size_t wdp, zt,
       rinfo,            // [n_idx][kl + 4] per selected row: its kl stored reference rows
@@ -110,7 +110,7 @@ struct RestoreWorkspace {
       rpos, nrp, tab, total;
 };
 RestoreWorkspace plan_restore(const Shape& sh, int64_t n_idx);
-// The decoder weight packed for the restore's matrix cores ([C][kr] rows):
+// The decoder weight packed for the restore's matrix cores ([C][d_c] rows):
 // its bytes, and the launch that writes it from wd [d_c][C].
 size_t packed_decoder_bytes(const Shape& sh);
 hipError_t launch_pack_decoder(const Shape& sh, const void* wd, char* wdp, hipStream_t st);

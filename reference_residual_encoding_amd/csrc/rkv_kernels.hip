@@ -126,14 +126,12 @@ constexpr int kEpiLd(int bn) { return bn + 8; }  // padded fp32 row of an LDS-st
 // ------------------------------------------------------------------ packing
 // dst[map(c) * ld + r] = src[r * cols + c] for the weight matrices, one
 // launch for all three.  map: 0 identity, 1 W1 slot 64*(c/32) + c%32, 2 W2
-// slot 64*(c/32) + 32 + c%32.  With pair set, each value is written twice,
-// at dst[map(c) * ld + 2r] and [.. + 2r + 1]: the K order of a delta_h row
-// stored as (hi, lo) bf16 pairs.  A workgroup moves one 64 x 64 tile with
+// slot 64*(c/32) + 32 + c%32.  A workgroup moves one 64 x 64 tile with
 // 16-byte loads and stores (rows and columns are multiples of 32).
 struct PackJob {
   const void* src;
   void* dst;
-  int rows, cols, ld, mode, pair, tiles_c, first;
+  int rows, cols, ld, mode, tiles_c, first;
 };
 struct PackJobs { PackJob j[3]; };
 
@@ -165,16 +163,7 @@ __device__ __forceinline__ void pack_tile(const PackJobs& jobs, int w, E (*tile)
     E v[V];
 #pragma unroll
     for (int e = 0; e < V; ++e) v[e] = tile[rv + e][c];
-    if (J.pair) {
-      E d[2 * V];
-#pragma unroll
-      for (int e = 0; e < V; ++e) { d[2 * e] = v[e]; d[2 * e + 1] = v[e]; }
-      u32x4* o = reinterpret_cast<u32x4*>(dst + size_t(n) * J.ld + 2 * rg);
-      o[0] = *reinterpret_cast<const u32x4*>(&d[0]);
-      o[1] = *reinterpret_cast<const u32x4*>(&d[V]);
-    } else {
-      *reinterpret_cast<u32x4*>(dst + size_t(n) * J.ld + rg) = *reinterpret_cast<const u32x4*>(&v[0]);
-    }
+    *reinterpret_cast<u32x4*>(dst + size_t(n) * J.ld + rg) = *reinterpret_cast<const u32x4*>(&v[0]);
   }
 }
 
@@ -1027,8 +1016,10 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ z, i
 // note).  Two kernels: the selected records are dequantised into the A
 // operand of the decoder product, then the product's epilogue adds the
 // reference mean and applies the rotation.
+// bf16 runs: z~ as (hi, lo) pairs against W_d rows holding each value once
+// (gemm_mainloop_dma_hl), three stages of 128 bytes of z~ and 64 of W_d
 template <typename E> struct RsCfg {
-  static constexpr int BM = 256, BN = 256, SB = 128, NS = 2, WGM = 2, WGN = 4, kMinWaves = 1;
+  static constexpr int BM = 256, BN = 256, SB = 128, NS = 3, WGM = 2, WGN = 4, kMinWaves = 1;
   static constexpr int kThreads = 64 * WGM * WGN;
 };
 template <> struct RsCfg<float> {
@@ -1039,20 +1030,20 @@ template <> struct RsCfg<float> {
 // 128 x 256, half the work of a 256 x 256 tile (measured better than 8-wave
 // 128 x 128 tiles, whose rounds took about 0.9 of a wide round)
 struct RsCfgTail {
-  static constexpr int BM = 128, BN = 256, SB = 128, NS = 2, WGM = 2, WGN = 4, kMinWaves = 1;
+  static constexpr int BM = 128, BN = 256, SB = 128, NS = 3, WGM = 2, WGN = 4, kMinWaves = 1;
   static constexpr int kThreads = 64 * WGM * WGN;
 };
 // bf16 restore tiles two to a CU, so that one workgroup's epilogue (mean
 // loads, rotation, stores) runs beside the other's main loop: 128 x 128 on
-// 4 waves, a four-stage ring of 64-byte slices (128 columns hold whole heads:
-// D divides 128)
+// 4 waves, three stages (128 columns hold whole heads: D divides 128)
 struct RsCfgNarrow {
-  static constexpr int BM = 128, BN = 128, SB = 64, NS = 4, WGM = 2, WGN = 2, kMinWaves = 2;
+  static constexpr int BM = 128, BN = 128, SB = 128, NS = 3, WGM = 2, WGN = 2, kMinWaves = 2;
   static constexpr int kThreads = 64 * WGM * WGN;
 };
 
 // z~ of each selected token as the decoder product's A row: bf16 runs store
-// a (hi, lo) bf16 pair per latent (K positions 2c, 2c + 1), fp32 runs the
+// a (hi, lo) bf16 pair per latent, each 8 latents as 16 bytes of hi values
+// then 16 of lo values (the A layout of gemm_mainloop_dma_hl), fp32 runs the
 // float; zeros for reference tokens (all -1 ref_idx rows) and indices
 // outside [0, B*T).  z~ is
 // fmaf(q, Delta_h, m_h), as rkv_dequant_gather gives it.
@@ -1127,8 +1118,19 @@ __global__ __launch_bounds__(256) void k_restore_prep(const uint8_t* __restrict_
       w[e] = sizeof(E) == 2 ? bf16_hi_lo(v) : __float_as_uint(v);
     }
     u32x4* dst = reinterpret_cast<u32x4*>(zt + i * d_c + o);
-    dst[0] = u32x4{w[0], w[1], w[2], w[3]};
-    dst[1] = u32x4{w[4], w[5], w[6], w[7]};
+    if constexpr (sizeof(E) == 2) {
+      uint32_t hv[4], lv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hv[e] = (w[2 * e] & 0xFFFFu) | (w[2 * e + 1] << 16);
+        lv[e] = (w[2 * e] >> 16) | (w[2 * e + 1] & 0xFFFF0000u);
+      }
+      dst[0] = u32x4{hv[0], hv[1], hv[2], hv[3]};
+      dst[1] = u32x4{lv[0], lv[1], lv[2], lv[3]};
+    } else {
+      dst[0] = u32x4{w[0], w[1], w[2], w[3]};
+      dst[1] = u32x4{w[4], w[5], w[6], w[7]};
+    }
   }
 }
 
@@ -1142,10 +1144,18 @@ struct RateTable {
   double r[64];
 };
 
+template <typename E, typename CF>
+constexpr int restore_main_lds() {
+  if constexpr (sizeof(E) == 2)
+    return DmaTileHL<CF::BM, CF::BN, CF::SB, CF::NS, CF::WGM, CF::WGN>::kLds;
+  else
+    return mainloop_lds<E, CF::BM, CF::BN, CF::SB, CF::NS, CF::WGM, CF::WGN>();
+}
+
 template <typename E, typename CF, int KL>
 constexpr int restore_lds() {
   constexpr int LD = kEpiLd(CF::BN), HALF = CF::BM / 2;
-  constexpr int kMain = mainloop_lds<E, CF::BM, CF::BN, CF::SB, CF::NS, CF::WGM, CF::WGN>();
+  constexpr int kMain = restore_main_lds<E, CF>();
   constexpr int kStaged = kMain > HALF * LD * 4 ? kMain : HALF * LD * 4;
   return kStaged + CF::BM * (KL + 2) * 4 + 64 * 8;
 }
@@ -1201,7 +1211,7 @@ __device__ __forceinline__ void restore_tile(
   static_assert(WGM == 2, "the epilogue stages one wave-row (half the tile) at a time");
   constexpr int LD = kEpiLd(BN);
   constexpr int HALF = BM / 2;
-  constexpr int kMain = mainloop_lds<E, BM, BN, CF::SB, CF::NS, WGM, WGN>();
+  constexpr int kMain = restore_main_lds<E, CF>();
   constexpr int kStaged = kMain > HALF * LD * 4 ? kMain : HALF * LD * 4;
   int* rows_lds = reinterpret_cast<int*>(lds + kStaged);            // [BM][KL] kv rows, -1 none
   float* inv_lds = reinterpret_cast<float*>(lds + kStaged + BM * KL * 4);  // [BM] 1 / count
@@ -1222,11 +1232,16 @@ __device__ __forceinline__ void restore_tile(
   }
   if (theta > 0.0f)
     for (int i = tid; i < D / 2; i += NT) rate[i] = rt.r[i];
-  const size_t rowa = size_t(K) * sizeof(E);
+  // K latents: a z~ row carries 4 bytes each (bf16 hi and lo, or fp32), a
+  // packed W_d row one element each
+  const size_t rowa = size_t(K) * 4, rowb = size_t(K) * sizeof(E);
   auto rowA = [&](int r) { return zt + size_t(min(m0 + r, n_idx - 1)) * rowa; };
-  auto rowB = [&](int r) { return wdp + size_t(min(n0 + r, C - 1)) * rowa; };
+  auto rowB = [&](int r) { return wdp + size_t(min(n0 + r, C - 1)) * rowb; };
   f32x16 acc[BM / WGM / 32][BN / WGN / 32];
-  tile_product<E, BM, BN, CF::SB, CF::NS, WGM, WGN>(rowA, rowB, int(rowa), lds, acc);
+  if constexpr (sizeof(E) == 2)
+    tile_product_hl<BM, BN, CF::SB, CF::NS, WGM, WGN>(rowA, rowB, K, lds, acc);
+  else
+    tile_product<E, BM, BN, CF::SB, CF::NS, WGM, WGN>(rowA, rowB, int(rowb), lds, acc);
   if (tid < BM) {
     const int* v = reinterpret_cast<const int*>(ri);
 #pragma unroll
@@ -1562,9 +1577,9 @@ hipError_t launch_setup(const Shape& sh, const void* w1, const void* w2, const v
   int n_pack = 0;
   if (w1) {
     auto tiles = [](int n) { return (n + 63) / 64; };
-    J.j[0] = {w1, ws + L.wp, sh.C, sh.d_ff, sh.C, 1, 0, tiles(sh.d_ff), 0};
-    J.j[1] = {w2, ws + L.wp, sh.C, sh.d_ff, sh.C, 2, 0, tiles(sh.d_ff), 0};
-    J.j[2] = {w3, ws + L.w3p, sh.d_ff, sh.d_c, sh.k3, 0, 0, tiles(sh.d_c), 0};
+    J.j[0] = {w1, ws + L.wp, sh.C, sh.d_ff, sh.C, 1, tiles(sh.d_ff), 0};
+    J.j[1] = {w2, ws + L.wp, sh.C, sh.d_ff, sh.C, 2, tiles(sh.d_ff), 0};
+    J.j[2] = {w3, ws + L.w3p, sh.d_ff, sh.d_c, sh.k3, 0, tiles(sh.d_c), 0};
     for (auto& j : J.j) {
       j.first = n_pack;
       n_pack += tiles(j.rows) * j.tiles_c;
@@ -1612,9 +1627,9 @@ hipError_t launch_pack_weights(const Shape& sh, const void* w1, const void* w2, 
   const PackedLayout P = plan_packed(sh);
   auto tiles = [](int n) { return (n + 63) / 64; };
   PackJobs J{};
-  J.j[0] = {w1, packed + P.wp, sh.C, sh.d_ff, sh.C, 1, 0, tiles(sh.d_ff), 0};
-  J.j[1] = {w2, packed + P.wp, sh.C, sh.d_ff, sh.C, 2, 0, tiles(sh.d_ff), 0};
-  J.j[2] = {w3, packed + P.w3p, sh.d_ff, sh.d_c, sh.k3, 0, 0, tiles(sh.d_c), 0};
+  J.j[0] = {w1, packed + P.wp, sh.C, sh.d_ff, sh.C, 1, tiles(sh.d_ff), 0};
+  J.j[1] = {w2, packed + P.wp, sh.C, sh.d_ff, sh.C, 2, tiles(sh.d_ff), 0};
+  J.j[2] = {w3, packed + P.w3p, sh.d_ff, sh.d_c, sh.k3, 0, tiles(sh.d_c), 0};
   int n_pack = 0;
   for (auto& j : J.j) {
     j.first = n_pack;
@@ -1840,7 +1855,7 @@ RestoreWorkspace plan_restore(const Shape& sh, int64_t n_idx) {
   RestoreWorkspace L{};
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t at = off; off += align256(bytes); return at; };
-  L.kr = sh.bf16 ? 2 * sh.d_c : sh.d_c;
+  L.kr = sh.d_c;
   L.wdp = take(size_t(sh.C) * L.kr * sh.esize);
   L.zt = take(size_t(n_idx) * sh.d_c * 4);
   L.rinfo = take(size_t(n_idx) * (sh.kl + 4) * 4);
@@ -1901,15 +1916,13 @@ static int restore_wide_rows(const Shape& sh, int n_idx) {
 }
 
 size_t packed_decoder_bytes(const Shape& sh) {
-  const int kr = sh.bf16 ? 2 * sh.d_c : sh.d_c;
-  return size_t(sh.C) * kr * sh.esize;
+  return size_t(sh.C) * sh.d_c * sh.esize;
 }
 
 hipError_t launch_pack_decoder(const Shape& sh, const void* wd, char* wdp, hipStream_t st) {
-  // W_d [d_c][C] -> [C][K] rows (bf16: each value twice, matching the pairs)
-  const int kr = sh.bf16 ? 2 * sh.d_c : sh.d_c;
+  // W_d [d_c][C] -> [C][d_c] K-contiguous rows
   PackJobs J{};
-  J.j[0] = {wd, wdp, sh.d_c, sh.C, kr, 0, sh.bf16 ? 1 : 0, (sh.C + 63) / 64, 0};
+  J.j[0] = {wd, wdp, sh.d_c, sh.C, sh.d_c, 0, (sh.C + 63) / 64, 0};
   const int tiles = (sh.d_c + 63) / 64 * J.j[0].tiles_c;
   J.j[1].first = tiles;
   J.j[2].first = tiles;
