@@ -256,7 +256,9 @@ __global__ __launch_bounds__(256) void k_sched_tables(const int* __restrict__ rp
 // ------------------------------------------------------------------ references
 // Copy the reference rows (positions j*s of each sequence) into a compact
 // [B*nref][C] block, which the distance and projection contractions stream
-// (the references sit a whole stride apart in kv), and compute ||kv_j||^2.
+// (the references sit a whole stride apart in kv), and compute ||kv_j||^2;
+// the row after the block is written all zero (the distance tiles read it
+// for rows no token of a tile may use).
 // A reference token is stored as it is ([RKV] §2.4): its ref_idx row is all
 // -1 and, when a record is given, its record (codes, scale, zmin, z) is all
 // zero; one wave writes each with coalesced stores.
@@ -285,7 +287,14 @@ __device__ __forceinline__ void ref_rows(const RefArgs& a, int blk) {
   const int fp8 = a.fp8;
   const int wid = blk * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (wid >= a.B * nref) return;
+  if (wid >= a.B * nref) {
+    if (wid == a.B * nref) {                             // the zero row after the block
+      char* zr = refs + size_t(wid) * C * sizeof(E);
+      for (size_t o = size_t(lane) * 16; o < size_t(C) * sizeof(E); o += 64 * 16)
+        *reinterpret_cast<uint4*>(zr + o) = make_uint4(0u, 0u, 0u, 0u);
+    }
+    return;
+  }
   const int b = wid / nref, j = wid % nref;
   const size_t rec = size_t(b) * T + size_t(ref_position(a.sv, j));   // the reference token's row
   for (int i = lane; i < k; i += 64) ref_idx[rec * k + i] = -1;
@@ -453,7 +462,7 @@ __global__ __launch_bounds__(CF::kThreads, CF::kMinWaves) void k_dist_topk(
     const char* __restrict__ kv, const char* __restrict__ refs, const float* __restrict__ ysq,
     float2* __restrict__ part, int B, int T, int C, const int* __restrict__ nrp, int nref,
     int nr, int n_lists, int n_tt, int n_dist, const char* __restrict__ wp,
-    float* __restrict__ proj, int proj_n, int proj_tiles_m) {
+    float* __restrict__ proj, int proj_n, int proj_tiles_m, const char* __restrict__ zrow) {
   using PF = typename CF::Proj;
   constexpr int BM = CF::BM, BN = CF::BN, WGM = CF::WGM, WGN = CF::WGN;
   constexpr int kLists = 2 * WGM;                        // partial lists per token
@@ -519,7 +528,17 @@ __global__ __launch_bounds__(CF::kThreads, CF::kMinWaves) void k_dist_topk(
   static_assert(BM <= CF::kThreads, "one norm per thread");
   const float ysq_r = tid < BM ? ysq[size_t(b) * nref + min(m0 + tid, nref - 1)] : 0.0f;
   const char* rbase = refs + size_t(b) * nref * rowb;
-  auto rowA = [&](int r) { return rbase + size_t(min(m0 + r, nref - 1)) * rowb; };
+  // Rows of the chunk that no token of the tile may use (past the last
+  // token's pool, or past the last reference) read the all-zero row after
+  // the reference block (zrow, when given): their dot products are masked
+  // anyway, and the matrix cores draw far less power on zero operands than
+  // on a duplicated reference row.  The row lies past every reference row,
+  // so the addresses stay non-decreasing in r.
+  const int qlast = min(n0 + BN, nr) - 1;
+  const int nvalid = zrow ? min(nrp[qlast] - qlast, nref) - m0 : BM;
+  auto rowA = [&](int r) {
+    return r < nvalid ? rbase + size_t(min(m0 + r, nref - 1)) * rowb : zrow;
+  };
   auto rowB = [&](int r) { return base + size_t(nrp[min(n0 + r, nr - 1)]) * rowb; };
   f32x16 acc[BM / WGM / 32][BN / WGN / 32];
   tile_product<E, BM, BN, CF::SB, CF::NS, WGM, WGN, BUF>(rowA, rowB, int(rowb), lds, acc);
@@ -1496,7 +1515,7 @@ Workspace plan_workspace(const Shape& sh) {
   L.wp = take(size_t(2) * sh.d_ff * sh.C * sh.esize);
   L.w3p = take(size_t(sh.d_c) * sh.k3 * sh.esize);
   L.ysq = take(size_t(sh.B) * sh.nref * 4);
-  L.refs = take(size_t(sh.B) * sh.nref * sh.C * sh.esize);
+  L.refs = take((size_t(sh.B) * sh.nref + 1) * sh.C * sh.esize);   // + the zero row
   L.proj = take(size_t(sh.B) * sh.nref * 2 * sh.d_ff * 4);
   L.part = take(size_t(sh.B) * cdiv(sh.nref, kMinChunk) * sh.nr * sh.kl * 8);
   L.dh = take(size_t(sh.B) * sh.nr * sh.kdh * sh.esize);
@@ -1605,7 +1624,7 @@ hipError_t launch_setup(const Shape& sh, const void* w1, const void* w2, const v
   ra.ng = sh.b == kIdentityBits ? 0 : sh.d_c / sh.g;     // identity mode stores no group numbers
   ra.d_c = sh.d_c;
   ra.fp8 = sh.ref_fp8;
-  const int n_ref = cdiv(long(sh.B) * sh.nref, 4);
+  const int n_ref = cdiv(long(sh.B) * sh.nref + 1, 4);   // + the zero row
   const int grid = n_pack + n_tab + n_ref;
   if (sh.bf16)
     k_setup<uint16_t><<<grid, 256, 0, st>>>(J, n_pack, sa, n_tab, ra);
@@ -1683,6 +1702,15 @@ hipError_t launch_dist(const Shape& sh, const void* kv, char* ws, const Workspac
   const auto* nrp = reinterpret_cast<const int*>(ws + L.nrp);
   auto* proj = reinterpret_cast<float*>(ws + L.proj);
   const int pM = sh.B * sh.nref, pN = 2 * sh.d_ff;
+  // the zero row after the reference block (written by the set-up), while
+  // every reference row and it lie within one buffer resource's reach
+  // (RKV_DIST_ZERO=0 in the environment, read at every launch, repeats a
+  // reference row instead; the bits are the same)
+  const size_t zoff = size_t(sh.B) * sh.nref * sh.C * sh.esize;
+  const char* force_zero = std::getenv("RKV_DIST_ZERO");
+  const bool use_zero = zoff + size_t(sh.C) * sh.esize < (size_t(1) << 31) &&
+                        !(force_zero && !std::strcmp(force_zero, "0"));
+  const char* zrow = use_zero ? ws + L.refs + zoff : nullptr;
   auto go = [&](auto e, auto cf) {
     using E = decltype(e);
     using CF = decltype(cf);
@@ -1695,7 +1723,7 @@ hipError_t launch_dist(const Shape& sh, const void* kv, char* ws, const Workspac
 #define RKV_DIST(KL, BUF)                                                                    \
     k_dist_topk<E, CF, KL, BUF><<<n_dist + n_proj, CF::kThreads, 0, st>>>(                   \
         p, ws + L.refs, y, part, sh.B, sh.T, sh.C, nrp, sh.nref, sh.nr, sh.n_chunks, n_tt,   \
-        n_dist, wp, proj, pN, ptm)
+        n_dist, wp, proj, pN, ptm, zrow)
     if constexpr (sizeof(E) == 2) {
       if (sh.kl == 4) { if (buf) RKV_DIST(4, true); else RKV_DIST(4, false); }
       else { if (buf) RKV_DIST(8, true); else RKV_DIST(8, false); }

@@ -289,14 +289,21 @@ def test_distance_tilings_bit_identical(cfg):
     tilings only group each token's candidates into lists differently, and
     the merge orders them by (d, j), so all outputs (and the reference
     projection that rides in the same launch) are the same bits, for k = 4
-    and k > 4 lists, a growing schedule and several sequences."""
+    and k > 4 lists, a growing schedule and several sequences.  Rows of a
+    chunk that no token of its tile may use read a zero row; with
+    RKV_DIST_ZERO=0 they repeat a reference row instead, and the bits stay
+    the same (those products are masked)."""
     outs = []
-    for tiling in ("wide", "narrow", "short"):
+    for tiling, zero in (("wide", None), ("narrow", None), ("short", None), ("wide", "0"),
+                         ("short", "0")):
         os.environ["RKV_DIST_TILE"] = tiling
+        if zero is not None:
+            os.environ["RKV_DIST_ZERO"] = zero
         try:
             _, _, h, _ = P.run_encode(generate(cfg))
         finally:
             del os.environ["RKV_DIST_TILE"]
+            os.environ.pop("RKV_DIST_ZERO", None)
         outs.append(h)
     for key in ("ref_idx", "codes", "scale", "zmin", "z"):
         for other in outs[1:]:
