@@ -349,6 +349,52 @@ def bench_variants(R, RB, cfg, kv, w1, w2, w3, idx, stream, args):
     return out
 
 
+def bench_vendor_gemm(cfg, refs, dev, reps: int = 20):
+    """hipBLASLt (torch.matmul, bf16 in, fp32 accumulate) on the plain dense
+    product of each contraction shape of the workload: the rate the vendor
+    library reaches on that shape, and the encode's matrix-core time if every
+    contraction ran at that rate with no epilogue, no top-k scan and no
+    launch between them (the algorithmic flops of each stage over the
+    library's rate for its shape; the causal distance work at the rate of the
+    full token x reference product).  A reference point for the kernels, not
+    a path of the library."""
+    import torch
+    nref, nr, pairs = schedule_counts(refs, cfg.T)
+    B, C = cfg.B, cfg.C
+    shapes = {  # stage: (M, N, K, algorithmic flops of the stage)
+        "dist": (B * nr, nref, C, 2.0 * C * pairs * B),
+        "proj": (B * nref, 2 * cfg.d_ff, C, 2.0 * C * 2 * cfg.d_ff * B * nref),
+        "swiglu": (B * nr, 2 * cfg.d_ff, C, 2.0 * C * 2 * cfg.d_ff * B * nr),
+        "w3": (B * nr, cfg.d_c, cfg.d_ff, 2.0 * cfg.d_ff * cfg.d_c * B * nr),
+    }
+    out, total_ms = {}, 0.0
+    for name, (m, n, k, work) in shapes.items():
+        a = torch.randn((m, k), device=dev).to(torch.bfloat16)
+        b = torch.randn((k, n), device=dev).to(torch.bfloat16)
+        for _ in range(5):
+            c = a @ b
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            c = a @ b
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        rate = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+        stage_ms = work / (rate * 1e12) * 1e3
+        total_ms += stage_ms
+        out[name] = {"m": m, "n": n, "k": k, "ms": round(ms, 4), "tflops": round(rate, 1),
+                     "stage_ms_at_this_rate": round(stage_ms, 4)}
+        del a, b, c
+    mfma = sum(v[3] for v in shapes.values())
+    out["encode_mfma_ms_at_vendor_rates"] = round(total_ms, 4)
+    out["pct_bf16_peak_at_vendor_rates"] = round(
+        100.0 * mfma / (total_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)
+    return out
+
+
 STAGE_PASS_STEPS = 20   # untimed steps with every stage bracketed (the stage breakdown)
 FLUSH_MB = 512          # written before every cold gather call: twice the 256 MB MALL
 
@@ -416,6 +462,9 @@ def main():
                          "matrix-core op counters")
     ap.add_argument("--no-gather-cold", action="store_true",
                     help="skip the cold-cache gather measurement")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="also time hipBLASLt (torch.matmul) on the plain product of each "
+                         "contraction shape, as a reference point for the kernels")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: librkv has no multi-GPU path (the encode "
@@ -577,6 +626,8 @@ def main():
         line["append"] = bench_append(R, cfg, p, kv, w1, w2, w3, stream, args)
     if not args.no_variants:
         line["variants"] = bench_variants(R, RB, cfg, kv, w1, w2, w3, idx, stream, args)
+    if args.vendor_gemm:
+        line["vendor_gemm"] = bench_vendor_gemm(cfg, R.rkv_reference_positions(p), dev)
     if not args.no_cpu_baseline:
         print(f"[bench] cpu baseline on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens)
