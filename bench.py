@@ -368,26 +368,30 @@ def bench_vendor_gemm(cfg, refs, dev, reps: int = 20):
         "w3": (B * nr, cfg.d_c, cfg.d_ff, 2.0 * cfg.d_ff * cfg.d_c * B * nr),
     }
     out, total_ms = {}, 0.0
+    best = {}
+    for _ in range(2):                 # two passes over the shapes; the faster of each counts
+        for name, (m, n, k, work) in shapes.items():
+            a = torch.randn((m, k), device=dev).to(torch.bfloat16)
+            b = torch.randn((k, n), device=dev).to(torch.bfloat16)
+            for _ in range(10):
+                c = a @ b
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                c = a @ b
+            e1.record()
+            torch.cuda.synchronize()
+            best[name] = min(best.get(name, float("inf")), e0.elapsed_time(e1) / reps)
+            del a, b, c
     for name, (m, n, k, work) in shapes.items():
-        a = torch.randn((m, k), device=dev).to(torch.bfloat16)
-        b = torch.randn((k, n), device=dev).to(torch.bfloat16)
-        for _ in range(5):
-            c = a @ b
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            c = a @ b
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
+        ms = best[name]
         rate = 2.0 * m * n * k / (ms * 1e-3) / 1e12
         stage_ms = work / (rate * 1e12) * 1e3
         total_ms += stage_ms
         out[name] = {"m": m, "n": n, "k": k, "ms": round(ms, 4), "tflops": round(rate, 1),
                      "stage_ms_at_this_rate": round(stage_ms, 4)}
-        del a, b, c
     mfma = sum(v[3] for v in shapes.values())
     out["encode_mfma_ms_at_vendor_rates"] = round(total_ms, 4)
     out["pct_bf16_peak_at_vendor_rates"] = round(
