@@ -462,7 +462,8 @@ __global__ __launch_bounds__(CF::kThreads, CF::kMinWaves) void k_dist_topk(
     const char* __restrict__ kv, const char* __restrict__ refs, const float* __restrict__ ysq,
     float2* __restrict__ part, int B, int T, int C, const int* __restrict__ nrp, int nref,
     int nr, int n_lists, int n_tt, int n_dist, const char* __restrict__ wp,
-    float* __restrict__ proj, int proj_n, int proj_tiles_m, const char* __restrict__ zrow) {
+    float* __restrict__ proj, int proj_n, int proj_tiles_m, const char* __restrict__ zrow,
+    int serp) {
   using PF = typename CF::Proj;
   constexpr int BM = CF::BM, BN = CF::BN, WGM = CF::WGM, WGN = CF::WGN;
   constexpr int kLists = 2 * WGM;                        // partial lists per token
@@ -480,9 +481,11 @@ __global__ __launch_bounds__(CF::kThreads, CF::kMinWaves) void k_dist_topk(
   float* ysq_l = reinterpret_cast<float*>(lds + kStaged);
   // Work items are the causal (token tile, reference chunk) pairs.  The
   // dispatcher deals workgroups to the 8 XCDs in turn, so workgroup w runs
-  // on XCD w % 8: that XCD takes the token tiles g = x, x+8, x+16, ... and
-  // all of their chunks, one after the other, which keeps a token tile in
-  // its own L2 while the chunks stream past.
+  // on XCD w % 8: that XCD takes one token tile of every row of 8, g = 8m +
+  // x (or, with serp, 8m + 7 - x for odd m: later tiles have longer pools,
+  // so the alternation evens the XCDs' item counts), and all of their
+  // chunks, one after the other, which keeps a token tile in its own L2
+  // while the chunks stream past.
   // Every wave finds the item alike: its 64 lanes take 64 of the XCD's token
   // tiles at once (one load each, not a chain of dependent loads), and a
   // prefix sum of their chunk counts over the lanes locates item l.
@@ -490,8 +493,9 @@ __global__ __launch_bounds__(CF::kThreads, CF::kMinWaves) void k_dist_topk(
   const int l = blockIdx.x >> 3;
   const int lane = threadIdx.x & 63;
   int g = -1, c = -1;
-  for (int g0 = x, before = 0; g0 < B * n_tt; g0 += 8 * 64) {
-    const int gl = g0 + 8 * lane;
+  for (int m0l = 0, before = 0; 8 * m0l < B * n_tt; m0l += 64) {
+    const int ml = m0l + lane;
+    const int gl = 8 * ml + ((serp && (ml & 1)) ? 7 - x : x);
     int np = 0, nch = 0;
     if (gl < B * n_tt) {
       const int tt_ = gl % n_tt;
@@ -1459,7 +1463,22 @@ const Schedule& schedule_for(int T, int s0, double alpha, int n_sink) {
 }
 
 template <typename CF>
-static int dist_items(const Shape& sh, int n_tt);
+static int dist_items(const Shape& sh, int n_tt, int serp);
+
+// How the distance launch deals token tiles to the XCDs: in turn (x, x + 8,
+// ...), or alternating direction every row of 8 (serpentine), which evens
+// the XCDs' item counts.  Measured in one process, per step: serpentine
+// 0.4387 against 0.4459 ms at qwen7b_like_B2_T32k and 0.9692 against
+// 0.9729 ms at multimodal_int2_B4_T16k, but 0.5436 against 0.5376 ms at
+// llama8b_T32k (llama8b_T8k tied); so several sequences take it.
+// RKV_DIST_DEAL=turn or =serp in the environment (read at every launch)
+// forces either; both give the same bits.
+static bool dist_serpentine(const Shape& sh) {
+  const char* force = std::getenv("RKV_DIST_DEAL");
+  if (force && !std::strcmp(force, "turn")) return false;
+  if (force && !std::strcmp(force, "serp")) return true;
+  return sh.B > 1;
+}
 
 // The distance launch's tiling for bf16 runs (fp32 runs: 0): narrow tiles
 // (1) where the wide ones would give the chip fewer than two rounds of
@@ -1483,7 +1502,7 @@ static int choose_dist_tiling(const Shape& sh) {
   if (hipGetDevice(&dev) == hipSuccess)
     (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   using W = DistCfg<uint16_t>;
-  if (dist_items<W>(sh, cdiv(sh.nr, W::BN)) < 2 * cus) return 2;
+  if (dist_items<W>(sh, cdiv(sh.nr, W::BN), dist_serpentine(sh) ? 1 : 0) < 2 * cus) return 2;
   return sh.C <= 1024 ? 1 : 0;
 }
 
@@ -1660,7 +1679,7 @@ hipError_t launch_pack_weights(const Shape& sh, const void* w1, const void* w2, 
 }
 
 template <typename CF>
-static int dist_items(const Shape& sh, int n_tt) {
+static int dist_items(const Shape& sh, int n_tt, int serp) {
   // per-XCD item counts (same enumeration as the kernel); grid = 8 x max
   constexpr int BM = CF::BM, BN = CF::BN;
   long per_xcd[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -1668,7 +1687,8 @@ static int dist_items(const Shape& sh, int n_tt) {
     const int tt = g % n_tt;
     const int q = std::min(tt * BN + BN, sh.nr) - 1;
     const int np = sh.sched->nrp[q] - q;               // references before the tile's last token
-    per_xcd[g & 7] += (np + BM - 1) / BM;
+    const int m = g >> 3, x = (serp && (m & 1)) ? 7 - (g & 7) : (g & 7);
+    per_xcd[x] += (np + BM - 1) / BM;
   }
   return int(8 * *std::max_element(per_xcd, per_xcd + 8));
 }
@@ -1711,19 +1731,20 @@ hipError_t launch_dist(const Shape& sh, const void* kv, char* ws, const Workspac
   const bool use_zero = zoff + size_t(sh.C) * sh.esize < (size_t(1) << 31) &&
                         !(force_zero && !std::strcmp(force_zero, "0"));
   const char* zrow = use_zero ? ws + L.refs + zoff : nullptr;
+  const int serp = dist_serpentine(sh) ? 1 : 0;
   auto go = [&](auto e, auto cf) {
     using E = decltype(e);
     using CF = decltype(cf);
     using PF = typename CF::Proj;
     const int n_tt = cdiv(sh.nr, CF::BN);
-    const int n_dist = dist_items<CF>(sh, n_tt);
+    const int n_dist = dist_items<CF>(sh, n_tt, serp);
     const int ptm = cdiv(pM, PF::BM);
     const int n_proj = wp != nullptr && pM > 0 ? ptm * cdiv(pN, PF::BN) : 0;
     const bool buf = sizeof(E) == 2 && kv_tiles_fit_buffer(sh, CF::BN, false);
 #define RKV_DIST(KL, BUF)                                                                    \
     k_dist_topk<E, CF, KL, BUF><<<n_dist + n_proj, CF::kThreads, 0, st>>>(                   \
         p, ws + L.refs, y, part, sh.B, sh.T, sh.C, nrp, sh.nref, sh.nr, sh.n_chunks, n_tt,   \
-        n_dist, wp, proj, pN, ptm, zrow)
+        n_dist, wp, proj, pN, ptm, zrow, serp)
     if constexpr (sizeof(E) == 2) {
       if (sh.kl == 4) { if (buf) RKV_DIST(4, true); else RKV_DIST(4, false); }
       else { if (buf) RKV_DIST(8, true); else RKV_DIST(8, false); }

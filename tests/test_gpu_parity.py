@@ -292,18 +292,21 @@ def test_distance_tilings_bit_identical(cfg):
     and k > 4 lists, a growing schedule and several sequences.  Rows of a
     chunk that no token of its tile may use read a zero row; with
     RKV_DIST_ZERO=0 they repeat a reference row instead, and the bits stay
-    the same (those products are masked)."""
+    the same (those products are masked).  Token tiles go to the XCDs in
+    turn or in serpentine order (RKV_DIST_DEAL), with the same bits."""
     outs = []
-    for tiling, zero in (("wide", None), ("narrow", None), ("short", None), ("wide", "0"),
-                         ("short", "0")):
+    for tiling, extra in (("wide", {}), ("narrow", {}), ("short", {}),
+                          ("wide", {"RKV_DIST_ZERO": "0"}), ("short", {"RKV_DIST_ZERO": "0"}),
+                          ("wide", {"RKV_DIST_DEAL": "serp"}),
+                          ("narrow", {"RKV_DIST_DEAL": "turn"})):
         os.environ["RKV_DIST_TILE"] = tiling
-        if zero is not None:
-            os.environ["RKV_DIST_ZERO"] = zero
+        os.environ.update(extra)
         try:
             _, _, h, _ = P.run_encode(generate(cfg))
         finally:
             del os.environ["RKV_DIST_TILE"]
-            os.environ.pop("RKV_DIST_ZERO", None)
+            for key in extra:
+                os.environ.pop(key, None)
         outs.append(h)
     for key in ("ref_idx", "codes", "scale", "zmin", "z"):
         for other in outs[1:]:
