@@ -95,13 +95,16 @@ struct TileCfg {
 // slices, two workgroups per CU, so that one scans its lists while the other
 // runs its main loop) where the host finds the wide ones short of work, on
 // chunks of 128 references where the wide tiles would not fill two rounds.
+// Both take 256-reference chunks (measured 1.9% faster per step than 192 at
+// llama8b_T32k, 1% at qwen7b_like_B2_T32k, since the projection tiles fill
+// the last round of items).
 template <typename E> struct DistCfg {
-  static constexpr int BM = 192, BN = 256, SB = 128, NS = 2, WGM = 2, WGN = 4, kMinWaves = 1;
+  static constexpr int BM = 256, BN = 256, SB = 128, NS = 2, WGM = 2, WGN = 4, kMinWaves = 1;
   static constexpr int kThreads = 64 * WGM * WGN;
   using Proj = TileCfg<128, 256, 128, 2, WGM, WGN>;
 };
 struct DistCfgNarrow {
-  static constexpr int BM = 192, BN = 128, SB = 64, NS = 3, WGM = 2, WGN = 2, kMinWaves = 2;
+  static constexpr int BM = 256, BN = 128, SB = 64, NS = 3, WGM = 2, WGN = 2, kMinWaves = 2;
   static constexpr int kThreads = 64 * WGM * WGN;
   using Proj = TileCfg<128, 128, 64, 3, WGM, WGN>;
 };
