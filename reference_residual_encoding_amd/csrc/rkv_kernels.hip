@@ -101,12 +101,12 @@ struct TileCfg {
 template <typename E> struct DistCfg {
   static constexpr int BM = 256, BN = 256, SB = 128, NS = 2, WGM = 2, WGN = 4, kMinWaves = 1;
   static constexpr int kThreads = 64 * WGM * WGN;
-  using Proj = TileCfg<128, 256, 128, 2, WGM, WGN>;
+  using Proj = TileCfg<256, 256, 128, 2, WGM, WGN>;
 };
 struct DistCfgNarrow {
   static constexpr int BM = 256, BN = 128, SB = 64, NS = 3, WGM = 2, WGN = 2, kMinWaves = 2;
   static constexpr int kThreads = 64 * WGM * WGN;
-  using Proj = TileCfg<128, 128, 64, 3, WGM, WGN>;
+  using Proj = TileCfg<256, 128, 64, 3, WGM, WGN>;
 };
 template <> struct DistCfg<float> {
   static constexpr int BM = 128, BN = 256, SB = 128, NS = 2, WGM = 2, WGN = 2, kMinWaves = 1;
