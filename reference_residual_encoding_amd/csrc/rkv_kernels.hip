@@ -745,7 +745,7 @@ __device__ __forceinline__ float silu_fast(float x) {
 // a (hi, lo) bf16 pair, each granule of 8 features as 16 bytes of hi values
 // then 16 bytes of lo values (the A layout of gemm_mainloop_dma_hl); fp32
 // otherwise, feature f at float index Q*d_ff + f.
-template <typename E, int KL, bool BUF>
+template <typename E, int KL, bool BUF, bool STREAM>
 __global__ __launch_bounds__(SwCfg<E>::kThreads) void k_swiglu(const char* __restrict__ kv,
                                                 const char* __restrict__ wp,
                                                 const float* __restrict__ proj,
@@ -913,7 +913,9 @@ __global__ __launch_bounds__(SwCfg<E>::kThreads) void k_swiglu(const char* __res
         const u32x4 wv = odd ? u32x4{r0, r1, lo01, lo23} : u32x4{hi01, hi23, r0, r1};
         const uint32_t so =
             colv ? uint32_t(rt * d_ff + (f & ~7)) * 4u + (odd ? 16u : 0u) : kNone;
-        __builtin_amdgcn_raw_buffer_store_b128(wv, drs, int(so), 0, 0);
+        // STREAM: non-temporal (slc), so delta_h streams out without evicting
+        // the kv rows and P columns the later tiles read again
+        __builtin_amdgcn_raw_buffer_store_b128(wv, drs, int(so), 0, STREAM ? 2 : 0);
       } else {
         const u32x4 wv = {w[0], w[1], w[2], w[3]};
         const uint32_t so = colv ? uint32_t(rt * d_ff + f) * 4u : kNone;
@@ -1794,27 +1796,46 @@ static int swiglu_col_order(const Shape& sh) {
   return kv_bytes > 192.0 * (1 << 20) ? 1 : 0;
 }
 
+// Whether k_swiglu writes delta_h non-temporally.  Where delta_h outgrows
+// the caches, streaming it out keeps the kv rows and P columns that later
+// tiles read again (measured per step in one process: multimodal_int2_B4_T16k,
+// 252 MB of delta_h, 0.9636 -> 0.9509 ms; llama8b_T32k and
+// qwen7b_like_B2_T32k, 126 MB, 1.5 us faster); where it fits, the W3 product
+// finds it in the caches (llama8b_T8k, 31 MB: 3 us slower non-temporal).
+// RKV_DH_NT=0 or =1 in the environment (read at every launch) forces either;
+// the bits are the same.
+static bool swiglu_nt(const Shape& sh) {
+  const char* force = std::getenv("RKV_DH_NT");
+  if (force && force[0] == '0') return false;
+  if (force && force[0] == '1') return true;
+  return double(sh.B) * sh.nr * sh.kdh * sh.esize > 64.0 * (1 << 20);
+}
+
 hipError_t launch_swiglu(const Shape& sh, const void* kv, char* ws,
                          const Workspace& L, const char* wp, hipStream_t st) {
   const int M = sh.B * sh.nr, N = 2 * sh.d_ff;
   if (M == 0) return hipGetLastError();
   const int col_order = swiglu_col_order(sh);
+  const bool nt = swiglu_nt(sh);
   const auto* p = static_cast<const char*>(kv);
   const auto* proj = reinterpret_cast<const float*>(ws + L.proj);
   // P is addressed with 32-bit byte offsets (its size is checked on the host)
   const uint32_t pbytes = uint32_t(size_t(sh.B) * sh.nref * N * 4);
-#define RKV_SW(E, KL, BUF)                                                                      \
-  k_swiglu<E, KL, BUF><<<cdiv(N, SwCfg<E>::BN) * cdiv(M, SwCfg<E>::BM), SwCfg<E>::kThreads, 0,    \
-                         st>>>(                                                                 \
+#define RKV_SW(E, KL, BUF, ST)                                                                  \
+  k_swiglu<E, KL, BUF, ST><<<cdiv(N, SwCfg<E>::BN) * cdiv(M, SwCfg<E>::BM), SwCfg<E>::kThreads, \
+                             0, st>>>(                                                          \
       p, wp, proj, pbytes, reinterpret_cast<const int*>(ws + L.selj), ws + L.dh, sh.T,          \
       sh.C, reinterpret_cast<const int*>(ws + L.nrp), sh.nref, sh.nr, sh.d_ff, M, col_order)
+#define RKV_SW_NT(E, KL, BUF) \
+  if (nt) RKV_SW(E, KL, BUF, true); else RKV_SW(E, KL, BUF, false);
   if (sh.bf16) {
     const bool buf = kv_tiles_fit_buffer(sh, SwCfg<uint16_t>::BM, true);
-    if (sh.kl == 4) { if (buf) RKV_SW(uint16_t, 4, true); else RKV_SW(uint16_t, 4, false); }
-    else { if (buf) RKV_SW(uint16_t, 8, true); else RKV_SW(uint16_t, 8, false); }
+    if (sh.kl == 4) { if (buf) { RKV_SW_NT(uint16_t, 4, true) } else { RKV_SW_NT(uint16_t, 4, false) } }
+    else { if (buf) { RKV_SW_NT(uint16_t, 8, true) } else { RKV_SW_NT(uint16_t, 8, false) } }
   } else {
-    if (sh.kl == 4) RKV_SW(float, 4, false); else RKV_SW(float, 8, false);
+    if (sh.kl == 4) RKV_SW(float, 4, false, false); else RKV_SW(float, 8, false, false);
   }
+#undef RKV_SW_NT
 #undef RKV_SW
   return hipGetLastError();
 }

@@ -265,17 +265,22 @@ def test_swiglu_tile_orders_bit_identical(cfg):
     """k_swiglu runs its tiles row tile fastest, or column tile fastest once
     the kv rows outgrow the MALL; RKV_SWIGLU_ORDER forces either.  The order
     only moves work between workgroups, so both give the same bits, with
-    ragged column tiles (d_ff = 96, 64) and token tiles that cross sequences."""
+    ragged column tiles (d_ff = 96, 64) and token tiles that cross sequences.
+    delta_h is written non-temporally once it outgrows the caches;
+    RKV_DH_NT forces either, with the same bits."""
     outs = []
-    for order in ("row", "col"):
+    for order, nt in (("row", "0"), ("col", "0"), ("row", "1")):
         os.environ["RKV_SWIGLU_ORDER"] = order
+        os.environ["RKV_DH_NT"] = nt
         try:
             _, _, h, _ = P.run_encode(generate(cfg))
         finally:
             del os.environ["RKV_SWIGLU_ORDER"]
+            del os.environ["RKV_DH_NT"]
         outs.append(h)
     for key in ("ref_idx", "codes", "scale", "zmin", "z"):
-        assert np.array_equal(outs[0][key].view(np.uint8), outs[1][key].view(np.uint8)), key
+        for other in outs[1:]:
+            assert np.array_equal(outs[0][key].view(np.uint8), other[key].view(np.uint8)), key
 
 
 @pytest.mark.parametrize("cfg", [LLAMA8K.with_(name="llama_B3_T1500", B=3, T=1500), RAGGED[0],
