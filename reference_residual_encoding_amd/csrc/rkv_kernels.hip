@@ -1166,8 +1166,9 @@ __global__ __launch_bounds__(256) void k_restore_prep(const uint8_t* __restrict_
 // tile holds whole heads and every rotation partner (d +- D/2) is in it.
 // The rows of the stored references whose mean it adds come from the prep
 // kernel's table (FP8: rows of the E4M3 store).
-// theta^(-2i/D) for the D/2 <= 64 rotation pairs of a head, computed in
-// fp64 on the host once per call (a kernel argument)
+// theta^(-2i/D) / (2 pi), the rotation rate of each of the D/2 <= 64 pairs
+// of a head in revolutions per position, computed in fp64 on the host once
+// per call (a kernel argument)
 struct RateTable {
   double r[64];
 };
@@ -1244,7 +1245,7 @@ __device__ __forceinline__ void restore_tile(
   int* rows_lds = reinterpret_cast<int*>(lds + kStaged);            // [BM][KL] kv rows, -1 none
   float* inv_lds = reinterpret_cast<float*>(lds + kStaged + BM * KL * 4);  // [BM] 1 / count
   int* pos_lds = reinterpret_cast<int*>(lds + kStaged + BM * (KL + 1) * 4);  // [BM] t, -1 invalid
-  double* rate = reinterpret_cast<double*>(lds + kStaged + BM * (KL + 2) * 4);  // [D/2] theta^(-2i/D)
+  double* rate = reinterpret_cast<double*>(lds + kStaged + BM * (KL + 2) * 4);  // [D/2] rates, revolutions
   const int tid = threadIdx.x;
   // The row's entry of the prep kernel's table: loaded before the main loop
   // (its latency passes under the first stages' copies), written to LDS
@@ -1346,11 +1347,11 @@ __device__ __forceinline__ void restore_tile(
         const int i0 = first ? d0 : d0 - D / 2;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          // angle pos * rate reduced to [-pi, pi] in fp64, then sin/cos in fp32
+          // angle pos * rate in revolutions, reduced to [-1/2, 1/2] in fp64,
+          // then the hardware sine and cosine of revolutions
           const double a = double(pos) * rate[i0 + e];
-          const float ar = float(a - 6.283185307179586 * rint(a * 0.15915494309189535));
-          float sn, cs;
-          sincosf(ar, &sn, &cs);
+          const float ar = float(a - rint(a));
+          const float sn = __builtin_amdgcn_sinf(ar), cs = __builtin_amdgcn_cosf(ar);
           y[e] = first ? tr[e] * cs - pr[e] * sn : tr[e] * cs + pr[e] * sn;
         }
       }
@@ -2047,7 +2048,8 @@ hipError_t launch_restore(const Shape& sh, int N, int D, const uint8_t* codes,
   const auto* kvp = static_cast<const char*>(kv);
   RateTable rt{};
   if (theta > 0.0f)
-    for (int i = 0; i < D / 2; ++i) rt.r[i] = std::pow(double(theta), -2.0 * i / double(D));
+    for (int i = 0; i < D / 2; ++i)   // in revolutions per position
+      rt.r[i] = std::pow(double(theta), -2.0 * i / double(D)) / 6.283185307179586;
   // n_wide CF tiles over rows [0, rows_wide), then CT tiles over the rest
   auto go = [&](auto e, auto cf, auto ct, int rows_wide) {
     using E = decltype(e);
