@@ -9,22 +9,26 @@
 // products are bound by reading the weights and the references once):
 //   dist     one workgroup per 8 pool references of a sequence: squared L2
 //            by direct differences, the workgroup's best KL as a list
-//   sel_proj one workgroup per 16 features (and 4 tokens): each merges its
-//            tokens' lists by (distance, position) itself, then x W1, x W2,
-//            m W1, m W2 over all C rows (the mean m of the chosen references
-//            formed in fp32 at the rows it needs), reduced in LDS, then
-//            delta_h = Swish(x W1) (x W2) - Swish(m W1) (m W2) ([RKV] §2.3);
-//            the first feature block writes ref_idx, and stores a reference
-//            token in the cache with a zero record
-//   w3       one workgroup per (token, 32 or 64 latent columns): z =
-//            delta_h W3 (W3 is linear, so f_c(kv) - f_c(m) = (h(kv) - h(m))
-//            W3), then the group quantiser of [RKV] §2.4 and the record
+//   sel_proj one workgroup per 16 features, slice of the C rows and 4
+//            tokens: each merges its tokens' lists by (distance, position)
+//            itself, then x W1, x W2, m W1, m W2 over its rows (the mean m of
+//            the chosen references formed in fp32 at the rows it needs),
+//            reduced in LDS to one partial sum per slice; the first feature
+//            block writes ref_idx, and stores a reference token in the cache
+//            with a zero record
+//   w3       one workgroup per (token, 32 or 64 latent columns): the slices'
+//            partial sums added in slice order, delta_h = Swish(x W1) (x W2)
+//            - Swish(m W1) (m W2) ([RKV] §2.3), z = delta_h W3 (W3 is
+//            linear, so f_c(kv) - f_c(m) = (h(kv) - h(m)) W3), then the group
+//            quantiser of [RKV] §2.4 and the record
 #include "rkv_device.h"
 #include "rkv_internal.h"
 #include "rkv_quant.h"
 
 #include <cfloat>
+#include <cstdlib>
 #include <mutex>
+#include <type_traits>
 
 namespace rkv {
 
@@ -50,25 +54,70 @@ __device__ __forceinline__ void load8(const E* p, float (&v)[8]) {
   }
 }
 
-template <typename E>
-__device__ __forceinline__ void load4(const E* p, float (&v)[4]) {
-  if constexpr (sizeof(E) == 2) {
-    const uint2 w = *reinterpret_cast<const uint2*>(p);
+// Four consecutive weights loaded as raw words now and converted to float
+// later, so the load can be requested ahead of its use.
+template <typename E> struct RawW4;
+template <> struct RawW4<uint16_t> {
+  uint2 w;
+  __device__ __forceinline__ void load(const uint16_t* p) { w = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ void decode(float (&v)[4]) const {
     v[0] = __uint_as_float(w.x << 16);
     v[1] = __uint_as_float(w.x & 0xFFFF0000u);
     v[2] = __uint_as_float(w.y << 16);
     v[3] = __uint_as_float(w.y & 0xFFFF0000u);
-  } else {
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
   }
-}
+};
+template <> struct RawW4<float> {
+  float4 w;
+  __device__ __forceinline__ void load(const float* p) { w = *reinterpret_cast<const float4*>(p); }
+  __device__ __forceinline__ void decode(float (&v)[4]) const {
+    v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+  }
+};
 
 template <typename E>
 __device__ __forceinline__ float load1(const E* p) {
   if constexpr (sizeof(E) == 2) return bf16_to_f32(*p);
   else return *p;
 }
+
+// Eight consecutive values loaded as raw words now and converted to float
+// later, so that a batch of loads can be requested before any is used.
+template <typename E> struct RawW8;
+template <> struct RawW8<uint16_t> {
+  u32x4 w;
+  __device__ __forceinline__ void load(const uint16_t* p) { w = *reinterpret_cast<const u32x4*>(p); }
+  __device__ __forceinline__ void decode(float (&v)[8]) const {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = __uint_as_float(w[e] << 16);
+      v[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+    }
+  }
+};
+template <> struct RawW8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = reinterpret_cast<const float4*>(p)[0];
+    b = reinterpret_cast<const float4*>(p)[1];
+  }
+  __device__ __forceinline__ void decode(float (&v)[8]) const {
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
+
+template <typename E> struct RawF8x8 {                   // 8 E4M3 bytes
+  uint2 w;
+  __device__ __forceinline__ void load(const uint8_t* p) { w = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ void decode(float (&v)[8]) const {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = fp8_e4m3_to_f32((w.x >> (8 * e)) & 0xFFu);
+      v[4 + e] = fp8_e4m3_to_f32((w.y >> (8 * e)) & 0xFFu);
+    }
+  }
+};
 
 // Stored reference j of sequence b: the row at its position in kv
 // [B][T][C] (input precision), or row j of the FP8 store [B][nref][C].
@@ -80,7 +129,15 @@ struct RefRows {
   __device__ __forceinline__ size_t row(int b, int j) const {
     return FP8 ? size_t(b) * sv.nref + j : size_t(b) * T + ref_position(sv, j);
   }
-  // 8 coordinates [o, o + 8) of stored row `r` (from row())
+  // 8 coordinates [o, o + 8) of stored row `r` (from row()), raw
+  using Raw = std::conditional_t<FP8, RawF8x8<E>, RawW8<E>>;
+  __device__ __forceinline__ void load_raw(size_t r, int o, Raw& w) const {
+    if constexpr (FP8)
+      w.load(static_cast<const uint8_t*>(base) + r * C + o);
+    else
+      w.load(static_cast<const E*>(base) + r * C + o);
+  }
+  // the same, converted
   __device__ __forceinline__ void load(size_t r, int o, float (&v)[8]) const {
     if constexpr (FP8) {
       const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(base) + r * C + o);
@@ -101,11 +158,9 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// State of sequence b's new token: -1 nothing to encode (invalid position
-// or a reference), else the size of its pool.
-__device__ __forceinline__ int pool_of(const SchedView& v, const int32_t* pos, int b, int T,
-                                       int& t) {
-  t = pos[b];
+// State of a new token at position t: -1 nothing to encode (invalid
+// position or a reference), else the size of its pool.
+__device__ __forceinline__ int pool_at(const SchedView& v, int t, int T) {
   if (t < 0 || t >= T) return -1;
   bool is_ref;
   const int n = refs_before(v, t, is_ref);
@@ -114,65 +169,101 @@ __device__ __forceinline__ int pool_of(const SchedView& v, const int32_t* pos, i
 
 // ---------------------------------------------------------------- distance
 // Workgroup (b, c): pool references j in [8c, 8c + 8) of sequence b, two
-// per wave with both rows' loads in flight; d = sum (x - y)^2 in fp32.
-template <typename E, int KL, bool FP8>
+// per wave with both rows' loads in flight; d = sum (x - y)^2 in fp32.  The
+// rows are requested before the pool is known (j clamped into the
+// references), together with the position's load.  The workgroup's list is
+// then ranked in parallel: each of 8 lanes counts the candidates that order
+// before its own by (d, j), and candidates that no list slot would take
+// (past the pool, or d not <= FLT_MAX) leave their slots to padding.
+template <typename E, int KL, bool FP8, int U>
 __global__ __launch_bounds__(256) void k_app_dist(const void* __restrict__ kv,
                                                   const E* __restrict__ kv_new,
                                                   const int32_t* __restrict__ pos, SchedView sv,
                                                   int T, int C, int n_lists,
                                                   float2* __restrict__ part) {
   const RefRows<E, FP8> refs{kv, sv, T, C};
+  if (sv.nref <= 0) return;                              // no references: no lists
   const int b = blockIdx.x / n_lists, c = blockIdx.x % n_lists;
-  int t;
-  const int pool = pool_of(sv, pos, b, T, t);
   const int j0 = c * kAppCH;
-  if (pool < 0 || j0 >= pool) return;
   __shared__ float dl[kAppCH];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int ja = j0 + 2 * wave, jb = ja + 1;
-  const bool va = ja < pool, vb = jb < pool;
   const E* x = kv_new + size_t(b) * C;
-  const size_t ya = refs.row(b, va ? ja : j0), yb = refs.row(b, vb ? jb : j0);
+  const size_t ya = refs.row(b, min(ja, sv.nref - 1)), yb = refs.row(b, min(jb, sv.nref - 1));
+  // the position through a vector load requested after the rows' addresses
+  // are known: its wait then comes after the rows' (a scalar load would be
+  // waited for with the kernel arguments the loop needs)
+  asm volatile("" ::: "memory");
+  int zero;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+  const int t = pos[b + zero];
   float sa = 0.0f, sb = 0.0f;
-#pragma unroll 4
-  for (int o = lane * 8; o < C; o += 512) {
-    float xv[8], av[8], bv[8];
-    load8(x + o, xv);
-    refs.load(ya, o, av);
-    refs.load(yb, o, bv);
+  // U x 512 coordinates at a time: all 3U loads of a lane requested before
+  // any is used (coordinates past C read coordinate 0 and add nothing)
+  for (int o0 = 0; o0 < C; o0 += U * 512) {
+    RawW8<E> xr[U];
+    typename RefRows<E, FP8>::Raw ar[U], br[U];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float da = xv[e] - av[e], db = xv[e] - bv[e];
-      sa = fmaf(da, da, sa);
-      sb = fmaf(db, db, sb);
+    for (int u = 0; u < U; ++u) {
+      const int o = o0 + u * 512 + lane * 8;
+      const int oc = o < C ? o : 0;
+      xr[u].load(x + oc);
+      refs.load_raw(ya, oc, ar[u]);
+      refs.load_raw(yb, oc, br[u]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool in = o0 + u * 512 + lane * 8 < C;
+      float xv[8], av[8], bv[8];
+      xr[u].decode(xv);
+      ar[u].decode(av);
+      br[u].decode(bv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float da = in ? xv[e] - av[e] : 0.0f, db = in ? xv[e] - bv[e] : 0.0f;
+        sa = fmaf(da, da, sa);
+        sb = fmaf(db, db, sb);
+      }
     }
   }
+  asm volatile("" ::: "memory");                        // the row loads stay ahead of the exit
+  const int pool = pool_at(sv, t, T);                    // uniform over the workgroup
+  if (pool < 0 || j0 >= pool) return;
   sa = wave_sum(sa);
   sb = wave_sum(sb);
   if (lane == 0) {
-    dl[2 * wave] = va ? sa : FLT_MAX;
-    dl[2 * wave + 1] = vb ? sb : FLT_MAX;
+    dl[2 * wave] = sa;
+    dl[2 * wave + 1] = sb;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    float bd[KL];
-    int bi[KL];
+  if (threadIdx.x < 64) {
+    static_assert(kAppCH <= 64 && KL <= kAppCH, "one lane per candidate and per slot");
+    const int i = lane;
+    const float di = dl[min(i, kAppCH - 1)];
+    // a slot takes (d, j) when it orders before the padding (FLT_MAX, kNoRef)
+    const bool ok = i < kAppCH && j0 + i < pool && di <= FLT_MAX;
+    int rank = 0;
 #pragma unroll
-    for (int e = 0; e < KL; ++e) { bd[e] = FLT_MAX; bi[e] = kNoRef; }
-    for (int i = 0; i < kAppCH && j0 + i < pool; ++i) topk_push_lex(bd, bi, dl[i], j0 + i);
+    for (int e = 0; e < kAppCH; ++e) {
+      const float de = dl[e];
+      const bool oe = j0 + e < pool && de <= FLT_MAX;
+      rank += (oe && (de < di || (de == di && e < i))) ? 1 : 0;
+    }
+    const int n_ok = __popcll(__ballot(ok));
     float2* dst = part + size_t(blockIdx.x) * KL;
-#pragma unroll
-    for (int e = 0; e < KL; ++e) dst[e] = make_float2(bd[e], __int_as_float(bi[e]));
+    if (ok && rank < KL) dst[rank] = make_float2(di, __int_as_float(j0 + i));
+    if (i >= n_ok && i < KL) dst[i] = make_float2(FLT_MAX, __int_as_float(kNoRef));
   }
 }
 
 // ---------------------------------------------------------------- select + projection
-// One launch does both: every workgroup (16 features of RB appended tokens)
-// first chooses its tokens' references itself, from the distance lists
-// (they are small and L2-resident), so no launch waits for a separate
-// selection.  Workgroups with fb == 0 also write the token's ref_idx, store
-// a reference token as it is (with a zero record) and set act[b] = 1 when
-// the token is to be encoded.
+// One launch does both: every workgroup (16 features of RB appended tokens,
+// one slice of rows) first chooses its tokens' references itself, from the
+// distance lists (they are small and L2-resident), so no launch waits for a
+// separate selection.  The workgroup of feature block 0 and slice 0 also
+// writes the token's ref_idx, stores a reference token as it is (with a
+// zero record) and sets act[b] = 1 when the token is to be encoded.
 //
 // Selection of sequence b's token by one wave: every lane merges the lists
 // l, l + 64, ... of the ceil(pool/8) lists, then the lanes' lists are merged
@@ -181,14 +272,39 @@ __global__ __launch_bounds__(256) void k_app_dist(const void* __restrict__ kv,
 // depend on the merge order.  Writes the chosen stored rows (ascending
 // position) to sel[0..KL) and returns k_t; -1 when the token is not encoded
 // (no append this call, or a reference).  With `writer`, also writes
-// ref_idx and act[b], and stores a reference token as it is.
-template <typename E, int KL, bool FP8>
+// ref_idx and act[b], and stores a reference token as it is.  `pre()` is
+// called once, right after the first lists are requested (the caller's own
+// loads then queue behind them, not in front).  b must be uniform over the
+// wave.
+template <typename E, int KL, bool FP8, typename Pre>
 __device__ int select_token(void* kv, const E* kv_new, const int32_t* pos, SchedView sv, int T,
                             int C, int k, int rec_bytes, int n_groups, int d_c, int n_lists,
                             const float2* part, int32_t* ref_idx, uint8_t* codes, uint16_t* scale,
-                            uint16_t* zmin, float* z, int* act, int b, bool writer, int* sel) {
+                            uint16_t* zmin, float* z, int* act, int b, bool writer, int* sel,
+                            Pre pre) {
   const int lane = threadIdx.x & 63;
   const int t = pos[b];
+  // The lists' addresses do not depend on the position: the first LU per
+  // lane are requested together with it (l >= n_lists reads the last list;
+  // only lists below the pool's count are merged, as padding otherwise).
+  constexpr int LU = 4;
+  float4 w[LU][KL / 2];
+  auto request = [&](int l0) {
+#pragma unroll
+    for (int u = 0; u < LU; ++u) {
+      const int l = min(l0 + 64 * u, n_lists - 1);
+      const float4* src = reinterpret_cast<const float4*>(part + (size_t(b) * n_lists + l) * KL);
+#pragma unroll
+      for (int e = 0; e < KL / 2; ++e) w[u][e] = src[e];
+    }
+  };
+  request(lane);
+  // the lists' loads, then pre()'s, then the rest: nothing moves across
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  pre();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
   if (t < 0 || t >= T) {                                 // not appended this call
     if (writer && lane == 0) act[b] = 0;
     return -1;
@@ -235,16 +351,23 @@ __device__ int select_token(void* kv, const E* kv_new, const int32_t* pos, Sched
   int bi[KL];
 #pragma unroll
   for (int e = 0; e < KL; ++e) { bd[e] = FLT_MAX; bi[e] = kNoRef; }
-  for (int l = lane; l < nch; l += 64) {
-    const float4* src = reinterpret_cast<const float4*>(part + (size_t(b) * n_lists + l) * KL);
-    float4 w[KL / 2];
+  auto merge = [&](int l0) {
 #pragma unroll
-    for (int e = 0; e < KL / 2; ++e) w[e] = src[e];      // the whole list in flight at once
+    for (int u = 0; u < LU; ++u) {
+      // a list past the pool's enters as padding, which no slot takes (the
+      // loads are used either way, so none is moved under a branch)
+      const bool in = l0 + 64 * u < nch;
 #pragma unroll
-    for (int e = 0; e < KL / 2; ++e) {
-      topk_push_lex(bd, bi, w[e].x, __float_as_int(w[e].y));
-      topk_push_lex(bd, bi, w[e].z, __float_as_int(w[e].w));
+      for (int e = 0; e < KL / 2; ++e) {
+        topk_push_lex(bd, bi, in ? w[u][e].x : FLT_MAX, in ? __float_as_int(w[u][e].y) : kNoRef);
+        topk_push_lex(bd, bi, in ? w[u][e].z : FLT_MAX, in ? __float_as_int(w[u][e].w) : kNoRef);
+      }
     }
+  };
+  merge(lane);
+  for (int l0 = lane + 64 * LU; l0 - lane < nch; l0 += 64 * LU) {   // uniform over the wave
+    request(l0);
+    merge(l0);
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {             // butterfly over the wave
@@ -277,29 +400,32 @@ __device__ int select_token(void* kv, const E* kv_new, const int32_t* pos, Sched
   return kt;
 }
 
-// Workgroup: features [16w, 16w + 16) of RB appended tokens (the feature
-// block runs fastest, so the workgroups of one block of W share it in L2).
-// After choosing the tokens' references, four consecutive lanes cover the
-// 16 features of one row of W1 and of W2 (32 contiguous bytes each at
-// bf16), so a wave's load touches 16 rows; the 64 row groups of the
-// workgroup take 8 consecutive rows each of every 512-row chunk, the loads
-// of a chunk in flight together.  The mean of the chosen references is
-// formed at the rows a thread needs, in fp32 from the stored rows (sum in
-// order, times 1/k_t).  For its RB tokens a thread accumulates x.W1, x.W2,
-// m.W1, m.W2 for its 4 features; the 64 partial sums of each value are
-// reduced through LDS in a fixed order, then
-// delta_h = Swish(x W1) (x W2) - Swish(m W1) (m W2) ([RKV] §2.3).
+// Workgroup: features [16 fb, 16 fb + 16) of RB appended tokens over the
+// 512-row chunks s, s + S, s + 2S, ... of the C rows (S slices; the feature
+// block runs fastest, then the slice).  After choosing the tokens'
+// references, four consecutive lanes cover the 16 features of one row of W1
+// and of W2 (32 contiguous bytes each at bf16), so a wave's load touches 16
+// rows; the 64 row groups of the workgroup take 8 consecutive rows each of
+// a chunk.  The first chunk's W1 and W2 are requested before the selection
+// and each next chunk's while the current one is multiplied.  The mean of
+// the chosen references is formed at the rows a thread needs, in fp32 from
+// the stored rows (sum in order, times 1/k_t).  For its RB tokens a thread
+// accumulates x.W1, x.W2, m.W1, m.W2 for its 4 features; the 64 partial
+// sums of each value are reduced through LDS in a fixed order into the
+// slice's partial sums ph[b][s][x.W1 | x.W2 | m.W1 | m.W2][d_ff].
 template <typename E, int KL, bool FP8>
 __global__ __launch_bounds__(256) void k_app_sel_proj(
     void* __restrict__ kv, const E* __restrict__ kv_new, const int32_t* __restrict__ pos,
     SchedView sv, int T, int C, int k, int rec_bytes, int n_groups, int d_c, int n_lists,
     const float2* __restrict__ part, int32_t* __restrict__ ref_idx, uint8_t* __restrict__ codes,
     uint16_t* __restrict__ scale, uint16_t* __restrict__ zmin, float* __restrict__ z,
-    const E* __restrict__ w1, const E* __restrict__ w2, int B, int d_ff,
-    float* __restrict__ dh, int* __restrict__ act) {
+    const E* __restrict__ w1, const E* __restrict__ w2, int B, int d_ff, int S,
+    float* __restrict__ ph, int* __restrict__ act) {
   constexpr int RB = 4, NV = RB * 16, RPT = 8, RG = 64;  // values: [token][x|m][W1|W2][feature]
+  constexpr int CH = RG * RPT;                           // rows per chunk
   const int nfb = d_ff / 16;                             // feature blocks; tokens RB at a time
-  const int fb = blockIdx.x % nfb, b0 = (blockIdx.x / nfb) * RB;
+  const int fb = blockIdx.x % nfb, sl = (blockIdx.x / nfb) % S;
+  const int b0 = (blockIdx.x / (nfb * S)) * RB;
   const int tid = threadIdx.x, fq = tid & 3, rg = tid >> 2;
   const int f0 = fb * 16 + fq * 4;                       // this lane's 4 features
   __shared__ float red[NV * (256 + 1)];
@@ -307,13 +433,28 @@ __global__ __launch_bounds__(256) void k_app_sel_proj(
   __shared__ int sel_l[RB][KL];
   __shared__ int kt_l[RB];
   static_assert(RB == 4, "one wave selects each of the workgroup's tokens");
+  // W1 and W2 of the first chunk do not depend on the selection: requested
+  // during it, so their latency passes under the merge (rows past C read row
+  // C - 8 and go unused)
+  const int c1_first = min(sl * CH + rg * RPT, C - RPT);
+  RawW4<E> wa[RPT], wb[RPT];
+  auto prefetch = [&]() {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      wa[i].load(w1 + size_t(c1_first + i) * d_ff + f0);
+      wb[i].load(w2 + size_t(c1_first + i) * d_ff + f0);
+    }
+  };
   {
-    const int r = tid >> 6, b = b0 + r;                  // wave r selects token r
+    const int r = tid >> 6;                              // wave r selects token r
+    const int b = __builtin_amdgcn_readfirstlane(b0 + r);
     int kt = -1;
     if (b < B)
       kt = select_token<E, KL, FP8>(kv, kv_new, pos, sv, T, C, k, rec_bytes, n_groups, d_c,
                                     n_lists, part, ref_idx, codes, scale, zmin, z, act, b,
-                                    fb == 0, sel_l[r]);
+                                    fb == 0 && sl == 0, sel_l[r], prefetch);
+    else
+      prefetch();
     if ((tid & 63) == 0) kt_l[r] = kt;
   }
   __syncthreads();
@@ -325,28 +466,37 @@ __global__ __launch_bounds__(256) void k_app_sel_proj(
     bool live[RB];
     int kt[RB];
     float inv[RB];
-    size_t srow[RB][KL];
+    int srow[RB][KL];                                    // stored rows (B*T < 2^31)
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
       kt[r] = kt_l[r];
       live[r] = kt[r] > 0;
       inv[r] = 1.0f / float(max(kt[r], 1));
 #pragma unroll
-      for (int i = 0; i < KL; ++i) srow[r][i] = size_t(max(sel_l[r][min(i, max(kt[r], 1) - 1)], 0));
+      for (int i = 0; i < KL; ++i) srow[r][i] = max(sel_l[r][min(i, max(kt[r], 1) - 1)], 0);
     }
-    for (int c0 = 0; c0 < C; c0 += RG * RPT) {
-      // rows c1 .. c1 + 7 of this thread: W1 and W2 for its 4 features, and
-      // every token's x and its references' values there, all in flight
-      // together and none under a branch (C is a multiple of 8, so a
-      // thread's 8 rows are all in range or all past the end)
+    for (int c0 = sl * CH; c0 < C; c0 += S * CH) {
+      // rows c1 .. c1 + 7 of this thread: W1 and W2 for its 4 features
+      // (requested a chunk ahead), and every token's x and its references'
+      // values there, all in flight together and none under a branch (C is
+      // a multiple of 8, so a thread's 8 rows are all in range or all past
+      // the end)
       const int c1 = c0 + rg * RPT;
       const bool in = c1 < C;
       const int cb = in ? c1 : 0;
       float a1[RPT][4], a2[RPT][4];
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
-        load4(w1 + size_t(cb + i) * d_ff + f0, a1[i]);
-        load4(w2 + size_t(cb + i) * d_ff + f0, a2[i]);
+        wa[i].decode(a1[i]);
+        wb[i].decode(a2[i]);
+      }
+      if (c0 + S * CH < C) {                             // uniform: the next chunk's W
+        const int cn = min(c1 + S * CH, C - RPT);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+          wa[i].load(w1 + size_t(cn + i) * d_ff + f0);
+          wb[i].load(w2 + size_t(cn + i) * d_ff + f0);
+        }
       }
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
@@ -354,7 +504,7 @@ __global__ __launch_bounds__(256) void k_app_sel_proj(
         float xv[RPT], mv[RPT], v[KL][RPT];
         load8(kv_new + size_t(b0 + r) * C + cb, xv);
 #pragma unroll
-        for (int i = 0; i < KL; ++i) refs.load(srow[r][i], cb, v[i]);
+        for (int i = 0; i < KL; ++i) refs.load(size_t(srow[r][i]), cb, v[i]);
 #pragma unroll
         for (int e = 0; e < RPT; ++e) {
           float m = 0.0f;
@@ -390,23 +540,27 @@ __global__ __launch_bounds__(256) void k_app_sel_proj(
       const int r = tid / 16, q = (tid / 4) & 3, f = tid & 3;
       if (live[r]) {
         const float* u = tot + q * NV + r * 16;
-        const float hk = silu(u[0 + f]) * u[4 + f];
-        const float hm = silu(u[8 + f]) * u[12 + f];
-        dh[size_t(b0 + r) * d_ff + fb * 16 + q * 4 + f] = hk - hm;
+        float* dst = ph + (size_t(b0 + r) * S + sl) * 4 * d_ff + fb * 16 + q * 4 + f;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) dst[size_t(v) * d_ff] = u[4 * v + f];
       }
     }
   }
 }
 
 // ---------------------------------------------------------------- W3 + quantiser
-// Workgroup (token b, columns [CB*w, CB*w + CB)), CB = 32 (g <= 32) or 64:
-// LPR = CB/8 lanes cover a row of the block, 8 columns each; the 256/LPR
-// row groups sum delta_h[f] W3[f][.] over f = rg + (256/LPR) i, 16 rows'
-// loads in flight at a time; the partial rows are reduced in LDS; the first
-// LPR lanes then hold 8 consecutive latents each and run the group
-// quantiser ([RKV] §2.4).
+constexpr int kAppF = 4096;         // delta_h features the W3 kernel holds in LDS at a time
+
+// Workgroup (token b, columns [CB*w, CB*w + CB)), CB = 32 (g <= 32) or 64,
+// over the features in blocks of kAppF: delta_h of the block is formed in
+// LDS from the S slices' partial sums (added in slice order, [RKV] §2.3),
+// the first rows of W3 already in flight; then LPR = CB/8 lanes cover a row
+// of the column block, 8 columns each, and the 256/LPR row groups sum
+// delta_h[f] W3[f][.] over f = rg + (256/LPR) i, 16 rows' loads in flight at
+// a time; the partial rows are reduced in LDS; the first LPR lanes then hold
+// 8 consecutive latents each and run the group quantiser ([RKV] §2.4).
 template <typename E, int BITS, int G8, int CB>
-__global__ __launch_bounds__(256) void k_app_w3(const float* __restrict__ dh,
+__global__ __launch_bounds__(256) void k_app_w3(const float* __restrict__ ph, int S,
                                                 const int* __restrict__ act,
                                                 const int32_t* __restrict__ pos,
                                                 const E* __restrict__ w3, int T, int d_ff,
@@ -417,25 +571,71 @@ __global__ __launch_bounds__(256) void k_app_w3(const float* __restrict__ dh,
   constexpr int LPR = CB / 8, RG = 256 / LPR, UN = 16;
   const int nblk = d_c / CB;
   const int b = blockIdx.x / nblk, c0 = (blockIdx.x % nblk) * CB;
-  if (act[b] != 1) return;
+  // no early exit: the loads below go out together with this flag's, and a
+  // token not encoded (a reference, or no append) only has its writes
+  // skipped (its partial sums were not written; they are read in bounds and
+  // their results dropped)
+  const bool live = act[b] == 1;
   const int tid = threadIdx.x, cg = tid % LPR, rg = tid / LPR;
   __shared__ float red[RG * (CB + 1)];
   __shared__ float zl[CB];
+  __shared__ float dhl[kAppF];
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  const float* dhb = dh + size_t(b) * d_ff;
+  const float* phb = ph + size_t(b) * S * 4 * d_ff;
   const E* wcol = w3 + c0 + cg * 8;
-  for (int f1 = rg; f1 < d_ff; f1 += RG * UN) {
-    float d[UN], w[UN][8];
+  for (int fc = 0; fc < d_ff; fc += kAppF) {
+    const int nf = min(kAppF, d_ff - fc);                // a multiple of 16
+    RawW8<E> wr[UN];
 #pragma unroll
-    for (int u = 0; u < UN; ++u) {
-      const int f = min(f1 + RG * u, d_ff - 1);
-      d[u] = f1 + RG * u < d_ff ? dhb[f] : 0.0f;
-      load8(wcol + size_t(f) * d_c, w[u]);
+    for (int u = 0; u < UN; ++u) wr[u].load(wcol + size_t(fc + min(rg + RG * u, nf - 1)) * d_c);
+    for (int f = tid * 4; f < nf; f += 256 * 4) {
+      // four slices' loads in flight at once, added in slice order (a
+      // slice past the last re-reads the last and is not added)
+      float4 a[4];
+      auto batch = [&](int s0) {
+        float4 t[4][4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            t[j][v] = *reinterpret_cast<const float4*>(
+                phb + size_t(4 * min(s0 + j, S - 1) + v) * d_ff + fc + f);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bool first = s0 + j == 0, add = s0 + j > 0 && s0 + j < S;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            a[v].x = first ? t[j][v].x : (add ? a[v].x + t[j][v].x : a[v].x);
+            a[v].y = first ? t[j][v].y : (add ? a[v].y + t[j][v].y : a[v].y);
+            a[v].z = first ? t[j][v].z : (add ? a[v].z + t[j][v].z : a[v].z);
+            a[v].w = first ? t[j][v].w : (add ? a[v].w + t[j][v].w : a[v].w);
+          }
+        }
+      };
+      batch(0);
+      for (int s0 = 4; s0 < S; s0 += 4) batch(s0);
+      float4 o;
+      o.x = silu(a[0].x) * a[1].x - silu(a[2].x) * a[3].x;
+      o.y = silu(a[0].y) * a[1].y - silu(a[2].y) * a[3].y;
+      o.z = silu(a[0].z) * a[1].z - silu(a[2].z) * a[3].z;
+      o.w = silu(a[0].w) * a[1].w - silu(a[2].w) * a[3].w;
+      *reinterpret_cast<float4*>(dhl + f) = o;
     }
+    __syncthreads();
+    for (int f1 = rg; f1 < nf; f1 += RG * UN) {
+      if (f1 != rg)
 #pragma unroll
-    for (int u = 0; u < UN; ++u)
+        for (int u = 0; u < UN; ++u) wr[u].load(wcol + size_t(fc + min(f1 + RG * u, nf - 1)) * d_c);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = fmaf(d[u], w[u][e], acc[e]);
+      for (int u = 0; u < UN; ++u) {
+        const float d = f1 + RG * u < nf ? dhl[f1 + RG * u] : 0.0f;
+        float w[8];
+        wr[u].decode(w);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(d, w[e], acc[e]);
+      }
+    }
+    __syncthreads();                                     // dhl is rewritten by the next block
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) red[rg * (CB + 1) + cg * 8 + e] = acc[e];
@@ -450,10 +650,10 @@ __global__ __launch_bounds__(256) void k_app_w3(const float* __restrict__ dh,
     float v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = tid < LPR ? zl[min(tid, LPR - 1) * 8 + e] : 0.0f;
-    const size_t row = size_t(b) * T + pos[b];
+    const size_t row = size_t(b) * T + (live ? pos[b] : 0);
     const int64_t unit = int64_t(row) * (d_c / 8) + c0 / 8 + tid;
-    write_record8<BITS, G8>(v, tid < LPR, tid, unit, codes, scale, zmin);
-    if (tid < LPR) {
+    write_record8<BITS, G8>(v, live && tid < LPR, tid, unit, codes, scale, zmin);
+    if (live && tid < LPR) {
       if (z) {
         float4* dst = reinterpret_cast<float4*>(z + unit * 8);
         dst[0] = make_float4(v[0], v[1], v[2], v[3]);
@@ -495,14 +695,30 @@ hipError_t append_scratch(char** ptr) {
   return hipSuccess;
 }
 
+// Slices of the C rows in the projection launch: enough that it has about
+// two workgroups per compute unit (512) where the tokens and feature blocks
+// alone give fewer, at most one 512-row chunk each.  More slices mean more
+// partial sums to add in the W3 launch, and other sums in fp32 (the slices
+// are added in order, so a shape always gives the same bits).
+// RKV_APP_SPLIT=n in the environment (read at every call, the workspace
+// query included) forces n slices, clamped to [1, chunks].
+static int append_split(const Shape& sh) {
+  const int chunks = cdiv(sh.C, 512);
+  const int groups = sh.d_ff / 16 * cdiv(sh.B, 4);
+  int s = std::max(1, cdiv(512, groups));
+  if (const char* force = std::getenv("RKV_APP_SPLIT")) s = std::atoi(force);
+  return std::min(std::max(s, 1), chunks);
+}
+
 AppendWorkspace plan_append(const Shape& sh) {
   AppendWorkspace L{};
   L.n_lists = cdiv(std::max(sh.nref, 1), kAppCH);
+  L.n_split = append_split(sh);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t at = off; off += align256(bytes); return at; };
   L.rpos = take(size_t(sh.nref) * 4);
   L.part = take(size_t(sh.B) * L.n_lists * sh.kl * 8);
-  L.dh = take(size_t(sh.B) * sh.d_ff * 4);
+  L.ph = take(size_t(sh.B) * L.n_split * 4 * sh.d_ff * 4);
   L.act = take(size_t(sh.B) * 4);
   L.total = off;
   return L;
@@ -520,20 +736,31 @@ hipError_t launch_append(const Shape& sh, void* kv, const void* kv_new, const in
     sv.rpos = rpos;
   }
   auto* part = reinterpret_cast<float2*>(ws + L.part);
-  auto* dh = reinterpret_cast<float*>(ws + L.dh);
+  auto* ph = reinterpret_cast<float*>(ws + L.ph);
   auto* act = reinterpret_cast<int*>(ws + L.act);
   const int rec_bytes = sh.d_c * sh.b / 8;
   const int n_groups = sh.b == kIdentityBits ? 0 : sh.d_c / sh.g;   // identity: no group numbers
   const int cb = sh.g <= 32 || sh.b == kIdentityBits ? 32 : 64;   // a block holds whole groups
   const int n_dist = sh.B * L.n_lists;
+  // coordinates per lane in flight in the distance launch: 4 x 8 where it
+  // has at most two workgroups per compute unit (its time is then the
+  // latency of one batch), 2 x 8 above (more waves fit, which a launch
+  // bound by HBM bandwidth prefers).  RKV_APP_DIST_U=2|4 in the environment
+  // forces one; both give the same bits.
+  int dist_u = n_dist <= 512 ? 4 : 2;
+  if (const char* force = std::getenv("RKV_APP_DIST_U")) dist_u = std::atoi(force) == 4 ? 4 : 2;
 
 #define RKV_APP(E, KL, F8)                                                                        \
-  k_app_dist<E, KL, F8><<<n_dist, 256, 0, st>>>(kv, static_cast<const E*>(kv_new), pos, sv, sh.T, \
-                                                sh.C, L.n_lists, part);                          \
-  k_app_sel_proj<E, KL, F8><<<sh.d_ff / 16 * cdiv(sh.B, 4), 256, 0, st>>>(                         \
+  if (dist_u == 4)                                                                                \
+    k_app_dist<E, KL, F8, 4><<<n_dist, 256, 0, st>>>(kv, static_cast<const E*>(kv_new), pos, sv,  \
+                                                     sh.T, sh.C, L.n_lists, part);               \
+  else                                                                                            \
+    k_app_dist<E, KL, F8, 2><<<n_dist, 256, 0, st>>>(kv, static_cast<const E*>(kv_new), pos, sv,  \
+                                                     sh.T, sh.C, L.n_lists, part);               \
+  k_app_sel_proj<E, KL, F8><<<sh.d_ff / 16 * L.n_split * cdiv(sh.B, 4), 256, 0, st>>>(             \
       kv, static_cast<const E*>(kv_new), pos, sv, sh.T, sh.C, sh.k, rec_bytes, n_groups, sh.d_c, \
       L.n_lists, part, ref_idx, codes, scale, zmin, z, static_cast<const E*>(w1),              \
-      static_cast<const E*>(w2), sh.B, sh.d_ff, dh, act)
+      static_cast<const E*>(w2), sh.B, sh.d_ff, L.n_split, ph, act)
 #define RKV_APPK(E, F8) \
   if (sh.kl == 4) { RKV_APP(E, 4, F8); } else { RKV_APP(E, 8, F8); }
   if (sh.bf16) {
@@ -547,10 +774,10 @@ hipError_t launch_append(const Shape& sh, void* kv, const void* kv_new, const in
   const int n_w3 = sh.B * (sh.d_c / cb);
 #define RKV_W3(E, BITS, G8)                                                                        \
   if (cb == 32)                                                                                    \
-    k_app_w3<E, BITS, G8, 32><<<n_w3, 256, 0, st>>>(dh, act, pos, static_cast<const E*>(w3),      \
+    k_app_w3<E, BITS, G8, 32><<<n_w3, 256, 0, st>>>(ph, L.n_split, act, pos, static_cast<const E*>(w3),      \
                                                     sh.T, sh.d_ff, sh.d_c, codes, scale, zmin, z); \
   else                                                                                             \
-    k_app_w3<E, BITS, G8, 64><<<n_w3, 256, 0, st>>>(dh, act, pos, static_cast<const E*>(w3),      \
+    k_app_w3<E, BITS, G8, 64><<<n_w3, 256, 0, st>>>(ph, L.n_split, act, pos, static_cast<const E*>(w3),      \
                                                     sh.T, sh.d_ff, sh.d_c, codes, scale, zmin, z)
 #define RKV_W3G(E, BITS)                   \
   switch (sh.g) {                          \

@@ -125,7 +125,8 @@ hipError_t launch_restore(const Shape& sh, int N, int D, const uint8_t* codes,
 // Append ([RKV] §2.7 decode step 4): one new token per sequence.
 struct AppendWorkspace {
   int n_lists;          // distance workgroups (partial lists) per sequence
-  size_t rpos, part, dh, act, total;
+  int n_split;          // slices of the C rows of W1 | W2, one workgroup each
+  size_t rpos, part, ph, act, total;
 };
 AppendWorkspace plan_append(const Shape& sh);
 // Size of the fixed device scratch the allocation-free append works in.

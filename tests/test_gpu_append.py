@@ -218,3 +218,33 @@ def test_append_exact_ties_keep_smaller_positions(dtype):
         assert np.array_equal(got[t], want), (t, got[t], want)
     c.check(cfg.name)
 
+
+
+_KNOB_BITS = {}      # records of the four-slice runs, one per distance batch size
+
+
+@pytest.mark.parametrize("split,batch", [(1, 2), (2, 4), (4, 2), (4, 4)])
+def test_append_row_slices_and_distance_batches(monkeypatch, split, batch):
+    """Every slicing of the C rows in the projection (the slices' partial
+    sums are added in slice order, so each slicing has its own fp32 sums)
+    and both distance batch sizes (the same bits) match the oracle; five
+    sequences leave three tokens of the second block of four empty."""
+    cfg = LLAMA8K.with_(name=f"append_split{split}_u{batch}", B=5, T=4096)
+    monkeypatch.setenv("RKV_APP_SPLIT", str(split))
+    monkeypatch.setenv("RKV_APP_DIST_U", str(batch))
+    _log(f"[case] append {cfg.name}")
+    c = _make(cfg, prefill=True)
+    rng = np.random.default_rng(split)              # the same positions for both batch sizes
+    for i in range(3):
+        pos = rng.integers(1, cfg.T, size=cfg.B)
+        if i == 1:
+            pos[2] = -1
+        c.append(pos)
+    c.check(cfg.name)
+    if split == 4:
+        torch.cuda.synchronize()
+        got = [t.cpu().numpy().view(np.uint8) for t in (c.codes, c.scale, c.zmin, c.ref_idx)]
+        _KNOB_BITS[batch] = got
+        if len(_KNOB_BITS) == 2:
+            for a, b in zip(_KNOB_BITS[2], _KNOB_BITS[4]):
+                assert np.array_equal(a, b), "the distance batch sizes gave different records"
