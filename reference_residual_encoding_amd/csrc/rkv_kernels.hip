@@ -300,6 +300,21 @@ __device__ __forceinline__ void ref_rows(const RefArgs& a, int blk) {
   }
   const int b = wid / nref, j = wid % nref;
   const size_t rec = size_t(b) * T + size_t(ref_position(a.sv, j));   // the reference token's row
+  const size_t rowb = size_t(C) * sizeof(E);
+  const char* src = kv + rec * rowb;
+  char* dst = refs + size_t(wid) * rowb;
+  // the row's first 4 KiB requested before the record's stores, every load
+  // of a batch before any is used (bytes past the row re-read byte 0)
+  constexpr int U = 4;
+  uint4 w[U];
+  auto request = [&](size_t o0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t o = o0 + size_t(u) * 1024 + size_t(lane) * 16;
+      w[u] = *reinterpret_cast<const uint4*>(src + (o < rowb ? o : 0));
+    }
+  };
+  request(0);
   for (int i = lane; i < k; i += 64) ref_idx[rec * k + i] = -1;
   if (codes) {
     for (int o = lane * 4; o < cb; o += 256) *reinterpret_cast<uint32_t*>(codes + rec * cb + o) = 0u;
@@ -308,39 +323,41 @@ __device__ __forceinline__ void ref_rows(const RefArgs& a, int blk) {
       for (int i = lane * 4; i < d_c; i += 256)
         *reinterpret_cast<float4*>(z + rec * d_c + i) = make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  const size_t rowb = size_t(C) * sizeof(E);
-  const char* src = kv + rec * rowb;
-  char* dst = refs + size_t(wid) * rowb;
   float acc = 0.0f;
-  for (size_t o = size_t(lane) * 16; o < rowb; o += 64 * 16) {
-    uint4 w = *reinterpret_cast<const uint4*>(src + o);
-    if (fp8) {                                           // the values the FP8 store holds
-      uint32_t* u = reinterpret_cast<uint32_t*>(&w);
+  for (size_t o0 = 0; o0 < rowb; o0 += U * 1024) {
+    if (o0 > 0) request(o0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if constexpr (sizeof(E) == 2) {
-          const float lo = fp8_round(__uint_as_float(u[e] << 16));
-          const float hi = fp8_round(__uint_as_float(u[e] & 0xFFFF0000u));
-          u[e] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);  // exact in bf16
-        } else {
-          u[e] = __float_as_uint(fp8_round(__uint_as_float(u[e])));
+    for (int v = 0; v < U; ++v) {
+      const size_t o = o0 + size_t(v) * 1024 + size_t(lane) * 16;
+      if (o >= rowb) break;
+      uint32_t u[4] = {w[v].x, w[v].y, w[v].z, w[v].w};
+      if (fp8) {                                         // the values the FP8 store holds
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (sizeof(E) == 2) {
+            const float lo = fp8_round(__uint_as_float(u[e] << 16));
+            const float hi = fp8_round(__uint_as_float(u[e] & 0xFFFF0000u));
+            u[e] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);  // exact in bf16
+          } else {
+            u[e] = __float_as_uint(fp8_round(__uint_as_float(u[e])));
+          }
         }
       }
-    }
-    *reinterpret_cast<uint4*>(dst + o) = w;
-    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-    if constexpr (sizeof(E) == 2) {
+      *reinterpret_cast<uint4*>(dst + o) = make_uint4(u[0], u[1], u[2], u[3]);
+      if constexpr (sizeof(E) == 2) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float lo = __uint_as_float(u[e] << 16), hi = __uint_as_float(u[e] & 0xFFFF0000u);
-        acc = fmaf(lo, lo, acc);
-        acc = fmaf(hi, hi, acc);
-      }
-    } else {
+        for (int e = 0; e < 4; ++e) {
+          const float lo = __uint_as_float(u[e] << 16), hi = __uint_as_float(u[e] & 0xFFFF0000u);
+          acc = fmaf(lo, lo, acc);
+          acc = fmaf(hi, hi, acc);
+        }
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float f = __uint_as_float(u[e]);
-        acc = fmaf(f, f, acc);
+        for (int e = 0; e < 4; ++e) {
+          const float f = __uint_as_float(u[e]);
+          acc = fmaf(f, f, acc);
+        }
       }
     }
   }
@@ -653,44 +670,50 @@ __global__ __launch_bounds__(CF::kThreads, CF::kMinWaves) void k_dist_topk(
 // (d, j), so equal distances keep the smaller position whatever order the
 // lists come in.  (Reference tokens' all -1 rows and zero records are
 // written by the set-up kernel: references are stored as they are, [RKV]
-// §2.4.)
+// §2.4.)  kMergeLanes consecutive lanes share a token: lane s merges lists
+// s, s + 4, ..., two at a time with both in flight, then the lanes' lists
+// are merged by a butterfly over the four, and the first writes the result.
+constexpr int kMergeLanes = 4;
+
 template <int KL>
-__global__ __launch_bounds__(64) void k_topk_merge(const float2* __restrict__ part,
-                                                    int32_t* __restrict__ ref_idx, int B, int T,
-                                                    const int* __restrict__ tab,
-                                                    const int* __restrict__ rpos, int k, int nr,
-                                                    int n_lists, int chunk,
-                                                    int* __restrict__ selj) {
-  const long gid = long(blockIdx.x) * 64 + threadIdx.x;
-  if (gid >= long(B) * T) return;
-  const int b = int(gid / T), t = int(gid % T);
-  int32_t* out = ref_idx + gid * k;
+__global__ __launch_bounds__(256) void k_topk_merge(const float2* __restrict__ part,
+                                                     int32_t* __restrict__ ref_idx, int B, int T,
+                                                     const int* __restrict__ tab,
+                                                     const int* __restrict__ rpos, int k, int nr,
+                                                     int n_lists, int chunk,
+                                                     int* __restrict__ selj) {
+  const long gid = long(blockIdx.x) * 256 + threadIdx.x;
+  const long tok = gid / kMergeLanes;
+  const int sub = int(gid % kMergeLanes);
+  // every lane stays to the butterfly; lanes past the last token, and the
+  // lanes of a reference token, merge nothing and write nothing
+  const bool in = tok < long(B) * T;
+  const int b = in ? int(tok / T) : 0, t = in ? int(tok % T) : 0;
   const int q = tab[t];
-  if (q < 0) return;                                    // a reference
-  const int npool = t - q;
+  const bool enc = in && q >= 0;
+  const int npool = enc ? t - q : 0;
   const int kt = min(k, npool);
   const int nch = (npool + chunk - 1) / chunk;          // lists that cover the pool
   float bd[KL];
   int bi[KL];
 #pragma unroll
   for (int i = 0; i < KL; ++i) { bd[i] = __builtin_inff(); bi[i] = 0x7fffffff; }
-  const float2* p = part + (size_t(b) * n_lists * nr + q) * KL;
+  const float2* p = part + (size_t(b) * n_lists * nr + max(q, 0)) * KL;
   const size_t cstride = size_t(nr) * KL;
-  // kB lists per batch (every list of a typical pool at once), 16-byte
-  // loads; every load is unconditional (a list index past the last one is
-  // clamped and its values are replaced by +inf)
-  constexpr int kB = KL <= 4 ? 12 : 6;
-  for (int c0 = 0; c0 < nch; c0 += kB) {
-    float4 v[kB][KL / 2];
+  for (int c0 = sub; c0 < nch; c0 += 2 * kMergeLanes) {
+    // lists c0 and c0 + 4; one past the last re-reads the last and enters
+    // as padding
+    float4 v[2][KL / 2];
 #pragma unroll
-    for (int u = 0; u < kB; ++u) {
-      const float4* src = reinterpret_cast<const float4*>(p + min(c0 + u, nch - 1) * cstride);
+    for (int u = 0; u < 2; ++u) {
+      const float4* src =
+          reinterpret_cast<const float4*>(p + min(c0 + u * kMergeLanes, nch - 1) * cstride);
 #pragma unroll
       for (int h = 0; h < KL / 2; ++h) v[u][h] = src[h];
     }
 #pragma unroll
-    for (int u = 0; u < kB; ++u) {
-      const bool live = c0 + u < nch;
+    for (int u = 0; u < 2; ++u) {
+      const bool live = c0 + u * kMergeLanes < nch;
 #pragma unroll
       for (int h = 0; h < KL / 2; ++h) {
         topk_push_lex<KL>(bd, bi, live ? v[u][h].x : __builtin_inff(),
@@ -700,6 +723,17 @@ __global__ __launch_bounds__(64) void k_topk_merge(const float2* __restrict__ pa
       }
     }
   }
+#pragma unroll
+  for (int off = 1; off < kMergeLanes; off <<= 1) {
+    float od[KL];
+    int oi[KL];
+#pragma unroll
+    for (int i = 0; i < KL; ++i) { od[i] = __shfl_xor(bd[i], off); oi[i] = __shfl_xor(bi[i], off); }
+#pragma unroll
+    for (int i = 0; i < KL; ++i) topk_push_lex<KL>(bd, bi, od[i], oi[i]);
+  }
+  if (!enc || sub != 0) return;
+  int32_t* out = ref_idx + tok * k;
   int sel[KL];
 #pragma unroll
   for (int i = 0; i < KL; ++i) sel[i] = i < kt ? bi[i] : 0x7fffffff;
@@ -1769,12 +1803,12 @@ hipError_t launch_dist(const Shape& sh, const void* kv, char* ws, const Workspac
 hipError_t launch_merge(const Shape& sh, int32_t* ref_idx, char* ws, const Workspace& L,
                         hipStream_t st) {
   const auto* part = reinterpret_cast<const float2*>(ws + L.part);
-  const int nb = cdiv(long(sh.B) * sh.T, 64);   // one wave per block: every CU takes part
+  const int nb = int(cdiv(long(sh.B) * sh.T * kMergeLanes, 256));
   const int chunk = sh.dist_bm;
   const auto* tab = reinterpret_cast<const int*>(ws + L.tab);
   const auto* rpos = reinterpret_cast<const int*>(ws + L.rpos);
 #define RKV_MERGE(KL)                                                                        \
-  k_topk_merge<KL><<<nb, 64, 0, st>>>(part, ref_idx, sh.B, sh.T, tab, rpos, sh.k, sh.nr,    \
+  k_topk_merge<KL><<<nb, 256, 0, st>>>(part, ref_idx, sh.B, sh.T, tab, rpos, sh.k, sh.nr,   \
                                       sh.n_chunks, chunk, reinterpret_cast<int*>(ws + L.selj))
   if (sh.kl == 4) RKV_MERGE(4); else RKV_MERGE(8);
 #undef RKV_MERGE
