@@ -286,7 +286,10 @@ def bench_append(R, cfg, p_enc, kv, w1, w2, w3, stream, args, batches=(1, 16)):
             call()
         st = R.STAGES.index("append")
         reps = max(args.steps, 50)
-        R.rkv_profile_begin(1 << st)
+        # per call: back-to-back calls between two events, without the stage
+        # profiler (its event pair per call costs host time that a call this
+        # short would otherwise wait on); then the library's own stage events
+        # in a second pass
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
@@ -296,6 +299,10 @@ def bench_append(R, cfg, p_enc, kv, w1, w2, w3, stream, args, batches=(1, 16)):
         e1.record(stream)
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / reps
+        R.rkv_profile_begin(1 << st)
+        for _ in range(reps):
+            call()
+        torch.cuda.synchronize()
         tot, cnt = R.rkv_profile_read(st)
         R.rkv_profile_begin(0)
         pools = np.searchsorted(np.asarray(refs), pos_h)          # references before each position
