@@ -132,9 +132,17 @@ RAGGED_F32 = LLAMA8K.with_(name="append_ragged_f32_k8_g64", B=2, T=700, N=1, D=6
                            d_c=128, k=8, g=64, b=4, stride=3, dtype="f32", n_protos=12, noise=0.3)
 
 
+# C = 1280 rows of W1 | W2 in two slices (chunks 0 and 2, and chunk 1; the
+# last chunk half past C) and d_ff = 4352 features, past the 4096 that the W3
+# launch holds in LDS at a time
+WIDE_FF = LLAMA8K.with_(name="append_c1280_dff4352_two_slices", B=2, T=600, N=5, D=128,
+                        d_ff=4352, d_c=64, k=3, g=16, b=4, stride=5, n_protos=16)
+
+
 @pytest.mark.parametrize("cfg", [RAGGED_BF16, RAGGED_F32,
                                  RAGGED_BF16.with_(name="append_ragged_bf16_identity", b=16),
-                                 RAGGED_BF16.with_(name="append_ragged_bf16_fp8ref", ref_fp8=True)],
+                                 RAGGED_BF16.with_(name="append_ragged_bf16_fp8ref", ref_fp8=True),
+                                 WIDE_FF],
                          ids=lambda c: c.name)
 def test_append_independent_positions_per_sequence(cfg):
     """Continuous batching: every call appends a different position in each
