@@ -400,20 +400,22 @@ __device__ int select_token(void* kv, const E* kv_new, const int32_t* pos, Sched
   return kt;
 }
 
-// Workgroup: features [16 fb, 16 fb + 16) of RB appended tokens over the
-// 512-row chunks s, s + S, s + 2S, ... of the C rows (S slices; the feature
-// block runs fastest, then the slice).  After choosing the tokens'
-// references, four consecutive lanes cover the 16 features of one row of W1
-// and of W2 (32 contiguous bytes each at bf16), so a wave's load touches 16
-// rows; the 64 row groups of the workgroup take 8 consecutive rows each of
-// a chunk.  The first chunk's W1 and W2 are requested before the selection
-// and each next chunk's while the current one is multiplied.  The mean of
-// the chosen references is formed at the rows a thread needs, in fp32 from
-// the stored rows (sum in order, times 1/k_t).  For its RB tokens a thread
-// accumulates x.W1, x.W2, m.W1, m.W2 for its 4 features; the 64 partial
-// sums of each value are reduced through LDS in a fixed order into the
-// slice's partial sums ph[b][s][x.W1 | x.W2 | m.W1 | m.W2][d_ff].
-template <typename E, int KL, bool FP8>
+// Workgroup: features [16 fb, 16 fb + 16) of RB (2 or 4) appended tokens
+// over the 512-row chunks s, s + S, s + 2S, ... of the C rows (S slices; the
+// feature block runs fastest, then the slice).  After choosing the tokens'
+// references (wave r for token r), four consecutive lanes cover the 16
+// features of one row of W1 and of W2 (32 contiguous bytes each at bf16), so
+// a wave's load touches 16 rows; the 64 row groups of the workgroup take 8
+// consecutive rows each of a chunk.  The first chunk's W1 and W2 are
+// requested during the selection and each next chunk's while the current
+// one is multiplied; with two tokens, both tokens' rows of a chunk are
+// requested together.  The mean of the chosen references is formed at the
+// rows a thread needs, in fp32 from the stored rows (sum in order, times
+// 1/k_t).  For its RB tokens a thread accumulates x.W1, x.W2, m.W1, m.W2 for
+// its 4 features; the 64 partial sums of each value are reduced through LDS
+// in a fixed order into the slice's partial sums
+// ph[b][s][x.W1 | x.W2 | m.W1 | m.W2][d_ff].
+template <typename E, int KL, bool FP8, int RB>
 __global__ __launch_bounds__(256) void k_app_sel_proj(
     void* __restrict__ kv, const E* __restrict__ kv_new, const int32_t* __restrict__ pos,
     SchedView sv, int T, int C, int k, int rec_bytes, int n_groups, int d_c, int n_lists,
@@ -421,7 +423,7 @@ __global__ __launch_bounds__(256) void k_app_sel_proj(
     uint16_t* __restrict__ scale, uint16_t* __restrict__ zmin, float* __restrict__ z,
     const E* __restrict__ w1, const E* __restrict__ w2, int B, int d_ff, int S,
     float* __restrict__ ph, int* __restrict__ act) {
-  constexpr int RB = 4, NV = RB * 16, RPT = 8, RG = 64;  // values: [token][x|m][W1|W2][feature]
+  constexpr int NV = RB * 16, RPT = 8, RG = 64;           // values: [token][x|m][W1|W2][feature]
   constexpr int CH = RG * RPT;                           // rows per chunk
   const int nfb = d_ff / 16;                             // feature blocks; tokens RB at a time
   const int fb = blockIdx.x % nfb, sl = (blockIdx.x / nfb) % S;
@@ -432,7 +434,7 @@ __global__ __launch_bounds__(256) void k_app_sel_proj(
   __shared__ float tot[4 * NV];
   __shared__ int sel_l[RB][KL];
   __shared__ int kt_l[RB];
-  static_assert(RB == 4, "one wave selects each of the workgroup's tokens");
+  static_assert(RB == 2 || RB == 4, "one wave selects each of the workgroup's tokens");
   // W1 and W2 of the first chunk do not depend on the selection: requested
   // during it, so their latency passes under the merge (rows past C read row
   // C - 8 and go unused)
@@ -446,16 +448,16 @@ __global__ __launch_bounds__(256) void k_app_sel_proj(
     }
   };
   {
-    const int r = tid >> 6;                              // wave r selects token r
+    const int r = tid >> 6;                              // wave r < RB selects token r
     const int b = __builtin_amdgcn_readfirstlane(b0 + r);
     int kt = -1;
-    if (b < B)
+    if (r < RB && b < B)
       kt = select_token<E, KL, FP8>(kv, kv_new, pos, sv, T, C, k, rec_bytes, n_groups, d_c,
                                     n_lists, part, ref_idx, codes, scale, zmin, z, act, b,
                                     fb == 0 && sl == 0, sel_l[r], prefetch);
     else
       prefetch();
-    if ((tid & 63) == 0) kt_l[r] = kt;
+    if (r < RB && (tid & 63) == 0) kt_l[r] = kt;
   }
   __syncthreads();
   const RefRows<E, FP8> refs{kv, sv, T, C};
@@ -473,9 +475,15 @@ __global__ __launch_bounds__(256) void k_app_sel_proj(
       live[r] = kt[r] > 0;
       inv[r] = 1.0f / float(max(kt[r], 1));
 #pragma unroll
-      for (int i = 0; i < KL; ++i) srow[r][i] = max(sel_l[r][min(i, max(kt[r], 1) - 1)], 0);
+      for (int i = 0; i < KL; ++i)                       // row 0 for a token not encoded
+        srow[r][i] = live[r] ? max(sel_l[r][min(i, kt[r] - 1)], 0) : 0;
     }
-    for (int c0 = sl * CH; c0 < C; c0 += S * CH) {
+    // with a token encoded here there is a reference row 0, which the
+    // batched loads of a token not encoded read (and drop)
+    bool any_live = false;
+#pragma unroll
+    for (int r = 0; r < RB; ++r) any_live = any_live || live[r];
+    for (int c0 = sl * CH; any_live && c0 < C; c0 += S * CH) {
       // rows c1 .. c1 + 7 of this thread: W1 and W2 for its 4 features
       // (requested a chunk ahead), and every token's x and its references'
       // values there, all in flight together and none under a branch (C is
@@ -498,13 +506,9 @@ __global__ __launch_bounds__(256) void k_app_sel_proj(
           wb[i].load(w2 + size_t(cn + i) * d_ff + f0);
         }
       }
-#pragma unroll
-      for (int r = 0; r < RB; ++r) {
-        if (!live[r] || !in) continue;                   // uniform per workgroup
-        float xv[RPT], mv[RPT], v[KL][RPT];
-        load8(kv_new + size_t(b0 + r) * C + cb, xv);
-#pragma unroll
-        for (int i = 0; i < KL; ++i) refs.load(size_t(srow[r][i]), cb, v[i]);
+      // the chunk's contribution of token r from its decoded rows
+      auto accumulate = [&](int r, const float (&xv)[RPT], const float (&v)[KL][RPT]) {
+        float mv[RPT];
 #pragma unroll
         for (int e = 0; e < RPT; ++e) {
           float m = 0.0f;
@@ -522,15 +526,46 @@ __global__ __launch_bounds__(256) void k_app_sel_proj(
             acc[r * 16 + 8 + f] = fmaf(mv[i], a1[i][f], acc[r * 16 + 8 + f]);
             acc[r * 16 + 12 + f] = fmaf(mv[i], a2[i][f], acc[r * 16 + 12 + f]);
           }
+      };
+      if constexpr (RB == 2) {
+        // both tokens' rows requested before either is used
+        RawW8<E> xr[RB];
+        typename RefRows<E, FP8>::Raw rr[RB][KL];
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+          xr[r].load(kv_new + size_t(min(b0 + r, B - 1)) * C + cb);
+#pragma unroll
+          for (int i = 0; i < KL; ++i) refs.load_raw(size_t(srow[r][i]), cb, rr[r][i]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+          if (!live[r] || !in) continue;                 // uniform per workgroup
+          float xv[RPT], v[KL][RPT];
+          xr[r].decode(xv);
+#pragma unroll
+          for (int i = 0; i < KL; ++i) rr[r][i].decode(v[i]);
+          accumulate(r, xv, v);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+          if (!live[r] || !in) continue;                 // uniform per workgroup
+          float xv[RPT], v[KL][RPT];
+          load8(kv_new + size_t(b0 + r) * C + cb, xv);
+#pragma unroll
+          for (int i = 0; i < KL; ++i) refs.load(size_t(srow[r][i]), cb, v[i]);
+          accumulate(r, xv, v);
+        }
       }
     }
 #pragma unroll
     for (int v = 0; v < NV; ++v) red[v * 257 + tid] = acc[v];
     __syncthreads();
-    {
+    for (int i = tid; i < 4 * NV; i += 256) {
       // output (v, q): value v of the lanes with fq == q, summed over the
       // 64 row groups in order
-      const int q = tid & 3, v = tid >> 2;
+      const int q = i & 3, v = i >> 2;
       float s = 0.0f;
       for (int g = 0; g < RG; ++g) s += red[v * 257 + g * 4 + q];
       tot[q * NV + v] = s;
@@ -702,9 +737,20 @@ hipError_t append_scratch(char** ptr) {
 // are added in order, so a shape always gives the same bits).
 // RKV_APP_SPLIT=n in the environment (read at every call, the workspace
 // query included) forces n slices, clamped to [1, chunks].
-static int append_split(const Shape& sh) {
+// Appended tokens per projection workgroup: 2 for one or two sequences
+// (fewer accumulators, both tokens' rows requested together), else 4 (the
+// workgroups of four tokens read each chunk of W once for all four).  In one
+// process at C = 2048, d_ff = 1024: B = 1 23.3 against 24.3 us per call with
+// 4; B = 16 54.3 against 53.1 us.  RKV_APP_RB=2|4 in the environment (read
+// at every call, the workspace query included) forces one.
+static int append_tokens_per_block(const Shape& sh) {
+  if (const char* force = std::getenv("RKV_APP_RB")) return std::atoi(force) == 4 ? 4 : 2;
+  return sh.B <= 2 ? 2 : 4;
+}
+
+static int append_split(const Shape& sh, int rb) {
   const int chunks = cdiv(sh.C, 512);
-  const int groups = sh.d_ff / 16 * cdiv(sh.B, 4);
+  const int groups = sh.d_ff / 16 * cdiv(sh.B, rb);
   int s = std::max(1, cdiv(512, groups));
   if (const char* force = std::getenv("RKV_APP_SPLIT")) s = std::atoi(force);
   return std::min(std::max(s, 1), chunks);
@@ -713,7 +759,8 @@ static int append_split(const Shape& sh) {
 AppendWorkspace plan_append(const Shape& sh) {
   AppendWorkspace L{};
   L.n_lists = cdiv(std::max(sh.nref, 1), kAppCH);
-  L.n_split = append_split(sh);
+  L.rb = append_tokens_per_block(sh);
+  L.n_split = append_split(sh, L.rb);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t at = off; off += align256(bytes); return at; };
   L.rpos = take(size_t(sh.nref) * 4);
@@ -757,10 +804,16 @@ hipError_t launch_append(const Shape& sh, void* kv, const void* kv_new, const in
   else                                                                                            \
     k_app_dist<E, KL, F8, 2><<<n_dist, 256, 0, st>>>(kv, static_cast<const E*>(kv_new), pos, sv,  \
                                                      sh.T, sh.C, L.n_lists, part);               \
-  k_app_sel_proj<E, KL, F8><<<sh.d_ff / 16 * L.n_split * cdiv(sh.B, 4), 256, 0, st>>>(             \
-      kv, static_cast<const E*>(kv_new), pos, sv, sh.T, sh.C, sh.k, rec_bytes, n_groups, sh.d_c, \
-      L.n_lists, part, ref_idx, codes, scale, zmin, z, static_cast<const E*>(w1),              \
-      static_cast<const E*>(w2), sh.B, sh.d_ff, L.n_split, ph, act)
+  if (L.rb == 2)                                                                                   \
+    k_app_sel_proj<E, KL, F8, 2><<<sh.d_ff / 16 * L.n_split * cdiv(sh.B, 2), 256, 0, st>>>(        \
+        kv, static_cast<const E*>(kv_new), pos, sv, sh.T, sh.C, sh.k, rec_bytes, n_groups, sh.d_c, \
+        L.n_lists, part, ref_idx, codes, scale, zmin, z, static_cast<const E*>(w1),            \
+        static_cast<const E*>(w2), sh.B, sh.d_ff, L.n_split, ph, act);                         \
+  else                                                                                            \
+    k_app_sel_proj<E, KL, F8, 4><<<sh.d_ff / 16 * L.n_split * cdiv(sh.B, 4), 256, 0, st>>>(        \
+        kv, static_cast<const E*>(kv_new), pos, sv, sh.T, sh.C, sh.k, rec_bytes, n_groups, sh.d_c, \
+        L.n_lists, part, ref_idx, codes, scale, zmin, z, static_cast<const E*>(w1),            \
+        static_cast<const E*>(w2), sh.B, sh.d_ff, L.n_split, ph, act)
 #define RKV_APPK(E, F8) \
   if (sh.kl == 4) { RKV_APP(E, 4, F8); } else { RKV_APP(E, 8, F8); }
   if (sh.bf16) {

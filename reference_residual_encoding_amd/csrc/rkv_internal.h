@@ -126,6 +126,7 @@ hipError_t launch_restore(const Shape& sh, int N, int D, const uint8_t* codes,
 struct AppendWorkspace {
   int n_lists;          // distance workgroups (partial lists) per sequence
   int n_split;          // slices of the C rows of W1 | W2, one workgroup each
+  int rb;               // appended tokens per projection workgroup (2 or 4)
   size_t rpos, part, ph, act, total;
 };
 AppendWorkspace plan_append(const Shape& sh);

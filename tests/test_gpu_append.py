@@ -231,15 +231,17 @@ def test_append_exact_ties_keep_smaller_positions(dtype):
 _KNOB_BITS = {}      # records of the four-slice runs, one per distance batch size
 
 
-@pytest.mark.parametrize("split,batch", [(1, 2), (2, 4), (4, 2), (4, 4)])
-def test_append_row_slices_and_distance_batches(monkeypatch, split, batch):
+@pytest.mark.parametrize("split,batch,rb", [(1, 2, 2), (2, 4, 2), (2, 2, 4), (4, 2, 4), (4, 4, 4)])
+def test_append_row_slices_and_distance_batches(monkeypatch, split, batch, rb):
     """Every slicing of the C rows in the projection (the slices' partial
-    sums are added in slice order, so each slicing has its own fp32 sums)
-    and both distance batch sizes (the same bits) match the oracle; five
-    sequences leave three tokens of the second block of four empty."""
-    cfg = LLAMA8K.with_(name=f"append_split{split}_u{batch}", B=5, T=4096)
+    sums are added in slice order, so each slicing has its own fp32 sums),
+    two or four tokens per projection workgroup, and both distance batch
+    sizes (the same bits) match the oracle; five sequences leave the last
+    block of two or four tokens part empty."""
+    cfg = LLAMA8K.with_(name=f"append_split{split}_u{batch}_rb{rb}", B=5, T=4096)
     monkeypatch.setenv("RKV_APP_SPLIT", str(split))
     monkeypatch.setenv("RKV_APP_DIST_U", str(batch))
+    monkeypatch.setenv("RKV_APP_RB", str(rb))
     _log(f"[case] append {cfg.name}")
     c = _make(cfg, prefill=True)
     rng = np.random.default_rng(split)              # the same positions for both batch sizes
