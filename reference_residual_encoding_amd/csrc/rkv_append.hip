@@ -9,7 +9,7 @@
 // products are bound by reading the weights and the references once):
 //   dist     one workgroup per 8 pool references of a sequence: squared L2
 //            by direct differences, the workgroup's best KL as a list
-//   sel_proj one workgroup per 16 features, slice of the C rows and 4
+//   sel_proj one workgroup per 16 features, slice of the C rows and 2 or 4
 //            tokens: each merges its tokens' lists by (distance, position)
 //            itself, then x W1, x W2, m W1, m W2 over its rows (the mean m of
 //            the chosen references formed in fp32 at the rows it needs),
