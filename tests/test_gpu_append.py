@@ -258,3 +258,22 @@ def test_append_row_slices_and_distance_batches(monkeypatch, split, batch, rb):
         if len(_KNOB_BITS) == 2:
             for a, b in zip(_KNOB_BITS[2], _KNOB_BITS[4]):
                 assert np.array_equal(a, b), "the distance batch sizes gave different records"
+
+
+@pytest.mark.parametrize("B", [1, 3])
+def test_append_with_no_position_is_a_no_op(B):
+    """A call in which no sequence appends (every position -1 or T) writes
+    nothing: records keep their pattern, the cache its rows."""
+    cfg = RAGGED_BF16.with_(name=f"append_none_b{B}", B=B)
+    _log(f"[case] append {cfg.name} no positions")
+    c = _make(cfg, prefill=True)
+    for pos in (np.full(B, -1), np.full(B, cfg.T), np.array([-1, cfg.T, -5][:B])):
+        c.append(pos)
+    torch.cuda.synchronize()
+    assert not c.appended.any()
+    assert (c.codes.cpu().numpy() == SENTINEL).all()
+    assert (c.ref_idx.cpu().numpy().view(np.uint8) == SENTINEL).all()
+    assert (c.scale.cpu().numpy().view(np.uint8) == SENTINEL).all()
+    assert (c.z.cpu().numpy().view(np.uint8) == SENTINEL).all()
+    kv = c.kv.cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(kv, c.expected_kv.view(np.uint16))
