@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define RKV_ABI_VERSION 7
+#define RKV_ABI_VERSION 8
 
 typedef enum {
   RKV_OK = 0,
@@ -313,6 +313,47 @@ rkv_status rkv_append_noalloc(const rkv_params* p, void* kv, const void* kv_new,
                               const void* w3, int32_t* ref_idx, uint8_t* codes,
                               uint16_t* scale, uint16_t* zmin, float* z,
                               hipStream_t stream);
+
+/* Reference projections kept with the cache: ref_proj[b][j][o] =
+ * r_j [W1 | W2][o], o < 2 d_ff (the first d_ff outputs through W1, the
+ * next through W2), fp32, for the j-th stored reference r_j of sequence b
+ * (its stored values: input precision, or the E4M3 values of an FP8
+ * store).  The first layer of f_c is linear, so the projection of the
+ * chosen references' mean is the mean of their projections ([RKV] §2.2 mean
+ * eq., §2.3 f_c): rkv_append_proj reads k_t rows of it instead of
+ * projecting the mean through W1 and W2.  rkv_ref_proj_bytes(p) = B *
+ * n_ref * 2 * d_ff * 4 (n_ref = rkv_reference_positions(p, NULL, 0)).
+ *
+ * rkv_project_refs fills every row from the cache kv (laid out as for
+ * rkv_append; a row whose reference is not stored yet gets whatever its
+ * kv row holds projected); w1, w2 as in rkv_encode.  workspace: at least
+ * rkv_append_proj_workspace_bytes(p) bytes (private, need not be
+ * initialised).  Arithmetic: fp32 on the vector ALUs from the stored
+ * values, each output summed over C in chunks of 512 rows. */
+size_t rkv_ref_proj_bytes(const rkv_params* p);
+size_t rkv_append_proj_workspace_bytes(const rkv_params* p);
+rkv_status rkv_project_refs(const rkv_params* p, const void* kv, const void* w1,
+                            const void* w2, float* ref_proj, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/* rkv_append with the cache's reference projections ref_proj (above): the
+ * same outputs and semantics as rkv_append, and, for a sequence whose new
+ * token is a reference, ref_proj[b][j] written for it (j its index among
+ * the references; from its E4M3 values with an FP8 store).  The mean
+ * branch m [W1 | W2] is the mean of the chosen references' rows of
+ * ref_proj (summed in ascending position, times 1/k_t) in place of the mean
+ * row projected through W1 and W2, so the call runs in two launches: the
+ * distances together with x [W1 | W2], then the selection, delta_h, z =
+ * delta_h W3 and the quantiser.  Rows of ref_proj of references not in a
+ * token's pool are not read.  workspace: at least
+ * rkv_append_proj_workspace_bytes(p) bytes (private, need not be
+ * initialised).  Results agree with rkv_append within fp32 rounding
+ * (the projections are summed in another order). */
+rkv_status rkv_append_proj(const rkv_params* p, void* kv, float* ref_proj,
+                           const void* kv_new, const int32_t* pos, const void* w1,
+                           const void* w2, const void* w3, int32_t* ref_idx,
+                           uint8_t* codes, uint16_t* scale, uint16_t* zmin, float* z,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* The FP8 reference store of a prefix (p->ref_format == RKV_REF_FP8,
  * [RKV] §2.4 last paragraph): ref_store[b][j][c] = E4M3 byte of

@@ -50,13 +50,17 @@ EXPORTS = (
     "rkv_append_workspace_bytes",
     "rkv_append",
     "rkv_append_noalloc",
+    "rkv_ref_proj_bytes",
+    "rkv_append_proj_workspace_bytes",
+    "rkv_project_refs",
+    "rkv_append_proj",
     "rkv_reference_positions",
     "rkv_store_refs",
 )
 
 STAGES = ("pack", "norms", "dist", "merge", "proj", "swiglu", "w3", "quant", "gather", "restore",
           "append", "store")
-RKV_ABI_VERSION = 7
+RKV_ABI_VERSION = 8
 RKV_REF_INPUT = 0
 RKV_REF_FP8 = 1
 
@@ -132,6 +136,14 @@ def lib() -> ctypes.CDLL:
         L.rkv_append.restype = ctypes.c_int
         L.rkv_append_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.rkv_append_noalloc.restype = ctypes.c_int
+        L.rkv_ref_proj_bytes.argtypes = [P]
+        L.rkv_ref_proj_bytes.restype = sz
+        L.rkv_append_proj_workspace_bytes.argtypes = [P]
+        L.rkv_append_proj_workspace_bytes.restype = sz
+        L.rkv_project_refs.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
+        L.rkv_project_refs.restype = ctypes.c_int
+        L.rkv_append_proj.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.rkv_append_proj.restype = ctypes.c_int
         L.rkv_reference_positions.argtypes = [P, vp, i32]
         L.rkv_reference_positions.restype = i32
         L.rkv_store_refs.argtypes = [P, vp, vp, vp]
@@ -434,6 +446,45 @@ def rkv_append_noalloc(p: rkv_params, kv, kv_new, pos, w1, w2, w3, ref_idx, code
         _p(scale, "scale", _HALF, sb), _p(zmin, "zmin", _HALF, sb),
         _p(z, "z", _F32, rows * p.d_c * 4), _s(stream))
     return _check("rkv_append_noalloc", st) if check else st
+
+
+def rkv_ref_proj_bytes(p: rkv_params) -> int:
+    return int(lib().rkv_ref_proj_bytes(ctypes.byref(p)))
+
+
+def rkv_append_proj_workspace_bytes(p: rkv_params) -> int:
+    return int(lib().rkv_append_proj_workspace_bytes(ctypes.byref(p)))
+
+
+def rkv_project_refs(p: rkv_params, kv, w1, w2, ref_proj, workspace, workspace_bytes: int,
+                     stream=None, *, check: bool = True) -> int:
+    dt, es = _elem(p)
+    C = 2 * p.N * p.D
+    st = lib().rkv_project_refs(ctypes.byref(p), _ref_store(p, kv), _p(w1, "w1", dt, C * p.d_ff * es),
+                                _p(w2, "w2", dt, C * p.d_ff * es),
+                                _p(ref_proj, "ref_proj", _F32, rkv_ref_proj_bytes(p)),
+                                _p(workspace, "workspace", None, workspace_bytes),
+                                int(workspace_bytes), _s(stream))
+    return _check("rkv_project_refs", st) if check else st
+
+
+def rkv_append_proj(p: rkv_params, kv, ref_proj, kv_new, pos, w1, w2, w3, ref_idx, codes, scale,
+                    zmin, z, workspace, workspace_bytes: int, stream=None, *,
+                    check: bool = True) -> int:
+    dt, es = _elem(p)
+    C, rows = 2 * p.N * p.D, p.B * p.T
+    cb, sb = _record_sizes(p, rows)
+    st = lib().rkv_append_proj(ctypes.byref(p), _ref_store(p, kv),
+                               _p(ref_proj, "ref_proj", _F32, rkv_ref_proj_bytes(p)),
+                               _p(kv_new, "kv_new", dt, p.B * C * es),
+                               _p(pos, "pos", _I32, p.B * 4), _p(w1, "w1", dt, C * p.d_ff * es),
+                               _p(w2, "w2", dt, C * p.d_ff * es), _p(w3, "w3", dt, p.d_ff * p.d_c * es),
+                               _p(ref_idx, "ref_idx", _I32, rows * p.k * 4), _p(codes, "codes", _U8, cb),
+                               _p(scale, "scale", _HALF, sb), _p(zmin, "zmin", _HALF, sb),
+                               _p(z, "z", _F32, rows * p.d_c * 4),
+                               _p(workspace, "workspace", None, workspace_bytes),
+                               int(workspace_bytes), _s(stream))
+    return _check("rkv_append_proj", st) if check else st
 
 
 def rkv_reference_positions(p: rkv_params):

@@ -532,6 +532,72 @@ rkv_status rkv_append_noalloc(const rkv_params* p, void* kv, const void* kv_new,
   return ok();
 }
 
+size_t rkv_ref_proj_bytes(const rkv_params* p) {
+  if (check_params(p) != RKV_OK) return 0;
+  const rkv::Shape sh = shape_of(p);
+  return size_t(sh.B) * sh.nref * 2 * sh.d_ff * 4;
+}
+
+size_t rkv_append_proj_workspace_bytes(const rkv_params* p) {
+  if (check_params(p) != RKV_OK) return 0;
+  return rkv::plan_append_proj(shape_of(p)).total;
+}
+
+rkv_status rkv_project_refs(const rkv_params* p, const void* kv, const void* w1, const void* w2,
+                            float* ref_proj, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  rkv_status st = check_params(p);
+  if (st != RKV_OK) return st;
+  RKV_NEED_PTR(kv);
+  RKV_NEED_PTR(w1);
+  RKV_NEED_PTR(w2);
+  RKV_NEED_PTR(ref_proj);
+  RKV_NEED_PTR(workspace);
+  const rkv::Shape sh = shape_of(p);
+  const rkv::AppendWorkspace L = rkv::plan_append_proj(sh);
+  if (workspace_bytes < L.total)
+    return fail(RKV_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
+  hipError_t e;
+  RKV_STAGE(RKV_STAGE_APPEND,
+            rkv::launch_project_refs(sh, kv, w1, w2, ref_proj, static_cast<char*>(workspace), L,
+                                     stream),
+            "project_refs");
+  return ok();
+}
+
+rkv_status rkv_append_proj(const rkv_params* p, void* kv, float* ref_proj, const void* kv_new,
+                           const int32_t* pos, const void* w1, const void* w2, const void* w3,
+                           int32_t* ref_idx, uint8_t* codes, uint16_t* scale, uint16_t* zmin,
+                           float* z, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  rkv_status st = check_params(p);
+  if (st != RKV_OK) return st;
+  RKV_NEED_PTR(kv);
+  RKV_NEED_PTR(ref_proj);
+  RKV_NEED_PTR(kv_new);
+  RKV_NEED_PTR(pos);
+  RKV_NEED_PTR(w1);
+  RKV_NEED_PTR(w2);
+  RKV_NEED_PTR(w3);
+  RKV_NEED_PTR(ref_idx);
+  RKV_NEED_PTR(codes);
+  RKV_NEED_GROUP_PTR(scale);
+  RKV_NEED_GROUP_PTR(zmin);
+  RKV_NEED_PTR(workspace);
+  if (z != nullptr && !aligned16(z)) return fail(RKV_ERR_INVALID_ARG, "z is not 16-byte aligned");
+  if (!aligned16(ref_proj)) return fail(RKV_ERR_INVALID_ARG, "ref_proj is not 16-byte aligned");
+  const rkv::Shape sh = shape_of(p);
+  const rkv::AppendWorkspace L = rkv::plan_append_proj(sh);
+  if (workspace_bytes < L.total)
+    return fail(RKV_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
+  hipError_t e;
+  RKV_STAGE(RKV_STAGE_APPEND,
+            rkv::launch_append_proj(sh, kv, ref_proj, kv_new, pos, w1, w2, w3, ref_idx, codes,
+                                    scale, zmin, z, static_cast<char*>(workspace), L, stream),
+            "append_proj");
+  return ok();
+}
+
 rkv_status rkv_store_refs(const rkv_params* p, const void* kv, uint8_t* ref_store,
                           hipStream_t stream) {
   rkv_status st = check_params(p);

@@ -176,14 +176,14 @@ __device__ __forceinline__ int pool_at(const SchedView& v, int t, int T) {
 // before its own by (d, j), and candidates that no list slot would take
 // (past the pool, or d not <= FLT_MAX) leave their slots to padding.
 template <typename E, int KL, bool FP8, int U>
-__global__ __launch_bounds__(256) void k_app_dist(const void* __restrict__ kv,
-                                                  const E* __restrict__ kv_new,
-                                                  const int32_t* __restrict__ pos, SchedView sv,
-                                                  int T, int C, int n_lists,
-                                                  float2* __restrict__ part) {
+__device__ __forceinline__ void dist_block(const void* __restrict__ kv,
+                                           const E* __restrict__ kv_new,
+                                           const int32_t* __restrict__ pos, SchedView sv, int T,
+                                           int C, int n_lists, float2* __restrict__ part,
+                                           int blk) {
   const RefRows<E, FP8> refs{kv, sv, T, C};
   if (sv.nref <= 0) return;                              // no references: no lists
-  const int b = blockIdx.x / n_lists, c = blockIdx.x % n_lists;
+  const int b = blk / n_lists, c = blk % n_lists;
   const int j0 = c * kAppCH;
   __shared__ float dl[kAppCH];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -251,10 +251,19 @@ __global__ __launch_bounds__(256) void k_app_dist(const void* __restrict__ kv,
       rank += (oe && (de < di || (de == di && e < i))) ? 1 : 0;
     }
     const int n_ok = __popcll(__ballot(ok));
-    float2* dst = part + size_t(blockIdx.x) * KL;
+    float2* dst = part + size_t(blk) * KL;
     if (ok && rank < KL) dst[rank] = make_float2(di, __int_as_float(j0 + i));
     if (i >= n_ok && i < KL) dst[i] = make_float2(FLT_MAX, __int_as_float(kNoRef));
   }
+}
+
+template <typename E, int KL, bool FP8, int U>
+__global__ __launch_bounds__(256) void k_app_dist(const void* __restrict__ kv,
+                                                  const E* __restrict__ kv_new,
+                                                  const int32_t* __restrict__ pos, SchedView sv,
+                                                  int T, int C, int n_lists,
+                                                  float2* __restrict__ part) {
+  dist_block<E, KL, FP8, U>(kv, kv_new, pos, sv, T, C, n_lists, part, int(blockIdx.x));
 }
 
 // ---------------------------------------------------------------- select + projection
@@ -267,11 +276,13 @@ __global__ __launch_bounds__(256) void k_app_dist(const void* __restrict__ kv,
 //
 // Selection of sequence b's token by one wave: every lane merges the lists
 // l, l + 64, ... of the ceil(pool/8) lists, then the lanes' lists are merged
-// by a butterfly over the wave; by (distance, position), which orders every
+// by a butterfly over the wave (each a merge of two sorted lists,
+// merge_sorted_lex); by (distance, position), which orders every
 // candidate uniquely, so the kept k_t = min(k, |pool|) ([RKV] §2.1) do not
 // depend on the merge order.  Writes the chosen stored rows (ascending
-// position) to sel[0..KL) and returns k_t; -1 when the token is not encoded
-// (no append this call, or a reference).  With `writer`, also writes
+// position) to sel[0..KL), and their reference indices to selj[0..KL) when
+// selj is given, and returns k_t; -1 when the token is not encoded (no
+// append this call, or a reference).  With `writer`, also writes
 // ref_idx and act[b], and stores a reference token as it is.  `pre()` is
 // called once, right after the first lists are requested (the caller's own
 // loads then queue behind them, not in front).  b must be uniform over the
@@ -281,7 +292,7 @@ __device__ int select_token(void* kv, const E* kv_new, const int32_t* pos, Sched
                             int C, int k, int rec_bytes, int n_groups, int d_c, int n_lists,
                             const float2* part, int32_t* ref_idx, uint8_t* codes, uint16_t* scale,
                             uint16_t* zmin, float* z, int* act, int b, bool writer, int* sel,
-                            Pre pre) {
+                            Pre pre, int* selj = nullptr) {
   const int lane = threadIdx.x & 63;
   const int t = pos[b];
   // The lists' addresses do not depend on the position: the first LU per
@@ -306,7 +317,7 @@ __device__ int select_token(void* kv, const E* kv_new, const int32_t* pos, Sched
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
   if (t < 0 || t >= T) {                                 // not appended this call
-    if (writer && lane == 0) act[b] = 0;
+    if (writer && act && lane == 0) act[b] = 0;
     return -1;
   }
   const size_t row = size_t(b) * T + t;
@@ -343,7 +354,7 @@ __device__ int select_token(void* kv, const E* kv_new, const int32_t* pos, Sched
     }
     if (z)
       for (int i = lane; i < d_c; i += 64) z[row * d_c + i] = 0.0f;
-    if (lane == 0) act[b] = 0;
+    if (act && lane == 0) act[b] = 0;
     return -1;
   }
   const int nch = (pool + kAppCH - 1) / kAppCH;
@@ -355,13 +366,19 @@ __device__ int select_token(void* kv, const E* kv_new, const int32_t* pos, Sched
 #pragma unroll
     for (int u = 0; u < LU; ++u) {
       // a list past the pool's enters as padding, which no slot takes (the
-      // loads are used either way, so none is moved under a branch)
+      // loads are used either way, so none is moved under a branch); each
+      // list is in ascending (d, j) order
       const bool in = l0 + 64 * u < nch;
+      float ld[KL];
+      int li[KL];
 #pragma unroll
       for (int e = 0; e < KL / 2; ++e) {
-        topk_push_lex(bd, bi, in ? w[u][e].x : FLT_MAX, in ? __float_as_int(w[u][e].y) : kNoRef);
-        topk_push_lex(bd, bi, in ? w[u][e].z : FLT_MAX, in ? __float_as_int(w[u][e].w) : kNoRef);
+        ld[2 * e] = in ? w[u][e].x : FLT_MAX;
+        li[2 * e] = in ? __float_as_int(w[u][e].y) : kNoRef;
+        ld[2 * e + 1] = in ? w[u][e].z : FLT_MAX;
+        li[2 * e + 1] = in ? __float_as_int(w[u][e].w) : kNoRef;
       }
+      merge_sorted_lex(bd, bi, ld, li);
     }
   };
   merge(lane);
@@ -375,8 +392,7 @@ __device__ int select_token(void* kv, const E* kv_new, const int32_t* pos, Sched
     int oi[KL];
 #pragma unroll
     for (int e = 0; e < KL; ++e) { od[e] = __shfl_xor(bd[e], off); oi[e] = __shfl_xor(bi[e], off); }
-#pragma unroll
-    for (int e = 0; e < KL; ++e) topk_push_lex(bd, bi, od[e], oi[e]);
+    merge_sorted_lex(bd, bi, od, oi);
   }
   const int kt = min(k, pool);                           // k_t = min(k, |pool|) ([RKV] §2.1)
   int jj[KL];
@@ -394,8 +410,9 @@ __device__ int select_token(void* kv, const E* kv_new, const int32_t* pos, Sched
     for (int e = 0; e < k; ++e) {
       if (writer) ref_idx[row * k + e] = e < kt ? ref_position(sv, jj[e]) : -1;
       if (e < KL) sel[e] = e < kt ? int(refs.row(b, jj[e])) : -1;   // stored row
+      if (selj && e < KL) selj[e] = e < kt ? jj[e] : -1;             // reference index
     }
-    if (writer) act[b] = 1;
+    if (writer && act) act[b] = 1;
   }
   return kt;
 }
@@ -586,76 +603,51 @@ __global__ __launch_bounds__(256) void k_app_sel_proj(
 // ---------------------------------------------------------------- W3 + quantiser
 constexpr int kAppF = 4096;         // delta_h features the W3 kernel holds in LDS at a time
 
-// Workgroup (token b, columns [CB*w, CB*w + CB)), CB = 32 (g <= 32) or 64,
-// over the features in blocks of kAppF: delta_h of the block is formed in
-// LDS from the S slices' partial sums (added in slice order, [RKV] §2.3),
-// the first rows of W3 already in flight; then LPR = CB/8 lanes cover a row
-// of the column block, 8 columns each, and the 256/LPR row groups sum
-// delta_h[f] W3[f][.] over f = rg + (256/LPR) i, 16 rows' loads in flight at
-// a time; the partial rows are reduced in LDS; the first LPR lanes then hold
-// 8 consecutive latents each and run the group quantiser ([RKV] §2.4).
-template <typename E, int BITS, int G8, int CB>
-__global__ __launch_bounds__(256) void k_app_w3(const float* __restrict__ ph, int S,
-                                                const int* __restrict__ act,
-                                                const int32_t* __restrict__ pos,
-                                                const E* __restrict__ w3, int T, int d_ff,
-                                                int d_c, uint8_t* __restrict__ codes,
-                                                uint16_t* __restrict__ scale,
-                                                uint16_t* __restrict__ zmin,
-                                                float* __restrict__ z) {
-  constexpr int LPR = CB / 8, RG = 256 / LPR, UN = 16;
-  const int nblk = d_c / CB;
-  const int b = blockIdx.x / nblk, c0 = (blockIdx.x % nblk) * CB;
-  // no early exit: the loads below go out together with this flag's, and a
-  // token not encoded (a reference, or no append) only has its writes
-  // skipped (its partial sums were not written; they are read in bounds and
-  // their results dropped)
-  const bool live = act[b] == 1;
+// z = delta_h W3 for columns [c0, c0 + CB) of token b, CB = 32 (g <= 32) or
+// 64, then the group quantiser ([RKV] §2.4) and the record, written when
+// `live` (row = b T + pos_of(), read only then and only at the end).  Over
+// the features in blocks of kAppF: produce(fc,
+// nf, dhl) fills dhl[0, nf) with delta_h of features [fc, fc + nf) (every
+// thread takes part; the first rows of W3 of the block are already in
+// flight); then LPR = CB/8 lanes cover a row of the column block, 8 columns
+// each, and the 256/LPR row groups sum delta_h[f] W3[f][.] over f = rg +
+// (256/LPR) i, 16 rows' loads in flight at a time; the partial rows are
+// reduced in LDS; the first LPR lanes then hold 8 consecutive latents each
+// and run the quantiser.
+constexpr int kW3Un = 16;          // W3 rows in flight per thread
+
+// The first block's W3 rows of a thread of w3_quantise, for a caller that
+// requests them early (PRE).
+template <typename E, int CB>
+__device__ __forceinline__ void w3_first_rows(RawW8<E> (&wr)[kW3Un], const E* __restrict__ w3,
+                                              int c0, int d_ff, int d_c) {
+  constexpr int LPR = CB / 8, RG = 256 / LPR;
+  const int tid = threadIdx.x, cg = tid % LPR, rg = tid / LPR;
+  const int nf = min(kAppF, d_ff);
+#pragma unroll
+  for (int u = 0; u < kW3Un; ++u) wr[u].load(w3 + c0 + cg * 8 + size_t(min(rg + RG * u, nf - 1)) * d_c);
+}
+
+template <typename E, int BITS, int G8, int CB, bool PRE, typename Produce, typename PosOf>
+__device__ __forceinline__ void w3_quantise(int b, int c0, bool live, PosOf pos_of, int T, int d_ff,
+                                            int d_c, const E* __restrict__ w3,
+                                            uint8_t* __restrict__ codes,
+                                            uint16_t* __restrict__ scale,
+                                            uint16_t* __restrict__ zmin, float* __restrict__ z,
+                                            Produce produce, RawW8<E> (&wr)[kW3Un]) {
+  constexpr int LPR = CB / 8, RG = 256 / LPR, UN = kW3Un;
   const int tid = threadIdx.x, cg = tid % LPR, rg = tid / LPR;
   __shared__ float red[RG * (CB + 1)];
   __shared__ float zl[CB];
   __shared__ float dhl[kAppF];
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  const float* phb = ph + size_t(b) * S * 4 * d_ff;
   const E* wcol = w3 + c0 + cg * 8;
   for (int fc = 0; fc < d_ff; fc += kAppF) {
     const int nf = min(kAppF, d_ff - fc);                // a multiple of 16
-    RawW8<E> wr[UN];
+    if (!PRE || fc > 0)                                  // (PRE: the first block's came in wr)
 #pragma unroll
-    for (int u = 0; u < UN; ++u) wr[u].load(wcol + size_t(fc + min(rg + RG * u, nf - 1)) * d_c);
-    for (int f = tid * 4; f < nf; f += 256 * 4) {
-      // four slices' loads in flight at once, added in slice order (a
-      // slice past the last re-reads the last and is not added)
-      float4 a[4];
-      auto batch = [&](int s0) {
-        float4 t[4][4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            t[j][v] = *reinterpret_cast<const float4*>(
-                phb + size_t(4 * min(s0 + j, S - 1) + v) * d_ff + fc + f);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bool first = s0 + j == 0, add = s0 + j > 0 && s0 + j < S;
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            a[v].x = first ? t[j][v].x : (add ? a[v].x + t[j][v].x : a[v].x);
-            a[v].y = first ? t[j][v].y : (add ? a[v].y + t[j][v].y : a[v].y);
-            a[v].z = first ? t[j][v].z : (add ? a[v].z + t[j][v].z : a[v].z);
-            a[v].w = first ? t[j][v].w : (add ? a[v].w + t[j][v].w : a[v].w);
-          }
-        }
-      };
-      batch(0);
-      for (int s0 = 4; s0 < S; s0 += 4) batch(s0);
-      float4 o;
-      o.x = silu(a[0].x) * a[1].x - silu(a[2].x) * a[3].x;
-      o.y = silu(a[0].y) * a[1].y - silu(a[2].y) * a[3].y;
-      o.z = silu(a[0].z) * a[1].z - silu(a[2].z) * a[3].z;
-      o.w = silu(a[0].w) * a[1].w - silu(a[2].w) * a[3].w;
-      *reinterpret_cast<float4*>(dhl + f) = o;
-    }
+      for (int u = 0; u < UN; ++u) wr[u].load(wcol + size_t(fc + min(rg + RG * u, nf - 1)) * d_c);
+    produce(fc, nf, dhl);
     __syncthreads();
     for (int f1 = rg; f1 < nf; f1 += RG * UN) {
       if (f1 != rg)
@@ -685,7 +677,7 @@ __global__ __launch_bounds__(256) void k_app_w3(const float* __restrict__ ph, in
     float v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = tid < LPR ? zl[min(tid, LPR - 1) * 8 + e] : 0.0f;
-    const size_t row = size_t(b) * T + (live ? pos[b] : 0);
+    const size_t row = size_t(b) * T + (live ? pos_of() : 0);
     const int64_t unit = int64_t(row) * (d_c / 8) + c0 / 8 + tid;
     write_record8<BITS, G8>(v, live && tid < LPR, tid, unit, codes, scale, zmin);
     if (live && tid < LPR) {
@@ -696,6 +688,330 @@ __global__ __launch_bounds__(256) void k_app_w3(const float* __restrict__ ph, in
       }
     }
   }
+}
+
+// Workgroup (token b, columns [CB*w, CB*w + CB)): delta_h of each block of
+// features formed in LDS from the S slices' partial sums (added in slice
+// order, [RKV] §2.3), then w3_quantise.  No early exit: the loads go out
+// together with the act flag's, and a token not encoded (a reference, or no
+// append) only has its writes skipped (its partial sums were not written;
+// they are read in bounds and their results dropped).
+template <typename E, int BITS, int G8, int CB>
+__global__ __launch_bounds__(256) void k_app_w3(const float* __restrict__ ph, int S,
+                                                const int* __restrict__ act,
+                                                const int32_t* __restrict__ pos,
+                                                const E* __restrict__ w3, int T, int d_ff,
+                                                int d_c, uint8_t* __restrict__ codes,
+                                                uint16_t* __restrict__ scale,
+                                                uint16_t* __restrict__ zmin,
+                                                float* __restrict__ z) {
+  const int nblk = d_c / CB;
+  const int b = blockIdx.x / nblk, c0 = (blockIdx.x % nblk) * CB;
+  const bool live = act[b] == 1;
+  const float* phb = ph + size_t(b) * S * 4 * d_ff;
+  auto produce = [&](int fc, int nf, float* dhl) {
+    for (int f = threadIdx.x * 4; f < nf; f += 256 * 4) {
+      // four slices' loads in flight at once, added in slice order (a
+      // slice past the last re-reads the last and is not added)
+      float4 a[4];
+      auto batch = [&](int s0) {
+        float4 t4[4][4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            t4[j][v] = *reinterpret_cast<const float4*>(
+                phb + size_t(4 * min(s0 + j, S - 1) + v) * d_ff + fc + f);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bool first = s0 + j == 0, add = s0 + j > 0 && s0 + j < S;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            a[v].x = first ? t4[j][v].x : (add ? a[v].x + t4[j][v].x : a[v].x);
+            a[v].y = first ? t4[j][v].y : (add ? a[v].y + t4[j][v].y : a[v].y);
+            a[v].z = first ? t4[j][v].z : (add ? a[v].z + t4[j][v].z : a[v].z);
+            a[v].w = first ? t4[j][v].w : (add ? a[v].w + t4[j][v].w : a[v].w);
+          }
+        }
+      };
+      batch(0);
+      for (int s0 = 4; s0 < S; s0 += 4) batch(s0);
+      float4 o;
+      o.x = silu(a[0].x) * a[1].x - silu(a[2].x) * a[3].x;
+      o.y = silu(a[0].y) * a[1].y - silu(a[2].y) * a[3].y;
+      o.z = silu(a[0].z) * a[1].z - silu(a[2].z) * a[3].z;
+      o.w = silu(a[0].w) * a[1].w - silu(a[2].w) * a[3].w;
+      *reinterpret_cast<float4*>(dhl + f) = o;
+    }
+  };
+  RawW8<E> wr[kW3Un];
+  w3_quantise<E, BITS, G8, CB, false>(b, c0, live, [&]() { return pos[b]; }, T, d_ff, d_c, w3,
+                                      codes, scale, zmin, z, produce, wr);
+}
+
+// ---------------------------------------------------------------- projections of rows
+// Rows of the reference-projection path: out[(v * S + sl) * 2 d_ff + o] =
+// sum over the C rows c of slice sl's 512-row chunks (sl, sl + S, ...) of
+// vec_v[c] [W1 | W2][c][o] in fp32, for the RB row vectors v0 .. v0 + RB - 1
+// and the 16 outputs o of block ob of [W1 | W2] (a block lies in W1 or in W2:
+// d_ff is a multiple of 16).  Workgroup blk = ob + (2 d_ff / 16) (sl + S
+// (v0 / RB)), the output block fastest.  Four consecutive lanes cover the
+// block's 16 outputs of a row of W (32 contiguous bytes at bf16); the 64 row
+// groups take 8 consecutive rows each of a chunk; the first chunk's W is
+// requested first and each next chunk's while the current one is
+// multiplied; four vectors' rows are requested together.  The 64 row
+// groups' partial sums are added through LDS in a fixed order.  `vecs`
+// gives, for local vector r: valid(r), load(r, c, raw) (8 values at row c,
+// in bounds whatever r) and decode(r, raw, v).
+template <typename E, int RB, typename Vecs>
+__device__ __forceinline__ void proj_block(const E* __restrict__ w1, const E* __restrict__ w2,
+                                           int C, int d_ff, int S, int blk, const Vecs vecs,
+                                           float* __restrict__ out) {
+  constexpr int NV = RB * 4, RPT = 8, RG = 64, CH = RG * RPT, TB = 4;
+  static_assert(RB % TB == 0, "vectors in batches of four");
+  const int nob = 2 * d_ff / 16;
+  const int ob = blk % nob, sl = (blk / nob) % S, v0 = (blk / (nob * S)) * RB;
+  const int tid = threadIdx.x, fq = tid & 3, rg = tid >> 2;
+  const int o0 = ob * 16 + fq * 4;                       // this lane's 4 outputs
+  const E* w = o0 < d_ff ? w1 + o0 : w2 + (o0 - d_ff);
+  __shared__ float red[NV * (256 + 1)];
+  static_assert(RB <= 32, "one bit per vector");
+  uint32_t vmask = 0;                                    // bit r: vector r is valid
+#pragma unroll
+  for (int r = 0; r < RB; ++r) vmask |= vecs.valid(r) ? 1u << r : 0u;
+  if (vmask == 0) return;                                // uniform over the workgroup
+  float acc[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) acc[v] = 0.0f;
+  const int c1_first = min(sl * CH + rg * RPT, C - RPT);
+  RawW4<E> wa[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) wa[i].load(w + size_t(c1_first + i) * d_ff);
+  for (int c0 = sl * CH; c0 < C; c0 += S * CH) {
+    const int c1 = c0 + rg * RPT;
+    const bool in = c1 < C;                              // C is a multiple of 8
+    const int cb = in ? c1 : 0;
+    float a[RPT][4];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) wa[i].decode(a[i]);
+    if (c0 + S * CH < C) {                               // uniform: the next chunk's W
+      const int cn = min(c1 + S * CH, C - RPT);
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) wa[i].load(w + size_t(cn + i) * d_ff);
+    }
+#pragma unroll
+    for (int r0 = 0; r0 < RB; r0 += TB) {
+      typename Vecs::Raw raw[TB];
+#pragma unroll
+      for (int u = 0; u < TB; ++u) vecs.load(r0 + u, cb, raw[u]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < TB; ++u) {
+        const int r = r0 + u;
+        if (!((vmask >> r) & 1u) || !in) continue;       // uniform per workgroup
+        float xv[RPT];
+        vecs.decode(r, raw[u], xv);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i)
+#pragma unroll
+          for (int f = 0; f < 4; ++f) acc[r * 4 + f] = fmaf(xv[i], a[i][f], acc[r * 4 + f]);
+      }
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < NV; ++v) red[v * 257 + tid] = acc[v];
+  __syncthreads();
+  const int n2 = 2 * d_ff;
+  for (int i = tid; i < 4 * NV; i += 256) {
+    // value v (vector v / 4, output v % 4 of a lane) of the lanes with
+    // fq == q, summed over the 64 row groups in order
+    const int q = i & 3, v = i >> 2, r = v >> 2, f = v & 3;
+    float sum = 0.0f;
+    for (int g = 0; g < RG; ++g) sum += red[v * 257 + g * 4 + q];
+    if ((vmask >> r) & 1u) out[(size_t(v0 + r) * S + sl) * n2 + ob * 16 + q * 4 + f] = sum;
+  }
+}
+
+// The appended tokens as row vectors: token b0 + r, valid when its position
+// is in [0, T); a token whose position is a reference of an FP8 store
+// enters with its E4M3 values (the values the store will hold).
+template <typename E, int RB, bool FP8>
+struct NewTokenVecs {
+  using Raw = RawW8<E>;
+  const E* kv_new;
+  int C, B, b0;
+  int st[RB];                                            // 0 not appended, 1 encoded, 2 reference
+  __device__ bool valid(int r) const { return st[r] != 0; }
+  __device__ void load(int r, int c, Raw& raw) const {
+    raw.load(kv_new + size_t(min(b0 + r, B - 1)) * C + c);
+  }
+  __device__ void decode(int r, const Raw& raw, float (&v)[8]) const {
+    raw.decode(v);
+    if constexpr (FP8)
+      if (st[r] == 2)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = fp8_round(v[e]);
+  }
+};
+
+// The stored references as row vectors: vector v0 + r = reference j of
+// sequence b, v = b nref + j, valid below B nref.
+template <typename E, int RB, bool FP8>
+struct StoredRefVecs {
+  using Raw = typename RefRows<E, FP8>::Raw;
+  RefRows<E, FP8> refs;
+  int nref, n_vec, v0;
+  __device__ bool valid(int r) const { return v0 + r < n_vec; }
+  __device__ void load(int r, int c, Raw& raw) const {
+    const int v = min(v0 + r, n_vec - 1);
+    refs.load_raw(refs.row(v / nref, v % nref), c, raw);
+  }
+  __device__ void decode(int, const Raw& raw, float (&v)[8]) const { raw.decode(v); }
+};
+
+// P[b][j] = r_j [W1 | W2] for every reference the cache holds (rkv_project_refs).
+template <typename E, bool FP8>
+__global__ __launch_bounds__(256) void k_ref_proj(const void* __restrict__ kv, SchedView sv,
+                                                  int T, int C, int B,
+                                                  const E* __restrict__ w1,
+                                                  const E* __restrict__ w2, int d_ff,
+                                                  float* __restrict__ ref_proj) {
+  constexpr int RB = 16;
+  const int nob = 2 * d_ff / 16;
+  StoredRefVecs<E, RB, FP8> vecs{RefRows<E, FP8>{kv, sv, T, C}, sv.nref, B * sv.nref,
+                                 int(blockIdx.x / nob) * RB};
+  proj_block<E, RB>(w1, w2, C, d_ff, 1, int(blockIdx.x), vecs, ref_proj);
+}
+
+// The first launch of the append with reference projections: workgroups
+// below n_dist are the distance workgroups; the rest project the appended
+// tokens: px[b][sl][.] = the slice's partial sums of x [W1 | W2].
+template <typename E, int KL, bool FP8, int U, int RB>
+__global__ __launch_bounds__(256) void k_app_dist_xproj(
+    const void* __restrict__ kv, const E* __restrict__ kv_new, const int32_t* __restrict__ pos,
+    SchedView sv, int T, int C, int n_lists, float2* __restrict__ part, int n_dist,
+    const E* __restrict__ w1, const E* __restrict__ w2, int d_ff, int S, int B,
+    float* __restrict__ px) {
+  const int blk = int(blockIdx.x);
+  if (blk < n_dist) {
+    dist_block<E, KL, FP8, U>(kv, kv_new, pos, sv, T, C, n_lists, part, blk);
+    return;
+  }
+  const int w = blk - n_dist, nob = 2 * d_ff / 16;
+  NewTokenVecs<E, RB, FP8> vecs{kv_new, C, B, (w / (nob * S)) * RB, {}};
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    const int b = vecs.b0 + r;
+    int st = 0;
+    if (b < B) {
+      const int t = pos[b];
+      if (t >= 0 && t < T) {
+        bool is_ref;
+        (void)refs_before(sv, t, is_ref);
+        st = is_ref ? 2 : 1;
+      }
+    }
+    vecs.st[r] = st;
+  }
+  proj_block<E, RB>(w1, w2, C, d_ff, S, w, vecs, px);
+}
+
+// The second launch of the append with reference projections.  Workgroup
+// (token b, columns [CB w, CB w + CB)): its first wave chooses the token's
+// references from the distance lists (select_token; the workgroup of the
+// first column block writes ref_idx, and stores a reference token in the
+// cache with a zero record and its row of P, the sum of its slices'
+// partial projections in slice order).  For an encoded token, delta_h =
+// Swish(x W1) (x W2) - Swish(m W1) (m W2) ([RKV] §2.3), with x [W1 | W2]
+// from the slices' partial sums (in slice order) and m [W1 | W2] the mean of
+// the chosen references' rows of P (the first layer of f_c is linear, so
+// the projection of their mean is the mean of their projections, [RKV] §2.2
+// mean eq.; summed in order, times 1/k_t); then w3_quantise.
+template <typename E, int KL, bool FP8, int BITS, int G8, int CB>
+__global__ __launch_bounds__(256) void k_app_sel_w3(
+    void* __restrict__ kv, const E* __restrict__ kv_new, const int32_t* __restrict__ pos,
+    SchedView sv, int T, int C, int k, int rec_bytes, int n_groups, int d_c, int n_lists,
+    const float2* __restrict__ part, int32_t* __restrict__ ref_idx, uint8_t* __restrict__ codes,
+    uint16_t* __restrict__ scale, uint16_t* __restrict__ zmin, float* __restrict__ z,
+    const float* __restrict__ px, int S, float* __restrict__ ref_proj,
+    const E* __restrict__ w3, int d_ff) {
+  const int nblk = d_c / CB;
+  const int b = int(blockIdx.x) / nblk, c0 = (int(blockIdx.x) % nblk) * CB;
+  const bool writer = c0 == 0;
+  const int tid = threadIdx.x, n2 = 2 * d_ff;
+  __shared__ int sel_l[KL], selj_l[KL];
+  __shared__ int kt_l;
+  // the first block's W3 rows do not depend on the selection: requested
+  // during it (by the selecting wave right after its lists)
+  RawW8<E> wr[kW3Un];
+  auto pre = [&]() { w3_first_rows<E, CB>(wr, w3, c0, d_ff, d_c); };
+  if (tid < 64) {
+    const int bb = __builtin_amdgcn_readfirstlane(b);
+    const int kt = select_token<E, KL, FP8>(kv, kv_new, pos, sv, T, C, k, rec_bytes, n_groups,
+                                            d_c, n_lists, part, ref_idx, codes, scale, zmin, z,
+                                            nullptr, bb, writer, sel_l, pre, selj_l);
+    if (tid == 0) kt_l = kt;
+  } else {
+    pre();
+  }
+  __syncthreads();
+  const int kt = kt_l;
+  const float* pxb = px + size_t(b) * S * n2;
+  if (kt <= 0) {                                         // not encoded
+    if (writer) {
+      const int t = pos[b];
+      if (t >= 0 && t < T) {
+        bool is_ref;
+        const int j = refs_before(sv, t, is_ref);
+        if (is_ref)                                      // its row of P
+          for (int o = tid; o < n2; o += 256) {
+            float sum = pxb[o];
+            for (int s = 1; s < S; ++s) sum += pxb[size_t(s) * n2 + o];
+            ref_proj[(size_t(b) * sv.nref + j) * n2 + o] = sum;
+          }
+      }
+    }
+    return;
+  }
+  const float inv = 1.0f / float(kt);
+  int jr[KL];
+#pragma unroll
+  for (int i = 0; i < KL; ++i) jr[i] = max(selj_l[min(i, kt - 1)], 0);
+  const float* pb = ref_proj + size_t(b) * sv.nref * n2;
+  auto ld4 = [](const float* p) { return *reinterpret_cast<const float4*>(p); };
+  auto add4 = [](float4& a, const float4& t) { a.x += t.x; a.y += t.y; a.z += t.z; a.w += t.w; };
+  auto produce = [&](int fc, int nf, float* dhl) {
+    for (int f = tid * 4; f < nf; f += 256 * 4) {
+      // every load of the 4 features in flight together: the chosen
+      // references' rows of P, then the slices' partial sums
+      float4 pa[KL], pm[KL];
+#pragma unroll
+      for (int i = 0; i < KL; ++i) {
+        pa[i] = ld4(pb + size_t(jr[i]) * n2 + fc + f);
+        pm[i] = ld4(pb + size_t(jr[i]) * n2 + d_ff + fc + f);
+      }
+      float4 xa = ld4(pxb + fc + f), xb = ld4(pxb + d_ff + fc + f);
+      for (int s = 1; s < S; ++s) {
+        add4(xa, ld4(pxb + size_t(s) * n2 + fc + f));
+        add4(xb, ld4(pxb + size_t(s) * n2 + d_ff + fc + f));
+      }
+      float4 ma = pa[0], mb = pm[0];
+#pragma unroll
+      for (int i = 1; i < KL; ++i)
+        if (i < kt) {
+          add4(ma, pa[i]);
+          add4(mb, pm[i]);
+        }
+      float4 o;
+      o.x = silu(xa.x) * xb.x - silu(ma.x * inv) * (mb.x * inv);
+      o.y = silu(xa.y) * xb.y - silu(ma.y * inv) * (mb.y * inv);
+      o.z = silu(xa.z) * xb.z - silu(ma.z * inv) * (mb.z * inv);
+      o.w = silu(xa.w) * xb.w - silu(ma.w * inv) * (mb.w * inv);
+      *reinterpret_cast<float4*>(dhl + f) = o;
+    }
+  };
+  w3_quantise<E, BITS, G8, CB, true>(b, c0, true, [&]() { return pos[b]; }, T, d_ff, d_c, w3,
+                                     codes, scale, zmin, z, produce, wr);
 }
 
 }  // namespace
@@ -848,6 +1164,133 @@ hipError_t launch_append(const Shape& sh, void* kv, const void* kv_new, const in
   }
 #undef RKV_W3G
 #undef RKV_W3
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- with reference projections
+// Slices of the C rows in the token projection of the first launch: about
+// 512 projection workgroups where the output blocks and token blocks alone
+// give fewer, at most one 512-row chunk each (RKV_APP_SPLIT=n forces n, as
+// for rkv_append).
+static int append_proj_split(const Shape& sh) {
+  const int chunks = cdiv(sh.C, 512);
+  int s = std::max(1, cdiv(512, 2 * sh.d_ff / 16 * cdiv(sh.B, 4)));
+  if (const char* force = std::getenv("RKV_APP_SPLIT")) s = std::atoi(force);
+  return std::min(std::max(s, 1), chunks);
+}
+
+AppendWorkspace plan_append_proj(const Shape& sh) {
+  AppendWorkspace L{};
+  L.n_lists = cdiv(std::max(sh.nref, 1), kAppCH);
+  L.n_split = append_proj_split(sh);
+  L.rb = 4;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off += align256(bytes); return at; };
+  L.rpos = take(size_t(sh.nref) * 4);
+  L.part = take(size_t(sh.B) * L.n_lists * sh.kl * 8);
+  L.ph = take(size_t(sh.B) * L.n_split * 2 * sh.d_ff * 4);   // x [W1 | W2] partial sums
+  L.act = take(0);
+  L.total = std::max<size_t>(off, 256);
+  return L;
+}
+
+static hipError_t sched_view(const Shape& sh, char* ws, const AppendWorkspace& L, hipStream_t st,
+                             SchedView& sv) {
+  sv = SchedView{nullptr, sh.nref, sh.s, sh.n_sink};
+  if (sh.alpha != 0.0) {
+    int* rpos = reinterpret_cast<int*>(ws + L.rpos);
+    const hipError_t e = launch_ref_positions(sh, rpos, st);
+    if (e != hipSuccess) return e;
+    sv.rpos = rpos;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_project_refs(const Shape& sh, const void* kv, const void* w1, const void* w2,
+                               float* ref_proj, char* ws, const AppendWorkspace& L,
+                               hipStream_t st) {
+  if (sh.nref == 0) return hipGetLastError();
+  SchedView sv;
+  const hipError_t e = sched_view(sh, ws, L, st, sv);
+  if (e != hipSuccess) return e;
+  const int grid = 2 * sh.d_ff / 16 * cdiv(long(sh.B) * sh.nref, 16);
+#define RKV_RP(E, F8)                                                                             \
+  k_ref_proj<E, F8><<<grid, 256, 0, st>>>(kv, sv, sh.T, sh.C, sh.B, static_cast<const E*>(w1),    \
+                                          static_cast<const E*>(w2), sh.d_ff, ref_proj)
+  if (sh.bf16) {
+    if (sh.ref_fp8) RKV_RP(uint16_t, true); else RKV_RP(uint16_t, false);
+  } else {
+    if (sh.ref_fp8) RKV_RP(float, true); else RKV_RP(float, false);
+  }
+#undef RKV_RP
+  return hipGetLastError();
+}
+
+hipError_t launch_append_proj(const Shape& sh, void* kv, float* ref_proj, const void* kv_new,
+                              const int32_t* pos, const void* w1, const void* w2, const void* w3,
+                              int32_t* ref_idx, uint8_t* codes, uint16_t* scale, uint16_t* zmin,
+                              float* z, char* ws, const AppendWorkspace& L, hipStream_t st) {
+  SchedView sv;
+  hipError_t e = sched_view(sh, ws, L, st, sv);
+  if (e != hipSuccess) return e;
+  auto* part = reinterpret_cast<float2*>(ws + L.part);
+  auto* px = reinterpret_cast<float*>(ws + L.ph);
+  const int rec_bytes = sh.d_c * sh.b / 8;
+  const int n_groups = sh.b == kIdentityBits ? 0 : sh.d_c / sh.g;
+  const int n_dist = sh.B * L.n_lists;
+  const int n_xp = 2 * sh.d_ff / 16 * L.n_split * cdiv(sh.B, 4);
+  int dist_u = n_dist <= 512 ? 4 : 2;                    // as in rkv_append
+  if (const char* force = std::getenv("RKV_APP_DIST_U")) dist_u = std::atoi(force) == 4 ? 4 : 2;
+#define RKV_A1(E, KL, F8)                                                                        \
+  if (dist_u == 4)                                                                               \
+    k_app_dist_xproj<E, KL, F8, 4, 4><<<n_dist + n_xp, 256, 0, st>>>(                            \
+        kv, static_cast<const E*>(kv_new), pos, sv, sh.T, sh.C, L.n_lists, part, n_dist,        \
+        static_cast<const E*>(w1), static_cast<const E*>(w2), sh.d_ff, L.n_split, sh.B, px);    \
+  else                                                                                           \
+    k_app_dist_xproj<E, KL, F8, 2, 4><<<n_dist + n_xp, 256, 0, st>>>(                            \
+        kv, static_cast<const E*>(kv_new), pos, sv, sh.T, sh.C, L.n_lists, part, n_dist,        \
+        static_cast<const E*>(w1), static_cast<const E*>(w2), sh.d_ff, L.n_split, sh.B, px)
+#define RKV_A1K(E, F8) \
+  if (sh.kl == 4) { RKV_A1(E, 4, F8); } else { RKV_A1(E, 8, F8); }
+  if (sh.bf16) {
+    if (sh.ref_fp8) { RKV_A1K(uint16_t, true) } else { RKV_A1K(uint16_t, false) }
+  } else {
+    if (sh.ref_fp8) { RKV_A1K(float, true) } else { RKV_A1K(float, false) }
+  }
+#undef RKV_A1K
+#undef RKV_A1
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  // a workgroup's columns hold whole groups: 64 for g = 64, else 32
+  const int cb = sh.g <= 32 || sh.b == kIdentityBits ? 32 : 64;
+  const int n_w3 = sh.B * (sh.d_c / cb);
+#define RKV_A2(E, KL, F8, BITS, G8)                                                              \
+  k_app_sel_w3<E, KL, F8, BITS, G8, (G8 == 8 ? 64 : 32)><<<n_w3, 256, 0, st>>>(                  \
+      kv, static_cast<const E*>(kv_new), pos, sv, sh.T, sh.C, sh.k, rec_bytes, n_groups, sh.d_c, \
+      L.n_lists, part, ref_idx, codes, scale, zmin, z, px, L.n_split, ref_proj,                  \
+      static_cast<const E*>(w3), sh.d_ff)
+#define RKV_A2G(E, KL, F8, BITS)            \
+  switch (sh.g) {                           \
+    case 8: RKV_A2(E, KL, F8, BITS, 1); break;  \
+    case 16: RKV_A2(E, KL, F8, BITS, 2); break; \
+    case 32: RKV_A2(E, KL, F8, BITS, 4); break; \
+    default: RKV_A2(E, KL, F8, BITS, 8); break; \
+  }
+#define RKV_A2B(E, KL, F8)                                                              \
+  if (sh.b == 4) { RKV_A2G(E, KL, F8, 4) } else if (sh.b == 2) { RKV_A2G(E, KL, F8, 2) } \
+  else { RKV_A2(E, KL, F8, kIdentityBits, 1); }
+#define RKV_A2K(E, F8) \
+  if (sh.kl == 4) { RKV_A2B(E, 4, F8) } else { RKV_A2B(E, 8, F8) }
+  if (sh.bf16) {
+    if (sh.ref_fp8) { RKV_A2K(uint16_t, true) } else { RKV_A2K(uint16_t, false) }
+  } else {
+    if (sh.ref_fp8) { RKV_A2K(float, true) } else { RKV_A2K(float, false) }
+  }
+#undef RKV_A2K
+#undef RKV_A2B
+#undef RKV_A2G
+#undef RKV_A2
   return hipGetLastError();
 }
 

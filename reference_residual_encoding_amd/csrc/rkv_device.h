@@ -147,4 +147,36 @@ __device__ __forceinline__ void topk_push_lex(float (&bd)[KL], int (&bi)[KL], fl
   }
 }
 
+// The KL smallest (d, j) pairs of two lists each in ascending (d, j) order,
+// in ascending order, into (ad, ai): the elementwise lexicographic minima of
+// a and of b reversed form a bitonic sequence that holds them, which the
+// half-cleaners of a bitonic sort then order (KL a power of two).  Gives
+// the same list as pushing b's pairs into a with topk_push_lex.
+template <int KL>
+__device__ __forceinline__ void merge_sorted_lex(float (&ad)[KL], int (&ai)[KL],
+                                                 const float (&bd)[KL], const int (&bi)[KL]) {
+  static_assert((KL & (KL - 1)) == 0, "a power of two");
+  auto less = [](float d, int j, float d2, int j2) { return (d < d2) | ((d == d2) & (j < j2)); };
+#pragma unroll
+  for (int i = 0; i < KL; ++i) {
+    const float d2 = bd[KL - 1 - i];
+    const int j2 = bi[KL - 1 - i];
+    const bool t = less(d2, j2, ad[i], ai[i]);
+    ad[i] = t ? d2 : ad[i];
+    ai[i] = t ? j2 : ai[i];
+  }
+#pragma unroll
+  for (int h = KL / 2; h >= 1; h >>= 1)
+#pragma unroll
+    for (int i = 0; i < KL; ++i)
+      if ((i & h) == 0) {
+        const int q = i + h;
+        const bool t = less(ad[q], ai[q], ad[i], ai[i]);
+        const float dl = t ? ad[q] : ad[i], dh = t ? ad[i] : ad[q];
+        const int jl = t ? ai[q] : ai[i], jh = t ? ai[i] : ai[q];
+        ad[i] = dl; ai[i] = jl;
+        ad[q] = dh; ai[q] = jh;
+      }
+}
+
 }  // namespace rkv

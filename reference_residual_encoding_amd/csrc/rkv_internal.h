@@ -139,5 +139,17 @@ hipError_t launch_append(const Shape& sh, void* kv, const void* kv_new, const in
                          const void* w1, const void* w2, const void* w3, int32_t* ref_idx,
                          uint8_t* codes, uint16_t* scale, uint16_t* zmin, float* z, char* ws,
                          const AppendWorkspace& L, hipStream_t st);
+// The append with reference projections: P[b][j] = r_j [W1 | W2] kept with
+// the cache (rkv_project_refs fills it, the append extends it).  Its
+// workspace (ph holds the tokens' partial projections) also serves
+// rkv_project_refs.
+AppendWorkspace plan_append_proj(const Shape& sh);
+hipError_t launch_project_refs(const Shape& sh, const void* kv, const void* w1, const void* w2,
+                               float* ref_proj, char* ws, const AppendWorkspace& L,
+                               hipStream_t st);
+hipError_t launch_append_proj(const Shape& sh, void* kv, float* ref_proj, const void* kv_new,
+                              const int32_t* pos, const void* w1, const void* w2, const void* w3,
+                              int32_t* ref_idx, uint8_t* codes, uint16_t* scale, uint16_t* zmin,
+                              float* z, char* ws, const AppendWorkspace& L, hipStream_t st);
 
 }  // namespace rkv

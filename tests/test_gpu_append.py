@@ -28,9 +28,11 @@ def _log(msg):
 class Cache:
     """Device cache of one configuration: kv rows + records, in the
     layouts of include/rkv.h.  Non-reference kv rows hold NaN, and so do
-    the reference rows unless prefill_refs."""
+    the reference rows unless prefill_refs.  With proj, the cache also keeps
+    the references' projections (rkv_project_refs after the prefill) and
+    appends through rkv_append_proj."""
 
-    def __init__(self, w, prefill_refs: bool, device="cuda"):
+    def __init__(self, w, prefill_refs: bool, device="cuda", proj: bool = False):
         cfg = self.cfg = w.cfg
         self.w = w
         self.p = P.params_of(cfg)
@@ -60,9 +62,20 @@ class Cache:
         self.scale = u8(n * ng * 2).view(torch.float16).view(cfg.B, cfg.T, -1)
         self.zmin = u8(n * ng * 2).view(torch.float16).view(cfg.B, cfg.T, -1)
         self.z = u8(n * cfg.d_c * 4).view(torch.float32).view(cfg.B, cfg.T, cfg.d_c)
-        self.ws_bytes = R.rkv_append_workspace_bytes(self.p)
+        self.proj = proj
+        if proj:
+            self.ws_bytes = R.rkv_append_proj_workspace_bytes(self.p)
+            nbytes = R.rkv_ref_proj_bytes(self.p)
+            assert nbytes == cfg.B * len(R.rkv_reference_positions(self.p)) * 2 * cfg.d_ff * 4
+            self.ref_proj = torch.full((max(nbytes // 4, 1),), float("nan"), dtype=torch.float32,
+                                       device=device)
+        else:
+            self.ws_bytes = R.rkv_append_workspace_bytes(self.p)
         assert self.ws_bytes > 0
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        if proj and prefill_refs:
+            R.rkv_project_refs(self.p, self.kv, self.w1, self.w2, self.ref_proj, self.ws,
+                               self.ws_bytes, torch.cuda.current_stream())
         self.appended = np.zeros((cfg.B, cfg.T), bool)
 
     def append(self, pos):
@@ -81,9 +94,14 @@ class Cache:
                     self.expected_kv[b, t] = self.w.kv[b, t]
         kv_new = P.to_device(rows, cfg.dtype)
         d_pos = torch.from_numpy(pos.astype(np.int32)).cuda()
-        R.rkv_append(self.p, self.kv, kv_new, d_pos, self.w1, self.w2, self.w3, self.ref_idx,
-                     self.codes, self.scale, self.zmin, self.z, self.ws, self.ws_bytes,
-                     torch.cuda.current_stream())
+        if self.proj:
+            R.rkv_append_proj(self.p, self.kv, self.ref_proj, kv_new, d_pos, self.w1, self.w2,
+                              self.w3, self.ref_idx, self.codes, self.scale, self.zmin, self.z,
+                              self.ws, self.ws_bytes, torch.cuda.current_stream())
+        else:
+            R.rkv_append(self.p, self.kv, kv_new, d_pos, self.w1, self.w2, self.w3, self.ref_idx,
+                         self.codes, self.scale, self.zmin, self.z, self.ws, self.ws_bytes,
+                         torch.cuda.current_stream())
 
     def check(self, name):
         """Parity of every appended row; untouched records keep the pattern;
@@ -109,18 +127,24 @@ class Cache:
         return summary
 
 
-def _make(cfg, prefill):
-    return Cache(generate(cfg), prefill)
+def _make(cfg, prefill, proj=False):
+    return Cache(generate(cfg), prefill, proj=proj)
+
+
+PROJ = pytest.mark.parametrize("proj", [False, True], ids=["append", "append_proj"])
 
 
 @pytest.mark.parametrize("cfg", [TINY, TINY_DYN,
                                  TINY_DYN.with_(name="tiny_f32_dynamic_fp8ref", ref_fp8=True)],
                          ids=lambda c: c.name)
-def test_append_every_position_in_order(cfg):
+@PROJ
+def test_append_every_position_in_order(cfg, proj):
     """An empty cache (all NaN) filled token by token reaches the same records
-    as the oracle's encode of the prefix; reference rows land in the cache."""
-    _log(f"[case] append {cfg.name} in order")
-    c = _make(cfg, prefill=False)
+    as the oracle's encode of the prefix; reference rows land in the cache
+    (with proj, so do their projections, which the later tokens' means
+    read)."""
+    _log(f"[case] append {cfg.name} in order proj={proj}")
+    c = _make(cfg, prefill=False, proj=proj)
     for t in range(cfg.T):
         c.append(np.full(cfg.B, t))
     c.check(cfg.name)
@@ -144,11 +168,12 @@ WIDE_FF = LLAMA8K.with_(name="append_c1280_dff4352_two_slices", B=2, T=600, N=5,
                                  RAGGED_BF16.with_(name="append_ragged_bf16_fp8ref", ref_fp8=True),
                                  WIDE_FF],
                          ids=lambda c: c.name)
-def test_append_independent_positions_per_sequence(cfg):
+@PROJ
+def test_append_independent_positions_per_sequence(cfg, proj):
     """Continuous batching: every call appends a different position in each
     sequence, in random order, with some sequences skipped (pos -1 or T)."""
-    _log(f"[case] append {cfg.name} random positions")
-    c = _make(cfg, prefill=True)
+    _log(f"[case] append {cfg.name} random positions proj={proj}")
+    c = _make(cfg, prefill=True, proj=proj)
     rng = np.random.default_rng(17)
     perms = [rng.permutation(cfg.T) for _ in range(cfg.B)]
     for i in range(60):
@@ -164,11 +189,12 @@ def test_append_independent_positions_per_sequence(cfg):
 @pytest.mark.parametrize("cfg", [LLAMA8K.with_(B=2), LLAMA8K_DYN,
                                  LLAMA8K.with_(name="llama8b_T8k_fp8ref", B=2, ref_fp8=True)],
                          ids=lambda c: c.name)
-def test_append_full_size_sampled(cfg):
+@PROJ
+def test_append_full_size_sampled(cfg, proj):
     """The Llama layer shape at 8k context: sampled positions (warm-up, tail,
     random), one per sequence per call."""
-    _log(f"[case] append {cfg.name} sampled")
-    c = _make(cfg, prefill=True)
+    _log(f"[case] append {cfg.name} sampled proj={proj}")
+    c = _make(cfg, prefill=True, proj=proj)
     pos = [P.sample_positions(cfg.T, cfg.stride, 150, seed=40 + b, cfg=cfg) for b in range(cfg.B)]
     n = min(len(p) for p in pos)
     for i in range(n):
@@ -176,20 +202,22 @@ def test_append_full_size_sampled(cfg):
     c.check(cfg.name)
 
 
-def test_append_bench_shape():
+@PROJ
+def test_append_bench_shape(proj):
     """The benchmark's append launch: 16 sequences at the end of a 32k
     context (pool of 2,048 references each), compared with the oracle."""
     from synth.configs import LLAMA32K
     cfg = LLAMA32K.with_(B=16, gather_frac=None)
-    _log("[case] append bench shape B=16 T=32k")
-    c = _make(cfg, prefill=True)
+    _log(f"[case] append bench shape B=16 T=32k proj={proj}")
+    c = _make(cfg, prefill=True, proj=proj)
     pos = np.array([cfg.T - 1 - 3 * b for b in range(cfg.B)])
     c.append(pos)
     c.check("bench shape")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_append_exact_ties_keep_smaller_positions(dtype):
+@PROJ
+def test_append_exact_ties_keep_smaller_positions(dtype, proj):
     """The encode's exact-tie case on the append path: six references are
     one identical row, a later reference equals the appended tokens, so each
     token keeps that reference and the three smallest duplicate positions
@@ -216,7 +244,7 @@ def test_append_exact_ties_keep_smaller_positions(dtype):
     else:
         w.kv[0] = kv
     _log(f"[case] append exact ties {dtype}")
-    c = Cache(w, prefill_refs=True)
+    c = Cache(w, prefill_refs=True, proj=proj)
     for t in probes:
         c.append(np.array([t]))
     torch.cuda.synchronize()
@@ -261,12 +289,14 @@ def test_append_row_slices_and_distance_batches(monkeypatch, split, batch, rb):
 
 
 @pytest.mark.parametrize("B", [1, 3])
-def test_append_with_no_position_is_a_no_op(B):
+@PROJ
+def test_append_with_no_position_is_a_no_op(B, proj):
     """A call in which no sequence appends (every position -1 or T) writes
     nothing: records keep their pattern, the cache its rows."""
     cfg = RAGGED_BF16.with_(name=f"append_none_b{B}", B=B)
     _log(f"[case] append {cfg.name} no positions")
-    c = _make(cfg, prefill=True)
+    c = _make(cfg, prefill=True, proj=proj)
+    ref_proj = c.ref_proj.cpu().numpy().copy() if proj else None
     for pos in (np.full(B, -1), np.full(B, cfg.T), np.array([-1, cfg.T, -5][:B])):
         c.append(pos)
     torch.cuda.synchronize()
@@ -277,3 +307,52 @@ def test_append_with_no_position_is_a_no_op(B):
     assert (c.z.cpu().numpy().view(np.uint8) == SENTINEL).all()
     kv = c.kv.cpu().view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(kv, c.expected_kv.view(np.uint16))
+    if proj:
+        assert np.array_equal(c.ref_proj.cpu().numpy().view(np.uint32), ref_proj.view(np.uint32))
+
+
+@pytest.mark.parametrize("cfg", [RAGGED_BF16, RAGGED_F32,
+                                 RAGGED_BF16.with_(name="append_ragged_bf16_fp8ref", ref_fp8=True),
+                                 WIDE_FF],
+                         ids=lambda c: c.name)
+def test_project_refs_against_fp64(cfg):
+    """rkv_project_refs: every stored reference's r_j [W1 | W2] against the
+    fp64 product of the stored values (E4M3 values for an FP8 store); fp32
+    sums over C rows of exact products, so within 1e-5 of the row's scale."""
+    from oracle import rkv_oracle as O
+    w = generate(cfg)
+    _log(f"[case] project refs {cfg.name}")
+    c = Cache(w, prefill_refs=True, proj=True)
+    torch.cuda.synchronize()
+    refs = np.asarray(R.rkv_reference_positions(c.p))
+    W = np.concatenate([x.astype(np.float64) for x in w.weights_f32()[:2]], axis=1)
+    got = c.ref_proj.cpu().numpy().reshape(cfg.B, len(refs), 2 * cfg.d_ff)
+    kv = w.kv_f32().astype(np.float64)
+    for b in range(cfg.B):
+        rows = kv[b, refs]
+        if cfg.ref_fp8:
+            rows = O.fp8_e4m3(rows)
+        want = rows @ W
+        scale = np.abs(rows) @ np.abs(W)
+        err = np.abs(got[b] - want) / np.maximum(scale, 1e-30)
+        assert err.max() < 1e-5, (b, err.max())
+
+
+def test_append_proj_extends_the_projections():
+    """Filling an empty cache through rkv_append_proj writes each appended
+    reference's row of the projections: they match rkv_project_refs of the
+    filled cache within fp32 summation order."""
+    cfg = RAGGED_BF16.with_(name="append_proj_rows", B=2, T=300)
+    w = generate(cfg)
+    _log("[case] append_proj projection rows")
+    c = Cache(w, prefill_refs=False, proj=True)
+    for t in range(cfg.T):
+        c.append(np.full(cfg.B, t))
+    torch.cuda.synchronize()
+    built = c.ref_proj.cpu().numpy().copy()
+    R.rkv_project_refs(c.p, c.kv, c.w1, c.w2, c.ref_proj, c.ws, c.ws_bytes,
+                       torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    fresh = c.ref_proj.cpu().numpy()
+    assert np.all(np.isfinite(built))
+    assert np.allclose(built, fresh, rtol=1e-5, atol=1e-5 * np.abs(fresh).max())
