@@ -251,7 +251,9 @@ def bench_append(R, cfg, p_enc, kv, w1, w2, w3, stream, args, batches=(1, 16)):
     timed with events over repeated calls (each call rewrites the same
     records).  HBM bytes per call are algorithmic: the pool rows read by the
     distances, the chosen rows of the mean, the new rows, W1, W2 and W3 once,
-    and the records written."""
+    and the records written.  The same calls through rkv_append_proj (the
+    cache's reference projections computed once beforehand) are timed
+    beside them ("proj")."""
     import numpy as np
     import torch
     dev = kv.device
@@ -305,6 +307,32 @@ def bench_append(R, cfg, p_enc, kv, w1, w2, w3, stream, args, batches=(1, 16)):
         torch.cuda.synchronize()
         tot, cnt = R.rkv_profile_read(st)
         R.rkv_profile_begin(0)
+        # the same call through rkv_append_proj, with the references'
+        # projections of the cache computed once beforehand (rkv_project_refs)
+        wsp = R.rkv_append_proj_workspace_bytes(p)
+        wsp_t = torch.empty(wsp, dtype=torch.uint8, device=dev)
+        ref_proj = torch.empty(R.rkv_ref_proj_bytes(p) // 4, dtype=torch.float32, device=dev)
+        R.rkv_project_refs(p, cache, w1, w2, ref_proj, wsp_t, wsp, stream)
+
+        def call_proj():
+            R.rkv_append_proj(p, cache, ref_proj, kv_new, pos, w1, w2, w3, ref_idx, codes, scale,
+                              zmin, None, wsp_t, wsp, stream)
+
+        for _ in range(max(args.warmup, 3)):
+            call_proj()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            call_proj()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_proj = e0.elapsed_time(e1) / reps
+        R.rkv_profile_begin(1 << st)
+        for _ in range(reps):
+            call_proj()
+        torch.cuda.synchronize()
+        tot_p, cnt_p = R.rkv_profile_read(st)
+        R.rkv_profile_begin(0)
         pools = np.searchsorted(np.asarray(refs), pos_h)          # references before each position
         nbytes = (int(pools.sum()) * cfg.C * esz + B * (cfg.k + 1) * cfg.C * esz
                   + (2 * cfg.C * cfg.d_ff + cfg.d_ff * cfg.d_c) * esz + B * rec)
@@ -313,8 +341,12 @@ def bench_append(R, cfg, p_enc, kv, w1, w2, w3, stream, args, batches=(1, 16)):
                     "stage_us": round(tot / cnt * 1e3, 2), "hbm_bytes_algorithmic": nbytes,
                     "hbm_gb_s": round(nbytes / (tot / cnt * 1e-3) / 1e9, 1),
                     "hbm_frac": round(nbytes / (tot / cnt * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                    "pool_refs": int(pools.max())})
-        del cache, kv_new, ref_idx, codes, scale, zmin, ws
+                    "pool_refs": int(pools.max()),
+                    "proj": {"call": "rkv_append_proj (reference projections kept with the cache)",
+                             "us_per_call": round(ms_proj * 1e3, 2),
+                             "tokens_per_s": round(B / (ms_proj * 1e-3), 1),
+                             "stage_us": round(tot_p / cnt_p * 1e3, 2)}})
+        del cache, kv_new, ref_idx, codes, scale, zmin, ws, wsp_t, ref_proj
     return out
 
 

@@ -301,9 +301,9 @@ rkv_status rkv_append(const rkv_params* p, void* kv, const void* kv_new,
  * held until the process ends; its address is looked up on the first call
  * on each device).  Nothing is allocated or freed and no allocating routine
  * is called.  Returns RKV_ERR_WORKSPACE, with nothing enqueued, when the
- * call needs more than 4 MiB (rkv_append_workspace_bytes(p) > 4 MiB, e.g.
- * more than 340 sequences at C = 2048, d_ff = 1024 with 2,048 references
- * each): use rkv_append
+ * call needs more than 4 MiB (rkv_append_workspace_bytes(p) > 4 MiB; at
+ * C = 2048, d_ff = 1024 with 2,048 references per sequence every B that
+ * rkv_params allows fits: 82 KB at B = 1, 1.6 MB at B = 64): use rkv_append
  * there.  Every call on a GPU shares that GPU's array, so calls that
  * overlap on one GPU (on different streams, or from different threads) race
  * and give undefined results; serialise them on one stream.  The array keeps
