@@ -652,12 +652,17 @@ __global__ __launch_bounds__(CF::kThreads, CF::kMinWaves) void k_dist_topk(
 #pragma unroll
     for (int i = 0; i < KL; ++i) { md[i] = __builtin_inff(); mi[i] = 0x7fffffff; }
 #pragma unroll
-    for (int o = 0; o < kLists; ++o)
+    for (int o = 0; o < kLists; ++o) {                   // each list in ascending (d, j)
+      float ld[KL];
+      int li[KL];
 #pragma unroll
       for (int i = 0; i < KL; ++i) {
         const float2 v = xl[(t * kLists + o) * KL + i];
-        topk_push_lex<KL>(md, mi, v.x, __float_as_int(v.y));
+        ld[i] = v.x;
+        li[i] = __float_as_int(v.y);
       }
+      merge_sorted_lex<KL>(md, mi, ld, li);
+    }
     float2* out = part + ((size_t(b) * n_lists + c) * nr + q) * KL;
 #pragma unroll
     for (int i = 0; i < KL; ++i) out[i] = make_float2(md[i], __int_as_float(mi[i]));
@@ -672,7 +677,9 @@ __global__ __launch_bounds__(CF::kThreads, CF::kMinWaves) void k_dist_topk(
 // written by the set-up kernel: references are stored as they are, [RKV]
 // §2.4.)  kMergeLanes consecutive lanes share a token: lane s merges lists
 // s, s + 4, ..., two at a time with both in flight, then the lanes' lists
-// are merged by a butterfly over the four, and the first writes the result.
+// are merged by a butterfly over the four, and the first writes the result;
+// every list is in ascending (d, j) order, so each step merges two sorted
+// lists (merge_sorted_lex).
 constexpr int kMergeLanes = 4;
 
 template <int KL>
@@ -712,15 +719,18 @@ __global__ __launch_bounds__(256) void k_topk_merge(const float2* __restrict__ p
       for (int h = 0; h < KL / 2; ++h) v[u][h] = src[h];
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < 2; ++u) {                        // each list in ascending (d, j)
       const bool live = c0 + u * kMergeLanes < nch;
+      float ld[KL];
+      int li[KL];
 #pragma unroll
       for (int h = 0; h < KL / 2; ++h) {
-        topk_push_lex<KL>(bd, bi, live ? v[u][h].x : __builtin_inff(),
-                          live ? __float_as_int(v[u][h].y) : 0x7fffffff);
-        topk_push_lex<KL>(bd, bi, live ? v[u][h].z : __builtin_inff(),
-                          live ? __float_as_int(v[u][h].w) : 0x7fffffff);
+        ld[2 * h] = live ? v[u][h].x : __builtin_inff();
+        li[2 * h] = live ? __float_as_int(v[u][h].y) : 0x7fffffff;
+        ld[2 * h + 1] = live ? v[u][h].z : __builtin_inff();
+        li[2 * h + 1] = live ? __float_as_int(v[u][h].w) : 0x7fffffff;
       }
+      merge_sorted_lex<KL>(bd, bi, ld, li);
     }
   }
 #pragma unroll
@@ -729,8 +739,7 @@ __global__ __launch_bounds__(256) void k_topk_merge(const float2* __restrict__ p
     int oi[KL];
 #pragma unroll
     for (int i = 0; i < KL; ++i) { od[i] = __shfl_xor(bd[i], off); oi[i] = __shfl_xor(bi[i], off); }
-#pragma unroll
-    for (int i = 0; i < KL; ++i) topk_push_lex<KL>(bd, bi, od[i], oi[i]);
+    merge_sorted_lex<KL>(bd, bi, od, oi);
   }
   if (!enc || sub != 0) return;
   int32_t* out = ref_idx + tok * k;
