@@ -312,7 +312,14 @@ def bench_append(R, cfg, p_enc, kv, w1, w2, w3, stream, args, batches=(1, 16)):
         wsp = R.rkv_append_proj_workspace_bytes(p)
         wsp_t = torch.empty(wsp, dtype=torch.uint8, device=dev)
         ref_proj = torch.empty(R.rkv_ref_proj_bytes(p) // 4, dtype=torch.float32, device=dev)
-        R.rkv_project_refs(p, cache, w1, w2, ref_proj, wsp_t, wsp, stream)
+        wpr = R.rkv_project_refs_workspace_bytes(p)
+        wpr_t = torch.empty(wpr, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        R.rkv_project_refs(p, cache, w1, w2, ref_proj, wpr_t, wpr, stream)
+        torch.cuda.synchronize()
+        project_ms = (time.perf_counter() - t0) * 1e3
+        del wpr_t
 
         def call_proj():
             R.rkv_append_proj(p, cache, ref_proj, kv_new, pos, w1, w2, w3, ref_idx, codes, scale,
@@ -345,7 +352,8 @@ def bench_append(R, cfg, p_enc, kv, w1, w2, w3, stream, args, batches=(1, 16)):
                     "proj": {"call": "rkv_append_proj (reference projections kept with the cache)",
                              "us_per_call": round(ms_proj * 1e3, 2),
                              "tokens_per_s": round(B / (ms_proj * 1e-3), 1),
-                             "stage_us": round(tot_p / cnt_p * 1e3, 2)}})
+                             "stage_us": round(tot_p / cnt_p * 1e3, 2),
+                             "project_refs_ms_once": round(project_ms, 3)}})
         del cache, kv_new, ref_idx, codes, scale, zmin, ws, wsp_t, ref_proj
     return out
 

@@ -327,10 +327,13 @@ rkv_status rkv_append_noalloc(const rkv_params* p, void* kv, const void* kv_new,
  * rkv_project_refs fills every row from the cache kv (laid out as for
  * rkv_append; a row whose reference is not stored yet gets whatever its
  * kv row holds projected); w1, w2 as in rkv_encode.  workspace: at least
- * rkv_append_proj_workspace_bytes(p) bytes (private, need not be
- * initialised).  Arithmetic: fp32 on the vector ALUs from the stored
- * values, each output summed over C in chunks of 512 rows. */
+ * rkv_project_refs_workspace_bytes(p) bytes (private, need not be
+ * initialised).  Arithmetic: with bf16 references kept at input precision,
+ * the encode's projection tiles on the matrix cores (bf16 products, fp32
+ * sums); otherwise fp32 on the vector ALUs, each output summed over C in
+ * chunks of 512 rows. */
 size_t rkv_ref_proj_bytes(const rkv_params* p);
+size_t rkv_project_refs_workspace_bytes(const rkv_params* p);
 size_t rkv_append_proj_workspace_bytes(const rkv_params* p);
 rkv_status rkv_project_refs(const rkv_params* p, const void* kv, const void* w1,
                             const void* w2, float* ref_proj, void* workspace,

@@ -51,6 +51,7 @@ EXPORTS = (
     "rkv_append",
     "rkv_append_noalloc",
     "rkv_ref_proj_bytes",
+    "rkv_project_refs_workspace_bytes",
     "rkv_append_proj_workspace_bytes",
     "rkv_project_refs",
     "rkv_append_proj",
@@ -138,6 +139,8 @@ def lib() -> ctypes.CDLL:
         L.rkv_append_noalloc.restype = ctypes.c_int
         L.rkv_ref_proj_bytes.argtypes = [P]
         L.rkv_ref_proj_bytes.restype = sz
+        L.rkv_project_refs_workspace_bytes.argtypes = [P]
+        L.rkv_project_refs_workspace_bytes.restype = sz
         L.rkv_append_proj_workspace_bytes.argtypes = [P]
         L.rkv_append_proj_workspace_bytes.restype = sz
         L.rkv_project_refs.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
@@ -450,6 +453,10 @@ def rkv_append_noalloc(p: rkv_params, kv, kv_new, pos, w1, w2, w3, ref_idx, code
 
 def rkv_ref_proj_bytes(p: rkv_params) -> int:
     return int(lib().rkv_ref_proj_bytes(ctypes.byref(p)))
+
+
+def rkv_project_refs_workspace_bytes(p: rkv_params) -> int:
+    return int(lib().rkv_project_refs_workspace_bytes(ctypes.byref(p)))
 
 
 def rkv_append_proj_workspace_bytes(p: rkv_params) -> int:

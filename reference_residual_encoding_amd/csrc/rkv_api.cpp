@@ -543,6 +543,11 @@ size_t rkv_append_proj_workspace_bytes(const rkv_params* p) {
   return rkv::plan_append_proj(shape_of(p)).total;
 }
 
+size_t rkv_project_refs_workspace_bytes(const rkv_params* p) {
+  if (check_params(p) != RKV_OK) return 0;
+  return rkv::plan_project_refs(shape_of(p)).total;
+}
+
 rkv_status rkv_project_refs(const rkv_params* p, const void* kv, const void* w1, const void* w2,
                             float* ref_proj, void* workspace, size_t workspace_bytes,
                             hipStream_t stream) {
@@ -554,7 +559,7 @@ rkv_status rkv_project_refs(const rkv_params* p, const void* kv, const void* w1,
   RKV_NEED_PTR(ref_proj);
   RKV_NEED_PTR(workspace);
   const rkv::Shape sh = shape_of(p);
-  const rkv::AppendWorkspace L = rkv::plan_append_proj(sh);
+  const rkv::AppendWorkspace L = rkv::plan_project_refs(sh);
   if (workspace_bytes < L.total)
     return fail(RKV_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
   hipError_t e;

@@ -1206,6 +1206,16 @@ static hipError_t sched_view(const Shape& sh, char* ws, const AppendWorkspace& L
   return hipSuccess;
 }
 
+AppendWorkspace plan_project_refs(const Shape& sh) {
+  AppendWorkspace L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off += align256(bytes); return at; };
+  L.rpos = take(size_t(sh.nref) * 4);
+  L.ph = take(ref_proj_pack_bytes(sh));                  // packed W1 | W2 (matrix-core form)
+  L.total = std::max<size_t>(off, 256);
+  return L;
+}
+
 hipError_t launch_project_refs(const Shape& sh, const void* kv, const void* w1, const void* w2,
                                float* ref_proj, char* ws, const AppendWorkspace& L,
                                hipStream_t st) {
@@ -1213,6 +1223,8 @@ hipError_t launch_project_refs(const Shape& sh, const void* kv, const void* w1, 
   SchedView sv;
   const hipError_t e = sched_view(sh, ws, L, st, sv);
   if (e != hipSuccess) return e;
+  if (ref_proj_pack_bytes(sh) > 0 && std::getenv("RKV_REF_PROJ_VALU") == nullptr)
+    return launch_ref_proj_mfma(sh, kv, w1, w2, sv, ws + L.ph, ref_proj, st);
   const int grid = 2 * sh.d_ff / 16 * cdiv(long(sh.B) * sh.nref, 16);
 #define RKV_RP(E, F8)                                                                             \
   k_ref_proj<E, F8><<<grid, 256, 0, st>>>(kv, sv, sh.T, sh.C, sh.B, static_cast<const E*>(w1),    \

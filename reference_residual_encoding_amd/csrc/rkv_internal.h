@@ -144,6 +144,14 @@ hipError_t launch_append(const Shape& sh, void* kv, const void* kv_new, const in
 // workspace (ph holds the tokens' partial projections) also serves
 // rkv_project_refs.
 AppendWorkspace plan_append_proj(const Shape& sh);
+AppendWorkspace plan_project_refs(const Shape& sh);
+struct SchedView;  // rkv_device.h
+// rkv_project_refs on the matrix cores (bf16 input-precision references):
+// the bytes of its packed W1 | W2, 0 where it does not apply (fp32, FP8
+// store: the vector-ALU kernel), and the launch (packing, then the tiles).
+size_t ref_proj_pack_bytes(const Shape& sh);
+hipError_t launch_ref_proj_mfma(const Shape& sh, const void* kv, const void* w1, const void* w2,
+                                const SchedView& sv, char* wp, float* proj, hipStream_t st);
 hipError_t launch_project_refs(const Shape& sh, const void* kv, const void* w1, const void* w2,
                                float* ref_proj, char* ws, const AppendWorkspace& L,
                                hipStream_t st);

@@ -435,18 +435,36 @@ __global__ __launch_bounds__(256) void k_ref_store(const E* __restrict__ kv, int
 // first layer applied to their mean).  R is the compact reference rows
 // (M = B * nref), wp the packed [W1|W2] (N = 2 d_ff rows of C).  Tile `tile`
 // of tiles_m x tiles_n, row tile fastest.
+template <typename E, typename CF, bool UNPACK, typename RowOf>
+__device__ __forceinline__ void ref_proj_tile_rows(const RowOf& rowof, const char* __restrict__ wp,
+                                                   float* __restrict__ proj, int C, int M, int N,
+                                                   int tiles_m, int tile, char* lds);
+
 template <typename E, typename CF>
 __device__ __forceinline__ void ref_proj_tile(const char* __restrict__ refs,
                                               const char* __restrict__ wp,
                                               float* __restrict__ proj, int C, int M, int N,
                                               int tiles_m, int tile, char* lds) {
+  const size_t rb = size_t(C) * sizeof(E);
+  ref_proj_tile_rows<E, CF, false>([&](int m) { return refs + size_t(m) * rb; }, wp, proj, C, M,
+                                   N, tiles_m, tile, lds);
+}
+
+// The same tile with row m of R at rowof(m) (m < M).  The packed weights
+// interleave W1 and W2 in blocks of 32 outputs (32 of W1, then the same 32
+// of W2); with UNPACK the columns are stored in the order [W1 | W2].
+template <typename E, typename CF, bool UNPACK, typename RowOf>
+__device__ __forceinline__ void ref_proj_tile_rows(const RowOf& rowof,
+                                                   const char* __restrict__ wp,
+                                                   float* __restrict__ proj, int C, int M, int N,
+                                                   int tiles_m, int tile, char* lds) {
   constexpr int BM = CF::BM, BN = CF::BN, WGM = CF::WGM, WGN = CF::WGN;
   constexpr int kWM = BM / WGM, kWN = BN / WGN, kTM = kWM / 32, kTN = kWN / 32;
   const int mt = tile % tiles_m, nt = tile / tiles_m;
   const int m0 = mt * BM, n0 = nt * BN;
   const size_t rowb = size_t(C) * sizeof(E);
   const int tid = threadIdx.x;
-  auto rowA = [&](int r) { return refs + size_t(min(m0 + r, M - 1)) * rowb; };
+  auto rowA = [&](int r) { return rowof(min(m0 + r, M - 1)); };
   auto rowB = [&](int r) { return wp + size_t(min(n0 + r, N - 1)) * rowb; };
   f32x16 acc[kTM][kTN];
   tile_product<E, BM, BN, CF::SB, CF::NS, WGM, WGN>(rowA, rowB, int(rowb), lds, acc);
@@ -459,7 +477,10 @@ __device__ __forceinline__ void ref_proj_tile(const char* __restrict__ refs,
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = m0 + wm * kWM + tm * 32 + mfma32_row(r, lane);
-        if (row < M && col < N) proj[size_t(row) * N + col] = acc[tm][tn][r];
+        if (row < M && col < N) {
+          const int o = UNPACK ? ((col >> 5) & 1) * (N >> 1) + (col >> 6) * 32 + (col & 31) : col;
+          proj[size_t(row) * N + o] = acc[tm][tn][r];
+        }
       }
     }
 }
@@ -1481,6 +1502,28 @@ __global__ __launch_bounds__(256) void k_gather(const uint8_t* __restrict__ code
   }
 }
 
+// P = R [W1 | W2] for the references a bf16 cache holds, rows in place: row
+// m = b nref + j of R is kv row b T + p_j ([RKV] §2.2 mean eq.: the
+// projections whose mean the append's mean branch takes); the encode's
+// projection tiles on the same packed weights.
+template <typename CF>
+__global__ __launch_bounds__(CF::kThreads, 1) void k_ref_proj_rows(const char* __restrict__ kv,
+                                                                   SchedView sv, int T, int C,
+                                                                   int B,
+                                                                   const char* __restrict__ wp,
+                                                                   float* __restrict__ proj,
+                                                                   int N, int tiles_m) {
+  constexpr int kL = mainloop_lds<uint16_t, CF::BM, CF::BN, CF::SB, CF::NS, CF::WGM, CF::WGN>();
+  __shared__ __attribute__((aligned(1024))) char lds[kL];
+  const size_t rowb = size_t(C) * sizeof(uint16_t);
+  const int nref = sv.nref;
+  auto rowof = [&](int m) {
+    return kv + (size_t(m / nref) * T + size_t(ref_position(sv, m % nref))) * rowb;
+  };
+  ref_proj_tile_rows<uint16_t, CF, true>(rowof, wp, proj, C, B * nref, N, tiles_m,
+                                         int(blockIdx.x), lds);
+}
+
 int grid_for(int64_t work_items, int per_block) {
   const int64_t g = (work_items + per_block - 1) / per_block;
   return int(std::min<int64_t>(std::max<int64_t>(g, 1), 256 * 64));
@@ -1698,6 +1741,34 @@ hipError_t launch_setup(const Shape& sh, const void* w1, const void* w2, const v
     k_setup<uint16_t><<<grid, 256, 0, st>>>(J, n_pack, sa, n_tab, ra);
   else
     k_setup<float><<<grid, 256, 0, st>>>(J, n_pack, sa, n_tab, ra);
+  return hipGetLastError();
+}
+
+size_t ref_proj_pack_bytes(const Shape& sh) {
+  return sh.bf16 && !sh.ref_fp8 ? size_t(2) * sh.d_ff * sh.C * sh.esize : 0;
+}
+
+hipError_t launch_ref_proj_mfma(const Shape& sh, const void* kv, const void* w1, const void* w2,
+                                const SchedView& sv, char* wp, float* proj, hipStream_t st) {
+  // W1 | W2 packed as the encode packs them (rows of C, K-contiguous)
+  auto tiles = [](int n) { return (n + 63) / 64; };
+  PackJobs J{};
+  J.j[0] = {w1, wp, sh.C, sh.d_ff, sh.C, 1, tiles(sh.d_ff), 0};
+  J.j[1] = {w2, wp, sh.C, sh.d_ff, sh.C, 2, tiles(sh.d_ff), 0};
+  int n_pack = 0;
+  for (int i = 0; i < 2; ++i) {
+    J.j[i].first = n_pack;
+    n_pack += tiles(J.j[i].rows) * J.j[i].tiles_c;
+  }
+  J.j[2].first = n_pack;                                 // no third job
+  k_pack_weights<uint16_t><<<n_pack, 256, 0, st>>>(J);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  using PF = DistCfg<uint16_t>::Proj;
+  const int M = sh.B * sh.nref, N = 2 * sh.d_ff;
+  const int tm = cdiv(M, PF::BM), tn = cdiv(N, PF::BN);
+  k_ref_proj_rows<PF><<<tm * tn, PF::kThreads, 0, st>>>(static_cast<const char*>(kv), sv, sh.T,
+                                                        sh.C, sh.B, wp, proj, N, tm);
   return hipGetLastError();
 }
 

@@ -74,9 +74,15 @@ class Cache:
         assert self.ws_bytes > 0
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
         if proj and prefill_refs:
-            R.rkv_project_refs(self.p, self.kv, self.w1, self.w2, self.ref_proj, self.ws,
-                               self.ws_bytes, torch.cuda.current_stream())
+            self.project()
         self.appended = np.zeros((cfg.B, cfg.T), bool)
+
+    def project(self):
+        """rkv_project_refs of the cache's stored references into ref_proj."""
+        nbytes = R.rkv_project_refs_workspace_bytes(self.p)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=self.kv.device)
+        R.rkv_project_refs(self.p, self.kv, self.w1, self.w2, self.ref_proj, ws, nbytes,
+                           torch.cuda.current_stream())
 
     def append(self, pos):
         cfg = self.cfg
@@ -313,15 +319,20 @@ def test_append_with_no_position_is_a_no_op(B, proj):
 
 @pytest.mark.parametrize("cfg", [RAGGED_BF16, RAGGED_F32,
                                  RAGGED_BF16.with_(name="append_ragged_bf16_fp8ref", ref_fp8=True),
-                                 WIDE_FF],
+                                 WIDE_FF, LLAMA8K.with_(B=2)],
                          ids=lambda c: c.name)
-def test_project_refs_against_fp64(cfg):
+@pytest.mark.parametrize("valu", [False, True], ids=["default", "valu"])
+def test_project_refs_against_fp64(cfg, valu, monkeypatch):
     """rkv_project_refs: every stored reference's r_j [W1 | W2] against the
     fp64 product of the stored values (E4M3 values for an FP8 store); fp32
-    sums over C rows of exact products, so within 1e-5 of the row's scale."""
+    sums over C rows of exact products, so within 1e-5 of the row's scale.
+    bf16 input-precision references take the matrix cores unless
+    RKV_REF_PROJ_VALU is set."""
     from oracle import rkv_oracle as O
+    if valu:
+        monkeypatch.setenv("RKV_REF_PROJ_VALU", "1")
     w = generate(cfg)
-    _log(f"[case] project refs {cfg.name}")
+    _log(f"[case] project refs {cfg.name} valu={valu}")
     c = Cache(w, prefill_refs=True, proj=True)
     torch.cuda.synchronize()
     refs = np.asarray(R.rkv_reference_positions(c.p))
@@ -350,8 +361,7 @@ def test_append_proj_extends_the_projections():
         c.append(np.full(cfg.B, t))
     torch.cuda.synchronize()
     built = c.ref_proj.cpu().numpy().copy()
-    R.rkv_project_refs(c.p, c.kv, c.w1, c.w2, c.ref_proj, c.ws, c.ws_bytes,
-                       torch.cuda.current_stream())
+    c.project()
     torch.cuda.synchronize()
     fresh = c.ref_proj.cpu().numpy()
     assert np.all(np.isfinite(built))
