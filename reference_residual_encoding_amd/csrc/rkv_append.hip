@@ -21,6 +21,12 @@
 //            - Swish(m W1) (m W2) ([RKV] §2.3), z = delta_h W3 (W3 is
 //            linear, so f_c(kv) - f_c(m) = (h(kv) - h(m)) W3), then the group
 //            quantiser of [RKV] §2.4 and the record
+// With the references' projections P = R [W1 | W2] kept beside the cache
+// (rkv_append_proj), two launches do the same: dist_xproj (the distance
+// workgroups and, in the same grid, x [W1 | W2] in slices of the C rows)
+// and sel_w3 (per token and column block: the selection, m [W1 | W2] as the
+// mean of k_t rows of P, delta_h, W3 and the quantiser); ref_proj fills P
+// on the vector ALUs where the matrix-core tiles do not apply.
 #include "rkv_device.h"
 #include "rkv_internal.h"
 #include "rkv_quant.h"
